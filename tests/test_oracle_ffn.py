@@ -1,0 +1,197 @@
+"""Pins for the oracle's expert FFN and combine.
+
+The FFN is gate/up matvec -> SwiGLU -> down matvec over group-wise dequantised
+weights (fused SwiGLU and combine + residual: page "Flash-MoE ...
+(translation)", section 3; weight = code * scale + bias: same page, section 2).
+Structured experts give closed forms that a dropped term, a wrong group or row
+index, a swapped gate/up or a transposed matrix would all break:
+  * permutation experts (each row picks one input) -> Y_n = silu(x_a) * c x_b;
+  * zero expert -> Y = 0;
+  * per-group constant experts -> sums of group sums of x;
+  * per-(row, group) scales with unit codes;
+  * a dense float64 reference built from numpy-decoded weights on the tiny shape.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+
+
+def _bf16_f64(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _f16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _pack_matrix(codes, scale_f, bias_f, bits=4):
+    return (mi.pack_codes(codes, bits), mi.f32_to_f16_bits(scale_f), mi.f32_to_f16_bits(bias_f))
+
+
+def _selection_expert(N, K, cols, value_code=1, scale=1.0, bits=4):
+    """Row n has a single nonzero code at column cols[n] (bias 0)."""
+    q = np.zeros((N, K), np.uint8)
+    q[np.arange(N), cols] = value_code
+    return _pack_matrix(q, np.full((N, K // 128), scale), np.zeros((N, K // 128)), bits)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_ffn_permutation_expert_closed_form(orc, bits):
+    H, I = 256, 512
+    rng = np.random.default_rng(30 + bits)
+    x = mi.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32))
+    pg = rng.integers(0, H, I)                    # gate row i reads x[pg[i]]
+    pu = rng.integers(0, H, I)                    # up row i reads x[pu[i]]
+    pd = rng.permutation(I)[:H]                   # down row n reads h[pd[n]]
+    w = {"gate": _selection_expert(I, H, pg, 1, 1.0, bits),
+         "up": _selection_expert(I, H, pu, 2, 0.25, bits),       # weight 0.5
+         "down": _selection_expert(H, I, pd, 3, 0.5, bits)}      # weight 1.5
+    h, y = orc.expert_ffn_row(x, w, bits)
+    xf = _bf16_f64(x)
+    a = xf[pg]
+    u = 0.5 * xf[pu]
+    h_ref = (a / (1.0 + np.exp(-a)) * u).astype(np.float32)
+    assert np.array_equal(h, h_ref)
+    y_ref = mi.f32_to_bf16_bits((1.5 * h_ref[pd].astype(np.float64)).astype(np.float32))
+    assert np.array_equal(y, y_ref)
+
+
+def test_ffn_identity_expert_is_swiglu_of_input(orc):
+    """Identity gate/up/down (code 1, scale 1, bias 0): Y_n = silu(x_n) * x_n for
+    n < min(H, I) and 0 beyond."""
+    H, I = 256, 512
+    rng = np.random.default_rng(40)
+    x = mi.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32))
+    eye_gu = np.arange(I) % H                     # rows >= H repeat (still one pick per row)
+    w = {"gate": _selection_expert(I, H, eye_gu), "up": _selection_expert(I, H, eye_gu),
+         "down": _selection_expert(H, I, np.arange(H))}
+    _, y = orc.expert_ffn_row(x, w, 4)
+    xf = _bf16_f64(x)
+    ref = mi.f32_to_bf16_bits((xf / (1 + np.exp(-xf)) * xf).astype(np.float32))
+    assert np.array_equal(y, ref)
+
+
+def test_ffn_zero_expert(orc):
+    H, I = 256, 256
+    z = _pack_matrix(np.zeros((I, H), np.uint8), np.full((I, 2), 0.01), np.zeros((I, 2)))
+    w = {"gate": z, "up": z, "down": z}
+    x = mi.f32_to_bf16_bits(np.random.default_rng(1).standard_normal(H).astype(np.float32))
+    h, y = orc.expert_ffn_row(x, w, 4)
+    assert np.all(h == 0) and np.all(y == 0)
+
+
+def test_ffn_group_constants_closed_form(orc):
+    """Codes 0, bias beta[n, g]: a_i = sum_g beta_g(i) * X_g with X_g the sum of x
+    over group g; codes 1 with scale s[n, g] and bias 0 give the same form."""
+    H, I = 512, 256
+    rng = np.random.default_rng(50)
+    x = mi.f32_to_bf16_bits(rng.standard_normal(H).astype(np.float32))
+    xf = _bf16_f64(x)
+    Xg = xf.reshape(4, 128).sum(1)
+    beta = mi.f32_to_f16_bits(rng.normal(0, 0.01, (I, 4)))
+    sc = mi.f32_to_f16_bits(rng.uniform(0.005, 0.02, (I, 4)))
+    gate = (mi.pack_codes(np.zeros((I, H), np.uint8), 4), sc, beta)          # a = sum beta X
+    up = (mi.pack_codes(np.ones((I, H), np.uint8), 4), sc, np.zeros((I, 4), np.uint16))  # u = sum s X
+    down = _selection_expert(H, I, np.arange(H) % I)
+    h, y = orc.expert_ffn_row(x, {"gate": gate, "up": up, "down": down}, 4)
+    a = (_f16(beta) * Xg).sum(1).astype(np.float32).astype(np.float64)
+    u = (_f16(sc) * Xg).sum(1).astype(np.float32).astype(np.float64)
+    h_ref = (a / (1 + np.exp(-a)) * u).astype(np.float32)
+    assert np.allclose(h, h_ref, rtol=1e-6, atol=0)
+    # down: per-group constant again, now over h
+    dn_beta = mi.f32_to_f16_bits(rng.normal(0, 0.01, (H, 2)))
+    down2 = (mi.pack_codes(np.zeros((H, I), np.uint8), 4), np.zeros((H, 2), np.uint16), dn_beta)
+    h2, y2 = orc.expert_ffn_row(x, {"gate": gate, "up": up, "down": down2}, 4)
+    Hg = h2.astype(np.float64).reshape(2, 128).sum(1)
+    y_ref = (_f16(dn_beta) * Hg).sum(1)
+    assert np.allclose(_bf16_f64(y2), y_ref, rtol=2 ** -8, atol=0)
+
+
+def test_ffn_dense_float64_reference_tiny(orc):
+    """Random tiny-shape expert against a dense float64 evaluation whose weights
+    are decoded by numpy bit operations (not by the oracle)."""
+    shape = mi.CONFIGS["tiny"]
+    W = mi.make_expert_weights(shape, 4, seed=0, experts=[3])
+    xb, _ = mi.make_activations(shape.H, 2, seed=0)
+    dense = {}
+    for m in mi.MATRICES:
+        q = W.q[m][0]
+        codes = np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1).astype(np.float64)
+        g = np.arange(codes.shape[1]) // 128
+        dense[m] = codes * _f16(W.scale[m][0])[:, g] + _f16(W.bias[m][0])[:, g]
+    ow = {m: (W.q[m][0], W.scale[m][0], W.bias[m][0]) for m in mi.MATRICES}
+    for t in range(2):
+        h, y = orc.expert_ffn_row(xb[t], ow, 4)
+        xf = _bf16_f64(xb[t])
+        a = (dense["gate"] @ xf).astype(np.float32).astype(np.float64)
+        u = (dense["up"] @ xf).astype(np.float32).astype(np.float64)
+        h_ref = (a / (1 + np.exp(-a)) * u).astype(np.float32)
+        assert np.allclose(h, h_ref, rtol=1e-6, atol=1e-6)
+        yd = dense["down"] @ h.astype(np.float64)
+        assert np.max(np.abs(_bf16_f64(y) - yd) / np.maximum(np.abs(yd), 1e-3)) <= 2 ** -8
+
+
+def test_ffn_sampled_outputs_match_full(orc):
+    shape = mi.CONFIGS["tiny"]
+    W = mi.make_expert_weights(shape, 4, seed=0, experts=[1])
+    xb, _ = mi.make_activations(shape.H, 1, seed=0)
+    ow = {m: (W.q[m][0], W.scale[m][0], W.bias[m][0]) for m in mi.MATRICES}
+    h, y = orc.expert_ffn_row(xb[0], ow, 4)
+    idx = np.array([0, 17, 255, 128], np.int32)
+    h2, ys = orc.expert_ffn_row(xb[0], ow, 4, n_idx=idx)
+    assert np.array_equal(h, h2) and np.array_equal(ys, y[idx])
+
+
+def test_combine_closed_forms(orc):
+    rng = np.random.default_rng(60)
+    T, H, k = 3, 256, 2
+    res = mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    Y = mi.f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32) * 100)
+    # every pair of token t uses the same Y row; gates 0.5 + 0.5 (exact halves)
+    Yr = np.repeat(Y[::k], k, axis=0)
+    p2r = np.arange(T * k, dtype=np.int32)
+    g = np.full((T, k), 0.5, np.float32)
+    out = orc.combine(Yr, p2r, g, res)
+    r32 = _bf16_f64(res).astype(np.float32)
+    y32 = _bf16_f64(Y[::k]).astype(np.float32)
+    # fma(0.5, y, r) = round(r + y/2) since y/2 is exact; applied twice in order
+    acc = (r32 + np.float32(0.5) * y32).astype(np.float32)
+    acc = (acc + np.float32(0.5) * y32).astype(np.float32)
+    assert np.array_equal(out, mi.f32_to_bf16_bits(acc))
+    # one pick with gate 1: out = bf16(residual + Y)
+    out1 = orc.combine(Y[:T], np.arange(T, dtype=np.int32), np.ones((T, 1), np.float32), res)
+    assert np.array_equal(out1, mi.f32_to_bf16_bits((r32 + _bf16_f64(Y[:T]).astype(np.float32)).astype(np.float32)))
+    # rows are gathered through pair_to_row: reversing the storage order of Y
+    # together with the map leaves the result unchanged
+    rev = np.arange(T * k)[::-1].astype(np.int32)
+    g2 = rng.random((T, k)).astype(np.float32)
+    a = orc.combine(Y, p2r, g2, res)
+    b = orc.combine(Y[::-1].copy(), rev, g2, res)
+    assert np.array_equal(a, b)
+
+
+def test_layer_identity_experts_end_to_end(orc):
+    """All experts identity, gates sum to 1: out ~= residual + silu(x) * x."""
+    shape = mi.CONFIGS["tiny"]
+    H, I, E, k, T = shape.H, shape.I, shape.E, shape.k, 4
+    eye_gu = np.arange(I) % H
+    one = {"gate": _selection_expert(I, H, eye_gu), "up": _selection_expert(I, H, eye_gu),
+           "down": _selection_expert(H, I, np.arange(H))}
+    W = mi.ExpertWeights(bits=4, experts=np.arange(E),
+                         q={m: np.stack([one[m][0]] * E) for m in mi.MATRICES},
+                         scale={m: np.stack([one[m][1]] * E) for m in mi.MATRICES},
+                         bias={m: np.stack([one[m][2]] * E) for m in mi.MATRICES})
+    xb, res = mi.make_activations(H, T, seed=3)
+    Wr, _ = mi.make_router(shape, seed=3)
+    out = orc.layer(xb, Wr, None, W, k, np.arange(E, dtype=np.int32), E, res)
+    assert out["perm"]["counts"].sum() == T * k
+    assert np.allclose(out["gates"].sum(1), 1.0, atol=4e-7)
+    xf = _bf16_f64(xb)
+    y = _bf16_f64(mi.f32_to_bf16_bits((xf / (1 + np.exp(-xf)) * xf).astype(np.float32)))
+    ref = _bf16_f64(res) + y
+    got = _bf16_f64(out["out"])
+    # one bf16 rounding of the sum plus float32 gate rounding (gates sum to 1 +- 4e-7)
+    assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-6 * np.abs(y))

@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Bench of the routed MoE decode layer on one MI355X.
+
+Workload: the A3B-style decode layer (hidden 2048, 256 experts, top-8 with
+renormalised gates, expert intermediate 512, SwiGLU, 4-bit weights with fp16
+scale and bias per group of 128, Zipf(1.1) expert popularity), a batch of
+--tokens decode tokens (default 32).  A step is one pass of the whole layer:
+
+    route_topk -> slot_lookup -> permute -> expert_gateup -> expert_down -> combine
+
+Successive steps cycle through --layers independently generated weight sets
+(like successive layers of a model; 4 x 428 MB by default), so the weights
+cannot stay in the 256 MB last-level cache and every step streams them from
+HBM.  Inputs are resident in HBM before the timed region starts.
+
+Printed: one JSON line with
+  value         tokens/s over the K timed steps (tokens * K / elapsed);
+  roofline      the gate/up kernel (2/3 of the weight bytes): algorithmic
+                weight bytes per launch (experts used * 2 * I * H * (bits/8 + 4/128))
+                over its mean duration, timed with HIP events around each launch
+                on the stream it runs on, against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle (single-threaded C) timed on one full step of
+                weight set 0 on this host.
+With --gpus N > 1 it exits: this bench measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+CONTEXT = [
+    "page 'Luce Spark': ~100 tok/s at 60% expert residency vs 119 tok/s fully resident, RTX 3090, whole 33B-A3B model",
+    "page 'Betelgeuse': 22 tok/s, RTX 3060 12GB, whole 68GB MoE model",
+    "page 'Flash-MoE': 4.36 tok/s with a ~418 GiB/s 4-bit dequant matvec kernel, M3 Max, whole 397B model",
+]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--tokens", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=4, help="rotating weight sets")
+    ap.add_argument("--sweep", default="1,8", help="extra token counts timed after the main run ('' = none)")
+    ap.add_argument("--algo", choices=["auto", "gemv", "mfma"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def upload_layer(shape, bits, seed, torch, mi, moe):
+    Wr, bias = mi.make_router(shape, seed)
+    table = mi.make_slot_table(shape, seed)
+    q, s, b = [], [], []
+    for m in mi.MATRICES:
+        N, K = mi.matrix_dims(shape, m)
+        q.append(torch.empty((shape.E, N, K * bits // 8), dtype=torch.uint8, device="cuda"))
+        s.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device="cuda"))
+        b.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device="cuda"))
+    for e, mats in mi.iter_expert_weights(shape, bits, seed):
+        for i, m in enumerate(mi.MATRICES):
+            qq, ss, bb = mats[m]
+            q[i][e].copy_(torch.from_numpy(qq))
+            s[i][e].copy_(torch.from_numpy(ss.view("int16")))
+            b[i][e].copy_(torch.from_numpy(bb.view("int16")))
+    dev = lambda a: torch.from_numpy(a).cuda()
+    return dict(Wr_np=Wr, bias_np=bias, table_np=table, Wr=dev(Wr), bias=None if bias is None else dev(bias),
+                table=dev(table), w=moe.QWeights(bits, q, s, b))
+
+
+class Runner:
+    """Enqueues layer steps over rotating weight sets; optional events around the FFN halves."""
+
+    def __init__(self, torch, mi, moe, shape, layers, T, algo):
+        self.torch, self.mi, self.moe = torch, mi, moe
+        self.shape, self.layers, self.T, self.algo = shape, layers, T, algo
+        sh = shape
+        self.d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+        self.buf = moe.LayerBuffers.allocate(self.d, layers[0]["w"].bits, algo)
+        self.h = torch.empty((max(T * sh.k, 1), sh.I), dtype=torch.float32, device="cuda")
+        self.x, self.res = [], []
+        for li in range(len(layers)):
+            xb, rb = mi.make_activations(sh.H, T, seed=1000 + li)
+            self.x.append(torch.from_numpy(xb.view("int16")).cuda())
+            self.res.append(torch.from_numpy(rb.view("int16")).cuda())
+        self.out = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
+
+    def step(self, i, ev=None):
+        moe, b, d = self.moe, self.buf, self.d
+        L = self.layers[i % len(self.layers)]
+        x, res = self.x[i % len(self.layers)], self.res[i % len(self.layers)]
+        bits = L["w"].bits
+        moe.route_topk(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w)
+        moe.slot_lookup(d, b.topk_ids, L["table"], self.shape.E, b.pair_slot, b.miss, b.n_miss)
+        moe.permute(d, b.topk_ids, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row, b.active, b.n_active)
+        if ev is not None:
+            ev[0].record()
+        moe.expert_gateup(d, bits, x, b.sorted_pairs, b.counts, b.offsets, b.active, b.n_active, L["w"], self.h,
+                          self.algo)
+        if ev is not None:
+            ev[1].record()
+        moe.expert_down(d, bits, self.h, b.counts, b.offsets, b.active, b.n_active, L["w"], b.y_rows, self.algo)
+        if ev is not None:
+            ev[2].record()
+        moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
+
+    def experts_used(self):
+        """Distinct experts per weight set for this batch (read back once, untimed)."""
+        U = []
+        for li in range(len(self.layers)):
+            self.step(li)
+            self.torch.cuda.synchronize()
+            U.append(int(self.buf.n_active.item()))
+        return U
+
+    def timed(self, steps, warmup, with_events=True):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)] if with_events else None
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(steps):
+            self.step(i, evs[i] if evs else None)
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t0.elapsed_time(t1)
+        gate_ms = [e[0].elapsed_time(e[1]) for e in evs] if evs else None
+        down_ms = [e[1].elapsed_time(e[2]) for e in evs] if evs else None
+        return total_ms, wall, gate_ms, down_ms
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_record(kernel_src):
+    """HBM traffic of the gate/up kernel from the committed counter summary, if it
+    was taken on the current source of that kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "gateup_a3b_T32_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(mi, shape, layer0, T):
+    """Oracle timed on one full layer step of weight set 0 (same inputs as the GPU)."""
+    import numpy as np
+    import oracle
+    xb, rb = mi.make_activations(shape.H, T, seed=1000)
+    logits = oracle.router_logits(xb, layer0["Wr_np"], layer0["bias_np"])
+    ids, _ = oracle.topk(logits, shape.k)
+    W = mi.make_expert_weights(shape, 4, seed=0, experts=np.unique(ids))
+    t0 = time.perf_counter()
+    oracle.layer(xb, layer0["Wr_np"], layer0["bias_np"], W, shape.k, layer0["table_np"], shape.E, rb)
+    sec = time.perf_counter() - t0
+    return dict(value=round(T / sec, 3), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"one full layer step of weight set 0: T={T} tokens, {T * shape.k} routed rows, "
+                       f"single-threaded C oracle (double accumulation), {sec:.2f} s",
+                seconds=round(sec, 3), host_cpus=os.cpu_count())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU expert-parallel design is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import quantized_expert_ffn_gemv_amd as moe
+
+    torch.cuda.set_device(0)
+    moe.lib()
+    shape = mi.CONFIGS["a3b"]
+    bits = 4
+    algo = {"auto": moe.ALGO_AUTO, "gemv": moe.ALGO_GEMV, "mfma": moe.ALGO_MFMA}[args.algo]
+    log(f"[bench] uploading {args.layers} weight sets of {shape.E * shape.bytes_per_expert(bits) / 1e6:.0f} MB")
+    layers = [upload_layer(shape, bits, seed=li, torch=torch, mi=mi, moe=moe) for li in range(args.layers)]
+    torch.cuda.synchronize()
+
+    per_expert = shape.bytes_per_expert(bits)
+    gate_bytes_per_expert = per_expert * 2 // 3
+    down_bytes_per_expert = per_expert // 3
+    router_bytes = shape.E * shape.H * 4
+
+    def measure(T, steps, warmup):
+        r = Runner(torch, mi, moe, shape, layers, T, algo)
+        U = r.experts_used()
+        total_ms, wall, gate_ms, down_ms = r.timed(steps, warmup)
+        Us = [U[i % len(U)] for i in range(steps)]
+        gate_bytes = sum(u * gate_bytes_per_expert for u in Us)
+        down_bytes = sum(u * down_bytes_per_expert for u in Us)
+        gate_s = sum(gate_ms) / 1e3
+        down_s = sum(down_ms) / 1e3
+        ms_step = total_ms / steps
+        return dict(T=T, steps=steps, ms_per_step=ms_step, tokens_per_s=T * steps / (total_ms / 1e3),
+                    wall_s=wall, U_mean=float(np.mean(U)), U_per_set=U,
+                    gateup_us=gate_s / steps * 1e6, down_us=down_s / steps * 1e6,
+                    gateup_GBps=gate_bytes / gate_s / 1e9, down_GBps=down_bytes / down_s / 1e9,
+                    ffn_GBps=(gate_bytes + down_bytes) / (gate_s + down_s) / 1e9,
+                    layer_GBps=(sum(Us) * per_expert + steps * router_bytes) / (total_ms / 1e3) / 1e9,
+                    gateup_bytes_per_launch=gate_bytes / steps)
+
+    log(f"[bench] T={args.tokens}: {args.warmup} warmup + {args.steps} timed steps")
+    main_run = measure(args.tokens, args.steps, args.warmup)
+    log(f"[bench] {main_run['tokens_per_s']:.0f} tokens/s, gate/up {main_run['gateup_GBps']:.0f} GB/s")
+
+    sweep = []
+    for tok in [int(t) for t in args.sweep.split(",") if t.strip()]:
+        if tok == args.tokens:
+            continue
+        m = measure(tok, max(args.steps // 2, 10), max(args.warmup // 2, 2))
+        log(f"[bench] sweep T={tok}: {m['tokens_per_s']:.0f} tokens/s, gate/up {m['gateup_GBps']:.0f} GB/s")
+        sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()})
+
+    kernel_src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc", "ffn_gemv.hip")
+    achieved = main_run["gateup_GBps"]
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(kernel_src),
+                    kernel="ffn_gateup (gate/up matvec + SwiGLU)",
+                    algorithmic_bytes_per_launch=round(main_run["gateup_bytes_per_launch"]),
+                    mean_launch_us=round(main_run["gateup_us"], 3))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one step")
+        cpu = cpu_baseline(mi, shape, layers[0], args.tokens)
+
+    result = {
+        "metric": "MoE-layer decode tokens/s + weight-stream HBM GB/s (% of MI355X peak)",
+        "value": round(main_run["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_run["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"A3B-style MoE decode layer, T={args.tokens} tokens: hidden 2048, 256 experts top-8 "
+                        f"(renormalised gates), intermediate 512, SwiGLU, 4-bit g128 weights "
+                        f"(fp16 scale+bias), bf16 activations, Zipf(1.1) routing, "
+                        f"{shape.n_resident}/256 resident, {args.layers} rotating weight sets",
+            "H": shape.H, "E": shape.E, "k": shape.k, "I": shape.I, "T": args.tokens, "bits": bits,
+            "group": 128, "weight_sets": args.layers, "algo": args.algo,
+            "parallelism": "none (one GPU)",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "weight_stream": {
+            "experts_used_mean": main_run["U_mean"],
+            "gateup_GBps": round(main_run["gateup_GBps"], 1),
+            "down_GBps": round(main_run["down_GBps"], 1),
+            "ffn_GBps": round(main_run["ffn_GBps"], 1),
+            "ffn_frac_of_peak": round(main_run["ffn_GBps"] / HBM_PEAK_GBPS, 4),
+            "layer_GBps_incl_router": round(main_run["layer_GBps"], 1),
+            "gateup_us": round(main_run["gateup_us"], 3),
+            "down_us": round(main_run["down_us"], 3),
+        },
+        "sweep": sweep,
+        "context_not_comparable": CONTEXT,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

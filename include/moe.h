@@ -1,0 +1,235 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the routed mixture-of-experts layer at decode
+ * time on one AMD Instinct MI355X (gfx950).
+ *
+ * One call per step of the layer.  For T tokens of hidden size H the layer
+ *   1. scores every expert with a linear router             (moe_route_topk)
+ *   2. keeps the k best experts per token, softmax gates     (moe_route_topk /
+ *      renormalised over the k picked                          moe_topk_from_logits)
+ *   3. looks up each picked expert in a resident-slot table  (moe_slot_lookup)
+ *      and lists the experts that miss it
+ *   4. groups the T*k (token, expert) pairs by expert        (moe_permute)
+ *   5. runs each expert's quantised FFN on its tokens:       (moe_expert_ffn_q4 /
+ *      gate/up matvec with fused group-wise dequant, SwiGLU,   moe_expert_ffn_q2)
+ *      down matvec
+ *   6. adds the gate-weighted expert outputs to the residual (moe_combine)
+ *
+ * Sources (pages cited by title and section):
+ *   - "12GB card runs a 68GB model: Betelgeuse engine measured at 22 tok/s",
+ *     MoE primer (router scores each expert from the hidden state, top-k run)
+ *     and "in-stream GPU doorbell" (hits resolved on the device, the host is
+ *     told only about misses);
+ *   - "Luce Spark: running a 35B MoE in 16GB", hot / warm / cold expert tiers;
+ *   - "Strata" (125B MoE at 100+ tok/s on one RTX 3090), sec. 2.2 (INT4,
+ *     groups of 128 with a scale and offset), sec. 2.3 (tokens that picked the
+ *     same expert share one fetch of its weights), sec. 3.4 (hand-written
+ *     INT4 decode GEMV, group-contiguous weights, experts in one buffer);
+ *   - "Flash-MoE: running a big model on a small laptop (translation)",
+ *     sec. 2 (weight = nibble*scale + bias, FMA form) and sec. 3 (4/2-bit
+ *     dequant matvec, fused SwiGLU, fused combine + residual).
+ *
+ * Conventions for every call
+ *   - All array pointers are DEVICE pointers unless a parameter says
+ *     otherwise.  The caller allocates and owns every buffer, including the
+ *     workspace; the library keeps no device memory between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls only enqueue work on `stream` and return; they never synchronise
+ *     and never allocate.
+ *   - Arguments are validated on the host before anything is enqueued: a
+ *     call that returns an error has enqueued nothing.  moe_last_error()
+ *     returns a thread-local description of the last failure.  Errors raised
+ *     by the GPU while the work runs surface at the caller's next
+ *     synchronisation.
+ *   - Limits: 0 <= T, T*k <= 65536; 1 <= E <= 1024; 1 <= k <= min(E, 32);
+ *     H and I multiples of 128 with 128 <= H <= 8192 and 128 <= I <= 16384;
+ *     group_size == 128.  Device pointers to weights and activations must be
+ *     16-byte aligned.
+ *   - Ids passed back in must come from these calls (or satisfy the same
+ *     invariants); kernels skip out-of-range ids rather than touch memory
+ *     outside the buffers, and the results for such ids are unspecified.
+ *
+ * Data layout
+ *   x, residual, out   bf16 bit patterns (uint16) [T][H], row-major
+ *   w_router           float32 [E][H]; router_bias float32 [E] or NULL
+ *   logits             float32 [T][E]
+ *   topk_ids           int32 [T][k], in rank order (best first)
+ *   topk_w             float32 [T][k], gates in the same order
+ *   pairs              p = t*k + j is the j-th pick of token t
+ *   expert weights     see moe_qweights; codes packed along K, groups of 128
+ *                      along K, one fp16 scale and one fp16 bias per group:
+ *                      w[n][k] = code[n][k] * scale[n][k/128] + bias[n][k/128]
+ *   y_rows             bf16 [T*k][H]: row r is the FFN output for the pair
+ *                      sorted_pairs[r] (rows in expert-grouped order)
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes returned by every call. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1   /* null pointer, bad size, misalignment */
+#define MOE_ERR_UNSUPPORTED 2   /* outside the limits above, unknown algo */
+#define MOE_ERR_WORKSPACE 3     /* workspace missing or too small */
+#define MOE_ERR_HIP 4           /* the HIP runtime rejected a launch */
+
+/* FFN algorithms (argument `algo` of the FFN calls). */
+#define MOE_ALGO_AUTO 0   /* choose per call from the shape */
+#define MOE_ALGO_GEMV 1   /* vector-ALU matvec, one pass over the weights per token tile */
+#define MOE_ALGO_MFMA 2   /* matrix-core tiles (bf16 MFMA with exact code operands) */
+
+/* Operations for moe_workspace_bytes. */
+#define MOE_OP_ROUTE 0
+#define MOE_OP_LOOKUP 1
+#define MOE_OP_PERMUTE 2
+#define MOE_OP_FFN 3
+#define MOE_OP_COMBINE 4
+
+typedef struct moe_dims {
+    int32_t T;           /* tokens in this call */
+    int32_t H;           /* hidden size */
+    int32_t I;           /* expert intermediate size */
+    int32_t E;           /* routed experts */
+    int32_t k;           /* experts per token */
+    int32_t group_size;  /* quantisation group along K; must be 128 */
+} moe_dims;
+
+/* Quantised expert weights, expert-major so that every expert's matrices sit
+ * in one buffer per matrix ("Strata" sec. 3.4).  Index m: 0 = gate [I][H],
+ * 1 = up [I][H], 2 = down [H][I], written [N][K] below.
+ *   q[m]      uint8 [E][N][K*bits/8].  4-bit: byte j of a row holds k = 2j in
+ *             its low nibble and k = 2j+1 in its high nibble.  2-bit: bits
+ *             2i..2i+1 of byte j hold k = 4j + i.
+ *   scale[m]  fp16 bit patterns [E][N][K/128]
+ *   bias[m]   fp16 bit patterns [E][N][K/128]
+ * The struct itself is a host object holding device pointers; it is read
+ * during the call only. */
+typedef struct moe_qweights {
+    const uint8_t* q[3];
+    const uint16_t* scale[3];
+    const uint16_t* bias[3];
+} moe_qweights;
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* Thread-local description of this thread's last failed call ("" if none). */
+const char* moe_last_error(void);
+
+/* Device workspace that `op` needs for these dims (host-only, no GPU work).
+ * Only MOE_OP_FFN needs any: float32 [T*k][I] for the SwiGLU activations
+ * plus a small tail; the others report 0.  bits in {2, 4}. */
+int moe_workspace_bytes(const moe_dims* dims, int op, int bits, int algo, size_t* bytes);
+
+/* Router logits and top-k (steps 1-2; Betelgeuse page, MoE primer).
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h] (+ router_bias[e]),
+ *                  float32 accumulation
+ *   topk_ids[t][0..k)  the k experts with the largest logits, best first;
+ *                  equal logits (also -0 vs +0) rank the lower expert id
+ *                  first; NaN ranks below every number
+ *   topk_w[t][j]   renormalize != 0: exp(L_j - L_0) / sum_{j'<k} exp(L_j' - L_0)
+ *                  renormalize == 0: softmax over all E logits at the pick
+ * logits is a required [T][E] output (it is also the input of the top-k). */
+int moe_route_topk(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                   const float* router_bias, int renormalize, float* logits,
+                   int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Step 2 alone, from caller-provided float32 logits [T][E]; same rules. */
+int moe_topk_from_logits(const moe_dims* dims, const float* logits, int renormalize,
+                         int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Resident-slot lookup (step 3; Betelgeuse page, "in-stream GPU doorbell";
+ * Luce Spark page, hot/warm/cold tiers).
+ *   slot_of_expert int32 [E]: slot holding the expert, or any value outside
+ *                  [0, n_slots) when it is not resident
+ *   pair_slot      int32 [T*k] out: the pair's slot, or -1 on a miss
+ *   miss_experts   int32 [E] out: the distinct missing experts, ascending, in
+ *                  entries [0, *n_miss); the rest is left untouched
+ *   n_miss         int32 [1] out
+ *   host_doorbell  NULL, or a device-visible pointer to pinned host memory
+ *                  (hipHostMalloc): set to n_miss only when n_miss > 0,
+ *                  never written otherwise -- the host clears it
+ *   last_use       NULL, or uint32 [n_slots]: last_use[slot] = step for
+ *                  every slot hit in this call */
+int moe_slot_lookup(const moe_dims* dims, const int32_t* topk_ids, const int32_t* slot_of_expert,
+                    int32_t n_slots, int32_t* pair_slot, int32_t* miss_experts, int32_t* n_miss,
+                    int32_t* host_doorbell, uint32_t* last_use, uint32_t step, void* stream);
+
+/* Group pairs by expert (step 4; "Strata" sec. 2.3).  A stable counting sort.
+ *   expert_counts  int32 [E]     pairs per expert
+ *   expert_offsets int32 [E+1]   exclusive prefix sum, offsets[E] = T*k
+ *   sorted_pairs   int32 [T*k]   pairs grouped by expert, ascending p within
+ *                                an expert
+ *   pair_to_row    int32 [T*k]   inverse: sorted_pairs[pair_to_row[p]] == p
+ *   active_experts int32 [E]     experts with count > 0, ascending, first
+ *                                *n_active entries written
+ *   n_active       int32 [1] */
+int moe_permute(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
+                int32_t* active_experts, int32_t* n_active, void* stream);
+
+/* Quantised expert FFN (step 5), 4-bit codes.  For every sorted row r with
+ * pair p = sorted_pairs[r], token t = p / k and expert e (the expert whose
+ * [offsets[e], offsets[e+1]) holds r):
+ *   a_i = sum_k Wg[e][i][k] x[t][k],  u_i = sum_k Wu[e][i][k] x[t][k]
+ *   h_i = silu(a_i) * u_i                            (float32)
+ *   y_rows[r][n] = bf16( sum_i Wd[e][n][i] h_i )     (round to nearest even)
+ * Each expert's weights are read once per call for all of its tokens.
+ * Inputs come from moe_permute; n_active is read on the device, so the call
+ * never waits for routing results on the host.
+ * workspace: at least moe_workspace_bytes(dims, MOE_OP_FFN, 4, algo), 256-byte
+ * aligned.  algo: MOE_ALGO_*. */
+int moe_expert_ffn_q4(const moe_dims* dims, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* expert_counts, const int32_t* expert_offsets,
+                      const int32_t* active_experts, const int32_t* n_active,
+                      const moe_qweights* weights, uint16_t* y_rows, int algo,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as moe_expert_ffn_q4 with 2-bit codes (Flash-MoE page, sec. 3). */
+int moe_expert_ffn_q2(const moe_dims* dims, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* expert_counts, const int32_t* expert_offsets,
+                      const int32_t* active_experts, const int32_t* n_active,
+                      const moe_qweights* weights, uint16_t* y_rows, int algo,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 5 in two halves, for callers that want the SwiGLU activations or time
+ * the halves apart.  bits in {2, 4}; the other arguments are as above.
+ *   moe_expert_gateup: h[r][i] = silu(a_i) * u_i as float32 [T*k][I]
+ *                      (the scope row "gate/up matvec + SwiGLU");
+ *   moe_expert_down:   y_rows[r][n] = bf16(sum_i Wd[e][n][i] h[r][i])
+ *                      (the scope row "down matvec").
+ * moe_expert_ffn_q4/q2 == moe_expert_gateup then moe_expert_down with h in
+ * the workspace. */
+int moe_expert_gateup(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* expert_counts, const int32_t* expert_offsets,
+                      const int32_t* active_experts, const int32_t* n_active,
+                      const moe_qweights* weights, int algo, float* h, void* stream);
+
+int moe_expert_down(const moe_dims* dims, int bits, const float* h, const int32_t* expert_counts,
+                    const int32_t* expert_offsets, const int32_t* active_experts,
+                    const int32_t* n_active, const moe_qweights* weights, int algo,
+                    uint16_t* y_rows, void* stream);
+
+/* Combine + residual (step 6; Flash-MoE page, sec. 3):
+ *   acc = residual[t][n];  for j = 0..k-1 in order:
+ *       acc = fmaf(topk_w[t][j], y_rows[pair_to_row[t*k+j]][n], acc)
+ *   out[t][n] = bf16(acc)   (float32 accumulation, round to nearest even)
+ * out may be the same buffer as residual. */
+int moe_combine(const moe_dims* dims, const uint16_t* y_rows, const int32_t* pair_to_row,
+                const float* topk_w, const uint16_t* residual, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

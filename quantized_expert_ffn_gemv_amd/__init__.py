@@ -1,0 +1,218 @@
+"""Routed MoE decode layer for AMD Instinct MI355X (gfx950).
+
+Python binding of libmoe.so, the C ABI declared in include/moe.h.  Each
+function here has the name of a C entry point without the ``moe_`` prefix and
+only marshals arguments: tensors become device pointers, the current torch
+stream becomes the HIP stream, and a non-zero status becomes a ``MoeError``.
+Every step of the layer runs in the library's HIP kernels; there is no
+Python or CPU fallback, and a missing library raises at first use.
+
+PyTorch supplies device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA = 0, 1, 2
+OP_ROUTE, OP_LOOKUP, OP_PERMUTE, OP_FFN, OP_COMBINE = 0, 1, 2, 3, 4
+
+# entry points declared in include/moe.h
+EXPORTS = (
+    "moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
+    "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute",
+    "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_combine",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class QWeightsC(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p * 3), ("scale", ctypes.c_void_p * 3), ("bias", ctypes.c_void_p * 3)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m quantized_expert_ffn_gemv_amd._build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    Dp, Wp = ctypes.POINTER(Dims), ctypes.POINTER(QWeightsC)
+    L.moe_abi_version.argtypes = []; L.moe_abi_version.restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]; L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []; L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_workspace_bytes.argtypes = [Dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz)]
+    L.moe_route_topk.argtypes = [Dp, P, P, P, ctypes.c_int, P, P, P, P]
+    L.moe_topk_from_logits.argtypes = [Dp, P, ctypes.c_int, P, P, P]
+    L.moe_slot_lookup.argtypes = [Dp, P, P, i32, P, P, P, P, P, u32, P]
+    L.moe_permute.argtypes = [Dp, P, P, P, P, P, P, P, P]
+    for name in ("moe_expert_ffn_q4", "moe_expert_ffn_q2"):
+        getattr(L, name).argtypes = [Dp, P, P, P, P, P, P, Wp, P, ctypes.c_int, P, sz, P]
+    L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, P, P, P, Wp, ctypes.c_int, P, P]
+    L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, P, P, P, Wp, ctypes.c_int, P, P]
+    L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
+    for name in EXPORTS[3:]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise MoeError(status, last_error() or status_string(status))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dims(T: int, H: int, I: int, E: int, k: int, group_size: int = 128) -> Dims:
+    return Dims(T, H, I, E, k, group_size)
+
+
+@dataclass
+class QWeights:
+    """Device tensors of the quantised expert weights (layout in include/moe.h)."""
+    bits: int
+    q: Sequence          # [gate, up, down] uint8 tensors [E, N, K*bits/8]
+    scale: Sequence      # fp16 bit patterns (int16/uint16 tensors) [E, N, K/128]
+    bias: Sequence
+
+    def c_struct(self) -> QWeightsC:
+        w = QWeightsC()
+        for m in range(3):
+            w.q[m] = _ptr(self.q[m])
+            w.scale[m] = _ptr(self.scale[m])
+            w.bias[m] = _ptr(self.bias[m])
+        return w
+
+
+def workspace_bytes(d: Dims, op: int, bits: int = 4, algo: int = ALGO_AUTO) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_bytes(ctypes.byref(d), op, bits, algo, ctypes.byref(out)))
+    return int(out.value)
+
+
+def route_topk(d: Dims, x, w_router, router_bias, renormalize: bool, logits, topk_ids, topk_w, stream=None):
+    _check(lib().moe_route_topk(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                int(bool(renormalize)), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                _stream(stream)))
+
+
+def topk_from_logits(d: Dims, logits, renormalize: bool, topk_ids, topk_w, stream=None):
+    _check(lib().moe_topk_from_logits(ctypes.byref(d), _ptr(logits), int(bool(renormalize)),
+                                      _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+
+
+def slot_lookup(d: Dims, topk_ids, slot_of_expert, n_slots: int, pair_slot, miss_experts, n_miss,
+                host_doorbell=None, last_use=None, step: int = 0, stream=None):
+    _check(lib().moe_slot_lookup(ctypes.byref(d), _ptr(topk_ids), _ptr(slot_of_expert), int(n_slots),
+                                 _ptr(pair_slot), _ptr(miss_experts), _ptr(n_miss), _ptr(host_doorbell),
+                                 _ptr(last_use), int(step) & 0xFFFFFFFF, _stream(stream)))
+
+
+def permute(d: Dims, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair_to_row,
+            active_experts, n_active, stream=None):
+    _check(lib().moe_permute(ctypes.byref(d), _ptr(topk_ids), _ptr(expert_counts), _ptr(expert_offsets),
+                             _ptr(sorted_pairs), _ptr(pair_to_row), _ptr(active_experts), _ptr(n_active),
+                             _stream(stream)))
+
+
+def _ffn(fn, d, x, sorted_pairs, counts, offsets, active, n_active, weights: QWeights, y_rows,
+         algo, workspace, workspace_bytes_, stream):
+    w = weights.c_struct()
+    nbytes = workspace_bytes_ if workspace_bytes_ is not None else (
+        0 if workspace is None else workspace.numel() * workspace.element_size())
+    _check(fn(ctypes.byref(d), _ptr(x), _ptr(sorted_pairs), _ptr(counts), _ptr(offsets), _ptr(active),
+              _ptr(n_active), ctypes.byref(w), _ptr(y_rows), int(algo), _ptr(workspace), nbytes,
+              _stream(stream)))
+
+
+def expert_ffn_q4(d: Dims, x, sorted_pairs, expert_counts, expert_offsets, active_experts, n_active,
+                  weights: QWeights, y_rows, algo: int = ALGO_AUTO, workspace=None,
+                  workspace_bytes_: Optional[int] = None, stream=None):
+    _ffn(lib().moe_expert_ffn_q4, d, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
+         n_active, weights, y_rows, algo, workspace, workspace_bytes_, stream)
+
+
+def expert_ffn_q2(d: Dims, x, sorted_pairs, expert_counts, expert_offsets, active_experts, n_active,
+                  weights: QWeights, y_rows, algo: int = ALGO_AUTO, workspace=None,
+                  workspace_bytes_: Optional[int] = None, stream=None):
+    _ffn(lib().moe_expert_ffn_q2, d, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
+         n_active, weights, y_rows, algo, workspace, workspace_bytes_, stream)
+
+
+def expert_gateup(d: Dims, bits: int, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
+                  n_active, weights: QWeights, h, algo: int = ALGO_AUTO, stream=None):
+    w = weights.c_struct()
+    _check(lib().moe_expert_gateup(ctypes.byref(d), int(bits), _ptr(x), _ptr(sorted_pairs), _ptr(expert_counts),
+                                   _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), ctypes.byref(w),
+                                   int(algo), _ptr(h), _stream(stream)))
+
+
+def expert_down(d: Dims, bits: int, h, expert_counts, expert_offsets, active_experts, n_active,
+                weights: QWeights, y_rows, algo: int = ALGO_AUTO, stream=None):
+    w = weights.c_struct()
+    _check(lib().moe_expert_down(ctypes.byref(d), int(bits), _ptr(h), _ptr(expert_counts), _ptr(expert_offsets),
+                                 _ptr(active_experts), _ptr(n_active), ctypes.byref(w), int(algo), _ptr(y_rows),
+                                 _stream(stream)))
+
+
+def combine(d: Dims, y_rows, pair_to_row, topk_w, residual, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(d), _ptr(y_rows), _ptr(pair_to_row), _ptr(topk_w),
+                             _ptr(residual), _ptr(out), _stream(stream)))
+
+
+from .layer import LayerBuffers, layer_forward  # noqa: E402  (orchestration of the calls above)
+
+__all__ = [
+    "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
+    "workspace_bytes", "route_topk", "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
+    "expert_ffn_q2", "expert_gateup", "expert_down", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
+    "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
+]

@@ -1,0 +1,303 @@
+// C ABI of libmoe.so: argument validation, status codes and dispatch to the
+// kernel launchers.  Every check runs on the host before anything is
+// enqueued, so a call that fails leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+#include "moe.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE_PTR(p, align)                                                            \
+    do {                                                                                 \
+        if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);  \
+        if (!aligned((p), (align)))                                                      \
+            return fail(MOE_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, #p,    \
+                        (int)(align));                                                   \
+    } while (0)
+
+// Checks shared by every call; `need_hi` also checks H/I (FFN, route, combine).
+int check_dims(const char* fn, const moe_dims* d, bool need_h, bool need_i) {
+    if (d == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: dims is NULL", fn);
+    if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d is negative", fn, d->T);
+    if (d->E < 1 || d->E > 1024)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d outside [1, 1024]", fn, d->E);
+    if (d->k < 1 || d->k > d->E || d->k > 32)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: k = %d outside [1, min(E, 32)]", fn, d->k);
+    if ((long long)d->T * d->k > 65536)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld exceeds 65536", fn, (long long)d->T * d->k);
+    if (d->group_size != 128)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: group_size = %d (only 128 is supported)", fn, d->group_size);
+    if (need_h && (d->H < 128 || d->H > 8192 || d->H % 128 != 0))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: H = %d must be a multiple of 128 in [128, 8192]", fn, d->H);
+    if (need_i && (d->I < 128 || d->I > 16384 || d->I % 128 != 0))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: I = %d must be a multiple of 128 in [128, 16384]", fn, d->I);
+    return MOE_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Checks shared by the FFN calls.  `mats` lists the weight matrices used.
+int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* counts,
+                   const int32_t* offsets, const int32_t* active, const int32_t* n_active,
+                   const moe_qweights* w, int algo, int m_begin, int m_end) {
+    int st = check_dims(fn, d, true, true);
+    if (st) return st;
+    if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED, "%s: bits = %d (2 or 4)", fn, bits);
+    if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: weights is NULL", fn);
+    if (algo != MOE_ALGO_AUTO && algo != MOE_ALGO_GEMV && algo != MOE_ALGO_MFMA)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: unknown algo %d", fn, algo);
+    if (algo == MOE_ALGO_MFMA)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: algo MFMA is not available in this build", fn);
+    if (d->T == 0) return MOE_OK;
+    REQUIRE_PTR(counts, 4);
+    REQUIRE_PTR(offsets, 4);
+    REQUIRE_PTR(active, 4);
+    REQUIRE_PTR(n_active, 4);
+    for (int m = m_begin; m < m_end; ++m) {
+        if (!w->q[m] || !w->scale[m] || !w->bias[m])
+            return fail(MOE_ERR_INVALID_ARG, "%s: weights matrix %d has a NULL pointer", fn, m);
+        if (!aligned(w->q[m], 16))
+            return fail(MOE_ERR_INVALID_ARG, "%s: weights.q[%d] is not 16-byte aligned", fn, m);
+        if (!aligned(w->scale[m], 2) || !aligned(w->bias[m], 2))
+            return fail(MOE_ERR_INVALID_ARG, "%s: weights.scale/bias[%d] misaligned", fn, m);
+    }
+    return MOE_OK;
+}
+
+moe::FfnArgs ffn_args(const moe_dims* d, int bits, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
+                      const int32_t* n_active, const moe_qweights* w, float* h, uint16_t* y) {
+    moe::FfnArgs a{};
+    a.d = *d;
+    a.bits = bits;
+    a.x = x;
+    a.sorted_pairs = sorted_pairs;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.active = active;
+    a.n_active = n_active;
+    a.w = *w;
+    a.y = y;
+    a.h = h;
+    return a;
+}
+
+int ffn_common(const char* fn, int bits, const moe_dims* d, const uint16_t* x,
+               const int32_t* sorted_pairs, const int32_t* counts, const int32_t* offsets,
+               const int32_t* active, const int32_t* n_active, const moe_qweights* w, uint16_t* y,
+               int algo, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 0, 3);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(sorted_pairs, 4);
+    REQUIRE_PTR(y, 16);
+    const size_t need = moe::ffn_workspace_bytes(*d, bits, algo);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+    moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w,
+                              static_cast<float*>(ws), y);
+    st = moe::launch_gateup_gemv(a, as_stream(stream));
+    if (!st) st = moe::launch_down_gemv(a, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+int moe_workspace_bytes(const moe_dims* d, int op, int bits, int algo, size_t* bytes) {
+    const char* fn = "moe_workspace_bytes";
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+    if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED, "%s: bits = %d", fn, bits);
+    if (op < MOE_OP_ROUTE || op > MOE_OP_COMBINE) return fail(MOE_ERR_INVALID_ARG, "%s: op = %d", fn, op);
+    int st = check_dims(fn, d, op == MOE_OP_FFN, op == MOE_OP_FFN);
+    if (st) return st;
+    *bytes = (op == MOE_OP_FFN) ? moe::ffn_workspace_bytes(*d, bits, algo) : 0;
+    return ok();
+}
+
+int moe_route_topk(const moe_dims* d, const uint16_t* x, const float* w_router,
+                   const float* router_bias, int renormalize, float* logits, int32_t* topk_ids,
+                   float* topk_w, void* stream) {
+    const char* fn = "moe_route_topk";
+    int st = check_dims(fn, d, true, false);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(w_router, 16);
+    if (router_bias && !aligned(router_bias, 4))
+        return fail(MOE_ERR_INVALID_ARG, "%s: router_bias misaligned", fn);
+    REQUIRE_PTR(logits, 4);
+    REQUIRE_PTR(topk_ids, 4);
+    REQUIRE_PTR(topk_w, 4);
+    st = moe::launch_router_logits(*d, x, w_router, router_bias, logits, as_stream(stream));
+    if (!st) st = moe::launch_topk(*d, logits, renormalize, topk_ids, topk_w, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_topk_from_logits(const moe_dims* d, const float* logits, int renormalize, int32_t* topk_ids,
+                         float* topk_w, void* stream) {
+    const char* fn = "moe_topk_from_logits";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(logits, 4);
+    REQUIRE_PTR(topk_ids, 4);
+    REQUIRE_PTR(topk_w, 4);
+    st = moe::launch_topk(*d, logits, renormalize, topk_ids, topk_w, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_slot_lookup(const moe_dims* d, const int32_t* topk_ids, const int32_t* slot_of_expert,
+                    int32_t n_slots, int32_t* pair_slot, int32_t* miss_experts, int32_t* n_miss,
+                    int32_t* host_doorbell, uint32_t* last_use, uint32_t step, void* stream) {
+    const char* fn = "moe_slot_lookup";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    if (n_slots < 0) return fail(MOE_ERR_INVALID_ARG, "%s: n_slots = %d is negative", fn, n_slots);
+    REQUIRE_PTR(slot_of_expert, 4);
+    REQUIRE_PTR(miss_experts, 4);
+    REQUIRE_PTR(n_miss, 4);
+    if (d->T > 0) {
+        REQUIRE_PTR(topk_ids, 4);
+        REQUIRE_PTR(pair_slot, 4);
+    }
+    if (host_doorbell && !aligned(host_doorbell, 4))
+        return fail(MOE_ERR_INVALID_ARG, "%s: host_doorbell misaligned", fn);
+    if (last_use && !aligned(last_use, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: last_use misaligned", fn);
+    st = moe::launch_slot_lookup(*d, topk_ids, slot_of_expert, n_slots, pair_slot, miss_experts,
+                                 n_miss, host_doorbell, last_use, step, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_permute(const moe_dims* d, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
+                void* stream) {
+    const char* fn = "moe_permute";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    REQUIRE_PTR(counts, 4);
+    REQUIRE_PTR(offsets, 4);
+    REQUIRE_PTR(active, 4);
+    REQUIRE_PTR(n_active, 4);
+    if (d->T > 0) {
+        REQUIRE_PTR(topk_ids, 4);
+        REQUIRE_PTR(sorted_pairs, 4);
+        REQUIRE_PTR(pair_to_row, 4);
+    }
+    st = moe::launch_permute(*d, topk_ids, counts, offsets, sorted_pairs, pair_to_row, active,
+                             n_active, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_expert_ffn_q4(const moe_dims* d, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
+                      const int32_t* n_active, const moe_qweights* w, uint16_t* y, int algo,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common("moe_expert_ffn_q4", 4, d, x, sorted_pairs, counts, offsets, active, n_active,
+                      w, y, algo, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_q2(const moe_dims* d, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
+                      const int32_t* n_active, const moe_qweights* w, uint16_t* y, int algo,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return ffn_common("moe_expert_ffn_q2", 2, d, x, sorted_pairs, counts, offsets, active, n_active,
+                      w, y, algo, ws, ws_bytes, stream);
+}
+
+int moe_expert_gateup(const moe_dims* d, int bits, const uint16_t* x, const int32_t* sorted_pairs,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
+                      const int32_t* n_active, const moe_qweights* w, int algo, float* h,
+                      void* stream) {
+    const char* fn = "moe_expert_gateup";
+    int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 0, 2);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(sorted_pairs, 4);
+    REQUIRE_PTR(h, 16);
+    moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w, h, nullptr);
+    st = moe::launch_gateup_gemv(a, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_expert_down(const moe_dims* d, int bits, const float* h, const int32_t* counts,
+                    const int32_t* offsets, const int32_t* active, const int32_t* n_active,
+                    const moe_qweights* w, int algo, uint16_t* y, void* stream) {
+    const char* fn = "moe_expert_down";
+    int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 2, 3);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(h, 16);
+    REQUIRE_PTR(y, 16);
+    moe::FfnArgs a = ffn_args(d, bits, nullptr, nullptr, counts, offsets, active, n_active, w,
+                              const_cast<float*>(h), y);
+    st = moe::launch_down_gemv(a, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* pair_to_row,
+                const float* topk_w, const uint16_t* residual, uint16_t* out, void* stream) {
+    const char* fn = "moe_combine";
+    int st = check_dims(fn, d, true, false);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(y_rows, 16);
+    REQUIRE_PTR(pair_to_row, 4);
+    REQUIRE_PTR(topk_w, 4);
+    REQUIRE_PTR(residual, 16);
+    REQUIRE_PTR(out, 16);
+    st = moe::launch_combine(*d, y_rows, pair_to_row, topk_w, residual, out, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+}  // extern "C"

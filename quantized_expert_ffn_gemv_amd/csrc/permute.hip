@@ -1,0 +1,203 @@
+// Resident-slot lookup and grouping of (token, expert) pairs by expert.
+//
+// Slot lookup follows the Betelgeuse page ("in-stream GPU doorbell"): the
+// device resolves hits against the resident table and signals the host only
+// on a miss.  Grouping follows the "Strata" page, sec. 2.3: tokens that picked
+// the same expert are served by one pass over its weights.
+//
+// Both run as a single workgroup: at decode sizes they touch a few KB, so one
+// CU finishes them in a few microseconds without any grid-wide sync, and the
+// integer results are deterministic by construction.
+#include "common.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive scan of one flag/count per thread over the workgroup (blockDim =
+// 1024, at most 16 waves).  Returns this thread's exclusive prefix; *total gets
+// the sum.  `wsum` is LDS scratch of 16 ints.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    int incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        int s = wsum[w];
+        base += (w < wid) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+constexpr int kMaxE = 1024;
+
+// ---------------------------------------------------------------- lookup
+__global__ __launch_bounds__(1024) void slot_lookup_kernel(const int32_t* __restrict__ ids, int P,
+                                                           int E, const int32_t* __restrict__ table,
+                                                           int n_slots, int32_t* __restrict__ pair_slot,
+                                                           int32_t* __restrict__ miss,
+                                                           int32_t* __restrict__ n_miss,
+                                                           int32_t* doorbell,
+                                                           uint32_t* __restrict__ last_use,
+                                                           uint32_t step) {
+    __shared__ int flag[kMaxE];
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) flag[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int e = ids[p];
+        if (e < 0 || e >= E) {
+            pair_slot[p] = -1;
+            continue;
+        }
+        const int s = table[e];
+        const bool hit = (s >= 0 && s < n_slots);
+        pair_slot[p] = hit ? s : -1;
+        if (!hit) flag[e] = 1;
+        else if (last_use) last_use[s] = step;
+    }
+    __syncthreads();
+    int count = 0;
+    for (int e0 = 0; e0 < E; e0 += blockDim.x) {
+        const int e = e0 + tid;
+        const int f = (e < E) ? flag[e] : 0;
+        int total;
+        const int pos = block_exclusive_scan(f, wsum, &total);
+        if (f) miss[count + pos] = e;
+        count += total;
+    }
+    if (tid == 0) {
+        *n_miss = count;
+        if (doorbell && count > 0) {
+            __hip_atomic_store(doorbell, count, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
+
+int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* table, int32_t n_slots,
+                       int32_t* pair_slot, int32_t* miss, int32_t* n_miss, int32_t* doorbell,
+                       uint32_t* last_use, uint32_t step, hipStream_t s) {
+    hipLaunchKernelGGL(slot_lookup_kernel, dim3(1), dim3(1024), 0, s, ids, d.T * d.k, d.E, table,
+                       n_slots, pair_slot, miss, n_miss, doorbell, last_use, step);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// --------------------------------------------------------------- permute
+// Stable counting sort of the P pairs by expert with 8 waves:
+//   1. wave w counts the experts of its contiguous pair range into cnt[w][e];
+//   2. one pass over experts: totals, a single exclusive scan (offsets), and
+//      per-(wave, expert) starting rows base[w][e] = offsets[e] + earlier waves;
+//   3. each wave walks its range in order, 64 pairs at a time; lanes holding
+//      the same expert find each other with ballots over the id bits, take
+//      rank = earlier equal lanes, and the last of them advances base[w][e].
+// Pairs of one expert therefore keep ascending p order.
+constexpr int kPermWaves = 8;
+
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted_pairs,
+                                                       int32_t* __restrict__ pair_to_row,
+                                                       int32_t* __restrict__ active,
+                                                       int32_t* __restrict__ n_active) {
+    __shared__ int cnt[kPermWaves][kMaxE];
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int chunk = (P + kPermWaves - 1) / kPermWaves;
+
+    for (int i = tid; i < kPermWaves * E; i += blockDim.x) cnt[i / E][i % E] = 0;
+    __syncthreads();
+    if (wid < kPermWaves) {
+        const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
+        for (int p = p0 + lane; p < p1; p += 64) {
+            const int e = ids[p];
+            if (e >= 0 && e < E) atomicAdd(&cnt[wid][e], 1);
+        }
+    }
+    __syncthreads();
+
+    int running = 0, nact = 0;
+    for (int e0 = 0; e0 < E; e0 += blockDim.x) {
+        const int e = e0 + tid;
+        int tot = 0;
+        if (e < E)
+#pragma unroll
+            for (int w = 0; w < kPermWaves; ++w) tot += cnt[w][e];
+        int sum, nsum;
+        const int excl = block_exclusive_scan(tot, wsum, &sum);
+        const int apos = block_exclusive_scan(tot > 0 ? 1 : 0, wsum, &nsum);
+        if (e < E) {
+            counts[e] = tot;
+            offsets[e] = running + excl;
+            if (tot > 0) active[nact + apos] = e;
+            int b = running + excl;
+#pragma unroll
+            for (int w = 0; w < kPermWaves; ++w) {
+                const int c = cnt[w][e];
+                cnt[w][e] = b;
+                b += c;
+            }
+        }
+        running += sum;
+        nact += nsum;
+    }
+    if (tid == 0) {
+        offsets[E] = running;
+        *n_active = nact;
+    }
+    __syncthreads();
+
+    if (wid < kPermWaves) {
+        const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
+        for (int pb = p0; pb < p1; pb += 64) {
+            const int p = pb + lane;
+            const bool live = p < p1;
+            int e = live ? ids[p] : -1;
+            const bool ok = live && e >= 0 && e < E;
+            if (!ok) e = -1;
+            // lanes with the same expert id: AND over the id's bits of the
+            // ballot (bit set) or its complement (bit clear)
+            uint64_t same = __ballot(ok);
+#pragma unroll
+            for (int b = 0; b < 10; ++b) {
+                const uint64_t bal = __ballot(ok && ((e >> b) & 1));
+                same &= ((e >> b) & 1) ? bal : ~bal;
+            }
+            const int rank = __popcll(same & lanemask_lt());
+            const int n_same = __popcll(same);
+            int row = 0;
+            if (ok) row = cnt[wid][e] + rank;
+            // all reads of this step happen before the last lane's update
+            __builtin_amdgcn_wave_barrier();
+            if (ok) {
+                sorted_pairs[row] = p;
+                pair_to_row[p] = row;
+                if (rank == n_same - 1) cnt[wid][e] = row + 1;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
+                   hipStream_t s) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, d.T * d.k, d.E, counts,
+                       offsets, sorted_pairs, pair_to_row, active, n_active);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

@@ -1,0 +1,236 @@
+// Router logits and top-k gating (Betelgeuse page, MoE primer: the router
+// scores every expert from the token's hidden state and only the k best run;
+// gates are a softmax renormalised over the k picked).
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ router, small T
+// Decode shapes: T <= 64.  One wave per EB experts streams their float32 router
+// rows once (16-byte loads, 1 KB per wave per step) and applies them to a tile
+// of TT tokens whose bf16 activations come through L1/L2.  Partial sums are
+// reduced across the wave with xor shuffles.
+template <int EB, int TT>
+__global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int T, int H,
+                                                          int E) {
+    const int lane = threadIdx.x;
+    const int e0 = blockIdx.x * EB;
+    for (int t0 = 0; t0 < T; t0 += TT) {
+        float acc[EB][TT];
+#pragma unroll
+        for (int a = 0; a < EB; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b) acc[a][b] = 0.f;
+        for (int k = lane * 4; k < H; k += 256) {
+            float4 wv[EB];
+#pragma unroll
+            for (int a = 0; a < EB; ++a)
+                wv[a] = (e0 + a < E) ? *reinterpret_cast<const float4*>(w + (size_t)(e0 + a) * H + k)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int b = 0; b < TT; ++b) {
+                if (t0 + b < T) {
+                    uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + b) * H + k);
+                    float x0 = bf16_bits_to_f32(xv.x & 0xFFFFu), x1 = bf16_bits_to_f32(xv.x >> 16);
+                    float x2 = bf16_bits_to_f32(xv.y & 0xFFFFu), x3 = bf16_bits_to_f32(xv.y >> 16);
+#pragma unroll
+                    for (int a = 0; a < EB; ++a) {
+                        float s = acc[a][b];
+                        s = fmaf(x0, wv[a].x, s);
+                        s = fmaf(x1, wv[a].y, s);
+                        s = fmaf(x2, wv[a].z, s);
+                        s = fmaf(x3, wv[a].w, s);
+                        acc[a][b] = s;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < EB; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b) {
+                float v = wave_sum_xor(acc[a][b], kWave);
+                if (lane == 0 && e0 + a < E && t0 + b < T)
+                    logits[(size_t)(t0 + b) * E + e0 + a] = v + (bias ? bias[e0 + a] : 0.f);
+            }
+    }
+}
+
+// ------------------------------------------------------------ router, large T
+// Prefill shapes: a 64x64 (tokens x experts) tile per 256-thread workgroup,
+// K staged through LDS 32 at a time, 4x4 outputs per thread, float32 FMA.
+constexpr int RT_BM = 64, RT_BN = 64, RT_BK = 32;
+
+__global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ logits, int T, int H,
+                                                            int E) {
+    __shared__ float xs[RT_BK][RT_BM + 4];
+    __shared__ float ws[RT_BK][RT_BN + 4];
+    const int tid = threadIdx.x;
+    const int m0 = blockIdx.x * RT_BM;   // tokens
+    const int n0 = blockIdx.y * RT_BN;   // experts
+    const int ty = tid / 16, tx = tid % 16;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < H; k0 += RT_BK) {
+        // x tile: 64 tokens x 32 k bf16 = 256 x 8 values
+        {
+            int row = tid / 4, col = (tid % 4) * 8;
+            int t = m0 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (t < T) v = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + col);
+            uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xs[col + 2 * i][row] = bf16_bits_to_f32(wds[i] & 0xFFFFu);
+                xs[col + 2 * i + 1][row] = bf16_bits_to_f32(wds[i] >> 16);
+            }
+        }
+        // w tile: 64 experts x 32 k float = 256 x 8 values
+        {
+            int row = tid / 4, col = (tid % 4) * 8;
+            int e = n0 + row;
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+            if (e < E) {
+                a = *reinterpret_cast<const float4*>(w + (size_t)e * H + k0 + col);
+                b = *reinterpret_cast<const float4*>(w + (size_t)e * H + k0 + col + 4);
+            }
+            ws[col + 0][row] = a.x; ws[col + 1][row] = a.y; ws[col + 2][row] = a.z; ws[col + 3][row] = a.w;
+            ws[col + 4][row] = b.x; ws[col + 5][row] = b.y; ws[col + 6][row] = b.z; ws[col + 7][row] = b.w;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int kk = 0; kk < RT_BK; ++kk) {
+            float4 av = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
+            float4 bv = *reinterpret_cast<const float4*>(&ws[kk][tx * 4]);
+            float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int t = m0 + ty * 4 + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int e = n0 + tx * 4 + j;
+            if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+        }
+    }
+}
+
+int launch_router_logits(const moe_dims& d, const uint16_t* x, const float* w, const float* bias,
+                         float* logits, hipStream_t s) {
+    if (d.T == 0) return MOE_OK;
+    if (d.T <= 64) {
+        constexpr int EB = 2, TT = 8;
+        dim3 grid((d.E + EB - 1) / EB);
+        hipLaunchKernelGGL((router_gemv_kernel<EB, TT>), grid, dim3(64), 0, s, x, w, bias, logits,
+                           d.T, d.H, d.E);
+    } else {
+        dim3 grid((d.T + RT_BM - 1) / RT_BM, (d.E + RT_BN - 1) / RT_BN);
+        hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H,
+                           d.E);
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ------------------------------------------------------------------- top-k
+// One wave per token.  Each candidate gets a 64-bit key whose unsigned order
+// is the ranking: class (removed < NaN < number), then the value (with -0
+// folded onto +0), then the lower expert id.  k rounds of a wave-wide max
+// pick the experts in rank order; lane j keeps the j-th pick.
+__device__ __forceinline__ uint64_t rank_key(float v, int id) {
+    const uint64_t idpart = (uint64_t)(0xFFFFFu - (uint32_t)id);
+    if (v != v) return (1ull << 62) | idpart;
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;   // -0 -> +0: equal values tie
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (2ull << 62) | ((uint64_t)ord << 20) | idpart;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                    int k, int renorm, int32_t* __restrict__ ids,
+                                                    float* __restrict__ gates) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* L = logits + (size_t)t * E;
+    float v[PER];
+    uint64_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        int e = lane + 64 * i;
+        v[i] = (e < E) ? L[e] : 0.f;
+        key[i] = (e < E) ? rank_key(v[i], e) : 0ull;
+    }
+    int my_id = -1;
+    float my_v = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        const int id = (int)(0xFFFFFu - (uint32_t)(best & 0xFFFFFu));
+        // the owner removes the pick from its candidates
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (lane + 64 * i == id) key[i] = 0ull;
+        if (lane == j && id < E) {
+            my_id = id;
+            my_v = L[id];
+        }
+    }
+    const float top = __shfl(my_v, 0, kWave);
+    float den;
+    float num = (lane < k) ? expf(my_v - top) : 0.f;
+    if (renorm) {
+        den = wave_sum_xor(num, kWave);
+    } else {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (lane + 64 * i < E) part += expf(v[i] - top);
+        den = wave_sum_xor(part, kWave);
+    }
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = my_id;
+        gates[(size_t)t * k + lane] = num / den;
+    }
+}
+
+int launch_topk(const moe_dims& d, const float* logits, int renorm, int32_t* ids, float* gates,
+                hipStream_t s) {
+    if (d.T == 0) return MOE_OK;
+    dim3 grid((d.T + 3) / 4), block(256);
+    if (d.E <= 64)
+        hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, d.T, d.E, d.k, renorm, ids, gates);
+    else if (d.E <= 256)
+        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, d.T, d.E, d.k, renorm, ids, gates);
+    else if (d.E <= 512)
+        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, d.T, d.E, d.k, renorm, ids, gates);
+    else
+        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, d.T, d.E, d.k, renorm, ids, gates);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

@@ -1,0 +1,80 @@
+"""One routed-MoE layer step as a fixed sequence of library calls.
+
+``LayerBuffers`` preallocates every intermediate once (logits, picks, slot
+lookup results, permutation, workspace, expert outputs) so that a step is six
+C calls on one stream with no allocation and no host synchronisation:
+
+    route_topk -> slot_lookup -> permute -> expert_ffn_q{4,2} -> combine
+
+This module only orders the calls; the arithmetic is in the HIP kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import (ALGO_AUTO, OP_FFN, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4, permute,
+               route_topk, slot_lookup, workspace_bytes)
+
+
+@dataclass
+class LayerBuffers:
+    d: Dims
+    bits: int
+    logits: torch.Tensor          # float32 [T, E]
+    topk_ids: torch.Tensor        # int32 [T, k]
+    topk_w: torch.Tensor          # float32 [T, k]
+    pair_slot: torch.Tensor       # int32 [T*k]
+    miss: torch.Tensor            # int32 [E]
+    n_miss: torch.Tensor          # int32 [1]
+    counts: torch.Tensor          # int32 [E]
+    offsets: torch.Tensor         # int32 [E+1]
+    sorted_pairs: torch.Tensor    # int32 [T*k]
+    pair_to_row: torch.Tensor     # int32 [T*k]
+    active: torch.Tensor          # int32 [E]
+    n_active: torch.Tensor        # int32 [1]
+    workspace: torch.Tensor       # uint8, 256-byte aligned by the allocator
+    y_rows: torch.Tensor          # bf16 bits as int16 [T*k, H]
+
+    @staticmethod
+    def allocate(d: Dims, bits: int = 4, algo: int = ALGO_AUTO, device="cuda") -> "LayerBuffers":
+        T, H, E, k = d.T, d.H, d.E, d.k
+        i32 = dict(dtype=torch.int32, device=device)
+        ws = workspace_bytes(d, OP_FFN, bits, algo)
+        return LayerBuffers(
+            d=d, bits=bits,
+            logits=torch.empty((T, E), dtype=torch.float32, device=device),
+            topk_ids=torch.empty((T, k), **i32),
+            topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+            pair_slot=torch.empty((T * k,), **i32),
+            miss=torch.empty((E,), **i32),
+            n_miss=torch.zeros((1,), **i32),
+            counts=torch.empty((E,), **i32),
+            offsets=torch.empty((E + 1,), **i32),
+            sorted_pairs=torch.empty((max(T * k, 1),), **i32),
+            pair_to_row=torch.empty((max(T * k, 1),), **i32),
+            active=torch.empty((E,), **i32),
+            n_active=torch.zeros((1,), **i32),
+            workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
+            y_rows=torch.empty((max(T * k, 1), H), dtype=torch.int16, device=device),
+        )
+
+
+def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
+                  router_bias: Optional[torch.Tensor], weights: QWeights,
+                  slot_of_expert: torch.Tensor, n_slots: int, residual: torch.Tensor,
+                  out: torch.Tensor, algo: int = ALGO_AUTO, renormalize: bool = True,
+                  host_doorbell=None, last_use=None, step: int = 0, stream=None) -> None:
+    """Enqueue one layer step; `out` may be `residual`."""
+    d = buf.d
+    route_topk(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w, stream)
+    slot_lookup(d, buf.topk_ids, slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss,
+                host_doorbell, last_use, step, stream)
+    permute(d, buf.topk_ids, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active,
+            buf.n_active, stream)
+    ffn = expert_ffn_q4 if weights.bits == 4 else expert_ffn_q2
+    ffn(d, x, buf.sorted_pairs, buf.counts, buf.offsets, buf.active, buf.n_active, weights,
+        buf.y_rows, algo, buf.workspace, None, stream)
+    combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)

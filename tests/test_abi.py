@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libmoe.so loads and exports every entry point that include/moe.h declares;
+* argument validation rejects bad calls before anything is enqueued, with the
+  documented status code and a readable moe_last_error().
+Pointers used here are fake addresses: every call below fails validation on
+the host, which is exactly what is being tested.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_ffn_gemv_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000          # 256-byte aligned, never dereferenced
+MISALIGNED = FAKE + 2
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_lists():
+    assert header_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert moe.abi_version() == 1
+    assert moe.status_string(moe.ERR_WORKSPACE).startswith("workspace")
+
+
+def test_library_exports_nothing_else_with_the_prefix():
+    out = os.popen(f"nm -D --defined-only {moe.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\b", out)))
+    assert exported == header_functions()
+
+
+@pytest.mark.parametrize("T,H,I,E,k,g,status", [
+    (-1, 256, 256, 8, 2, 128, moe.ERR_INVALID_ARG),
+    (4, 250, 256, 8, 2, 128, moe.ERR_UNSUPPORTED),      # H not a multiple of 128
+    (4, 256, 200, 8, 2, 128, moe.ERR_UNSUPPORTED),      # I not a multiple of 128
+    (4, 256, 256, 8, 9, 128, moe.ERR_UNSUPPORTED),      # k > E
+    (4, 256, 256, 2000, 2, 128, moe.ERR_UNSUPPORTED),   # E too large
+    (4, 256, 256, 8, 2, 64, moe.ERR_UNSUPPORTED),       # group size
+    (40000, 256, 256, 8, 2, 128, moe.ERR_UNSUPPORTED),  # T*k too large
+    (4, 16384, 256, 8, 2, 128, moe.ERR_UNSUPPORTED),    # H too large
+])
+def test_dims_validation(T, H, I, E, k, g, status):
+    d = moe.Dims(T, H, I, E, k, g)
+    with pytest.raises(moe.MoeError) as ex:
+        moe.workspace_bytes(d, moe.OP_FFN, 4)
+    assert ex.value.status == status
+    assert moe.last_error()
+
+
+def test_workspace_size():
+    d = moe.dims(32, 2048, 512, 256, 8)
+    assert moe.workspace_bytes(d, moe.OP_FFN, 4) >= 32 * 8 * 512 * 4
+    assert moe.workspace_bytes(d, moe.OP_ROUTE, 4) == 0
+    with pytest.raises(moe.MoeError):
+        moe.workspace_bytes(d, moe.OP_FFN, 3)
+
+
+def _qw(ptr=FAKE):
+    w = moe.QWeightsC()
+    for m in range(3):
+        w.q[m] = ptr
+        w.scale[m] = FAKE
+        w.bias[m] = FAKE
+    return w
+
+
+def _ffn(d, x=FAKE, y=FAKE, w=None, algo=0, ws=FAKE, ws_bytes=1 << 30, sp=FAKE):
+    L = moe.lib()
+    w = w or _qw()
+    return L.moe_expert_ffn_q4(ctypes.byref(d), x, sp, FAKE, FAKE, FAKE, FAKE, ctypes.byref(w), y, algo,
+                               ws, ws_bytes, None)
+
+
+def test_ffn_validation_paths():
+    d = moe.dims(4, 256, 512, 8, 2)
+    assert _ffn(d, x=None) == moe.ERR_INVALID_ARG
+    assert "x is NULL" in moe.last_error()
+    assert _ffn(d, x=MISALIGNED) == moe.ERR_INVALID_ARG
+    assert "aligned" in moe.last_error()
+    assert _ffn(d, sp=None) == moe.ERR_INVALID_ARG
+    assert _ffn(d, w=_qw(MISALIGNED)) == moe.ERR_INVALID_ARG
+    assert _ffn(d, algo=7) == moe.ERR_UNSUPPORTED
+    assert _ffn(d, ws=None) == moe.ERR_WORKSPACE
+    assert _ffn(d, ws_bytes=100) == moe.ERR_WORKSPACE
+    assert "workspace" in moe.last_error()
+    assert _ffn(d, ws=FAKE + 16) == moe.ERR_INVALID_ARG
+
+
+def test_route_and_combine_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    assert L.moe_route_topk(ctypes.byref(d), FAKE, None, None, 1, FAKE, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_route_topk(ctypes.byref(d), MISALIGNED, FAKE, None, 1, FAKE, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_topk_from_logits(ctypes.byref(d), None, 1, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_slot_lookup(ctypes.byref(d), FAKE, FAKE, -1, FAKE, FAKE, FAKE, None, None, 0, None) == moe.ERR_INVALID_ARG
+    assert L.moe_permute(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_workspace_bytes(None, 3, 4, 0, None) == moe.ERR_INVALID_ARG
+
+
+def test_zero_tokens_need_no_buffers():
+    """T = 0: route, FFN and combine return OK without touching any pointer."""
+    L = moe.lib()
+    d = moe.dims(0, 256, 512, 8, 2)
+    assert L.moe_route_topk(ctypes.byref(d), None, None, None, 1, None, None, None, None) == moe.OK
+    assert L.moe_combine(ctypes.byref(d), None, None, None, None, None, None) == moe.OK
+    w = _qw()
+    assert L.moe_expert_ffn_q4(ctypes.byref(d), None, None, None, None, None, None, ctypes.byref(w), None,
+                               0, None, 0, None) == moe.OK

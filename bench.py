@@ -89,7 +89,6 @@ class Runner:
         sh = shape
         self.d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
         self.buf = moe.LayerBuffers.allocate(self.d, layers[0]["w"].bits, algo)
-        self.h = torch.empty((max(T * sh.k, 1), sh.I), dtype=torch.float32, device="cuda")
         self.x, self.res = [], []
         for li in range(len(layers)):
             xb, rb = mi.make_activations(sh.H, T, seed=1000 + li)
@@ -107,11 +106,12 @@ class Runner:
         moe.permute(d, b.topk_ids, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row, b.active, b.n_active)
         if ev is not None:
             ev[0].record()
-        moe.expert_gateup(d, bits, x, b.sorted_pairs, b.counts, b.offsets, b.active, b.n_active, L["w"], self.h,
-                          self.algo)
+        moe.expert_gateup(d, bits, x, b.sorted_pairs, b.counts, b.offsets, b.active, b.n_active, L["w"],
+                          b.workspace, self.algo)
         if ev is not None:
             ev[1].record()
-        moe.expert_down(d, bits, self.h, b.counts, b.offsets, b.active, b.n_active, L["w"], b.y_rows, self.algo)
+        moe.expert_down(d, bits, b.counts, b.offsets, b.active, b.n_active, L["w"], b.workspace, b.y_rows,
+                        self.algo)
         if ev is not None:
             ev[2].record()
         moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
@@ -240,7 +240,8 @@ def main():
         log(f"[bench] sweep T={tok}: {m['tokens_per_s']:.0f} tokens/s, gate/up {m['gateup_GBps']:.0f} GB/s")
         sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()})
 
-    kernel_src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc", "ffn_gemv.hip")
+    kernel_src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc",
+                              "ffn_gemv.hip" if args.algo == "gemv" else "ffn_mfma.hip")
     achieved = main_run["gateup_GBps"]
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(kernel_src),

@@ -42,8 +42,8 @@
  *     synchronisation.
  *   - Limits: 0 <= T, T*k <= 65536; 1 <= E <= 1024; 1 <= k <= min(E, 32);
  *     H and I multiples of 128 with 128 <= H <= 8192 and 128 <= I <= 16384;
- *     group_size == 128.  Device pointers to weights and activations must be
- *     16-byte aligned.
+ *     group_size == 128.  Device pointers to codes and activations must be
+ *     16-byte aligned, scale and bias arrays 4-byte aligned.
  *   - Ids passed back in must come from these calls (or satisfy the same
  *     invariants); kernels skip out-of-range ids rather than touch memory
  *     outside the buffers, and the results for such ids are unspecified.
@@ -127,8 +127,9 @@ const char* moe_status_string(int status);
 const char* moe_last_error(void);
 
 /* Device workspace that `op` needs for these dims (host-only, no GPU work).
- * Only MOE_OP_FFN needs any: float32 [T*k][I] for the SwiGLU activations
- * plus a small tail; the others report 0.  bits in {2, 4}. */
+ * Only MOE_OP_FFN needs any (the SwiGLU activations between the two halves of
+ * the FFN: 4*T*k*I bytes for MOE_ALGO_GEMV, about 6.25*T*k*I for
+ * MOE_ALGO_MFMA and AUTO); the others report 0.  bits in {2, 4}. */
 int moe_workspace_bytes(const moe_dims* dims, int op, int bits, int algo, size_t* bytes);
 
 /* Router logits and top-k (steps 1-2; Betelgeuse page, MoE primer).
@@ -202,23 +203,29 @@ int moe_expert_ffn_q2(const moe_dims* dims, const uint16_t* x, const int32_t* so
                       const moe_qweights* weights, uint16_t* y_rows, int algo,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Step 5 in two halves, for callers that want the SwiGLU activations or time
- * the halves apart.  bits in {2, 4}; the other arguments are as above.
- *   moe_expert_gateup: h[r][i] = silu(a_i) * u_i as float32 [T*k][I]
- *                      (the scope row "gate/up matvec + SwiGLU");
- *   moe_expert_down:   y_rows[r][n] = bf16(sum_i Wd[e][n][i] h[r][i])
- *                      (the scope row "down matvec").
- * moe_expert_ffn_q4/q2 == moe_expert_gateup then moe_expert_down with h in
- * the workspace. */
+/* Step 5 in two halves (the scope rows "gate/up matvec + SwiGLU" and "down
+ * matvec"), for callers that time or schedule them apart.  bits in {2, 4};
+ * the other arguments are as for moe_expert_ffn_q4.  moe_expert_gateup writes
+ * the SwiGLU activations h_i = silu(a_i) * u_i of every routed row into the
+ * workspace and moe_expert_down reads them from there, so both calls must get
+ * the same workspace, dims, bits and algo.  Workspace contents:
+ *   MOE_ALGO_GEMV: float32 h [T*k][I] at offset 0;
+ *   MOE_ALGO_MFMA (and AUTO): h as three bf16 planes hi, mid, lo [3][T*k][I]
+ *     with hi + mid + lo == h to float32 precision, stored in the pair order
+ *     of the matrix-core operands, followed by float32 partial sums of h over
+ *     16 consecutive i [T*k][I/16].
+ * moe_expert_ffn_q4/q2 == moe_expert_gateup followed by moe_expert_down. */
 int moe_expert_gateup(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* sorted_pairs,
                       const int32_t* expert_counts, const int32_t* expert_offsets,
                       const int32_t* active_experts, const int32_t* n_active,
-                      const moe_qweights* weights, int algo, float* h, void* stream);
+                      const moe_qweights* weights, int algo, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
-int moe_expert_down(const moe_dims* dims, int bits, const float* h, const int32_t* expert_counts,
+int moe_expert_down(const moe_dims* dims, int bits, const int32_t* expert_counts,
                     const int32_t* expert_offsets, const int32_t* active_experts,
                     const int32_t* n_active, const moe_qweights* weights, int algo,
-                    uint16_t* y_rows, void* stream);
+                    const void* workspace, size_t workspace_bytes, uint16_t* y_rows,
+                    void* stream);
 
 /* Combine + residual (step 6; Flash-MoE page, sec. 3):
  *   acc = residual[t][n];  for j = 0..k-1 in order:

@@ -70,8 +70,8 @@ def lib() -> ctypes.CDLL:
     L.moe_permute.argtypes = [Dp, P, P, P, P, P, P, P, P]
     for name in ("moe_expert_ffn_q4", "moe_expert_ffn_q2"):
         getattr(L, name).argtypes = [Dp, P, P, P, P, P, P, Wp, P, ctypes.c_int, P, sz, P]
-    L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, P, P, P, Wp, ctypes.c_int, P, P]
-    L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, P, P, P, Wp, ctypes.c_int, P, P]
+    L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, P, P, P, Wp, ctypes.c_int, P, sz, P]
+    L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, P, P, Wp, ctypes.c_int, P, sz, P, P]
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = ctypes.c_int
@@ -187,20 +187,24 @@ def expert_ffn_q2(d: Dims, x, sorted_pairs, expert_counts, expert_offsets, activ
          n_active, weights, y_rows, algo, workspace, workspace_bytes_, stream)
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def expert_gateup(d: Dims, bits: int, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
-                  n_active, weights: QWeights, h, algo: int = ALGO_AUTO, stream=None):
+                  n_active, weights: QWeights, workspace, algo: int = ALGO_AUTO, stream=None):
     w = weights.c_struct()
     _check(lib().moe_expert_gateup(ctypes.byref(d), int(bits), _ptr(x), _ptr(sorted_pairs), _ptr(expert_counts),
                                    _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), ctypes.byref(w),
-                                   int(algo), _ptr(h), _stream(stream)))
+                                   int(algo), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def expert_down(d: Dims, bits: int, h, expert_counts, expert_offsets, active_experts, n_active,
-                weights: QWeights, y_rows, algo: int = ALGO_AUTO, stream=None):
+def expert_down(d: Dims, bits: int, expert_counts, expert_offsets, active_experts, n_active,
+                weights: QWeights, workspace, y_rows, algo: int = ALGO_AUTO, stream=None):
     w = weights.c_struct()
-    _check(lib().moe_expert_down(ctypes.byref(d), int(bits), _ptr(h), _ptr(expert_counts), _ptr(expert_offsets),
-                                 _ptr(active_experts), _ptr(n_active), ctypes.byref(w), int(algo), _ptr(y_rows),
-                                 _stream(stream)))
+    _check(lib().moe_expert_down(ctypes.byref(d), int(bits), _ptr(expert_counts), _ptr(expert_offsets),
+                                 _ptr(active_experts), _ptr(n_active), ctypes.byref(w), int(algo),
+                                 _ptr(workspace), _nbytes(workspace), _ptr(y_rows), _stream(stream)))
 
 
 def combine(d: Dims, y_rows, pair_to_row, topk_w, residual, out, stream=None):

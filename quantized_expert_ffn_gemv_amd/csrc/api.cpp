@@ -68,8 +68,6 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* c
     if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: weights is NULL", fn);
     if (algo != MOE_ALGO_AUTO && algo != MOE_ALGO_GEMV && algo != MOE_ALGO_MFMA)
         return fail(MOE_ERR_UNSUPPORTED, "%s: unknown algo %d", fn, algo);
-    if (algo == MOE_ALGO_MFMA)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: algo MFMA is not available in this build", fn);
     if (d->T == 0) return MOE_OK;
     REQUIRE_PTR(counts, 4);
     REQUIRE_PTR(offsets, 4);
@@ -80,8 +78,8 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* c
             return fail(MOE_ERR_INVALID_ARG, "%s: weights matrix %d has a NULL pointer", fn, m);
         if (!aligned(w->q[m], 16))
             return fail(MOE_ERR_INVALID_ARG, "%s: weights.q[%d] is not 16-byte aligned", fn, m);
-        if (!aligned(w->scale[m], 2) || !aligned(w->bias[m], 2))
-            return fail(MOE_ERR_INVALID_ARG, "%s: weights.scale/bias[%d] misaligned", fn, m);
+        if (!aligned(w->scale[m], 4) || !aligned(w->bias[m], 4))
+            return fail(MOE_ERR_INVALID_ARG, "%s: weights.scale/bias[%d] is not 4-byte aligned", fn, m);
     }
     return MOE_OK;
 }
@@ -104,6 +102,15 @@ moe::FfnArgs ffn_args(const moe_dims* d, int bits, const uint16_t* x, const int3
     return a;
 }
 
+int check_workspace(const char* fn, const moe_dims* d, int bits, int algo, const void* ws, size_t ws_bytes) {
+    const size_t need = moe::ffn_workspace_bytes(*d, bits, algo);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+    return MOE_OK;
+}
+
 int ffn_common(const char* fn, int bits, const moe_dims* d, const uint16_t* x,
                const int32_t* sorted_pairs, const int32_t* counts, const int32_t* offsets,
                const int32_t* active, const int32_t* n_active, const moe_qweights* w, uint16_t* y,
@@ -114,18 +121,17 @@ int ffn_common(const char* fn, int bits, const moe_dims* d, const uint16_t* x,
     REQUIRE_PTR(x, 16);
     REQUIRE_PTR(sorted_pairs, 4);
     REQUIRE_PTR(y, 16);
-    const size_t need = moe::ffn_workspace_bytes(*d, bits, algo);
-    if (ws == nullptr || ws_bytes < need)
-        return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                    ws == nullptr ? (size_t)0 : ws_bytes);
-    if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+    st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
+    if (st) return st;
     moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w,
                               static_cast<float*>(ws), y);
-    st = moe::launch_gateup_gemv(a, as_stream(stream));
-    if (!st) st = moe::launch_down_gemv(a, as_stream(stream));
+    const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
+    st = mfma ? moe::launch_gateup_mfma(a, as_stream(stream)) : moe::launch_gateup_gemv(a, as_stream(stream));
+    if (!st) st = mfma ? moe::launch_down_mfma(a, as_stream(stream)) : moe::launch_down_gemv(a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }
+
 
 }  // namespace
 
@@ -253,33 +259,38 @@ int moe_expert_ffn_q2(const moe_dims* d, const uint16_t* x, const int32_t* sorte
 
 int moe_expert_gateup(const moe_dims* d, int bits, const uint16_t* x, const int32_t* sorted_pairs,
                       const int32_t* counts, const int32_t* offsets, const int32_t* active,
-                      const int32_t* n_active, const moe_qweights* w, int algo, float* h,
-                      void* stream) {
+                      const int32_t* n_active, const moe_qweights* w, int algo, void* ws,
+                      size_t ws_bytes, void* stream) {
     const char* fn = "moe_expert_gateup";
     int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 0, 2);
     if (st) return st;
     if (d->T == 0) return ok();
     REQUIRE_PTR(x, 16);
     REQUIRE_PTR(sorted_pairs, 4);
-    REQUIRE_PTR(h, 16);
-    moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w, h, nullptr);
-    st = moe::launch_gateup_gemv(a, as_stream(stream));
+    st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
+    if (st) return st;
+    moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w,
+                              static_cast<float*>(ws), nullptr);
+    const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
+    st = mfma ? moe::launch_gateup_mfma(a, as_stream(stream)) : moe::launch_gateup_gemv(a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }
 
-int moe_expert_down(const moe_dims* d, int bits, const float* h, const int32_t* counts,
-                    const int32_t* offsets, const int32_t* active, const int32_t* n_active,
-                    const moe_qweights* w, int algo, uint16_t* y, void* stream) {
+int moe_expert_down(const moe_dims* d, int bits, const int32_t* counts, const int32_t* offsets,
+                    const int32_t* active, const int32_t* n_active, const moe_qweights* w, int algo,
+                    const void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
     const char* fn = "moe_expert_down";
     int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 2, 3);
     if (st) return st;
     if (d->T == 0) return ok();
-    REQUIRE_PTR(h, 16);
     REQUIRE_PTR(y, 16);
+    st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
+    if (st) return st;
     moe::FfnArgs a = ffn_args(d, bits, nullptr, nullptr, counts, offsets, active, n_active, w,
-                              const_cast<float*>(h), y);
-    st = moe::launch_down_gemv(a, as_stream(stream));
+                              static_cast<float*>(const_cast<void*>(ws)), y);
+    const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
+    st = mfma ? moe::launch_down_mfma(a, as_stream(stream)) : moe::launch_down_gemv(a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }

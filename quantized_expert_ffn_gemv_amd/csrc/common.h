@@ -29,11 +29,71 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
+// ------------------------------------------------------ exact code operands
+// A code q of BITS bits is placed in the top mantissa bits of the bf16 value
+// 128 (pattern 0x4300): the result 128 + kLever * q is exact (all values lie in
+// [128, 256) where the bf16 spacing is 1).  A dot product with such operands
+// is C = 128 * sum(x) + kLever * sum(q x), hence
+//   sum((q s + b) x) = (s / kLever) * C + (b - kOffset * s) * sum(x),
+// with kOffset = 128 / kLever.
+template <int BITS> constexpr int kLever = (BITS == 4) ? 8 : 32;
+template <int BITS> constexpr float kInvLever = 1.0f / (float)kLever<BITS>;
+template <int BITS> constexpr float kOffset = 128.0f / (float)kLever<BITS>;
+
+// v >> sh for sh >= 0, v << -sh otherwise (sh is a compile-time constant)
+__device__ __forceinline__ uint32_t shift_to(uint32_t v, int sh) { return sh >= 0 ? (v >> sh) : (v << (-sh)); }
+
 // --------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum_xor(float v, int width) {
     for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
+}
+
+// Sum N values per lane over all 64 lanes of the wave (N a power of two <= 64)
+// by a butterfly transpose: at each of log2(N) stages lanes exchange half of
+// their values with the partner lane and add, so the cost is ~N shuffles in
+// total instead of N * 6.  Afterwards lane l holds the sum of value index
+// (l >> (6 - log2 N)) & (N - 1) ... see wave_transpose_index.
+template <int N>
+constexpr int log2_of() { return (N <= 1) ? 0 : 1 + log2_of<N / 2>(); }
+
+// One butterfly stage: n values in play, exchanged with the lane at xor `off`.
+template <int N, int STAGE>
+__device__ __forceinline__ void transpose_stage(float (&v)[N], int lane) {
+    constexpr int n = N >> STAGE, off = 32 >> STAGE, h = n / 2;
+    const bool upper = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+        const float keep = upper ? v[i + h] : v[i];
+        const float send = upper ? v[i] : v[i + h];
+        v[i] = keep + __shfl_xor(send, off, kWave);
+    }
+}
+
+template <int N, int STAGE>
+__device__ __forceinline__ void transpose_stages(float (&v)[N], int lane) {
+    if constexpr ((N >> STAGE) > 1) {
+        transpose_stage<N, STAGE>(v, lane);
+        transpose_stages<N, STAGE + 1>(v, lane);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[N]) {
+    const int lane = threadIdx.x & 63;
+    transpose_stages<N, 0>(v, lane);
+    // remaining lane bits: plain butterfly over the lanes that share an index
+    float r = v[0];
+#pragma unroll
+    for (int off = 32 >> log2_of<N>(); off > 0; off >>= 1) r += __shfl_xor(r, off, kWave);
+    return r;
+}
+
+// Value index whose total lane `lane` holds after wave_transpose_sum<N>.
+template <int N>
+__device__ __forceinline__ int wave_transpose_index(int lane) {
+    return (lane >> (6 - log2_of<N>())) & (N - 1);
 }
 
 // ---------------------------------------------------------- launch helpers
@@ -70,12 +130,17 @@ struct FfnArgs {
     const int32_t* n_active;
     moe_qweights w;
     uint16_t* y;
-    float* h;          // workspace: float32 [T*k][I]
+    float* h;          // FFN workspace (layout depends on the algorithm)
 };
 
+size_t gemv_workspace_bytes(const moe_dims& d);
+size_t mfma_workspace_bytes(const moe_dims& d);
 size_t ffn_workspace_bytes(const moe_dims& d, int bits, int algo);
+int resolve_algo(const moe_dims& d, int bits, int algo);
 int launch_gateup_gemv(const FfnArgs& a, hipStream_t s);
 int launch_down_gemv(const FfnArgs& a, hipStream_t s);
+int launch_gateup_mfma(const FfnArgs& a, hipStream_t s);
+int launch_down_mfma(const FfnArgs& a, hipStream_t s);
 int launch_combine(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,
                    const uint16_t* residual, uint16_t* out, hipStream_t s);
 

@@ -13,12 +13,13 @@
 //  * Each row of codes is read once per token tile with 16-byte loads; LG
 //    consecutive lanes cover one row (LG * 16 contiguous bytes per load), each
 //    lane group carries 4 rows so every activation fetch from LDS serves 4 rows.
-//  * Gate/up: a code q is turned into the exact bf16 value 128 + q by OR-ing it
-//    into the bf16 pattern 0x4300, two codes per 32-bit register, and
-//    multiplied against bf16 activation pairs with v_dot2_f32_bf16 (products
-//    exact, float32 accumulation).  Per 16-byte chunk (one group) the sum
-//    D = sum (128 + q) x folds into the row total as
-//        s * D + (b - 128 s) * X,      X = sum of x over the chunk,
+//  * Gate/up: a code q is turned into the exact bf16 value 128 + L q by OR-ing
+//    it into the top mantissa bits of the bf16 pattern 0x4300 (L = 8 for 4-bit,
+//    32 for 2-bit), two codes per 32-bit register, and multiplied against bf16
+//    activation pairs with v_dot2_f32_bf16 (products exact, float32
+//    accumulation).  Per 16-byte chunk (inside one group) the sum
+//    D = sum (128 + L q) x folds into the row total as
+//        (s / L) D + (b - (128 / L) s) X,      X = sum of x over the chunk,
 //    i.e. sum (q s + b) x with the scale and bias applied once per chunk -- the
 //    FMA form of the Flash-MoE page with the bias term carried by X.
 //  * Down: the activations h are float32, so codes are converted with
@@ -47,15 +48,15 @@ struct GemvParams {
     int items_per_expert;
 };
 
-// codes of one 32-bit word -> bf16 pairs (128 + q_j, 128 + q_{j+W/2})
+// codes of one 32-bit word -> bf16 pairs (128 + L q_j, 128 + L q_{j+W/2})
 template <int BITS>
 __device__ __forceinline__ void codes_to_bf16_pairs(uint32_t w, uint32_t* out) {
     if constexpr (BITS == 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = ((w >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+        for (int j = 0; j < 4; ++j) out[j] = (shift_to(w, 4 * j - 3) & 0x00780078u) | 0x43004300u;
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = ((w >> (2 * j)) & 0x00030003u) | 0x43004300u;
+        for (int j = 0; j < 8; ++j) out[j] = (shift_to(w, 2 * j - 5) & 0x00600060u) | 0x43004300u;
     }
 }
 
@@ -188,7 +189,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
                     const bool ok = (r & 1) ? v1 : v0;
                     sc[r] = ok ? f16_bits_to_f32(srow[r][g]) : 0.f;
                     bc[r] = ok ? f16_bits_to_f32(brow[r][g]) : 0.f;
-                    bc[r] = fmaf(-128.f, sc[r], bc[r]);
+                    bc[r] = fmaf(-kOffset<BITS>, sc[r], bc[r]);
+                    sc[r] *= kInvLever<BITS>;
                 }
                 float d[4][PT];
 #pragma unroll
@@ -475,9 +477,19 @@ static int launch_down_bits(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-size_t ffn_workspace_bytes(const moe_dims& d, int /*bits*/, int /*algo*/) {
+size_t gemv_workspace_bytes(const moe_dims& d) {
     const size_t h = (size_t)d.T * d.k * d.I * sizeof(float);
     return (h + 255) & ~(size_t)255;
+}
+
+// MOE_ALGO_AUTO -> the matrix-core path (its cost per weight does not grow with
+// the tokens an expert serves); explicit choices are kept.
+int resolve_algo(const moe_dims& /*d*/, int /*bits*/, int algo) {
+    return algo == MOE_ALGO_AUTO ? MOE_ALGO_MFMA : algo;
+}
+
+size_t ffn_workspace_bytes(const moe_dims& d, int bits, int algo) {
+    return resolve_algo(d, bits, algo) == MOE_ALGO_GEMV ? gemv_workspace_bytes(d) : mfma_workspace_bytes(d);
 }
 
 int launch_gateup_gemv(const FfnArgs& a, hipStream_t s) {

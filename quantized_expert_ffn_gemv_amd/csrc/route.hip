@@ -6,56 +6,81 @@
 namespace moe {
 
 // ------------------------------------------------------------ router, small T
-// Decode shapes: T <= 64.  One wave per EB experts streams their float32 router
-// rows once (16-byte loads, 1 KB per wave per step) and applies them to a tile
-// of TT tokens whose bf16 activations come through L1/L2.  Partial sums are
-// reduced across the wave with xor shuffles.
-template <int EB, int TT>
-__global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x,
+// Decode shapes: T <= 64.  A 256-thread workgroup owns EB experts; its 4 waves
+// split K into quarters and each lane covers 4 consecutive k per 256-wide step
+// (NJ steps).  All router-weight loads of the workgroup are issued up front
+// (EB * NJ float4 per lane), then tokens are processed TT at a time with their
+// activation loads independent of each other, so the kernel is a couple of
+// memory latencies long instead of a chain of dependent loads.  Partial sums
+// are reduced across the wave with xor shuffles and across the 4 waves in LDS.
+template <int EB, int TT, int NJ>
+__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ w,
                                                           const float* __restrict__ bias,
                                                           float* __restrict__ logits, int T, int H,
                                                           int E) {
-    const int lane = threadIdx.x;
+    __shared__ float part[4][EB][TT];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int e0 = blockIdx.x * EB;
+    const int kq = H / 4;                        // this wave's quarter of K
+    const int kbase = wv * kq + lane * 4;
+    float4 wr[EB][NJ];
+#pragma unroll
+    for (int a = 0; a < EB; ++a)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int k = kbase + 256 * j;
+            const bool ok = (e0 + a < E) && (lane * 4 + 256 * j < kq);
+            wr[a][j] = ok ? *reinterpret_cast<const float4*>(w + (size_t)(e0 + a) * H + k)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     for (int t0 = 0; t0 < T; t0 += TT) {
+        uint2 xv[TT][NJ];
+#pragma unroll
+        for (int b = 0; b < TT; ++b)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool ok = (t0 + b < T) && (lane * 4 + 256 * j < kq);
+                xv[b][j] = ok ? *reinterpret_cast<const uint2*>(x + (size_t)(t0 + b) * H + kbase + 256 * j)
+                              : make_uint2(0, 0);
+            }
         float acc[EB][TT];
 #pragma unroll
-        for (int a = 0; a < EB; ++a)
+        for (int b = 0; b < TT; ++b) {
 #pragma unroll
-            for (int b = 0; b < TT; ++b) acc[a][b] = 0.f;
-        for (int k = lane * 4; k < H; k += 256) {
-            float4 wv[EB];
+            for (int a = 0; a < EB; ++a) acc[a][b] = 0.f;
 #pragma unroll
-            for (int a = 0; a < EB; ++a)
-                wv[a] = (e0 + a < E) ? *reinterpret_cast<const float4*>(w + (size_t)(e0 + a) * H + k)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < NJ; ++j) {
+                const float x0 = bf16_bits_to_f32(xv[b][j].x & 0xFFFFu), x1 = bf16_bits_to_f32(xv[b][j].x >> 16);
+                const float x2 = bf16_bits_to_f32(xv[b][j].y & 0xFFFFu), x3 = bf16_bits_to_f32(xv[b][j].y >> 16);
 #pragma unroll
-            for (int b = 0; b < TT; ++b) {
-                if (t0 + b < T) {
-                    uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + b) * H + k);
-                    float x0 = bf16_bits_to_f32(xv.x & 0xFFFFu), x1 = bf16_bits_to_f32(xv.x >> 16);
-                    float x2 = bf16_bits_to_f32(xv.y & 0xFFFFu), x3 = bf16_bits_to_f32(xv.y >> 16);
-#pragma unroll
-                    for (int a = 0; a < EB; ++a) {
-                        float s = acc[a][b];
-                        s = fmaf(x0, wv[a].x, s);
-                        s = fmaf(x1, wv[a].y, s);
-                        s = fmaf(x2, wv[a].z, s);
-                        s = fmaf(x3, wv[a].w, s);
-                        acc[a][b] = s;
-                    }
+                for (int a = 0; a < EB; ++a) {
+                    float s = acc[a][b];
+                    s = fmaf(x0, wr[a][j].x, s);
+                    s = fmaf(x1, wr[a][j].y, s);
+                    s = fmaf(x2, wr[a][j].z, s);
+                    s = fmaf(x3, wr[a][j].w, s);
+                    acc[a][b] = s;
                 }
             }
         }
+        float flat[EB * TT];
 #pragma unroll
         for (int a = 0; a < EB; ++a)
 #pragma unroll
-            for (int b = 0; b < TT; ++b) {
-                float v = wave_sum_xor(acc[a][b], kWave);
-                if (lane == 0 && e0 + a < E && t0 + b < T)
-                    logits[(size_t)(t0 + b) * E + e0 + a] = v + (bias ? bias[e0 + a] : 0.f);
+            for (int b = 0; b < TT; ++b) flat[a * TT + b] = acc[a][b];
+        const float tot = wave_transpose_sum<EB * TT>(flat);
+        const int idx = wave_transpose_index<EB * TT>(lane);
+        if ((lane & ((64 / (EB * TT)) - 1)) == 0) part[wv][idx / TT][idx % TT] = tot;
+        __syncthreads();
+        if (tid < EB * TT) {
+            const int a = tid / TT, b = tid % TT;
+            if (e0 + a < E && t0 + b < T) {
+                const float v = (part[0][a][b] + part[1][a][b]) + (part[2][a][b] + part[3][a][b]);
+                logits[(size_t)(t0 + b) * E + e0 + a] = v + (bias ? bias[e0 + a] : 0.f);
             }
+        }
+        __syncthreads();
     }
 }
 
@@ -131,10 +156,18 @@ int launch_router_logits(const moe_dims& d, const uint16_t* x, const float* w, c
                          float* logits, hipStream_t s) {
     if (d.T == 0) return MOE_OK;
     if (d.T <= 64) {
-        constexpr int EB = 2, TT = 8;
+        // each lane covers NJ steps of 4 k within its wave's quarter of H
+        const int nj = (d.H / 4 + 255) / 256;
+        constexpr int EB = 4, TT = 8;
         dim3 grid((d.E + EB - 1) / EB);
-        hipLaunchKernelGGL((router_gemv_kernel<EB, TT>), grid, dim3(64), 0, s, x, w, bias, logits,
-                           d.T, d.H, d.E);
+        switch (nj) {
+            case 1: hipLaunchKernelGGL((router_gemv_kernel<EB, TT, 1>), grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
+            case 2: hipLaunchKernelGGL((router_gemv_kernel<EB, TT, 2>), grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
+            case 3: hipLaunchKernelGGL((router_gemv_kernel<EB, TT, 3>), grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
+            case 4: hipLaunchKernelGGL((router_gemv_kernel<EB, TT, 4>), grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
+            case 5: case 6: hipLaunchKernelGGL((router_gemv_kernel<2, TT, 6>), dim3((d.E + 1) / 2), dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
+            default: hipLaunchKernelGGL((router_gemv_kernel<2, TT, 8>), dim3((d.E + 1) / 2), dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
+        }
     } else {
         dim3 grid((d.T + RT_BM - 1) / RT_BM, (d.E + RT_BN - 1) / RT_BN);
         hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H,

@@ -47,9 +47,14 @@ def _stages(L, T, seed=0, ffn_rows=None, n_idx=None, algo=moe.ALGO_AUTO):
     return g, xb, res
 
 
-def test_tiny_layer_all_stages_and_end_to_end():
+ALGOS = [moe.ALGO_MFMA, moe.ALGO_GEMV]
+ALGO_IDS = ["mfma", "gemv"]
+
+
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
+def test_tiny_layer_all_stages_and_end_to_end(algo):
     L = layer("tiny")
-    g, xb, res = _stages(L, 4)
+    g, xb, res = _stages(L, 4, algo=algo)
     # end to end from raw inputs (oracle routes on its own logits)
     W = mi.make_expert_weights(L.shape, 4, 0)
     ref = oracle.layer(xb, L.Wr, L.bias, W, L.shape.k, L.table, L.shape.E, res)
@@ -58,12 +63,13 @@ def test_tiny_layer_all_stages_and_end_to_end():
     assert mr <= 1e-2 and mae <= 1e-3
 
 
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
 @pytest.mark.parametrize("T", [1, 8, 32])
-def test_a3b_layer(T):
+def test_a3b_layer(T, algo):
     L = layer("a3b")
     P = T * L.shape.k
     rows = None if T <= 8 else list(range(0, P, 3))
-    _stages(L, T, ffn_rows=rows)
+    _stages(L, T, ffn_rows=rows, algo=algo)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -76,10 +82,11 @@ def test_e64_layer_with_miss_list(seed):
     say(f"[e64 seed {seed}] n_miss={g['n_miss']} miss={g['miss'][:g['n_miss']].tolist()}")
 
 
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
 @pytest.mark.parametrize("bits", [4, 2])
-def test_e512_layer(bits):
+def test_e512_layer(bits, algo):
     L = layer("e512", bits)
-    _stages(L, 1)
+    _stages(L, 1, algo=algo)
 
 
 def test_prefill_layer_sampled_rows():
@@ -113,11 +120,48 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
 @pytest.mark.parametrize("shape", RAGGED, ids=[s.name for s in RAGGED])
 @pytest.mark.parametrize("bits", [4, 2])
-def test_ragged_shapes(shape, bits):
+def test_ragged_shapes(shape, bits, algo):
     L = layer(shape.name, bits, shape)
-    _stages(L, shape.tokens[0], seed=3)
+    _stages(L, shape.tokens[0], seed=3, algo=algo)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_many_tokens_per_expert_mfma(bits):
+    """Experts serving more than one 16-token tile (several MFMA passes)."""
+    shape = mi.LayerShape("crowd", H=512, E=4, k=2, I=256, tokens=(40,), bits=(bits,), zipf_s=None, n_resident=2)
+    L = layer(shape.name, bits, shape)
+    g, _, _ = _stages(L, 40, seed=4, algo=moe.ALGO_MFMA)
+    assert g["counts"].max() > 16
+
+
+def test_split_calls_gateup_h_matches_oracle():
+    """moe_expert_gateup alone (vector path): float32 h rows against the oracle."""
+    L = layer("a3b")
+    sh = L.shape
+    T = 8
+    xb, res = mi.make_activations(sh.H, T, 9)
+    g = run_layer(L, xb, res, algo=moe.ALGO_GEMV)
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+    buf = moe.LayerBuffers.allocate(d, 4, moe.ALGO_GEMV)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    moe.expert_gateup(d, 4, dev(xb.view(np.int16)), dev(g["sorted_pairs"]), dev(g["counts"]), dev(g["offsets"]),
+                      dev(g["active"]), dev(np.array([g["n_active"]], np.int32)), L.weights_d, buf.workspace,
+                      moe.ALGO_GEMV)
+    torch.cuda.synchronize()
+    P = T * sh.k
+    h = buf.workspace[: P * sh.I * 4].view(torch.float32).reshape(P, sh.I).cpu().numpy()
+    ids = g["ids"].ravel()
+    W = mi.make_expert_weights(sh, 4, 0, experts=np.unique(ids))
+    hs, _ = oracle.expert_ffn(xb, ids, g["sorted_pairs"], W, sh.k, rows=list(range(0, P, 5)), n_idx=np.array([0], np.int32))
+    for r, href in hs.items():
+        # float32 accumulation: error relative to the row's scale, not to h_i itself
+        # (h_i = silu(a_i) * u_i has zero crossings)
+        href = href.astype(np.float64)
+        err = np.abs(h[r].astype(np.float64) - href) / (np.abs(href) + np.sqrt(np.mean(href ** 2)))
+        assert err.max() < 1e-5, (r, err.max())
 
 
 def test_zero_tokens_is_a_no_op():

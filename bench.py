@@ -54,9 +54,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--tokens", type=int, default=32)
     ap.add_argument("--layers", type=int, default=4, help="rotating weight sets")
-    ap.add_argument("--sweep", default="1,8", help="extra token counts timed after the main run ('' = none)")
+    ap.add_argument("--sweep", default="1,8", help="extra token counts timed after the main run ('none' = none)")
     ap.add_argument("--algo", choices=["auto", "gemv", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the runs, copy a buffer of this many MiB device to device 5 times "
+                         "(the known-size kernel that scales the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                         "'bench.py --copy-calib-mib N' into the traffic record under profiles/")
     return ap.parse_args()
 
 
@@ -103,15 +109,14 @@ class Runner:
         bits = L["w"].bits
         moe.route_topk(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w)
         moe.slot_lookup(d, b.topk_ids, L["table"], self.shape.E, b.pair_slot, b.miss, b.n_miss)
-        moe.permute(d, b.topk_ids, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row, b.active, b.n_active)
+        moe.permute(d, b.topk_ids, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row, b.active, b.n_active,
+                    b.work_list, b.n_work)
         if ev is not None:
             ev[0].record()
-        moe.expert_gateup(d, bits, x, b.sorted_pairs, b.counts, b.offsets, b.active, b.n_active, L["w"],
-                          b.workspace, self.algo)
+        moe.expert_gateup(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, self.algo)
         if ev is not None:
             ev[1].record()
-        moe.expert_down(d, bits, b.counts, b.offsets, b.active, b.n_active, L["w"], b.workspace, b.y_rows,
-                        self.algo)
+        moe.expert_down(d, bits, b.work_list, b.n_work, L["w"], b.workspace, b.y_rows, self.algo)
         if ev is not None:
             ev[2].record()
         moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
@@ -165,6 +170,64 @@ def traffic_record(kernel_src):
     return rec.get("bytes_per_launch")
 
 
+TRAFFIC_KERNELS = {"gateup": "ffn_gateup_mfma_kernel", "down": "ffn_down_mfma_kernel",
+                   "copy": "copyBuffer"}
+
+
+def _counter_rows(d):
+    """Per-dispatch counter values from a rocprofv3 --pmc csv output folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, copy_mib):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
+    what the same counters read for the plain copy of copy_mib MiB."""
+    import statistics
+    res = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d)
+        for key, pat in TRAFFIC_KERNELS.items():
+            vals = [v for k, c, v in rows if c == cname and pat in k]
+            if key == "copy":   # the calibration copies are the largest copies of the run
+                vals = sorted(vals)[-5:]
+            res.setdefault(key, {})[cname] = dict(mean_kib=statistics.mean(vals) if vals else None,
+                                                  dispatches=len(vals))
+    copy_bytes = copy_mib * 1024 * 1024
+    f_copy = res["copy"]["FETCH_SIZE"]["mean_kib"] * 1024
+    w_copy = res["copy"]["WRITE_SIZE"]["mean_kib"] * 1024
+    scale_f, scale_w = copy_bytes / f_copy, copy_bytes / w_copy
+    kern = {}
+    for key in ("gateup", "down"):
+        f = res[key]["FETCH_SIZE"]["mean_kib"] * 1024 * scale_f
+        w = res[key]["WRITE_SIZE"]["mean_kib"] * 1024 * scale_w
+        kern[key] = dict(fetch_bytes=round(f), write_bytes=round(w), bytes_per_launch=round(f + w),
+                         dispatches=res[key]["FETCH_SIZE"]["dispatches"])
+    src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc", "ffn_mfma.hip")
+    rec = dict(kernel="ffn_gateup_mfma_kernel", workload="a3b T=32 (bench.py default)",
+               bytes_per_launch=kern["gateup"]["bytes_per_launch"], per_kernel=kern,
+               copy_calibration=dict(copy_bytes=copy_bytes, fetch_scale=round(scale_f, 4),
+                                     write_scale=round(scale_w, 4)),
+               source_sha256_16=source_hash(src),
+               command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir> -o run --output-format csv "
+                       "-- python3 bench.py --steps 20 --warmup 5 --sweep=none --no-cpu-baseline "
+                       f"--copy-calib-mib {copy_mib}")
+    path = os.path.join(ROOT, "profiles", "gateup_a3b_T32_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(mi, shape, layer0, T):
     """Oracle timed on one full layer step of weight set 0 (same inputs as the GPU)."""
     import numpy as np
@@ -184,6 +247,9 @@ def cpu_baseline(mi, shape, layer0, T):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.copy_calib_mib or 256)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -233,7 +299,7 @@ def main():
     log(f"[bench] {main_run['tokens_per_s']:.0f} tokens/s, gate/up {main_run['gateup_GBps']:.0f} GB/s")
 
     sweep = []
-    for tok in [int(t) for t in args.sweep.split(",") if t.strip()]:
+    for tok in [int(t) for t in args.sweep.split(",") if t.strip() and t.strip() != "none"]:
         if tok == args.tokens:
             continue
         m = measure(tok, max(args.steps // 2, 10), max(args.warmup // 2, 2))
@@ -248,6 +314,15 @@ def main():
                     kernel="ffn_gateup (gate/up matvec + SwiGLU)",
                     algorithmic_bytes_per_launch=round(main_run["gateup_bytes_per_launch"]),
                     mean_launch_us=round(main_run["gateup_us"], 3))
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

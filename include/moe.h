@@ -9,6 +9,7 @@
  *   3. looks up each picked expert in a resident-slot table  (moe_slot_lookup)
  *      and lists the experts that miss it
  *   4. groups the T*k (token, expert) pairs by expert        (moe_permute)
+ *      and writes the FFN's device work list
  *   5. runs each expert's quantised FFN on its tokens:       (moe_expert_ffn_q4 /
  *      gate/up matvec with fused group-wise dequant, SwiGLU,   moe_expert_ffn_q2)
  *      down matvec
@@ -84,6 +85,15 @@ extern "C" {
 #define MOE_ALGO_AUTO 0   /* choose per call from the shape */
 #define MOE_ALGO_GEMV 1   /* vector-ALU matvec, one pass over the weights per token tile */
 #define MOE_ALGO_MFMA 2   /* matrix-core tiles (bf16 MFMA with exact code operands) */
+
+/* FFN work list (written by moe_permute, read by the FFN calls): one entry per
+ * tile of up to MOE_WORK_TILE_ROWS consecutive sorted rows of one expert,
+ * expert-major in ascending expert order.  Entry = int32[MOE_WORK_ENTRY_INTS]:
+ *   [0] expert id   [1] first sorted row of the tile   [2] rows in the tile
+ *   [3] 0           [4 + j] token of row j (j < rows; slots past the tile's
+ *                   rows repeat the token of row 0) */
+#define MOE_WORK_TILE_ROWS 16
+#define MOE_WORK_ENTRY_INTS 20
 
 /* Operations for moe_workspace_bytes. */
 #define MOE_OP_ROUTE 0
@@ -174,33 +184,37 @@ int moe_slot_lookup(const moe_dims* dims, const int32_t* topk_ids, const int32_t
  *   pair_to_row    int32 [T*k]   inverse: sorted_pairs[pair_to_row[p]] == p
  *   active_experts int32 [E]     experts with count > 0, ascending, first
  *                                *n_active entries written
- *   n_active       int32 [1] */
+ *   n_active       int32 [1]
+ *   work_list      int32 [capacity][MOE_WORK_ENTRY_INTS], capacity from
+ *                  moe_work_list_capacity, 16-byte aligned; first *n_work
+ *                  entries written
+ *   n_work         int32 [1] */
 int moe_permute(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_counts,
                 int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_to_row,
-                int32_t* active_experts, int32_t* n_active, void* stream);
+                int32_t* active_experts, int32_t* n_active, int32_t* work_list, int32_t* n_work,
+                void* stream);
 
-/* Quantised expert FFN (step 5), 4-bit codes.  For every sorted row r with
- * pair p = sorted_pairs[r], token t = p / k and expert e (the expert whose
- * [offsets[e], offsets[e+1]) holds r):
+/* Entries the work list of these dims can need (host-only):
+ * min(E, T*k) + T*k / MOE_WORK_TILE_ROWS. */
+int moe_work_list_capacity(const moe_dims* dims, int32_t* entries);
+
+/* Quantised expert FFN (step 5), 4-bit codes.  For every sorted row r of
+ * expert e and token t (from the work list of moe_permute):
  *   a_i = sum_k Wg[e][i][k] x[t][k],  u_i = sum_k Wu[e][i][k] x[t][k]
  *   h_i = silu(a_i) * u_i                            (float32)
  *   y_rows[r][n] = bf16( sum_i Wd[e][n][i] h_i )     (round to nearest even)
- * Each expert's weights are read once per call for all of its tokens.
- * Inputs come from moe_permute; n_active is read on the device, so the call
- * never waits for routing results on the host.
+ * Each expert's weights are read once per call for all of its tokens (once per
+ * work-list tile of up to 16 tokens).  n_work is read on the device, so the
+ * call never waits for routing results on the host.
  * workspace: at least moe_workspace_bytes(dims, MOE_OP_FFN, 4, algo), 256-byte
  * aligned.  algo: MOE_ALGO_*. */
-int moe_expert_ffn_q4(const moe_dims* dims, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* expert_counts, const int32_t* expert_offsets,
-                      const int32_t* active_experts, const int32_t* n_active,
-                      const moe_qweights* weights, uint16_t* y_rows, int algo,
+int moe_expert_ffn_q4(const moe_dims* dims, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* weights, uint16_t* y_rows, int algo,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Same as moe_expert_ffn_q4 with 2-bit codes (Flash-MoE page, sec. 3). */
-int moe_expert_ffn_q2(const moe_dims* dims, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* expert_counts, const int32_t* expert_offsets,
-                      const int32_t* active_experts, const int32_t* n_active,
-                      const moe_qweights* weights, uint16_t* y_rows, int algo,
+int moe_expert_ffn_q2(const moe_dims* dims, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* weights, uint16_t* y_rows, int algo,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 5 in two halves (the scope rows "gate/up matvec + SwiGLU" and "down
@@ -215,17 +229,13 @@ int moe_expert_ffn_q2(const moe_dims* dims, const uint16_t* x, const int32_t* so
  *     of the matrix-core operands, followed by float32 partial sums of h over
  *     16 consecutive i [T*k][I/16].
  * moe_expert_ffn_q4/q2 == moe_expert_gateup followed by moe_expert_down. */
-int moe_expert_gateup(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* expert_counts, const int32_t* expert_offsets,
-                      const int32_t* active_experts, const int32_t* n_active,
-                      const moe_qweights* weights, int algo, void* workspace,
+int moe_expert_gateup(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* weights, int algo, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-int moe_expert_down(const moe_dims* dims, int bits, const int32_t* expert_counts,
-                    const int32_t* expert_offsets, const int32_t* active_experts,
-                    const int32_t* n_active, const moe_qweights* weights, int algo,
-                    const void* workspace, size_t workspace_bytes, uint16_t* y_rows,
-                    void* stream);
+int moe_expert_down(const moe_dims* dims, int bits, const int32_t* work_list, const int32_t* n_work,
+                    const moe_qweights* weights, int algo, const void* workspace,
+                    size_t workspace_bytes, uint16_t* y_rows, void* stream);
 
 /* Combine + residual (step 6; Flash-MoE page, sec. 3):
  *   acc = residual[t][n];  for j = 0..k-1 in order:

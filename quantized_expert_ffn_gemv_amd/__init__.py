@@ -26,7 +26,7 @@ OP_ROUTE, OP_LOOKUP, OP_PERMUTE, OP_FFN, OP_COMBINE = 0, 1, 2, 3, 4
 # entry points declared in include/moe.h
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
-    "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute",
+    "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute", "moe_work_list_capacity",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_combine",
 )
 
@@ -67,11 +67,12 @@ def lib() -> ctypes.CDLL:
     L.moe_route_topk.argtypes = [Dp, P, P, P, ctypes.c_int, P, P, P, P]
     L.moe_topk_from_logits.argtypes = [Dp, P, ctypes.c_int, P, P, P]
     L.moe_slot_lookup.argtypes = [Dp, P, P, i32, P, P, P, P, P, u32, P]
-    L.moe_permute.argtypes = [Dp, P, P, P, P, P, P, P, P]
+    L.moe_permute.argtypes = [Dp, P, P, P, P, P, P, P, P, P, P]
+    L.moe_work_list_capacity.argtypes = [Dp, ctypes.POINTER(i32)]
     for name in ("moe_expert_ffn_q4", "moe_expert_ffn_q2"):
-        getattr(L, name).argtypes = [Dp, P, P, P, P, P, P, Wp, P, ctypes.c_int, P, sz, P]
-    L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, P, P, P, Wp, ctypes.c_int, P, sz, P]
-    L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, P, P, Wp, ctypes.c_int, P, sz, P, P]
+        getattr(L, name).argtypes = [Dp, P, P, P, Wp, P, ctypes.c_int, P, sz, P]
+    L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P]
+    L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, Wp, ctypes.c_int, P, sz, P, P]
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = ctypes.c_int
@@ -156,55 +157,59 @@ def slot_lookup(d: Dims, topk_ids, slot_of_expert, n_slots: int, pair_slot, miss
                                  _ptr(last_use), int(step) & 0xFFFFFFFF, _stream(stream)))
 
 
+WORK_TILE_ROWS, WORK_ENTRY_INTS = 16, 20     # MOE_WORK_TILE_ROWS, MOE_WORK_ENTRY_INTS
+
+
+def work_list_capacity(d: Dims) -> int:
+    out = ctypes.c_int32(0)
+    _check(lib().moe_work_list_capacity(ctypes.byref(d), ctypes.byref(out)))
+    return int(out.value)
+
+
 def permute(d: Dims, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair_to_row,
-            active_experts, n_active, stream=None):
+            active_experts, n_active, work_list, n_work, stream=None):
     _check(lib().moe_permute(ctypes.byref(d), _ptr(topk_ids), _ptr(expert_counts), _ptr(expert_offsets),
                              _ptr(sorted_pairs), _ptr(pair_to_row), _ptr(active_experts), _ptr(n_active),
-                             _stream(stream)))
-
-
-def _ffn(fn, d, x, sorted_pairs, counts, offsets, active, n_active, weights: QWeights, y_rows,
-         algo, workspace, workspace_bytes_, stream):
-    w = weights.c_struct()
-    nbytes = workspace_bytes_ if workspace_bytes_ is not None else (
-        0 if workspace is None else workspace.numel() * workspace.element_size())
-    _check(fn(ctypes.byref(d), _ptr(x), _ptr(sorted_pairs), _ptr(counts), _ptr(offsets), _ptr(active),
-              _ptr(n_active), ctypes.byref(w), _ptr(y_rows), int(algo), _ptr(workspace), nbytes,
-              _stream(stream)))
-
-
-def expert_ffn_q4(d: Dims, x, sorted_pairs, expert_counts, expert_offsets, active_experts, n_active,
-                  weights: QWeights, y_rows, algo: int = ALGO_AUTO, workspace=None,
-                  workspace_bytes_: Optional[int] = None, stream=None):
-    _ffn(lib().moe_expert_ffn_q4, d, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
-         n_active, weights, y_rows, algo, workspace, workspace_bytes_, stream)
-
-
-def expert_ffn_q2(d: Dims, x, sorted_pairs, expert_counts, expert_offsets, active_experts, n_active,
-                  weights: QWeights, y_rows, algo: int = ALGO_AUTO, workspace=None,
-                  workspace_bytes_: Optional[int] = None, stream=None):
-    _ffn(lib().moe_expert_ffn_q2, d, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
-         n_active, weights, y_rows, algo, workspace, workspace_bytes_, stream)
+                             _ptr(work_list), _ptr(n_work), _stream(stream)))
 
 
 def _nbytes(t) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def expert_gateup(d: Dims, bits: int, x, sorted_pairs, expert_counts, expert_offsets, active_experts,
-                  n_active, weights: QWeights, workspace, algo: int = ALGO_AUTO, stream=None):
+def _ffn(fn, d, x, work_list, n_work, weights: QWeights, y_rows, algo, workspace, workspace_bytes_, stream):
     w = weights.c_struct()
-    _check(lib().moe_expert_gateup(ctypes.byref(d), int(bits), _ptr(x), _ptr(sorted_pairs), _ptr(expert_counts),
-                                   _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), ctypes.byref(w),
-                                   int(algo), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+    nbytes = workspace_bytes_ if workspace_bytes_ is not None else _nbytes(workspace)
+    _check(fn(ctypes.byref(d), _ptr(x), _ptr(work_list), _ptr(n_work), ctypes.byref(w), _ptr(y_rows),
+              int(algo), _ptr(workspace), nbytes, _stream(stream)))
 
 
-def expert_down(d: Dims, bits: int, expert_counts, expert_offsets, active_experts, n_active,
-                weights: QWeights, workspace, y_rows, algo: int = ALGO_AUTO, stream=None):
+def expert_ffn_q4(d: Dims, x, work_list, n_work, weights: QWeights, y_rows, algo: int = ALGO_AUTO,
+                  workspace=None, workspace_bytes_: Optional[int] = None, stream=None):
+    _ffn(lib().moe_expert_ffn_q4, d, x, work_list, n_work, weights, y_rows, algo, workspace,
+         workspace_bytes_, stream)
+
+
+def expert_ffn_q2(d: Dims, x, work_list, n_work, weights: QWeights, y_rows, algo: int = ALGO_AUTO,
+                  workspace=None, workspace_bytes_: Optional[int] = None, stream=None):
+    _ffn(lib().moe_expert_ffn_q2, d, x, work_list, n_work, weights, y_rows, algo, workspace,
+         workspace_bytes_, stream)
+
+
+def expert_gateup(d: Dims, bits: int, x, work_list, n_work, weights: QWeights, workspace,
+                  algo: int = ALGO_AUTO, stream=None):
     w = weights.c_struct()
-    _check(lib().moe_expert_down(ctypes.byref(d), int(bits), _ptr(expert_counts), _ptr(expert_offsets),
-                                 _ptr(active_experts), _ptr(n_active), ctypes.byref(w), int(algo),
-                                 _ptr(workspace), _nbytes(workspace), _ptr(y_rows), _stream(stream)))
+    _check(lib().moe_expert_gateup(ctypes.byref(d), int(bits), _ptr(x), _ptr(work_list), _ptr(n_work),
+                                   ctypes.byref(w), int(algo), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)))
+
+
+def expert_down(d: Dims, bits: int, work_list, n_work, weights: QWeights, workspace, y_rows,
+                algo: int = ALGO_AUTO, stream=None):
+    w = weights.c_struct()
+    _check(lib().moe_expert_down(ctypes.byref(d), int(bits), _ptr(work_list), _ptr(n_work), ctypes.byref(w),
+                                 int(algo), _ptr(workspace), _nbytes(workspace), _ptr(y_rows),
+                                 _stream(stream)))
 
 
 def combine(d: Dims, y_rows, pair_to_row, topk_w, residual, out, stream=None):
@@ -216,7 +221,8 @@ from .layer import LayerBuffers, layer_forward  # noqa: E402  (orchestration of 
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
-    "workspace_bytes", "route_topk", "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
+    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk",
+    "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
     "expert_ffn_q2", "expert_gateup", "expert_down", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
     "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

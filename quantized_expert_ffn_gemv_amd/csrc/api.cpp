@@ -58,10 +58,9 @@ int check_dims(const char* fn, const moe_dims* d, bool need_h, bool need_i) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// Checks shared by the FFN calls.  `mats` lists the weight matrices used.
-int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* counts,
-                   const int32_t* offsets, const int32_t* active, const int32_t* n_active,
-                   const moe_qweights* w, int algo, int m_begin, int m_end) {
+// Checks shared by the FFN calls.  Matrices [m_begin, m_end) of `w` are used.
+int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* work_list,
+                   const int32_t* n_work, const moe_qweights* w, int algo, int m_begin, int m_end) {
     int st = check_dims(fn, d, true, true);
     if (st) return st;
     if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED, "%s: bits = %d (2 or 4)", fn, bits);
@@ -69,10 +68,8 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* c
     if (algo != MOE_ALGO_AUTO && algo != MOE_ALGO_GEMV && algo != MOE_ALGO_MFMA)
         return fail(MOE_ERR_UNSUPPORTED, "%s: unknown algo %d", fn, algo);
     if (d->T == 0) return MOE_OK;
-    REQUIRE_PTR(counts, 4);
-    REQUIRE_PTR(offsets, 4);
-    REQUIRE_PTR(active, 4);
-    REQUIRE_PTR(n_active, 4);
+    REQUIRE_PTR(work_list, 16);
+    REQUIRE_PTR(n_work, 4);
     for (int m = m_begin; m < m_end; ++m) {
         if (!w->q[m] || !w->scale[m] || !w->bias[m])
             return fail(MOE_ERR_INVALID_ARG, "%s: weights matrix %d has a NULL pointer", fn, m);
@@ -84,18 +81,14 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* c
     return MOE_OK;
 }
 
-moe::FfnArgs ffn_args(const moe_dims* d, int bits, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
-                      const int32_t* n_active, const moe_qweights* w, float* h, uint16_t* y) {
+moe::FfnArgs ffn_args(const moe_dims* d, int bits, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* w, float* h, uint16_t* y) {
     moe::FfnArgs a{};
     a.d = *d;
     a.bits = bits;
     a.x = x;
-    a.sorted_pairs = sorted_pairs;
-    a.counts = counts;
-    a.offsets = offsets;
-    a.active = active;
-    a.n_active = n_active;
+    a.work = work_list;
+    a.n_work = n_work;
     a.w = *w;
     a.y = y;
     a.h = h;
@@ -112,19 +105,16 @@ int check_workspace(const char* fn, const moe_dims* d, int bits, int algo, const
 }
 
 int ffn_common(const char* fn, int bits, const moe_dims* d, const uint16_t* x,
-               const int32_t* sorted_pairs, const int32_t* counts, const int32_t* offsets,
-               const int32_t* active, const int32_t* n_active, const moe_qweights* w, uint16_t* y,
+               const int32_t* work_list, const int32_t* n_work, const moe_qweights* w, uint16_t* y,
                int algo, void* ws, size_t ws_bytes, void* stream) {
-    int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 0, 3);
+    int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 0, 3);
     if (st) return st;
     if (d->T == 0) return ok();
     REQUIRE_PTR(x, 16);
-    REQUIRE_PTR(sorted_pairs, 4);
     REQUIRE_PTR(y, 16);
     st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
     if (st) return st;
-    moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w,
-                              static_cast<float*>(ws), y);
+    moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), y);
     const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
     st = mfma ? moe::launch_gateup_mfma(a, as_stream(stream)) : moe::launch_gateup_gemv(a, as_stream(stream));
     if (!st) st = mfma ? moe::launch_down_mfma(a, as_stream(stream)) : moe::launch_down_gemv(a, as_stream(stream));
@@ -220,9 +210,18 @@ int moe_slot_lookup(const moe_dims* d, const int32_t* topk_ids, const int32_t* s
     return ok();
 }
 
+int moe_work_list_capacity(const moe_dims* d, int32_t* entries) {
+    const char* fn = "moe_work_list_capacity";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    if (entries == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: entries is NULL", fn);
+    *entries = (int32_t)moe::work_capacity(*d);
+    return ok();
+}
+
 int moe_permute(const moe_dims* d, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
                 int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
-                void* stream) {
+                int32_t* work_list, int32_t* n_work, void* stream) {
     const char* fn = "moe_permute";
     int st = check_dims(fn, d, false, false);
     if (st) return st;
@@ -230,64 +229,59 @@ int moe_permute(const moe_dims* d, const int32_t* topk_ids, int32_t* counts, int
     REQUIRE_PTR(offsets, 4);
     REQUIRE_PTR(active, 4);
     REQUIRE_PTR(n_active, 4);
+    REQUIRE_PTR(n_work, 4);
     if (d->T > 0) {
         REQUIRE_PTR(topk_ids, 4);
         REQUIRE_PTR(sorted_pairs, 4);
         REQUIRE_PTR(pair_to_row, 4);
+        REQUIRE_PTR(work_list, 16);
     }
     st = moe::launch_permute(*d, topk_ids, counts, offsets, sorted_pairs, pair_to_row, active,
-                             n_active, as_stream(stream));
+                             n_active, work_list, n_work, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }
 
-int moe_expert_ffn_q4(const moe_dims* d, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
-                      const int32_t* n_active, const moe_qweights* w, uint16_t* y, int algo,
-                      void* ws, size_t ws_bytes, void* stream) {
-    return ffn_common("moe_expert_ffn_q4", 4, d, x, sorted_pairs, counts, offsets, active, n_active,
-                      w, y, algo, ws, ws_bytes, stream);
-}
-
-int moe_expert_ffn_q2(const moe_dims* d, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
-                      const int32_t* n_active, const moe_qweights* w, uint16_t* y, int algo,
-                      void* ws, size_t ws_bytes, void* stream) {
-    return ffn_common("moe_expert_ffn_q2", 2, d, x, sorted_pairs, counts, offsets, active, n_active,
-                      w, y, algo, ws, ws_bytes, stream);
-}
-
-int moe_expert_gateup(const moe_dims* d, int bits, const uint16_t* x, const int32_t* sorted_pairs,
-                      const int32_t* counts, const int32_t* offsets, const int32_t* active,
-                      const int32_t* n_active, const moe_qweights* w, int algo, void* ws,
+int moe_expert_ffn_q4(const moe_dims* d, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* w, uint16_t* y, int algo, void* ws,
                       size_t ws_bytes, void* stream) {
+    return ffn_common("moe_expert_ffn_q4", 4, d, x, work_list, n_work, w, y, algo, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_q2(const moe_dims* d, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* w, uint16_t* y, int algo, void* ws,
+                      size_t ws_bytes, void* stream) {
+    return ffn_common("moe_expert_ffn_q2", 2, d, x, work_list, n_work, w, y, algo, ws, ws_bytes, stream);
+}
+
+int moe_expert_gateup(const moe_dims* d, int bits, const uint16_t* x, const int32_t* work_list,
+                      const int32_t* n_work, const moe_qweights* w, int algo, void* ws, size_t ws_bytes,
+                      void* stream) {
     const char* fn = "moe_expert_gateup";
-    int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 0, 2);
+    int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 0, 2);
     if (st) return st;
     if (d->T == 0) return ok();
     REQUIRE_PTR(x, 16);
-    REQUIRE_PTR(sorted_pairs, 4);
     st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
     if (st) return st;
-    moe::FfnArgs a = ffn_args(d, bits, x, sorted_pairs, counts, offsets, active, n_active, w,
-                              static_cast<float*>(ws), nullptr);
+    moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), nullptr);
     const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
     st = mfma ? moe::launch_gateup_mfma(a, as_stream(stream)) : moe::launch_gateup_gemv(a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }
 
-int moe_expert_down(const moe_dims* d, int bits, const int32_t* counts, const int32_t* offsets,
-                    const int32_t* active, const int32_t* n_active, const moe_qweights* w, int algo,
-                    const void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+int moe_expert_down(const moe_dims* d, int bits, const int32_t* work_list, const int32_t* n_work,
+                    const moe_qweights* w, int algo, const void* ws, size_t ws_bytes, uint16_t* y,
+                    void* stream) {
     const char* fn = "moe_expert_down";
-    int st = check_ffn_args(fn, d, bits, counts, offsets, active, n_active, w, algo, 2, 3);
+    int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 2, 3);
     if (st) return st;
     if (d->T == 0) return ok();
     REQUIRE_PTR(y, 16);
     st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
     if (st) return st;
-    moe::FfnArgs a = ffn_args(d, bits, nullptr, nullptr, counts, offsets, active, n_active, w,
+    moe::FfnArgs a = ffn_args(d, bits, nullptr, work_list, n_work, w,
                               static_cast<float*>(const_cast<void*>(ws)), y);
     const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
     st = mfma ? moe::launch_down_mfma(a, as_stream(stream)) : moe::launch_down_gemv(a, as_stream(stream));

@@ -10,6 +10,15 @@ namespace moe {
 
 constexpr int kWave = 64;
 constexpr int kGroup = 128;
+constexpr int kWorkRows = MOE_WORK_TILE_ROWS;      // rows per FFN work-list tile
+constexpr int kWorkInts = MOE_WORK_ENTRY_INTS;     // int32 per work-list entry
+
+// Entries a work list needs: sum over experts of ceil(count / kWorkRows), at
+// most min(E, T*k) + T*k / kWorkRows.
+inline long work_capacity(const moe_dims& d) {
+    const long P = (long)d.T * d.k;
+    return (d.E < P ? d.E : P) + P / kWorkRows;
+}
 
 // ---------------------------------------------------------------- formats
 
@@ -117,17 +126,14 @@ int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* tab
                        uint32_t* last_use, uint32_t step, hipStream_t s);
 int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
-                   hipStream_t s);
+                   int32_t* work, int32_t* n_work, hipStream_t s);
 
 struct FfnArgs {
     moe_dims d;
     int bits;
     const uint16_t* x;
-    const int32_t* sorted_pairs;
-    const int32_t* counts;
-    const int32_t* offsets;
-    const int32_t* active;
-    const int32_t* n_active;
+    const int32_t* work;       // work list (entries of kWorkInts int32)
+    const int32_t* n_work;     // number of entries (device)
     moe_qweights w;
     uint16_t* y;
     float* h;          // FFN workspace (layout depends on the algorithm)

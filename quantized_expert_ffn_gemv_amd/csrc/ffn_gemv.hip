@@ -7,9 +7,10 @@
 // input cache; sec. 2: weight = nibble*scale + bias with the FMA rewrite).
 // This is a fresh design for wave64 CDNA4:
 //
-//  * Work item = (active expert, block of output rows).  Items are pulled by a
-//    grid-stride loop over n_active * items_per_expert, with n_active read on
-//    the device, so the launch never depends on routing results.
+//  * Work item = (work-list tile of up to 16 rows of one expert, block of
+//    output rows).  Items are pulled by a grid-stride loop over
+//    n_work * items_per_expert, with n_work read on the device, so the launch
+//    never depends on routing results.
 //  * Each row of codes is read once per token tile with 16-byte loads; LG
 //    consecutive lanes cover one row (LG * 16 contiguous bytes per load), each
 //    lane group carries 4 rows so every activation fetch from LDS serves 4 rows.
@@ -34,11 +35,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct GemvParams {
     const uint16_t* x;
-    const int32_t* sorted_pairs;
-    const int32_t* counts;
-    const int32_t* offsets;
-    const int32_t* active;
-    const int32_t* n_active;
+    const int32_t* work;        // work list entries (kWorkInts int32 each)
+    const int32_t* n_work;
     const uint8_t* qa;  const uint16_t* sa;  const uint16_t* ba;   // gate, or down
     const uint8_t* qb;  const uint16_t* sb;  const uint16_t* bb;   // up (gate/up kernel only)
     float* h;
@@ -85,7 +83,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-__device__ __forceinline__ int clamp_pair(int p, int P) { return (p >= 0 && p < P) ? p : -1; }
+__device__ __forceinline__ int clamp_token(int t, int T) { return (t >= 0 && t < T) ? t : -1; }
 
 // --------------------------------------------------------------- gate / up
 // LDS: xs = bf16 activation pairs of the token tile, laid out
@@ -107,12 +105,12 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
     const int IB = 8 * RPW;
     const size_t rowbytes = (size_t)H * BITS / 8;
 
-    const int n_items = (*p.n_active) * p.items_per_expert;
+    const int n_items = (*p.n_work) * p.items_per_expert;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int a = item / p.items_per_expert, ib = item % p.items_per_expert;
-        const int e = p.active[a];
-        if (e < 0 || e >= p.E) continue;
-        const int cnt = p.counts[e], r0 = p.offsets[e];
+        const int wi = item / p.items_per_expert, ib = item % p.items_per_expert;
+        const int32_t* ent = p.work + (size_t)wi * kWorkInts;
+        const int e = ent[0], r0 = ent[1], cnt = ent[2];
+        if (e < 0 || e >= p.E || cnt < 1 || cnt > kWorkRows || r0 < 0 || r0 + cnt > P) continue;
         const int i0 = ib * IB + (wv * RPW + rs) * 2;
         const bool v0 = i0 < I, v1 = i0 + 1 < I;
         const uint8_t* qrow[4];
@@ -134,12 +132,12 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
                 const int t = idx / NC, c = idx % NC;
                 uint32_t in[CK / 2];
                 if (t < np) {
-                    const int pr = clamp_pair(p.sorted_pairs[r0 + tt + t], P);
-                    const int tok = pr < 0 ? 0 : pr / p.k;
+                    const int tk = clamp_token(ent[4 + tt + t], p.T);
+                    const int tok = tk < 0 ? 0 : tk;
                     const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * H + c * CK);
 #pragma unroll
                     for (int v = 0; v < CK / 8; ++v) {
-                        uint4 q = pr < 0 ? make_uint4(0, 0, 0, 0) : src[v];
+                        uint4 q = tk < 0 ? make_uint4(0, 0, 0, 0) : src[v];
                         in[4 * v] = q.x; in[4 * v + 1] = q.y; in[4 * v + 2] = q.z; in[4 * v + 3] = q.w;
                     }
                 } else {
@@ -278,12 +276,13 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
     const int NB = 16 * RPW;                // rows per item
     const size_t rowbytes = (size_t)I * BITS / 8;
 
-    const int n_items = (*p.n_active) * p.items_per_expert;
+    const int P = p.T * p.k;
+    const int n_items = (*p.n_work) * p.items_per_expert;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int a = item / p.items_per_expert, nb = item % p.items_per_expert;
-        const int e = p.active[a];
-        if (e < 0 || e >= p.E) continue;
-        const int cnt = p.counts[e], r0 = p.offsets[e];
+        const int wi = item / p.items_per_expert, nb = item % p.items_per_expert;
+        const int32_t* ent = p.work + (size_t)wi * kWorkInts;
+        const int e = ent[0], r0 = ent[1], cnt = ent[2];
+        if (e < 0 || e >= p.E || cnt < 1 || cnt > kWorkRows || r0 < 0 || r0 + cnt > P) continue;
         const int n0 = nb * NB + (wv * RPW + rs) * 4;
         const uint8_t* qrow[4];
         const uint16_t* srow[4];
@@ -419,16 +418,13 @@ template <int BITS>
 static GemvParams base_params(const FfnArgs& a) {
     const moe_dims& d = a.d;
     GemvParams p{};
-    p.x = a.x; p.sorted_pairs = a.sorted_pairs; p.counts = a.counts; p.offsets = a.offsets;
-    p.active = a.active; p.n_active = a.n_active; p.h = a.h; p.y = a.y;
+    p.x = a.x; p.work = a.work; p.n_work = a.n_work; p.h = a.h; p.y = a.y;
     p.T = d.T; p.H = d.H; p.I = d.I; p.k = d.k; p.E = d.E;
     return p;
 }
 
 static int grid_for(const moe_dims& d, int items_per_expert) {
-    const int P = d.T * d.k;
-    const long maxU = d.E < P ? d.E : P;
-    const long max_items = maxU * items_per_expert;
+    const long max_items = work_capacity(d) * items_per_expert;
     return (int)(max_items < 4096 ? max_items : 4096);
 }
 

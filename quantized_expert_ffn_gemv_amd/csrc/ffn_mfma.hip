@@ -29,6 +29,8 @@
 // Gate/up writes h = silu(a) * u as three bf16 planes hi + mid + lo (about 24
 // significant bits, i.e. float32 h) in the pair order the down kernel's B
 // operand needs, plus per-16-row partial sums of h for the down bias fold.
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -46,18 +48,15 @@ constexpr int kWaves = 4;
 
 struct MfmaParams {
     const uint16_t* x;
-    const int32_t* sorted_pairs;
-    const int32_t* counts;
-    const int32_t* offsets;
-    const int32_t* active;
-    const int32_t* n_active;
+    const int32_t* work;        // work list entries (kWorkInts int32 each)
+    const int32_t* n_work;
     const uint8_t* qa;  const uint16_t* sa;  const uint16_t* ba;   // gate, or down
     const uint8_t* qb;  const uint16_t* sb;  const uint16_t* bb;   // up
     uint16_t* hp;       // bf16 planes [3][P][I]
     float* hpart;       // [P][I/16] partial sums of h over 16-row tiles
     uint16_t* y;        // [P][H]
     int T, H, I, k, E, P;
-    int items_per_expert;
+    int items_per_entry;        // output blocks per work-list entry
 };
 
 __device__ __forceinline__ floatx4_t mfma16(const uint32_t (&a)[4], const uint32_t (&b)[4], floatx4_t c) {
@@ -138,150 +137,176 @@ __device__ __forceinline__ int pair_order_row(int m) {
 }
 
 // --------------------------------------------------------------- gate / up
-// LDS: [kWaves][NGW][4][16] float scales (per wave: s/L and b - (128/L) s of
-// gate, then of up, for the tile's 16 output rows), then [kWaves][64][8]
-// partial sums.  SJ = scale entries per lane per matrix (>= NGW / 4).
+// Persistent: workgroup b handles items b, b + G, b + 2G, ... (G = grid size)
+// of the n_work * (I / 16) items; an item is one work-list tile (<= 16 tokens
+// of one expert) times 16 output rows of gate and up.  Wave w streams its
+// quarter of the K groups; its D-deep prefetch ring runs across item
+// boundaries: during the last D groups of item j it already loads item j+1,
+// whose metadata, token ids and scales were fetched while item j computed.
+// LDS: [kWaves][2][NGW][4][16] float scales (double-buffered by item parity;
+// per wave: s/L and b - (128/L) s of gate, then up, for the 16 output rows),
+// then [kWaves][64][8] partial sums.  SJ = scale entries per lane per matrix.
+// D must divide the groups of every wave (the launcher guarantees it).
 template <int BITS, int D, int SJ>
 __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
     constexpr int LB = 128 * BITS / 8 / 4;     // bytes per lane per group (16 or 8)
     constexpr int LW = LB / 4;                 // code words per lane per group
     extern __shared__ float lds[];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
-    const int a = blockIdx.x / p.items_per_expert, it = blockIdx.x % p.items_per_expert;
-    if (a >= ld_scalar(p.n_active, 0)) return;
-    const int e = ld_scalar(p.active, a);
-    if (e < 0 || e >= p.E) return;
+    const int ipe = p.items_per_entry;
+    const int n_items = ld_scalar(p.n_work, 0) * ipe;
+    if ((int)blockIdx.x >= n_items) return;
+    const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
     const int H = p.H, I = p.I, NG = H / kGroup, NGW = (NG + kWaves - 1) / kWaves;
     int gb, ng;
     wave_groups(NG, w, gb, ng);
-    const int i0 = it * 16;
     const size_t rowbytes = (size_t)H * BITS / 8;
-    const size_t wrow = (size_t)e * I + i0 + pair_order_row<BITS>(m);   // this lane's weight row
-    const uint8_t* grow = p.qa + wrow * rowbytes + q * LB;
-    const uint8_t* urow = p.qb + wrow * rowbytes + q * LB;
-    const int cnt = ld_scalar(p.counts, e), r0 = ld_scalar(p.offsets, e);
-    float* my_sc = lds + w * NGW * 64;
-    float* red = lds + kWaves * NGW * 64;
+    float* sc_base = lds + w * 2 * NGW * 64;
+    float* red = lds + kWaves * 2 * NGW * 64;
     uint32_t ONE[4] = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
-    for (int t0 = 0; t0 < cnt; t0 += 16) {
-        const int n_tile = min(16, cnt - t0);
-        const bool tok_ok = m < n_tile;
-        floatx4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-
+    // ---- per-item state: uniform metadata + this lane's pointers and scales
+    struct Item {
+        int e, it, row0, n;
+        const uint8_t* g;
+        const uint8_t* u;
+        const uint16_t* x;
+        uint32_t sv[4][SJ];
+    };
+    auto fetch = [&](int j, Item& I_) {
+        const int idx = (int)blockIdx.x + j * (int)gridDim.x;
+        const int32_t* ent = p.work + (size_t)(idx / ipe) * kWorkInts;
+        I_.it = idx % ipe;
+        I_.e = ld_scalar(ent, 0);
+        I_.row0 = ld_scalar(ent, 1);
+        I_.n = ld_scalar(ent, 2);
+        int tok = ld_scalar(ent, 4);
+#pragma unroll
+        for (int jj = 1; jj < kWorkRows; ++jj) {
+            const int v = ld_scalar(ent, 4 + jj);
+            tok = (m == jj) ? v : tok;
+        }
+        const int e = (I_.e >= 0 && I_.e < p.E) ? I_.e : 0;
+        tok = (tok >= 0 && tok < p.T) ? tok : 0;
+        const size_t wrow = (size_t)e * I + I_.it * 16 + pair_order_row<BITS>(m);
+        I_.g = p.qa + wrow * rowbytes + q * LB;
+        I_.u = p.qb + wrow * rowbytes + q * LB;
+        I_.x = p.x + (size_t)tok * H + q * 32;
         if (ng > 0) {
-            // 1. scales of this wave's groups (oldest loads: waiting for them
-            //    does not wait for the code stream issued after them)
-            uint32_t sv[4][SJ];
-            if (t0 == 0) {
 #pragma unroll
-                for (int j = 0; j < SJ; ++j) {
-                    const int idx = lane + 64 * j;
-                    const int gl = min(idx >> 4, ng - 1), r = idx & 15;
-                    const size_t src = ((size_t)e * I + i0 + pair_order_row<BITS>(r)) * NG + gb + gl;
-                    sv[0][j] = p.sa[src]; sv[1][j] = p.ba[src];
-                    sv[2][j] = p.sb[src]; sv[3][j] = p.bb[src];
-                }
-            }
-            // 2. the code stream
-            uint32_t wg[D][LW], wu[D][LW], xv[D][16];
-            auto issue_codes = [&](int slot, int g) {
-                if constexpr (BITS == 4) {
-                    const uint4 A = *reinterpret_cast<const uint4*>(grow + (size_t)g * 64);
-                    const uint4 B = *reinterpret_cast<const uint4*>(urow + (size_t)g * 64);
-                    wg[slot][0] = A.x; wg[slot][1] = A.y; wg[slot][2] = A.z; wg[slot][3] = A.w;
-                    wu[slot][0] = B.x; wu[slot][1] = B.y; wu[slot][2] = B.z; wu[slot][3] = B.w;
-                } else {
-                    const uint2 A = *reinterpret_cast<const uint2*>(grow + (size_t)g * 32);
-                    const uint2 B = *reinterpret_cast<const uint2*>(urow + (size_t)g * 32);
-                    wg[slot][0] = A.x; wg[slot][1] = A.y;
-                    wu[slot][0] = B.x; wu[slot][1] = B.y;
-                }
-            };
-#pragma unroll
-            for (int d = 0; d < D; ++d) issue_codes(d, gb + min(d, ng - 1));
-
-            // 3. token of this lane's column from scalar loads (columns past the
-            //    tile's end reuse the first token; their outputs are never written)
-            int pr = ld_scalar(p.sorted_pairs, r0 + t0);
-#pragma unroll
-            for (int j = 1; j < 16; ++j) {
-                const int v = ld_scalar(p.sorted_pairs, r0 + t0 + min(j, n_tile - 1));
-                pr = (m == j && j < n_tile) ? v : pr;
-            }
-            const int tok = (pr >= 0 && pr < p.P) ? pr / p.k : 0;
-            const uint16_t* xrow = p.x + (size_t)tok * H + q * 32;
-            auto issue_act = [&](int slot, int g) {
-                const uint4* xs = reinterpret_cast<const uint4*>(xrow + (size_t)g * kGroup);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint4 X = xs[v];
-                    xv[slot][4 * v] = X.x; xv[slot][4 * v + 1] = X.y;
-                    xv[slot][4 * v + 2] = X.z; xv[slot][4 * v + 3] = X.w;
-                }
-            };
-#pragma unroll
-            for (int d = 0; d < D; ++d) issue_act(d, gb + min(d, ng - 1));
-
-            // 4. scales -> LDS, converted once: s/L and b - (128/L) s
-            if (t0 == 0) {
-#pragma unroll
-                for (int j = 0; j < SJ; ++j) {
-                    const int idx = lane + 64 * j;
-                    const int gl = idx >> 4, r = idx & 15;
-                    if (gl < ng) {
-                        const float s1 = f16_bits_to_f32(sv[0][j]), b1 = f16_bits_to_f32(sv[1][j]);
-                        const float s2 = f16_bits_to_f32(sv[2][j]), b2 = f16_bits_to_f32(sv[3][j]);
-                        float* dst = my_sc + gl * 64 + r;
-                        dst[0] = s1 * kInvLever<BITS>;
-                        dst[16] = fmaf(-kOffset<BITS>, s1, b1);
-                        dst[32] = s2 * kInvLever<BITS>;
-                        dst[48] = fmaf(-kOffset<BITS>, s2, b2);
-                    }
-                }
-            }
-
-            for (int g0 = 0; g0 < ng; g0 += D) {
-#pragma unroll
-                for (int d = 0; d < D; ++d) {
-                    const int gl = g0 + d;
-                    uint32_t cw[LW], cu[LW], cx[16];
-#pragma unroll
-                    for (int v = 0; v < LW; ++v) { cw[v] = wg[d][v]; cu[v] = wu[d][v]; }
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) cx[v] = xv[d][v];
-                    const int gn = gb + min(gl + D, ng - 1);   // past the end: a harmless reload
-                    issue_codes(d, gn);
-                    issue_act(d, gn);
-                    if (gl < ng) {
-                        floatx4_t Cg = {0.f, 0.f, 0.f, 0.f}, Cu = Cg, Cx = Cg;
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            uint32_t Ag[4], Au[4], Bx[4];
-                            code_operand<BITS>(cw, s, Ag);
-                            code_operand<BITS>(cu, s, Au);
-                            act_operand<BITS>(cx, s, Bx);
-                            Cg = mfma16(Ag, Bx, Cg);
-                            Cu = mfma16(Au, Bx, Cu);
-                            Cx = mfma16(ONE, Bx, Cx);
-                        }
-                        const float* scg = my_sc + gl * 64 + 4 * q;
-                        const float4 sg = *reinterpret_cast<const float4*>(scg);
-                        const float4 bg = *reinterpret_cast<const float4*>(scg + 16);
-                        const float4 su = *reinterpret_cast<const float4*>(scg + 32);
-                        const float4 bu = *reinterpret_cast<const float4*>(scg + 48);
-                        accg[0] = fmaf(sg.x, Cg[0], fmaf(bg.x, Cx[0], accg[0]));
-                        accg[1] = fmaf(sg.y, Cg[1], fmaf(bg.y, Cx[1], accg[1]));
-                        accg[2] = fmaf(sg.z, Cg[2], fmaf(bg.z, Cx[2], accg[2]));
-                        accg[3] = fmaf(sg.w, Cg[3], fmaf(bg.w, Cx[3], accg[3]));
-                        accu[0] = fmaf(su.x, Cu[0], fmaf(bu.x, Cx[0], accu[0]));
-                        accu[1] = fmaf(su.y, Cu[1], fmaf(bu.y, Cx[1], accu[1]));
-                        accu[2] = fmaf(su.z, Cu[2], fmaf(bu.z, Cx[2], accu[2]));
-                        accu[3] = fmaf(su.w, Cu[3], fmaf(bu.w, Cx[3], accu[3]));
-                    }
-                }
+            for (int jj = 0; jj < SJ; ++jj) {
+                const int id2 = lane + 64 * jj;
+                const int gl = min(id2 >> 4, ng - 1), r = id2 & 15;
+                const size_t src = ((size_t)e * I + I_.it * 16 + pair_order_row<BITS>(r)) * NG + gb + gl;
+                I_.sv[0][jj] = p.sa[src]; I_.sv[1][jj] = p.ba[src];
+                I_.sv[2][jj] = p.sb[src]; I_.sv[3][jj] = p.bb[src];
             }
         }
+    };
+    auto stage = [&](const Item& I_, float* dst_base) {
+#pragma unroll
+        for (int jj = 0; jj < SJ; ++jj) {
+            const int id2 = lane + 64 * jj;
+            const int gl = id2 >> 4, r = id2 & 15;
+            if (gl < ng) {
+                const float s1 = f16_bits_to_f32(I_.sv[0][jj]), b1 = f16_bits_to_f32(I_.sv[1][jj]);
+                const float s2 = f16_bits_to_f32(I_.sv[2][jj]), b2 = f16_bits_to_f32(I_.sv[3][jj]);
+                float* dst = dst_base + gl * 64 + r;
+                dst[0] = s1 * kInvLever<BITS>;
+                dst[16] = fmaf(-kOffset<BITS>, s1, b1);
+                dst[32] = s2 * kInvLever<BITS>;
+                dst[48] = fmaf(-kOffset<BITS>, s2, b2);
+            }
+        }
+    };
+
+    uint32_t wg[D][LW], wu[D][LW], xv[D][16];
+    auto issue = [&](int slot, const uint8_t* gp, const uint8_t* up, const uint16_t* xp, int g) {
+        if constexpr (BITS == 4) {
+            const uint4 A = *reinterpret_cast<const uint4*>(gp + (size_t)g * 64);
+            const uint4 B = *reinterpret_cast<const uint4*>(up + (size_t)g * 64);
+            wg[slot][0] = A.x; wg[slot][1] = A.y; wg[slot][2] = A.z; wg[slot][3] = A.w;
+            wu[slot][0] = B.x; wu[slot][1] = B.y; wu[slot][2] = B.z; wu[slot][3] = B.w;
+        } else {
+            const uint2 A = *reinterpret_cast<const uint2*>(gp + (size_t)g * 32);
+            const uint2 B = *reinterpret_cast<const uint2*>(up + (size_t)g * 32);
+            wg[slot][0] = A.x; wg[slot][1] = A.y;
+            wu[slot][0] = B.x; wu[slot][1] = B.y;
+        }
+        const uint4* xs = reinterpret_cast<const uint4*>(xp + (size_t)g * kGroup);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint4 X = xs[v];
+            xv[slot][4 * v] = X.x; xv[slot][4 * v + 1] = X.y;
+            xv[slot][4 * v + 2] = X.z; xv[slot][4 * v + 3] = X.w;
+        }
+    };
+
+    Item cur, nxt;
+    fetch(0, cur);
+    // every wave walks NGP = NGW rounded up to D ring steps; steps past its own
+    // ng groups reload its last group (or group gb) and skip the math
+    const int NGP = (NGW + D - 1) / D * D;
+    auto gaddr = [&](int gl) { return gb + max(0, min(gl, ng - 1)); };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, cur.g, cur.u, cur.x, gaddr(d));
+    stage(cur, sc_base);
+
+    for (int j = 0; j < n_my; ++j) {
+        const bool has_next = j + 1 < n_my;
+        if (has_next) fetch(j + 1, nxt);
+        else nxt = cur;
+        const float* my_sc = sc_base + (j & 1) * NGW * 64;
+        floatx4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+
+        // do-while: the body runs at least once (NGP >= D), so the loads of the next
+        // item's scales are always followed by ring refills and the wait before
+        // staging them leaves the refills in flight
+        int g0 = 0;
+        do {
+            const bool last = g0 + D >= NGP;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int gl = g0 + d;
+                // consume slot d, then refill the same registers: the old and new
+                // contents are never live together, so the ring needs no register
+                // copies (which would wait for the refill) at the block's end
+                if (gl < ng) {
+                    floatx4_t Cg = {0.f, 0.f, 0.f, 0.f}, Cu = Cg, Cx = Cg;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        uint32_t Ag[4], Au[4], Bx[4];
+                        code_operand<BITS>(wg[d], s, Ag);
+                        code_operand<BITS>(wu[d], s, Au);
+                        act_operand<BITS>(xv[d], s, Bx);
+                        Cg = mfma16(Ag, Bx, Cg);
+                        Cu = mfma16(Au, Bx, Cu);
+                        Cx = mfma16(ONE, Bx, Cx);
+                    }
+                    const float* scg = my_sc + gl * 64 + 4 * q;
+                    const float4 sg = *reinterpret_cast<const float4*>(scg);
+                    const float4 bg = *reinterpret_cast<const float4*>(scg + 16);
+                    const float4 su = *reinterpret_cast<const float4*>(scg + 32);
+                    const float4 bu = *reinterpret_cast<const float4*>(scg + 48);
+                    accg[0] = fmaf(sg.x, Cg[0], fmaf(bg.x, Cx[0], accg[0]));
+                    accg[1] = fmaf(sg.y, Cg[1], fmaf(bg.y, Cx[1], accg[1]));
+                    accg[2] = fmaf(sg.z, Cg[2], fmaf(bg.z, Cx[2], accg[2]));
+                    accg[3] = fmaf(sg.w, Cg[3], fmaf(bg.w, Cx[3], accg[3]));
+                    accu[0] = fmaf(su.x, Cu[0], fmaf(bu.x, Cx[0], accu[0]));
+                    accu[1] = fmaf(su.y, Cu[1], fmaf(bu.y, Cx[1], accu[1]));
+                    accu[2] = fmaf(su.z, Cu[2], fmaf(bu.z, Cx[2], accu[2]));
+                    accu[3] = fmaf(su.w, Cu[3], fmaf(bu.w, Cx[3], accu[3]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // refill: same item D groups on, else the next item's group at
+                // the same ring position (the last item reloads its own last
+                // group: harmless, keeps every step's loads alike)
+                const bool go_next = last && has_next;
+                issue(d, go_next ? nxt.g : cur.g, go_next ? nxt.u : cur.u, go_next ? nxt.x : cur.x,
+                      gaddr(!last ? gl + D : (has_next ? d : ng - 1)));
+            }
+            g0 += D;
+        } while (g0 < NGP);
 
         // ---- sum the 4 waves' partials (fixed order), epilogue in wave 0
         float* mine = red + (w * 64 + lane) * 8;
@@ -294,17 +319,18 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
             for (int i = 0; i < 4; ++i) {
                 const float gt = ((red[(0 * 64 + lane) * 8 + i] + red[(1 * 64 + lane) * 8 + i]) +
                                   red[(2 * 64 + lane) * 8 + i]) + red[(3 * 64 + lane) * 8 + i];
-                const float up = ((red[(0 * 64 + lane) * 8 + 4 + i] + red[(1 * 64 + lane) * 8 + 4 + i]) +
-                                  red[(2 * 64 + lane) * 8 + 4 + i]) + red[(3 * 64 + lane) * 8 + 4 + i];
-                hv[i] = gt / (1.f + expf(-gt)) * up;
+                const float upv = ((red[(0 * 64 + lane) * 8 + 4 + i] + red[(1 * 64 + lane) * 8 + 4 + i]) +
+                                   red[(2 * 64 + lane) * 8 + 4 + i]) + red[(3 * 64 + lane) * 8 + 4 + i];
+                hv[i] = gt / (1.f + expf(-gt)) * upv;
             }
             // sum of h over the tile's 16 rows for this token (fixed order)
             float part = (hv[0] + hv[1]) + (hv[2] + hv[3]);
             part += __shfl_xor(part, 16, kWave);
             part += __shfl_xor(part, 32, kWave);
-            if (tok_ok) {
-                const int r = r0 + t0 + m;
-                if (q == 0) p.hpart[(size_t)r * (I / 16) + it] = part;
+            if (m < cur.n && cur.row0 >= 0 && cur.row0 + cur.n <= p.P) {
+                const int r = cur.row0 + m;
+                const int i0 = cur.it * 16;
+                if (q == 0) p.hpart[(size_t)r * (I / 16) + cur.it] = part;
                 // positions 4q..4q+3 of the tile in all three planes
                 uint32_t hi[4], mid[4], lo[4];
 #pragma unroll
@@ -316,150 +342,193 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
                 *reinterpret_cast<uint2*>(base + 2 * plane) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
             }
         }
-        __syncthreads();   // red is reused by the next pass
+        __syncthreads();   // red is reused by the next item
+        if (has_next) stage(nxt, sc_base + ((j + 1) & 1) * NGW * 64);
+        cur = nxt;
     }
 }
 
 // ------------------------------------------------------------------- down
-// Output block: 2 tiles of 16 rows of one expert.  B operand = the three bf16
+// Persistent like gate/up.  The 4 waves form 4/KS row tiles of 32 output rows
+// times KS parts of K: with a short K (I / 128 small) each wave keeps several
+// groups to stream, so its ring has something to prefetch.  An item is one
+// work-list tile times 32 * 4/KS output rows.  B operand = the three bf16
 // planes of h (already in pair order), three MFMAs per step; the bias term
-// uses the per-16-row partial sums of h.  LDS: [kWaves][NGW][2][32] float
-// scales (s/L, b - (128/L) s), then [kWaves][64][8] partial sums.
-template <int BITS, int D>
+// uses the per-16-row partial sums of h.
+// LDS: [kWaves][2][NGW][2][32] float scales (s/L, b - (128/L) s) by item
+// parity, then [kWaves][64][8] partial sums.
+template <int BITS, int D, int SJ, int KS>
 __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaParams p) {
     constexpr int LB = 128 * BITS / 8 / 4;
     constexpr int LW = LB / 4;
     extern __shared__ float lds[];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
-    const int a = blockIdx.x / p.items_per_expert, nt = blockIdx.x % p.items_per_expert;
-    if (a >= *p.n_active) return;
-    const int e = p.active[a];
-    if (e < 0 || e >= p.E) return;
-    const int H = p.H, I = p.I, NG = I / kGroup, NGW = (NG + kWaves - 1) / kWaves;
-    int gb, ng;
-    wave_groups(NG, w, gb, ng);
-    const int n0 = nt * 32;
+    const int ipe = p.items_per_entry;
+    const int n_items = ld_scalar(p.n_work, 0) * ipe;
+    if ((int)blockIdx.x >= n_items) return;
+    const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+    constexpr int RT = kWaves / KS;            // row tiles per item
+    const int tw = w / KS, kp = w % KS;        // this wave's row tile and K part
+    const int H = p.H, I = p.I, NG = I / kGroup, NGW = (NG + KS - 1) / KS;
+    const int gb = (kp * NG) / KS, ng = ((kp + 1) * NG) / KS - gb;
     const size_t rowbytes = (size_t)I * BITS / 8;
-    const uint8_t* row0 = p.qa + ((size_t)e * H + n0 + m) * rowbytes + q * LB;
-    const uint8_t* row1 = row0 + 16 * rowbytes;
-    const int cnt = p.counts[e], r0 = p.offsets[e];
-    float* my_sc = lds + w * NGW * 64;
-    float* red = lds + kWaves * NGW * 64;
+    float* sc_base = lds + w * 2 * NGW * 64;
+    float* red = lds + kWaves * 2 * NGW * 64;
     const size_t plane = (size_t)p.P * I;
 
-    for (int t0 = 0; t0 < cnt; t0 += 16) {
-        const bool tok_ok = t0 + m < cnt;
-        floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    struct Item {
+        int e, it, row0, n;
+        const uint8_t* c0;
+        const uint16_t* h;
+        const float* part;
+        uint32_t sv[2][SJ];
+    };
+    auto fetch = [&](int j, Item& I_) {
+        const int idx = (int)blockIdx.x + j * (int)gridDim.x;
+        const int32_t* ent = p.work + (size_t)(idx / ipe) * kWorkInts;
+        I_.it = idx % ipe;
+        I_.e = ld_scalar(ent, 0);
+        I_.row0 = ld_scalar(ent, 1);
+        I_.n = ld_scalar(ent, 2);
+        const int e = (I_.e >= 0 && I_.e < p.E) ? I_.e : 0;
+        const bool ok_rows = I_.row0 >= 0 && I_.n >= 1 && I_.n <= kWorkRows && I_.row0 + I_.n <= p.P;
+        const int r = ok_rows ? I_.row0 + (m < I_.n ? m : 0) : 0;   // empty columns reuse row 0
+        const int n0 = (I_.it * RT + tw) * 32;
+        I_.c0 = p.qa + ((size_t)e * H + n0 + m) * rowbytes + q * LB;
+        I_.h = p.hp + (size_t)r * I + q * 32;
+        I_.part = p.hpart + (size_t)r * (I / 16);
         if (ng > 0) {
-            const int r = r0 + t0 + (tok_ok ? m : 0);      // empty columns reuse a valid row
-            const uint16_t* hrow = p.hp + (size_t)r * I + q * 32;
-            const float* prow = p.hpart + (size_t)r * (I / 16);
-            uint32_t w0[D][LW], w1[D][LW], hv[D][3][16];
-            float4 hp0[D], hp1[D];
-            auto issue_codes = [&](int slot, int g) {
-                if constexpr (BITS == 4) {
-                    const uint4 A = *reinterpret_cast<const uint4*>(row0 + (size_t)g * 64);
-                    const uint4 B = *reinterpret_cast<const uint4*>(row1 + (size_t)g * 64);
-                    w0[slot][0] = A.x; w0[slot][1] = A.y; w0[slot][2] = A.z; w0[slot][3] = A.w;
-                    w1[slot][0] = B.x; w1[slot][1] = B.y; w1[slot][2] = B.z; w1[slot][3] = B.w;
-                } else {
-                    const uint2 A = *reinterpret_cast<const uint2*>(row0 + (size_t)g * 32);
-                    const uint2 B = *reinterpret_cast<const uint2*>(row1 + (size_t)g * 32);
-                    w0[slot][0] = A.x; w0[slot][1] = A.y;
-                    w1[slot][0] = B.x; w1[slot][1] = B.y;
-                }
-            };
-            auto issue_act = [&](int slot, int g) {
 #pragma unroll
-                for (int pl = 0; pl < 3; ++pl) {
-                    const uint4* src = reinterpret_cast<const uint4*>(hrow + pl * plane + (size_t)g * kGroup);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const uint4 X = src[v];
-                        hv[slot][pl][4 * v] = X.x; hv[slot][pl][4 * v + 1] = X.y;
-                        hv[slot][pl][4 * v + 2] = X.z; hv[slot][pl][4 * v + 3] = X.w;
-                    }
-                }
-                hp0[slot] = *reinterpret_cast<const float4*>(prow + 8 * g);
-                hp1[slot] = *reinterpret_cast<const float4*>(prow + 8 * g + 4);
-            };
-#pragma unroll
-            for (int d = 0; d < D; ++d) issue_codes(d, gb + min(d, ng - 1));
-            if (t0 == 0) {
-                const size_t rb = ((size_t)e * H + n0) * NG + gb;
-                for (int idx = lane; idx < ng * 32; idx += 64) {
-                    const int gl = idx >> 5, rr = idx & 31;
-                    const size_t src = rb + (size_t)rr * NG + gl;
-                    const float sv = f16_bits_to_f32(p.sa[src]), bv = f16_bits_to_f32(p.ba[src]);
-                    my_sc[gl * 64 + rr] = sv * kInvLever<BITS>;
-                    my_sc[gl * 64 + 32 + rr] = fmaf(-kOffset<BITS>, sv, bv);
-                }
-            }
-#pragma unroll
-            for (int d = 0; d < D; ++d) issue_act(d, gb + min(d, ng - 1));
-
-            for (int g0 = 0; g0 < ng; g0 += D) {
-#pragma unroll
-                for (int d = 0; d < D; ++d) {
-                    const int gl = g0 + d;
-                    uint32_t c0[LW], c1[LW], ch[3][16];
-#pragma unroll
-                    for (int v = 0; v < LW; ++v) { c0[v] = w0[d][v]; c1[v] = w1[d][v]; }
-#pragma unroll
-                    for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) ch[pl][v] = hv[d][pl][v];
-                    const float4 q0 = hp0[d], q1 = hp1[d];
-                    const int gn = gb + min(gl + D, ng - 1);
-                    issue_codes(d, gn);
-                    issue_act(d, gn);
-                    if (gl < ng) {
-                        // sum of this lane's token's h over the group (8 partial sums)
-                        const float Hs = ((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w));
-                        floatx4_t C0 = {0.f, 0.f, 0.f, 0.f}, C1 = C0;
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            uint32_t A0[4], A1[4];
-                            code_operand<BITS>(c0, s, A0);
-                            code_operand<BITS>(c1, s, A1);
-#pragma unroll
-                            for (int pl = 0; pl < 3; ++pl) {
-                                // planes are stored in pair order: step s = words 4s..4s+3
-                                const uint32_t Bh[4] = {ch[pl][4 * s], ch[pl][4 * s + 1], ch[pl][4 * s + 2],
-                                                        ch[pl][4 * s + 3]};
-                                C0 = mfma16(A0, Bh, C0);
-                                C1 = mfma16(A1, Bh, C1);
-                            }
-                        }
-                        const float* scg = my_sc + gl * 64 + 4 * q;
-                        const float4 s0 = *reinterpret_cast<const float4*>(scg);
-                        const float4 s1 = *reinterpret_cast<const float4*>(scg + 16);
-                        const float4 b0 = *reinterpret_cast<const float4*>(scg + 32);
-                        const float4 b1 = *reinterpret_cast<const float4*>(scg + 48);
-                        // C = sum (128 + L q) h  ->  (s/L) C + (b - (128/L) s) Hsum
-                        acc0[0] = fmaf(s0.x, C0[0], fmaf(b0.x, Hs, acc0[0]));
-                        acc0[1] = fmaf(s0.y, C0[1], fmaf(b0.y, Hs, acc0[1]));
-                        acc0[2] = fmaf(s0.z, C0[2], fmaf(b0.z, Hs, acc0[2]));
-                        acc0[3] = fmaf(s0.w, C0[3], fmaf(b0.w, Hs, acc0[3]));
-                        acc1[0] = fmaf(s1.x, C1[0], fmaf(b1.x, Hs, acc1[0]));
-                        acc1[1] = fmaf(s1.y, C1[1], fmaf(b1.y, Hs, acc1[1]));
-                        acc1[2] = fmaf(s1.z, C1[2], fmaf(b1.z, Hs, acc1[2]));
-                        acc1[3] = fmaf(s1.w, C1[3], fmaf(b1.w, Hs, acc1[3]));
-                    }
-                }
+            for (int jj = 0; jj < SJ; ++jj) {
+                const int id2 = lane + 64 * jj;
+                const int gl = min(id2 >> 5, ng - 1), rr = id2 & 31;
+                const size_t src = ((size_t)e * H + n0 + rr) * NG + gb + gl;
+                I_.sv[0][jj] = p.sa[src]; I_.sv[1][jj] = p.ba[src];
             }
         }
+    };
+    auto stage = [&](const Item& I_, float* dst_base) {
+#pragma unroll
+        for (int jj = 0; jj < SJ; ++jj) {
+            const int id2 = lane + 64 * jj;
+            const int gl = id2 >> 5, rr = id2 & 31;
+            if (gl < ng) {
+                const float sv = f16_bits_to_f32(I_.sv[0][jj]), bv = f16_bits_to_f32(I_.sv[1][jj]);
+                dst_base[gl * 64 + rr] = sv * kInvLever<BITS>;
+                dst_base[gl * 64 + 32 + rr] = fmaf(-kOffset<BITS>, sv, bv);
+            }
+        }
+    };
+
+    uint32_t w0[D][LW], w1[D][LW], hv[D][3][16];
+    float4 hp0[D], hp1[D];
+    auto issue = [&](int slot, const uint8_t* cp, const uint16_t* hpp, const float* pp, int g) {
+        if constexpr (BITS == 4) {
+            const uint4 A = *reinterpret_cast<const uint4*>(cp + (size_t)g * 64);
+            const uint4 B = *reinterpret_cast<const uint4*>(cp + 16 * rowbytes + (size_t)g * 64);
+            w0[slot][0] = A.x; w0[slot][1] = A.y; w0[slot][2] = A.z; w0[slot][3] = A.w;
+            w1[slot][0] = B.x; w1[slot][1] = B.y; w1[slot][2] = B.z; w1[slot][3] = B.w;
+        } else {
+            const uint2 A = *reinterpret_cast<const uint2*>(cp + (size_t)g * 32);
+            const uint2 B = *reinterpret_cast<const uint2*>(cp + 16 * rowbytes + (size_t)g * 32);
+            w0[slot][0] = A.x; w0[slot][1] = A.y;
+            w1[slot][0] = B.x; w1[slot][1] = B.y;
+        }
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) {
+            const uint4* src = reinterpret_cast<const uint4*>(hpp + pl * plane + (size_t)g * kGroup);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 X = src[v];
+                hv[slot][pl][4 * v] = X.x; hv[slot][pl][4 * v + 1] = X.y;
+                hv[slot][pl][4 * v + 2] = X.z; hv[slot][pl][4 * v + 3] = X.w;
+            }
+        }
+        hp0[slot] = *reinterpret_cast<const float4*>(pp + 8 * g);
+        hp1[slot] = *reinterpret_cast<const float4*>(pp + 8 * g + 4);
+    };
+
+    Item cur, nxt;
+    fetch(0, cur);
+    const int NGP = (NGW + D - 1) / D * D;
+    auto gaddr = [&](int gl) { return gb + max(0, min(gl, ng - 1)); };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, cur.c0, cur.h, cur.part, gaddr(d));
+    stage(cur, sc_base);
+
+    for (int j = 0; j < n_my; ++j) {
+        const bool has_next = j + 1 < n_my;
+        if (has_next) fetch(j + 1, nxt);
+        else nxt = cur;
+        const float* my_sc = sc_base + (j & 1) * NGW * 64;
+        floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+
+        // do-while: the body runs at least once (NGP >= D), so the loads of the next
+        // item's scales are always followed by ring refills and the wait before
+        // staging them leaves the refills in flight
+        int g0 = 0;
+        do {
+            const bool last = g0 + D >= NGP;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int gl = g0 + d;
+                // consume slot d, then refill it (see the gate/up kernel)
+                if (gl < ng) {
+                    // sum of this lane's token's h over group g (8 partial sums)
+                    const float Hs = ((hp0[d].x + hp0[d].y) + (hp0[d].z + hp0[d].w)) +
+                                     ((hp1[d].x + hp1[d].y) + (hp1[d].z + hp1[d].w));
+                    floatx4_t C0 = {0.f, 0.f, 0.f, 0.f}, C1 = C0;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        uint32_t A0[4], A1[4];
+                        code_operand<BITS>(w0[d], s, A0);
+                        code_operand<BITS>(w1[d], s, A1);
+#pragma unroll
+                        for (int pl = 0; pl < 3; ++pl) {
+                            // planes are stored in pair order: step s = words 4s..4s+3
+                            const uint32_t Bh[4] = {hv[d][pl][4 * s], hv[d][pl][4 * s + 1], hv[d][pl][4 * s + 2],
+                                                    hv[d][pl][4 * s + 3]};
+                            C0 = mfma16(A0, Bh, C0);
+                            C1 = mfma16(A1, Bh, C1);
+                        }
+                    }
+                    const float* scg = my_sc + gl * 64 + 4 * q;
+                    const float4 s0 = *reinterpret_cast<const float4*>(scg);
+                    const float4 s1 = *reinterpret_cast<const float4*>(scg + 16);
+                    const float4 b0 = *reinterpret_cast<const float4*>(scg + 32);
+                    const float4 b1 = *reinterpret_cast<const float4*>(scg + 48);
+                    // C = sum (128 + L q) h  ->  (s/L) C + (b - (128/L) s) Hsum
+                    acc0[0] = fmaf(s0.x, C0[0], fmaf(b0.x, Hs, acc0[0]));
+                    acc0[1] = fmaf(s0.y, C0[1], fmaf(b0.y, Hs, acc0[1]));
+                    acc0[2] = fmaf(s0.z, C0[2], fmaf(b0.z, Hs, acc0[2]));
+                    acc0[3] = fmaf(s0.w, C0[3], fmaf(b0.w, Hs, acc0[3]));
+                    acc1[0] = fmaf(s1.x, C1[0], fmaf(b1.x, Hs, acc1[0]));
+                    acc1[1] = fmaf(s1.y, C1[1], fmaf(b1.y, Hs, acc1[1]));
+                    acc1[2] = fmaf(s1.z, C1[2], fmaf(b1.z, Hs, acc1[2]));
+                    acc1[3] = fmaf(s1.w, C1[3], fmaf(b1.w, Hs, acc1[3]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const bool go_next = last && has_next;
+                issue(d, go_next ? nxt.c0 : cur.c0, go_next ? nxt.h : cur.h, go_next ? nxt.part : cur.part,
+                      gaddr(!last ? gl + D : (has_next ? d : ng - 1)));
+            }
+            g0 += D;
+        } while (g0 < NGP);
         float* mine = red + (w * 64 + lane) * 8;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { mine[i] = acc0[i]; mine[4 + i] = acc1[i]; }
         __syncthreads();
-        if (w == 0 && tok_ok) {
+        if (kp == 0 && m < cur.n && cur.row0 >= 0 && cur.row0 + cur.n <= p.P) {
+            // the tile's KS partial sums in fixed order
             float o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                o[i] = ((red[(0 * 64 + lane) * 8 + i] + red[(1 * 64 + lane) * 8 + i]) +
-                        red[(2 * 64 + lane) * 8 + i]) + red[(3 * 64 + lane) * 8 + i];
-            uint16_t* yrow = p.y + (size_t)(r0 + t0 + m) * H + n0 + 4 * q;
+            for (int i = 0; i < 8; ++i) {
+                float v = red[(w * 64 + lane) * 8 + i];
+#pragma unroll
+                for (int k2 = 1; k2 < KS; ++k2) v += red[((w + k2) * 64 + lane) * 8 + i];
+                o[i] = v;
+            }
+            uint16_t* yrow = p.y + (size_t)(cur.row0 + m) * H + (cur.it * RT + tw) * 32 + 4 * q;
             uint2 o0, o1;
             o0.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
             o0.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
@@ -469,6 +538,8 @@ __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaParams p) {
             *reinterpret_cast<uint2*>(yrow + 16) = o1;
         }
         __syncthreads();
+        if (has_next) stage(nxt, sc_base + ((j + 1) & 1) * NGW * 64);
+        cur = nxt;
     }
 }
 
@@ -484,8 +555,7 @@ size_t mfma_workspace_bytes(const moe_dims& d) {
 static MfmaParams mfma_params(const FfnArgs& a) {
     const moe_dims& d = a.d;
     MfmaParams p{};
-    p.x = a.x; p.sorted_pairs = a.sorted_pairs; p.counts = a.counts; p.offsets = a.offsets;
-    p.active = a.active; p.n_active = a.n_active; p.y = a.y;
+    p.x = a.x; p.work = a.work; p.n_work = a.n_work; p.y = a.y;
     p.T = d.T; p.H = d.H; p.I = d.I; p.k = d.k; p.E = d.E; p.P = d.T * d.k;
     const size_t P = (size_t)p.P;
     char* ws = reinterpret_cast<char*>(a.h);
@@ -494,38 +564,109 @@ static MfmaParams mfma_params(const FfnArgs& a) {
     return p;
 }
 
-static long max_experts(const moe_dims& d) {
-    const long P = (long)d.T * d.k;
-    return d.E < P ? d.E : P;
-}
-
 static size_t mfma_lds_bytes(int NG) {
     const int NGW = (NG + kWaves - 1) / kWaves;
-    return ((size_t)kWaves * NGW * 64 + (size_t)kWaves * 64 * 8) * sizeof(float);
+    return ((size_t)kWaves * 2 * NGW * 64 + (size_t)kWaves * 64 * 8) * sizeof(float);
 }
 
-// Prefetch depth per wave: each wave streams at most ceil(NG/4) groups; up to
-// 4 (gate/up) or 2 (down, whose slots also hold three activation planes) are
-// kept in flight.
+static int num_cus() {
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
+// Workgroups of a persistent launch: as many as fit on the chip at once (from
+// the kernel's registers and LDS), never more than there can be items.  The
+// occupancy answer is cached (per kernel, by the caller) for the last LDS size.
+template <typename K>
+static dim3 persistent_grid(K kernel, std::atomic<uint64_t>& cache, size_t lds, const moe_dims& d,
+                            int items_per_entry) {
+    const uint64_t c = cache.load(std::memory_order_relaxed);
+    int per_cu = (int)(c & 0xFF);
+    if (per_cu == 0 || (c >> 8) != lds) {
+        per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        per_cu = per_cu > 8 ? 8 : per_cu;
+        cache.store(((uint64_t)lds << 8) | (uint64_t)per_cu, std::memory_order_relaxed);
+    }
+    const long max_items = work_capacity(d) * items_per_entry;
+    const long g = (long)per_cu * num_cus();
+    return dim3((unsigned)(max_items < g ? max_items : g));
+}
+
+// Prefetch depth: the deepest ring (up to cap) that pads a wave's NGW groups
+// by at most a quarter; padded steps cost a reload of a cached group.
+static int ring_depth_waves(int NG, int parts, int cap) {
+    const int NGW = (NG + parts - 1) / parts;
+    for (int d = cap < NGW ? cap : NGW; d > 1; --d) {
+        const int ngp = (NGW + d - 1) / d * d;
+        if (4 * ngp <= 5 * NGW) return d;
+    }
+    return 1;
+}
+
+static int ring_depth(int NG, int cap) { return ring_depth_waves(NG, kWaves, cap); }
+
 template <int BITS, int D, int SJ>
-static void gateup_launch(dim3 grid, size_t lds, hipStream_t s, const MfmaParams& p) {
+static void gateup_launch(const moe_dims& d, size_t lds, hipStream_t s, const MfmaParams& p) {
+    static std::atomic<uint64_t> occ{0};
+    const dim3 grid = persistent_grid(ffn_gateup_mfma_kernel<BITS, D, SJ>, occ, lds, d, p.items_per_entry);
     hipLaunchKernelGGL((ffn_gateup_mfma_kernel<BITS, D, SJ>), grid, dim3(256), lds, s, p);
 }
 
-// (depth, scale entries per lane) for a wave of NGW groups
-template <int BITS>
-static void gateup_dispatch(int NGW, dim3 grid, size_t lds, hipStream_t s, const MfmaParams& p) {
-    if (NGW <= 1) gateup_launch<BITS, 1, 1>(grid, lds, s, p);
-    else if (NGW <= 2) gateup_launch<BITS, 2, 1>(grid, lds, s, p);
-    else if (NGW <= 4) gateup_launch<BITS, 4, 1>(grid, lds, s, p);
-    else if (NGW <= 8) gateup_launch<BITS, 4, 2>(grid, lds, s, p);
-    else if (NGW <= 12) gateup_launch<BITS, 4, 3>(grid, lds, s, p);
-    else gateup_launch<BITS, 4, 4>(grid, lds, s, p);
+template <int BITS, int D, int SJ, int KS>
+static void down_launch(const moe_dims& d, size_t lds, hipStream_t s, const MfmaParams& p) {
+    static std::atomic<uint64_t> occ{0};
+    const dim3 grid = persistent_grid(ffn_down_mfma_kernel<BITS, D, SJ, KS>, occ, lds, d, p.items_per_entry);
+    hipLaunchKernelGGL((ffn_down_mfma_kernel<BITS, D, SJ, KS>), grid, dim3(256), lds, s, p);
 }
 
 template <int BITS, int D>
-static void down_launch(dim3 grid, size_t lds, hipStream_t s, const MfmaParams& p) {
-    hipLaunchKernelGGL((ffn_down_mfma_kernel<BITS, D>), grid, dim3(256), lds, s, p);
+static void gateup_sj(int SJ, const moe_dims& d, size_t lds, hipStream_t s, const MfmaParams& p) {
+    // SJ >= ceil(16 * NGW / 64) scale entries per lane per matrix
+    if (SJ <= 1) gateup_launch<BITS, D, 1>(d, lds, s, p);
+    else if (SJ <= 2) gateup_launch<BITS, D, 2>(d, lds, s, p);
+    else if (SJ <= 3) gateup_launch<BITS, D, 3>(d, lds, s, p);
+    else gateup_launch<BITS, D, 4>(d, lds, s, p);
+}
+
+template <int BITS>
+static void gateup_dispatch(int D, int SJ, const moe_dims& d, size_t lds, hipStream_t s, const MfmaParams& p) {
+    if (D == 4) gateup_sj<BITS, 4>(SJ, d, lds, s, p);
+    else if (D == 3) gateup_sj<BITS, 3>(SJ, d, lds, s, p);
+    else if (D == 2) gateup_sj<BITS, 2>(SJ, d, lds, s, p);
+    else gateup_sj<BITS, 1>(SJ, d, lds, s, p);
+}
+
+template <int BITS, int D, int KS>
+static void down_sj(int SJ, const moe_dims& d, size_t lds, hipStream_t s, const MfmaParams& p) {
+    // SJ >= ceil(32 * NGW / 64) scale entries per lane per matrix
+    if (SJ <= 1) down_launch<BITS, D, 1, KS>(d, lds, s, p);
+    else if (SJ <= 2) down_launch<BITS, D, 2, KS>(d, lds, s, p);
+    else if (SJ <= 4) down_launch<BITS, D, 4, KS>(d, lds, s, p);
+    else if (SJ <= 8) down_launch<BITS, D, 8, KS>(d, lds, s, p);
+    else down_launch<BITS, D, 16, KS>(d, lds, s, p);
+}
+
+template <int BITS>
+static void down_dispatch(int D, int SJ, int KS, const moe_dims& d, size_t lds, hipStream_t s,
+                          const MfmaParams& p) {
+    if (KS == 4) {
+        if (D >= 2) down_sj<BITS, 2, 4>(SJ, d, lds, s, p);
+        else down_sj<BITS, 1, 4>(SJ, d, lds, s, p);
+    } else if (KS == 2) {
+        if (D >= 2) down_sj<BITS, 2, 2>(SJ, d, lds, s, p);
+        else down_sj<BITS, 1, 2>(SJ, d, lds, s, p);
+    } else {
+        if (D >= 2) down_sj<BITS, 2, 1>(SJ, d, lds, s, p);
+        else down_sj<BITS, 1, 1>(SJ, d, lds, s, p);
+    }
 }
 
 int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
@@ -534,32 +675,34 @@ int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     MfmaParams p = mfma_params(a);
     p.qa = a.w.q[0]; p.sa = a.w.scale[0]; p.ba = a.w.bias[0];
     p.qb = a.w.q[1]; p.sb = a.w.scale[1]; p.bb = a.w.bias[1];
-    p.items_per_expert = d.I / 16;
-    const dim3 grid((unsigned)(max_experts(d) * p.items_per_expert));
+    p.items_per_entry = d.I / 16;
     const int NG = d.H / kGroup, NGW = (NG + kWaves - 1) / kWaves;
+    const int SJ = (16 * NGW + 63) / 64;
+    if (SJ > 4) return MOE_ERR_UNSUPPORTED;
     const size_t lds = mfma_lds_bytes(NG);
-    if (a.bits == 4) gateup_dispatch<4>(NGW, grid, lds, s, p);
-    else gateup_dispatch<2>(NGW, grid, lds, s, p);
+    const int D = ring_depth(NG, 4);
+    if (a.bits == 4) gateup_dispatch<4>(D, SJ, d, lds, s, p);
+    else gateup_dispatch<2>(D, SJ, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
+
+// K parts of the down kernel: enough that each wave streams at least 4 groups
+// when K allows, the rest of the waves spread over output rows.
+static int down_k_split(int NG) { return NG >= 16 ? 4 : (NG >= 8 ? 2 : 1); }
 
 int launch_down_mfma(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     MfmaParams p = mfma_params(a);
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
-    p.items_per_expert = d.H / 32;
-    const dim3 grid((unsigned)(max_experts(d) * p.items_per_expert));
-    const int NG = d.I / kGroup, NGW = (NG + kWaves - 1) / kWaves;
-    const size_t lds = mfma_lds_bytes(NG);
-    // depth 2 costs two thirds of the waves per SIMD: only worth it for long K
-    if (a.bits == 4) {
-        if (NGW >= 4) down_launch<4, 2>(grid, lds, s, p);
-        else down_launch<4, 1>(grid, lds, s, p);
-    } else {
-        if (NGW >= 4) down_launch<2, 2>(grid, lds, s, p);
-        else down_launch<2, 1>(grid, lds, s, p);
-    }
+    const int NG = d.I / kGroup, KS = down_k_split(NG), NGW = (NG + KS - 1) / KS;
+    p.items_per_entry = d.H / (32 * (kWaves / KS));
+    const int SJ = (32 * NGW + 63) / 64;
+    if (SJ > 16) return MOE_ERR_UNSUPPORTED;
+    const size_t lds = ((size_t)kWaves * 2 * NGW * 64 + (size_t)kWaves * 64 * 8) * sizeof(float);
+    const int D = ring_depth_waves(NG, KS, 2);
+    if (a.bits == 4) down_dispatch<4>(D, SJ, KS, d, lds, s, p);
+    else down_dispatch<2>(D, SJ, KS, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -104,16 +104,25 @@ int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* tab
 //      the same expert find each other with ballots over the id bits, take
 //      rank = earlier equal lanes, and the last of them advances base[w][e].
 // Pairs of one expert therefore keep ascending p order.
+// The same pass writes the FFN work list: one entry per tile of up to
+// kWorkRows consecutive rows of an expert (expert-major), holding the expert,
+// the tile's first row, its row count and the tokens of its rows, so that an
+// FFN workgroup learns everything about its tile from one 80-byte read.
 constexpr int kPermWaves = 8;
 
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                       int32_t* __restrict__ counts,
+                                                       int k, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted_pairs,
                                                        int32_t* __restrict__ pair_to_row,
                                                        int32_t* __restrict__ active,
-                                                       int32_t* __restrict__ n_active) {
+                                                       int32_t* __restrict__ n_active,
+                                                       int32_t* __restrict__ work,
+                                                       int32_t* __restrict__ n_work) {
     __shared__ int cnt[kPermWaves][kMaxE];
+    __shared__ int offs[kMaxE];
+    __shared__ int cnts[kMaxE];
+    __shared__ int wpos[kMaxE];
     __shared__ int wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int chunk = (P + kPermWaves - 1) / kPermWaves;
@@ -129,19 +138,24 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     }
     __syncthreads();
 
-    int running = 0, nact = 0;
+    int running = 0, nact = 0, ntile_run = 0;
     for (int e0 = 0; e0 < E; e0 += blockDim.x) {
         const int e = e0 + tid;
         int tot = 0;
         if (e < E)
 #pragma unroll
             for (int w = 0; w < kPermWaves; ++w) tot += cnt[w][e];
-        int sum, nsum;
+        int sum, nsum, tsum;
         const int excl = block_exclusive_scan(tot, wsum, &sum);
         const int apos = block_exclusive_scan(tot > 0 ? 1 : 0, wsum, &nsum);
+        const int tiles = (tot + kWorkRows - 1) / kWorkRows;
+        const int tpos = block_exclusive_scan(tiles, wsum, &tsum);
         if (e < E) {
             counts[e] = tot;
             offsets[e] = running + excl;
+            offs[e] = running + excl;
+            cnts[e] = tot;
+            wpos[e] = ntile_run + tpos;
             if (tot > 0) active[nact + apos] = e;
             int b = running + excl;
 #pragma unroll
@@ -153,10 +167,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
         }
         running += sum;
         nact += nsum;
+        ntile_run += tsum;
     }
     if (tid == 0) {
         offsets[E] = running;
         *n_active = nact;
+        *n_work = ntile_run;
     }
     __syncthreads();
 
@@ -186,6 +202,21 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                 sorted_pairs[row] = p;
                 pair_to_row[p] = row;
                 if (rank == n_same - 1) cnt[wid][e] = row + 1;
+                // work list: the row's slot in its expert's tile of kWorkRows rows
+                const int off = row - offs[e];
+                int32_t* ent = work + (size_t)(wpos[e] + off / kWorkRows) * kWorkInts;
+                const int slot = off % kWorkRows;
+                const int tok = p / k;
+                ent[4 + slot] = tok;
+                if (slot == 0) {
+                    // header, and the token of slot 0 in the unused slots of a short tile
+                    const int rows = min(kWorkRows, cnts[e] - off);
+                    ent[0] = e;
+                    ent[1] = row;
+                    ent[2] = rows;
+                    ent[3] = 0;
+                    for (int j = rows; j < kWorkRows; ++j) ent[4 + j] = tok;
+                }
             }
             __builtin_amdgcn_wave_barrier();
         }
@@ -194,9 +225,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 
 int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
-                   hipStream_t s) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, d.T * d.k, d.E, counts,
-                       offsets, sorted_pairs, pair_to_row, active, n_active);
+                   int32_t* work, int32_t* n_work, hipStream_t s) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, d.T * d.k, d.E, d.k, counts,
+                       offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -15,8 +15,8 @@ from typing import Optional
 
 import torch
 
-from . import (ALGO_AUTO, OP_FFN, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4, permute,
-               route_topk, slot_lookup, workspace_bytes)
+from . import (ALGO_AUTO, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4,
+               permute, route_topk, slot_lookup, work_list_capacity, workspace_bytes)
 
 
 @dataclass
@@ -35,6 +35,8 @@ class LayerBuffers:
     pair_to_row: torch.Tensor     # int32 [T*k]
     active: torch.Tensor          # int32 [E]
     n_active: torch.Tensor        # int32 [1]
+    work_list: torch.Tensor       # int32 [capacity, WORK_ENTRY_INTS]
+    n_work: torch.Tensor          # int32 [1]
     workspace: torch.Tensor       # uint8, 256-byte aligned by the allocator
     y_rows: torch.Tensor          # bf16 bits as int16 [T*k, H]
 
@@ -43,6 +45,7 @@ class LayerBuffers:
         T, H, E, k = d.T, d.H, d.E, d.k
         i32 = dict(dtype=torch.int32, device=device)
         ws = workspace_bytes(d, OP_FFN, bits, algo)
+        cap = work_list_capacity(d)
         return LayerBuffers(
             d=d, bits=bits,
             logits=torch.empty((T, E), dtype=torch.float32, device=device),
@@ -57,6 +60,8 @@ class LayerBuffers:
             pair_to_row=torch.empty((max(T * k, 1),), **i32),
             active=torch.empty((E,), **i32),
             n_active=torch.zeros((1,), **i32),
+            work_list=torch.empty((max(cap, 1), WORK_ENTRY_INTS), **i32),
+            n_work=torch.zeros((1,), **i32),
             workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
             y_rows=torch.empty((max(T * k, 1), H), dtype=torch.int16, device=device),
         )
@@ -73,8 +78,7 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
     slot_lookup(d, buf.topk_ids, slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss,
                 host_doorbell, last_use, step, stream)
     permute(d, buf.topk_ids, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active,
-            buf.n_active, stream)
+            buf.n_active, buf.work_list, buf.n_work, stream)
     ffn = expert_ffn_q4 if weights.bits == 4 else expert_ffn_q2
-    ffn(d, x, buf.sorted_pairs, buf.counts, buf.offsets, buf.active, buf.n_active, weights,
-        buf.y_rows, algo, buf.workspace, None, stream)
+    ffn(d, x, buf.work_list, buf.n_work, weights, buf.y_rows, algo, buf.workspace, None, stream)
     combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)

@@ -105,7 +105,7 @@ def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, tab
     d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
     buf = moe.LayerBuffers.allocate(d, L.bits, algo)
     for name in ("logits", "topk_ids", "topk_w", "pair_slot", "miss", "counts", "offsets",
-                 "sorted_pairs", "pair_to_row", "active", "y_rows"):
+                 "sorted_pairs", "pair_to_row", "active", "work_list", "y_rows"):
         poison_(getattr(buf, name))
     x_d, r_d = to_dev(xb), to_dev(res)
     out_d = torch.empty_like(r_d)
@@ -119,6 +119,7 @@ def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, tab
         pair_slot=to_host(buf.pair_slot)[:P], miss=to_host(buf.miss), n_miss=int(to_host(buf.n_miss)[0]),
         counts=to_host(buf.counts), offsets=to_host(buf.offsets), sorted_pairs=to_host(buf.sorted_pairs)[:P],
         pair_to_row=to_host(buf.pair_to_row)[:P], active=to_host(buf.active), n_active=int(to_host(buf.n_active)[0]),
+        work_list=to_host(buf.work_list), n_work=int(to_host(buf.n_work)[0]),
         y_rows=to_host(buf.y_rows, np.uint16)[:P], out=to_host(out_d, np.uint16),
     )
 
@@ -155,6 +156,9 @@ def check_permute(g: Dict, L: Layer):
         assert np.array_equal(g[key], ref[key]), key
     assert g["n_active"] == ref["n_active"]
     assert np.array_equal(g["active"][: ref["n_active"]], ref["active"])
+    wl = oracle.work_list(g["ids"], L.shape.E, L.shape.k, moe.WORK_TILE_ROWS)
+    assert g["n_work"] == wl.shape[0]
+    assert np.array_equal(g["work_list"][: wl.shape[0]], wl), "work list"
 
 
 def tolerance_metrics(a_bits: np.ndarray, b_bits: np.ndarray):

@@ -78,11 +78,18 @@ def _qw(ptr=FAKE):
     return w
 
 
-def _ffn(d, x=FAKE, y=FAKE, w=None, algo=0, ws=FAKE, ws_bytes=1 << 30, sp=FAKE):
+def _ffn(d, x=FAKE, y=FAKE, w=None, algo=0, ws=FAKE, ws_bytes=1 << 30, wl=FAKE, nw=FAKE):
     L = moe.lib()
     w = w or _qw()
-    return L.moe_expert_ffn_q4(ctypes.byref(d), x, sp, FAKE, FAKE, FAKE, FAKE, ctypes.byref(w), y, algo,
-                               ws, ws_bytes, None)
+    return L.moe_expert_ffn_q4(ctypes.byref(d), x, wl, nw, ctypes.byref(w), y, algo, ws, ws_bytes, None)
+
+
+def test_work_list_capacity():
+    # min(E, T*k) + T*k / 16: enough for every expert's partial tile plus the full ones
+    assert moe.work_list_capacity(moe.dims(32, 2048, 512, 256, 8)) == 256 + 16
+    assert moe.work_list_capacity(moe.dims(1, 4096, 1024, 512, 4)) == 4
+    assert moe.work_list_capacity(moe.dims(0, 256, 512, 8, 2)) == 0
+    assert moe.lib().moe_work_list_capacity(ctypes.byref(moe.dims(1, 256, 512, 8, 2)), None) == moe.ERR_INVALID_ARG
 
 
 def test_ffn_validation_paths():
@@ -91,7 +98,9 @@ def test_ffn_validation_paths():
     assert "x is NULL" in moe.last_error()
     assert _ffn(d, x=MISALIGNED) == moe.ERR_INVALID_ARG
     assert "aligned" in moe.last_error()
-    assert _ffn(d, sp=None) == moe.ERR_INVALID_ARG
+    assert _ffn(d, wl=None) == moe.ERR_INVALID_ARG
+    assert _ffn(d, wl=FAKE + 4) == moe.ERR_INVALID_ARG
+    assert _ffn(d, nw=None) == moe.ERR_INVALID_ARG
     assert _ffn(d, w=_qw(MISALIGNED)) == moe.ERR_INVALID_ARG
     assert _ffn(d, algo=7) == moe.ERR_UNSUPPORTED
     assert _ffn(d, ws=None) == moe.ERR_WORKSPACE
@@ -108,7 +117,9 @@ def test_route_and_combine_validation():
     assert L.moe_topk_from_logits(ctypes.byref(d), None, 1, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
     assert L.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, None) == moe.ERR_INVALID_ARG
     assert L.moe_slot_lookup(ctypes.byref(d), FAKE, FAKE, -1, FAKE, FAKE, FAKE, None, None, 0, None) == moe.ERR_INVALID_ARG
-    assert L.moe_permute(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_permute(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_permute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_permute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == moe.ERR_INVALID_ARG
     assert L.moe_workspace_bytes(None, 3, 4, 0, None) == moe.ERR_INVALID_ARG
 
 
@@ -119,5 +130,5 @@ def test_zero_tokens_need_no_buffers():
     assert L.moe_route_topk(ctypes.byref(d), None, None, None, 1, None, None, None, None) == moe.OK
     assert L.moe_combine(ctypes.byref(d), None, None, None, None, None, None) == moe.OK
     w = _qw()
-    assert L.moe_expert_ffn_q4(ctypes.byref(d), None, None, None, None, None, None, ctypes.byref(w), None,
-                               0, None, 0, None) == moe.OK
+    assert L.moe_expert_ffn_q4(ctypes.byref(d), None, None, None, ctypes.byref(w), None, 0, None, 0,
+                               None) == moe.OK

@@ -147,9 +147,8 @@ def test_split_calls_gateup_h_matches_oracle():
     d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
     buf = moe.LayerBuffers.allocate(d, 4, moe.ALGO_GEMV)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    moe.expert_gateup(d, 4, dev(xb.view(np.int16)), dev(g["sorted_pairs"]), dev(g["counts"]), dev(g["offsets"]),
-                      dev(g["active"]), dev(np.array([g["n_active"]], np.int32)), L.weights_d, buf.workspace,
-                      moe.ALGO_GEMV)
+    moe.expert_gateup(d, 4, dev(xb.view(np.int16)), dev(g["work_list"]), dev(np.array([g["n_work"]], np.int32)),
+                      L.weights_d, buf.workspace, moe.ALGO_GEMV)
     torch.cuda.synchronize()
     P = T * sh.k
     h = buf.workspace[: P * sh.I * 4].view(torch.float32).reshape(P, sh.I).cpu().numpy()
@@ -173,7 +172,7 @@ def test_zero_tokens_is_a_no_op():
     out = torch.zeros((0, sh.H), dtype=torch.int16, device="cuda")
     moe.layer_forward(buf, x, L.Wr_d, L.bias_d, L.weights_d, L.table_d, sh.E, x, out)
     torch.cuda.synchronize()
-    assert int(buf.n_miss.item()) == 0 and int(buf.n_active.item()) == 0
+    assert int(buf.n_miss.item()) == 0 and int(buf.n_active.item()) == 0 and int(buf.n_work.item()) == 0
     assert int(buf.counts.sum().item()) == 0
 
 

@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--sweep", default="1,8", help="extra token counts timed after the main run ('none' = none)")
     ap.add_argument("--algo", choices=["auto", "gemv", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="timed steps of the T=4096 prefill layer on the grouped GEMM (0 = skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the runs, copy a buffer of this many MiB device to device 5 times "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -168,6 +170,37 @@ def traffic_record(kernel_src):
     if rec.get("source_sha256_16") != source_hash(kernel_src):
         return None
     return rec.get("bytes_per_launch")
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def measure_prefill(torch, mi, moe, steps, warmup):
+    """The prefill-shape layer (T = 4096) with the FFN on the grouped GEMM:
+    matrix-core utilisation = useful FFN flops / FFN kernel time / bf16 peak."""
+    shape = mi.CONFIGS["prefill"]
+    T = shape.tokens[0]
+    log(f"[bench] prefill: uploading {shape.E * shape.bytes_per_expert(4) / 1e6:.0f} MB, T={T}")
+    layer = upload_layer(shape, 4, seed=0, torch=torch, mi=mi, moe=moe)
+    r = Runner(torch, mi, moe, shape, [layer], T, moe.ALGO_AUTO)
+    U = r.experts_used()[0]
+    total_ms, _, gate_ms, down_ms = r.timed(steps, warmup)
+    P = T * shape.k
+    gate_flop, down_flop = 2.0 * P * 2 * shape.H * shape.I, 2.0 * P * shape.H * shape.I
+    g_s, d_s = sum(gate_ms) / 1e3 / steps, sum(down_ms) / 1e3 / steps
+    util = (gate_flop + down_flop) / (g_s + d_s) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    del r, layer
+    torch.cuda.empty_cache()
+    return dict(workload=f"prefill layer T={T}: hidden {shape.H}, {shape.E} experts top-{shape.k}, "
+                         f"intermediate {shape.I}, 4-bit g128, Zipf(1.0) routing",
+                algo="grouped GEMM (AUTO)", steps=steps, experts_used=U,
+                tokens_per_s=round(T / (total_ms / 1e3 / steps), 1), ms_per_step=round(total_ms / steps, 4),
+                gateup_us=round(g_s * 1e6, 2), down_us=round(d_s * 1e6, 2),
+                ffn_tflops=round((gate_flop + down_flop) / (g_s + d_s) / 1e12, 1),
+                gateup_tflops=round(gate_flop / g_s / 1e12, 1), down_tflops=round(down_flop / d_s / 1e12, 1),
+                mfma_util=round(util, 4), mfma_peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                note="useful FFN flops (2*T*k*3*H*I) only; the exact-operand scheme also runs all-ones "
+                     "MFMAs for the group sums and two h planes in the down GEMM")
 
 
 TRAFFIC_KERNELS = {"gateup": "ffn_gateup_mfma_kernel", "down": "ffn_down_mfma_kernel",
@@ -306,6 +339,12 @@ def main():
         log(f"[bench] sweep T={tok}: {m['tokens_per_s']:.0f} tokens/s, gate/up {m['gateup_GBps']:.0f} GB/s")
         sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()})
 
+    prefill = None
+    if args.prefill_steps > 0:
+        prefill = measure_prefill(torch, mi, moe, args.prefill_steps, 3)
+        log(f"[bench] prefill: {prefill['tokens_per_s']:.0f} tokens/s, FFN {prefill['ffn_tflops']} TFLOP/s "
+            f"({100 * prefill['mfma_util']:.1f}% of bf16 MFMA peak)")
+
     kernel_src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc",
                               "ffn_gemv.hip" if args.algo == "gemv" else "ffn_mfma.hip")
     achieved = main_run["gateup_GBps"]
@@ -364,6 +403,7 @@ def main():
             "down_us": round(main_run["down_us"], 3),
         },
         "sweep": sweep,
+        "prefill": prefill,
         "context_not_comparable": CONTEXT,
     }
     print(json.dumps(result), flush=True)

@@ -85,13 +85,19 @@ extern "C" {
 #define MOE_ALGO_AUTO 0   /* choose per call from the shape */
 #define MOE_ALGO_GEMV 1   /* vector-ALU matvec, one pass over the weights per token tile */
 #define MOE_ALGO_MFMA 2   /* matrix-core tiles (bf16 MFMA with exact code operands) */
+#define MOE_ALGO_GEMM 3   /* grouped GEMM on the matrix cores for experts with many
+                             tokens (prefill): 64-token items, 4-bit codes only,
+                             I and H multiples of 128 and at least 256; AUTO
+                             picks it when the experts average at least 64
+                             tokens */
 
 /* FFN work list (written by moe_permute, read by the FFN calls): one entry per
  * tile of up to MOE_WORK_TILE_ROWS consecutive sorted rows of one expert,
  * expert-major in ascending expert order.  Entry = int32[MOE_WORK_ENTRY_INTS]:
  *   [0] expert id   [1] first sorted row of the tile   [2] rows in the tile
- *   [3] 0           [4 + j] token of row j (j < rows; slots past the tile's
- *                   rows repeat the token of row 0) */
+ *   [3] index of the tile among its expert's tiles (0, 1, ...)
+ *   [4 + j] token of row j (j < rows; slots past the tile's rows repeat the
+ *           token of row 0) */
 #define MOE_WORK_TILE_ROWS 16
 #define MOE_WORK_ENTRY_INTS 20
 

@@ -171,8 +171,8 @@ def work_list(ids: np.ndarray, E: int, k: int, tile: int = 16) -> np.ndarray:
     consecutive sorted rows; the library hands that run to its FFN in tiles of
     at most `tile` rows.  The tile format is the library's own (the pages fix
     only the grouping): per expert in ascending id, per tile in row order,
-    [expert, first row, rows, 0, token of each row..., then the token of the
-    tile's first row repeated].  Built here from the oracle's permutation with
+    [expert, first row, rows, index of the tile among the expert's tiles,
+    token of each row..., then the token of the tile's first row repeated].  Built here from the oracle's permutation with
     plain loops."""
     perm = permute(ids, E)
     counts, offsets, sp = perm["counts"], perm["offsets"], perm["sorted_pairs"]
@@ -183,7 +183,7 @@ def work_list(ids: np.ndarray, E: int, k: int, tile: int = 16) -> np.ndarray:
             rows = min(tile, int(counts[e]) - start)
             toks = [int(sp[row0 + j]) // k for j in range(rows)]
             toks += [toks[0]] * (tile - rows)
-            out.append([e, row0, rows, 0] + toks)
+            out.append([e, row0, rows, start // tile] + toks)
     return np.array(out, dtype=np.int32).reshape(-1, tile + 4)
 
 

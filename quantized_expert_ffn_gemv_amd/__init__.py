@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ALGO_AUTO, ALGO_GEMV, ALGO_MFMA = 0, 1, 2
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA, ALGO_GEMM = 0, 1, 2, 3
 OP_ROUTE, OP_LOOKUP, OP_PERMUTE, OP_FFN, OP_COMBINE = 0, 1, 2, 3, 4
 
 # entry points declared in include/moe.h
@@ -224,5 +224,5 @@ __all__ = [
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
     "expert_ffn_q2", "expert_gateup", "expert_down", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
-    "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
+    "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

@@ -65,8 +65,10 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* w
     if (st) return st;
     if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED, "%s: bits = %d (2 or 4)", fn, bits);
     if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: weights is NULL", fn);
-    if (algo != MOE_ALGO_AUTO && algo != MOE_ALGO_GEMV && algo != MOE_ALGO_MFMA)
+    if (algo != MOE_ALGO_AUTO && algo != MOE_ALGO_GEMV && algo != MOE_ALGO_MFMA && algo != MOE_ALGO_GEMM)
         return fail(MOE_ERR_UNSUPPORTED, "%s: unknown algo %d", fn, algo);
+    if (algo == MOE_ALGO_GEMM && !moe::gemm_supported(*d, bits))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: the grouped GEMM needs 4-bit codes and H, I multiples of 128, at least 256", fn);
     if (d->T == 0) return MOE_OK;
     REQUIRE_PTR(work_list, 16);
     REQUIRE_PTR(n_work, 4);
@@ -104,6 +106,22 @@ int check_workspace(const char* fn, const moe_dims* d, int bits, int algo, const
     return MOE_OK;
 }
 
+int launch_gateup(int alg, const moe::FfnArgs& a, hipStream_t s) {
+    switch (alg) {
+        case MOE_ALGO_GEMV: return moe::launch_gateup_gemv(a, s);
+        case MOE_ALGO_GEMM: return moe::launch_gateup_gemm(a, s);
+        default: return moe::launch_gateup_mfma(a, s);
+    }
+}
+
+int launch_down(int alg, const moe::FfnArgs& a, hipStream_t s) {
+    switch (alg) {
+        case MOE_ALGO_GEMV: return moe::launch_down_gemv(a, s);
+        case MOE_ALGO_GEMM: return moe::launch_down_gemm(a, s);
+        default: return moe::launch_down_mfma(a, s);
+    }
+}
+
 int ffn_common(const char* fn, int bits, const moe_dims* d, const uint16_t* x,
                const int32_t* work_list, const int32_t* n_work, const moe_qweights* w, uint16_t* y,
                int algo, void* ws, size_t ws_bytes, void* stream) {
@@ -115,9 +133,9 @@ int ffn_common(const char* fn, int bits, const moe_dims* d, const uint16_t* x,
     st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
     if (st) return st;
     moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), y);
-    const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
-    st = mfma ? moe::launch_gateup_mfma(a, as_stream(stream)) : moe::launch_gateup_gemv(a, as_stream(stream));
-    if (!st) st = mfma ? moe::launch_down_mfma(a, as_stream(stream)) : moe::launch_down_gemv(a, as_stream(stream));
+    const int alg = moe::resolve_algo(*d, bits, algo);
+    st = launch_gateup(alg, a, as_stream(stream));
+    if (!st) st = launch_down(alg, a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }
@@ -265,8 +283,7 @@ int moe_expert_gateup(const moe_dims* d, int bits, const uint16_t* x, const int3
     st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
     if (st) return st;
     moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), nullptr);
-    const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
-    st = mfma ? moe::launch_gateup_mfma(a, as_stream(stream)) : moe::launch_gateup_gemv(a, as_stream(stream));
+    st = launch_gateup(moe::resolve_algo(*d, bits, algo), a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }
@@ -283,8 +300,7 @@ int moe_expert_down(const moe_dims* d, int bits, const int32_t* work_list, const
     if (st) return st;
     moe::FfnArgs a = ffn_args(d, bits, nullptr, work_list, n_work, w,
                               static_cast<float*>(const_cast<void*>(ws)), y);
-    const bool mfma = moe::resolve_algo(*d, bits, algo) == MOE_ALGO_MFMA;
-    st = mfma ? moe::launch_down_mfma(a, as_stream(stream)) : moe::launch_down_gemv(a, as_stream(stream));
+    st = launch_down(moe::resolve_algo(*d, bits, algo), a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();
 }

@@ -142,6 +142,10 @@ struct FfnArgs {
 size_t gemv_workspace_bytes(const moe_dims& d);
 size_t mfma_workspace_bytes(const moe_dims& d);
 size_t ffn_workspace_bytes(const moe_dims& d, int bits, int algo);
+bool gemm_supported(const moe_dims& d, int bits);
+size_t gemm_workspace_bytes(const moe_dims& d);
+int launch_gateup_gemm(const FfnArgs& a, hipStream_t s);
+int launch_down_gemm(const FfnArgs& a, hipStream_t s);
 int resolve_algo(const moe_dims& d, int bits, int algo);
 int launch_gateup_gemv(const FfnArgs& a, hipStream_t s);
 int launch_down_gemv(const FfnArgs& a, hipStream_t s);

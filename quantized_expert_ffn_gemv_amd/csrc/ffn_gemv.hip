@@ -480,12 +480,20 @@ size_t gemv_workspace_bytes(const moe_dims& d) {
 
 // MOE_ALGO_AUTO -> the matrix-core path (its cost per weight does not grow with
 // the tokens an expert serves); explicit choices are kept.
-int resolve_algo(const moe_dims& /*d*/, int /*bits*/, int algo) {
-    return algo == MOE_ALGO_AUTO ? MOE_ALGO_MFMA : algo;
+// AUTO: the grouped GEMM once experts average at least 64 tokens (a weight
+// tile then meets a full 64-token item), else the per-tile matrix-core path.
+int resolve_algo(const moe_dims& d, int bits, int algo) {
+    if (algo != MOE_ALGO_AUTO) return algo;
+    const long P = (long)d.T * d.k;
+    return (gemm_supported(d, bits) && P >= 64L * d.E) ? MOE_ALGO_GEMM : MOE_ALGO_MFMA;
 }
 
 size_t ffn_workspace_bytes(const moe_dims& d, int bits, int algo) {
-    return resolve_algo(d, bits, algo) == MOE_ALGO_GEMV ? gemv_workspace_bytes(d) : mfma_workspace_bytes(d);
+    switch (resolve_algo(d, bits, algo)) {
+        case MOE_ALGO_GEMV: return gemv_workspace_bytes(d);
+        case MOE_ALGO_GEMM: return gemm_workspace_bytes(d);
+        default: return mfma_workspace_bytes(d);
+    }
 }
 
 int launch_gateup_gemv(const FfnArgs& a, hipStream_t s) {

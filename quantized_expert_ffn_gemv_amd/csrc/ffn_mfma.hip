@@ -31,12 +31,9 @@
 // operand needs, plus per-16-row partial sums of h for the down bias fold.
 #include <atomic>
 
-#include "common.h"
+#include "mfma_ops.h"
 
 namespace moe {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 // Work split: a 256-thread workgroup owns an output block (16 gate + 16 up
 // rows, or 32 down rows) of one expert; its 4 waves take disjoint quarters of
@@ -59,81 +56,10 @@ struct MfmaParams {
     int items_per_entry;        // output blocks per work-list entry
 };
 
-__device__ __forceinline__ floatx4_t mfma16(const uint32_t (&a)[4], const uint32_t (&b)[4], floatx4_t c) {
-    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a);
-    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, b);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, c, 0, 0, 0);
-}
-
-// A operand of MFMA step s for one group: the lane's codes (4-bit: 4 words,
-// 2-bit: 2 words) -> 4 packed pairs of bf16 128 + L*q (see kLever).  Pair i of
-// a word holds codes (i, i + W/2) of that word (W codes per word).
-template <int BITS>
-__device__ __forceinline__ void code_operand(const uint32_t* w, int s, uint32_t (&out)[4]) {
-    if constexpr (BITS == 4) {
-        const uint32_t v = w[s];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = (shift_to(v, 4 * i - 3) & 0x00780078u) | 0x43004300u;
-    } else {
-        const uint32_t v = w[s >> 1];
-        const int base = 4 * (s & 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = (shift_to(v, 2 * (base + i) - 5) & 0x00600060u) | 0x43004300u;
-    }
-}
-
-// B operand of MFMA step s from the lane's 32 natural-order bf16 activations
-// X (16 packed words), in the pair order of code_operand: pair i = elements
-// (a, a + W/2), built with one v_perm_b32.
-template <int BITS>
-__device__ __forceinline__ void act_operand(const uint32_t* X, int s, uint32_t (&out)[4]) {
-    constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;   // low / high halves of two words
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int lo_word, hi_word;
-        if constexpr (BITS == 4) {            // elements 8s + i and 8s + i + 4
-            lo_word = 4 * s + (i >> 1);
-            hi_word = lo_word + 2;
-        } else {                              // elements 16(s/2) + 4(s%2) + i and that + 8
-            lo_word = 8 * (s >> 1) + 2 * (s & 1) + (i >> 1);
-            hi_word = lo_word + 4;
-        }
-        out[i] = __builtin_amdgcn_perm(X[hi_word], X[lo_word], (i & 1) ? HI : LO);
-    }
-}
-
-__device__ __forceinline__ void split3_bf16(float h, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    hi = f32_to_bf16_bits(h);
-    const float r1 = h - bf16_bits_to_f32(hi);
-    mid = f32_to_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(mid);
-    lo = f32_to_bf16_bits(r2);
-}
-
 // Groups [gb, ge) of K handled by wave w (an even split; a wave may get none).
 __device__ __forceinline__ void wave_groups(int NG, int w, int& gb, int& ng) {
     gb = (w * NG) / kWaves;
     ng = ((w + 1) * NG) / kWaves - gb;
-}
-
-// Read a value that no kernel writes while this one runs through the scalar
-// path: uniform addresses in the constant address space become s_load, which
-// waits on its own counter instead of queueing behind the vector loads of the
-// code stream.  Used for the routing lists written by earlier kernels.
-template <typename T>
-__device__ __forceinline__ T ld_scalar(const T* p, size_t i) {
-    typedef const __attribute__((address_space(4))) T* cptr;
-    return ((cptr)(p))[i];
-}
-
-// Weight row held by output row m (0..15) of a 16-row tile.  The gate/up
-// kernel stores h of its output rows 4q..4q+3 at consecutive positions, and
-// the down kernel reads h in the pair order of its code operands; loading the
-// gate/up rows in that order makes the two agree with no data exchange.
-template <int BITS>
-__device__ __forceinline__ int pair_order_row(int m) {
-    if constexpr (BITS == 4) return 8 * (m >> 3) + ((m & 7) >> 1) + 4 * (m & 1);   // 0,4,1,5,2,6,3,7 per 8
-    else return (m >> 1) + 8 * (m & 1);                                           // 0,8,1,9,...,7,15
 }
 
 // --------------------------------------------------------------- gate / up

@@ -106,8 +106,9 @@ int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* tab
 // Pairs of one expert therefore keep ascending p order.
 // The same pass writes the FFN work list: one entry per tile of up to
 // kWorkRows consecutive rows of an expert (expert-major), holding the expert,
-// the tile's first row, its row count and the tokens of its rows, so that an
-// FFN workgroup learns everything about its tile from one 80-byte read.
+// the tile's first row, its row count, its index among the expert's tiles and
+// the tokens of its rows, so that an FFN workgroup learns everything about its
+// tile from one 80-byte read.
 constexpr int kPermWaves = 8;
 
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                     ent[0] = e;
                     ent[1] = row;
                     ent[2] = rows;
-                    ent[3] = 0;
+                    ent[3] = off / kWorkRows;   // the tile's index within its expert
                     for (int j = rows; j < kWorkRows; ++j) ent[4 + j] = tok;
                 }
             }

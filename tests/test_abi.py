@@ -62,6 +62,10 @@ def test_dims_validation(T, H, I, E, k, g, status):
 
 
 def test_workspace_size():
+    # the grouped GEMM adds its heads list after the matrix-core workspace
+    dp = moe.dims(4096, 2048, 768, 128, 8)
+    assert moe.workspace_bytes(dp, moe.OP_FFN, 4, moe.ALGO_GEMM) > moe.workspace_bytes(dp, moe.OP_FFN, 4, moe.ALGO_MFMA)
+    assert moe.workspace_bytes(dp, moe.OP_FFN, 4) == moe.workspace_bytes(dp, moe.OP_FFN, 4, moe.ALGO_GEMM)
     d = moe.dims(32, 2048, 512, 256, 8)
     assert moe.workspace_bytes(d, moe.OP_FFN, 4) >= 32 * 8 * 512 * 4
     assert moe.workspace_bytes(d, moe.OP_ROUTE, 4) == 0
@@ -103,6 +107,12 @@ def test_ffn_validation_paths():
     assert _ffn(d, nw=None) == moe.ERR_INVALID_ARG
     assert _ffn(d, w=_qw(MISALIGNED)) == moe.ERR_INVALID_ARG
     assert _ffn(d, algo=7) == moe.ERR_UNSUPPORTED
+    # the grouped GEMM takes 4-bit codes only
+    L = moe.lib()
+    w = _qw()
+    assert L.moe_expert_ffn_q2(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(w), FAKE, moe.ALGO_GEMM, FAKE,
+                               1 << 30, None) == moe.ERR_UNSUPPORTED
+    assert "grouped GEMM" in moe.last_error()
     assert _ffn(d, ws=None) == moe.ERR_WORKSPACE
     assert _ffn(d, ws_bytes=100) == moe.ERR_WORKSPACE
     assert "workspace" in moe.last_error()

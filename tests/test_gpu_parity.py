@@ -89,12 +89,13 @@ def test_e512_layer(bits, algo):
     _stages(L, 1, algo=algo)
 
 
-def test_prefill_layer_sampled_rows():
+@pytest.mark.parametrize("algo", [moe.ALGO_AUTO, moe.ALGO_MFMA], ids=["auto_gemm", "mfma"])
+def test_prefill_layer_sampled_rows(algo):
     L = layer("prefill")
     T = 4096
     xb, res = mi.make_activations(L.shape.H, T, 0)
-    say("[run] prefill T=4096")
-    g = run_layer(L, xb, res)
+    say(f"[run] prefill T=4096 algo={algo}")
+    g = run_layer(L, xb, res, algo=algo)
     check_logits(g, L, xb)
     check_topk(g, L)
     check_lookup(g, L)
@@ -135,6 +136,38 @@ def test_many_tokens_per_expert_mfma(bits):
     L = layer(shape.name, bits, shape)
     g, _, _ = _stages(L, 40, seed=4, algo=moe.ALGO_MFMA)
     assert g["counts"].max() > 16
+
+
+# Grouped-GEMM shapes: ring depths 1, 2 and 4 on both kernels, items with fewer
+# than 4 tiles, ragged last tiles, k = 1.
+GEMM_SHAPES = [
+    mi.LayerShape("gemm_a", H=256, E=4, k=2, I=256, tokens=(200,), bits=(4,), zipf_s=None, n_resident=2),
+    mi.LayerShape("gemm_b", H=1024, E=6, k=3, I=384, tokens=(130,), bits=(4,), zipf_s=0.8, n_resident=3),
+    mi.LayerShape("gemm_c", H=640, E=3, k=1, I=512, tokens=(97,), bits=(4,), zipf_s=None, n_resident=1),
+]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=[s.name for s in GEMM_SHAPES])
+def test_grouped_gemm_shapes(shape):
+    L = layer(shape.name, 4, shape)
+    T = shape.tokens[0]
+    rows = None if shape.name != "gemm_b" else list(range(0, T * shape.k, 4))
+    g, _, _ = _stages(L, T, seed=5, ffn_rows=rows, algo=moe.ALGO_GEMM)
+    assert g["counts"].max() > 16       # several work tiles per expert
+
+
+def test_grouped_gemm_auto_choice():
+    """AUTO takes the grouped GEMM when experts average >= 64 tokens, and its
+    outputs agree with the per-tile path to the same tolerance."""
+    shape = GEMM_SHAPES[0]
+    L = layer(shape.name, 4, shape)
+    xb, res = mi.make_activations(shape.H, 200, 6)
+    a = run_layer(L, xb, res, algo=moe.ALGO_AUTO)
+    b = run_layer(L, xb, res, algo=moe.ALGO_GEMM)
+    c = run_layer(L, xb, res, algo=moe.ALGO_MFMA)
+    assert np.array_equal(a["y_rows"], b["y_rows"])
+    mr, mae = tolerance_metrics(b["y_rows"], c["y_rows"])
+    assert mr <= 1e-2 and mae <= 1e-3
 
 
 def test_split_calls_gateup_h_matches_oracle():

@@ -192,7 +192,10 @@ def test_work_list_covers_every_pair_once(orc):
         wl = orc.work_list(ids, E, k, 16)
         counts = np.bincount(ids.ravel(), minlength=E)
         assert wl.shape == (int(np.sum((counts + 15) // 16)), 20)
-        assert np.all(np.diff(wl[:, 0]) >= 0) and np.all(wl[:, 3] == 0)
+        assert np.all(np.diff(wl[:, 0]) >= 0)
+        # tile index within the expert: 0 at each expert's first tile, then +1
+        first = np.r_[True, wl[1:, 0] != wl[:-1, 0]]
+        assert np.all(wl[first, 3] == 0) and np.all(wl[~first, 3] == wl[np.r_[~first[1:], False], 3] + 1)
         assert np.all((wl[:, 2] >= 1) & (wl[:, 2] <= 16))
         # rows tile [0, T*k) contiguously in order
         assert wl[0, 1] == 0 and np.array_equal(wl[1:, 1], (wl[:, 1] + wl[:, 2])[:-1])

@@ -44,7 +44,7 @@
  *   - Limits: 0 <= T, T*k <= 65536; 1 <= E <= 1024; 1 <= k <= min(E, 32);
  *     H and I multiples of 128 with 128 <= H <= 8192 and 128 <= I <= 16384;
  *     group_size == 128.  Device pointers to codes and activations must be
- *     16-byte aligned, scale and bias arrays 4-byte aligned.
+ *     16-byte aligned, and so must scale and bias arrays.
  *   - Ids passed back in must come from these calls (or satisfy the same
  *     invariants); kernels skip out-of-range ids rather than touch memory
  *     outside the buffers, and the results for such ids are unspecified.

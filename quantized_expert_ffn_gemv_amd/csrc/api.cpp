@@ -77,8 +77,8 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* w
             return fail(MOE_ERR_INVALID_ARG, "%s: weights matrix %d has a NULL pointer", fn, m);
         if (!aligned(w->q[m], 16))
             return fail(MOE_ERR_INVALID_ARG, "%s: weights.q[%d] is not 16-byte aligned", fn, m);
-        if (!aligned(w->scale[m], 4) || !aligned(w->bias[m], 4))
-            return fail(MOE_ERR_INVALID_ARG, "%s: weights.scale/bias[%d] is not 4-byte aligned", fn, m);
+        if (!aligned(w->scale[m], 16) || !aligned(w->bias[m], 16))
+            return fail(MOE_ERR_INVALID_ARG, "%s: weights.scale/bias[%d] is not 16-byte aligned", fn, m);
     }
     return MOE_OK;
 }

@@ -151,6 +151,10 @@ int launch_gateup_gemv(const FfnArgs& a, hipStream_t s);
 int launch_down_gemv(const FfnArgs& a, hipStream_t s);
 int launch_gateup_mfma(const FfnArgs& a, hipStream_t s);
 int launch_down_mfma(const FfnArgs& a, hipStream_t s);
+bool dec_gateup_fits(const moe_dims& d);
+bool dec_down_fits(const moe_dims& d);
+int launch_gateup_dec(const FfnArgs& a, hipStream_t s);
+int launch_down_dec(const FfnArgs& a, hipStream_t s);
 int launch_combine(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,
                    const uint16_t* residual, uint16_t* out, hipStream_t s);
 

@@ -598,6 +598,8 @@ static void down_dispatch(int D, int SJ, int KS, const moe_dims& d, size_t lds, 
 int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
+    // shapes whose activation tile fits in LDS take the staged-tile kernel
+    if (dec_gateup_fits(d)) return launch_gateup_dec(a, s);
     MfmaParams p = mfma_params(a);
     p.qa = a.w.q[0]; p.sa = a.w.scale[0]; p.ba = a.w.bias[0];
     p.qb = a.w.q[1]; p.sb = a.w.scale[1]; p.bb = a.w.bias[1];
@@ -619,6 +621,7 @@ static int down_k_split(int NG) { return NG >= 16 ? 4 : (NG >= 8 ? 2 : 1); }
 int launch_down_mfma(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
+    if (dec_down_fits(d)) return launch_down_dec(a, s);
     MfmaParams p = mfma_params(a);
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
     const int NG = d.I / kGroup, KS = down_k_split(NG), NGW = (NG + KS - 1) / KS;

@@ -6,7 +6,7 @@ renormalised gates, expert intermediate 512, SwiGLU, 4-bit weights with fp16
 scale and bias per group of 128, Zipf(1.1) expert popularity), a batch of
 --tokens decode tokens (default 32).  A step is one pass of the whole layer:
 
-    route_topk -> slot_lookup -> permute -> expert_gateup -> expert_down -> combine
+    route_dispatch (router, top-k, slot lookup, grouping) -> expert_gateup -> expert_down -> combine
 
 Successive steps cycle through --layers independently generated weight sets
 (like successive layers of a model; 4 x 428 MB by default), so the weights
@@ -109,10 +109,9 @@ class Runner:
         L = self.layers[i % len(self.layers)]
         x, res = self.x[i % len(self.layers)], self.res[i % len(self.layers)]
         bits = L["w"].bits
-        moe.route_topk(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w)
-        moe.slot_lookup(d, b.topk_ids, L["table"], self.shape.E, b.pair_slot, b.miss, b.n_miss)
-        moe.permute(d, b.topk_ids, b.counts, b.offsets, b.sorted_pairs, b.pair_to_row, b.active, b.n_active,
-                    b.work_list, b.n_work)
+        moe.route_dispatch(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w, L["table"],
+                           self.shape.E, b.pair_slot, b.miss, b.n_miss, b.counts, b.offsets, b.sorted_pairs,
+                           b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work)
         if ev is not None:
             ev[0].record()
         moe.expert_gateup(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, self.algo)

@@ -200,6 +200,39 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_c
                 int32_t* active_experts, int32_t* n_active, int32_t* work_list, int32_t* n_work,
                 void* stream);
 
+/* Steps 1-4 with one argument block: moe_route_topk, then moe_slot_lookup and
+ * moe_permute on the ids it picked, with the same outputs bit for bit.  When
+ * T*k <= 4096 the last three run as one workgroup in a single launch (a
+ * decode step then costs two launches for routing instead of four); larger
+ * calls enqueue the kernels of the separate calls.  Every field has the
+ * meaning, layout and alignment it has in those calls; host_doorbell and
+ * last_use may be NULL.  The struct itself is read on the host during the
+ * call only. */
+typedef struct moe_dispatch {
+    int32_t* topk_ids;              /* [T][k] */
+    float* topk_w;                  /* [T][k] */
+    const int32_t* slot_of_expert;  /* [E] */
+    int32_t n_slots;
+    int32_t* pair_slot;             /* [T*k] */
+    int32_t* miss_experts;          /* [E] */
+    int32_t* n_miss;                /* [1] */
+    int32_t* host_doorbell;         /* pinned host, or NULL */
+    uint32_t* last_use;             /* [n_slots], or NULL */
+    uint32_t step;
+    int32_t* expert_counts;         /* [E] */
+    int32_t* expert_offsets;        /* [E+1] */
+    int32_t* sorted_pairs;          /* [T*k] */
+    int32_t* pair_to_row;           /* [T*k] */
+    int32_t* active_experts;        /* [E] */
+    int32_t* n_active;              /* [1] */
+    int32_t* work_list;             /* [capacity][MOE_WORK_ENTRY_INTS] */
+    int32_t* n_work;                /* [1] */
+} moe_dispatch;
+
+int moe_route_dispatch(const moe_dims* dims, const uint16_t* x, const float* w_router,
+                       const float* router_bias, int renormalize, float* logits,
+                       const moe_dispatch* out, void* stream);
+
 /* Entries the work list of these dims can need (host-only):
  * min(E, T*k) + T*k / MOE_WORK_TILE_ROWS. */
 int moe_work_list_capacity(const moe_dims* dims, int32_t* entries);

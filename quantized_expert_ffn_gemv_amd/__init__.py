@@ -27,6 +27,7 @@ OP_ROUTE, OP_LOOKUP, OP_PERMUTE, OP_FFN, OP_COMBINE = 0, 1, 2, 3, 4
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
     "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute", "moe_work_list_capacity",
+    "moe_route_dispatch",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_combine",
 )
 
@@ -40,6 +41,18 @@ class MoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class DispatchC(ctypes.Structure):
+    """struct moe_dispatch (include/moe.h)."""
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("slot_of_expert", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
+                ("pair_slot", ctypes.c_void_p), ("miss_experts", ctypes.c_void_p), ("n_miss", ctypes.c_void_p),
+                ("host_doorbell", ctypes.c_void_p), ("last_use", ctypes.c_void_p), ("step", ctypes.c_uint32),
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("sorted_pairs", ctypes.c_void_p), ("pair_to_row", ctypes.c_void_p),
+                ("active_experts", ctypes.c_void_p), ("n_active", ctypes.c_void_p),
+                ("work_list", ctypes.c_void_p), ("n_work", ctypes.c_void_p)]
 
 
 class QWeightsC(ctypes.Structure):
@@ -69,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.moe_slot_lookup.argtypes = [Dp, P, P, i32, P, P, P, P, P, u32, P]
     L.moe_permute.argtypes = [Dp, P, P, P, P, P, P, P, P, P, P]
     L.moe_work_list_capacity.argtypes = [Dp, ctypes.POINTER(i32)]
+    L.moe_route_dispatch.argtypes = [Dp, P, P, P, ctypes.c_int, P, ctypes.POINTER(DispatchC), P]
     for name in ("moe_expert_ffn_q4", "moe_expert_ffn_q2"):
         getattr(L, name).argtypes = [Dp, P, P, P, Wp, P, ctypes.c_int, P, sz, P]
     L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P]
@@ -173,6 +187,19 @@ def permute(d: Dims, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair
                              _ptr(work_list), _ptr(n_work), _stream(stream)))
 
 
+def route_dispatch(d: Dims, x, w_router, router_bias, renormalize: bool, logits, topk_ids, topk_w,
+                   slot_of_expert, n_slots: int, pair_slot, miss_experts, n_miss, expert_counts, expert_offsets,
+                   sorted_pairs, pair_to_row, active_experts, n_active, work_list, n_work,
+                   host_doorbell=None, last_use=None, step: int = 0, stream=None):
+    """moe_route_dispatch: route_topk + slot_lookup + permute in one call."""
+    o = DispatchC(_ptr(topk_ids), _ptr(topk_w), _ptr(slot_of_expert), int(n_slots), _ptr(pair_slot),
+                  _ptr(miss_experts), _ptr(n_miss), _ptr(host_doorbell), _ptr(last_use), int(step) & 0xFFFFFFFF,
+                  _ptr(expert_counts), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_to_row),
+                  _ptr(active_experts), _ptr(n_active), _ptr(work_list), _ptr(n_work))
+    _check(lib().moe_route_dispatch(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                    int(bool(renormalize)), _ptr(logits), ctypes.byref(o), _stream(stream)))
+
+
 def _nbytes(t) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
@@ -221,7 +248,7 @@ from .layer import LayerBuffers, layer_forward  # noqa: E402  (orchestration of 
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
-    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk",
+    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
     "expert_ffn_q2", "expert_gateup", "expert_down", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
     "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",

@@ -260,6 +260,64 @@ int moe_permute(const moe_dims* d, const int32_t* topk_ids, int32_t* counts, int
     return ok();
 }
 
+int moe_route_dispatch(const moe_dims* d, const uint16_t* x, const float* w_router, const float* router_bias,
+                       int renormalize, float* logits, const moe_dispatch* o, void* stream) {
+    const char* fn = "moe_route_dispatch";
+    int st = check_dims(fn, d, true, false);
+    if (st) return st;
+    if (o == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (o->n_slots < 0) return fail(MOE_ERR_INVALID_ARG, "%s: n_slots = %d is negative", fn, o->n_slots);
+    REQUIRE_PTR(o->slot_of_expert, 4);
+    REQUIRE_PTR(o->miss_experts, 4);
+    REQUIRE_PTR(o->n_miss, 4);
+    REQUIRE_PTR(o->expert_counts, 4);
+    REQUIRE_PTR(o->expert_offsets, 4);
+    REQUIRE_PTR(o->active_experts, 4);
+    REQUIRE_PTR(o->n_active, 4);
+    REQUIRE_PTR(o->n_work, 4);
+    if (d->T > 0) {
+        REQUIRE_PTR(x, 16);
+        REQUIRE_PTR(w_router, 16);
+        REQUIRE_PTR(logits, 4);
+        REQUIRE_PTR(o->topk_ids, 4);
+        REQUIRE_PTR(o->topk_w, 4);
+        REQUIRE_PTR(o->pair_slot, 4);
+        REQUIRE_PTR(o->sorted_pairs, 4);
+        REQUIRE_PTR(o->pair_to_row, 4);
+        REQUIRE_PTR(o->work_list, 16);
+    }
+    if (router_bias && !aligned(router_bias, 4))
+        return fail(MOE_ERR_INVALID_ARG, "%s: router_bias misaligned", fn);
+    if (o->host_doorbell && !aligned(o->host_doorbell, 4))
+        return fail(MOE_ERR_INVALID_ARG, "%s: host_doorbell misaligned", fn);
+    if (o->last_use && !aligned(o->last_use, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: last_use misaligned", fn);
+    const hipStream_t s = as_stream(stream);
+    st = moe::launch_router_logits(*d, x, w_router, router_bias, logits, s);
+    if (!st && moe::dispatch_fused(*d)) {
+        moe::DispatchArgs a{};
+        a.renorm = renormalize;
+        a.ids = o->topk_ids; a.gates = o->topk_w;
+        a.table = o->slot_of_expert; a.n_slots = o->n_slots;
+        a.pair_slot = o->pair_slot; a.miss = o->miss_experts; a.n_miss = o->n_miss;
+        a.doorbell = o->host_doorbell; a.last_use = o->last_use; a.step = o->step;
+        a.counts = o->expert_counts; a.offsets = o->expert_offsets; a.sorted_pairs = o->sorted_pairs;
+        a.pair_to_row = o->pair_to_row; a.active = o->active_experts; a.n_active = o->n_active;
+        a.work = o->work_list; a.n_work = o->n_work;
+        st = moe::launch_dispatch(*d, logits, a, s);
+    } else if (!st) {
+        // too many pairs for one workgroup's LDS: the three kernels of the separate calls
+        if (d->T > 0) st = moe::launch_topk(*d, logits, renormalize, o->topk_ids, o->topk_w, s);
+        if (!st)
+            st = moe::launch_slot_lookup(*d, o->topk_ids, o->slot_of_expert, o->n_slots, o->pair_slot,
+                                         o->miss_experts, o->n_miss, o->host_doorbell, o->last_use, o->step, s);
+        if (!st)
+            st = moe::launch_permute(*d, o->topk_ids, o->expert_counts, o->expert_offsets, o->sorted_pairs,
+                                     o->pair_to_row, o->active_experts, o->n_active, o->work_list, o->n_work, s);
+    }
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 int moe_expert_ffn_q4(const moe_dims* d, const uint16_t* x, const int32_t* work_list,
                       const int32_t* n_work, const moe_qweights* w, uint16_t* y, int algo, void* ws,
                       size_t ws_bytes, void* stream) {

@@ -128,6 +128,31 @@ int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32
                    int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
                    int32_t* work, int32_t* n_work, hipStream_t s);
 
+// Outputs of top-k, slot lookup and grouping, for the one-launch dispatch.
+struct DispatchArgs {
+    int T, E, k, P, renorm;
+    int32_t* ids;
+    float* gates;
+    const int32_t* table;
+    int n_slots;
+    int32_t* pair_slot;
+    int32_t* miss;
+    int32_t* n_miss;
+    int32_t* doorbell;
+    uint32_t* last_use;
+    uint32_t step;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_pairs;
+    int32_t* pair_to_row;
+    int32_t* active;
+    int32_t* n_active;
+    int32_t* work;
+    int32_t* n_work;
+};
+bool dispatch_fused(const moe_dims& d);
+int launch_dispatch(const moe_dims& d, const float* logits, const DispatchArgs& a, hipStream_t s);
+
 struct FfnArgs {
     moe_dims d;
     int bits;

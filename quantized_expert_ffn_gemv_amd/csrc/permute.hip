@@ -7,8 +7,10 @@
 //
 // Both run as a single workgroup: at decode sizes they touch a few KB, so one
 // CU finishes them in a few microseconds without any grid-wide sync, and the
-// integer results are deterministic by construction.
-#include "common.h"
+// integer results are deterministic by construction.  dispatch_kernel runs
+// top-k, the lookup and the grouping back to back in one workgroup, so a
+// decode step pays one launch for all three.
+#include "topk_ops.h"
 
 namespace moe {
 
@@ -44,16 +46,12 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
 constexpr int kMaxE = 1024;
 
 // ---------------------------------------------------------------- lookup
-__global__ __launch_bounds__(1024) void slot_lookup_kernel(const int32_t* __restrict__ ids, int P,
-                                                           int E, const int32_t* __restrict__ table,
-                                                           int n_slots, int32_t* __restrict__ pair_slot,
-                                                           int32_t* __restrict__ miss,
-                                                           int32_t* __restrict__ n_miss,
-                                                           int32_t* doorbell,
-                                                           uint32_t* __restrict__ last_use,
-                                                           uint32_t step) {
-    __shared__ int flag[kMaxE];
-    __shared__ int wsum[16];
+// Workgroup-wide body (blockDim = 1024): `ids` may live in global memory or
+// LDS; `flag` is LDS scratch of E ints, `wsum` of 16.
+__device__ void slot_lookup_body(const int32_t* ids, int P, int E, const int32_t* __restrict__ table,
+                                 int n_slots, int32_t* __restrict__ pair_slot, int32_t* __restrict__ miss,
+                                 int32_t* __restrict__ n_miss, int32_t* doorbell,
+                                 uint32_t* __restrict__ last_use, uint32_t step, int* flag, int* wsum) {
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x) flag[e] = 0;
     __syncthreads();
@@ -87,6 +85,19 @@ __global__ __launch_bounds__(1024) void slot_lookup_kernel(const int32_t* __rest
     }
 }
 
+__global__ __launch_bounds__(1024) void slot_lookup_kernel(const int32_t* __restrict__ ids, int P,
+                                                           int E, const int32_t* __restrict__ table,
+                                                           int n_slots, int32_t* __restrict__ pair_slot,
+                                                           int32_t* __restrict__ miss,
+                                                           int32_t* __restrict__ n_miss,
+                                                           int32_t* doorbell,
+                                                           uint32_t* __restrict__ last_use,
+                                                           uint32_t step) {
+    __shared__ int flag[kMaxE];
+    __shared__ int wsum[16];
+    slot_lookup_body(ids, P, E, table, n_slots, pair_slot, miss, n_miss, doorbell, last_use, step, flag, wsum);
+}
+
 int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* table, int32_t n_slots,
                        int32_t* pair_slot, int32_t* miss, int32_t* n_miss, int32_t* doorbell,
                        uint32_t* last_use, uint32_t step, hipStream_t s) {
@@ -111,30 +122,25 @@ int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* tab
 // tile from one 80-byte read.
 constexpr int kPermWaves = 8;
 
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                       int k, int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ sorted_pairs,
-                                                       int32_t* __restrict__ pair_to_row,
-                                                       int32_t* __restrict__ active,
-                                                       int32_t* __restrict__ n_active,
-                                                       int32_t* __restrict__ work,
-                                                       int32_t* __restrict__ n_work) {
-    __shared__ int cnt[kPermWaves][kMaxE];
-    __shared__ int offs[kMaxE];
-    __shared__ int cnts[kMaxE];
-    __shared__ int wpos[kMaxE];
-    __shared__ int wsum[16];
+// Workgroup-wide body (blockDim = 1024).  LDS scratch: `cnt` kPermWaves x E
+// ints (row stride E), `offs`, `cnts`, `wpos` E ints each, `wsum` 16.
+__device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* __restrict__ counts,
+                             int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+                             int32_t* __restrict__ pair_to_row, int32_t* __restrict__ active,
+                             int32_t* __restrict__ n_active, int32_t* __restrict__ work,
+                             int32_t* __restrict__ n_work, int* cnt_flat, int* offs, int* cnts, int* wpos,
+                             int* wsum) {
+    auto cnt = [&](int w, int e) -> int& { return cnt_flat[w * E + e]; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int chunk = (P + kPermWaves - 1) / kPermWaves;
 
-    for (int i = tid; i < kPermWaves * E; i += blockDim.x) cnt[i / E][i % E] = 0;
+    for (int i = tid; i < kPermWaves * E; i += blockDim.x) cnt_flat[i] = 0;
     __syncthreads();
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
         for (int p = p0 + lane; p < p1; p += 64) {
             const int e = ids[p];
-            if (e >= 0 && e < E) atomicAdd(&cnt[wid][e], 1);
+            if (e >= 0 && e < E) atomicAdd(&cnt(wid, e), 1);
         }
     }
     __syncthreads();
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
         int tot = 0;
         if (e < E)
 #pragma unroll
-            for (int w = 0; w < kPermWaves; ++w) tot += cnt[w][e];
+            for (int w = 0; w < kPermWaves; ++w) tot += cnt(w, e);
         int sum, nsum, tsum;
         const int excl = block_exclusive_scan(tot, wsum, &sum);
         const int apos = block_exclusive_scan(tot > 0 ? 1 : 0, wsum, &nsum);
@@ -161,8 +167,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
             int b = running + excl;
 #pragma unroll
             for (int w = 0; w < kPermWaves; ++w) {
-                const int c = cnt[w][e];
-                cnt[w][e] = b;
+                const int c = cnt(w, e);
+                cnt(w, e) = b;
                 b += c;
             }
         }
@@ -196,13 +202,13 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
             const int rank = __popcll(same & lanemask_lt());
             const int n_same = __popcll(same);
             int row = 0;
-            if (ok) row = cnt[wid][e] + rank;
+            if (ok) row = cnt(wid, e) + rank;
             // all reads of this step happen before the last lane's update
             __builtin_amdgcn_wave_barrier();
             if (ok) {
                 sorted_pairs[row] = p;
                 pair_to_row[p] = row;
-                if (rank == n_same - 1) cnt[wid][e] = row + 1;
+                if (rank == n_same - 1) cnt(wid, e) = row + 1;
                 // work list: the row's slot in its expert's tile of kWorkRows rows
                 const int off = row - offs[e];
                 int32_t* ent = work + (size_t)(wpos[e] + off / kWorkRows) * kWorkInts;
@@ -224,11 +230,80 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     }
 }
 
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                       int k, int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted_pairs,
+                                                       int32_t* __restrict__ pair_to_row,
+                                                       int32_t* __restrict__ active,
+                                                       int32_t* __restrict__ n_active,
+                                                       int32_t* __restrict__ work,
+                                                       int32_t* __restrict__ n_work) {
+    __shared__ int cnt[kPermWaves * kMaxE];
+    __shared__ int offs[kMaxE];
+    __shared__ int cnts[kMaxE];
+    __shared__ int wpos[kMaxE];
+    __shared__ int wsum[16];
+    permute_body(ids, P, E, k, counts, offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work, cnt,
+                 offs, cnts, wpos, wsum);
+}
+
 int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
                    int32_t* work, int32_t* n_work, hipStream_t s) {
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, d.T * d.k, d.E, d.k, counts,
                        offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// -------------------------------------------------------------- dispatch
+// Top-k, slot lookup and grouping in one workgroup of 16 waves: wave w picks
+// the experts of tokens w, w + 16, ...; the ids also go to LDS, from where the
+// lookup and the counting sort read them.  P = T k <= kDispatchMaxP.
+constexpr int kDispatchMaxP = 4096;
+
+template <int PER>
+__global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict__ logits, DispatchArgs a) {
+    __shared__ int ids_s[kDispatchMaxP];
+    __shared__ int scratch[kPermWaves * kMaxE];          // lookup flags, then counting-sort counts
+    __shared__ int offs[kMaxE];
+    __shared__ int cnts[kMaxE];
+    __shared__ int wpos[kMaxE];
+    __shared__ int wsum[16];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int t = wid; t < a.T; t += 16) {
+        int my_id;
+        float my_gate;
+        topk_one_token<PER>(logits + (size_t)t * a.E, a.E, a.k, a.renorm, my_id, my_gate);
+        if (lane < a.k) {
+            a.ids[(size_t)t * a.k + lane] = my_id;
+            a.gates[(size_t)t * a.k + lane] = my_gate;
+            ids_s[t * a.k + lane] = my_id;
+        }
+    }
+    __syncthreads();
+    slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
+                     a.step, scratch, wsum);
+    __syncthreads();
+    permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
+                 a.work, a.n_work, scratch, offs, cnts, wpos, wsum);
+}
+
+bool dispatch_fused(const moe_dims& d) { return (long)d.T * d.k <= kDispatchMaxP && d.E <= kMaxE; }
+
+// T = 0 still launches: the lookup and grouping outputs (zero counts) are written.
+int launch_dispatch(const moe_dims& d, const float* logits, const DispatchArgs& args, hipStream_t s) {
+    if (!dispatch_fused(d)) return MOE_ERR_UNSUPPORTED;
+    DispatchArgs a = args;
+    a.T = d.T; a.E = d.E; a.k = d.k; a.P = d.T * d.k;
+    if (d.E <= 64)
+        hipLaunchKernelGGL(dispatch_kernel<1>, dim3(1), dim3(1024), 0, s, logits, a);
+    else if (d.E <= 256)
+        hipLaunchKernelGGL(dispatch_kernel<4>, dim3(1), dim3(1024), 0, s, logits, a);
+    else if (d.E <= 512)
+        hipLaunchKernelGGL(dispatch_kernel<8>, dim3(1), dim3(1024), 0, s, logits, a);
+    else
+        hipLaunchKernelGGL(dispatch_kernel<16>, dim3(1), dim3(1024), 0, s, logits, a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -1,7 +1,7 @@
 // Router logits and top-k gating (Betelgeuse page, MoE primer: the router
 // scores every expert from the token's hidden state and only the k best run;
 // gates are a softmax renormalised over the k picked).
-#include "common.h"
+#include "topk_ops.h"
 
 namespace moe {
 
@@ -177,29 +177,7 @@ int launch_router_logits(const moe_dims& d, const uint16_t* x, const float* w, c
 }
 
 // ------------------------------------------------------------------- top-k
-// One wave per token.  Each candidate gets a 64-bit key whose unsigned order
-// is the ranking: class (removed < NaN < number), then the value (with -0
-// folded onto +0), then the lower expert id.  k rounds of a wave-wide max
-// pick the experts in rank order; lane j keeps the j-th pick.
-__device__ __forceinline__ uint64_t rank_key(float v, int id) {
-    const uint64_t idpart = (uint64_t)(0xFFFFFu - (uint32_t)id);
-    if (v != v) return (1ull << 62) | idpart;
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;   // -0 -> +0: equal values tie
-    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return (2ull << 62) | ((uint64_t)ord << 20) | idpart;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    for (int off = 32; off > 0; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
+// One wave per token (topk_ops.h); lane j writes the j-th pick.
 template <int PER>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int renorm, int32_t* __restrict__ ids,
@@ -207,47 +185,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float* L = logits + (size_t)t * E;
-    float v[PER];
-    uint64_t key[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        int e = lane + 64 * i;
-        v[i] = (e < E) ? L[e] : 0.f;
-        key[i] = (e < E) ? rank_key(v[i], e) : 0ull;
-    }
-    int my_id = -1;
-    float my_v = 0.f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        const int id = (int)(0xFFFFFu - (uint32_t)(best & 0xFFFFFu));
-        // the owner removes the pick from its candidates
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (lane + 64 * i == id) key[i] = 0ull;
-        if (lane == j && id < E) {
-            my_id = id;
-            my_v = L[id];
-        }
-    }
-    const float top = __shfl(my_v, 0, kWave);
-    float den;
-    float num = (lane < k) ? expf(my_v - top) : 0.f;
-    if (renorm) {
-        den = wave_sum_xor(num, kWave);
-    } else {
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (lane + 64 * i < E) part += expf(v[i] - top);
-        den = wave_sum_xor(part, kWave);
-    }
+    int my_id;
+    float my_gate;
+    topk_one_token<PER>(logits + (size_t)t * E, E, k, renorm, my_id, my_gate);
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;
-        gates[(size_t)t * k + lane] = num / den;
+        gates[(size_t)t * k + lane] = my_gate;
     }
 }
 

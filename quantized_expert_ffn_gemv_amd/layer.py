@@ -1,10 +1,12 @@
 """One routed-MoE layer step as a fixed sequence of library calls.
 
 ``LayerBuffers`` preallocates every intermediate once (logits, picks, slot
-lookup results, permutation, workspace, expert outputs) so that a step is six
+lookup results, permutation, workspace, expert outputs) so that a step is three
 C calls on one stream with no allocation and no host synchronisation:
 
-    route_topk -> slot_lookup -> permute -> expert_ffn_q{4,2} -> combine
+    route_dispatch (route_topk + slot_lookup + permute) -> expert_ffn_q{4,2} -> combine
+
+``fused=False`` makes the same step from the separate routing calls.
 
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
@@ -16,7 +18,7 @@ from typing import Optional
 import torch
 
 from . import (ALGO_AUTO, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4,
-               permute, route_topk, slot_lookup, work_list_capacity, workspace_bytes)
+               permute, route_dispatch, route_topk, slot_lookup, work_list_capacity, workspace_bytes)
 
 
 @dataclass
@@ -71,14 +73,20 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
                   router_bias: Optional[torch.Tensor], weights: QWeights,
                   slot_of_expert: torch.Tensor, n_slots: int, residual: torch.Tensor,
                   out: torch.Tensor, algo: int = ALGO_AUTO, renormalize: bool = True,
-                  host_doorbell=None, last_use=None, step: int = 0, stream=None) -> None:
+                  host_doorbell=None, last_use=None, step: int = 0, stream=None, fused: bool = True) -> None:
     """Enqueue one layer step; `out` may be `residual`."""
     d = buf.d
-    route_topk(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w, stream)
-    slot_lookup(d, buf.topk_ids, slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss,
-                host_doorbell, last_use, step, stream)
-    permute(d, buf.topk_ids, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active,
-            buf.n_active, buf.work_list, buf.n_work, stream)
+    if fused:
+        route_dispatch(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w,
+                       slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets,
+                       buf.sorted_pairs, buf.pair_to_row, buf.active, buf.n_active, buf.work_list, buf.n_work,
+                       host_doorbell, last_use, step, stream)
+    else:
+        route_topk(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w, stream)
+        slot_lookup(d, buf.topk_ids, slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss,
+                    host_doorbell, last_use, step, stream)
+        permute(d, buf.topk_ids, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active,
+                buf.n_active, buf.work_list, buf.n_work, stream)
     ffn = expert_ffn_q4 if weights.bits == 4 else expert_ffn_q2
     ffn(d, x, buf.work_list, buf.n_work, weights, buf.y_rows, algo, buf.workspace, None, stream)
     combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)

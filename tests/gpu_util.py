@@ -98,7 +98,8 @@ def poison_(t: torch.Tensor):
         t.fill_(-7777)
 
 
-def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, table: Optional[np.ndarray] = None):
+def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, table: Optional[np.ndarray] = None,
+              fused: bool = True):
     """All stages on the GPU; returns host copies of every output."""
     sh = L.shape
     T = xb.shape[0]
@@ -111,7 +112,7 @@ def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, tab
     out_d = torch.empty_like(r_d)
     poison_(out_d)
     tab = L.table_d if table is None else to_dev(table)
-    moe.layer_forward(buf, x_d, L.Wr_d, L.bias_d, L.weights_d, tab, sh.E, r_d, out_d, algo=algo)
+    moe.layer_forward(buf, x_d, L.Wr_d, L.bias_d, L.weights_d, tab, sh.E, r_d, out_d, algo=algo, fused=fused)
     torch.cuda.synchronize()
     P = T * sh.k
     return dict(

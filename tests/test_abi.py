@@ -142,3 +142,32 @@ def test_zero_tokens_need_no_buffers():
     w = _qw()
     assert L.moe_expert_ffn_q4(ctypes.byref(d), None, None, None, ctypes.byref(w), None, 0, None, 0,
                                None) == moe.OK
+
+
+def _dispatch(**over):
+    f = {name: FAKE for name, _ in moe.DispatchC._fields_}
+    f.update(n_slots=8, step=0, host_doorbell=None, last_use=None)
+    f.update(over)
+    return moe.DispatchC(**f)
+
+
+def test_route_dispatch_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    call = lambda o, x=FAKE, bias=None: L.moe_route_dispatch(ctypes.byref(d), x, FAKE, bias, 1, FAKE,
+                                                              None if o is None else ctypes.byref(o), None)
+    assert call(None) == moe.ERR_INVALID_ARG
+    assert "out is NULL" in moe.last_error()
+    assert call(_dispatch(), x=MISALIGNED) == moe.ERR_INVALID_ARG
+    assert call(_dispatch(), bias=MISALIGNED) == moe.ERR_INVALID_ARG
+    assert call(_dispatch(n_slots=-1)) == moe.ERR_INVALID_ARG
+    for name in ("topk_ids", "slot_of_expert", "pair_slot", "miss_experts", "n_miss", "expert_counts",
+                 "expert_offsets", "sorted_pairs", "pair_to_row", "active_experts", "n_active", "work_list",
+                 "n_work"):
+        assert call(_dispatch(**{name: None})) == moe.ERR_INVALID_ARG, name
+        assert name in moe.last_error()
+    assert call(_dispatch(work_list=FAKE + 4)) == moe.ERR_INVALID_ARG
+    assert call(_dispatch(host_doorbell=MISALIGNED)) == moe.ERR_INVALID_ARG
+    bad = moe.Dims(4, 256, 512, 8, 9, 128)
+    assert L.moe_route_dispatch(ctypes.byref(bad), FAKE, FAKE, None, 1, FAKE, ctypes.byref(_dispatch()),
+                                None) == moe.ERR_UNSUPPORTED

@@ -257,3 +257,49 @@ def test_doorbell_and_last_use():
                     buf.pair_slot, buf.miss, buf.n_miss, host_doorbell=bell)
     torch.cuda.synchronize()
     assert int(bell.item()) == 0 and int(buf.n_miss.item()) == 0
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("a3b", 1), ("a3b", 32), ("e512", 1), ("e64", 8)])
+def test_route_dispatch_matches_separate_calls(name, T):
+    """moe_route_dispatch (one launch for top-k, lookup and grouping) gives the
+    separate calls' outputs bit for bit; every layer test above also checks it
+    against the oracle, since layer_forward uses it."""
+    L = layer(name)
+    xb, res = mi.make_activations(L.shape.H, T, 11)
+    a = run_layer(L, xb, res, fused=True)
+    b = run_layer(L, xb, res, fused=False)
+    for key in ("logits", "ids", "gates", "pair_slot", "miss", "n_miss", "counts", "offsets", "sorted_pairs",
+                "pair_to_row", "active", "n_active", "work_list", "n_work", "y_rows", "out"):
+        if np.ndim(a[key]) == 0:
+            assert a[key] == b[key], key
+            continue
+        va, vb = np.asarray(a[key]), np.asarray(b[key])
+        if key in ("miss", "active"):
+            n = a["n_miss"] if key == "miss" else a["n_active"]
+            va, vb = va[:n], vb[:n]
+        if key == "work_list":
+            va, vb = va[: a["n_work"]], vb[: a["n_work"]]
+        assert np.array_equal(va.view(np.uint8), vb.view(np.uint8)), key
+
+
+def test_route_dispatch_doorbell_and_last_use():
+    L = layer("e64")
+    sh = L.shape
+    xb, _ = mi.make_activations(sh.H, 8, 0)
+    d = moe.dims(8, sh.H, sh.I, sh.E, sh.k)
+    buf = moe.LayerBuffers.allocate(d, 4)
+    x_d = torch.from_numpy(xb.view(np.int16)).cuda()
+    bell = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    last_use = torch.zeros(sh.E, dtype=torch.int32, device="cuda")
+    table = mi.make_slot_table(sh, 0, n_resident=4)
+    moe.route_dispatch(d, x_d, L.Wr_d, L.bias_d, True, buf.logits, buf.topk_ids, buf.topk_w,
+                       torch.from_numpy(table).cuda(), sh.E, buf.pair_slot, buf.miss, buf.n_miss, buf.counts,
+                       buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active, buf.n_active, buf.work_list,
+                       buf.n_work, host_doorbell=bell, last_use=last_use, step=91)
+    torch.cuda.synchronize()
+    ids = buf.topk_ids.cpu().numpy()
+    check_topk(dict(logits=buf.logits.cpu().numpy(), ids=ids, gates=buf.topk_w.cpu().numpy()), L)
+    ref = oracle.slot_lookup(ids, table, sh.E, last_use=np.zeros(sh.E, np.uint32), step=91, doorbell=0)
+    assert np.array_equal(buf.miss.cpu().numpy()[: ref["n_miss"]], ref["miss"])
+    assert int(bell.item()) == ref["doorbell"] == ref["n_miss"] > 0
+    assert np.array_equal(last_use.cpu().numpy().view(np.uint32), ref["last_use"])

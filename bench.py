@@ -111,7 +111,7 @@ class Runner:
         bits = L["w"].bits
         moe.route_dispatch(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w, L["table"],
                            self.shape.E, b.pair_slot, b.miss, b.n_miss, b.counts, b.offsets, b.sorted_pairs,
-                           b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work)
+                           b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work, sync=b.sync)
         if ev is not None:
             ev[0].record()
         moe.expert_gateup(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, self.algo)

@@ -201,13 +201,19 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_c
                 void* stream);
 
 /* Steps 1-4 with one argument block: moe_route_topk, then moe_slot_lookup and
- * moe_permute on the ids it picked, with the same outputs bit for bit.  When
- * T*k <= 4096 the last three run as one workgroup in a single launch (a
- * decode step then costs two launches for routing instead of four); larger
- * calls enqueue the kernels of the separate calls.  Every field has the
- * meaning, layout and alignment it has in those calls; host_doorbell and
- * last_use may be NULL.  The struct itself is read on the host during the
- * call only. */
+ * moe_permute on the ids it picked, with the same outputs bit for bit.  Every
+ * field has the meaning, layout and alignment it has in those calls;
+ * host_doorbell and last_use may be NULL.  The struct itself is read on the
+ * host during the call only.
+ *   sync  NULL, or int32 [MOE_DISPATCH_SYNC_INTS] device memory that holds
+ *         zeros before the first call (each call leaves it zero again).
+ *         With sync and 1 <= T <= 64, T*k <= 4096, the whole routing is one
+ *         launch: workgroups that finish a stage late run the next one,
+ *         signalled through these counters.  Calls that share one sync
+ *         buffer must be ordered (one stream).  Without sync, or for larger
+ *         calls, the router runs first, then (T*k <= 4096) top-k, lookup and
+ *         grouping in one workgroup, else the separate calls' kernels. */
+#define MOE_DISPATCH_SYNC_INTS 16
 typedef struct moe_dispatch {
     int32_t* topk_ids;              /* [T][k] */
     float* topk_w;                  /* [T][k] */
@@ -227,6 +233,7 @@ typedef struct moe_dispatch {
     int32_t* n_active;              /* [1] */
     int32_t* work_list;             /* [capacity][MOE_WORK_ENTRY_INTS] */
     int32_t* n_work;                /* [1] */
+    int32_t* sync;                  /* [MOE_DISPATCH_SYNC_INTS], or NULL */
 } moe_dispatch;
 
 int moe_route_dispatch(const moe_dims* dims, const uint16_t* x, const float* w_router,

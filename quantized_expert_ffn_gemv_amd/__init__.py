@@ -52,7 +52,7 @@ class DispatchC(ctypes.Structure):
                 ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
                 ("sorted_pairs", ctypes.c_void_p), ("pair_to_row", ctypes.c_void_p),
                 ("active_experts", ctypes.c_void_p), ("n_active", ctypes.c_void_p),
-                ("work_list", ctypes.c_void_p), ("n_work", ctypes.c_void_p)]
+                ("work_list", ctypes.c_void_p), ("n_work", ctypes.c_void_p), ("sync", ctypes.c_void_p)]
 
 
 class QWeightsC(ctypes.Structure):
@@ -172,6 +172,7 @@ def slot_lookup(d: Dims, topk_ids, slot_of_expert, n_slots: int, pair_slot, miss
 
 
 WORK_TILE_ROWS, WORK_ENTRY_INTS = 16, 20     # MOE_WORK_TILE_ROWS, MOE_WORK_ENTRY_INTS
+DISPATCH_SYNC_INTS = 16                      # MOE_DISPATCH_SYNC_INTS
 
 
 def work_list_capacity(d: Dims) -> int:
@@ -190,12 +191,13 @@ def permute(d: Dims, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair
 def route_dispatch(d: Dims, x, w_router, router_bias, renormalize: bool, logits, topk_ids, topk_w,
                    slot_of_expert, n_slots: int, pair_slot, miss_experts, n_miss, expert_counts, expert_offsets,
                    sorted_pairs, pair_to_row, active_experts, n_active, work_list, n_work,
-                   host_doorbell=None, last_use=None, step: int = 0, stream=None):
-    """moe_route_dispatch: route_topk + slot_lookup + permute in one call."""
+                   host_doorbell=None, last_use=None, step: int = 0, sync=None, stream=None):
+    """moe_route_dispatch: route_topk + slot_lookup + permute in one call.  `sync`:
+    None, or an int32 device tensor of DISPATCH_SYNC_INTS zeros (left zero)."""
     o = DispatchC(_ptr(topk_ids), _ptr(topk_w), _ptr(slot_of_expert), int(n_slots), _ptr(pair_slot),
                   _ptr(miss_experts), _ptr(n_miss), _ptr(host_doorbell), _ptr(last_use), int(step) & 0xFFFFFFFF,
                   _ptr(expert_counts), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_to_row),
-                  _ptr(active_experts), _ptr(n_active), _ptr(work_list), _ptr(n_work))
+                  _ptr(active_experts), _ptr(n_active), _ptr(work_list), _ptr(n_work), _ptr(sync))
     _check(lib().moe_route_dispatch(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(router_bias),
                                     int(bool(renormalize)), _ptr(logits), ctypes.byref(o), _stream(stream)))
 
@@ -248,7 +250,7 @@ from .layer import LayerBuffers, layer_forward  # noqa: E402  (orchestration of 
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
-    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch",
+    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
     "expert_ffn_q2", "expert_gateup", "expert_down", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
     "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",

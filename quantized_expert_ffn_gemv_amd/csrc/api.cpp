@@ -291,18 +291,25 @@ int moe_route_dispatch(const moe_dims* d, const uint16_t* x, const float* w_rout
     if (o->host_doorbell && !aligned(o->host_doorbell, 4))
         return fail(MOE_ERR_INVALID_ARG, "%s: host_doorbell misaligned", fn);
     if (o->last_use && !aligned(o->last_use, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: last_use misaligned", fn);
+    if (o->sync && !aligned(o->sync, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: sync misaligned", fn);
     const hipStream_t s = as_stream(stream);
+    moe::DispatchArgs a{};
+    a.renorm = renormalize;
+    a.ids = o->topk_ids; a.gates = o->topk_w;
+    a.table = o->slot_of_expert; a.n_slots = o->n_slots;
+    a.pair_slot = o->pair_slot; a.miss = o->miss_experts; a.n_miss = o->n_miss;
+    a.doorbell = o->host_doorbell; a.last_use = o->last_use; a.step = o->step;
+    a.counts = o->expert_counts; a.offsets = o->expert_offsets; a.sorted_pairs = o->sorted_pairs;
+    a.pair_to_row = o->pair_to_row; a.active = o->active_experts; a.n_active = o->n_active;
+    a.work = o->work_list; a.n_work = o->n_work;
+    if (o->sync && moe::route_dispatch_fused(*d)) {
+        // the whole routing in one launch
+        st = moe::launch_route_dispatch(*d, x, w_router, router_bias, logits, a, o->sync, s);
+        if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+        return ok();
+    }
     st = moe::launch_router_logits(*d, x, w_router, router_bias, logits, s);
     if (!st && moe::dispatch_fused(*d)) {
-        moe::DispatchArgs a{};
-        a.renorm = renormalize;
-        a.ids = o->topk_ids; a.gates = o->topk_w;
-        a.table = o->slot_of_expert; a.n_slots = o->n_slots;
-        a.pair_slot = o->pair_slot; a.miss = o->miss_experts; a.n_miss = o->n_miss;
-        a.doorbell = o->host_doorbell; a.last_use = o->last_use; a.step = o->step;
-        a.counts = o->expert_counts; a.offsets = o->expert_offsets; a.sorted_pairs = o->sorted_pairs;
-        a.pair_to_row = o->pair_to_row; a.active = o->active_experts; a.n_active = o->n_active;
-        a.work = o->work_list; a.n_work = o->n_work;
         st = moe::launch_dispatch(*d, logits, a, s);
     } else if (!st) {
         // too many pairs for one workgroup's LDS: the three kernels of the separate calls

@@ -130,7 +130,7 @@ int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32
 
 // Outputs of top-k, slot lookup and grouping, for the one-launch dispatch.
 struct DispatchArgs {
-    int T, E, k, P, renorm;
+    int T, H, E, k, P, renorm;
     int32_t* ids;
     float* gates;
     const int32_t* table;
@@ -152,6 +152,9 @@ struct DispatchArgs {
 };
 bool dispatch_fused(const moe_dims& d);
 int launch_dispatch(const moe_dims& d, const float* logits, const DispatchArgs& a, hipStream_t s);
+bool route_dispatch_fused(const moe_dims& d);
+int launch_route_dispatch(const moe_dims& d, const uint16_t* x, const float* w, const float* bias, float* logits,
+                          const DispatchArgs& a, int32_t* sync, hipStream_t s);
 
 struct FfnArgs {
     moe_dims d;

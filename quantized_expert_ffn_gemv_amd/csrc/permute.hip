@@ -10,6 +10,7 @@
 // integer results are deterministic by construction.  dispatch_kernel runs
 // top-k, the lookup and the grouping back to back in one workgroup, so a
 // decode step pays one launch for all three.
+#include "router_ops.h"
 #include "topk_ops.h"
 
 namespace moe {
@@ -304,6 +305,127 @@ int launch_dispatch(const moe_dims& d, const float* logits, const DispatchArgs& 
         hipLaunchKernelGGL(dispatch_kernel<8>, dim3(1), dim3(1024), 0, s, logits, a);
     else
         hipLaunchKernelGGL(dispatch_kernel<16>, dim3(1), dim3(1024), 0, s, logits, a);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// --------------------------------------------------------- route + dispatch
+// The whole routing of a decode batch in one launch.  Grid = (expert blocks)
+// x (token groups of kRouteTG tokens); workgroups of 1024 threads:
+//   1. every workgroup computes the logits of its 4 EB experts for its token
+//      group (router_ops.h, four 256-thread groups side by side);
+//   2. the last workgroup to finish a token group (a ticket counter per
+//      group) picks the top-k of that group's tokens, one wave per token;
+//   3. the last token group to finish (a second ticket) copies all ids to LDS
+//      and runs the slot lookup and the counting sort.
+// Nothing waits on another workgroup: the late arrivals do the next stage.
+// Writes before a ticket are released to the device with a fence, and the
+// winner acquires them with a fence, so the logits and ids written on other
+// CUs (other L2 slices) are seen.  Tickets live in sync[0] (token groups
+// done) and sync[1 + g] (expert blocks done for group g); each winner puts
+// its counter back to 0, so the buffer is all zero between calls.
+constexpr int kRouteTG = 8;
+constexpr int kRouteMaxT = 64;
+
+// Arrive at `counter` (out of `n` arrivals); true in every thread of the last
+// workgroup to arrive.  Every wave first waits for its own stores, so after
+// the barrier one release fence (thread 0) publishes the whole workgroup's
+// writes; the winner's acquire fence (thread 0, before the closing barrier)
+// makes the other workgroups' writes visible to all of its waves.  One fence
+// per workgroup: each is a write-back or invalidate of the CU's L2 slice.
+__device__ __forceinline__ bool ticket(int32_t* counter, int n, int* winner) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *winner = old == n - 1;
+        if (*winner) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    return *winner;
+}
+
+template <int EB, int NJ, int PER>
+__global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ w,
+                                                              const float* __restrict__ bias,
+                                                              float* __restrict__ logits, DispatchArgs a,
+                                                              int32_t* __restrict__ sync) {
+    __shared__ float part[4][4][EB][kRouteTG];
+    __shared__ int ids_s[kDispatchMaxP];
+    __shared__ int scratch[kPermWaves * kMaxE];
+    __shared__ int offs[kMaxE];
+    __shared__ int cnts[kMaxE];
+    __shared__ int wpos[kMaxE];
+    __shared__ int wsum[16];
+    __shared__ int winner;
+    const int tid = threadIdx.x, sub = tid >> 8, lane = tid & 63, wid = tid >> 6;
+    const int tg = blockIdx.y;
+    const int tb = tg * kRouteTG, te = min(a.T, tb + kRouteTG);
+
+    // 1. logits of this (expert block, token group)
+    router_block<EB, kRouteTG, NJ>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
+                                   part[sub], tid & 255);
+    if (!ticket(&sync[1 + tg], (int)gridDim.x, &winner)) return;
+
+    // 2. top-k of the group's tokens
+    if (wid < te - tb) {
+        const int t = tb + wid;
+        int my_id;
+        float my_gate;
+        topk_one_token<PER>(logits + (size_t)t * a.E, a.E, a.k, a.renorm, my_id, my_gate);
+        if (lane < a.k) {
+            a.ids[(size_t)t * a.k + lane] = my_id;
+            a.gates[(size_t)t * a.k + lane] = my_gate;
+        }
+    }
+    if (tid == 0) __hip_atomic_store(&sync[1 + tg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!ticket(&sync[0], (int)gridDim.y, &winner)) return;
+
+    // 3. lookup and grouping over all pairs
+    for (int p = tid; p < a.P; p += blockDim.x) ids_s[p] = a.ids[p];
+    __syncthreads();
+    slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
+                     a.step, scratch, wsum);
+    __syncthreads();
+    permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
+                 a.work, a.n_work, scratch, offs, cnts, wpos, wsum);
+    if (tid == 0) __hip_atomic_store(&sync[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+bool route_dispatch_fused(const moe_dims& d) {
+    return d.T >= 1 && d.T <= kRouteMaxT && dispatch_fused(d) && (d.H / 4 + 255) / 256 <= 8;
+}
+
+template <int EB, int NJ>
+static void rd_go(const moe_dims& d, const uint16_t* x, const float* w, const float* bias, float* logits,
+                  const DispatchArgs& a, int32_t* sync, hipStream_t s) {
+    const dim3 grid((unsigned)((d.E + 4 * EB - 1) / (4 * EB)), (unsigned)((d.T + kRouteTG - 1) / kRouteTG));
+    if (d.E <= 64)
+        hipLaunchKernelGGL((route_dispatch_kernel<EB, NJ, 1>), grid, dim3(1024), 0, s, x, w, bias, logits, a, sync);
+    else if (d.E <= 256)
+        hipLaunchKernelGGL((route_dispatch_kernel<EB, NJ, 4>), grid, dim3(1024), 0, s, x, w, bias, logits, a, sync);
+    else if (d.E <= 512)
+        hipLaunchKernelGGL((route_dispatch_kernel<EB, NJ, 8>), grid, dim3(1024), 0, s, x, w, bias, logits, a, sync);
+    else
+        hipLaunchKernelGGL((route_dispatch_kernel<EB, NJ, 16>), grid, dim3(1024), 0, s, x, w, bias, logits, a, sync);
+}
+
+int launch_route_dispatch(const moe_dims& d, const uint16_t* x, const float* w, const float* bias, float* logits,
+                          const DispatchArgs& args, int32_t* sync, hipStream_t s) {
+    if (!route_dispatch_fused(d)) return MOE_ERR_UNSUPPORTED;
+    DispatchArgs a = args;
+    a.T = d.T; a.H = d.H; a.E = d.E; a.k = d.k; a.P = d.T * d.k;
+    // one expert per 256-thread group; NJ 256-wide steps cover a quarter of H
+    const int nj = (d.H / 4 + 255) / 256;
+    switch (nj) {
+        case 1: rd_go<1, 1>(d, x, w, bias, logits, a, sync, s); break;
+        case 2: rd_go<1, 2>(d, x, w, bias, logits, a, sync, s); break;
+        case 3: rd_go<1, 3>(d, x, w, bias, logits, a, sync, s); break;
+        case 4: rd_go<1, 4>(d, x, w, bias, logits, a, sync, s); break;
+        case 5: case 6: rd_go<1, 6>(d, x, w, bias, logits, a, sync, s); break;
+        default: rd_go<1, 8>(d, x, w, bias, logits, a, sync, s); break;
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

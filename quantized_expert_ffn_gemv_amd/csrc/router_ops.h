@@ -1,0 +1,86 @@
+// Router logits for decode batches (Betelgeuse page, MoE primer: the router
+// scores every expert from the token's hidden state):
+//   logits[t][e] = sum_h x[t][h] * w[e][h] + bias[e]      (float32)
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// One 256-thread group (stid = 0..255) computes experts [e0, e0 + EB) for
+// tokens [tb, te).  Its 4 waves split K into quarters and each lane covers 4
+// consecutive k per 256-wide step (NJ steps).  All router-weight loads are
+// issued up front (EB * NJ float4 per lane), then tokens are processed TT at a
+// time with their activation loads independent of each other, so the group
+// is a couple of memory latencies long instead of a chain of dependent loads.
+// Partial sums are reduced across the wave with xor shuffles and across the 4
+// waves through `part` (LDS, this group's own).  Contains __syncthreads():
+// every group of the workgroup must call it with the same token range.
+template <int EB, int TT, int NJ>
+__device__ __forceinline__ void router_block(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                             const float* __restrict__ bias, float* __restrict__ logits, int H,
+                                             int E, int e0, int tb, int te, float (*part)[EB][TT], int stid) {
+    const int lane = stid & 63, wv = stid >> 6;
+    const int kq = H / 4;                        // this wave's quarter of K
+    const int kbase = wv * kq + lane * 4;
+    float4 wr[EB][NJ];
+#pragma unroll
+    for (int a = 0; a < EB; ++a)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int k = kbase + 256 * j;
+            const bool ok = (e0 + a < E) && (lane * 4 + 256 * j < kq);
+            wr[a][j] = ok ? *reinterpret_cast<const float4*>(w + (size_t)(e0 + a) * H + k)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    for (int t0 = tb; t0 < te; t0 += TT) {
+        uint2 xv[TT][NJ];
+#pragma unroll
+        for (int b = 0; b < TT; ++b)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool ok = (t0 + b < te) && (lane * 4 + 256 * j < kq);
+                xv[b][j] = ok ? *reinterpret_cast<const uint2*>(x + (size_t)(t0 + b) * H + kbase + 256 * j)
+                              : make_uint2(0, 0);
+            }
+        float acc[EB][TT];
+#pragma unroll
+        for (int b = 0; b < TT; ++b) {
+#pragma unroll
+            for (int a = 0; a < EB; ++a) acc[a][b] = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float x0 = bf16_bits_to_f32(xv[b][j].x & 0xFFFFu), x1 = bf16_bits_to_f32(xv[b][j].x >> 16);
+                const float x2 = bf16_bits_to_f32(xv[b][j].y & 0xFFFFu), x3 = bf16_bits_to_f32(xv[b][j].y >> 16);
+#pragma unroll
+                for (int a = 0; a < EB; ++a) {
+                    float s = acc[a][b];
+                    s = fmaf(x0, wr[a][j].x, s);
+                    s = fmaf(x1, wr[a][j].y, s);
+                    s = fmaf(x2, wr[a][j].z, s);
+                    s = fmaf(x3, wr[a][j].w, s);
+                    acc[a][b] = s;
+                }
+            }
+        }
+        float flat[EB * TT];
+#pragma unroll
+        for (int a = 0; a < EB; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b) flat[a * TT + b] = acc[a][b];
+        const float tot = wave_transpose_sum<EB * TT>(flat);
+        const int idx = wave_transpose_index<EB * TT>(lane);
+        if ((lane & ((64 / (EB * TT)) - 1)) == 0) part[wv][idx / TT][idx % TT] = tot;
+        __syncthreads();
+        if (stid < EB * TT) {
+            const int a = stid / TT, b = stid % TT;
+            if (e0 + a < E && t0 + b < te) {
+                const float v = (part[0][a][b] + part[1][a][b]) + (part[2][a][b] + part[3][a][b]);
+                logits[(size_t)(t0 + b) * E + e0 + a] = v + (bias ? bias[e0 + a] : 0.f);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace moe

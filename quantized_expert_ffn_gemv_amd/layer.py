@@ -17,7 +17,7 @@ from typing import Optional
 
 import torch
 
-from . import (ALGO_AUTO, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4,
+from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4,
                permute, route_dispatch, route_topk, slot_lookup, work_list_capacity, workspace_bytes)
 
 
@@ -41,6 +41,7 @@ class LayerBuffers:
     n_work: torch.Tensor          # int32 [1]
     workspace: torch.Tensor       # uint8, 256-byte aligned by the allocator
     y_rows: torch.Tensor          # bf16 bits as int16 [T*k, H]
+    sync: torch.Tensor            # int32 [DISPATCH_SYNC_INTS], zeros (route_dispatch's counters)
 
     @staticmethod
     def allocate(d: Dims, bits: int = 4, algo: int = ALGO_AUTO, device="cuda") -> "LayerBuffers":
@@ -66,6 +67,7 @@ class LayerBuffers:
             n_work=torch.zeros((1,), **i32),
             workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
             y_rows=torch.empty((max(T * k, 1), H), dtype=torch.int16, device=device),
+            sync=torch.zeros((DISPATCH_SYNC_INTS,), **i32),
         )
 
 
@@ -80,7 +82,7 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
         route_dispatch(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w,
                        slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets,
                        buf.sorted_pairs, buf.pair_to_row, buf.active, buf.n_active, buf.work_list, buf.n_work,
-                       host_doorbell, last_use, step, stream)
+                       host_doorbell, last_use, step, buf.sync, stream)
     else:
         route_topk(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w, stream)
         slot_lookup(d, buf.topk_ids, slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss,

@@ -303,3 +303,45 @@ def test_route_dispatch_doorbell_and_last_use():
     assert np.array_equal(buf.miss.cpu().numpy()[: ref["n_miss"]], ref["miss"])
     assert int(bell.item()) == ref["doorbell"] == ref["n_miss"] > 0
     assert np.array_equal(last_use.cpu().numpy().view(np.uint32), ref["last_use"])
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("a3b", 32), ("e512", 1)])
+def test_route_dispatch_paths_agree(name, T):
+    """The one-launch routing (with the sync counters), the two-launch routing
+    (sync = NULL) and the separate calls give the same outputs bit for bit, and
+    the counters are left zero for the next call (which is checked too)."""
+    L = layer(name)
+    sh = L.shape
+    xb, _ = mi.make_activations(sh.H, T, 12)
+    x_d = torch.from_numpy(xb.view(np.int16)).cuda()
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+    keys = ("logits", "topk_ids", "topk_w", "pair_slot", "n_miss", "counts", "offsets", "sorted_pairs",
+            "pair_to_row", "n_active", "n_work")
+
+    def dispatch(buf, sync):
+        moe.route_dispatch(d, x_d, L.Wr_d, L.bias_d, True, buf.logits, buf.topk_ids, buf.topk_w, L.table_d, sh.E,
+                           buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets, buf.sorted_pairs,
+                           buf.pair_to_row, buf.active, buf.n_active, buf.work_list, buf.n_work, sync=sync)
+
+    one = moe.LayerBuffers.allocate(d, 4)
+    two = moe.LayerBuffers.allocate(d, 4)
+    sep = moe.LayerBuffers.allocate(d, 4)
+    for _ in range(2):                                   # the second call relies on the counters' reset
+        dispatch(one, one.sync)
+        dispatch(two, None)
+        moe.route_topk(d, x_d, L.Wr_d, L.bias_d, True, sep.logits, sep.topk_ids, sep.topk_w)
+        moe.slot_lookup(d, sep.topk_ids, L.table_d, sh.E, sep.pair_slot, sep.miss, sep.n_miss)
+        moe.permute(d, sep.topk_ids, sep.counts, sep.offsets, sep.sorted_pairs, sep.pair_to_row, sep.active,
+                    sep.n_active, sep.work_list, sep.n_work)
+        torch.cuda.synchronize()
+        assert int(one.sync.abs().sum().item()) == 0
+        for key in keys:
+            a = getattr(one, key).cpu().numpy().view(np.uint8)
+            assert np.array_equal(a, getattr(two, key).cpu().numpy().view(np.uint8)), key
+            assert np.array_equal(a, getattr(sep, key).cpu().numpy().view(np.uint8)), key
+        nw = int(one.n_work.item())
+        assert np.array_equal(one.work_list[:nw].cpu().numpy(), sep.work_list[:nw].cpu().numpy())
+        na = int(one.n_active.item())
+        assert np.array_equal(one.active[:na].cpu().numpy(), sep.active[:na].cpu().numpy())
+        g = dict(logits=one.logits.cpu().numpy(), ids=one.topk_ids.cpu().numpy(), gates=one.topk_w.cpu().numpy())
+        check_topk(g, L)

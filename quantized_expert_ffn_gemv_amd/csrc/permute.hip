@@ -318,29 +318,25 @@ int launch_dispatch(const moe_dims& d, const float* logits, const DispatchArgs& 
 //   3. the last token group to finish (a second ticket) copies all ids to LDS
 //      and runs the slot lookup and the counting sort.
 // Nothing waits on another workgroup: the late arrivals do the next stage.
-// Writes before a ticket are released to the device with a fence, and the
-// winner acquires them with a fence, so the logits and ids written on other
-// CUs (other L2 slices) are seen.  Tickets live in sync[0] (token groups
+// Logits and ids cross workgroups as device-scope atomic stores and loads
+// (see ticket()), so they are seen on other CUs and L2 slices.  Tickets live in sync[0] (token groups
 // done) and sync[1 + g] (expert blocks done for group g); each winner puts
 // its counter back to 0, so the buffer is all zero between calls.
 constexpr int kRouteTG = 8;
 constexpr int kRouteMaxT = 64;
 
 // Arrive at `counter` (out of `n` arrivals); true in every thread of the last
-// workgroup to arrive.  Every wave first waits for its own stores, so after
-// the barrier one release fence (thread 0) publishes the whole workgroup's
-// writes; the winner's acquire fence (thread 0, before the closing barrier)
-// makes the other workgroups' writes visible to all of its waves.  One fence
-// per workgroup: each is a write-back or invalidate of the CU's L2 slice.
+// workgroup to arrive.  Data handed between workgroups through a ticket is
+// written with device-scope atomic stores and read with device-scope atomic
+// loads, which go to the device's point of coherence: no L2 write-back or
+// invalidate is needed (as a fence would do, for the whole L2 slice, at a cost
+// of microseconds).  Every wave waits for its stores to complete before the
+// barrier, so they are all done before thread 0 takes the ticket.
 __device__ __forceinline__ bool ticket(int32_t* counter, int n, int* winner) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *winner = old == n - 1;
-        if (*winner) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
+    if (threadIdx.x == 0)
+        *winner = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
     __syncthreads();
     return *winner;
 }
@@ -364,8 +360,8 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     const int tb = tg * kRouteTG, te = min(a.T, tb + kRouteTG);
 
     // 1. logits of this (expert block, token group)
-    router_block<EB, kRouteTG, NJ>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
-                                   part[sub], tid & 255);
+    router_block<EB, kRouteTG, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
+                                         part[sub], tid & 255);
     if (!ticket(&sync[1 + tg], (int)gridDim.x, &winner)) return;
 
     // 2. top-k of the group's tokens
@@ -373,9 +369,9 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
         const int t = tb + wid;
         int my_id;
         float my_gate;
-        topk_one_token<PER>(logits + (size_t)t * a.E, a.E, a.k, a.renorm, my_id, my_gate);
+        topk_one_token<PER, true>(logits + (size_t)t * a.E, a.E, a.k, a.renorm, my_id, my_gate);
         if (lane < a.k) {
-            a.ids[(size_t)t * a.k + lane] = my_id;
+            __hip_atomic_store(a.ids + (size_t)t * a.k + lane, my_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             a.gates[(size_t)t * a.k + lane] = my_gate;
         }
     }
@@ -383,7 +379,8 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     if (!ticket(&sync[0], (int)gridDim.y, &winner)) return;
 
     // 3. lookup and grouping over all pairs
-    for (int p = tid; p < a.P; p += blockDim.x) ids_s[p] = a.ids[p];
+    for (int p = tid; p < a.P; p += blockDim.x)
+        ids_s[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);

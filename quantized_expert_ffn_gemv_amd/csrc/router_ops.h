@@ -16,7 +16,10 @@ namespace moe {
 // Partial sums are reduced across the wave with xor shuffles and across the 4
 // waves through `part` (LDS, this group's own).  Contains __syncthreads():
 // every group of the workgroup must call it with the same token range.
-template <int EB, int TT, int NJ>
+// COHERENT: store the logits with device-scope atomic stores, which reach the
+// device's point of coherence without a cache write-back (for readers on
+// other CUs in the same kernel).
+template <int EB, int TT, int NJ, bool COHERENT = false>
 __device__ __forceinline__ void router_block(const uint16_t* __restrict__ x, const float* __restrict__ w,
                                              const float* __restrict__ bias, float* __restrict__ logits, int H,
                                              int E, int e0, int tb, int te, float (*part)[EB][TT], int stid) {
@@ -76,7 +79,10 @@ __device__ __forceinline__ void router_block(const uint16_t* __restrict__ x, con
             const int a = stid / TT, b = stid % TT;
             if (e0 + a < E && t0 + b < te) {
                 const float v = (part[0][a][b] + part[1][a][b]) + (part[2][a][b] + part[3][a][b]);
-                logits[(size_t)(t0 + b) * E + e0 + a] = v + (bias ? bias[e0 + a] : 0.f);
+                const float out = v + (bias ? bias[e0 + a] : 0.f);
+                float* dst = logits + (size_t)(t0 + b) * E + e0 + a;
+                if constexpr (COHERENT) __hip_atomic_store(dst, out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else *dst = out;
             }
         }
         __syncthreads();

@@ -52,7 +52,9 @@ __device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
 // One token: the wave reads its E logits L[0..E) (PER per lane), picks k
 // (k <= 64) and returns, in lane j < k, the j-th pick and its gate.
 // renorm = 1: gates are a softmax over the k picked; 0: over all E.
-template <int PER>
+// COHERENT: read the logits with device-scope atomic loads (written by other
+// CUs in the same kernel).
+template <int PER, bool COHERENT = false>
 __device__ __forceinline__ void topk_one_token(const float* __restrict__ L, int E, int k, int renorm,
                                                int& my_id, float& my_gate) {
     const int lane = threadIdx.x & 63;
@@ -61,7 +63,8 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ L, int 
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        v[i] = (e < E) ? L[e] : 0.f;
+        if constexpr (COHERENT) v[i] = (e < E) ? __hip_atomic_load(L + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+        else v[i] = (e < E) ? L[e] : 0.f;
         key[i] = (e < E) ? rank_key(v[i], e) : 0ull;
     }
     my_id = -1;

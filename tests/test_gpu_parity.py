@@ -309,16 +309,18 @@ def test_route_dispatch_doorbell_and_last_use():
 def test_route_dispatch_paths_agree(name, T):
     """The one-launch routing (with the sync counters), the two-launch routing
     (sync = NULL) and the separate calls give the same outputs bit for bit, and
-    the counters are left zero for the next call (which is checked too)."""
+    the counters are left zero for the next call (which is checked too), on
+    two different batches in a row."""
     L = layer(name)
     sh = L.shape
-    xb, _ = mi.make_activations(sh.H, T, 12)
-    x_d = torch.from_numpy(xb.view(np.int16)).cuda()
+    # two different batches through the same buffers: a stage that read the
+    # previous call's logits or ids would show up in the second call
+    xs = [torch.from_numpy(mi.make_activations(sh.H, T, seed)[0].view(np.int16)).cuda() for seed in (12, 13)]
     d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
     keys = ("logits", "topk_ids", "topk_w", "pair_slot", "n_miss", "counts", "offsets", "sorted_pairs",
             "pair_to_row", "n_active", "n_work")
 
-    def dispatch(buf, sync):
+    def dispatch(buf, sync, x_d):
         moe.route_dispatch(d, x_d, L.Wr_d, L.bias_d, True, buf.logits, buf.topk_ids, buf.topk_w, L.table_d, sh.E,
                            buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets, buf.sorted_pairs,
                            buf.pair_to_row, buf.active, buf.n_active, buf.work_list, buf.n_work, sync=sync)
@@ -326,9 +328,9 @@ def test_route_dispatch_paths_agree(name, T):
     one = moe.LayerBuffers.allocate(d, 4)
     two = moe.LayerBuffers.allocate(d, 4)
     sep = moe.LayerBuffers.allocate(d, 4)
-    for _ in range(2):                                   # the second call relies on the counters' reset
-        dispatch(one, one.sync)
-        dispatch(two, None)
+    for x_d in xs:                                       # the second call relies on the counters' reset
+        dispatch(one, one.sync, x_d)
+        dispatch(two, None, x_d)
         moe.route_topk(d, x_d, L.Wr_d, L.bias_d, True, sep.logits, sep.topk_ids, sep.topk_w)
         moe.slot_lookup(d, sep.topk_ids, L.table_d, sh.E, sep.pair_slot, sep.miss, sep.n_miss)
         moe.permute(d, sep.topk_ids, sep.counts, sep.offsets, sep.sorted_pairs, sep.pair_to_row, sep.active,

@@ -153,20 +153,38 @@ class Runner:
         return total_ms, wall, gate_ms, down_ms
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+CSRC = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc")
+
+# The FFN kernels the default decode workload runs, per --algo (auto and mfma
+# take the LDS-staged decode kernels at these sizes), and the sources they are
+# built from.
+FFN_KERNELS = {
+    "mfma": dict(gateup="ffn_gateup_dec_kernel", down="ffn_down_dec_kernel",
+                 sources=("ffn_dec.hip", "mfma_ops.h", "common.h")),
+    "gemv": dict(gateup="ffn_gateup_gemv_kernel", down="ffn_down_gemv_kernel",
+                 sources=("ffn_gemv.hip", "common.h")),
+}
+FFN_KERNELS["auto"] = FFN_KERNELS["mfma"]
 
 
-def traffic_record(kernel_src):
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(algo):
     """HBM traffic of the gate/up kernel from the committed counter summary, if it
-    was taken on the current source of that kernel (else None)."""
+    was taken on that kernel's current sources (else None)."""
     path = os.path.join(ROOT, "profiles", "gateup_a3b_T32_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != source_hash(kernel_src):
+    k = FFN_KERNELS[algo]
+    if rec.get("kernel") != k["gateup"] or rec.get("source_sha256_16") != source_hash(k["sources"]):
         return None
     return rec.get("bytes_per_launch")
 
@@ -202,8 +220,9 @@ def measure_prefill(torch, mi, moe, steps, warmup):
                      "MFMAs for the group sums and two h planes in the down GEMM")
 
 
-TRAFFIC_KERNELS = {"gateup": "ffn_gateup_mfma_kernel", "down": "ffn_down_mfma_kernel",
-                   "copy": "copyBuffer"}
+def traffic_kernels(algo):
+    k = FFN_KERNELS[algo]
+    return {"gateup": k["gateup"], "down": k["down"], "copy": "copyBuffer"}
 
 
 def _counter_rows(d):
@@ -221,14 +240,14 @@ def _counter_rows(d):
     return out
 
 
-def summarize_counters(fetch_dir, write_dir, copy_mib):
+def summarize_counters(fetch_dir, write_dir, copy_mib, algo="auto"):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
     what the same counters read for the plain copy of copy_mib MiB."""
     import statistics
     res = {}
     for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d)
-        for key, pat in TRAFFIC_KERNELS.items():
+        for key, pat in traffic_kernels(algo).items():
             vals = [v for k, c, v in rows if c == cname and pat in k]
             if key == "copy":   # the calibration copies are the largest copies of the run
                 vals = sorted(vals)[-5:]
@@ -244,14 +263,14 @@ def summarize_counters(fetch_dir, write_dir, copy_mib):
         w = res[key]["WRITE_SIZE"]["mean_kib"] * 1024 * scale_w
         kern[key] = dict(fetch_bytes=round(f), write_bytes=round(w), bytes_per_launch=round(f + w),
                          dispatches=res[key]["FETCH_SIZE"]["dispatches"])
-    src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc", "ffn_mfma.hip")
-    rec = dict(kernel="ffn_gateup_mfma_kernel", workload="a3b T=32 (bench.py default)",
+    k = FFN_KERNELS[algo]
+    rec = dict(kernel=k["gateup"], workload="a3b T=32 (bench.py default)",
                bytes_per_launch=kern["gateup"]["bytes_per_launch"], per_kernel=kern,
                copy_calibration=dict(copy_bytes=copy_bytes, fetch_scale=round(scale_f, 4),
                                      write_scale=round(scale_w, 4)),
-               source_sha256_16=source_hash(src),
+               sources=list(k["sources"]), source_sha256_16=source_hash(k["sources"]),
                command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir> -o run --output-format csv "
-                       "-- python3 bench.py --steps 20 --warmup 5 --sweep=none --no-cpu-baseline "
+                       "-- python3 bench.py --steps 20 --warmup 5 --sweep=none --no-cpu-baseline --prefill-steps 0 "
                        f"--copy-calib-mib {copy_mib}")
     path = os.path.join(ROOT, "profiles", "gateup_a3b_T32_traffic.json")
     with open(path, "w") as f:
@@ -344,12 +363,10 @@ def main():
         log(f"[bench] prefill: {prefill['tokens_per_s']:.0f} tokens/s, FFN {prefill['ffn_tflops']} TFLOP/s "
             f"({100 * prefill['mfma_util']:.1f}% of bf16 MFMA peak)")
 
-    kernel_src = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc",
-                              "ffn_gemv.hip" if args.algo == "gemv" else "ffn_mfma.hip")
     achieved = main_run["gateup_GBps"]
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(kernel_src),
-                    kernel="ffn_gateup (gate/up matvec + SwiGLU)",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(args.algo),
+                    kernel=FFN_KERNELS[args.algo]["gateup"] + " (gate/up matvec + SwiGLU)",
                     algorithmic_bytes_per_launch=round(main_run["gateup_bytes_per_launch"]),
                     mean_launch_us=round(main_run["gateup_us"], 3))
 

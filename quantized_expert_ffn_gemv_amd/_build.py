@@ -30,9 +30,16 @@ COMMON = [
 ]
 
 
+# Per-source flags.  The decode kernels keep their few MFMA accumulators in
+# VGPRs, which saves an accumulator-register read per result element.
+PER_FILE = {
+    "ffn_dec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature
     noise = "'-packed-fp32-ops' is not a recognized feature"

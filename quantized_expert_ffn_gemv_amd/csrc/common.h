@@ -39,18 +39,25 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 }
 
 // ------------------------------------------------------ exact code operands
-// A code q of BITS bits is placed in the top mantissa bits of the bf16 value
-// 128 (pattern 0x4300): the result 128 + kLever * q is exact (all values lie in
+// A code q of BITS bits is OR-ed into the mantissa of the bf16 value 128
+// (pattern 0x4300): the result 128 + kLever * q is exact (all values lie in
 // [128, 256) where the bf16 spacing is 1).  A dot product with such operands
 // is C = 128 * sum(x) + kLever * sum(q x), hence
 //   sum((q s + b) x) = (s / kLever) * C + (b - kOffset * s) * sum(x),
-// with kOffset = 128 / kLever.
-template <int BITS> constexpr int kLever = (BITS == 4) ? 8 : 32;
+// with kOffset = 128 / kLever.  The lever keeps the 128 sum(x) part of C
+// within a few times the code part, so the float32 rounding of C stays small
+// next to the result: 4-bit codes take the top four mantissa bits (L = 8);
+// 2-bit codes take bits 4-5 (L = 16), where the codes at bit 4 of a packed
+// word need no shift.  (L = 1 would free a shift for 4-bit codes too, but the
+// offset part then outweighs the code part ~17 times and the 2-bit case ~43
+// times, which measurably degrades the results.)
+template <int BITS> constexpr int kLever = (BITS == 4) ? 8 : 16;
 template <int BITS> constexpr float kInvLever = 1.0f / (float)kLever<BITS>;
 template <int BITS> constexpr float kOffset = 128.0f / (float)kLever<BITS>;
 
 // v >> sh for sh >= 0, v << -sh otherwise (sh is a compile-time constant)
 __device__ __forceinline__ uint32_t shift_to(uint32_t v, int sh) { return sh >= 0 ? (v >> sh) : (v << (-sh)); }
+
 
 // --------------------------------------------------------- wave reductions
 

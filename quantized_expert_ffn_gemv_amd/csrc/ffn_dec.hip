@@ -4,14 +4,15 @@
 // The exact code operands and the per-group fold are those of mfma_ops.h.
 // What differs from the kernels in ffn_mfma.hip:
 //   * the tile's activations (gate/up: x rows; down: the three bf16 planes of
-//     h) are loaded once per workgroup into LDS, already in the pair order of
-//     the code operands, together with each row's sum over every group of
-//     128, so the waves read their MFMA operand with one LDS load per step and
-//     need neither a permute nor an all-ones MFMA for the group sums;
+//     h) and the item's scales and biases go from HBM/L2 straight into LDS
+//     with direct-to-LDS loads (global_load_lds_dwordx4), issued before the
+//     code ring and holding no registers; gate/up then rewrites its x tile
+//     once into the pair order of the code operands;
 //   * activations are the A operand (rows = tokens) and the codes the B
 //     operand (columns = weight rows): a lane's accumulators belong to one
-//     weight row, so each lane folds with a single scale pair per group, read
-//     from an LDS copy of the item's scales;
+//     weight row, so each lane folds with a single scale pair per group;
+//   * the per-group activation sums come from an MFMA with an all-ones B
+//     operand on the same LDS data;
 //   * one item per workgroup (no persistent loop): the grid covers every
 //     possible tile, and workgroups past the device-side tile count exit.
 // Gate/up: RW waves split the item's rows (16 gate + 16 up rows each) and
@@ -31,6 +32,7 @@ namespace {
 // Largest LDS a decode item may take (two workgroups per CU at 160 KB, with
 // room for the rest); bigger shapes use the kernels of ffn_mfma.hip.
 constexpr size_t kDecLdsLimit = 80 * 1024;
+constexpr int kDma = 1024;          // bytes one wave moves with one direct-to-LDS load
 
 struct DecParams {
     const uint16_t* x;
@@ -46,11 +48,48 @@ struct DecParams {
     int rows_cap;       // token rows of the LDS tile: min(16, T)
 };
 
-// LDS byte offset of 16-byte chunk c (0..15) of group g of token row j, rows
-// of `rowb` bytes (a multiple of 256).  Chunks are XOR-swizzled by the row's
-// low 4 bits: the 16 rows a quarter-wave reads at once hit 16 bank groups.
-__device__ __forceinline__ int tile_off(int j, int g, int c, int rowb) {
-    return j * rowb + g * 256 + 16 * (c ^ (j & 15));
+__host__ __device__ constexpr size_t round_dma(size_t b) { return (b + kDma - 1) / kDma * kDma; }
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// One direct-to-LDS load of the wave: lane l copies 16 bytes from `src` to
+// lds_base + 16 l (lds_base must be the same in every lane).  Written as
+// inline assembly so that the compiler does not track it: its own tracking
+// waits for every outstanding load (the code ring too) before the first LDS
+// access after it; completion is waited for explicitly with wait_vmem.
+// M0 holds the LDS address; one wait state between writing M0 and the load.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)lds_base;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Copy `bytes` (a multiple of 16) of contiguous global memory to LDS, waves
+// taking 1 KB pieces in turn; lanes past the end reload the last 16 bytes into
+// the padding (the LDS region is rounded up to a whole piece).
+__device__ __forceinline__ void dma_copy(const uint8_t* src, uint8_t* dst, int bytes, int wid, int lane) {
+    const int pieces = (bytes + kDma - 1) / kDma;
+    for (int i = wid; i < pieces; i += 4) {
+        const int off = i * kDma + 16 * lane;
+        dma16(src + (off < bytes ? off : bytes - 16), dst + i * kDma);
+    }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt off).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS only: global loads stay in flight (a plain
+// __syncthreads() waits for every outstanding load, the code ring included).
+// Direct-to-LDS data must be waited for with wait_vmem first.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Item of a decode launch: work-list entry and row block of blockIdx.x; the
@@ -88,48 +127,44 @@ __device__ __forceinline__ DecItem dec_item(const DecParams& p) {
     return it;
 }
 
-// Scale staging, split in an issue half and a store half so that its loads
-// join the other staging loads in one memory round trip.  Chunk c (of
-// rows * NG / 8) holds 8 consecutive fp16 scales and the matching biases of
-// the contiguous block starting at row `first`; the store half writes them to
-// LDS as packed (scale | bias << 16) words, row stride NGp.
-struct ScaleChunk {
-    uint4 s, b;
-};
-
-__device__ __forceinline__ ScaleChunk scale_chunk(const uint16_t* __restrict__ s, const uint16_t* __restrict__ b,
-                                                  size_t first, int NG, int c) {
-    ScaleChunk r;
-    r.s = *reinterpret_cast<const uint4*>(s + first * NG + (size_t)c * 8);
-    r.b = *reinterpret_cast<const uint4*>(b + first * NG + (size_t)c * 8);
-    return r;
+// The activation tile in LDS: rows of `rowb` bytes, each group of 128 along K
+// a run of 16 chunks of 16 bytes (8 values in natural order), the chunks
+// XOR-swizzled by the row's low 4 bits so that the 16 rows a quarter-wave
+// reads at once hit 16 bank groups.  Chunk c of group g of row j:
+__device__ __forceinline__ int tile_off(int j, int g, int c, int rowb) {
+    return j * rowb + g * 256 + 16 * (c ^ (j & 15));
 }
 
-__device__ __forceinline__ void store_scale_chunk(const ScaleChunk& k, int c, int NG, int NGp, uint32_t* dst) {
-    const uint32_t sw[4] = {k.s.x, k.s.y, k.s.z, k.s.w}, bw[4] = {k.b.x, k.b.y, k.b.z, k.b.w};
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-        const int f = c * 8 + v, r = f / NG, g = f - r * NG;
-        const uint32_t sv = (sw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
-        const uint32_t bv = (bw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
-        dst[r * NGp + g] = sv | (bv << 16);
+// Direct-to-LDS staging of `n` rows of such a tile (`rows_cap` rows of room):
+// piece i of the tile (1 KB) is loaded by one wave, lane l filling slot
+// 64 i + l.  src(j, g, c) is the global address of chunk c of group g of row
+// j; slots of rows past n reload a chunk of row 0 into unused room.
+template <typename Src>
+__device__ __forceinline__ void dma_tile(uint8_t* tile, int n, int rowb, int wid, int lane, Src src) {
+    const int chunks_row = rowb / 16;
+    const int pieces = (n * rowb + kDma - 1) / kDma;
+    for (int i = wid; i < pieces; i += 4) {
+        const int slot = i * (kDma / 16) + lane;
+        int j = slot / chunks_row;
+        const int r = slot - j * chunks_row, g = r >> 4, cs = r & 15;
+        j = j < n ? j : 0;
+        dma16(src(j, g, cs ^ (j & 15)), tile + i * kDma);
     }
 }
 
-// Staging tasks per thread per round (16 rows x 16 groups x 4 quarters fill
-// one round of 256 threads).
-constexpr int kStageX = 4;
-
-// acc += (s / L) C + (b - (128 / L) s) X for one packed (scale, bias) word.
+// acc += (s / L) C + (b - (128 / L) s) X for one fp16 scale and bias.
 template <int BITS>
-__device__ __forceinline__ void fold(floatx4_t& acc, const floatx4_t& C, uint32_t sb, const float4& X) {
-    const float sv = f16_bits_to_f32(sb & 0xFFFFu), bv = f16_bits_to_f32(sb >> 16);
+__device__ __forceinline__ void fold(floatx4_t& acc, const floatx4_t& C, uint32_t s16, uint32_t b16,
+                                     const floatx4_t& X) {
+    const float sv = f16_bits_to_f32(s16), bv = f16_bits_to_f32(b16);
     const float s1 = sv * kInvLever<BITS>, b1 = fmaf(-kOffset<BITS>, sv, bv);
-    acc[0] = fmaf(s1, C[0], fmaf(b1, X.x, acc[0]));
-    acc[1] = fmaf(s1, C[1], fmaf(b1, X.y, acc[1]));
-    acc[2] = fmaf(s1, C[2], fmaf(b1, X.z, acc[2]));
-    acc[3] = fmaf(s1, C[3], fmaf(b1, X.w, acc[3]));
+    acc[0] = fmaf(s1, C[0], fmaf(b1, X[0], acc[0]));
+    acc[1] = fmaf(s1, C[1], fmaf(b1, X[1], acc[1]));
+    acc[2] = fmaf(s1, C[2], fmaf(b1, X[2], acc[2]));
+    acc[3] = fmaf(s1, C[3], fmaf(b1, X[3], acc[3]));
 }
+
+constexpr uint32_t kOnesBf16 = 0x3F803F80u;   // two bf16 ones
 
 }  // namespace
 
@@ -137,11 +172,11 @@ __device__ __forceinline__ void fold(floatx4_t& acc, const floatx4_t& C, uint32_
 // Item = (work-list tile, block of 16 RW rows of gate and of up).  Wave
 // (wr, wk) = (wid / KS, wid % KS) computes rows 16 wr .. +16 of the block
 // (pair order) over its share of the K groups, with a D-deep register ring of
-// code loads.  LDS: x tile [rows_cap][H] bf16 (pair order, swizzled), group
-// sums [NG][16] float, scales [2][16 RW][NGp] packed; after the loop the
-// first 8 KB is reused for the partial sums over K.
+// code loads.  LDS: the x tile [rows_cap][H] bf16, then the raw fp16 scales
+// and biases of the block's gate and up rows, [RI][NG] each; after the loop
+// the first 8 KB holds the partial sums over K.
 template <int BITS, int RW, int D>
-__global__ __launch_bounds__(256) void ffn_gateup_dec_kernel(DecParams p) {
+__global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
     constexpr int KS = 4 / RW;
     constexpr int LB = 128 * BITS / 8 / 4;     // code bytes per lane per group
     constexpr int LW = LB / 4;
@@ -152,10 +187,25 @@ __global__ __launch_bounds__(256) void ffn_gateup_dec_kernel(DecParams p) {
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wid / KS, wk = wid % KS;
-    const int H = p.H, I = p.I, NG = H / kGroup, NGp = NG | 1, rowb = H * 2;
+    const int H = p.H, I = p.I, NG = H / kGroup, rowb = H * 2;
+    const int sc_bytes = RI * NG * 2;
+    const int sc_stride = (int)round_dma(sc_bytes);
     uint8_t* xs = smem;
-    float* xsum = reinterpret_cast<float*>(smem + (size_t)p.rows_cap * rowb);
-    uint32_t* sc = reinterpret_cast<uint32_t*>(xsum + NG * 16);
+    uint8_t* scl = smem + round_dma((size_t)p.rows_cap * rowb);          // gate s, gate b, up s, up b
+
+    // ---- x tile and scales straight to LDS.  Loads complete in issue order,
+    // so these go first: waiting for them leaves the code ring in flight.
+    const int tokv = it.tokv;
+    dma_tile(xs, it.n, rowb, wid, lane, [&](int j, int g, int c) {
+        return p.x + (size_t)__shfl(tokv, j, kWave) * H + g * kGroup + 8 * c;
+    });
+    {
+        const size_t first = ((size_t)it.e * I + (size_t)it.rb * RI) * NG;
+        dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
+        dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
+        dma_copy(reinterpret_cast<const uint8_t*>(p.sb + first), scl + 2 * sc_stride, sc_bytes, wid, lane);
+        dma_copy(reinterpret_cast<const uint8_t*>(p.bb + first), scl + 3 * sc_stride, sc_bytes, wid, lane);
+    }
 
     // ---- code ring: rows of this lane (pair order), groups [gb, gb + ng)
     const int gb = (wk * NG) / KS, ng = ((wk + 1) * NG) / KS - gb;
@@ -179,101 +229,67 @@ __global__ __launch_bounds__(256) void ffn_gateup_dec_kernel(DecParams p) {
             ru[slot][0] = B.x; ru[slot][1] = B.y;
         }
     };
-    // ---- staging of the x tile (pair order) with its group sums, and the
-    // scales, in rounds of kStageX tasks per thread.  A round issues all its
-    // loads, then stores; tasks past the end repeat the last task and write
-    // the same values to the same place, so the stores need no guard (a guard
-    // lets the compiler sink each load into its branch: one round trip per
-    // task).
-    const int tokv = it.tokv;
-    const int nq = it.n * NG * 4, nsc = 2 * (RI * NG / 8);
-    const size_t first = (size_t)it.e * I + (size_t)it.rb * RI;
-    struct Stage {
-        uint32_t X[kStageX][16];
-        int tj[kStageX], tg[kStageX], tqq[kStageX];
-        ScaleChunk sk;
-        int cc, cmat;
-    };
-    auto stage_issue = [&](int rd, Stage& S) {
 #pragma unroll
-        for (int u = 0; u < kStageX; ++u) {
-            int t = (rd * kStageX + u) * 256 + tid;
-            t = t < nq ? t : nq - 1;
-            const int j = t / (NG * 4), r = t - j * (NG * 4);
-            S.tj[u] = j; S.tg[u] = r >> 2; S.tqq[u] = r & 3;
-            const int tok = __shfl(tokv, j, kWave);
-            const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * H + S.tg[u] * kGroup + 32 * S.tqq[u]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 w = src[v];
-                S.X[u][4 * v] = w.x; S.X[u][4 * v + 1] = w.y; S.X[u][4 * v + 2] = w.z; S.X[u][4 * v + 3] = w.w;
-            }
-        }
-        int c = rd * 256 + tid;
-        c = c < nsc ? c : nsc - 1;
-        S.cmat = c >= nsc / 2;
-        S.cc = c - S.cmat * (nsc / 2);
-        S.sk = scale_chunk(S.cmat ? p.sb : p.sa, S.cmat ? p.bb : p.ba, first, NG, S.cc);
-    };
-    auto stage_store = [&](const Stage& S) {
-#pragma unroll
-        for (int u = 0; u < kStageX; ++u) {
+    for (int d = 0; d < D; ++d) issue(d, d);
+    wait_vmem<2 * D>();                        // the staging loads, older than the 2 D ring loads
+    lds_barrier();
+
+    // ---- the x tile into code pair order, once per workgroup.  Unit (j, g,
+    // qq) is the 32 activations that a lane of quarter qq uses for group g of
+    // row j; afterwards chunk 4 qq + st of the unit holds that lane's A operand
+    // of MFMA step st.  Each unit is read and rewritten by one thread.
+    {
+        const int units = it.n * NG * 4;
+        for (int u = tid; u < units; u += 256) {
+            const int j = u / (NG * 4), r = u - j * (NG * 4), g = r >> 2, qq = r & 3;
+            uint8_t* base = xs + j * rowb + g * 256;
+            uint32_t X[16];
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                uint32_t o[4];
-                act_operand<BITS>(S.X[u], st, o);
-                *reinterpret_cast<uint4*>(xs + tile_off(S.tj[u], S.tg[u], 4 * S.tqq[u] + st, rowb)) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
+                const uint4 v = *reinterpret_cast<const uint4*>(base + 16 * ((4 * qq + st) ^ (j & 15)));
+                X[4 * st] = v.x; X[4 * st + 1] = v.y; X[4 * st + 2] = v.z; X[4 * st + 3] = v.w;
             }
-            float sum = 0.f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sum += bf16_bits_to_f32(S.X[u][v] & 0xFFFFu) + bf16_bits_to_f32(S.X[u][v] >> 16);
-            sum += __shfl_xor(sum, 1, kWave);
-            sum += __shfl_xor(sum, 2, kWave);
-            if (S.tqq[u] == 0) xsum[S.tg[u] * 16 + S.tj[u]] = sum;
+            for (int st = 0; st < 4; ++st) {
+                uint32_t A[4];
+                act_operand<BITS>(X, st, A);
+                *reinterpret_cast<uint4*>(base + 16 * ((4 * qq + st) ^ (j & 15))) = make_uint4(A[0], A[1], A[2], A[3]);
+            }
         }
-        store_scale_chunk(S.sk, S.cc, NG, NGp, sc + S.cmat * RI * NGp);
-    };
-    {
-        // Loads complete in issue order, so round 0 is issued before the code
-        // ring: waiting for it then leaves the ring in flight.  Scheduling
-        // barriers keep the compiler from moving either across the other.
-        Stage S;
-        stage_issue(0, S);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int d = 0; d < D; ++d) issue(d, d);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_store(S);
-        const int rounds = max((nq + 256 * kStageX - 1) / (256 * kStageX), (nsc + 255) / 256);
-        for (int rd = 1; rd < rounds; ++rd) {
-            stage_issue(rd, S);
-            stage_store(S);
-        }
+        lds_barrier();
     }
-    __syncthreads();
 
-    // ---- main loop: consume a ring slot, refill it D groups on
     const int mrow = m < it.n ? m : 0;         // rows past the tile read row 0 (never stored)
-    const uint32_t* scg = sc + rloc * NGp;
-    const uint32_t* scu = sc + (RI + rloc) * NGp;
+    const uint8_t* xrow = xs + mrow * rowb;
+    int coff[4];                               // swizzled chunk offsets of this lane's quarter
+#pragma unroll
+    for (int st = 0; st < 4; ++st) coff[st] = 16 * ((4 * q + st) ^ (mrow & 15));
+    const uint16_t* gsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NG;
+    const uint16_t* gbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NG;
+    const uint16_t* usc = reinterpret_cast<const uint16_t*>(scl + 2 * sc_stride) + rloc * NG;
+    const uint16_t* ubi = reinterpret_cast<const uint16_t*>(scl + 3 * sc_stride) + rloc * NG;
+    const uint32_t ONES[4] = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+
     floatx4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
-    auto step = [&](int d, int gl) {
+    // One group: `valid` false for the padding steps of the last block, which
+    // repeat the last group (codes and activations) with zero scale and bias.
+    auto step = [&](int d, int gl, bool valid) {
         const int g = gb + gl;
-        floatx4_t Cg = {0.f, 0.f, 0.f, 0.f}, Cu = Cg;
+        floatx4_t Cg = {0.f, 0.f, 0.f, 0.f}, Cu = Cg, Cx = Cg;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const uint4 a4 = *reinterpret_cast<const uint4*>(xs + tile_off(mrow, g, 4 * q + st, rowb));
-            const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
+            const uint4 v = *reinterpret_cast<const uint4*>(xrow + g * 256 + coff[st]);
+            const uint32_t A[4] = {v.x, v.y, v.z, v.w};
             uint32_t Bg[4], Bu[4];
             code_operand<BITS>(rg[d], st, Bg);
             code_operand<BITS>(ru[d], st, Bu);
             Cg = mfma16(A, Bg, Cg);
             Cu = mfma16(A, Bu, Cu);
+            Cx = mfma16(A, ONES, Cx);           // group sum of x per token (any order)
         }
-        const float4 X = *reinterpret_cast<const float4*>(xsum + g * 16 + 4 * q);
-        fold<BITS>(accg, Cg, scg[g], X);
-        fold<BITS>(accu, Cu, scu[g], X);
+        const uint32_t keep = valid ? 0xFFFFu : 0u;    // loads stay unconditional (no branch)
+        fold<BITS>(accg, Cg, gsc[g] & keep, gbi[g] & keep, Cx);
+        fold<BITS>(accu, Cu, usc[g] & keep, ubi[g] & keep, Cx);
     };
     // Full blocks refill every slot unconditionally (the compiler then keeps
     // exact load counts across the loop and waits only for the slot it
@@ -283,14 +299,16 @@ __global__ __launch_bounds__(256) void ffn_gateup_dec_kernel(DecParams p) {
     for (; g0 + D < NGP; g0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            step(d, g0 + d);
+            step(d, g0 + d, true);
             __builtin_amdgcn_sched_barrier(0);
             issue(d, g0 + d + D);
         }
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (g0 + d < ng) step(d, g0 + d);
+    for (int d = 0; d < D; ++d) {
+        step(d, g0 + d < ng ? g0 + d : ng - 1, g0 + d < ng);
+        __builtin_amdgcn_sched_barrier(0);     // keep the steps' operands from all going live at once
+    }
 
     // ---- partial sums over K (fixed order), then SwiGLU in the wk = 0 waves
     if constexpr (KS > 1) {
@@ -341,11 +359,11 @@ __global__ __launch_bounds__(256) void ffn_gateup_dec_kernel(DecParams p) {
 // ------------------------------------------------------------------- down
 // Item = (work-list tile, block of 64 RT output rows).  Wave wid computes rows
 // 16 RT wid .. +16 RT (RT tiles of 16, natural order) over all K = I groups.
-// LDS: the three h planes [3][rows_cap][I] bf16 (pair order, swizzled), the
-// group sums [NG][16] float (from the 16-row partial sums of h), scales
-// [64 RT][NGp] packed.
+// LDS: the three h planes [3][rows_cap][I] bf16 (already in pair order), then
+// the raw fp16 scales and biases [64 RT][NG].  The group sums of h come from
+// all-ones MFMAs on the three planes.
 template <int BITS, int RT, int D>
-__global__ __launch_bounds__(256) void ffn_down_dec_kernel(DecParams p) {
+__global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
     constexpr int LB = 128 * BITS / 8 / 4;
     constexpr int LW = LB / 4;
     constexpr int RI = 64 * RT;
@@ -354,11 +372,26 @@ __global__ __launch_bounds__(256) void ffn_down_dec_kernel(DecParams p) {
     if (it.n == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.H, I = p.I, NG = I / kGroup, NGp = NG | 1, rowb = I * 2;
-    const size_t plane_b = (size_t)p.rows_cap * rowb;
+    const int H = p.H, I = p.I, NG = I / kGroup, rowb = I * 2;
+    const int plane_b = (int)round_dma((size_t)p.rows_cap * rowb);
+    const int sc_bytes = RI * NG * 2;
+    const int sc_stride = (int)round_dma(sc_bytes);
     uint8_t* hs = smem;
-    float* hsum = reinterpret_cast<float*>(smem + 3 * plane_b);
-    uint32_t* sc = reinterpret_cast<uint32_t*>(hsum + NG * 16);
+    uint8_t* scl = smem + 3 * (size_t)plane_b;                          // s, then b
+
+    // ---- h planes and scales straight to LDS, ahead of the code ring
+    {
+        const size_t plane = (size_t)p.P * I;
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) {
+            const uint16_t* hrows = p.hp + pl * plane + (size_t)it.row0 * I;
+            dma_tile(hs + (size_t)pl * plane_b, it.n, rowb, wid, lane,
+                     [&](int j, int g, int c) { return hrows + (size_t)j * I + g * kGroup + 8 * c; });
+        }
+        const size_t first = ((size_t)it.e * H + (size_t)it.rb * RI) * NG;
+        dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
+        dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
+    }
 
     // ---- code ring: RT rows of this lane, all groups
     const int rloc = 16 * RT * wid + m;               // + 16 rt
@@ -380,83 +413,26 @@ __global__ __launch_bounds__(256) void ffn_down_dec_kernel(DecParams p) {
             }
         }
     };
-    // ---- staging of the h planes (already in pair order), group sums and
-    // scales, in rounds as in the gate/up kernel (round 0 with the ring)
-    const size_t plane = (size_t)p.P * I;
-    const int per_plane = it.n * NG * 4;
-    const int nq = 3 * per_plane, nhs = it.n * NG, nsc = RI * NG / 8;
-    const size_t first = (size_t)it.e * H + (size_t)it.rb * RI;
-    struct Stage {
-        uint32_t V[kStageX][16];
-        int tpl[kStageX], tj[kStageX], tg[kStageX], tqq[kStageX];
-        float4 ha, hb;
-        int hj, hg;
-        ScaleChunk sk;
-        int c;
-    };
-    auto stage_issue = [&](int rd, Stage& S) {
 #pragma unroll
-        for (int u = 0; u < kStageX; ++u) {
-            int t = (rd * kStageX + u) * 256 + tid;
-            t = t < nq ? t : nq - 1;
-            const int pl = t / per_plane, r = t - pl * per_plane;
-            const int j = r / (NG * 4), r2 = r - j * (NG * 4);
-            S.tpl[u] = pl; S.tj[u] = j; S.tg[u] = r2 >> 2; S.tqq[u] = r2 & 3;
-            const uint4* src = reinterpret_cast<const uint4*>(p.hp + pl * plane + (size_t)(it.row0 + j) * I +
-                                                              S.tg[u] * kGroup + 32 * S.tqq[u]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 w = src[v];
-                S.V[u][4 * v] = w.x; S.V[u][4 * v + 1] = w.y; S.V[u][4 * v + 2] = w.z; S.V[u][4 * v + 3] = w.w;
-            }
-        }
-        int th = rd * 256 + tid;
-        th = th < nhs ? th : nhs - 1;
-        S.hj = th / NG;
-        S.hg = th - S.hj * NG;
-        const float4* hsrc = reinterpret_cast<const float4*>(p.hpart + (size_t)(it.row0 + S.hj) * (I / 16) + 8 * S.hg);
-        S.ha = hsrc[0];
-        S.hb = hsrc[1];
-        int c = rd * 256 + tid;
-        S.c = c < nsc ? c : nsc - 1;
-        S.sk = scale_chunk(p.sa, p.ba, first, NG, S.c);
-    };
-    auto stage_store = [&](const Stage& S) {
-#pragma unroll
-        for (int u = 0; u < kStageX; ++u) {
-            uint8_t* dst = hs + S.tpl[u] * plane_b;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                *reinterpret_cast<uint4*>(dst + tile_off(S.tj[u], S.tg[u], 4 * S.tqq[u] + v, rowb)) =
-                    make_uint4(S.V[u][4 * v], S.V[u][4 * v + 1], S.V[u][4 * v + 2], S.V[u][4 * v + 3]);
-        }
-        hsum[S.hg * 16 + S.hj] = ((S.ha.x + S.ha.y) + (S.ha.z + S.ha.w)) + ((S.hb.x + S.hb.y) + (S.hb.z + S.hb.w));
-        store_scale_chunk(S.sk, S.c, NG, NGp, sc);
-    };
-    {
-        // round 0 ahead of the ring (see the gate/up kernel)
-        Stage S;
-        stage_issue(0, S);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int d = 0; d < D; ++d) issue(d, d);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_store(S);
-        int rounds = (nq + 256 * kStageX - 1) / (256 * kStageX);
-        rounds = max(rounds, max((nhs + 255) / 256, (nsc + 255) / 256));
-        for (int rd = 1; rd < rounds; ++rd) {
-            stage_issue(rd, S);
-            stage_store(S);
-        }
-    }
-    __syncthreads();
+    for (int d = 0; d < D; ++d) issue(d, d);
+    wait_vmem<RT * D>();
+    lds_barrier();
 
     const int mrow = m < it.n ? m : 0;
+    const uint8_t* hrow = hs + mrow * rowb;
+    int coff[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) coff[st] = 16 * ((4 * q + st) ^ (mrow & 15));
+    const uint16_t* dsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NG;
+    const uint16_t* dbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NG;
+    const uint32_t ONES[4] = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
     floatx4_t acc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    auto step = [&](int d, int g) {
-        floatx4_t C[RT];
+    // `valid` false: padding step of the last block (last group again, zero
+    // scale and bias)
+    auto step = [&](int d, int g, bool valid) {
+        floatx4_t C[RT], Cx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) C[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -464,7 +440,7 @@ __global__ __launch_bounds__(256) void ffn_down_dec_kernel(DecParams p) {
             uint32_t A[3][4];
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl) {
-                const uint4 a4 = *reinterpret_cast<const uint4*>(hs + pl * plane_b + tile_off(mrow, g, 4 * q + st, rowb));
+                const uint4 a4 = *reinterpret_cast<const uint4*>(hrow + (size_t)pl * plane_b + g * 256 + coff[st]);
                 A[pl][0] = a4.x; A[pl][1] = a4.y; A[pl][2] = a4.z; A[pl][3] = a4.w;
             }
 #pragma unroll
@@ -475,10 +451,14 @@ __global__ __launch_bounds__(256) void ffn_down_dec_kernel(DecParams p) {
                 C[rt] = mfma16(A[1], B, C[rt]);
                 C[rt] = mfma16(A[2], B, C[rt]);
             }
+            Cx = mfma16(A[0], ONES, Cx);        // group sum of h per token, all three planes
+            Cx = mfma16(A[1], ONES, Cx);
+            Cx = mfma16(A[2], ONES, Cx);
         }
-        const float4 X = *reinterpret_cast<const float4*>(hsum + g * 16 + 4 * q);
+        const uint32_t keep = valid ? 0xFFFFu : 0u;    // loads stay unconditional (no branch)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) fold<BITS>(acc[rt], C[rt], sc[(rloc + 16 * rt) * NGp + g], X);
+        for (int rt = 0; rt < RT; ++rt)
+            fold<BITS>(acc[rt], C[rt], dsc[16 * rt * NG + g] & keep, dbi[16 * rt * NG + g] & keep, Cx);
     };
     // full blocks refill unconditionally, the peeled last block issues nothing
     const int NGP = (NG + D - 1) / D * D;
@@ -486,14 +466,16 @@ __global__ __launch_bounds__(256) void ffn_down_dec_kernel(DecParams p) {
     for (; g0 + D < NGP; g0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            step(d, g0 + d);
+            step(d, g0 + d, true);
             __builtin_amdgcn_sched_barrier(0);
             issue(d, g0 + d + D);
         }
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (g0 + d < NG) step(d, g0 + d);
+    for (int d = 0; d < D; ++d) {
+        step(d, g0 + d < NG ? g0 + d : NG - 1, g0 + d < NG);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     // ---- Y rows in bf16: token 4q + i, output row rloc + 16 rt
 #pragma unroll
@@ -526,7 +508,7 @@ static DecParams dec_params(const FfnArgs& a) {
 // to fill the chip; at least one group of K per wave.
 static int dec_gateup_rw(const moe_dims& d) {
     const long P = (long)d.T * d.k;
-    int rw = P >= 128 ? 4 : (P >= 32 ? 2 : 1);
+    int rw = P >= 32 ? 4 : 1;
     const int NG = d.H / kGroup;
     while (rw < 4 && 4 / rw > NG) rw *= 2;
     return rw;
@@ -542,23 +524,25 @@ static int dec_down_rt(const moe_dims& d) {
 
 static size_t dec_gateup_lds(const moe_dims& d, int rw) {
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
-    const int NG = d.H / kGroup, NGp = NG | 1;
-    const size_t stage = (size_t)rows_cap * d.H * 2 + (size_t)NG * 16 * 4 + (size_t)2 * 16 * rw * NGp * 4;
+    const int NG = d.H / kGroup;
+    const size_t stage = round_dma((size_t)rows_cap * d.H * 2) + 4 * round_dma((size_t)16 * rw * NG * 2);
     const size_t red = (rw < 4) ? (size_t)4 * 64 * 8 * 4 : 0;
     return stage > red ? stage : red;
 }
 
 static size_t dec_down_lds(const moe_dims& d, int rt) {
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
-    const int NG = d.I / kGroup, NGp = NG | 1;
-    return (size_t)3 * rows_cap * d.I * 2 + (size_t)NG * 16 * 4 + (size_t)64 * rt * NGp * 4;
+    const int NG = d.I / kGroup;
+    return 3 * round_dma((size_t)rows_cap * d.I * 2) + 2 * round_dma((size_t)64 * rt * NG * 2);
 }
 
-// Ring depth: the deepest of 16, 8, 4, 2 that pads the wave's groups by at
-// most a quarter.  At decode sizes a wave's whole stream (16 groups or fewer)
-// is then requested at once, before the first use.
-static int dec_depth(int ng) {
-    for (int dd = 16; dd > 1; dd >>= 1) {
+// Ring depth: the deepest of `cap`, cap / 2, ..., 2 that pads a wave's groups
+// by at most a quarter.  Shallow rings measure faster than requesting a wave's
+// whole stream at once: a wave that issues many loads stalls at issue (the
+// memory pipeline is full) and only starts its arithmetic once the last load
+// is out, so its compute no longer overlaps the stream.
+static int dec_depth(int ng, int cap) {
+    for (int dd = cap; dd > 1; dd >>= 1) {
         if (dd > ng) continue;
         const int ngp = (ng + dd - 1) / dd * dd;
         if (4 * ngp <= 5 * ng) return dd;
@@ -577,8 +561,7 @@ static void gu_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams&
 
 template <int BITS, int RW>
 static void gu_depth(int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (D >= 8) gu_go<BITS, RW, 8>(d, lds, s, p);
-    else if (D >= 4) gu_go<BITS, RW, 4>(d, lds, s, p);
+    if (D >= 4) gu_go<BITS, RW, 4>(d, lds, s, p);
     else if (D >= 2) gu_go<BITS, RW, 2>(d, lds, s, p);
     else gu_go<BITS, RW, 1>(d, lds, s, p);
 }
@@ -600,8 +583,7 @@ int launch_gateup_dec(const FfnArgs& a, hipStream_t s) {
     p.ipe = d.I / (16 * rw);
     const size_t lds = dec_gateup_lds(d, rw);
     if (lds > kDecLdsLimit) return MOE_ERR_UNSUPPORTED;
-    // the ring shares the registers with the staging round: at most 8 deep
-    const int D = std::min(8, dec_depth((d.H / kGroup) / (4 / rw)));
+    const int D = dec_depth((d.H / kGroup) / (4 / rw), 4);
     if (a.bits == 4) gu_rw<4>(rw, D, d, lds, s, p);
     else gu_rw<2>(rw, D, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -615,9 +597,7 @@ static void dn_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams&
 
 template <int BITS, int RT>
 static void dn_depth(int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (D >= 8) dn_go<BITS, RT, 8>(d, lds, s, p);
-    else if (D >= 4) dn_go<BITS, RT, 4>(d, lds, s, p);
-    else if (D >= 2) dn_go<BITS, RT, 2>(d, lds, s, p);
+    if (D >= 2) dn_go<BITS, RT, 2>(d, lds, s, p);
     else dn_go<BITS, RT, 1>(d, lds, s, p);
 }
 
@@ -630,7 +610,7 @@ int launch_down_dec(const FfnArgs& a, hipStream_t s) {
     p.ipe = d.H / (64 * rt);
     const size_t lds = dec_down_lds(d, rt);
     if (lds > kDecLdsLimit) return MOE_ERR_UNSUPPORTED;
-    const int D = std::min(8, dec_depth(d.I / kGroup));
+    const int D = dec_depth(d.I / kGroup, 2);
     if (a.bits == 4) {
         if (rt == 4) dn_depth<4, 4>(D, d, lds, s, p);
         else if (rt == 2) dn_depth<4, 2>(D, d, lds, s, p);

@@ -15,8 +15,8 @@
 //    consecutive lanes cover one row (LG * 16 contiguous bytes per load), each
 //    lane group carries 4 rows so every activation fetch from LDS serves 4 rows.
 //  * Gate/up: a code q is turned into the exact bf16 value 128 + L q by OR-ing
-//    it into the top mantissa bits of the bf16 pattern 0x4300 (L = 8 for 4-bit,
-//    32 for 2-bit), two codes per 32-bit register, and multiplied against bf16
+//    it into the mantissa of the bf16 pattern 0x4300 (L = kLever: 8 for 4-bit,
+//    16 for 2-bit), two codes per 32-bit register, and multiplied against bf16
 //    activation pairs with v_dot2_f32_bf16 (products exact, float32
 //    accumulation).  Per 16-byte chunk (inside one group) the sum
 //    D = sum (128 + L q) x folds into the row total as
@@ -54,7 +54,7 @@ __device__ __forceinline__ void codes_to_bf16_pairs(uint32_t w, uint32_t* out) {
         for (int j = 0; j < 4; ++j) out[j] = (shift_to(w, 4 * j - 3) & 0x00780078u) | 0x43004300u;
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = (shift_to(w, 2 * j - 5) & 0x00600060u) | 0x43004300u;
+        for (int j = 0; j < 8; ++j) out[j] = (shift_to(w, 2 * j - 4) & 0x00300030u) | 0x43004300u;
     }
 }
 

@@ -8,16 +8,16 @@
 // MFMA tile costs the same few vector instructions per weight (unpacking) at
 // any token count up to 16.
 //
-// Exactness: a code q becomes the bf16 value 128 + L q (q OR-ed into the top
-// mantissa bits of 0x4300; L = 8 for 4-bit, 32 for 2-bit codes), exact, and
+// Exactness: a code q becomes the bf16 value 128 + L q (q OR-ed into the
+// mantissa of 0x4300; L = kLever: 8 for 4-bit, 16 for 2-bit codes), exact, and
 // activations are bf16, so every product is exact and the matrix core
 // accumulates in float32.  Per group of 128 along K the tile accumulator
 // C = sum (128 + L q) x is folded into the output as
 //     (s / L) * C + (b - (128 / L) s) * X,    X = sum of x over the group,
 // which is sum (q s + b) x (the FMA form of the Flash-MoE page, sec. 2).  X
-// comes from a third MFMA with an all-ones A operand.  Putting q in the top
-// mantissa bits keeps the 128 X part of C within a few times the code part,
-// so float32 rounding in C stays at float32 level relative to the result.
+// comes from a third MFMA with an all-ones A operand.  The lever keeps the
+// 128 X part of C within a few times the code part, so float32 rounding in C
+// stays at float32 level relative to the result.
 //
 // Layout of one wave's MFMA work: rows m = lane % 16 of a 16-row tile (A operand),
 // tokens n = lane % 16 of a 16-token tile (B operand), quad q = lane / 16 owns

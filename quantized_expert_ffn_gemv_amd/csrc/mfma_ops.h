@@ -5,7 +5,7 @@
 // D, rows 4 (l / 16) + i of column l % 16.
 //
 // Exact code operands: a code q becomes the bf16 value 128 + L q (q OR-ed
-// into the top mantissa bits of 0x4300; L = 8 for 4-bit, 32 for 2-bit codes),
+// into the mantissa of 0x4300; L = kLever: 8 for 4-bit, 16 for 2-bit codes),
 // so products with bf16 activations are exact and the matrix core accumulates
 // in float32.  Per group of 128 along K the accumulator C = sum (128 + L q) x
 // folds into the output as (s / L) C + (b - (128 / L) s) X with X = sum x,
@@ -27,29 +27,35 @@ __device__ __forceinline__ floatx4_t mfma16(const uint32_t (&a)[4], const uint32
 }
 
 // A operand of MFMA step s for one group: the lane's codes (4-bit: 4 words,
-// 2-bit: 2 words) -> 4 packed pairs of bf16 128 + L*q (see kLever).  Pair i of
+// 2-bit: 2 words) -> 4 packed pairs of bf16 128 + L q (see kLever).  Pair i of
 // a word holds codes (i, i + W/2) of that word (W codes per word).
-// (x & m) | c in one instruction.  gfx9 VOP3 takes no literal and reads at
-// most one scalar operand, so with both constants immediate the compiler
-// emits a separate AND and OR; the constants are passed in registers here.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
-    return r;
+// A constant the optimiser cannot see through, held in a VGPR (the empty
+// statement emits no instruction).
+__device__ __forceinline__ uint32_t vreg_const(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
 }
+
+// (x & m) | c in one v_and_or_b32.  gfx9 VOP3 takes no literal and reads at
+// most one scalar operand, so with both constants visible the compiler emits
+// a separate AND and OR; with m and c opaque VGPR values it selects the one
+// instruction.  Written in plain C on purpose: the compiler then knows it is a
+// VALU write and keeps the wait states the matrix core needs before reading
+// the result (an instruction hidden in inline assembly gets none).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
 
 template <int BITS>
 __device__ __forceinline__ void code_operand(const uint32_t* w, int s, uint32_t (&out)[4]) {
-    const uint32_t hi = 0x43004300u;
+    const uint32_t hi = vreg_const(0x43004300u);
     if constexpr (BITS == 4) {
-        const uint32_t v = w[s], m = 0x00780078u;
+        const uint32_t v = w[s], m = vreg_const(0x00780078u);            // L = 8: bits 3-6
 #pragma unroll
         for (int i = 0; i < 4; ++i) out[i] = and_or(shift_to(v, 4 * i - 3), m, hi);
     } else {
-        const uint32_t v = w[s >> 1], m = 0x00600060u;
+        const uint32_t v = w[s >> 1], m = vreg_const(0x00300030u);       // L = 16: bits 4-5
         const int base = 4 * (s & 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = and_or(shift_to(v, 2 * (base + i) - 5), m, hi);
+        for (int i = 0; i < 4; ++i) out[i] = and_or(shift_to(v, 2 * (base + i) - 4), m, hi);
     }
 }
 

@@ -205,15 +205,17 @@ int moe_permute(const moe_dims* dims, const int32_t* topk_ids, int32_t* expert_c
  * field has the meaning, layout and alignment it has in those calls;
  * host_doorbell and last_use may be NULL.  The struct itself is read on the
  * host during the call only.
- *   sync  NULL, or int32 [MOE_DISPATCH_SYNC_INTS] device memory that holds
- *         zeros before the first call (each call leaves it zero again).
+ *   sync  NULL, or int32 [MOE_DISPATCH_SYNC_INTS] device memory, 256-byte
+ *         aligned, that holds zeros before the first call (each call leaves
+ *         it zero again).  Its counters sit 256 bytes apart: arrivals at
+ *         counters that share a cache line queue behind each other.
  *         With sync and 1 <= T <= 64, T*k <= 4096, the whole routing is one
  *         launch: workgroups that finish a stage late run the next one,
  *         signalled through these counters.  Calls that share one sync
  *         buffer must be ordered (one stream).  Without sync, or for larger
  *         calls, the router runs first, then (T*k <= 4096) top-k, lookup and
  *         grouping in one workgroup, else the separate calls' kernels. */
-#define MOE_DISPATCH_SYNC_INTS 16
+#define MOE_DISPATCH_SYNC_INTS 576
 typedef struct moe_dispatch {
     int32_t* topk_ids;              /* [T][k] */
     float* topk_w;                  /* [T][k] */

@@ -172,7 +172,7 @@ def slot_lookup(d: Dims, topk_ids, slot_of_expert, n_slots: int, pair_slot, miss
 
 
 WORK_TILE_ROWS, WORK_ENTRY_INTS = 16, 20     # MOE_WORK_TILE_ROWS, MOE_WORK_ENTRY_INTS
-DISPATCH_SYNC_INTS = 16                      # MOE_DISPATCH_SYNC_INTS
+DISPATCH_SYNC_INTS = 576                     # MOE_DISPATCH_SYNC_INTS
 
 
 def work_list_capacity(d: Dims) -> int:

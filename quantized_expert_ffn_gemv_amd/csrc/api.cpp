@@ -291,7 +291,7 @@ int moe_route_dispatch(const moe_dims* d, const uint16_t* x, const float* w_rout
     if (o->host_doorbell && !aligned(o->host_doorbell, 4))
         return fail(MOE_ERR_INVALID_ARG, "%s: host_doorbell misaligned", fn);
     if (o->last_use && !aligned(o->last_use, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: last_use misaligned", fn);
-    if (o->sync && !aligned(o->sync, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: sync misaligned", fn);
+    if (o->sync && !aligned(o->sync, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: sync not 256-byte aligned", fn);
     const hipStream_t s = as_stream(stream);
     moe::DispatchArgs a{};
     a.renorm = renormalize;

@@ -15,47 +15,74 @@
 
 namespace moe {
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every global store of the wave to complete, a memory round trip each time;
+// the bodies below write global outputs that no other thread of the
+// workgroup reads, so their barriers need only LDS order.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = threadIdx.x & 63;
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive scan of one flag/count per thread over the workgroup (blockDim =
-// 1024, at most 16 waves).  Returns this thread's exclusive prefix; *total gets
-// the sum.  `wsum` is LDS scratch of 16 ints.
-__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+// Inclusive prefix sum over the 64 lanes of a wave on DPP (Hillis-Steele
+// within each 16-lane row by row_shr 1, 2, 4, 8, then the row totals carried
+// by row_bcast 15 and 31); no LDS round trips.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += (int)__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (int)__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (int)__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (int)__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += (int)__builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+    v += (int)__builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Exclusive scans of N counts per thread over the workgroup (at most 16
+// waves), with one pair of barriers for all N.  Returns the thread's
+// exclusive prefixes in v; total[n] gets the sums.  `wsum` is LDS scratch of
+// 16 N ints.
+template <int N>
+__device__ void block_exclusive_scan(int (&v)[N], int* wsum, int (&total)[N]) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-    int incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
+    int incl[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        incl[n] = wave_inclusive_scan(v[n]);
+        if (lane == 63) wsum[16 * n + wid] = incl[n];
     }
-    if (lane == 63) wsum[wid] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-        int s = wsum[w];
-        base += (w < wid) ? s : 0;
-        tot += s;
+    lds_sync();
+    // the wave totals: lane w reads wave w's, one more wave scan gives every
+    // wave its base (all reads in parallel, no chain of LDS round trips)
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const int s = (lane < nw) ? wsum[16 * n + lane] : 0;
+        const int ws = wave_inclusive_scan(s);
+        const int base = __builtin_amdgcn_readlane(ws - s, wid);
+        total[n] = __builtin_amdgcn_readlane(ws, nw - 1);
+        v[n] = base + incl[n] - v[n];
     }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
+    lds_sync();
 }
 
 constexpr int kMaxE = 1024;
 
 // ---------------------------------------------------------------- lookup
 // Workgroup-wide body (blockDim = 1024): `ids` may live in global memory or
-// LDS; `flag` is LDS scratch of E ints, `wsum` of 16.
+// LDS; `flag` is LDS scratch of E ints, `wsum` of 32.
 __device__ void slot_lookup_body(const int32_t* ids, int P, int E, const int32_t* __restrict__ table,
                                  int n_slots, int32_t* __restrict__ pair_slot, int32_t* __restrict__ miss,
                                  int32_t* __restrict__ n_miss, int32_t* doorbell,
                                  uint32_t* __restrict__ last_use, uint32_t step, int* flag, int* wsum) {
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x) flag[e] = 0;
-    __syncthreads();
+    lds_sync();
     for (int p = tid; p < P; p += blockDim.x) {
         const int e = ids[p];
         if (e < 0 || e >= E) {
@@ -68,16 +95,19 @@ __device__ void slot_lookup_body(const int32_t* ids, int P, int E, const int32_t
         if (!hit) flag[e] = 1;
         else if (last_use) last_use[s] = step;
     }
-    __syncthreads();
+    lds_sync();
     int count = 0;
     for (int e0 = 0; e0 < E; e0 += blockDim.x) {
         const int e = e0 + tid;
         const int f = (e < E) ? flag[e] : 0;
-        int total;
-        const int pos = block_exclusive_scan(f, wsum, &total);
-        if (f) miss[count + pos] = e;
-        count += total;
+        int pos[1] = {f}, total[1];
+        block_exclusive_scan<1>(pos, wsum, total);
+        if (f) miss[count + pos[0]] = e;
+        count += total[0];
     }
+    // the doorbell is a release to the host: every wave's miss-list stores
+    // must be complete before it, hence the full barrier (it waits for them)
+    if (doorbell) __syncthreads();
     if (tid == 0) {
         *n_miss = count;
         if (doorbell && count > 0) {
@@ -95,7 +125,7 @@ __global__ __launch_bounds__(1024) void slot_lookup_kernel(const int32_t* __rest
                                                            uint32_t* __restrict__ last_use,
                                                            uint32_t step) {
     __shared__ int flag[kMaxE];
-    __shared__ int wsum[16];
+    __shared__ int wsum[32];
     slot_lookup_body(ids, P, E, table, n_slots, pair_slot, miss, n_miss, doorbell, last_use, step, flag, wsum);
 }
 
@@ -124,7 +154,7 @@ int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* tab
 constexpr int kPermWaves = 8;
 
 // Workgroup-wide body (blockDim = 1024).  LDS scratch: `cnt` kPermWaves x E
-// ints (row stride E), `offs`, `cnts`, `wpos` E ints each, `wsum` 16.
+// ints (row stride E), `offs`, `cnts`, `wpos` E ints each, `wsum` 32.
 __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* __restrict__ counts,
                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
                              int32_t* __restrict__ pair_to_row, int32_t* __restrict__ active,
@@ -136,7 +166,7 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
     const int chunk = (P + kPermWaves - 1) / kPermWaves;
 
     for (int i = tid; i < kPermWaves * E; i += blockDim.x) cnt_flat[i] = 0;
-    __syncthreads();
+    lds_sync();
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
         for (int p = p0 + lane; p < p1; p += 64) {
@@ -144,7 +174,7 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
             if (e >= 0 && e < E) atomicAdd(&cnt(wid, e), 1);
         }
     }
-    __syncthreads();
+    lds_sync();
 
     int running = 0, nact = 0, ntile_run = 0;
     for (int e0 = 0; e0 < E; e0 += blockDim.x) {
@@ -153,11 +183,13 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
         if (e < E)
 #pragma unroll
             for (int w = 0; w < kPermWaves; ++w) tot += cnt(w, e);
-        int sum, nsum, tsum;
-        const int excl = block_exclusive_scan(tot, wsum, &sum);
-        const int apos = block_exclusive_scan(tot > 0 ? 1 : 0, wsum, &nsum);
+        // one scan of (count | active flag << 16) and the tile count: counts
+        // sum to at most 4096 and flags to at most 1024, so the halves never mix
         const int tiles = (tot + kWorkRows - 1) / kWorkRows;
-        const int tpos = block_exclusive_scan(tiles, wsum, &tsum);
+        int sc[2] = {tot | ((tot > 0 ? 1 : 0) << 16), tiles}, st[2];
+        block_exclusive_scan<2>(sc, wsum, st);
+        const int excl = sc[0] & 0xFFFF, apos = sc[0] >> 16, tpos = sc[1];
+        const int sum = st[0] & 0xFFFF, nsum = st[0] >> 16, tsum = st[1];
         if (e < E) {
             counts[e] = tot;
             offsets[e] = running + excl;
@@ -182,7 +214,7 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
         *n_active = nact;
         *n_work = ntile_run;
     }
-    __syncthreads();
+    lds_sync();
 
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
@@ -244,7 +276,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     __shared__ int offs[kMaxE];
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
-    __shared__ int wsum[16];
+    __shared__ int wsum[32];
     permute_body(ids, P, E, k, counts, offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work, cnt,
                  offs, cnts, wpos, wsum);
 }
@@ -270,7 +302,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
     __shared__ int offs[kMaxE];
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
-    __shared__ int wsum[16];
+    __shared__ int wsum[32];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int t = wid; t < a.T; t += 16) {
         int my_id;
@@ -282,10 +314,10 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
             ids_s[t * a.k + lane] = my_id;
         }
     }
-    __syncthreads();
+    lds_sync();
     slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);
-    __syncthreads();
+    lds_sync();
     permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
                  a.work, a.n_work, scratch, offs, cnts, wpos, wsum);
 }
@@ -315,24 +347,29 @@ int launch_dispatch(const moe_dims& d, const float* logits, const DispatchArgs& 
 //      group (router_ops.h, four 256-thread groups side by side);
 //   2. the last workgroup to finish a token group (a ticket counter per
 //      group) picks the top-k of that group's tokens, one wave per token;
-//   3. the last token group to finish (a second ticket) copies all ids to LDS
-//      and runs the slot lookup and the counting sort.
+//   3. the last token group to finish (a second ticket; none with one token
+//      group) copies all ids to LDS and runs the slot lookup and the
+//      counting sort.
 // Nothing waits on another workgroup: the late arrivals do the next stage.
 // Logits and ids cross workgroups as device-scope atomic stores and loads
-// (see ticket()), so they are seen on other CUs and L2 slices.  Tickets live in sync[0] (token groups
-// done) and sync[1 + g] (expert blocks done for group g); each winner puts
-// its counter back to 0, so the buffer is all zero between calls.
+// (see ticket()), so they are seen on other CUs and L2 slices.  Counters sit
+// kSyncStride ints (256 bytes) apart: arrivals at counters in one cache line
+// queue behind each other at the atomic unit, which cost ~2 us per call with
+// 256 arrivals.  sync[0] counts token groups done, sync[kSyncStride (1 + g)]
+// the expert blocks done for group g; each winner puts its counter back to 0,
+// so the buffer is all zero between calls.
 constexpr int kRouteTG = 8;
 constexpr int kRouteMaxT = 64;
+constexpr int kSyncStride = 64;
+static_assert(kSyncStride * (1 + kRouteMaxT / kRouteTG) == MOE_DISPATCH_SYNC_INTS, "sync buffer layout");
 
 // Arrive at `counter` (out of `n` arrivals); true in every thread of the last
 // workgroup to arrive.  Data handed between workgroups through a ticket is
 // written with device-scope atomic stores and read with device-scope atomic
-// loads, which go to the device's point of coherence: no L2 write-back or
-// invalidate is needed (as a fence would do, for the whole L2 slice, at a cost
-// of microseconds).  Every wave waits for its stores to complete before the
-// barrier, so they are all done before thread 0 takes the ticket.
-__device__ __forceinline__ bool ticket(int32_t* counter, int n, int* winner) {
+// loads: those bypass the non-coherent per-CU caches, so the only ordering
+// needed is that this workgroup's stores have completed before its arrival is
+// counted, which the full s_waitcnt gives (no cache flush).
+__device__ bool ticket(int32_t* counter, int n, int* winner) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
@@ -347,47 +384,60 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
                                                               const float* __restrict__ bias,
                                                               float* __restrict__ logits, DispatchArgs a,
                                                               int32_t* __restrict__ sync) {
-    __shared__ float part[4][4][EB][kRouteTG];
+    // tokens per pass of the router: fewer for wide H, whose weight and
+    // activation registers would not fit the 1024-thread budget
+    constexpr int TT = NJ >= 6 ? kRouteTG / 2 : kRouteTG;
+    __shared__ float part[4][4][EB][TT];
     __shared__ int ids_s[kDispatchMaxP];
     __shared__ int scratch[kPermWaves * kMaxE];
     __shared__ int offs[kMaxE];
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
-    __shared__ int wsum[16];
+    __shared__ int wsum[32];
     __shared__ int winner;
     const int tid = threadIdx.x, sub = tid >> 8, lane = tid & 63, wid = tid >> 6;
     const int tg = blockIdx.y;
     const int tb = tg * kRouteTG, te = min(a.T, tb + kRouteTG);
+    int32_t* group_counter = sync + kSyncStride * (1 + tg);
 
     // 1. logits of this (expert block, token group)
-    router_block<EB, kRouteTG, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
-                                         part[sub], tid & 255);
-    if (!ticket(&sync[1 + tg], (int)gridDim.x, &winner)) return;
+    router_block<EB, TT, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
+                                   part[sub], tid & 255);
+    if (!ticket(group_counter, (int)gridDim.x, &winner)) return;
 
-    // 2. top-k of the group's tokens
+    // 2. top-k of the group's tokens.  With one token group this workgroup is
+    // also the last group: its ids go straight to LDS and the second ticket
+    // is skipped.
+    const bool single = gridDim.y == 1;
     if (wid < te - tb) {
         const int t = tb + wid;
         int my_id;
         float my_gate;
         topk_one_token<PER, true>(logits + (size_t)t * a.E, a.E, a.k, a.renorm, my_id, my_gate);
         if (lane < a.k) {
-            __hip_atomic_store(a.ids + (size_t)t * a.k + lane, my_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (single) {
+                a.ids[(size_t)t * a.k + lane] = my_id;
+                ids_s[t * a.k + lane] = my_id;
+            } else {
+                __hip_atomic_store(a.ids + (size_t)t * a.k + lane, my_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             a.gates[(size_t)t * a.k + lane] = my_gate;
         }
     }
-    if (tid == 0) __hip_atomic_store(&sync[1 + tg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!ticket(&sync[0], (int)gridDim.y, &winner)) return;
-
-    // 3. lookup and grouping over all pairs
-    for (int p = tid; p < a.P; p += blockDim.x)
-        ids_s[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+    if (tid == 0) __hip_atomic_store(group_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!single) {
+        if (!ticket(&sync[0], (int)gridDim.y, &winner)) return;
+        // 3. lookup and grouping over all pairs
+        for (int p = tid; p < a.P; p += blockDim.x)
+            ids_s[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_sync();
     slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);
-    __syncthreads();
+    lds_sync();
     permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
                  a.work, a.n_work, scratch, offs, cnts, wpos, wsum);
-    if (tid == 0) __hip_atomic_store(&sync[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0 && !single) __hip_atomic_store(&sync[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 bool route_dispatch_fused(const moe_dims& d) {

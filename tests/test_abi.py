@@ -169,6 +169,8 @@ def test_route_dispatch_validation():
     assert call(_dispatch(work_list=FAKE + 4)) == moe.ERR_INVALID_ARG
     assert call(_dispatch(host_doorbell=MISALIGNED)) == moe.ERR_INVALID_ARG
     assert call(_dispatch(sync=MISALIGNED)) == moe.ERR_INVALID_ARG
+    assert call(_dispatch(sync=FAKE + 128)) == moe.ERR_INVALID_ARG          # counters need 256-byte alignment
+    assert "sync" in moe.last_error()
     bad = moe.Dims(4, 256, 512, 8, 9, 128)
     assert L.moe_route_dispatch(ctypes.byref(bad), FAKE, FAKE, None, 1, FAKE, ctypes.byref(_dispatch()),
                                 None) == moe.ERR_UNSUPPORTED

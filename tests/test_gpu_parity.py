@@ -16,7 +16,7 @@ import oracle
 import quantized_expert_ffn_gemv_amd as moe
 
 from gpu_util import (check_combine_exact, check_ffn, check_logits, check_lookup, check_permute,
-                      check_topk, run_layer, say, tolerance_metrics, upload_layer)
+                      check_topk, run_layer, say, to_dev, to_host, tolerance_metrics, upload_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -347,3 +347,47 @@ def test_route_dispatch_paths_agree(name, T):
         assert np.array_equal(one.active[:na].cpu().numpy(), sep.active[:na].cpu().numpy())
         g = dict(logits=one.logits.cpu().numpy(), ids=one.topk_ids.cpu().numpy(), gates=one.topk_w.cpu().numpy())
         check_topk(g, L)
+
+
+def _edge_logits(T, E, seed):
+    """Logits built to exercise every ranking rule: ties (to the lower id), -0 == +0,
+    NaN below -inf, +-inf, and many exact duplicates."""
+    rng = np.random.default_rng(seed)
+    L = np.round(rng.standard_normal((T, E)), 1).astype(np.float32)   # ~60 distinct values: many ties
+    L[0, :] = 0.5                                                        # all equal
+    if T > 1:
+        L[1, :] = -1.0
+        L[1, rng.choice(E, size=min(E, 6), replace=False)] = -0.0
+        L[1, rng.choice(E, size=min(E, 6), replace=False)] = 0.0
+    if T > 2:
+        L[2, rng.choice(E, size=E // 3, replace=False)] = np.nan
+        L[2, rng.choice(E, size=min(E, 4), replace=False)] = -np.inf
+        L[2, rng.choice(E, size=min(E, 2), replace=False)] = np.inf
+    if T > 3:
+        L[3, :] = np.nan
+        L[3, rng.choice(E, size=min(E, 3), replace=False)] = rng.standard_normal(min(E, 3))
+    if T > 4:
+        L[4, E - 1] = 9.0
+        L[4, E // 2] = 9.0                                               # equal maxima, far apart
+    return L
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 8), (64, 8), (200, 8), (256, 32), (300, 5), (1000, 16), (1000, 1)])
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_topk_edge_cases(E, k, renorm):
+    """Top-k on constructed logits through moe_topk_from_logits: ids bit-exact against
+    the oracle, gates within 2e-6 (NaN where the oracle gives NaN)."""
+    T = 9
+    L = _edge_logits(T, E, seed=E * 100 + k)
+    d = moe.dims(T, 256, 256, E, k)
+    ids_d = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    g_d = torch.full((T, k), -7.0, dtype=torch.float32, device="cuda")
+    say(f"[topk] E={E} k={k} renorm={renorm}")
+    moe.topk_from_logits(d, to_dev(L), bool(renorm), ids_d, g_d)
+    torch.cuda.synchronize()
+    ids_ref, g_ref = oracle.topk(L, k, bool(renorm))
+    ids, g = to_host(ids_d), to_host(g_d)
+    assert np.array_equal(ids, ids_ref), f"ids differ in rows {np.nonzero((ids != ids_ref).any(1))[0].tolist()}"
+    nan_ref = np.isnan(g_ref)
+    assert np.array_equal(np.isnan(g), nan_ref)
+    assert np.max(np.abs(g[~nan_ref] - g_ref[~nan_ref]), initial=0.0) <= 2e-6

@@ -55,6 +55,16 @@ template <int BITS> constexpr int kLever = (BITS == 4) ? 8 : 16;
 template <int BITS> constexpr float kInvLever = 1.0f / (float)kLever<BITS>;
 template <int BITS> constexpr float kOffset = 128.0f / (float)kLever<BITS>;
 
+// Read a value that no kernel writes while this one runs through the scalar
+// path: uniform addresses in the constant address space become s_load, which
+// waits on its own counter instead of queueing behind vector loads.  Used for
+// the routing lists written by earlier kernels.
+template <typename T>
+__device__ __forceinline__ T ld_scalar(const T* p, size_t i) {
+    typedef const __attribute__((address_space(4))) T* cptr;
+    return ((cptr)(p))[i];
+}
+
 // v >> sh for sh >= 0, v << -sh otherwise (sh is a compile-time constant)
 __device__ __forceinline__ uint32_t shift_to(uint32_t v, int sh) { return sh >= 0 ? (v >> sh) : (v << (-sh)); }
 

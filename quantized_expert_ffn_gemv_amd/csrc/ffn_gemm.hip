@@ -24,6 +24,7 @@
 // bf16 rounding of the expert output).
 #include <atomic>
 
+#include "launch_util.h"
 #include "mfma_ops.h"
 
 namespace moe {
@@ -587,30 +588,9 @@ size_t gemm_workspace_bytes(const moe_dims& d) {
     return mfma_workspace_bytes(d) + (((size_t)max_heads(d) + 1 + 64) * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-static int num_cus_gemm() {
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
-}
-
 template <typename K>
 static dim3 gemm_grid(K kernel, std::atomic<uint64_t>& cache, size_t lds, long max_items) {
-    const uint64_t c = cache.load(std::memory_order_relaxed);
-    int per_cu = (int)(c & 0xFF);
-    if (per_cu == 0 || (c >> 8) != lds) {
-        per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        per_cu = per_cu > 8 ? 8 : per_cu;
-        cache.store(((uint64_t)lds << 8) | (uint64_t)per_cu, std::memory_order_relaxed);
-    }
-    const long g = (long)per_cu * num_cus_gemm();
-    return dim3((unsigned)(max_items < g ? (max_items > 0 ? max_items : 1) : g));
+    return dim3(persistent_blocks(kernel, cache, 256, lds, max_items));
 }
 
 static GemmParams gemm_params(const FfnArgs& a) {

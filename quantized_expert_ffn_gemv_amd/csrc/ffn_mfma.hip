@@ -31,6 +31,7 @@
 // operand needs, plus per-16-row partial sums of h for the down bias fold.
 #include <atomic>
 
+#include "launch_util.h"
 #include "mfma_ops.h"
 
 namespace moe {
@@ -495,35 +496,12 @@ static size_t mfma_lds_bytes(int NG) {
     return ((size_t)kWaves * 2 * NGW * 64 + (size_t)kWaves * 64 * 8) * sizeof(float);
 }
 
-static int num_cus() {
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
-}
-
-// Workgroups of a persistent launch: as many as fit on the chip at once (from
-// the kernel's registers and LDS), never more than there can be items.  The
-// occupancy answer is cached (per kernel, by the caller) for the last LDS size.
+// Workgroups of a persistent launch (launch_util.h): as many as fit on the
+// chip at once, never more than there can be items.
 template <typename K>
 static dim3 persistent_grid(K kernel, std::atomic<uint64_t>& cache, size_t lds, const moe_dims& d,
                             int items_per_entry) {
-    const uint64_t c = cache.load(std::memory_order_relaxed);
-    int per_cu = (int)(c & 0xFF);
-    if (per_cu == 0 || (c >> 8) != lds) {
-        per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        per_cu = per_cu > 8 ? 8 : per_cu;
-        cache.store(((uint64_t)lds << 8) | (uint64_t)per_cu, std::memory_order_relaxed);
-    }
-    const long max_items = work_capacity(d) * items_per_entry;
-    const long g = (long)per_cu * num_cus();
-    return dim3((unsigned)(max_items < g ? max_items : g));
+    return dim3(persistent_blocks(kernel, cache, 256, lds, work_capacity(d) * items_per_entry));
 }
 
 // Prefetch depth: the deepest ring (up to cap) that pads a wave's NGW groups

@@ -88,16 +88,6 @@ __device__ __forceinline__ void split3_bf16(float h, uint32_t& hi, uint32_t& mid
 }
 
 
-// Read a value that no kernel writes while this one runs through the scalar
-// path: uniform addresses in the constant address space become s_load, which
-// waits on its own counter instead of queueing behind the vector loads of the
-// code stream.  Used for the routing lists written by earlier kernels.
-template <typename T>
-__device__ __forceinline__ T ld_scalar(const T* p, size_t i) {
-    typedef const __attribute__((address_space(4))) T* cptr;
-    return ((cptr)(p))[i];
-}
-
 // Weight row held by output row m (0..15) of a 16-row tile.  The gate/up
 // kernel stores h of its output rows 4q..4q+3 at consecutive positions, and
 // the down kernel reads h in the pair order of its code operands; loading the

@@ -330,7 +330,12 @@ def main():
     def measure(T, steps, warmup):
         r = Runner(torch, mi, moe, shape, layers, T, algo)
         U = r.experts_used()
-        total_ms, wall, gate_ms, down_ms = r.timed(steps, warmup)
+        # throughput: the K steps back to back, nothing recorded between kernels
+        total_ms, wall, _, _ = r.timed(steps, warmup, with_events=False)
+        # kernel durations: the same K steps again with HIP events around the
+        # gate/up and down launches on their stream (events between kernels
+        # lengthen the step a little, so this pass does not set the throughput)
+        ev_total_ms, _, gate_ms, down_ms = r.timed(steps, 0)
         Us = [U[i % len(U)] for i in range(steps)]
         gate_bytes = sum(u * gate_bytes_per_expert for u in Us)
         down_bytes = sum(u * down_bytes_per_expert for u in Us)
@@ -338,6 +343,7 @@ def main():
         down_s = sum(down_ms) / 1e3
         ms_step = total_ms / steps
         return dict(T=T, steps=steps, ms_per_step=ms_step, tokens_per_s=T * steps / (total_ms / 1e3),
+                    ms_per_step_with_kernel_events=ev_total_ms / steps,
                     wall_s=wall, U_mean=float(np.mean(U)), U_per_set=U,
                     gateup_us=gate_s / steps * 1e6, down_us=down_s / steps * 1e6,
                     gateup_GBps=gate_bytes / gate_s / 1e9, down_GBps=down_bytes / down_s / 1e9,
@@ -417,6 +423,7 @@ def main():
             "layer_GBps_incl_router": round(main_run["layer_GBps"], 1),
             "gateup_us": round(main_run["gateup_us"], 3),
             "down_us": round(main_run["down_us"], 3),
+            "ms_per_step_with_kernel_events": round(main_run["ms_per_step_with_kernel_events"], 5),
         },
         "sweep": sweep,
         "prefill": prefill,

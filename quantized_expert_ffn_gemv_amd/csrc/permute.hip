@@ -25,6 +25,12 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Threads (and waves) of every workgroup that runs the bodies below.  A
+// constant rather than blockDim: reading blockDim is a scalar load from the
+// dispatch packet, a memory round trip each time.
+constexpr int kBodyThreads = 1024;
+constexpr int kBodyWaves = kBodyThreads / 64;
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = threadIdx.x & 63;
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -50,7 +56,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 template <int N>
 __device__ void block_exclusive_scan(int (&v)[N], int* wsum, int (&total)[N]) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
+    constexpr int nw = kBodyWaves;
     int incl[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -75,15 +81,17 @@ constexpr int kMaxE = 1024;
 
 // ---------------------------------------------------------------- lookup
 // Workgroup-wide body (blockDim = 1024): `ids` may live in global memory or
-// LDS; `flag` is LDS scratch of E ints, `wsum` of 32.
-__device__ void slot_lookup_body(const int32_t* ids, int P, int E, const int32_t* __restrict__ table,
+// LDS; `table` is the caller's LDS copy of slot_of_expert (staged early, so
+// the lookup waits on no global load); `flag` is LDS scratch of E ints,
+// `wsum` of 32.
+__device__ void slot_lookup_body(const int32_t* ids, int P, int E, const int* table,
                                  int n_slots, int32_t* __restrict__ pair_slot, int32_t* __restrict__ miss,
                                  int32_t* __restrict__ n_miss, int32_t* doorbell,
                                  uint32_t* __restrict__ last_use, uint32_t step, int* flag, int* wsum) {
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += blockDim.x) flag[e] = 0;
+    for (int e = tid; e < E; e += kBodyThreads) flag[e] = 0;
     lds_sync();
-    for (int p = tid; p < P; p += blockDim.x) {
+    for (int p = tid; p < P; p += kBodyThreads) {
         const int e = ids[p];
         if (e < 0 || e >= E) {
             pair_slot[p] = -1;
@@ -97,7 +105,7 @@ __device__ void slot_lookup_body(const int32_t* ids, int P, int E, const int32_t
     }
     lds_sync();
     int count = 0;
-    for (int e0 = 0; e0 < E; e0 += blockDim.x) {
+    for (int e0 = 0; e0 < E; e0 += kBodyThreads) {
         const int e = e0 + tid;
         const int f = (e < E) ? flag[e] : 0;
         int pos[1] = {f}, total[1];
@@ -125,8 +133,11 @@ __global__ __launch_bounds__(1024) void slot_lookup_kernel(const int32_t* __rest
                                                            uint32_t* __restrict__ last_use,
                                                            uint32_t step) {
     __shared__ int flag[kMaxE];
+    __shared__ int tab[kMaxE];
     __shared__ int wsum[32];
-    slot_lookup_body(ids, P, E, table, n_slots, pair_slot, miss, n_miss, doorbell, last_use, step, flag, wsum);
+    for (int e = (int)threadIdx.x; e < E; e += kBodyThreads) tab[e] = table[e];
+    lds_sync();
+    slot_lookup_body(ids, P, E, tab, n_slots, pair_slot, miss, n_miss, doorbell, last_use, step, flag, wsum);
 }
 
 int launch_slot_lookup(const moe_dims& d, const int32_t* ids, const int32_t* table, int32_t n_slots,
@@ -165,7 +176,7 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int chunk = (P + kPermWaves - 1) / kPermWaves;
 
-    for (int i = tid; i < kPermWaves * E; i += blockDim.x) cnt_flat[i] = 0;
+    for (int i = tid; i < kPermWaves * E; i += kBodyThreads) cnt_flat[i] = 0;
     lds_sync();
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
@@ -177,7 +188,7 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
     lds_sync();
 
     int running = 0, nact = 0, ntile_run = 0;
-    for (int e0 = 0; e0 < E; e0 += blockDim.x) {
+    for (int e0 = 0; e0 < E; e0 += kBodyThreads) {
         const int e = e0 + tid;
         int tot = 0;
         if (e < E)
@@ -303,7 +314,10 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
     __shared__ int wsum[32];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // the resident table is requested first and parked in `offs` (free until
+    // the grouping) once the top-k is done: the lookup then reads only LDS
+    const int tab_v = tid < a.E ? a.table[tid] : -1;
     for (int t = wid; t < a.T; t += 16) {
         int my_id;
         float my_gate;
@@ -314,8 +328,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
             ids_s[t * a.k + lane] = my_id;
         }
     }
+    if (tid < a.E) offs[tid] = tab_v;
     lds_sync();
-    slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
+    slot_lookup_body(ids_s, a.P, a.E, offs, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);
     lds_sync();
     permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
@@ -404,6 +419,8 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     router_block<EB, TT, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
                                    part[sub], tid & 255);
     if (!ticket(group_counter, (int)gridDim.x, &winner)) return;
+    // the resident table, requested now, parked in `offs` for the lookup
+    const int tab_v = tid < a.E ? a.table[tid] : -1;
 
     // 2. top-k of the group's tokens.  With one token group this workgroup is
     // also the last group: its ids go straight to LDS and the second ticket
@@ -428,11 +445,12 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     if (!single) {
         if (!ticket(&sync[0], (int)gridDim.y, &winner)) return;
         // 3. lookup and grouping over all pairs
-        for (int p = tid; p < a.P; p += blockDim.x)
+        for (int p = tid; p < a.P; p += kBodyThreads)
             ids_s[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid < a.E) offs[tid] = tab_v;
     lds_sync();
-    slot_lookup_body(ids_s, a.P, a.E, a.table, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
+    slot_lookup_body(ids_s, a.P, a.E, offs, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);
     lds_sync();
     permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,

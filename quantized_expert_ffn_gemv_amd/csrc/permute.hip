@@ -274,6 +274,121 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
     }
 }
 
+// ------------------------------------------------- lookup + grouping, one wave
+// The same outputs as slot_lookup_body followed by permute_body, computed by
+// one wave 64 pairs (or experts) at a time: no workgroup barriers, and LDS
+// accesses of one wave complete in program order.  Used for decode batches
+// (P <= kWaveMaxP), where the barriers of the workgroup version cost more than
+// the work.  LDS: `tab` the resident table, `cnt`, `offs`, `wpos` E ints each,
+// `rank` P ints.
+constexpr int kWaveMaxP = 64;
+
+__device__ void lookup_permute_wave(const int* ids, int P, int E, int k, const int* tab, int n_slots,
+                                    int32_t* __restrict__ pair_slot, int32_t* __restrict__ miss,
+                                    int32_t* __restrict__ n_miss, int32_t* doorbell,
+                                    uint32_t* __restrict__ last_use, uint32_t step, int32_t* __restrict__ counts,
+                                    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+                                    int32_t* __restrict__ pair_to_row, int32_t* __restrict__ active,
+                                    int32_t* __restrict__ n_active, int32_t* __restrict__ work,
+                                    int32_t* __restrict__ n_work, int* cnt, int* offs, int* wpos, int* rank) {
+    const int lane = threadIdx.x & 63;
+    // 1. per-expert counters, and miss flags (held in offs until step 4)
+    for (int e = lane; e < E; e += 64) {
+        cnt[e] = 0;
+        offs[e] = 0;
+    }
+    // 2. lookup, and each pair's stable rank within its expert
+    for (int p0 = 0; p0 < P; p0 += 64) {
+        const int p = p0 + lane;
+        const bool live = p < P;
+        int e = live ? ids[p] : -1;
+        const bool ok = live && e >= 0 && e < E;
+        if (live) {
+            int sl = -1;
+            if (ok) {
+                const int t = tab[e];
+                if (t >= 0 && t < n_slots) sl = t;
+            }
+            pair_slot[p] = sl;
+            if (ok && sl < 0) offs[e] = 1;
+            if (sl >= 0 && last_use) last_use[sl] = step;
+        }
+        if (!ok) e = -1;
+        uint64_t same = __ballot(ok);
+#pragma unroll
+        for (int b = 0; b < 10; ++b) {
+            const uint64_t bal = __ballot(ok && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? bal : ~bal;
+        }
+        const int r = __popcll(same & lanemask_lt()), n_same = __popcll(same);
+        const int base = ok ? cnt[e] : 0;
+        __builtin_amdgcn_wave_barrier();             // every read of cnt before the update
+        if (ok) {
+            rank[p] = base + r;
+            if (r == n_same - 1) cnt[e] = base + n_same;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    // 3. miss list: flagged experts, ascending
+    int count = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int f = e < E ? offs[e] : 0;
+        const int incl = wave_inclusive_scan(f);
+        if (f) miss[count + incl - 1] = e;
+        count += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) {
+        *n_miss = count;
+        // a release to the host: the miss-list stores above are this wave's
+        if (doorbell && count > 0) __hip_atomic_store(doorbell, count, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    // 4. offsets, active list, first work-list entry of each expert
+    int running = 0, nact = 0, ntiles = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int c = e < E ? cnt[e] : 0;
+        const int tiles = (c + kWorkRows - 1) / kWorkRows;
+        const int ic = wave_inclusive_scan(c), ia = wave_inclusive_scan(c > 0 ? 1 : 0);
+        const int it = wave_inclusive_scan(tiles);
+        if (e < E) {
+            counts[e] = c;
+            offsets[e] = running + ic - c;
+            offs[e] = running + ic - c;
+            wpos[e] = ntiles + it - tiles;
+            if (c > 0) active[nact + ia - 1] = e;
+        }
+        running += __builtin_amdgcn_readlane(ic, 63);
+        nact += __builtin_amdgcn_readlane(ia, 63);
+        ntiles += __builtin_amdgcn_readlane(it, 63);
+    }
+    if (lane == 0) {
+        offsets[E] = running;
+        *n_active = nact;
+        *n_work = ntiles;
+    }
+    // 5. scatter, inverse map and work list
+    for (int p = lane; p < P; p += 64) {
+        const int e = ids[p];
+        if (e < 0 || e >= E) continue;
+        const int off = rank[p], row = offs[e] + off;
+        sorted_pairs[row] = p;
+        pair_to_row[p] = row;
+        int32_t* ent = work + (size_t)(wpos[e] + off / kWorkRows) * kWorkInts;
+        const int slot = off % kWorkRows, tok = p / k;
+        ent[4 + slot] = tok;
+        if (slot == 0) {
+            // header, and the token of slot 0 in the unused slots of a short tile
+            const int rows = min(kWorkRows, cnt[e] - off);
+            ent[0] = e;
+            ent[1] = row;
+            ent[2] = rows;
+            ent[3] = off / kWorkRows;
+            for (int j = rows; j < kWorkRows; ++j) ent[4 + j] = tok;
+        }
+    }
+}
+
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                        int k, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets,
@@ -315,7 +430,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
     __shared__ int wpos[kMaxE];
     __shared__ int wsum[32];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    // the resident table is requested first and parked in `offs` (free until
+    // the resident table is requested first and parked in `cnts` (free until
     // the grouping) once the top-k is done: the lookup then reads only LDS
     const int tab_v = tid < a.E ? a.table[tid] : -1;
     for (int t = wid; t < a.T; t += 16) {
@@ -328,9 +443,16 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
             ids_s[t * a.k + lane] = my_id;
         }
     }
-    if (tid < a.E) offs[tid] = tab_v;
+    if (tid < a.E) cnts[tid] = tab_v;
     lds_sync();
-    slot_lookup_body(ids_s, a.P, a.E, offs, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
+    if (a.P <= kWaveMaxP) {
+        if (wid == 0)
+            lookup_permute_wave(ids_s, a.P, a.E, a.k, cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell,
+                                a.last_use, a.step, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active,
+                                a.n_active, a.work, a.n_work, scratch, offs, wpos, scratch + kMaxE);
+        return;
+    }
+    slot_lookup_body(ids_s, a.P, a.E, cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);
     lds_sync();
     permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
@@ -419,7 +541,7 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     router_block<EB, TT, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
                                    part[sub], tid & 255);
     if (!ticket(group_counter, (int)gridDim.x, &winner)) return;
-    // the resident table, requested now, parked in `offs` for the lookup
+    // the resident table, requested now, parked in `cnts` for the lookup
     const int tab_v = tid < a.E ? a.table[tid] : -1;
 
     // 2. top-k of the group's tokens.  With one token group this workgroup is
@@ -448,9 +570,18 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
         for (int p = tid; p < a.P; p += kBodyThreads)
             ids_s[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid < a.E) offs[tid] = tab_v;
+    if (tid < a.E) cnts[tid] = tab_v;
     lds_sync();
-    slot_lookup_body(ids_s, a.P, a.E, offs, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
+    if (a.P <= kWaveMaxP) {
+        if (wid == 0) {
+            lookup_permute_wave(ids_s, a.P, a.E, a.k, cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell,
+                                a.last_use, a.step, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active,
+                                a.n_active, a.work, a.n_work, scratch, offs, wpos, scratch + kMaxE);
+            if (lane == 0 && !single) __hip_atomic_store(&sync[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    slot_lookup_body(ids_s, a.P, a.E, cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
                      a.step, scratch, wsum);
     lds_sync();
     permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,

@@ -45,6 +45,7 @@ struct DecParams {
     uint16_t* y;        // [P][H]
     int T, H, I, E, P;
     int ipe;            // items per work-list entry
+    int cap;            // work-list capacity (entries)
     int rows_cap;       // token rows of the LDS tile: min(16, T)
 };
 
@@ -106,9 +107,14 @@ struct DecItem {
 __device__ __forceinline__ DecItem dec_item(const DecParams& p) {
     typedef int int4v __attribute__((ext_vector_type(4)));
     DecItem it;
-    it.entry = (int)blockIdx.x / p.ipe;
-    it.rb = (int)blockIdx.x % p.ipe;
-    const int4v* ent = reinterpret_cast<const int4v*>(p.work + (size_t)it.entry * kWorkInts);
+    // Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD
+    // b % 8): the items of entry e all go to XCD e % 8, so its activation or
+    // h tile is fetched into that XCD's L2 once and hit by the other items.
+    const int b = (int)blockIdx.x, xcd = b & 7, s = b >> 3;
+    it.entry = (s / p.ipe) * 8 + xcd;
+    it.rb = s % p.ipe;
+    const int re = it.entry < p.cap ? it.entry : p.cap - 1;      // the grid rounds entries up to 8
+    const int4v* ent = reinterpret_cast<const int4v*>(p.work + (size_t)re * kWorkInts);
     const int n_work = ld_scalar(p.n_work, 0);
     int4v v[kWorkInts / 4];
 #pragma unroll
@@ -497,6 +503,7 @@ static DecParams dec_params(const FfnArgs& a) {
     p.x = a.x; p.work = a.work; p.n_work = a.n_work; p.y = a.y;
     p.T = d.T; p.H = d.H; p.I = d.I; p.E = d.E; p.P = d.T * d.k;
     p.rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
+    p.cap = (int)work_capacity(d);
     char* ws = reinterpret_cast<char*>(a.h);
     const size_t P = (size_t)p.P;
     p.hp = reinterpret_cast<uint16_t*>(ws);
@@ -555,7 +562,7 @@ bool dec_down_fits(const moe_dims& d) { return dec_down_lds(d, dec_down_rt(d)) <
 
 template <int BITS, int RW, int D>
 static void gu_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    const dim3 grid((unsigned)(work_capacity(d) * p.ipe));
+    const dim3 grid((unsigned)((p.cap + 7) / 8 * 8 * p.ipe));      // entries rounded up to 8 (one per XCD)
     hipLaunchKernelGGL((ffn_gateup_dec_kernel<BITS, RW, D>), grid, dim3(256), lds, s, p);
 }
 
@@ -591,7 +598,7 @@ int launch_gateup_dec(const FfnArgs& a, hipStream_t s) {
 
 template <int BITS, int RT, int D>
 static void dn_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    const dim3 grid((unsigned)(work_capacity(d) * p.ipe));
+    const dim3 grid((unsigned)((p.cap + 7) / 8 * 8 * p.ipe));      // entries rounded up to 8 (one per XCD)
     hipLaunchKernelGGL((ffn_down_dec_kernel<BITS, RT, D>), grid, dim3(256), lds, s, p);
 }
 

@@ -79,7 +79,12 @@ __device__ __forceinline__ void act_operand(const uint32_t* X, int s, uint32_t (
     }
 }
 
+// h = hi + mid + lo exactly (each difference below is exact in float32).
+// Contraction is off: otherwise the compiler may fuse the multiply that made h
+// into h - hi, splitting the unrounded product instead, and then two kernels
+// that compute the same h would store different planes.
 __device__ __forceinline__ void split3_bf16(float h, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+#pragma clang fp contract(off)
     hi = f32_to_bf16_bits(h);
     const float r1 = h - bf16_bits_to_f32(hi);
     mid = f32_to_bf16_bits(r1);

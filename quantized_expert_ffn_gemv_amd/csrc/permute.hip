@@ -292,7 +292,7 @@ __device__ void lookup_permute_wave(const int* ids, int P, int E, int k, const i
                                     int32_t* __restrict__ n_active, int32_t* __restrict__ work,
                                     int32_t* __restrict__ n_work, int* cnt, int* offs, int* wpos, int* rank) {
     const int lane = threadIdx.x & 63;
-    // 1. per-expert counters, and miss flags (held in offs until step 4)
+    // 1. per-expert counters, and miss flags (held in offs until step 3)
     for (int e = lane; e < E; e += 64) {
         cnt[e] = 0;
         offs[e] = 0;
@@ -329,45 +329,44 @@ __device__ void lookup_permute_wave(const int* ids, int P, int E, int k, const i
         }
         __builtin_amdgcn_wave_barrier();
     }
-    // 3. miss list: flagged experts, ascending
-    int count = 0;
+    // 3. per chunk of 64 experts: counts, offsets, active list, miss list and
+    // each expert's first work-list entry, from two packed scans (within a
+    // chunk, rows sum to at most P < 2^16, tiles to at most P + 64, and the
+    // active and missed experts to at most 64 each)
+    int running = 0, nact = 0, ntiles = 0, nmiss = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
-        const int f = e < E ? offs[e] : 0;
-        const int incl = wave_inclusive_scan(f);
-        if (f) miss[count + incl - 1] = e;
-        count += __builtin_amdgcn_readlane(incl, 63);
-    }
-    if (lane == 0) {
-        *n_miss = count;
-        // a release to the host: the miss-list stores above are this wave's
-        if (doorbell && count > 0) __hip_atomic_store(doorbell, count, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    // 4. offsets, active list, first work-list entry of each expert
-    int running = 0, nact = 0, ntiles = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        const int c = e < E ? cnt[e] : 0;
+        const bool in = e < E;
+        const int c = in ? cnt[e] : 0;
+        const int f = in ? offs[e] : 0;
         const int tiles = (c + kWorkRows - 1) / kWorkRows;
-        const int ic = wave_inclusive_scan(c), ia = wave_inclusive_scan(c > 0 ? 1 : 0);
-        const int it = wave_inclusive_scan(tiles);
-        if (e < E) {
+        const int v1 = c | ((c > 0 ? 1 : 0) << 16), v2 = tiles | (f << 16);
+        const int i1 = wave_inclusive_scan(v1), i2 = wave_inclusive_scan(v2);
+        const int x1 = i1 - v1, x2 = i2 - v2;
+        if (in) {
+            const int off = running + (x1 & 0xFFFF);
             counts[e] = c;
-            offsets[e] = running + ic - c;
-            offs[e] = running + ic - c;
-            wpos[e] = ntiles + it - tiles;
-            if (c > 0) active[nact + ia - 1] = e;
+            offsets[e] = off;
+            offs[e] = off;
+            wpos[e] = ntiles + (x2 & 0xFFFF);
+            if (c > 0) active[nact + (x1 >> 16)] = e;
+            if (f) miss[nmiss + (x2 >> 16)] = e;
         }
-        running += __builtin_amdgcn_readlane(ic, 63);
-        nact += __builtin_amdgcn_readlane(ia, 63);
-        ntiles += __builtin_amdgcn_readlane(it, 63);
+        const int t1 = __builtin_amdgcn_readlane(i1, 63), t2 = __builtin_amdgcn_readlane(i2, 63);
+        running += t1 & 0xFFFF;
+        nact += t1 >> 16;
+        ntiles += t2 & 0xFFFF;
+        nmiss += t2 >> 16;
     }
     if (lane == 0) {
         offsets[E] = running;
         *n_active = nact;
         *n_work = ntiles;
+        *n_miss = nmiss;
+        // a release to the host: the miss-list stores above are this wave's
+        if (doorbell && nmiss > 0) __hip_atomic_store(doorbell, nmiss, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    // 5. scatter, inverse map and work list
+    // 4. scatter, inverse map and work list
     for (int p = lane; p < P; p += 64) {
         const int e = ids[p];
         if (e < 0 || e >= E) continue;

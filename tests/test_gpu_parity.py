@@ -349,6 +349,57 @@ def test_route_dispatch_paths_agree(name, T):
         check_topk(g, L)
 
 
+# (E, H, T, k, pool): the router is the identity on the first E features,
+# so each token's logits are its crafted activations; experts come from a pool
+# of `pool` ids, so they repeat across tokens and some get several tiles
+CRAFTED = [(1000, 1024, 8, 8, 24), (300, 384, 16, 4, 40), (1000, 1024, 32, 8, 12), (520, 640, 2, 32, 520),
+           (256, 256, 1, 8, 256), (64, 128, 64, 1, 5)]
+
+
+@pytest.mark.parametrize("E,H,T,k,pool", CRAFTED, ids=[f"E{c[0]}_T{c[2]}_k{c[3]}" for c in CRAFTED])
+def test_dispatch_crafted_ids(E, H, T, k, pool):
+    """Lookup and grouping on chosen expert ids (wide expert counts, repeated
+    experts, multi-tile experts, misses): the one-launch routing and the
+    two-launch routing against the oracle's lookup, permutation and work list."""
+    rng = np.random.default_rng(E + 7 * T + k)
+    choices = rng.permutation(E)[:pool]
+    ids_want = np.stack([rng.choice(choices, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = np.zeros((T, H), np.float32)
+    for t in range(T):
+        x[t, ids_want[t]] = 100.0 + np.arange(k)[::-1]          # exact in bf16, distinct, descending
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    w = np.zeros((E, H), np.float32)
+    w[np.arange(E), np.arange(E)] = 1.0
+    table = np.full(E, -1, np.int32)
+    res = rng.permutation(E)[: E // 3]
+    table[res] = np.arange(res.size, dtype=np.int32)
+    d = moe.dims(T, H, 256, E, k)
+    for sync in (True, False):
+        buf = moe.LayerBuffers.allocate(d, 4)
+        say(f"[run] crafted dispatch E={E} T={T} k={k} sync={sync}")
+        moe.route_dispatch(d, to_dev(xb), to_dev(w), None, True, buf.logits, buf.topk_ids, buf.topk_w, to_dev(table),
+                           res.size, buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets, buf.sorted_pairs,
+                           buf.pair_to_row, buf.active, buf.n_active, buf.work_list, buf.n_work,
+                           sync=buf.sync if sync else None)
+        torch.cuda.synchronize()
+        ids = to_host(buf.topk_ids)
+        assert np.array_equal(ids, ids_want)
+        P = T * k
+        lk = oracle.slot_lookup(ids, table, res.size)
+        assert np.array_equal(to_host(buf.pair_slot)[:P], lk["pair_slot"])
+        n_miss = int(to_host(buf.n_miss)[0])
+        assert n_miss == lk["n_miss"] and np.array_equal(to_host(buf.miss)[:n_miss], lk["miss"][:n_miss])
+        ref = oracle.permute(ids, E)
+        for key, n in (("counts", E), ("offsets", E + 1), ("sorted_pairs", P), ("pair_to_row", P)):
+            assert np.array_equal(to_host(getattr(buf, key))[:n], ref[key]), key
+        na = int(to_host(buf.n_active)[0])
+        assert na == ref["n_active"] and np.array_equal(to_host(buf.active)[:na], ref["active"])
+        wl = oracle.work_list(ids, E, k, moe.WORK_TILE_ROWS)
+        assert int(to_host(buf.n_work)[0]) == wl.shape[0]
+        assert np.array_equal(to_host(buf.work_list)[: wl.shape[0]], wl)
+        assert int(buf.sync.abs().sum().item()) == 0
+
+
 def _edge_logits(T, E, seed):
     """Logits built to exercise every ranking rule: ties (to the lower id), -0 == +0,
     NaN below -inf, +-inf, and many exact duplicates."""

@@ -6,7 +6,9 @@ renormalised gates, expert intermediate 512, SwiGLU, 4-bit weights with fp16
 scale and bias per group of 128, Zipf(1.1) expert popularity), a batch of
 --tokens decode tokens (default 32).  A step is one pass of the whole layer:
 
-    route_dispatch (router, top-k, slot lookup, grouping) -> expert_gateup -> expert_down -> combine
+    route_dispatch (router, top-k, slot lookup, grouping) -> expert_ffn_fused -> combine
+
+(--ffn split: expert_gateup -> expert_down in place of expert_ffn_fused).
 
 Successive steps cycle through --layers independently generated weight sets
 (like successive layers of a model; 4 x 428 MB by default), so the weights
@@ -15,10 +17,12 @@ HBM.  Inputs are resident in HBM before the timed region starts.
 
 Printed: one JSON line with
   value         tokens/s over the K timed steps (tokens * K / elapsed);
-  roofline      the gate/up kernel (2/3 of the weight bytes): algorithmic
-                weight bytes per launch (experts used * 2 * I * H * (bits/8 + 4/128))
-                over its mean duration, timed with HIP events around each launch
-                on the stream it runs on, against the 8 TB/s HBM peak;
+  roofline      the FFN kernel (the one-launch gate/up + down kernel; with
+                --ffn split or --algo gemv, the gate/up kernel): algorithmic
+                weight bytes per launch (experts used * 3 * I * H * (bits/8 +
+                4/128), or 2 * ... for gate/up alone) over its mean duration,
+                timed with HIP events around each launch on the stream it runs
+                on, against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle (single-threaded C) timed on one full step of
                 weight set 0 on this host.
 With --gpus N > 1 it exits: this bench measures one GPU.
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=4, help="rotating weight sets")
     ap.add_argument("--sweep", default="1,8", help="extra token counts timed after the main run ('none' = none)")
     ap.add_argument("--algo", choices=["auto", "gemv", "mfma"], default="auto")
+    ap.add_argument("--ffn", choices=["fused", "split"], default="fused",
+                    help="expert FFN as one call (expert_ffn_fused) or as expert_gateup + expert_down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed steps of the T=4096 prefill layer on the grouped GEMM (0 = skip)")
@@ -91,9 +97,10 @@ def upload_layer(shape, bits, seed, torch, mi, moe):
 class Runner:
     """Enqueues layer steps over rotating weight sets; optional events around the FFN halves."""
 
-    def __init__(self, torch, mi, moe, shape, layers, T, algo):
+    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False):
         self.torch, self.mi, self.moe = torch, mi, moe
         self.shape, self.layers, self.T, self.algo = shape, layers, T, algo
+        self.fused_ffn = fused_ffn
         sh = shape
         self.d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
         self.buf = moe.LayerBuffers.allocate(self.d, layers[0]["w"].bits, algo)
@@ -114,10 +121,16 @@ class Runner:
                            b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work, sync=b.sync)
         if ev is not None:
             ev[0].record()
-        moe.expert_gateup(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, self.algo)
-        if ev is not None:
-            ev[1].record()
-        moe.expert_down(d, bits, b.work_list, b.n_work, L["w"], b.workspace, b.y_rows, self.algo)
+        if self.fused_ffn:
+            moe.expert_ffn_fused(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, b.y_rows, b.ffn_sync,
+                                 self.algo)
+            if ev is not None:
+                ev[1].record()
+        else:
+            moe.expert_gateup(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, self.algo)
+            if ev is not None:
+                ev[1].record()
+            moe.expert_down(d, bits, b.work_list, b.n_work, L["w"], b.workspace, b.y_rows, self.algo)
         if ev is not None:
             ev[2].record()
         moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
@@ -132,6 +145,8 @@ class Runner:
         return U
 
     def timed(self, steps, warmup, with_events=True):
+        """(total ms, wall s, per-step ms from event 0 to 1, from 1 to 2): with
+        the FFN as one call, 0 -> 1 is that call and 1 -> 2 is empty."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -159,7 +174,7 @@ CSRC = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc")
 # take the LDS-staged decode kernels at these sizes), and the sources they are
 # built from.
 FFN_KERNELS = {
-    "mfma": dict(gateup="ffn_gateup_dec_kernel", down="ffn_down_dec_kernel",
+    "mfma": dict(gateup="ffn_gateup_dec_kernel", down="ffn_down_dec_kernel", fused="ffn_fused_dec_kernel",
                  sources=("ffn_dec.hip", "mfma_ops.h", "common.h")),
     "gemv": dict(gateup="ffn_gateup_gemv_kernel", down="ffn_down_gemv_kernel",
                  sources=("ffn_gemv.hip", "common.h")),
@@ -175,18 +190,20 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
-def traffic_record(algo):
-    """HBM traffic of the gate/up kernel from the committed counter summary, if it
-    was taken on that kernel's current sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "gateup_a3b_T32_traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "ffn_a3b_T32_traffic.json")
+
+
+def traffic_record(algo, key):
+    """HBM bytes per launch of FFN kernel `key` (gateup, down, fused) from the
+    committed counter summary, if it was taken on the current sources (else None)."""
+    if not os.path.exists(TRAFFIC_PATH):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_PATH) as f:
         rec = json.load(f)
     k = FFN_KERNELS[algo]
-    if rec.get("kernel") != k["gateup"] or rec.get("source_sha256_16") != source_hash(k["sources"]):
+    if key not in k or rec.get("source_sha256_16") != source_hash(k["sources"]):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("per_kernel", {}).get(k[key], {}).get("bytes_per_launch")
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -222,7 +239,7 @@ def measure_prefill(torch, mi, moe, steps, warmup):
 
 def traffic_kernels(algo):
     k = FFN_KERNELS[algo]
-    return {"gateup": k["gateup"], "down": k["down"], "copy": "copyBuffer"}
+    return {key: k[key] for key in ("gateup", "down", "fused") if key in k} | {"copy": "copyBuffer"}
 
 
 def _counter_rows(d):
@@ -258,22 +275,23 @@ def summarize_counters(fetch_dir, write_dir, copy_mib, algo="auto"):
     w_copy = res["copy"]["WRITE_SIZE"]["mean_kib"] * 1024
     scale_f, scale_w = copy_bytes / f_copy, copy_bytes / w_copy
     kern = {}
-    for key in ("gateup", "down"):
+    k = FFN_KERNELS[algo]
+    for key in traffic_kernels(algo):
+        if key == "copy" or res[key]["FETCH_SIZE"]["mean_kib"] is None:
+            continue
         f = res[key]["FETCH_SIZE"]["mean_kib"] * 1024 * scale_f
         w = res[key]["WRITE_SIZE"]["mean_kib"] * 1024 * scale_w
-        kern[key] = dict(fetch_bytes=round(f), write_bytes=round(w), bytes_per_launch=round(f + w),
-                         dispatches=res[key]["FETCH_SIZE"]["dispatches"])
-    k = FFN_KERNELS[algo]
-    rec = dict(kernel=k["gateup"], workload="a3b T=32 (bench.py default)",
-               bytes_per_launch=kern["gateup"]["bytes_per_launch"], per_kernel=kern,
+        kern[k[key]] = dict(fetch_bytes=round(f), write_bytes=round(w), bytes_per_launch=round(f + w),
+                            dispatches=res[key]["FETCH_SIZE"]["dispatches"])
+    rec = dict(workload="a3b T=32 (bench.py default: the one-launch FFN timed, then the two-launch FFN)",
+               per_kernel=kern,
                copy_calibration=dict(copy_bytes=copy_bytes, fetch_scale=round(scale_f, 4),
                                      write_scale=round(scale_w, 4)),
                sources=list(k["sources"]), source_sha256_16=source_hash(k["sources"]),
                command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir> -o run --output-format csv "
                        "-- python3 bench.py --steps 20 --warmup 5 --sweep=none --no-cpu-baseline --prefill-steps 0 "
                        f"--copy-calib-mib {copy_mib}")
-    path = os.path.join(ROOT, "profiles", "gateup_a3b_T32_traffic.json")
-    with open(path, "w") as f:
+    with open(TRAFFIC_PATH, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
@@ -327,40 +345,51 @@ def main():
     down_bytes_per_expert = per_expert // 3
     router_bytes = shape.E * shape.H * 4
 
+    fused = args.ffn == "fused" and "fused" in FFN_KERNELS[args.algo]
+
     def measure(T, steps, warmup):
-        r = Runner(torch, mi, moe, shape, layers, T, algo)
+        r = Runner(torch, mi, moe, shape, layers, T, algo, fused_ffn=fused)
         U = r.experts_used()
         # throughput: the K steps back to back, nothing recorded between kernels
         total_ms, wall, _, _ = r.timed(steps, warmup, with_events=False)
         # kernel durations: the same K steps again with HIP events around the
-        # gate/up and down launches on their stream (events between kernels
-        # lengthen the step a little, so this pass does not set the throughput)
-        ev_total_ms, _, gate_ms, down_ms = r.timed(steps, 0)
+        # FFN launches on their stream (events between kernels lengthen the
+        # step a little, so these passes do not set the throughput); the
+        # two-launch FFN is timed too, for its halves
+        ev_total_ms, _, ffn_ms, _ = r.timed(steps, 0)
+        r.fused_ffn = False
+        split_total_ms, _, gate_ms, down_ms = r.timed(steps, 2)
+        r.fused_ffn = fused
         Us = [U[i % len(U)] for i in range(steps)]
         gate_bytes = sum(u * gate_bytes_per_expert for u in Us)
         down_bytes = sum(u * down_bytes_per_expert for u in Us)
-        gate_s = sum(gate_ms) / 1e3
-        down_s = sum(down_ms) / 1e3
+        gate_s, down_s, ffn_s = sum(gate_ms) / 1e3, sum(down_ms) / 1e3, sum(ffn_ms) / 1e3
+        if not fused:
+            ffn_s = gate_s + down_s
         ms_step = total_ms / steps
         return dict(T=T, steps=steps, ms_per_step=ms_step, tokens_per_s=T * steps / (total_ms / 1e3),
                     ms_per_step_with_kernel_events=ev_total_ms / steps,
+                    split_ms_per_step_with_kernel_events=split_total_ms / steps,
                     wall_s=wall, U_mean=float(np.mean(U)), U_per_set=U,
-                    gateup_us=gate_s / steps * 1e6, down_us=down_s / steps * 1e6,
+                    ffn_us=ffn_s / steps * 1e6, gateup_us=gate_s / steps * 1e6, down_us=down_s / steps * 1e6,
                     gateup_GBps=gate_bytes / gate_s / 1e9, down_GBps=down_bytes / down_s / 1e9,
-                    ffn_GBps=(gate_bytes + down_bytes) / (gate_s + down_s) / 1e9,
+                    ffn_GBps=(gate_bytes + down_bytes) / ffn_s / 1e9,
+                    split_ffn_GBps=(gate_bytes + down_bytes) / (gate_s + down_s) / 1e9,
                     layer_GBps=(sum(Us) * per_expert + steps * router_bytes) / (total_ms / 1e3) / 1e9,
-                    gateup_bytes_per_launch=gate_bytes / steps)
+                    gateup_bytes_per_launch=gate_bytes / steps,
+                    ffn_bytes_per_launch=(gate_bytes + down_bytes) / steps)
 
     log(f"[bench] T={args.tokens}: {args.warmup} warmup + {args.steps} timed steps")
     main_run = measure(args.tokens, args.steps, args.warmup)
-    log(f"[bench] {main_run['tokens_per_s']:.0f} tokens/s, gate/up {main_run['gateup_GBps']:.0f} GB/s")
+    log(f"[bench] {main_run['tokens_per_s']:.0f} tokens/s, FFN {main_run['ffn_GBps']:.0f} GB/s "
+        f"(two launches: gate/up {main_run['gateup_GBps']:.0f}, down {main_run['down_GBps']:.0f} GB/s)")
 
     sweep = []
     for tok in [int(t) for t in args.sweep.split(",") if t.strip() and t.strip() != "none"]:
         if tok == args.tokens:
             continue
         m = measure(tok, max(args.steps // 2, 10), max(args.warmup // 2, 2))
-        log(f"[bench] sweep T={tok}: {m['tokens_per_s']:.0f} tokens/s, gate/up {m['gateup_GBps']:.0f} GB/s")
+        log(f"[bench] sweep T={tok}: {m['tokens_per_s']:.0f} tokens/s, FFN {m['ffn_GBps']:.0f} GB/s")
         sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()})
 
     prefill = None
@@ -369,12 +398,20 @@ def main():
         log(f"[bench] prefill: {prefill['tokens_per_s']:.0f} tokens/s, FFN {prefill['ffn_tflops']} TFLOP/s "
             f"({100 * prefill['mfma_util']:.1f}% of bf16 MFMA peak)")
 
-    achieved = main_run["gateup_GBps"]
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(args.algo),
-                    kernel=FFN_KERNELS[args.algo]["gateup"] + " (gate/up matvec + SwiGLU)",
-                    algorithmic_bytes_per_launch=round(main_run["gateup_bytes_per_launch"]),
-                    mean_launch_us=round(main_run["gateup_us"], 3))
+    if fused:
+        achieved = main_run["ffn_GBps"]
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(args.algo, "fused"),
+                        kernel=FFN_KERNELS[args.algo]["fused"] + " (gate/up matvec + SwiGLU + down matvec, one launch)",
+                        algorithmic_bytes_per_launch=round(main_run["ffn_bytes_per_launch"]),
+                        mean_launch_us=round(main_run["ffn_us"], 3))
+    else:
+        achieved = main_run["gateup_GBps"]
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(args.algo, "gateup"),
+                        kernel=FFN_KERNELS[args.algo]["gateup"] + " (gate/up matvec + SwiGLU)",
+                        algorithmic_bytes_per_launch=round(main_run["gateup_bytes_per_launch"]),
+                        mean_launch_us=round(main_run["gateup_us"], 3))
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib * 1024 * 1024
@@ -409,21 +446,24 @@ def main():
                         f"(fp16 scale+bias), bf16 activations, Zipf(1.1) routing, "
                         f"{shape.n_resident}/256 resident, {args.layers} rotating weight sets",
             "H": shape.H, "E": shape.E, "k": shape.k, "I": shape.I, "T": args.tokens, "bits": bits,
-            "group": 128, "weight_sets": args.layers, "algo": args.algo,
+            "group": 128, "weight_sets": args.layers, "algo": args.algo, "ffn": "fused" if fused else "split",
             "parallelism": "none (one GPU)",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
         "weight_stream": {
             "experts_used_mean": main_run["U_mean"],
-            "gateup_GBps": round(main_run["gateup_GBps"], 1),
-            "down_GBps": round(main_run["down_GBps"], 1),
             "ffn_GBps": round(main_run["ffn_GBps"], 1),
             "ffn_frac_of_peak": round(main_run["ffn_GBps"] / HBM_PEAK_GBPS, 4),
+            "ffn_us": round(main_run["ffn_us"], 3),
             "layer_GBps_incl_router": round(main_run["layer_GBps"], 1),
-            "gateup_us": round(main_run["gateup_us"], 3),
-            "down_us": round(main_run["down_us"], 3),
             "ms_per_step_with_kernel_events": round(main_run["ms_per_step_with_kernel_events"], 5),
+            "two_launch_gateup_GBps": round(main_run["gateup_GBps"], 1),
+            "two_launch_down_GBps": round(main_run["down_GBps"], 1),
+            "two_launch_ffn_GBps": round(main_run["split_ffn_GBps"], 1),
+            "two_launch_gateup_us": round(main_run["gateup_us"], 3),
+            "two_launch_down_us": round(main_run["down_us"], 3),
+            "two_launch_ms_per_step_with_kernel_events": round(main_run["split_ms_per_step_with_kernel_events"], 5),
         },
         "sweep": sweep,
         "prefill": prefill,

@@ -285,6 +285,26 @@ int moe_expert_down(const moe_dims* dims, int bits, const int32_t* work_list, co
                     const moe_qweights* weights, int algo, const void* workspace,
                     size_t workspace_bytes, uint16_t* y_rows, void* stream);
 
+/* Step 5 in one launch: the same results as moe_expert_gateup followed by
+ * moe_expert_down, bit for bit, for bits in {2, 4}.  At the decode shapes that
+ * have a one-launch kernel (matrix-core algorithm; tiles that fit the decode
+ * kernels; a work-list capacity of at most MOE_FFN_SYNC_INTS / 32 - 1
+ * entries), the gate/up and down items of the work list run in one launch and
+ * an entry's down items start streaming their weights while other entries are
+ * still in gate/up; they read h once its gate/up items have signalled through
+ * `sync`.  Other shapes, and algo GEMV or GEMM, run the two halves as two
+ * launches.  Arguments as for moe_expert_gateup / moe_expert_down, plus:
+ *   sync  int32 [MOE_FFN_SYNC_INTS] device memory, 256-byte aligned, holding
+ *         zeros before the first call; each call leaves it zero.  Calls that
+ *         share one sync buffer must be ordered (one stream).  The last 32
+ *         ints are a fault flag: nonzero after a call means a down item gave
+ *         up waiting for its h (about 10 ms), and that call's outputs are not
+ *         valid; the caller clears it. */
+#define MOE_FFN_SYNC_INTS 32800
+int moe_expert_ffn_fused(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* work_list,
+                         const int32_t* n_work, const moe_qweights* weights, int algo, void* workspace,
+                         size_t workspace_bytes, uint16_t* y_rows, int32_t* sync, void* stream);
+
 /* Combine + residual (step 6; Flash-MoE page, sec. 3):
  *   acc = residual[t][n];  for j = 0..k-1 in order:
  *       acc = fmaf(topk_w[t][j], y_rows[pair_to_row[t*k+j]][n], acc)

@@ -28,7 +28,8 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_workspace_bytes",
     "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute", "moe_work_list_capacity",
     "moe_route_dispatch",
-    "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_combine",
+    "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_expert_ffn_fused",
+    "moe_combine",
 )
 
 
@@ -87,6 +88,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).argtypes = [Dp, P, P, P, Wp, P, ctypes.c_int, P, sz, P]
     L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P]
     L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, Wp, ctypes.c_int, P, sz, P, P]
+    L.moe_expert_ffn_fused.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P, P, P]
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = ctypes.c_int
@@ -173,6 +175,7 @@ def slot_lookup(d: Dims, topk_ids, slot_of_expert, n_slots: int, pair_slot, miss
 
 WORK_TILE_ROWS, WORK_ENTRY_INTS = 16, 20     # MOE_WORK_TILE_ROWS, MOE_WORK_ENTRY_INTS
 DISPATCH_SYNC_INTS = 576                     # MOE_DISPATCH_SYNC_INTS
+FFN_SYNC_INTS = 32800                        # MOE_FFN_SYNC_INTS (the last 32: the fault flag)
 
 
 def work_list_capacity(d: Dims) -> int:
@@ -241,6 +244,16 @@ def expert_down(d: Dims, bits: int, work_list, n_work, weights: QWeights, worksp
                                  _stream(stream)))
 
 
+def expert_ffn_fused(d: Dims, bits: int, x, work_list, n_work, weights: QWeights, workspace, y_rows, sync,
+                     algo: int = ALGO_AUTO, stream=None):
+    """moe_expert_ffn_fused: gate/up and down in one launch where a kernel exists
+    (else two); `sync` is an int32 device tensor of FFN_SYNC_INTS zeros (left zero)."""
+    w = weights.c_struct()
+    _check(lib().moe_expert_ffn_fused(ctypes.byref(d), int(bits), _ptr(x), _ptr(work_list), _ptr(n_work),
+                                      ctypes.byref(w), int(algo), _ptr(workspace), _nbytes(workspace),
+                                      _ptr(y_rows), _ptr(sync), _stream(stream)))
+
+
 def combine(d: Dims, y_rows, pair_to_row, topk_w, residual, out, stream=None):
     _check(lib().moe_combine(ctypes.byref(d), _ptr(y_rows), _ptr(pair_to_row), _ptr(topk_w),
                              _ptr(residual), _ptr(out), _stream(stream)))
@@ -250,8 +263,8 @@ from .layer import LayerBuffers, layer_forward  # noqa: E402  (orchestration of 
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
-    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS",
+    "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
-    "expert_ffn_q2", "expert_gateup", "expert_down", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
+    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
     "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

@@ -370,6 +370,30 @@ int moe_expert_down(const moe_dims* d, int bits, const int32_t* work_list, const
     return ok();
 }
 
+int moe_expert_ffn_fused(const moe_dims* d, int bits, const uint16_t* x, const int32_t* work_list,
+                         const int32_t* n_work, const moe_qweights* w, int algo, void* ws, size_t ws_bytes,
+                         uint16_t* y, int32_t* sync, void* stream) {
+    const char* fn = "moe_expert_ffn_fused";
+    int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 0, 3);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(y, 16);
+    REQUIRE_PTR(sync, 256);
+    st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
+    if (st) return st;
+    moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), y);
+    const int alg = moe::resolve_algo(*d, bits, algo);
+    const hipStream_t s = as_stream(stream);
+    st = alg == MOE_ALGO_MFMA ? moe::launch_ffn_fused_dec(a, sync, s) : MOE_ERR_UNSUPPORTED;
+    if (st == MOE_ERR_UNSUPPORTED) {
+        st = launch_gateup(alg, a, s);
+        if (!st) st = launch_down(alg, a, s);
+    }
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* pair_to_row,
                 const float* topk_w, const uint16_t* residual, uint16_t* out, void* stream) {
     const char* fn = "moe_combine";

@@ -34,6 +34,16 @@ namespace {
 constexpr size_t kDecLdsLimit = 80 * 1024;
 constexpr int kDma = 1024;          // bytes one wave moves with one direct-to-LDS load
 
+// One-launch FFN (ffn_fused_dec_kernel): work-list entries per chunk of the
+// grid, the per-entry counters in `sync` (one 128-byte line each), the
+// time-out flag after them, and the bound on a down item's wait (polls of
+// about 0.5 us: some 10 ms in all, against waits of a few us).
+constexpr int kFfnChunk = 64;
+constexpr int kFfnStride = 32;
+constexpr int kFfnMaxEntries = MOE_FFN_SYNC_INTS / kFfnStride - 1;
+constexpr int kFfnErr = kFfnMaxEntries * kFfnStride;
+constexpr int kFfnSpinMax = 20000;
+
 struct DecParams {
     const uint16_t* x;
     const int32_t* work;
@@ -60,9 +70,15 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // waits for every outstanding load (the code ring too) before the first LDS
 // access after it; completion is waited for explicitly with wait_vmem.
 // M0 holds the LDS address; one wait state between writing M0 and the load.
+// COH: a device-scope load (sc1), for data that other workgroups of the same
+// launch wrote with device-scope stores.
+template <bool COH = false>
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
     const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)lds_base;
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+    if constexpr (COH)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src), "{m0}"(lds) : "memory");
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
 // Copy `bytes` (a multiple of 16) of contiguous global memory to LDS, waves
@@ -104,16 +120,12 @@ struct DecItem {
     int tokv;
 };
 
-__device__ __forceinline__ DecItem dec_item(const DecParams& p) {
+__device__ __forceinline__ DecItem dec_item_at(const DecParams& p, int entry, int rb) {
     typedef int int4v __attribute__((ext_vector_type(4)));
     DecItem it;
-    // Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD
-    // b % 8): the items of entry e all go to XCD e % 8, so its activation or
-    // h tile is fetched into that XCD's L2 once and hit by the other items.
-    const int b = (int)blockIdx.x, xcd = b & 7, s = b >> 3;
-    it.entry = (s / p.ipe) * 8 + xcd;
-    it.rb = s % p.ipe;
-    const int re = it.entry < p.cap ? it.entry : p.cap - 1;      // the grid rounds entries up to 8
+    it.entry = entry;
+    it.rb = rb;
+    const int re = it.entry < p.cap ? it.entry : p.cap - 1;      // grids round entries up
     const int4v* ent = reinterpret_cast<const int4v*>(p.work + (size_t)re * kWorkInts);
     const int n_work = ld_scalar(p.n_work, 0);
     int4v v[kWorkInts / 4];
@@ -133,6 +145,16 @@ __device__ __forceinline__ DecItem dec_item(const DecParams& p) {
     return it;
 }
 
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD b % 8).
+// Slot r of a range of 8 ipe m workgroups takes entry (r / 8 / ipe) 8 + r % 8
+// and row block (r / 8) % ipe: the items of entry e all run on one XCD, so its
+// activation or h tile is fetched into that XCD's L2 once and hit by the other
+// items.
+__device__ __forceinline__ DecItem dec_item_xcd(const DecParams& p, int entry0, int r) {
+    const int xcd = r & 7, s = r >> 3;
+    return dec_item_at(p, entry0 + (s / p.ipe) * 8 + xcd, s % p.ipe);
+}
+
 // The activation tile in LDS: rows of `rowb` bytes, each group of 128 along K
 // a run of 16 chunks of 16 bytes (8 values in natural order), the chunks
 // XOR-swizzled by the row's low 4 bits so that the 16 rows a quarter-wave
@@ -145,7 +167,7 @@ __device__ __forceinline__ int tile_off(int j, int g, int c, int rowb) {
 // piece i of the tile (1 KB) is loaded by one wave, lane l filling slot
 // 64 i + l.  src(j, g, c) is the global address of chunk c of group g of row
 // j; slots of rows past n reload a chunk of row 0 into unused room.
-template <typename Src>
+template <bool COH = false, typename Src>
 __device__ __forceinline__ void dma_tile(uint8_t* tile, int n, int rowb, int wid, int lane, Src src) {
     const int chunks_row = rowb / 16;
     const int pieces = (n * rowb + kDma - 1) / kDma;
@@ -154,7 +176,7 @@ __device__ __forceinline__ void dma_tile(uint8_t* tile, int n, int rowb, int wid
         int j = slot / chunks_row;
         const int r = slot - j * chunks_row, g = r >> 4, cs = r & 15;
         j = j < n ? j : 0;
-        dma16(src(j, g, cs ^ (j & 15)), tile + i * kDma);
+        dma16<COH>(src(j, g, cs ^ (j & 15)), tile + i * kDma);
     }
 }
 
@@ -181,14 +203,15 @@ constexpr uint32_t kOnesBf16 = 0x3F803F80u;   // two bf16 ones
 // code loads.  LDS: the x tile [rows_cap][H] bf16, then the raw fp16 scales
 // and biases of the block's gate and up rows, [RI][NG] each; after the loop
 // the first 8 KB holds the partial sums over K.
-template <int BITS, int RW, int D>
-__global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
+// COH: h leaves through device-scope stores (read by down items of the same
+// launch) and without the 16-row partial sums (only the non-staged down
+// kernel reads those).
+template <int BITS, int RW, int D, bool COH>
+__device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& it, uint8_t* smem) {
     constexpr int KS = 4 / RW;
     constexpr int LB = 128 * BITS / 8 / 4;     // code bytes per lane per group
     constexpr int LW = LB / 4;
     constexpr int RI = 16 * RW;                // gate (and up) rows per item
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const DecItem it = dec_item(p);
     if (it.n == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -354,12 +377,24 @@ __global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
             uint32_t hi, mid, lo;
             split3_bf16(hv[i], hi, mid, lo);
             uint16_t* dst = p.hp + r * I + ibase + m;
-            dst[0] = (uint16_t)hi;
-            dst[plane] = (uint16_t)mid;
-            dst[2 * plane] = (uint16_t)lo;
-            if (m == 0) p.hpart[r * (I / 16) + ibase / 16] = part[i];
+            if constexpr (COH) {
+                __hip_atomic_store(dst, (uint16_t)hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + plane, (uint16_t)mid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 2 * plane, (uint16_t)lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                dst[0] = (uint16_t)hi;
+                dst[plane] = (uint16_t)mid;
+                dst[2 * plane] = (uint16_t)lo;
+                if (m == 0) p.hpart[r * (I / 16) + ibase / 16] = part[i];
+            }
         }
     }
+}
+
+template <int BITS, int RW, int D>
+__global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    gateup_item<BITS, RW, D, false>(p, dec_item_xcd(p, 0, (int)blockIdx.x), smem);
 }
 
 // ------------------------------------------------------------------- down
@@ -368,13 +403,16 @@ __global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
 // LDS: the three h planes [3][rows_cap][I] bf16 (already in pair order), then
 // the raw fp16 scales and biases [64 RT][NG].  The group sums of h come from
 // all-ones MFMAs on the three planes.
-template <int BITS, int RT, int D>
-__global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
+// WAIT (one-launch FFN): h comes from gate/up items of the same launch.  The
+// scales and the first code-ring slots are requested first; then thread 0
+// waits until *ready reaches `need` (bounded; on time-out *err is set), and
+// only then are the h planes loaded (device-scope loads).
+template <int BITS, int RT, int D, bool WAIT>
+__device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it, uint8_t* smem,
+                                          int32_t* ready = nullptr, int need = 0, int32_t* err = nullptr) {
     constexpr int LB = 128 * BITS / 8 / 4;
     constexpr int LW = LB / 4;
     constexpr int RI = 64 * RT;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const DecItem it = dec_item(p);
     if (it.n == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -386,14 +424,17 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
     uint8_t* scl = smem + 3 * (size_t)plane_b;                          // s, then b
 
     // ---- h planes and scales straight to LDS, ahead of the code ring
-    {
+    auto stage_h = [&]() {
         const size_t plane = (size_t)p.P * I;
 #pragma unroll
         for (int pl = 0; pl < 3; ++pl) {
             const uint16_t* hrows = p.hp + pl * plane + (size_t)it.row0 * I;
-            dma_tile(hs + (size_t)pl * plane_b, it.n, rowb, wid, lane,
-                     [&](int j, int g, int c) { return hrows + (size_t)j * I + g * kGroup + 8 * c; });
+            dma_tile<WAIT>(hs + (size_t)pl * plane_b, it.n, rowb, wid, lane,
+                           [&](int j, int g, int c) { return hrows + (size_t)j * I + g * kGroup + 8 * c; });
         }
+    };
+    if constexpr (!WAIT) stage_h();
+    {
         const size_t first = ((size_t)it.e * H + (size_t)it.rb * RI) * NG;
         dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
         dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
@@ -421,7 +462,21 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d, d);
-    wait_vmem<RT * D>();
+    if constexpr (WAIT) {
+        if (tid == 0) {
+            int v = __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int spin = 0; v < need && spin < kFfnSpinMax; ++spin) {
+                __builtin_amdgcn_s_sleep(8);
+                v = __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (v < need) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();                       // (also waits for the ring slots above)
+        stage_h();
+        wait_vmem<0>();
+    } else {
+        wait_vmem<RT * D>();
+    }
     lds_barrier();
 
     const int mrow = m < it.n ? m : 0;
@@ -491,6 +546,63 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
             uint16_t* yrow = p.y + (size_t)(it.row0 + t) * H + (size_t)it.rb * RI + rloc;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) yrow[16 * rt] = (uint16_t)f32_to_bf16_bits(acc[rt][i]);
+        }
+    }
+}
+
+template <int BITS, int RT, int D>
+__global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    down_item<BITS, RT, D, false>(p, dec_item_xcd(p, 0, (int)blockIdx.x), smem);
+}
+
+// ------------------------------------------------------------ one-launch FFN
+// Gate/up and down in one launch.  The grid is cut into chunks of kFfnChunk
+// work-list entries; a chunk is its gate/up items, then its down items, each
+// numbered as in the two-launch kernels (an entry's items on one XCD).  A down
+// item requests its scales and first code slots, then waits until the gate/up
+// items of its entry have published h (a per-entry counter), then loads h.  So
+// the down items start streaming weights while the last gate/up items finish,
+// and the two halves share one ramp-up and one tail.
+// Why the wait ends: workgroups are dispatched in index order, and every
+// gate/up item a down item waits for has a lower index, so it is already
+// running (on the same XCD, since an entry's items share one), and gate/up
+// items wait for nothing.  The wait is bounded anyway: on time-out the item
+// goes on (its results are then wrong) and the flag sync[kFfnErr] is set.
+// h crosses workgroups as device-scope stores and loads (no cache flush).
+// Counters of entry e at sync[kFfnStride e]: [0] gate/up items done, [1] down
+// items done; the last down item puts both back to zero.
+struct FusedParams {
+    DecParams p;                                                 // gate/up: weights qa..bb, ipe
+    const uint8_t* qd; const uint16_t* sd; const uint16_t* bd;   // down weights
+    int ipe_d;                                                   // down items per entry
+};
+
+template <int BITS, int RW, int DG, int RT, int DD>
+__global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, int32_t* sync) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int ng = kFfnChunk * f.p.ipe, span = ng + kFfnChunk * f.ipe_d;
+    const int b = (int)blockIdx.x, chunk = b / span, r = b - chunk * span;
+    const int entry0 = chunk * kFfnChunk;
+    if (r < ng) {
+        const DecItem it = dec_item_xcd(f.p, entry0, r);
+        gateup_item<BITS, RW, DG, true>(f.p, it, smem);
+        if (it.n == 0) return;
+        __builtin_amdgcn_s_waitcnt(0);          // this wave's h stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(&sync[kFfnStride * it.entry], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        DecParams pd = f.p;
+        pd.qa = f.qd; pd.sa = f.sd; pd.ba = f.bd; pd.ipe = f.ipe_d;
+        const DecItem it = dec_item_xcd(pd, entry0, r - ng);
+        if (it.n == 0) return;
+        int32_t* ctr = &sync[kFfnStride * it.entry];
+        down_item<BITS, RT, DD, true>(pd, it, smem, ctr, f.p.ipe, &sync[kFfnErr]);
+        if (threadIdx.x == 0 &&
+            __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == f.ipe_d - 1) {
+            __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -628,6 +740,45 @@ int launch_down_dec(const FfnArgs& a, hipStream_t s) {
         else dn_depth<2, 1>(D, d, lds, s, p);
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ------------------------------------------------------------ one-launch FFN
+
+template <int BITS, int RW, int DG, int RT, int DD>
+static int fused_go(size_t lds, hipStream_t s, const FusedParams& f, int32_t* sync) {
+    const int chunks = (f.p.cap + kFfnChunk - 1) / kFfnChunk;
+    const dim3 grid((unsigned)(chunks * kFfnChunk * (f.p.ipe + f.ipe_d)));
+    hipLaunchKernelGGL((ffn_fused_dec_kernel<BITS, RW, DG, RT, DD>), grid, dim3(256), lds, s, f, sync);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// The decode configurations with a one-launch kernel; others take two launches.
+template <int BITS>
+static int fused_pick(int rw, int dg, int rt, int dd, size_t lds, hipStream_t s, const FusedParams& f,
+                      int32_t* sync) {
+    if (rw == 4 && dg == 4 && rt == 4 && dd == 2) return fused_go<BITS, 4, 4, 4, 2>(lds, s, f, sync);
+    if (rw == 4 && dg == 4 && rt == 2 && dd == 2) return fused_go<BITS, 4, 4, 2, 2>(lds, s, f, sync);
+    if (rw == 1 && dg == 4 && rt == 1 && dd == 2) return fused_go<BITS, 1, 4, 1, 2>(lds, s, f, sync);
+    return MOE_ERR_UNSUPPORTED;
+}
+
+int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s) {
+    const moe_dims& d = a.d;
+    if (d.T * d.k == 0) return MOE_OK;
+    if (!dec_gateup_fits(d) || !dec_down_fits(d) || work_capacity(d) > kFfnMaxEntries) return MOE_ERR_UNSUPPORTED;
+    FusedParams f{};
+    f.p = dec_params(a);
+    f.p.qa = a.w.q[0]; f.p.sa = a.w.scale[0]; f.p.ba = a.w.bias[0];
+    f.p.qb = a.w.q[1]; f.p.sb = a.w.scale[1]; f.p.bb = a.w.bias[1];
+    f.qd = a.w.q[2]; f.sd = a.w.scale[2]; f.bd = a.w.bias[2];
+    const int rw = dec_gateup_rw(d), rt = dec_down_rt(d);
+    f.p.ipe = d.I / (16 * rw);
+    f.ipe_d = d.H / (64 * rt);
+    const int dg = dec_depth((d.H / kGroup) / (4 / rw), 4), dd = dec_depth(d.I / kGroup, 2);
+    const size_t lg = dec_gateup_lds(d, rw), ld = dec_down_lds(d, rt);
+    const size_t lds = lg > ld ? lg : ld;
+    return a.bits == 4 ? fused_pick<4>(rw, dg, rt, dd, lds, s, f, sync)
+                       : fused_pick<2>(rw, dg, rt, dd, lds, s, f, sync);
 }
 
 }  // namespace moe

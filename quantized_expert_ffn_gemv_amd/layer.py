@@ -4,9 +4,10 @@
 lookup results, permutation, workspace, expert outputs) so that a step is three
 C calls on one stream with no allocation and no host synchronisation:
 
-    route_dispatch (route_topk + slot_lookup + permute) -> expert_ffn_q{4,2} -> combine
+    route_dispatch (route_topk + slot_lookup + permute) -> expert_ffn_fused -> combine
 
-``fused=False`` makes the same step from the separate routing calls.
+``fused=False`` makes the same step from the separate routing calls and the
+two-launch FFN (expert_ffn_q{4,2}).
 
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
@@ -17,8 +18,9 @@ from typing import Optional
 
 import torch
 
-from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine, expert_ffn_q2, expert_ffn_q4,
-               permute, route_dispatch, route_topk, slot_lookup, work_list_capacity, workspace_bytes)
+from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, FFN_SYNC_INTS, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine,
+               expert_ffn_fused, expert_ffn_q2, expert_ffn_q4, permute, route_dispatch, route_topk, slot_lookup,
+               work_list_capacity, workspace_bytes)
 
 
 @dataclass
@@ -42,6 +44,7 @@ class LayerBuffers:
     workspace: torch.Tensor       # uint8, 256-byte aligned by the allocator
     y_rows: torch.Tensor          # bf16 bits as int16 [T*k, H]
     sync: torch.Tensor            # int32 [DISPATCH_SYNC_INTS], zeros (route_dispatch's counters)
+    ffn_sync: torch.Tensor        # int32 [FFN_SYNC_INTS], zeros (expert_ffn_fused's counters)
 
     @staticmethod
     def allocate(d: Dims, bits: int = 4, algo: int = ALGO_AUTO, device="cuda") -> "LayerBuffers":
@@ -68,6 +71,7 @@ class LayerBuffers:
             workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
             y_rows=torch.empty((max(T * k, 1), H), dtype=torch.int16, device=device),
             sync=torch.zeros((DISPATCH_SYNC_INTS,), **i32),
+            ffn_sync=torch.zeros((FFN_SYNC_INTS,), **i32),
         )
 
 
@@ -89,6 +93,10 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
                     host_doorbell, last_use, step, stream)
         permute(d, buf.topk_ids, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active,
                 buf.n_active, buf.work_list, buf.n_work, stream)
-    ffn = expert_ffn_q4 if weights.bits == 4 else expert_ffn_q2
-    ffn(d, x, buf.work_list, buf.n_work, weights, buf.y_rows, algo, buf.workspace, None, stream)
+    if fused:
+        expert_ffn_fused(d, weights.bits, x, buf.work_list, buf.n_work, weights, buf.workspace, buf.y_rows,
+                         buf.ffn_sync, algo, stream)
+    else:
+        ffn = expert_ffn_q4 if weights.bits == 4 else expert_ffn_q2
+        ffn(d, x, buf.work_list, buf.n_work, weights, buf.y_rows, algo, buf.workspace, None, stream)
     combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)

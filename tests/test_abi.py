@@ -119,6 +119,25 @@ def test_ffn_validation_paths():
     assert _ffn(d, ws=FAKE + 16) == moe.ERR_INVALID_ARG
 
 
+def test_fused_ffn_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    w = _qw()
+    call = lambda x=FAKE, y=FAKE, sync=FAKE, ws=FAKE, bits=4: L.moe_expert_ffn_fused(
+        ctypes.byref(d), bits, x, FAKE, FAKE, ctypes.byref(w), moe.ALGO_AUTO, ws, 1 << 30, y, sync, None)
+    assert call(sync=None) == moe.ERR_INVALID_ARG
+    assert "sync is NULL" in moe.last_error()
+    assert call(sync=FAKE + 128) == moe.ERR_INVALID_ARG          # counters need 256-byte alignment
+    assert "sync" in moe.last_error()
+    assert call(x=None) == moe.ERR_INVALID_ARG
+    assert call(y=MISALIGNED) == moe.ERR_INVALID_ARG
+    assert call(ws=FAKE + 16) == moe.ERR_INVALID_ARG
+    assert call(bits=3) == moe.ERR_UNSUPPORTED
+    z = moe.dims(0, 256, 512, 8, 2)
+    assert L.moe_expert_ffn_fused(ctypes.byref(z), 4, None, None, None, ctypes.byref(w), 0, None, 0, None, None,
+                                  None) == moe.OK
+
+
 def test_route_and_combine_validation():
     L = moe.lib()
     d = moe.dims(4, 256, 512, 8, 2)

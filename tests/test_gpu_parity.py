@@ -399,6 +399,42 @@ def test_dispatch_crafted_ids(E, H, T, k, pool):
         assert np.array_equal(to_host(buf.work_list)[: wl.shape[0]], wl)
         assert int(buf.sync.abs().sum().item()) == 0
 
+FUSED_FFN_CASES = [("tiny", 4, 4, None), ("a3b", 4, 1, None), ("a3b", 4, 32, None), ("a3b", 2, 8, None),
+                   ("a3b", 4, 64, None), ("a3b", 2, 32, None),
+                   ("e512", 4, 1, None), ("e512", 2, 4, None), ("e64", 4, 8, None),
+                   ("ragged_a", 4, 7, RAGGED[0]), ("ragged_b", 2, 3, RAGGED[1])]
+
+
+@pytest.mark.parametrize("name,bits,T,shape", FUSED_FFN_CASES, ids=[f"{c[0]}_q{c[1]}_T{c[2]}" for c in FUSED_FFN_CASES])
+def test_ffn_one_launch_matches_two_launches(name, bits, T, shape):
+    """expert_ffn_fused (gate/up and down in one launch where a kernel exists,
+    two launches elsewhere) gives the results of expert_gateup + expert_down
+    bit for bit and leaves its counters zero, on two different batches in a
+    row through the same buffers (the second relies on the reset)."""
+    L = layer(name, bits, shape)
+    sh = L.shape
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+    one = moe.LayerBuffers.allocate(d, bits)
+    two = moe.LayerBuffers.allocate(d, bits)
+    P = T * sh.k
+    for seed in (21, 22):
+        xb, _ = mi.make_activations(sh.H, T, seed)
+        x_d = to_dev(xb)
+        say(f"[run] fused FFN {name} q{bits} T={T} seed={seed}")
+        moe.route_dispatch(d, x_d, L.Wr_d, L.bias_d, True, one.logits, one.topk_ids, one.topk_w, L.table_d, sh.E,
+                           one.pair_slot, one.miss, one.n_miss, one.counts, one.offsets, one.sorted_pairs,
+                           one.pair_to_row, one.active, one.n_active, one.work_list, one.n_work, sync=one.sync)
+        one.y_rows.fill_(-1)
+        two.y_rows.fill_(-2)
+        moe.expert_ffn_fused(d, bits, x_d, one.work_list, one.n_work, L.weights_d, one.workspace, one.y_rows,
+                             one.ffn_sync)
+        moe.expert_gateup(d, bits, x_d, one.work_list, one.n_work, L.weights_d, two.workspace)
+        moe.expert_down(d, bits, one.work_list, one.n_work, L.weights_d, two.workspace, two.y_rows)
+        torch.cuda.synchronize()
+        assert int(one.ffn_sync.abs().sum().item()) == 0        # counters back to zero, no wait timed out
+        a, b = to_host(one.y_rows, np.uint16)[:P], to_host(two.y_rows, np.uint16)[:P]
+        assert np.array_equal(a, b), f"{int((a != b).any(axis=1).sum())} of {P} rows differ"
+
 
 def _edge_logits(T, E, seed):
     """Logits built to exercise every ranking rule: ties (to the lower id), -0 == +0,

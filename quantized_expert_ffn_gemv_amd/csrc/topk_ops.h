@@ -5,11 +5,12 @@
 // Ranking: larger logit first, equal logits (-0 == +0) to the lower expert id,
 // NaN below every number (-inf included).  Each logit becomes a 32-bit key
 // whose unsigned order is the logit order (numbers in [0x007FFFFF,
-// 0xFF800000], NaN = 1, 0 = taken or absent).  k rounds each take the wave-wide
-// maximum key (DPP row shifts and row broadcasts, no LDS traffic), resolve the
-// owner (one ballot; on a tie, the lowest id wins through a second DPP
-// reduction) and clear that candidate.  The picked logit comes back from its
-// key, so no lane-to-lane copy is needed.
+// 0xFF800000], NaN = 1, 0 = taken or absent).  Each lane sorts its own
+// candidates; then k rounds each take the wave-wide maximum of the lanes'
+// heads (DPP row shifts and row broadcasts, no LDS traffic), resolve the owner
+// (one ballot; on a tie, the lowest id wins through a second DPP reduction) and
+// drop that lane's head.  The picked logit comes back from its key, so no
+// lane-to-lane copy is needed.
 #pragma once
 
 #include "common.h"
@@ -88,35 +89,79 @@ __device__ __forceinline__ void topk_load(const float* __restrict__ L, int E, fl
 // Picks k (1 <= k <= min(E, 64)) of the token whose logits topk_load read and
 // returns, in lane j < k, the j-th pick and its gate.
 // renorm = 1: gates are a softmax over the k picked; 0: over all E.
+// With at most 4 candidates per lane (E <= 256), each lane first sorts its
+// candidates (key descending, then id ascending: a total order), so that a
+// round only reduces each lane's head: the wave maximum of the heads is the
+// next pick's key, the lowest id among the lanes whose head has that key is the
+// pick, and that lane drops its head.
 template <int PER>
 __device__ __forceinline__ void topk_select(const float (&v)[PER], int E, int k, int renorm, int& my_id,
                                             float& my_gate) {
     const int lane = threadIdx.x & 63;
-    uint32_t key[PER];
+    uint32_t key[PER], kid[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) key[i] = (lane + 64 * i < E) ? order_key(v[i]) : 0u;
+    for (int i = 0; i < PER; ++i) {
+        key[i] = (lane + 64 * i < E) ? order_key(v[i]) : 0u;
+        kid[i] = (uint32_t)(lane + 64 * i);
+    }
     my_id = -1;
     uint32_t my_key = 0u;
-    for (int j = 0; j < k; ++j) {
-        uint32_t best = key[0];
+    if constexpr (PER > 4) {
+        // many candidates per lane: sorting them costs more than it saves, so
+        // each round takes the lane's best by a scan and clears the pick
+        for (int j = 0; j < k; ++j) {
+            uint32_t best = key[0];
 #pragma unroll
-        for (int i = 1; i < PER; ++i) best = max(best, key[i]);
-        const uint32_t M = wave_max_u32(best);
-        // this lane's lowest id holding M (slots ascend in id), or 0xFFFFFFFF
-        uint32_t mine = 0xFFFFFFFFu;
+            for (int i = 1; i < PER; ++i) best = max(best, key[i]);
+            const uint32_t M = wave_max_u32(best);
+            // this lane's lowest id holding M (slots ascend in id), or 0xFFFFFFFF
+            uint32_t mine = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = PER - 1; i >= 0; --i) mine = (key[i] == M) ? (uint32_t)(lane + 64 * i) : mine;
-        const uint64_t holders = __ballot(mine != 0xFFFFFFFFu);
-        uint32_t id;
-        if (__popcll(holders) == 1) id = __builtin_amdgcn_readlane(mine, __builtin_ctzll(holders));
-        else id = wave_min_u32(mine);                      // equal logits: the lowest id
-        const int owner = (int)(id & 63u), slot = (int)(id >> 6);
+            for (int i = PER - 1; i >= 0; --i) mine = (key[i] == M) ? kid[i] : mine;
+            const uint64_t holders = __ballot(mine != 0xFFFFFFFFu);
+            uint32_t id;
+            if (__popcll(holders) == 1) id = __builtin_amdgcn_readlane(mine, __builtin_ctzll(holders));
+            else id = wave_min_u32(mine);
+            const int owner = (int)(id & 63u), slot = (int)(id >> 6);
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (i == slot && lane == owner) key[i] = 0u;
-        if (lane == j) {
-            my_id = (int)id;
-            my_key = M;
+            for (int i = 0; i < PER; ++i)
+                if (i == slot && lane == owner) key[i] = 0u;
+            if (lane == j) {
+                my_id = (int)id;
+                my_key = M;
+            }
+        }
+    } else {
+        // sorted by compare-exchange of neighbours (PER - 1 passes)
+#pragma unroll
+        for (int pass = 0; pass < PER - 1; ++pass)
+#pragma unroll
+            for (int i = 0; i + 1 < PER - pass; ++i) {
+                const bool sw = key[i + 1] > key[i] || (key[i + 1] == key[i] && kid[i + 1] < kid[i]);
+                const uint32_t ka = key[i], kb = key[i + 1], ia = kid[i], ib = kid[i + 1];
+                key[i] = sw ? kb : ka;
+                key[i + 1] = sw ? ka : kb;
+                kid[i] = sw ? ib : ia;
+                kid[i + 1] = sw ? ia : ib;
+            }
+        for (int j = 0; j < k; ++j) {
+            const uint32_t M = wave_max_u32(key[0]);
+            const uint64_t holders = __ballot(key[0] == M);
+            uint32_t id;
+            if (__popcll(holders) == 1) id = __builtin_amdgcn_readlane(kid[0], __builtin_ctzll(holders));
+            else id = wave_min_u32(key[0] == M ? kid[0] : 0xFFFFFFFFu);   // equal logits: the lowest id
+            if (lane == (int)(id & 63u)) {
+#pragma unroll
+                for (int i = 0; i + 1 < PER; ++i) {
+                    key[i] = key[i + 1];
+                    kid[i] = kid[i + 1];
+                }
+                key[PER - 1] = 0u;
+            }
+            if (lane == j) {
+                my_id = (int)id;
+                my_key = M;
+            }
         }
     }
     const float top = key_value(__builtin_amdgcn_readfirstlane(my_key));

@@ -13,7 +13,9 @@ scale and bias per group of 128, Zipf(1.1) expert popularity), a batch of
 Successive steps cycle through --layers independently generated weight sets
 (like successive layers of a model; 4 x 428 MB by default), so the weights
 cannot stay in the 256 MB last-level cache and every step streams them from
-HBM.  Inputs are resident in HBM before the timed region starts.
+HBM.  Inputs are resident in HBM before the timed region starts.  The timed
+steps are eager library calls (--launch graph replays one captured HIP graph
+per weight set instead; every kernel of the step runs at each replay).
 
 Printed: one JSON line with
   value         tokens/s over the K timed steps (tokens * K / elapsed);
@@ -62,6 +64,9 @@ def parse():
     ap.add_argument("--algo", choices=["auto", "gemv", "mfma"], default="auto")
     ap.add_argument("--ffn", choices=["fused", "split"], default="fused",
                     help="expert FFN as one call (expert_ffn_fused) or as expert_gateup + expert_down")
+    ap.add_argument("--launch", choices=["eager", "graph"], default="eager",
+                    help="timed steps as eager library calls, or as replays of one captured HIP graph per weight "
+                         "set (each replays every kernel of the step; measured slower here)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed steps of the T=4096 prefill layer on the grouped GEMM (0 = skip)")
@@ -143,6 +148,36 @@ class Runner:
             self.torch.cuda.synchronize()
             U.append(int(self.buf.n_active.item()))
         return U
+
+    def capture(self):
+        """One HIP graph per weight set, each holding a whole layer step (its
+        kernels replay on the same buffers; nothing is allocated or copied)."""
+        torch = self.torch
+        self.graphs = []
+        for li in range(len(self.layers)):
+            self.step(li)                                     # eager first: caches launch sizes
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(li)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def timed_graphs(self, steps, warmup):
+        """(total ms, wall s) of `steps` graph replays, weight sets in turn."""
+        torch = self.torch
+        for i in range(warmup):
+            self.graphs[i % len(self.graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(steps):
+            self.graphs[i % len(self.graphs)].replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), time.perf_counter() - wall0
 
     def timed(self, steps, warmup, with_events=True):
         """(total ms, wall s, per-step ms from event 0 to 1, from 1 to 2): with
@@ -351,7 +386,13 @@ def main():
         r = Runner(torch, mi, moe, shape, layers, T, algo, fused_ffn=fused)
         U = r.experts_used()
         # throughput: the K steps back to back, nothing recorded between kernels
-        total_ms, wall, _, _ = r.timed(steps, warmup, with_events=False)
+        # (eager calls; with --launch graph, replays of captured graphs)
+        eager_ms, eager_wall, _, _ = r.timed(steps, warmup, with_events=False)
+        if args.launch == "graph":
+            r.capture()
+            total_ms, wall = r.timed_graphs(steps, warmup)
+        else:
+            total_ms, wall = eager_ms, eager_wall
         # kernel durations: the same K steps again with HIP events around the
         # FFN launches on their stream (events between kernels lengthen the
         # step a little, so these passes do not set the throughput); the
@@ -368,6 +409,7 @@ def main():
             ffn_s = gate_s + down_s
         ms_step = total_ms / steps
         return dict(T=T, steps=steps, ms_per_step=ms_step, tokens_per_s=T * steps / (total_ms / 1e3),
+                    eager_ms_per_step=eager_ms / steps,
                     ms_per_step_with_kernel_events=ev_total_ms / steps,
                     split_ms_per_step_with_kernel_events=split_total_ms / steps,
                     wall_s=wall, U_mean=float(np.mean(U)), U_per_set=U,
@@ -447,6 +489,7 @@ def main():
                         f"{shape.n_resident}/256 resident, {args.layers} rotating weight sets",
             "H": shape.H, "E": shape.E, "k": shape.k, "I": shape.I, "T": args.tokens, "bits": bits,
             "group": 128, "weight_sets": args.layers, "algo": args.algo, "ffn": "fused" if fused else "split",
+            "launch": "one HIP graph per layer step, replayed" if args.launch == "graph" else "eager calls",
             "parallelism": "none (one GPU)",
         },
         "roofline": roofline,
@@ -458,6 +501,7 @@ def main():
             "ffn_us": round(main_run["ffn_us"], 3),
             "layer_GBps_incl_router": round(main_run["layer_GBps"], 1),
             "ms_per_step_with_kernel_events": round(main_run["ms_per_step_with_kernel_events"], 5),
+            "eager_ms_per_step": round(main_run["eager_ms_per_step"], 5),
             "two_launch_gateup_GBps": round(main_run["gateup_GBps"], 1),
             "two_launch_down_GBps": round(main_run["down_GBps"], 1),
             "two_launch_ffn_GBps": round(main_run["split_ffn_GBps"], 1),

@@ -85,13 +85,13 @@ def upload_layer(shape, bits, seed, torch, mi, moe):
     q, s, b = [], [], []
     for m in mi.MATRICES:
         N, K = mi.matrix_dims(shape, m)
-        q.append(torch.empty((shape.E, N, K * bits // 8), dtype=torch.uint8, device="cuda"))
+        q.append(torch.empty((shape.E, K // 128, N, 16 * bits), dtype=torch.uint8, device="cuda"))
         s.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device="cuda"))
         b.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device="cuda"))
     for e, mats in mi.iter_expert_weights(shape, bits, seed):
         for i, m in enumerate(mi.MATRICES):
             qq, ss, bb = mats[m]
-            q[i][e].copy_(torch.from_numpy(qq))
+            q[i][e].copy_(torch.from_numpy(moe.group_major(qq, bits)))
             s[i][e].copy_(torch.from_numpy(ss.view("int16")))
             b[i][e].copy_(torch.from_numpy(bb.view("int16")))
     dev = lambda a: torch.from_numpy(a).cuda()

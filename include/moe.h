@@ -120,9 +120,16 @@ typedef struct moe_dims {
 /* Quantised expert weights, expert-major so that every expert's matrices sit
  * in one buffer per matrix ("Strata" sec. 3.4).  Index m: 0 = gate [I][H],
  * 1 = up [I][H], 2 = down [H][I], written [N][K] below.
- *   q[m]      uint8 [E][N][K*bits/8].  4-bit: byte j of a row holds k = 2j in
- *             its low nibble and k = 2j+1 in its high nibble.  2-bit: bits
- *             2i..2i+1 of byte j hold k = 4j + i.
+ *   q[m]      uint8 [E][K/128][N][16*bits], group-major: for each group of
+ *             128 along K, the codes of that group of all N rows follow one
+ *             another (row n's piece of group g at ((e K/128 + g) N + n)
+ *             16 bits), so a tile of rows reads one contiguous run per group.
+ *             Within a row's piece of a group, 4-bit: byte j holds k = 2j in
+ *             its low nibble and k = 2j+1 in its high nibble; 2-bit: bits
+ *             2i..2i+1 of byte j hold k = 4j + i (k counted from the group's
+ *             start).  A row-major [N][K*bits/8] array becomes this layout by
+ *             viewing it as [N][K/128][16*bits] and swapping the first two
+ *             axes (group_major() in the Python binding).
  *   scale[m]  fp16 bit patterns [E][N][K/128]
  *   bias[m]   fp16 bit patterns [E][N][K/128]
  * The struct itself is a host object holding device pointers; it is read

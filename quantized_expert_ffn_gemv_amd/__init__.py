@@ -132,11 +132,23 @@ def dims(T: int, H: int, I: int, E: int, k: int, group_size: int = 128) -> Dims:
     return Dims(T, H, I, E, k, group_size)
 
 
+def group_major(q, bits: int):
+    """Codes laid out [..., N, K*bits/8] (each row along K) -> the library's
+    layout [..., K/128, N, 16*bits] (for each group of 128 along K, all rows'
+    pieces of it in a row).  A view change and a copy; numpy in, numpy out."""
+    import numpy as np
+    gb = 16 * bits
+    *lead, n, kb = q.shape
+    if kb % gb:
+        raise ValueError(f"rows of {kb} bytes are not whole groups of {gb}")
+    return np.ascontiguousarray(np.asarray(q).reshape(*lead, n, kb // gb, gb).swapaxes(-3, -2))
+
+
 @dataclass
 class QWeights:
     """Device tensors of the quantised expert weights (layout in include/moe.h)."""
     bits: int
-    q: Sequence          # [gate, up, down] uint8 tensors [E, N, K*bits/8]
+    q: Sequence          # [gate, up, down] uint8 tensors [E, K/128, N, 16*bits] (group-major)
     scale: Sequence      # fp16 bit patterns (int16/uint16 tensors) [E, N, K/128]
     bias: Sequence
 
@@ -266,5 +278,5 @@ __all__ = [
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
     "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "combine", "LayerBuffers", "layer_forward", "EXPORTS",
-    "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
+    "group_major", "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

@@ -239,13 +239,14 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     // ---- code ring: rows of this lane (pair order), groups [gb, gb + ng)
     const int gb = (wk * NG) / KS, ng = ((wk + 1) * NG) / KS - gb;
     const int rloc = 16 * wr + pair_order_row<BITS>(m);
-    const size_t grow = (size_t)it.e * I + (size_t)it.rb * RI + rloc;
-    const size_t rowbytes = (size_t)H * BITS / 8;
-    const uint8_t* cg = p.qa + grow * rowbytes + q * LB;
-    const uint8_t* cu = p.qb + grow * rowbytes + q * LB;
+    // codes are group-major: row r of expert e, group g at ((e NG + g) I + r) 4 LB
+    const size_t gstride = (size_t)I * (4 * LB);
+    const size_t cbase = (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
+    const uint8_t* cg = p.qa + cbase;
+    const uint8_t* cu = p.qb + cbase;
     uint32_t rg[D][LW], ru[D][LW];
     auto issue = [&](int slot, int gl) {
-        const size_t off = (size_t)(gb + (gl < ng ? gl : ng - 1)) * (4 * LB);
+        const size_t off = (size_t)(gb + (gl < ng ? gl : ng - 1)) * gstride;
         if constexpr (BITS == 4) {
             const uint4 A = *reinterpret_cast<const uint4*>(cg + off);
             const uint4 B = *reinterpret_cast<const uint4*>(cu + off);
@@ -442,15 +443,15 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
 
     // ---- code ring: RT rows of this lane, all groups
     const int rloc = 16 * RT * wid + m;               // + 16 rt
-    const size_t grow = (size_t)it.e * H + (size_t)it.rb * RI + rloc;
-    const size_t rowbytes = (size_t)I * BITS / 8;
-    const uint8_t* cp = p.qa + grow * rowbytes + q * LB;
+    // codes are group-major: row r of expert e, group g at ((e NG + g) H + r) 4 LB
+    const size_t gstride = (size_t)H * (4 * LB);
+    const uint8_t* cp = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
     uint32_t rc[D][RT][LW];
     auto issue = [&](int slot, int g) {
-        const size_t off = (size_t)(g < NG ? g : NG - 1) * (4 * LB);
+        const size_t off = (size_t)(g < NG ? g : NG - 1) * gstride;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const uint8_t* src = cp + (size_t)(16 * rt) * rowbytes + off;
+            const uint8_t* src = cp + (size_t)(16 * rt) * (4 * LB) + off;
             if constexpr (BITS == 4) {
                 const uint4 A = *reinterpret_cast<const uint4*>(src);
                 rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y; rc[slot][rt][2] = A.z; rc[slot][rt][3] = A.w;

@@ -35,7 +35,7 @@ constexpr int kTilesPerHead = 4;                     // work-list tiles per item
 constexpr int kTokRows = kTilesPerHead * kWorkRows;  // token rows per item (64)
 constexpr int kGuRows = 128;                         // gate rows (and up rows) per gate/up item
 constexpr int kDnRows = 128;                         // down rows per down item
-constexpr int kCodeRowBytes = 64;                    // one 4-bit row of a 128-wide group
+constexpr int kCodeRowBytes = 64;                    // one 4-bit row of a 128-wide group (contiguous rows)
 constexpr int kActRowBytes = kGroup * 2;             // one bf16 row of a 128-wide group
 
 struct GemmParams {
@@ -164,7 +164,6 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemm_kernel(GemmParams p) {
     if ((int)blockIdx.x >= n_items) return;
     const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
     const int H = p.H, I = p.I, NG = H / kGroup;
-    const size_t rowbytes = (size_t)H / 2;
     const int tr = tid >> 2, tq = tid & 3;                     // staged token row, quarter
 
     // this lane's 4 weight rows relative to the item's first gate/up row:
@@ -198,7 +197,9 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int wt = 0; wt < 4; ++wt) {
             const size_t row = (size_t)(it.rbase + lrow[wt & 1]);
-            const uint8_t* cp = (wt < 2 ? p.qa : p.qb) + row * rowbytes + 16 * q + (size_t)g * kCodeRowBytes;
+            // codes are group-major: row r of expert e, group g at ((e NG + g) I + r) 64
+            const size_t crow = row + (size_t)it.mt.e * (NG - 1) * I + (size_t)g * I;
+            const uint8_t* cp = (wt < 2 ? p.qa : p.qb) + crow * kCodeRowBytes + 16 * q;
             const uint4 C = *reinterpret_cast<const uint4*>(cp);
             cr[slot][wt][0] = C.x; cr[slot][wt][1] = C.y; cr[slot][wt][2] = C.z; cr[slot][wt][3] = C.w;
             ssr[slot][wt] = (wt < 2 ? p.sa : p.sb)[row * NG + g];
@@ -381,7 +382,6 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
     if ((int)blockIdx.x >= n_items) return;
     const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
     const int H = p.H, I = p.I, NG = I / kGroup;
-    const size_t rowbytes = (size_t)I / 2;
     const size_t plane = (size_t)p.P * I;
     const int tr = tid >> 2, tq = tid & 3;
 
@@ -423,7 +423,9 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int wt = 0; wt < 2; ++wt) {
             const size_t row = (size_t)(it.rbase + 16 * wt);
-            const uint4 C = *reinterpret_cast<const uint4*>(p.qa + row * rowbytes + 16 * q + (size_t)g * kCodeRowBytes);
+            // codes are group-major: row r of expert e, group g at ((e NG + g) H + r) 64
+            const size_t crow = row + (size_t)it.mt.e * (NG - 1) * H + (size_t)g * H;
+            const uint4 C = *reinterpret_cast<const uint4*>(p.qa + crow * kCodeRowBytes + 16 * q);
             cr[slot][wt][0] = C.x; cr[slot][wt][1] = C.y; cr[slot][wt][2] = C.z; cr[slot][wt][3] = C.w;
             ssr[slot][wt] = p.sa[row * NG + g];
             sbr[slot][wt] = p.ba[row * NG + g];

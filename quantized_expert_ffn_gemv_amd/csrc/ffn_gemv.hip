@@ -103,7 +103,10 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
     const int LG = p.LG, RPW = 64 / LG;
     const int rs = lane / LG, sub = lane % LG;
     const int IB = 8 * RPW;
-    const size_t rowbytes = (size_t)H * BITS / 8;
+    // codes are group-major: row r of expert e, group g at ((e NG + g) I + r) GB;
+    // chunk c of a row (16 bytes) lies in group c / BITS
+    constexpr int GB = kGroup * BITS / 8;
+    const size_t gskip = (size_t)(I - 1) * GB;
 
     const int n_items = (*p.n_work) * p.items_per_expert;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -118,10 +121,11 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
         const uint16_t* brow[4];
         {
             const size_t ri0 = (size_t)e * I + (v0 ? i0 : 0), ri1 = (size_t)e * I + (v1 ? i0 + 1 : 0);
-            qrow[0] = p.qa + ri0 * rowbytes; srow[0] = p.sa + ri0 * NG; brow[0] = p.ba + ri0 * NG;
-            qrow[1] = p.qa + ri1 * rowbytes; srow[1] = p.sa + ri1 * NG; brow[1] = p.ba + ri1 * NG;
-            qrow[2] = p.qb + ri0 * rowbytes; srow[2] = p.sb + ri0 * NG; brow[2] = p.bb + ri0 * NG;
-            qrow[3] = p.qb + ri1 * rowbytes; srow[3] = p.sb + ri1 * NG; brow[3] = p.bb + ri1 * NG;
+            const size_t ci0 = ((size_t)e * NG * I + (v0 ? i0 : 0)) * GB, ci1 = ((size_t)e * NG * I + (v1 ? i0 + 1 : 0)) * GB;
+            qrow[0] = p.qa + ci0; srow[0] = p.sa + ri0 * NG; brow[0] = p.ba + ri0 * NG;
+            qrow[1] = p.qa + ci1; srow[1] = p.sa + ri1 * NG; brow[1] = p.ba + ri1 * NG;
+            qrow[2] = p.qb + ci0; srow[2] = p.sb + ri0 * NG; brow[2] = p.bb + ri0 * NG;
+            qrow[3] = p.qb + ci1; srow[3] = p.sb + ri1 * NG; brow[3] = p.bb + ri1 * NG;
         }
 
         for (int tt = 0; tt < cnt; tt += PT) {
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool ok = (r & 1) ? v1 : v0;
-                    raw[r] = ok ? *reinterpret_cast<const uint4*>(qrow[r] + (size_t)c * 16)
+                    raw[r] = ok ? *reinterpret_cast<const uint4*>(qrow[r] + (size_t)c * 16 + (size_t)(c / BITS) * gskip)
                                 : make_uint4(0, 0, 0, 0);
                 }
                 const int g = (c * CK) / kGroup;
@@ -274,7 +278,10 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
     const int LG = p.LG, RPW = 64 / LG;
     const int rs = lane / LG, sub = lane % LG;
     const int NB = 16 * RPW;                // rows per item
-    const size_t rowbytes = (size_t)I * BITS / 8;
+    // codes are group-major: row r of expert e, group g at ((e NG + g) H + r) GB;
+    // chunk c of a row (16 bytes) lies in group c / BITS
+    constexpr int GB = kGroup * BITS / 8;
+    const size_t gskip = (size_t)(H - 1) * GB;
 
     const int P = p.T * p.k;
     const int n_items = (*p.n_work) * p.items_per_expert;
@@ -292,7 +299,8 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
         for (int r = 0; r < 4; ++r) {
             vr[r] = n0 + r < H;
             const size_t ri = (size_t)e * H + (vr[r] ? n0 + r : 0);
-            qrow[r] = p.qa + ri * rowbytes; srow[r] = p.sa + ri * NG; brow[r] = p.ba + ri * NG;
+            qrow[r] = p.qa + ((size_t)e * NG * H + (vr[r] ? n0 + r : 0)) * GB;
+            srow[r] = p.sa + ri * NG; brow[r] = p.ba + ri * NG;
         }
 
         for (int tt = 0; tt < cnt; tt += PT) {
@@ -339,7 +347,8 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
                 const int g = (c * CK) / kGroup;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    raw[r] = vr[r] ? *reinterpret_cast<const uint4*>(qrow[r] + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+                    raw[r] = vr[r] ? *reinterpret_cast<const uint4*>(qrow[r] + (size_t)c * 16 + (size_t)(c / BITS) * gskip)
+                                   : make_uint4(0, 0, 0, 0);
                     sc[r] = vr[r] ? f16_bits_to_f32(srow[r][g]) : 0.f;
                     bc[r] = vr[r] ? f16_bits_to_f32(brow[r][g]) : 0.f;
                 }

@@ -87,7 +87,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
     const int H = p.H, I = p.I, NG = H / kGroup, NGW = (NG + kWaves - 1) / kWaves;
     int gb, ng;
     wave_groups(NG, w, gb, ng);
-    const size_t rowbytes = (size_t)H * BITS / 8;
+    constexpr int GB = kGroup * BITS / 8;      // code bytes of one row in one group
+    const size_t gstride = (size_t)I * GB;     // from one group of all I rows to the next
     float* sc_base = lds + w * 2 * NGW * 64;
     float* red = lds + kWaves * 2 * NGW * 64;
     uint32_t ONE[4] = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -115,9 +116,9 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
         }
         const int e = (I_.e >= 0 && I_.e < p.E) ? I_.e : 0;
         tok = (tok >= 0 && tok < p.T) ? tok : 0;
-        const size_t wrow = (size_t)e * I + I_.it * 16 + pair_order_row<BITS>(m);
-        I_.g = p.qa + wrow * rowbytes + q * LB;
-        I_.u = p.qb + wrow * rowbytes + q * LB;
+        const size_t wcode = (size_t)e * NG * gstride + (size_t)(I_.it * 16 + pair_order_row<BITS>(m)) * GB + q * LB;
+        I_.g = p.qa + wcode;
+        I_.u = p.qb + wcode;
         I_.x = p.x + (size_t)tok * H + q * 32;
         if (ng > 0) {
 #pragma unroll
@@ -150,13 +151,13 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
     uint32_t wg[D][LW], wu[D][LW], xv[D][16];
     auto issue = [&](int slot, const uint8_t* gp, const uint8_t* up, const uint16_t* xp, int g) {
         if constexpr (BITS == 4) {
-            const uint4 A = *reinterpret_cast<const uint4*>(gp + (size_t)g * 64);
-            const uint4 B = *reinterpret_cast<const uint4*>(up + (size_t)g * 64);
+            const uint4 A = *reinterpret_cast<const uint4*>(gp + (size_t)g * gstride);
+            const uint4 B = *reinterpret_cast<const uint4*>(up + (size_t)g * gstride);
             wg[slot][0] = A.x; wg[slot][1] = A.y; wg[slot][2] = A.z; wg[slot][3] = A.w;
             wu[slot][0] = B.x; wu[slot][1] = B.y; wu[slot][2] = B.z; wu[slot][3] = B.w;
         } else {
-            const uint2 A = *reinterpret_cast<const uint2*>(gp + (size_t)g * 32);
-            const uint2 B = *reinterpret_cast<const uint2*>(up + (size_t)g * 32);
+            const uint2 A = *reinterpret_cast<const uint2*>(gp + (size_t)g * gstride);
+            const uint2 B = *reinterpret_cast<const uint2*>(up + (size_t)g * gstride);
             wg[slot][0] = A.x; wg[slot][1] = A.y;
             wu[slot][0] = B.x; wu[slot][1] = B.y;
         }
@@ -298,7 +299,8 @@ __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaParams p) {
     const int tw = w / KS, kp = w % KS;        // this wave's row tile and K part
     const int H = p.H, I = p.I, NG = I / kGroup, NGW = (NG + KS - 1) / KS;
     const int gb = (kp * NG) / KS, ng = ((kp + 1) * NG) / KS - gb;
-    const size_t rowbytes = (size_t)I * BITS / 8;
+    constexpr int GB = kGroup * BITS / 8;      // code bytes of one row in one group
+    const size_t gstride = (size_t)H * GB;     // from one group of all H rows to the next
     float* sc_base = lds + w * 2 * NGW * 64;
     float* red = lds + kWaves * 2 * NGW * 64;
     const size_t plane = (size_t)p.P * I;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaParams p) {
         const bool ok_rows = I_.row0 >= 0 && I_.n >= 1 && I_.n <= kWorkRows && I_.row0 + I_.n <= p.P;
         const int r = ok_rows ? I_.row0 + (m < I_.n ? m : 0) : 0;   // empty columns reuse row 0
         const int n0 = (I_.it * RT + tw) * 32;
-        I_.c0 = p.qa + ((size_t)e * H + n0 + m) * rowbytes + q * LB;
+        I_.c0 = p.qa + (size_t)e * NG * gstride + (size_t)(n0 + m) * GB + q * LB;
         I_.h = p.hp + (size_t)r * I + q * 32;
         I_.part = p.hpart + (size_t)r * (I / 16);
         if (ng > 0) {
@@ -351,13 +353,13 @@ __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaParams p) {
     float4 hp0[D], hp1[D];
     auto issue = [&](int slot, const uint8_t* cp, const uint16_t* hpp, const float* pp, int g) {
         if constexpr (BITS == 4) {
-            const uint4 A = *reinterpret_cast<const uint4*>(cp + (size_t)g * 64);
-            const uint4 B = *reinterpret_cast<const uint4*>(cp + 16 * rowbytes + (size_t)g * 64);
+            const uint4 A = *reinterpret_cast<const uint4*>(cp + (size_t)g * gstride);
+            const uint4 B = *reinterpret_cast<const uint4*>(cp + 16 * GB + (size_t)g * gstride);
             w0[slot][0] = A.x; w0[slot][1] = A.y; w0[slot][2] = A.z; w0[slot][3] = A.w;
             w1[slot][0] = B.x; w1[slot][1] = B.y; w1[slot][2] = B.z; w1[slot][3] = B.w;
         } else {
-            const uint2 A = *reinterpret_cast<const uint2*>(cp + (size_t)g * 32);
-            const uint2 B = *reinterpret_cast<const uint2*>(cp + 16 * rowbytes + (size_t)g * 32);
+            const uint2 A = *reinterpret_cast<const uint2*>(cp + (size_t)g * gstride);
+            const uint2 B = *reinterpret_cast<const uint2*>(cp + 16 * GB + (size_t)g * gstride);
             w0[slot][0] = A.x; w0[slot][1] = A.y;
             w1[slot][0] = B.x; w1[slot][1] = B.y;
         }

@@ -75,13 +75,13 @@ def upload_layer(shape: mi.LayerShape, bits: int = 4, seed: int = 0) -> Layer:
     q, s, b = [], [], []
     for m in mi.MATRICES:
         N, K = mi.matrix_dims(shape, m)
-        q.append(torch.empty((shape.E, N, K * bits // 8), dtype=torch.uint8, device=DEV))
+        q.append(torch.empty((shape.E, K // 128, N, 16 * bits), dtype=torch.uint8, device=DEV))
         s.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device=DEV))
         b.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device=DEV))
     for e, mats in mi.iter_expert_weights(shape, bits, seed):
         for i, m in enumerate(mi.MATRICES):
             qq, ss, bb = mats[m]
-            q[i][e].copy_(torch.from_numpy(qq))
+            q[i][e].copy_(torch.from_numpy(moe.group_major(qq, bits)))
             s[i][e].copy_(torch.from_numpy(ss.view(np.int16)))
             b[i][e].copy_(torch.from_numpy(bb.view(np.int16)))
     return Layer(shape, bits, seed, Wr, bias, table, to_dev(Wr), None if bias is None else to_dev(bias),

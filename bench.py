@@ -332,21 +332,42 @@ def summarize_counters(fetch_dir, write_dir, copy_mib, algo="auto"):
     print(json.dumps(rec, indent=1))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(mi, shape, layer0, T):
-    """Oracle timed on one full layer step of weight set 0 (same inputs as the GPU)."""
+    """Oracle timed on one full layer step of weight set 0 (same inputs as the GPU),
+    pinned to one host core for the timed call."""
     import numpy as np
     import oracle
     xb, rb = mi.make_activations(shape.H, T, seed=1000)
     logits = oracle.router_logits(xb, layer0["Wr_np"], layer0["bias_np"])
     ids, _ = oracle.topk(logits, shape.k)
     W = mi.make_expert_weights(shape, 4, seed=0, experts=np.unique(ids))
-    t0 = time.perf_counter()
-    oracle.layer(xb, layer0["Wr_np"], layer0["bias_np"], W, shape.k, layer0["table_np"], shape.E, rb)
-    sec = time.perf_counter() - t0
+    U = len(np.unique(ids))
+    old = os.sched_getaffinity(0)
+    core = min(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        t0 = time.perf_counter()
+        oracle.layer(xb, layer0["Wr_np"], layer0["bias_np"], W, shape.k, layer0["table_np"], shape.E, rb)
+        sec = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, old)
     return dict(value=round(T / sec, 3), unit="tokens/s", cores=1, kind="oracle",
                 sample=f"one full layer step of weight set 0: T={T} tokens, {T * shape.k} routed rows, "
-                       f"single-threaded C oracle (double accumulation), {sec:.2f} s",
-                seconds=round(sec, 3), host_cpus=os.cpu_count())
+                       f"{U} experts, single-threaded C oracle (double accumulation) pinned to core {core}, "
+                       f"{sec:.2f} s",
+                seconds=round(sec, 3), weight_GBps=round(U * shape.bytes_per_expert(4) / sec / 1e9, 4),
+                host_cpus=os.cpu_count(), cpu_model=cpu_model())
 
 
 def main():
@@ -382,8 +403,8 @@ def main():
 
     fused = args.ffn == "fused" and "fused" in FFN_KERNELS[args.algo]
 
-    def measure(T, steps, warmup):
-        r = Runner(torch, mi, moe, shape, layers, T, algo, fused_ffn=fused)
+    def measure(T, steps, warmup, layer_sets=None):
+        r = Runner(torch, mi, moe, shape, layer_sets or layers, T, algo, fused_ffn=fused)
         U = r.experts_used()
         # throughput: the K steps back to back, nothing recorded between kernels
         # (eager calls; with --launch graph, replays of captured graphs)
@@ -433,6 +454,11 @@ def main():
         m = measure(tok, max(args.steps // 2, 10), max(args.warmup // 2, 2))
         log(f"[bench] sweep T={tok}: {m['tokens_per_s']:.0f} tokens/s, FFN {m['ffn_GBps']:.0f} GB/s")
         sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in m.items()})
+
+    # warm: one weight set only, so the experts a step touches (about 93 MB at
+    # T = 32) can stay in the 256 MB last-level cache between steps
+    warm = measure(args.tokens, max(args.steps // 2, 10), max(args.warmup // 2, 2), layer_sets=layers[:1])
+    log(f"[bench] warm (one weight set) T={args.tokens}: {warm['tokens_per_s']:.0f} tokens/s")
 
     prefill = None
     if args.prefill_steps > 0:
@@ -510,6 +536,9 @@ def main():
             "two_launch_ms_per_step_with_kernel_events": round(main_run["split_ms_per_step_with_kernel_events"], 5),
         },
         "sweep": sweep,
+        "warm_one_weight_set": {"tokens_per_s": round(warm["tokens_per_s"], 1),
+                                "ms_per_step": round(warm["ms_per_step"], 5),
+                                "ffn_GBps": round(warm["ffn_GBps"], 1)},
         "prefill": prefill,
         "context_not_comparable": CONTEXT,
     }

@@ -166,41 +166,73 @@ constexpr int kPermWaves = 8;
 
 // Workgroup-wide body (blockDim = 1024).  LDS scratch: `cnt` kPermWaves x E
 // ints (row stride E), `offs`, `cnts`, `wpos` E ints each, `wsum` 32.
+// Slot lookup folded into the grouping (the routing kernels): the same
+// outputs as slot_lookup_body, with the miss flags set in the counting pass
+// (held in `offs` until the scan) and the miss list placed by the scan.
+struct LookupArgs {
+    const int* table;                 // LDS copy of slot_of_expert [E]
+    int n_slots;
+    int32_t* pair_slot;
+    int32_t* miss;
+    int32_t* n_miss;
+    int32_t* doorbell;
+    uint32_t* last_use;
+    uint32_t step;
+};
+
+template <bool LOOKUP>
 __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* __restrict__ counts,
                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
                              int32_t* __restrict__ pair_to_row, int32_t* __restrict__ active,
                              int32_t* __restrict__ n_active, int32_t* __restrict__ work,
                              int32_t* __restrict__ n_work, int* cnt_flat, int* offs, int* cnts, int* wpos,
-                             int* wsum) {
+                             int* wsum, const LookupArgs& lk = LookupArgs{}) {
     auto cnt = [&](int w, int e) -> int& { return cnt_flat[w * E + e]; };
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int chunk = (P + kPermWaves - 1) / kPermWaves;
 
     for (int i = tid; i < kPermWaves * E; i += kBodyThreads) cnt_flat[i] = 0;
+    if constexpr (LOOKUP)
+        for (int e = tid; e < E; e += kBodyThreads) offs[e] = 0;
     lds_sync();
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
         for (int p = p0 + lane; p < p1; p += 64) {
             const int e = ids[p];
-            if (e >= 0 && e < E) atomicAdd(&cnt(wid, e), 1);
+            const bool ok = e >= 0 && e < E;
+            if (ok) atomicAdd(&cnt(wid, e), 1);
+            if constexpr (LOOKUP) {
+                int sl = -1;
+                if (ok) {
+                    const int t = lk.table[e];
+                    if (t >= 0 && t < lk.n_slots) sl = t;
+                }
+                lk.pair_slot[p] = sl;
+                if (ok && sl < 0) offs[e] = 1;
+                if (sl >= 0 && lk.last_use) lk.last_use[sl] = lk.step;
+            }
         }
     }
     lds_sync();
 
-    int running = 0, nact = 0, ntile_run = 0;
+    int running = 0, nact = 0, ntile_run = 0, nmiss = 0;
     for (int e0 = 0; e0 < E; e0 += kBodyThreads) {
         const int e = e0 + tid;
         int tot = 0;
         if (e < E)
 #pragma unroll
             for (int w = 0; w < kPermWaves; ++w) tot += cnt(w, e);
-        // one scan of (count | active flag << 16) and the tile count: counts
-        // sum to at most 4096 and flags to at most 1024, so the halves never mix
+        const int f = (LOOKUP && e < E) ? offs[e] : 0;     // miss flag
+        // one scan of (count | active flag << 16) and (tiles | miss flag << 16):
+        // counts sum to at most 4096, tiles to at most 4096 / 16 + 1024, and the
+        // flags to at most 1024, so the halves never mix
         const int tiles = (tot + kWorkRows - 1) / kWorkRows;
-        int sc[2] = {tot | ((tot > 0 ? 1 : 0) << 16), tiles}, st[2];
+        int sc[2] = {tot | ((tot > 0 ? 1 : 0) << 16), tiles | (f << 16)}, st[2];
         block_exclusive_scan<2>(sc, wsum, st);
-        const int excl = sc[0] & 0xFFFF, apos = sc[0] >> 16, tpos = sc[1];
-        const int sum = st[0] & 0xFFFF, nsum = st[0] >> 16, tsum = st[1];
+        const int excl = sc[0] & 0xFFFF, apos = sc[0] >> 16, tpos = sc[1] & 0xFFFF, mpos = sc[1] >> 16;
+        const int sum = st[0] & 0xFFFF, nsum = st[0] >> 16, tsum = st[1] & 0xFFFF, msum = st[1] >> 16;
+        if constexpr (LOOKUP)
+            if (f) lk.miss[nmiss + mpos] = e;
         if (e < E) {
             counts[e] = tot;
             offsets[e] = running + excl;
@@ -219,6 +251,17 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
         running += sum;
         nact += nsum;
         ntile_run += tsum;
+        nmiss += msum;
+    }
+    if constexpr (LOOKUP) {
+        // the doorbell is a release to the host: every wave's miss-list stores
+        // must be complete before it, hence the full barrier (it waits for them)
+        if (lk.doorbell) __syncthreads();
+        if (tid == 0) {
+            *lk.n_miss = nmiss;
+            if (lk.doorbell && nmiss > 0)
+                __hip_atomic_store(lk.doorbell, nmiss, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
     if (tid == 0) {
         offsets[E] = running;
@@ -402,7 +445,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
     __shared__ int wsum[32];
-    permute_body(ids, P, E, k, counts, offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work, cnt,
+    permute_body<false>(ids, P, E, k, counts, offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work, cnt,
                  offs, cnts, wpos, wsum);
 }
 
@@ -423,7 +466,7 @@ constexpr int kDispatchMaxP = 4096;
 template <int PER>
 __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict__ logits, DispatchArgs a) {
     __shared__ int ids_s[kDispatchMaxP];
-    __shared__ int scratch[kPermWaves * kMaxE];          // lookup flags, then counting-sort counts
+    __shared__ int scratch[kPermWaves * kMaxE];          // counting-sort counts
     __shared__ int offs[kMaxE];
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
@@ -451,11 +494,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const float* __restrict_
                                 a.n_active, a.work, a.n_work, scratch, offs, wpos, scratch + kMaxE);
         return;
     }
-    slot_lookup_body(ids_s, a.P, a.E, cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
-                     a.step, scratch, wsum);
-    lds_sync();
-    permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
-                 a.work, a.n_work, scratch, offs, cnts, wpos, wsum);
+    const LookupArgs lk{cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use, a.step};
+    permute_body<true>(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active,
+                       a.n_active, a.work, a.n_work, scratch, offs, cnts, wpos, wsum, lk);
 }
 
 bool dispatch_fused(const moe_dims& d) { return (long)d.T * d.k <= kDispatchMaxP && d.E <= kMaxE; }
@@ -580,11 +621,9 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
         }
         return;
     }
-    slot_lookup_body(ids_s, a.P, a.E, cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use,
-                     a.step, scratch, wsum);
-    lds_sync();
-    permute_body(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active, a.n_active,
-                 a.work, a.n_work, scratch, offs, cnts, wpos, wsum);
+    const LookupArgs lk{cnts, a.n_slots, a.pair_slot, a.miss, a.n_miss, a.doorbell, a.last_use, a.step};
+    permute_body<true>(ids_s, a.P, a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_to_row, a.active,
+                       a.n_active, a.work, a.n_work, scratch, offs, cnts, wpos, wsum, lk);
     if (tid == 0 && !single) __hip_atomic_store(&sync[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -282,20 +282,23 @@ def test_route_dispatch_matches_separate_calls(name, T):
         assert np.array_equal(va.view(np.uint8), vb.view(np.uint8)), key
 
 
-def test_route_dispatch_doorbell_and_last_use():
-    L = layer("e64")
+@pytest.mark.parametrize("name,T,n_res", [("e64", 8, 4), ("a3b", 32, 20)])
+def test_route_dispatch_doorbell_and_last_use(name, T, n_res):
+    """The one-launch routing's slot lookup (one-wave path at T*k <= 64, workgroup
+    path above) with a doorbell and last_use, against the oracle."""
+    L = layer(name)
     sh = L.shape
-    xb, _ = mi.make_activations(sh.H, 8, 0)
-    d = moe.dims(8, sh.H, sh.I, sh.E, sh.k)
+    xb, _ = mi.make_activations(sh.H, T, 0)
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
     buf = moe.LayerBuffers.allocate(d, 4)
     x_d = torch.from_numpy(xb.view(np.int16)).cuda()
     bell = torch.zeros(1, dtype=torch.int32, pin_memory=True)
     last_use = torch.zeros(sh.E, dtype=torch.int32, device="cuda")
-    table = mi.make_slot_table(sh, 0, n_resident=4)
+    table = mi.make_slot_table(sh, 0, n_resident=n_res)
     moe.route_dispatch(d, x_d, L.Wr_d, L.bias_d, True, buf.logits, buf.topk_ids, buf.topk_w,
                        torch.from_numpy(table).cuda(), sh.E, buf.pair_slot, buf.miss, buf.n_miss, buf.counts,
                        buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active, buf.n_active, buf.work_list,
-                       buf.n_work, host_doorbell=bell, last_use=last_use, step=91)
+                       buf.n_work, host_doorbell=bell, last_use=last_use, step=91, sync=buf.sync)
     torch.cuda.synchronize()
     ids = buf.topk_ids.cpu().numpy()
     check_topk(dict(logits=buf.logits.cpu().numpy(), ids=ids, gates=buf.topk_w.cpu().numpy()), L)

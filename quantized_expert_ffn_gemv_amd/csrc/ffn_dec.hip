@@ -759,6 +759,7 @@ static int fused_pick(int rw, int dg, int rt, int dd, size_t lds, hipStream_t s,
                       int32_t* sync) {
     if (rw == 4 && dg == 4 && rt == 4 && dd == 2) return fused_go<BITS, 4, 4, 4, 2>(lds, s, f, sync);
     if (rw == 4 && dg == 4 && rt == 2 && dd == 2) return fused_go<BITS, 4, 4, 2, 2>(lds, s, f, sync);
+    if (rw == 1 && dg == 4 && rt == 1 && dd == 4) return fused_go<BITS, 1, 4, 1, 4>(lds, s, f, sync);
     if (rw == 1 && dg == 4 && rt == 1 && dd == 2) return fused_go<BITS, 1, 4, 1, 2>(lds, s, f, sync);
     return MOE_ERR_UNSUPPORTED;
 }
@@ -775,7 +776,11 @@ int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s) {
     const int rw = dec_gateup_rw(d), rt = dec_down_rt(d);
     f.p.ipe = d.I / (16 * rw);
     f.ipe_d = d.H / (64 * rt);
-    const int dg = dec_depth((d.H / kGroup) / (4 / rw), 4), dd = dec_depth(d.I / kGroup, 2);
+    // One-tile down items (the smallest batches, where a few entries make the
+    // critical path) request up to four code groups before their wait, so that
+    // no HBM round trip is left once h arrives; with more entries the deeper
+    // ring measured no faster.
+    const int dg = dec_depth((d.H / kGroup) / (4 / rw), 4), dd = dec_depth(d.I / kGroup, rt == 1 ? 4 : 2);
     const size_t lg = dec_gateup_lds(d, rw), ld = dec_down_lds(d, rt);
     const size_t lds = lg > ld ? lg : ld;
     return a.bits == 4 ? fused_pick<4>(rw, dg, rt, dd, lds, s, f, sync)

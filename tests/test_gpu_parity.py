@@ -402,7 +402,7 @@ def test_dispatch_crafted_ids(E, H, T, k, pool):
         assert np.array_equal(to_host(buf.work_list)[: wl.shape[0]], wl)
         assert int(buf.sync.abs().sum().item()) == 0
 
-FUSED_FFN_CASES = [("tiny", 4, 4, None), ("a3b", 4, 1, None), ("a3b", 4, 32, None), ("a3b", 2, 8, None),
+FUSED_FFN_CASES = [("tiny", 4, 4, None), ("a3b", 4, 1, None), ("a3b", 2, 2, None), ("a3b", 4, 32, None), ("a3b", 2, 8, None),
                    ("a3b", 4, 64, None), ("a3b", 2, 32, None),
                    ("e512", 4, 1, None), ("e512", 2, 4, None), ("e64", 4, 8, None),
                    ("ragged_a", 4, 7, RAGGED[0]), ("ragged_b", 2, 3, RAGGED[1])]

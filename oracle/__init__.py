@@ -45,6 +45,8 @@ def lib():
         L.orc_f32_to_bf16.argtypes = [ctypes.c_float]; L.orc_f32_to_bf16.restype = ctypes.c_uint16
         L.orc_f64_to_bf16.argtypes = [f64]; L.orc_f64_to_bf16.restype = ctypes.c_uint16
         L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]; L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f64_to_f16.argtypes = [f64]; L.orc_f64_to_f16.restype = ctypes.c_uint16
+        L.orc_zero_point_bias.argtypes = [ctypes.c_int64, P, P, P]; L.orc_zero_point_bias.restype = None
         L.orc_code.argtypes = [P, i32, i32]; L.orc_code.restype = i32
         L.orc_weight.argtypes = [P, P, P, i32, i32]; L.orc_weight.restype = f64
         L.orc_dequant_matrix.argtypes = [i32, i32, i32, P, P, P, P]; L.orc_dequant_matrix.restype = None
@@ -91,6 +93,24 @@ def f64_to_bf16(vals) -> np.ndarray:
     L = lib()
     flat = np.asarray(vals, dtype=np.float64).ravel()
     return np.array([L.orc_f64_to_bf16(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(vals))
+
+
+def f64_to_f16(vals) -> np.ndarray:
+    """IEEE binary16 bit patterns of float64 values, one rounding (nearest, ties to even)."""
+    L = lib()
+    flat = np.asarray(vals, dtype=np.float64).ravel()
+    return np.array([L.orc_f64_to_f16(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(vals))
+
+
+def zero_point_bias(scale: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """fp16 bias bits b = -(z s) per group for zero-point weights w = (q - z) s,
+    so that q s + b is the same weight up to b's one rounding."""
+    scale, zeros = _c(scale, np.uint16), _c(zeros, np.uint8)
+    if scale.shape != zeros.shape:
+        raise ValueError("scale and zeros must have one entry per group each")
+    out = np.empty(scale.shape, dtype=np.uint16)
+    lib().orc_zero_point_bias(int(scale.size), _p(scale), _p(zeros), _p(out))
+    return out
 
 
 def code(row: np.ndarray, k: int, bits: int) -> int:

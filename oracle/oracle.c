@@ -26,6 +26,8 @@
  *   expert FFN            Flash-MoE page sec. 3: fused SwiGLU between the
  *                         gate/up and down matvecs.
  *   combine               Flash-MoE page sec. 3: MoE combine + residual.
+ *   zero-point adapter    "Strata" page sec. 2.2 and the laptop page sec. 4.2:
+ *                         (q - zero) scale groups, as bias = -zero scale.
  *
  * Parity status of every function is recorded in the test suite that pins
  * it; none is unpinned.
@@ -77,6 +79,31 @@ uint16_t orc_f64_to_bf16(double d) {
     return (uint16_t)(u >> 16);
 }
 
+/* double -> IEEE binary16, one rounding (nearest, ties to even).  binary16
+ * keeps 11 significant bits from 2^-14 up, a fixed spacing of 2^-24 below it,
+ * and its largest finite value is 65504: anything that rounds past it is an
+ * infinity.  NaN -> 0x7E00. */
+uint16_t orc_f64_to_f16(double d) {
+    const uint16_t sign = signbit(d) ? 0x8000u : 0u;
+    if (isnan(d)) return 0x7E00u;
+    const double a = fabs(d);
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+    if (a < ldexp(1.0, -14)) {
+        /* units of 2^-24; 1024 units is the smallest normal, whose bits are 0x0400 */
+        return (uint16_t)(sign | (uint16_t)nearbyint(a * ldexp(1.0, 24)));
+    }
+    int e;
+    const double m = frexp(a, &e);               /* a = m 2^e, m in [0.5, 1) */
+    double r = nearbyint(ldexp(m, 11));          /* a ~ (r / 1024) 2^(e-1), r in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    const int ex = e - 1 + 15;                   /* biased exponent, >= 1 here */
+    if (ex >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)(ex << 10) | (uint16_t)((int)r - 1024));
+}
+
 /* IEEE binary16 -> float, exact for normals, subnormals, inf and NaN */
 float orc_f16_to_f32(uint16_t h) {
     int sign = (h >> 15) & 1;
@@ -91,6 +118,15 @@ float orc_f16_to_f32(uint16_t h) {
         v = ldexp((double)(man | 0x400), ex - 25);
     }
     return (float)(sign ? -v : v);
+}
+
+/* Zero-point groups, w = (q - z) s (the "Strata" page, sec. 2.2: each group of
+ * 128 weights shares one scale and one zero point; the laptop page, sec. 4.2,
+ * the same form over groups of 32), written in this format's w = q s + b:
+ * b = -(z s), rounded once to fp16.  One entry per (row, group). */
+void orc_zero_point_bias(int64_t n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias) {
+    for (int64_t i = 0; i < n; ++i)
+        bias[i] = orc_f64_to_f16(-((double)zeros[i] * (double)orc_f16_to_f32(scale[i])));
 }
 
 /* Code of element k in a packed row: bits = 4 (low nibble = even k) or

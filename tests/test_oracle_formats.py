@@ -167,3 +167,72 @@ def test_expert_bytes_match_page_figure():
     got = shape.bytes_per_expert(4)
     assert got == gold["layout_bytes_q4_g128"]
     assert abs(got / 1e6 - gold["page_value_MB"]) / gold["page_value_MB"] < gold["rel_tolerance"]
+
+
+def _f16_neighbours(n, rng):
+    """Doubles across the binary16 range: random, exact ties between neighbours,
+    the subnormal range and the edge of overflow."""
+    pats = rng.integers(0, 0x7C00, size=n).astype(np.uint16)          # finite, non-negative
+    lo = pats.view(np.float16).astype(np.float64)
+    hi = (pats + 1).view(np.float16).astype(np.float64)               # next value up (0x7C00: inf)
+    hi = np.where(np.isinf(hi), 65536.0, hi)
+    mid = 0.5 * (lo + hi)                                             # exact ties
+    frac = lo + (hi - lo) * rng.random(n)
+    edge = np.array([0.0, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -24, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+                     65504.0, 65519.99, 65520.0, 1e6, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11])
+    v = np.concatenate([lo, mid, frac, edge])
+    return np.concatenate([v, -v])
+
+
+def test_f64_to_f16_matches_numpy(orc):
+    """Rounding to binary16 (nearest, ties to even, overflow to inf) agrees with
+    numpy's own float64 -> float16 conversion bit for bit."""
+    v = _f16_neighbours(4000, np.random.default_rng(7))
+    got = orc.f64_to_f16(v)
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref), v[got != ref][:5]
+    assert orc.f64_to_f16(np.array([np.nan]))[0] == 0x7E00
+
+
+def test_zero_point_bias_reproduces_zero_point_weights(orc):
+    """(q - z) s written as q s + b with b = -(z s): every weight agrees with
+    the zero-point form within b's one rounding (half an fp16 spacing of z s),
+    and exactly where z s is an fp16 value (power-of-two scales)."""
+    rng = np.random.default_rng(11)
+    for bits in (4, 2):
+        N, K = 6, 512
+        codes = rng.integers(0, 1 << bits, size=(N, K))
+        q = mi.pack_codes(codes, bits)
+        s = mi.f32_to_f16_bits(rng.uniform(0.005, 0.02, size=(N, K // 128)))
+        z = rng.integers(0, 1 << bits, size=(N, K // 128)).astype(np.uint8)
+        b = orc.zero_point_bias(s, z)
+        sv = s.view(np.float16).astype(np.float64)
+        zs = z.astype(np.float64) * sv
+        exact = (codes - np.repeat(z.astype(np.float64), 128, axis=1)) * np.repeat(sv, 128, axis=1)
+        got = orc.dequant_matrix(q, s, b, bits)
+        bound = np.repeat(np.abs(zs) * 2.0 ** -11, 128, axis=1)
+        assert np.all(np.abs(got - exact) <= bound)
+        # b is -(z s) rounded once: the nearest fp16 value
+        bv = b.view(np.float16).astype(np.float64)
+        assert np.all(np.abs(bv + zs) <= np.abs(zs) * 2.0 ** -11)
+        # power-of-two scales: z s is exact in fp16, so are the weights
+        s2 = mi.f32_to_f16_bits(2.0 ** rng.integers(-10, -4, size=(N, K // 128)).astype(np.float32))
+        b2 = orc.zero_point_bias(s2, z)
+        exact2 = (codes - np.repeat(z.astype(np.float64), 128, axis=1)) * \
+            np.repeat(s2.view(np.float16).astype(np.float64), 128, axis=1)
+        assert np.array_equal(orc.dequant_matrix(q, s2, b2, bits), exact2)
+
+
+def test_zero_point_bias_special_cases(orc):
+    """z = 0 gives -0 (weights q s); a negative scale flips the sign; z s past
+    the fp16 range gives an infinite bias."""
+    s = mi.f32_to_f16_bits(np.array([0.5, -0.25, 60000.0, 2.0 ** -24], np.float32))
+    z = np.array([0, 3, 2, 255], np.uint8)
+    b = orc.zero_point_bias(s, z)
+    assert b[0] == 0x8000
+    assert b[1] == np.float16(0.75).view(np.uint16)
+    assert b[2] == 0xFC00
+    assert b[3] == np.float16(-255 * 2.0 ** -24).view(np.uint16)
+    with pytest.raises(ValueError):
+        orc.zero_point_bias(s, z[:3])

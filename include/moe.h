@@ -320,6 +320,24 @@ int moe_expert_ffn_fused(const moe_dims* dims, int bits, const uint16_t* x, cons
 int moe_combine(const moe_dims* dims, const uint16_t* y_rows, const int32_t* pair_to_row,
                 const float* topk_w, const uint16_t* residual, uint16_t* out, void* stream);
 
+/* Weight-format adapter (run once when weights are loaded; not a step of the
+ * layer).  Zero-point groups, w = (q - z) s ("Strata" page, sec. 2.2: each
+ * group of 128 weights shares one scale and one zero point; the laptop page,
+ * sec. 4.2, the same form), are this library's w = q s + b with b = -(z s):
+ *   bias[i] = fp16(-(float)zeros[i] * scale[i]),  0 <= i < n.
+ * z s is exact in float32, so the one rounding is to fp16 (nearest, ties to
+ * even; past 65504 an infinity).  A NaN scale, or z = 0 with an infinite
+ * scale, gives a NaN bias.  The codes q are used unchanged.
+ *   n      number of (row, group) entries, e.g. E*N*(K/128) for one matrix;
+ *          0 is a no-op and the pointers are not used.
+ *   scale  fp16 bits [n], device memory, 2-byte aligned (moe_qweights.scale[m]).
+ *   zeros  uint8 [n], device memory: one zero point per entry, not packed.
+ *   bias   fp16 bits [n], device memory, 2-byte aligned (moe_qweights.bias[m]);
+ *          must not overlap scale or zeros.
+ * Errors: n < 0, a NULL or misaligned pointer, or overlapping buffers:
+ * MOE_ERR_INVALID_ARG before anything is enqueued.  Asynchronous on `stream`. */
+int moe_zero_point_bias(int64_t n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

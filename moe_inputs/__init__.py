@@ -41,7 +41,7 @@ GROUP = 128
 MATRICES = ("gate", "up", "down")
 
 # tags of the independent random streams
-_TAG_X, _TAG_RES, _TAG_WR, _TAG_PERM, _TAG_Q, _TAG_S, _TAG_B = 1, 2, 3, 4, 5, 6, 7
+_TAG_X, _TAG_RES, _TAG_WR, _TAG_PERM, _TAG_Q, _TAG_S, _TAG_B, _TAG_Z = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclasses.dataclass(frozen=True)
@@ -222,6 +222,14 @@ def iter_expert_weights(shape: LayerShape, bits: int = 4, seed: int = 0):
         yield e, {m: _draw_expert_matrix(shape, m, e, bits, seed) for m in MATRICES}
 
 
+def make_zero_points(shape: LayerShape, m: str, e: int, bits: int = 4, seed: int = 0) -> np.ndarray:
+    """Zero points of matrix m of expert e for zero-point weights (q - z) s:
+    uint8 [N][K/128], uniform over the codes 0 .. 2^bits - 1."""
+    N, K = matrix_dims(shape, m)
+    return _rng(seed, _TAG_Z, bits, MATRICES.index(m), e).integers(0, 1 << bits, size=(N, K // GROUP),
+                                                                    dtype=np.uint8)
+
+
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Pack integer codes [..., K] into bytes along the last axis (format above)."""
     codes = np.asarray(codes, dtype=np.uint8)
@@ -238,6 +246,6 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
 __all__ = [
     "GROUP", "MATRICES", "LayerShape", "CONFIGS", "CONFIG_ORDER", "ExpertWeights",
     "make_activations", "make_router", "make_slot_table", "make_expert_weights",
-    "iter_expert_weights", "expert_popularity", "popularity_order", "matrix_dims",
+    "iter_expert_weights", "make_zero_points", "expert_popularity", "popularity_order", "matrix_dims",
     "pack_codes", "f32_to_bf16_bits", "f32_to_f16_bits",
 ]

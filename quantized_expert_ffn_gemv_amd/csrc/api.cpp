@@ -410,4 +410,21 @@ int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* pair_t
     return ok();
 }
 
+int moe_zero_point_bias(int64_t n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias, void* stream) {
+    const char* fn = "moe_zero_point_bias";
+    if (n < 0) return fail(MOE_ERR_INVALID_ARG, "%s: n = %lld is negative", fn, (long long)n);
+    if (n == 0) return ok();
+    REQUIRE_PTR(scale, 2);
+    REQUIRE_PTR(zeros, 1);
+    REQUIRE_PTR(bias, 2);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(bias), b1 = b0 + 2 * (uintptr_t)n;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale), s1 = s0 + 2 * (uintptr_t)n;
+    const uintptr_t z0 = reinterpret_cast<uintptr_t>(zeros), z1 = z0 + (uintptr_t)n;
+    if ((b0 < s1 && s0 < b1) || (b0 < z1 && z0 < b1))
+        return fail(MOE_ERR_INVALID_ARG, "%s: bias overlaps scale or zeros", fn);
+    const int st = moe::launch_zero_point_bias((long)n, scale, zeros, bias, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 }  // extern "C"

@@ -193,3 +193,14 @@ def test_route_dispatch_validation():
     bad = moe.Dims(4, 256, 512, 8, 9, 128)
     assert L.moe_route_dispatch(ctypes.byref(bad), FAKE, FAKE, None, 1, FAKE, ctypes.byref(_dispatch()),
                                 None) == moe.ERR_UNSUPPORTED
+
+
+def test_zero_point_bias_validation():
+    L = moe.lib()
+    assert L.moe_zero_point_bias(-1, FAKE, FAKE, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_zero_point_bias(0, None, None, None, None) == moe.OK
+    assert L.moe_zero_point_bias(8, None, FAKE, FAKE + 4096, None) == moe.ERR_INVALID_ARG
+    assert L.moe_zero_point_bias(8, FAKE + 1, FAKE, FAKE + 4096, None) == moe.ERR_INVALID_ARG
+    assert L.moe_zero_point_bias(8, FAKE, FAKE + 4096, FAKE + 8, None) == moe.ERR_INVALID_ARG   # bias overlaps scale
+    assert "overlaps" in moe.last_error()
+    assert L.moe_zero_point_bias(8, FAKE + 4096, FAKE, FAKE + 4, None) == moe.ERR_INVALID_ARG   # bias overlaps zeros

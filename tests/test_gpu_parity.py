@@ -531,3 +531,75 @@ def test_topk_edge_cases(E, k, renorm):
     nan_ref = np.isnan(g_ref)
     assert np.array_equal(np.isnan(g), nan_ref)
     assert np.max(np.abs(g[~nan_ref] - g_ref[~nan_ref]), initial=0.0) <= 2e-6
+
+
+# ------------------------------------------------------ zero-point weights
+
+@pytest.mark.parametrize("n", [1, 7, 100003])
+def test_zero_point_bias_bit_exact(n):
+    """moe_zero_point_bias equals the oracle bit for bit over scales of every
+    finite fp16 class (subnormal, normal, negative, near the top of the range,
+    where z s overflows to an infinity) and zero points 0..255; entries past n
+    stay untouched; NaN in gives NaN out."""
+    rng = np.random.default_rng(n)
+    pats = rng.integers(0, 65536, size=n).astype(np.uint16)
+    pats[(pats & 0x7C00) == 0x7C00] &= 0xBFFF                  # no inf / NaN scales here
+    pats[: n // 2] = mi.f32_to_f16_bits(rng.uniform(0.005, 0.02, size=n // 2))
+    z = rng.integers(0, 256, size=n).astype(np.uint8)
+    ref = oracle.zero_point_bias(pats, z)
+    out = torch.full((n + 64,), 0x1234, dtype=torch.int16, device="cuda")
+    say(f"[run] zero_point_bias n={n}")
+    moe.zero_point_bias(to_dev(pats), to_dev(z), out[:n])
+    torch.cuda.synchronize()
+    got = to_host(out, np.uint16)
+    assert np.array_equal(got[:n], ref), f"{int((got[:n] != ref).sum())} of {n} differ"
+    assert np.all(got[n:] == 0x1234)
+    s_nan = to_dev(np.array([0x7E00, 0x7C00, 0xFC00], np.uint16))
+    z_nan = to_dev(np.array([3, 0, 0], np.uint8))
+    b_nan = torch.zeros(3, dtype=torch.int16, device="cuda")
+    moe.zero_point_bias(s_nan, z_nan, b_nan)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(to_host(b_nan, np.uint16).view(np.float16)))
+
+
+@pytest.mark.parametrize("name,bits,T", [("tiny", 4, 4), ("a3b", 2, 8), ("a3b", 4, 32)])
+def test_zero_point_weights_through_the_layer(name, bits, T):
+    """Zero-point weights (q - z) s: the biases moe_zero_point_bias makes on
+    the GPU equal the oracle's bit for bit, and the layer run on them matches
+    the oracle fed the oracle's biases (every FFN row, FFN tolerance; combine
+    bit-exact).  The biases here reach 15 s, several times those of the
+    scale-and-bias inputs, which loads the offset part of the exact-operand fold."""
+    L = layer(name, bits)
+    sh = L.shape
+    saved = [b.clone() for b in L.weights_d.bias]
+    try:
+        zs = {}
+        for i, m in enumerate(mi.MATRICES):
+            zs[m] = np.stack([mi.make_zero_points(sh, m, e, bits, seed=5) for e in range(sh.E)])
+            say(f"[run] zero-point biases {name} q{bits} {m}")
+            moe.zero_point_bias(L.weights_d.scale[i], to_dev(zs[m]), L.weights_d.bias[i])
+        torch.cuda.synchronize()
+        for i, m in enumerate(mi.MATRICES):
+            ref = oracle.zero_point_bias(to_host(L.weights_d.scale[i], np.uint16), zs[m])
+            assert np.array_equal(to_host(L.weights_d.bias[i], np.uint16), ref), m
+        xb, res = mi.make_activations(sh.H, T, 9)
+        say(f"[run] zero-point layer {name} q{bits} T={T}")
+        g = run_layer(L, xb, res)
+        check_topk(g, L)
+        check_permute(g, L)
+        ids = g["ids"].ravel()
+        used = sorted({int(e) for e in ids})
+        W = mi.make_expert_weights(sh, bits, L.seed, experts=used)
+        for m in mi.MATRICES:
+            for i, e in enumerate(W.experts):
+                W.bias[m][i] = oracle.zero_point_bias(W.scale[m][i], zs[m][int(e)])
+        P = T * sh.k
+        _, ys = oracle.expert_ffn(xb, ids, g["sorted_pairs"], W, sh.k)
+        max_rel, mae = tolerance_metrics(g["y_rows"], np.stack([ys[r] for r in range(P)]))
+        say(f"[ok] zero-point {name} q{bits} T={T}: FFN max_rel {max_rel:.2e} mae_norm {mae:.2e}")
+        assert max_rel <= 1e-2 and mae <= 1e-3, (max_rel, mae)
+        check_combine_exact(g, L, res)
+    finally:
+        for b, s in zip(L.weights_d.bias, saved):
+            b.copy_(s)
+        torch.cuda.synchronize()

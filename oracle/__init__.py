@@ -57,6 +57,8 @@ def lib():
         L.orc_expert_ffn_row.argtypes = [i32, i32, i32, P] + [P] * 9 + [i32, P, P, P]
         L.orc_expert_ffn_row.restype = None
         L.orc_combine.argtypes = [i32, i32, i32, P, P, P, P, P]; L.orc_combine.restype = None
+        L.orc_shared_gate.argtypes = [i32, i32, P, P, P]; L.orc_shared_gate.restype = None
+        L.orc_combine_shared.argtypes = [i32, i32, i32] + [P] * 7; L.orc_combine_shared.restype = None
         _lib = L
     return _lib
 
@@ -262,6 +264,32 @@ def combine(y_rows: np.ndarray, pair_to_row: np.ndarray, gates: np.ndarray, resi
     k = gates.shape[1]
     out = np.empty((T, H), dtype=np.uint16)
     lib().orc_combine(T, H, k, _p(y_rows), _p(p2r), _p(gates), _p(residual), _p(out))
+    return out
+
+
+def shared_gate(x_bits: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Sigmoid gate of the shared expert per token: float32 [T]."""
+    x_bits, w = _c(x_bits, np.uint16), _c(w, np.float32)
+    T, H = x_bits.shape
+    if w.shape != (H,):
+        raise ValueError("the gate weight has one entry per hidden unit")
+    out = np.empty(T, dtype=np.float32)
+    lib().orc_shared_gate(T, H, _p(x_bits), _p(w), _p(out))
+    return out
+
+
+def combine_shared(y_rows: np.ndarray, pair_to_row: np.ndarray, gates: np.ndarray, y_shared: np.ndarray,
+                   sgate: np.ndarray, residual: np.ndarray) -> np.ndarray:
+    """combine(), then + sgate[t] * y_shared[t] as one more float32 FMA, rounded once to bf16."""
+    y_rows, residual, y_shared = _c(y_rows, np.uint16), _c(residual, np.uint16), _c(y_shared, np.uint16)
+    p2r, gates, sgate = _c(pair_to_row, np.int32), _c(gates, np.float32), _c(sgate, np.float32)
+    T, H = residual.shape
+    k = gates.shape[1]
+    if y_shared.shape != (T, H) or sgate.shape != (T,):
+        raise ValueError("y_shared must be [T, H] and sgate [T]")
+    out = np.empty((T, H), dtype=np.uint16)
+    lib().orc_combine_shared(T, H, k, _p(y_rows), _p(p2r), _p(gates), _p(y_shared), _p(sgate), _p(residual),
+                             _p(out))
     return out
 
 

@@ -26,6 +26,9 @@
  *   expert FFN            Flash-MoE page sec. 3: fused SwiGLU between the
  *                         gate/up and down matvecs.
  *   combine               Flash-MoE page sec. 3: MoE combine + residual.
+ *   shared expert         Flash-MoE page sec. 3: combine + residual + sigmoid
+ *                         gate in one kernel (the gate read as that of an
+ *                         always-on shared expert).
  *   zero-point adapter    "Strata" page sec. 2.2 and the laptop page sec. 4.2:
  *                         (q - zero) scale groups, as bias = -zero scale.
  *
@@ -298,6 +301,35 @@ void orc_expert_ffn_row(int H, int I, int bits, const uint16_t* x,
 
 /* out[t,n] = residual[t,n] + sum_j g[t,j] * Y[row(t,j), n], accumulated in
  * float in j order with fused multiply-adds, then rounded to bf16. */
+/* Shared-expert gate (Flash-MoE page, sec. 3: the combine kernel also applies
+ * a sigmoid gate; read here as the gate of an always-on shared expert):
+ * gate[t] = 1 / (1 + exp(-L)), L = sum_h x[t][h] w[h] in double, rounded once. */
+void orc_shared_gate(int T, int H, const uint16_t* x, const float* w, float* gate) {
+    for (int t = 0; t < T; ++t) {
+        double L = 0.0;
+        for (int h = 0; h < H; ++h) L += (double)orc_bf16_to_f32(x[(size_t)t * H + h]) * (double)w[h];
+        gate[t] = (float)(1.0 / (1.0 + exp(-L)));
+    }
+}
+
+/* Combine with a shared expert: the routed chain of orc_combine, then one more
+ * float32 fused multiply-add of the shared row, rounded once to bf16:
+ *   acc = fmaf(sgate[t], y_shared[t][n], acc). */
+void orc_combine_shared(int T, int H, int k, const uint16_t* y_rows, const int32_t* pair_to_row,
+                        const float* gates, const uint16_t* y_shared, const float* sgate,
+                        const uint16_t* residual, uint16_t* out) {
+    for (int t = 0; t < T; ++t)
+        for (int n = 0; n < H; ++n) {
+            float acc = orc_bf16_to_f32(residual[(size_t)t * H + n]);
+            for (int j = 0; j < k; ++j) {
+                int row = pair_to_row[(size_t)t * k + j];
+                acc = fmaf(gates[(size_t)t * k + j], orc_bf16_to_f32(y_rows[(size_t)row * H + n]), acc);
+            }
+            acc = fmaf(sgate[t], orc_bf16_to_f32(y_shared[(size_t)t * H + n]), acc);
+            out[(size_t)t * H + n] = orc_f32_to_bf16(acc);
+        }
+}
+
 void orc_combine(int T, int H, int k, const uint16_t* y_rows, const int32_t* pair_to_row,
                  const float* gates, const uint16_t* residual, uint16_t* out) {
     for (int t = 0; t < T; ++t)

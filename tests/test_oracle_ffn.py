@@ -195,3 +195,56 @@ def test_layer_identity_experts_end_to_end(orc):
     got = _bf16_f64(out["out"])
     # one bf16 rounding of the sum plus float32 gate rounding (gates sum to 1 +- 4e-7)
     assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-6 * np.abs(y))
+
+
+def test_shared_gate_against_scipy_and_closed_forms(orc):
+    """Sigmoid gate of the shared expert: scipy's expit of numpy's float64 dot
+    product (to one float32 rounding), and closed forms: w = 0 gives 1/2 for
+    every token; L = ln 3 gives 3/4; a large |L| saturates to 0 or 1."""
+    from scipy.special import expit
+    rng = np.random.default_rng(61)
+    T, H = 5, 512
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = (rng.standard_normal(H) * 0.05).astype(np.float32)
+    got = orc.shared_gate(x, w)
+    L = _bf16_f64(x) @ w.astype(np.float64)
+    assert np.max(np.abs(got.astype(np.float64) - expit(L))) <= 2.0 ** -24
+    assert np.all(orc.shared_gate(x, np.zeros(H, np.float32)) == np.float32(0.5))
+    x1 = np.zeros((3, H), np.uint16)
+    x1[:, 0] = mi.f32_to_bf16_bits(np.array([1.0, 1.0, -1.0], np.float32))
+    for wv, want, tol in ((math.log(3.0), 0.75, 1e-7), (1000.0, 1.0, 0.0)):
+        w1 = np.zeros(H, np.float32)
+        w1[0] = wv
+        g = orc.shared_gate(x1, w1)
+        assert abs(float(g[0]) - want) <= tol and abs(float(g[1]) - want) <= tol
+        assert abs(float(g[2]) - (1.0 - want)) <= tol
+
+
+def test_combine_shared_closed_forms(orc):
+    """The shared row enters as one more float32 FMA after the routed picks:
+    a zero shared gate gives combine() bit for bit; with exact halves the result
+    is the float32 chain residual + Y/2 + Y/2 + Ys/2."""
+    rng = np.random.default_rng(62)
+    T, H, k = 3, 256, 2
+    res = mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    Y = mi.f32_to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32) * 100)
+    Ys = mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32) * 10)
+    p2r = np.arange(T * k, dtype=np.int32)
+    g = rng.random((T, k)).astype(np.float32)
+    base = orc.combine(Y, p2r, g, res)
+    assert np.array_equal(orc.combine_shared(Y, p2r, g, Ys, np.zeros(T, np.float32), res), base)
+    Yr = np.repeat(Y[::k], k, axis=0)
+    half = np.full((T, k), 0.5, np.float32)
+    out = orc.combine_shared(Yr, p2r, half, Ys, np.full(T, 0.5, np.float32), res)
+    r32 = _bf16_f64(res).astype(np.float32)
+    y32 = _bf16_f64(Y[::k]).astype(np.float32)
+    s32 = _bf16_f64(Ys).astype(np.float32)
+    acc = (r32 + np.float32(0.5) * y32).astype(np.float32)
+    acc = (acc + np.float32(0.5) * y32).astype(np.float32)
+    acc = (acc + np.float32(0.5) * s32).astype(np.float32)
+    assert np.array_equal(out, mi.f32_to_bf16_bits(acc))
+    # the shared gate is per token: gate 1 on token 0 only adds Ys[0] to row 0
+    sg = np.array([1.0, 0.0, 0.0], np.float32)
+    one = orc.combine_shared(Y, p2r, g, Ys, sg, res)
+    assert np.array_equal(one[1:], base[1:])
+    assert not np.array_equal(one[0], base[0])

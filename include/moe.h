@@ -320,6 +320,28 @@ int moe_expert_ffn_fused(const moe_dims* dims, int bits, const uint16_t* x, cons
 int moe_combine(const moe_dims* dims, const uint16_t* y_rows, const int32_t* pair_to_row,
                 const float* topk_w, const uint16_t* residual, uint16_t* out, void* stream);
 
+/* Combine + residual with a shared expert (step 6 with the sigmoid gate of the
+ * Flash-MoE page, sec. 3, which lists combine, residual and a sigmoid gate as
+ * one fused kernel; the gate is read as that of an always-on shared expert):
+ *   L_t = x[t] . shared_gate_w  (float32; a fixed summation order, the same on
+ *         every call), s_t = 1 / (1 + expf(-L_t)),
+ *   acc = residual[t][n];  for j = 0..k-1 in order:
+ *       acc = fmaf(topk_w[t][j], y_rows[pair_to_row[t*k+j]][n], acc)
+ *   acc = fmaf(s_t, y_shared[t][n], acc);   out[t][n] = bf16(acc) (RNE).
+ *   y_shared        bf16 [T][H]: the shared expert's FFN output per token, e.g.
+ *                   moe_expert_ffn_* run with E = 1, k = 1 on a work list of
+ *                   every token (moe_permute of all-zero ids).
+ *   x               bf16 [T][H]: the layer input the router saw.
+ *   shared_gate_w   fp32 [H]: the gate's weight row.
+ *   shared_gate_out fp32 [T] or NULL: receives s_t as used.
+ * Other arguments, alignment and errors as for moe_combine; y_shared, x and
+ * shared_gate_w 16-byte aligned, shared_gate_out 4-byte aligned.  out may be
+ * the same buffer as residual. */
+int moe_combine_shared(const moe_dims* dims, const uint16_t* y_rows, const int32_t* pair_to_row,
+                       const float* topk_w, const uint16_t* y_shared, const uint16_t* x,
+                       const float* shared_gate_w, const uint16_t* residual, uint16_t* out,
+                       float* shared_gate_out, void* stream);
+
 /* Weight-format adapter (run once when weights are loaded; not a step of the
  * layer).  Zero-point groups, w = (q - z) s ("Strata" page, sec. 2.2: each
  * group of 128 weights shares one scale and one zero point; the laptop page,

@@ -41,7 +41,7 @@ GROUP = 128
 MATRICES = ("gate", "up", "down")
 
 # tags of the independent random streams
-_TAG_X, _TAG_RES, _TAG_WR, _TAG_PERM, _TAG_Q, _TAG_S, _TAG_B, _TAG_Z = 1, 2, 3, 4, 5, 6, 7, 8
+_TAG_X, _TAG_RES, _TAG_WR, _TAG_PERM, _TAG_Q, _TAG_S, _TAG_B, _TAG_Z, _TAG_SG = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 @dataclasses.dataclass(frozen=True)
@@ -230,6 +230,19 @@ def make_zero_points(shape: LayerShape, m: str, e: int, bits: int = 4, seed: int
                                                                     dtype=np.uint8)
 
 
+def make_shared_expert(shape: LayerShape, bits: int = 4, seed: int = 0, I: Optional[int] = None):
+    """An always-on shared expert for `shape`: (its one-expert LayerShape of
+    intermediate size I, {m: (q, scale, bias)} drawn like a routed expert's but
+    from streams keyed past the routed experts, its gate's weight row fp32 [H]
+    ~ N(0, 0.02^2), the router's scale, so that x . w spreads the sigmoid over
+    (0, 1))."""
+    one = dataclasses.replace(shape, name=shape.name + "_shared", E=1, k=1, I=shape.I if I is None else int(I),
+                              n_resident=1)
+    mats = {m: _draw_expert_matrix(one, m, shape.E, bits, seed) for m in MATRICES}
+    w = (_rng(seed, _TAG_SG, shape.H).standard_normal(shape.H) * 0.02).astype(np.float32)
+    return one, mats, w
+
+
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Pack integer codes [..., K] into bytes along the last axis (format above)."""
     codes = np.asarray(codes, dtype=np.uint8)
@@ -246,6 +259,6 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
 __all__ = [
     "GROUP", "MATRICES", "LayerShape", "CONFIGS", "CONFIG_ORDER", "ExpertWeights",
     "make_activations", "make_router", "make_slot_table", "make_expert_weights",
-    "iter_expert_weights", "make_zero_points", "expert_popularity", "popularity_order", "matrix_dims",
+    "iter_expert_weights", "make_zero_points", "make_shared_expert", "expert_popularity", "popularity_order", "matrix_dims",
     "pack_codes", "f32_to_bf16_bits", "f32_to_f16_bits",
 ]

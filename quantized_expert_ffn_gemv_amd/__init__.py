@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute", "moe_work_list_capacity",
     "moe_route_dispatch",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_expert_ffn_fused",
-    "moe_combine",
+    "moe_combine", "moe_combine_shared",
     "moe_zero_point_bias",
 )
 
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, Wp, ctypes.c_int, P, sz, P, P]
     L.moe_expert_ffn_fused.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P, P, P]
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
+    L.moe_combine_shared.argtypes = [Dp, P, P, P, P, P, P, P, P, P, P]
     L.moe_zero_point_bias.argtypes = [ctypes.c_int64, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = ctypes.c_int
@@ -273,6 +274,14 @@ def combine(d: Dims, y_rows, pair_to_row, topk_w, residual, out, stream=None):
                              _ptr(residual), _ptr(out), _stream(stream)))
 
 
+def combine_shared(d: Dims, y_rows, pair_to_row, topk_w, y_shared, x, shared_gate_w, residual, out,
+                   shared_gate_out=None, stream=None):
+    """moe_combine_shared: combine() plus sigmoid(x . shared_gate_w) * y_shared."""
+    _check(lib().moe_combine_shared(ctypes.byref(d), _ptr(y_rows), _ptr(pair_to_row), _ptr(topk_w), _ptr(y_shared),
+                                    _ptr(x), _ptr(shared_gate_w), _ptr(residual), _ptr(out), _ptr(shared_gate_out),
+                                    _stream(stream)))
+
+
 def zero_point_bias(scale, zeros, bias, stream=None):
     """moe_zero_point_bias: bias = fp16(-(zeros * scale)) per group, turning
     zero-point weights (q - z) s into this library's q s + b.  scale and bias
@@ -283,12 +292,12 @@ def zero_point_bias(scale, zeros, bias, stream=None):
     _check(lib().moe_zero_point_bias(n, _ptr(scale), _ptr(zeros), _ptr(bias), _stream(stream)))
 
 
-from .layer import LayerBuffers, layer_forward  # noqa: E402  (orchestration of the calls above)
+from .layer import LayerBuffers, SharedBuffers, SharedExpert, layer_forward  # noqa: E402  (orchestration of the calls above)
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
-    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "combine", "zero_point_bias", "LayerBuffers", "layer_forward", "EXPORTS",
+    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "combine", "combine_shared", "zero_point_bias", "LayerBuffers", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
     "group_major", "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

@@ -410,6 +410,29 @@ int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* pair_t
     return ok();
 }
 
+int moe_combine_shared(const moe_dims* d, const uint16_t* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                       const uint16_t* y_shared, const uint16_t* x, const float* shared_gate_w,
+                       const uint16_t* residual, uint16_t* out, float* shared_gate_out, void* stream) {
+    const char* fn = "moe_combine_shared";
+    int st = check_dims(fn, d, true, false);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(y_rows, 16);
+    REQUIRE_PTR(pair_to_row, 4);
+    REQUIRE_PTR(topk_w, 4);
+    REQUIRE_PTR(y_shared, 16);
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(shared_gate_w, 16);
+    REQUIRE_PTR(residual, 16);
+    REQUIRE_PTR(out, 16);
+    if (shared_gate_out && !aligned(shared_gate_out, 4))
+        return fail(MOE_ERR_INVALID_ARG, "%s: shared_gate_out misaligned", fn);
+    st = moe::launch_combine_shared(*d, y_rows, pair_to_row, topk_w, y_shared, x, shared_gate_w, residual, out,
+                                    shared_gate_out, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 int moe_zero_point_bias(int64_t n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias, void* stream) {
     const char* fn = "moe_zero_point_bias";
     if (n < 0) return fail(MOE_ERR_INVALID_ARG, "%s: n = %lld is negative", fn, (long long)n);

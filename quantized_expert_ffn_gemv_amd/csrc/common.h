@@ -203,6 +203,9 @@ int launch_down_dec(const FfnArgs& a, hipStream_t s);
 int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s);
 int launch_combine(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,
                    const uint16_t* residual, uint16_t* out, hipStream_t s);
+int launch_combine_shared(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,
+                          const uint16_t* ys, const uint16_t* x, const float* w, const uint16_t* residual,
+                          uint16_t* out, float* gate_out, hipStream_t s);
 int launch_zero_point_bias(long n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias, hipStream_t s);
 
 }  // namespace moe

@@ -9,6 +9,12 @@ C calls on one stream with no allocation and no host synchronisation:
 ``fused=False`` makes the same step from the separate routing calls and the
 two-launch FFN (expert_ffn_q{4,2}).
 
+With a shared expert (``SharedExpert``: one more quantised FFN that every token
+uses, scaled by a per-token sigmoid gate), its FFN runs on a second stream
+while the routing and the routed FFN run, and ``combine_shared`` replaces
+``combine``.  Its work list (every token on expert 0 of a one-expert layer)
+depends only on T and is built once, when ``SharedBuffers`` are allocated.
+
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
 from __future__ import annotations
@@ -19,8 +25,8 @@ from typing import Optional
 import torch
 
 from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, FFN_SYNC_INTS, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine,
-               expert_ffn_fused, expert_ffn_q2, expert_ffn_q4, permute, route_dispatch, route_topk, slot_lookup,
-               work_list_capacity, workspace_bytes)
+               combine_shared, dims, expert_ffn_fused, expert_ffn_q2, expert_ffn_q4, permute, route_dispatch,
+               route_topk, slot_lookup, work_list_capacity, workspace_bytes)
 
 
 @dataclass
@@ -75,13 +81,53 @@ class LayerBuffers:
         )
 
 
+@dataclass
+class SharedExpert:
+    """An always-on shared expert: a quantised FFN of intermediate size I (one
+    expert, the library's weight format) and its sigmoid gate's weight row."""
+    weights: QWeights             # one expert: q[m] [1][K/128][N][16*bits], scale / bias [1][N][K/128]
+    gate_w: torch.Tensor          # float32 [H]
+    I: int
+
+
+@dataclass
+class SharedBuffers:
+    d: Dims                       # (T, H, I_shared, E = 1, k = 1)
+    buf: LayerBuffers             # the one-expert layer's work list, workspace, rows and counters
+    zeros: torch.Tensor           # int32 [T]: every token picks expert 0
+    gate_out: torch.Tensor        # float32 [T]: the gate values the last combine used
+    side: torch.cuda.Stream       # the shared FFN's stream (default priority)
+
+    @staticmethod
+    def allocate(T: int, H: int, I: int, bits: int = 4, algo: int = ALGO_AUTO, device="cuda") -> "SharedBuffers":
+        d = dims(T, H, I, 1, 1)
+        buf = LayerBuffers.allocate(d, bits, algo, device)
+        zeros = torch.zeros((max(T, 1),), dtype=torch.int32, device=device)
+        permute(d, zeros, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active, buf.n_active,
+                buf.work_list, buf.n_work)
+        return SharedBuffers(d=d, buf=buf, zeros=zeros,
+                             gate_out=torch.empty((max(T, 1),), dtype=torch.float32, device=device),
+                             side=torch.cuda.Stream(device=device))
+
+
 def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
                   router_bias: Optional[torch.Tensor], weights: QWeights,
                   slot_of_expert: torch.Tensor, n_slots: int, residual: torch.Tensor,
                   out: torch.Tensor, algo: int = ALGO_AUTO, renormalize: bool = True,
-                  host_doorbell=None, last_use=None, step: int = 0, stream=None, fused: bool = True) -> None:
-    """Enqueue one layer step; `out` may be `residual`."""
+                  host_doorbell=None, last_use=None, step: int = 0, stream=None, fused: bool = True,
+                  shared: Optional[SharedExpert] = None, shared_buf: Optional[SharedBuffers] = None) -> None:
+    """Enqueue one layer step; `out` may be `residual`.  With `shared` (and its
+    `shared_buf`), the shared expert's FFN runs on shared_buf.side, overlapped
+    with the routing and the routed FFN."""
     d = buf.d
+    main = torch.cuda.current_stream() if stream is None else stream
+    if shared is not None:
+        sb = shared_buf
+        if sb is None or sb.d.T != d.T or sb.d.H != d.H or sb.d.I != shared.I:
+            raise ValueError("shared expert needs SharedBuffers allocated for this T, H and its I")
+        sb.side.wait_stream(main)                       # x (and the buffers) are ready
+        expert_ffn_fused(sb.d, shared.weights.bits, x, sb.buf.work_list, sb.buf.n_work, shared.weights,
+                         sb.buf.workspace, sb.buf.y_rows, sb.buf.ffn_sync, algo, sb.side)
     if fused:
         route_dispatch(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w,
                        slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets,
@@ -99,4 +145,9 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
     else:
         ffn = expert_ffn_q4 if weights.bits == 4 else expert_ffn_q2
         ffn(d, x, buf.work_list, buf.n_work, weights, buf.y_rows, algo, buf.workspace, None, stream)
-    combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)
+    if shared is None:
+        combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)
+        return
+    main.wait_stream(sb.side)
+    combine_shared(d, buf.y_rows, buf.pair_to_row, buf.topk_w, sb.buf.y_rows, x, shared.gate_w, residual, out,
+                   sb.gate_out, stream)

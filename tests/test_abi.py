@@ -204,3 +204,19 @@ def test_zero_point_bias_validation():
     assert L.moe_zero_point_bias(8, FAKE, FAKE + 4096, FAKE + 8, None) == moe.ERR_INVALID_ARG   # bias overlaps scale
     assert "overlaps" in moe.last_error()
     assert L.moe_zero_point_bias(8, FAKE + 4096, FAKE, FAKE + 4, None) == moe.ERR_INVALID_ARG   # bias overlaps zeros
+
+
+def test_combine_shared_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    args = [FAKE] * 8
+    for i in range(8):
+        bad = list(args)
+        bad[i] = None
+        assert L.moe_combine_shared(ctypes.byref(d), *bad, None, None) == moe.ERR_INVALID_ARG
+    bad = list(args)
+    bad[4] = MISALIGNED                                                  # x
+    assert L.moe_combine_shared(ctypes.byref(d), *bad, None, None) == moe.ERR_INVALID_ARG
+    assert L.moe_combine_shared(ctypes.byref(d), *args, FAKE + 1, None) == moe.ERR_INVALID_ARG
+    d0 = moe.dims(0, 256, 512, 8, 2)
+    assert L.moe_combine_shared(ctypes.byref(d0), *([None] * 9), None) == moe.OK

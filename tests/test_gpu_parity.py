@@ -603,3 +603,56 @@ def test_zero_point_weights_through_the_layer(name, bits, T):
         for b, s in zip(L.weights_d.bias, saved):
             b.copy_(s)
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ shared expert
+
+def _upload_shared(mats, bits, gate_w, I):
+    q, s, b = [], [], []
+    for m in mi.MATRICES:
+        qq, ss, bb = mats[m]
+        q.append(torch.from_numpy(moe.group_major(qq, bits)[None].copy()).cuda())
+        s.append(torch.from_numpy(ss.view(np.int16)[None].copy()).cuda())
+        b.append(torch.from_numpy(bb.view(np.int16)[None].copy()).cuda())
+    return moe.SharedExpert(moe.QWeights(bits, q, s, b), to_dev(gate_w), I)
+
+
+@pytest.mark.parametrize("name,bits,T,i_mul", [("tiny", 4, 4, 2), ("a3b", 4, 32, 1), ("a3b", 2, 8, 1),
+                                               ("e64", 4, 8, 1)])
+def test_shared_expert_layer(name, bits, T, i_mul):
+    """A layer step with an always-on shared expert (its FFN on a second
+    stream): the shared rows match the oracle's FFN (FFN tolerance), the gate
+    values the oracle's sigmoid (logit bound as for the router), and the output
+    is the oracle's combine_shared of the GPU's own rows and gates bit for bit;
+    two steps in a row through the same buffers."""
+    L = layer(name, bits)
+    sh = L.shape
+    one, mats, gw = mi.make_shared_expert(sh, bits, seed=4, I=sh.I * i_mul)
+    shared = _upload_shared(mats, bits, gw, one.I)
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+    buf = moe.LayerBuffers.allocate(d, bits)
+    sbuf = moe.SharedBuffers.allocate(T, sh.H, one.I, bits)
+    for seed in (13, 14):
+        xb, res = mi.make_activations(sh.H, T, seed)
+        x_d, r_d = to_dev(xb), to_dev(res)
+        out_d = torch.empty_like(r_d)
+        say(f"[run] shared expert {name} q{bits} T={T} I_shared={one.I} seed={seed}")
+        moe.layer_forward(buf, x_d, L.Wr_d, L.bias_d, L.weights_d, L.table_d, sh.E, r_d, out_d,
+                          shared=shared, shared_buf=sbuf)
+        torch.cuda.synchronize()
+        P = T * sh.k
+        g = dict(logits=to_host(buf.logits), ids=to_host(buf.topk_ids), gates=to_host(buf.topk_w))
+        check_topk(g, L)
+        ys = to_host(sbuf.buf.y_rows, np.uint16)[:T]
+        ref_ys = np.stack([oracle.expert_ffn_row(xb[t], mats, bits)[1] for t in range(T)])
+        max_rel, mae = tolerance_metrics(ys, ref_ys)
+        assert max_rel <= 1e-2 and mae <= 1e-3, (max_rel, mae)
+        sg = to_host(sbuf.gate_out)[:T].astype(np.float64)
+        ref_sg = oracle.shared_gate(xb, gw).astype(np.float64)
+        xabs = np.abs((xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        bound = 0.25 * 1e-5 * (xabs @ np.abs(gw.astype(np.float64))) + 4e-7
+        assert np.all(np.abs(sg - ref_sg) <= bound), np.max(np.abs(sg - ref_sg) / bound)
+        ref_out = oracle.combine_shared(to_host(buf.y_rows, np.uint16)[:P], to_host(buf.pair_to_row)[:P],
+                                        g["gates"], ys, to_host(sbuf.gate_out)[:T], res)
+        assert np.array_equal(to_host(out_d, np.uint16), ref_out)
+        say(f"[ok] shared expert {name} T={T}: FFN max_rel {max_rel:.2e} mae_norm {mae:.2e}")

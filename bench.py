@@ -68,6 +68,8 @@ def parse():
                     help="timed steps as eager library calls, or as replays of one captured HIP graph per weight "
                          "set (each replays every kernel of the step; measured slower here)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared-expert", action="store_true",
+                    help="skip the extra measurement of the step with a shared expert")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed steps of the T=4096 prefill layer on the grouped GEMM (0 = skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -99,16 +101,33 @@ def upload_layer(shape, bits, seed, torch, mi, moe):
                 table=dev(table), w=moe.QWeights(bits, q, s, b))
 
 
-class Runner:
-    """Enqueues layer steps over rotating weight sets; optional events around the FFN halves."""
+def upload_shared(shape, bits, seed, torch, mi, moe):
+    """An always-on shared expert of the routed experts' size, with its gate row."""
+    one, mats, gate_w = mi.make_shared_expert(shape, bits, seed)
+    q, s, b = [], [], []
+    for m in mi.MATRICES:
+        qq, ss, bb = mats[m]
+        q.append(torch.from_numpy(moe.group_major(qq, bits)[None].copy()).cuda())
+        s.append(torch.from_numpy(ss.view("int16")[None].copy()).cuda())
+        b.append(torch.from_numpy(bb.view("int16")[None].copy()).cuda())
+    return moe.SharedExpert(moe.QWeights(bits, q, s, b), torch.from_numpy(gate_w).cuda(), one.I)
 
-    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False):
+
+class Runner:
+    """Enqueues layer steps over rotating weight sets; optional events around the
+    FFN halves; optionally a shared expert per weight set (its FFN first, its
+    gate in the combine)."""
+
+    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False, shared=None):
         self.torch, self.mi, self.moe = torch, mi, moe
         self.shape, self.layers, self.T, self.algo = shape, layers, T, algo
         self.fused_ffn = fused_ffn
         sh = shape
         self.d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
         self.buf = moe.LayerBuffers.allocate(self.d, layers[0]["w"].bits, algo)
+        self.shared = shared
+        if shared is not None:
+            self.sbuf = moe.SharedBuffers.allocate(T, sh.H, shared[0].I, layers[0]["w"].bits, algo)
         self.x, self.res = [], []
         for li in range(len(layers)):
             xb, rb = mi.make_activations(sh.H, T, seed=1000 + li)
@@ -121,6 +140,10 @@ class Runner:
         L = self.layers[i % len(self.layers)]
         x, res = self.x[i % len(self.layers)], self.res[i % len(self.layers)]
         bits = L["w"].bits
+        if self.shared is not None:
+            S, sb = self.shared[i % len(self.shared)], self.sbuf
+            moe.expert_ffn_fused(sb.d, bits, x, sb.buf.work_list, sb.buf.n_work, S.weights, sb.buf.workspace,
+                                 sb.buf.y_rows, sb.buf.ffn_sync, self.algo)
         moe.route_dispatch(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w, L["table"],
                            self.shape.E, b.pair_slot, b.miss, b.n_miss, b.counts, b.offsets, b.sorted_pairs,
                            b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work, sync=b.sync)
@@ -138,7 +161,11 @@ class Runner:
             moe.expert_down(d, bits, b.work_list, b.n_work, L["w"], b.workspace, b.y_rows, self.algo)
         if ev is not None:
             ev[2].record()
-        moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
+        if self.shared is None:
+            moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
+        else:
+            moe.combine_shared(d, b.y_rows, b.pair_to_row, b.topk_w, sb.buf.y_rows, x, S.gate_w, res, self.out,
+                               sb.gate_out)
 
     def experts_used(self):
         """Distinct experts per weight set for this batch (read back once, untimed)."""
@@ -325,7 +352,7 @@ def summarize_counters(fetch_dir, write_dir, copy_mib, algo="auto"):
                sources=list(k["sources"]), source_sha256_16=source_hash(k["sources"]),
                command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir> -o run --output-format csv "
                        "-- python3 bench.py --steps 20 --warmup 5 --sweep=none --no-cpu-baseline --prefill-steps 0 "
-                       f"--copy-calib-mib {copy_mib}")
+                       f"--no-shared-expert --copy-calib-mib {copy_mib}")
     with open(TRAFFIC_PATH, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -460,6 +487,25 @@ def main():
     warm = measure(args.tokens, max(args.steps // 2, 10), max(args.warmup // 2, 2), layer_sets=layers[:1])
     log(f"[bench] warm (one weight set) T={args.tokens}: {warm['tokens_per_s']:.0f} tokens/s")
 
+    shared_run = None
+    if not args.no_shared_expert:
+        # the same step with an always-on shared expert (routed experts' size):
+        # its FFN launch first, its sigmoid gate fused into the combine
+        shared_sets = [upload_shared(shape, bits, li, torch, mi, moe) for li in range(len(layers))]
+        rs = Runner(torch, mi, moe, shape, layers, args.tokens, algo, fused_ffn=fused, shared=shared_sets)
+        rs.experts_used()
+        n_sh = max(args.steps // 2, 10)
+        sh_ms, _, _, _ = rs.timed(n_sh, max(args.warmup // 2, 2), with_events=False)
+        shared_run = dict(I_shared=shared_sets[0].I, tokens_per_s=round(args.tokens * n_sh / (sh_ms / 1e3), 1),
+                          ms_per_step=round(sh_ms / n_sh, 5),
+                          added_us_per_step=round((sh_ms / n_sh - main_run["ms_per_step"]) * 1e3, 2),
+                          shared_weight_bytes=shape.bytes_per_expert(bits),
+                          note="shared expert FFN as its own launch before the routing; sigmoid gate fused "
+                               "into the combine")
+        log(f"[bench] with a shared expert T={args.tokens}: {shared_run['tokens_per_s']:.0f} tokens/s "
+            f"(+{shared_run['added_us_per_step']} us per step)")
+        del rs, shared_sets
+
     prefill = None
     if args.prefill_steps > 0:
         prefill = measure_prefill(torch, mi, moe, args.prefill_steps, 3)
@@ -539,6 +585,7 @@ def main():
         "warm_one_weight_set": {"tokens_per_s": round(warm["tokens_per_s"], 1),
                                 "ms_per_step": round(warm["ms_per_step"], 5),
                                 "ffn_GBps": round(warm["ffn_GBps"], 1)},
+        "shared_expert": shared_run,
         "prefill": prefill,
         "context_not_comparable": CONTEXT,
     }

@@ -10,10 +10,11 @@ C calls on one stream with no allocation and no host synchronisation:
 two-launch FFN (expert_ffn_q{4,2}).
 
 With a shared expert (``SharedExpert``: one more quantised FFN that every token
-uses, scaled by a per-token sigmoid gate), its FFN runs on a second stream
-while the routing and the routed FFN run, and ``combine_shared`` replaces
-``combine``.  Its work list (every token on expert 0 of a one-expert layer)
-depends only on T and is built once, when ``SharedBuffers`` are allocated.
+uses, scaled by a per-token sigmoid gate), its FFN runs first, on the same
+stream, and ``combine_shared`` replaces ``combine``.  Its work list (every token
+on expert 0 of a one-expert layer) depends only on T and is built once, when
+``SharedBuffers`` are allocated.  (A second stream measured slower here: the
+cross-stream event wait held the host for the whole step.)
 
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
@@ -96,7 +97,6 @@ class SharedBuffers:
     buf: LayerBuffers             # the one-expert layer's work list, workspace, rows and counters
     zeros: torch.Tensor           # int32 [T]: every token picks expert 0
     gate_out: torch.Tensor        # float32 [T]: the gate values the last combine used
-    side: torch.cuda.Stream       # the shared FFN's stream (default priority)
 
     @staticmethod
     def allocate(T: int, H: int, I: int, bits: int = 4, algo: int = ALGO_AUTO, device="cuda") -> "SharedBuffers":
@@ -106,8 +106,7 @@ class SharedBuffers:
         permute(d, zeros, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active, buf.n_active,
                 buf.work_list, buf.n_work)
         return SharedBuffers(d=d, buf=buf, zeros=zeros,
-                             gate_out=torch.empty((max(T, 1),), dtype=torch.float32, device=device),
-                             side=torch.cuda.Stream(device=device))
+                             gate_out=torch.empty((max(T, 1),), dtype=torch.float32, device=device))
 
 
 def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
@@ -117,17 +116,15 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
                   host_doorbell=None, last_use=None, step: int = 0, stream=None, fused: bool = True,
                   shared: Optional[SharedExpert] = None, shared_buf: Optional[SharedBuffers] = None) -> None:
     """Enqueue one layer step; `out` may be `residual`.  With `shared` (and its
-    `shared_buf`), the shared expert's FFN runs on shared_buf.side, overlapped
-    with the routing and the routed FFN."""
+    `shared_buf`), the shared expert's FFN runs first and the combine adds its
+    gated rows."""
     d = buf.d
-    main = torch.cuda.current_stream() if stream is None else stream
     if shared is not None:
         sb = shared_buf
         if sb is None or sb.d.T != d.T or sb.d.H != d.H or sb.d.I != shared.I:
             raise ValueError("shared expert needs SharedBuffers allocated for this T, H and its I")
-        sb.side.wait_stream(main)                       # x (and the buffers) are ready
         expert_ffn_fused(sb.d, shared.weights.bits, x, sb.buf.work_list, sb.buf.n_work, shared.weights,
-                         sb.buf.workspace, sb.buf.y_rows, sb.buf.ffn_sync, algo, sb.side)
+                         sb.buf.workspace, sb.buf.y_rows, sb.buf.ffn_sync, algo, stream)
     if fused:
         route_dispatch(d, x, w_router, router_bias, renormalize, buf.logits, buf.topk_ids, buf.topk_w,
                        slot_of_expert, n_slots, buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets,
@@ -148,6 +145,5 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
     if shared is None:
         combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)
         return
-    main.wait_stream(sb.side)
     combine_shared(d, buf.y_rows, buf.pair_to_row, buf.topk_w, sb.buf.y_rows, x, shared.gate_w, residual, out,
                    sb.gate_out, stream)

@@ -620,8 +620,8 @@ def _upload_shared(mats, bits, gate_w, I):
 @pytest.mark.parametrize("name,bits,T,i_mul", [("tiny", 4, 4, 2), ("a3b", 4, 32, 1), ("a3b", 2, 8, 1),
                                                ("e64", 4, 8, 1)])
 def test_shared_expert_layer(name, bits, T, i_mul):
-    """A layer step with an always-on shared expert (its FFN on a second
-    stream): the shared rows match the oracle's FFN (FFN tolerance), the gate
+    """A layer step with an always-on shared expert (its FFN a launch of its
+    own): the shared rows match the oracle's FFN (FFN tolerance), the gate
     values the oracle's sigmoid (logit bound as for the router), and the output
     is the oracle's combine_shared of the GPU's own rows and gates bit for bit;
     two steps in a row through the same buffers."""

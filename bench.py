@@ -82,35 +82,31 @@ def parse():
 
 
 def upload_layer(shape, bits, seed, torch, mi, moe):
+    """One weight set: the E routed experts, then an always-on shared expert of
+    the same size as expert E of the same arrays (`w` views the routed ones;
+    `shared` holds the shared expert both ways and its gate row)."""
     Wr, bias = mi.make_router(shape, seed)
     table = mi.make_slot_table(shape, seed)
+    E = shape.E
     q, s, b = [], [], []
     for m in mi.MATRICES:
         N, K = mi.matrix_dims(shape, m)
-        q.append(torch.empty((shape.E, K // 128, N, 16 * bits), dtype=torch.uint8, device="cuda"))
-        s.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device="cuda"))
-        b.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device="cuda"))
-    for e, mats in mi.iter_expert_weights(shape, bits, seed):
+        q.append(torch.empty((E + 1, K // 128, N, 16 * bits), dtype=torch.uint8, device="cuda"))
+        s.append(torch.empty((E + 1, N, K // 128), dtype=torch.int16, device="cuda"))
+        b.append(torch.empty((E + 1, N, K // 128), dtype=torch.int16, device="cuda"))
+    one, shared_mats, gate_w = mi.make_shared_expert(shape, bits, seed)
+    for e, mats in list(mi.iter_expert_weights(shape, bits, seed)) + [(E, shared_mats)]:
         for i, m in enumerate(mi.MATRICES):
             qq, ss, bb = mats[m]
             q[i][e].copy_(torch.from_numpy(moe.group_major(qq, bits)))
             s[i][e].copy_(torch.from_numpy(ss.view("int16")))
             b[i][e].copy_(torch.from_numpy(bb.view("int16")))
     dev = lambda a: torch.from_numpy(a).cuda()
+    head = lambda ts, lo, hi: [t[lo:hi] for t in ts]
+    shared = moe.SharedExpert(moe.QWeights(bits, head(q, E, E + 1), head(s, E, E + 1), head(b, E, E + 1)),
+                              dev(gate_w), one.I, fused_weights=moe.QWeights(bits, q, s, b))
     return dict(Wr_np=Wr, bias_np=bias, table_np=table, Wr=dev(Wr), bias=None if bias is None else dev(bias),
-                table=dev(table), w=moe.QWeights(bits, q, s, b))
-
-
-def upload_shared(shape, bits, seed, torch, mi, moe):
-    """An always-on shared expert of the routed experts' size, with its gate row."""
-    one, mats, gate_w = mi.make_shared_expert(shape, bits, seed)
-    q, s, b = [], [], []
-    for m in mi.MATRICES:
-        qq, ss, bb = mats[m]
-        q.append(torch.from_numpy(moe.group_major(qq, bits)[None].copy()).cuda())
-        s.append(torch.from_numpy(ss.view("int16")[None].copy()).cuda())
-        b.append(torch.from_numpy(bb.view("int16")[None].copy()).cuda())
-    return moe.SharedExpert(moe.QWeights(bits, q, s, b), torch.from_numpy(gate_w).cuda(), one.I)
+                table=dev(table), w=moe.QWeights(bits, head(q, 0, E), head(s, 0, E), head(b, 0, E)), shared=shared)
 
 
 class Runner:
@@ -118,14 +114,15 @@ class Runner:
     FFN halves; optionally a shared expert per weight set (its FFN first, its
     gate in the combine)."""
 
-    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False, shared=None):
+    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False, shared=None, one_launch=True):
         self.torch, self.mi, self.moe = torch, mi, moe
         self.shape, self.layers, self.T, self.algo = shape, layers, T, algo
         self.fused_ffn = fused_ffn
         sh = shape
         self.d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
-        self.buf = moe.LayerBuffers.allocate(self.d, layers[0]["w"].bits, algo)
         self.shared = shared
+        self.one_launch = shared is not None and one_launch and fused_ffn
+        self.buf = moe.LayerBuffers.allocate(self.d, layers[0]["w"].bits, algo, shared_rows=self.one_launch)
         if shared is not None:
             self.sbuf = moe.SharedBuffers.allocate(T, sh.H, shared[0].I, layers[0]["w"].bits, algo)
         self.x, self.res = [], []
@@ -142,14 +139,20 @@ class Runner:
         bits = L["w"].bits
         if self.shared is not None:
             S, sb = self.shared[i % len(self.shared)], self.sbuf
-            moe.expert_ffn_fused(sb.d, bits, x, sb.buf.work_list, sb.buf.n_work, S.weights, sb.buf.workspace,
-                                 sb.buf.y_rows, sb.buf.ffn_sync, self.algo)
+            if not self.one_launch:
+                moe.expert_ffn_fused(sb.d, bits, x, sb.buf.work_list, sb.buf.n_work, S.weights, sb.buf.workspace,
+                                     sb.buf.y_rows, sb.buf.ffn_sync, self.algo)
         moe.route_dispatch(d, x, L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w, L["table"],
                            self.shape.E, b.pair_slot, b.miss, b.n_miss, b.counts, b.offsets, b.sorted_pairs,
                            b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work, sync=b.sync)
         if ev is not None:
             ev[0].record()
-        if self.fused_ffn:
+        if self.one_launch:
+            moe.expert_ffn_fused_shared(d, bits, x, b.work_list, b.n_work, S.fused_weights, b.workspace, b.y_rows,
+                                        b.ffn_sync, self.algo)
+            if ev is not None:
+                ev[1].record()
+        elif self.fused_ffn:
             moe.expert_ffn_fused(d, bits, x, b.work_list, b.n_work, L["w"], b.workspace, b.y_rows, b.ffn_sync,
                                  self.algo)
             if ev is not None:
@@ -164,8 +167,9 @@ class Runner:
         if self.shared is None:
             moe.combine(d, b.y_rows, b.pair_to_row, b.topk_w, res, self.out)
         else:
-            moe.combine_shared(d, b.y_rows, b.pair_to_row, b.topk_w, sb.buf.y_rows, x, S.gate_w, res, self.out,
-                               sb.gate_out)
+            T, k = self.T, self.shape.k
+            ys = b.y_rows[T * k: T * k + T] if self.one_launch else sb.buf.y_rows
+            moe.combine_shared(d, b.y_rows, b.pair_to_row, b.topk_w, ys, x, S.gate_w, res, self.out, sb.gate_out)
 
     def experts_used(self):
         """Distinct experts per weight set for this batch (read back once, untimed)."""
@@ -491,20 +495,23 @@ def main():
     if not args.no_shared_expert:
         # the same step with an always-on shared expert (routed experts' size):
         # its FFN launch first, its sigmoid gate fused into the combine
-        shared_sets = [upload_shared(shape, bits, li, torch, mi, moe) for li in range(len(layers))]
-        rs = Runner(torch, mi, moe, shape, layers, args.tokens, algo, fused_ffn=fused, shared=shared_sets)
-        rs.experts_used()
+        shared_sets = [L["shared"] for L in layers]
         n_sh = max(args.steps // 2, 10)
-        sh_ms, _, _, _ = rs.timed(n_sh, max(args.warmup // 2, 2), with_events=False)
-        shared_run = dict(I_shared=shared_sets[0].I, tokens_per_s=round(args.tokens * n_sh / (sh_ms / 1e3), 1),
-                          ms_per_step=round(sh_ms / n_sh, 5),
-                          added_us_per_step=round((sh_ms / n_sh - main_run["ms_per_step"]) * 1e3, 2),
-                          shared_weight_bytes=shape.bytes_per_expert(bits),
-                          note="shared expert FFN as its own launch before the routing; sigmoid gate fused "
-                               "into the combine")
-        log(f"[bench] with a shared expert T={args.tokens}: {shared_run['tokens_per_s']:.0f} tokens/s "
-            f"(+{shared_run['added_us_per_step']} us per step)")
-        del rs, shared_sets
+        shared_run = dict(I_shared=shared_sets[0].I, shared_weight_bytes=shape.bytes_per_expert(bits),
+                          note="sigmoid gate fused into the combine; one_launch: the shared expert's tiles are "
+                               "extra entries of the routed FFN launch; own_launch: a one-expert FFN launch "
+                               "before the routing")
+        for key, one in (("one_launch", True), ("own_launch", False)):
+            rs = Runner(torch, mi, moe, shape, layers, args.tokens, algo, fused_ffn=fused, shared=shared_sets,
+                        one_launch=one)
+            rs.experts_used()
+            sh_ms, _, _, _ = rs.timed(n_sh, max(args.warmup // 2, 2), with_events=False)
+            shared_run[key] = dict(tokens_per_s=round(args.tokens * n_sh / (sh_ms / 1e3), 1),
+                                   ms_per_step=round(sh_ms / n_sh, 5),
+                                   added_us_per_step=round((sh_ms / n_sh - main_run["ms_per_step"]) * 1e3, 2))
+            log(f"[bench] with a shared expert ({key}) T={args.tokens}: {shared_run[key]['tokens_per_s']:.0f} "
+                f"tokens/s (+{shared_run[key]['added_us_per_step']} us per step)")
+            del rs
 
     prefill = None
     if args.prefill_steps > 0:

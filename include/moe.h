@@ -312,6 +312,29 @@ int moe_expert_ffn_fused(const moe_dims* dims, int bits, const uint16_t* x, cons
                          const int32_t* n_work, const moe_qweights* weights, int algo, void* workspace,
                          size_t workspace_bytes, uint16_t* y_rows, int32_t* sync, void* stream);
 
+/* Step 5 with an always-on shared expert in the same launch: the results of
+ * moe_expert_ffn_fused for the routed rows, and the shared expert's FFN for
+ * every token, the shared expert's tiles being extra entries after the routed
+ * ones (one launch streams both; the Flash-MoE page, sec. 3, gates the shared
+ * expert's output into the combine, see moe_combine_shared).
+ *   dims     the routed layer (E routed experts, k picks).
+ *   weights  E + 1 experts: the routed ones, then the shared expert (same H
+ *            and I), in the layout of moe_qweights.
+ *   y_rows   bf16 [T*(k+1)][H]: rows 0 .. T*k-1 as moe_expert_ffn_fused's,
+ *            then row T*k + t = the shared expert's output for token t.
+ *   workspace  at least moe_workspace_bytes of dims with E+1 and k+1.
+ *   work_list, n_work, x, sync, algo, stream as for moe_expert_ffn_fused.
+ * Runs on the matrix-core decode kernels (one launch where a one-launch kernel
+ * exists for the shape, else their two launches, with the same entries); for
+ * shapes they do not take, other algorithms, or E + 1 or k + 1 beyond the
+ * limits: MOE_ERR_UNSUPPORTED before anything is enqueued, and the caller runs
+ * the shared expert as its own moe_expert_ffn_* call (E = 1, k = 1).  Routed
+ * rows may differ from moe_expert_ffn_fused's in the last bits where the larger
+ * row count changes the split of K among a workgroup's waves. */
+int moe_expert_ffn_fused_shared(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* work_list,
+                                const int32_t* n_work, const moe_qweights* weights, int algo, void* workspace,
+                                size_t workspace_bytes, uint16_t* y_rows, int32_t* sync, void* stream);
+
 /* Combine + residual (step 6; Flash-MoE page, sec. 3):
  *   acc = residual[t][n];  for j = 0..k-1 in order:
  *       acc = fmaf(topk_w[t][j], y_rows[pair_to_row[t*k+j]][n], acc)

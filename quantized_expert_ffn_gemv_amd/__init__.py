@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute", "moe_work_list_capacity",
     "moe_route_dispatch",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_expert_ffn_fused",
+    "moe_expert_ffn_fused_shared",
     "moe_combine", "moe_combine_shared",
     "moe_zero_point_bias",
 )
@@ -90,6 +91,7 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_gateup.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P]
     L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, Wp, ctypes.c_int, P, sz, P, P]
     L.moe_expert_ffn_fused.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P, P, P]
+    L.moe_expert_ffn_fused_shared.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P, P, P]
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
     L.moe_combine_shared.argtypes = [Dp, P, P, P, P, P, P, P, P, P, P]
     L.moe_zero_point_bias.argtypes = [ctypes.c_int64, P, P, P, P]
@@ -269,6 +271,17 @@ def expert_ffn_fused(d: Dims, bits: int, x, work_list, n_work, weights: QWeights
                                       _ptr(y_rows), _ptr(sync), _stream(stream)))
 
 
+def expert_ffn_fused_shared(d: Dims, bits: int, x, work_list, n_work, weights: QWeights, workspace, y_rows, sync,
+                            algo: int = ALGO_AUTO, stream=None):
+    """moe_expert_ffn_fused_shared: the routed FFN and an always-on shared expert
+    (the last of E + 1 experts in `weights`) in one launch; y_rows has T*(k+1)
+    rows, the shared expert's T last."""
+    w = weights.c_struct()
+    _check(lib().moe_expert_ffn_fused_shared(ctypes.byref(d), int(bits), _ptr(x), _ptr(work_list), _ptr(n_work),
+                                             ctypes.byref(w), int(algo), _ptr(workspace), _nbytes(workspace),
+                                             _ptr(y_rows), _ptr(sync), _stream(stream)))
+
+
 def combine(d: Dims, y_rows, pair_to_row, topk_w, residual, out, stream=None):
     _check(lib().moe_combine(ctypes.byref(d), _ptr(y_rows), _ptr(pair_to_row), _ptr(topk_w),
                              _ptr(residual), _ptr(out), _stream(stream)))
@@ -298,6 +311,6 @@ __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
-    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "combine", "combine_shared", "zero_point_bias", "LayerBuffers", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
+    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "expert_ffn_fused_shared", "combine", "combine_shared", "zero_point_bias", "LayerBuffers", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
     "group_major", "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

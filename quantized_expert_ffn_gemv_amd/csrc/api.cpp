@@ -394,6 +394,33 @@ int moe_expert_ffn_fused(const moe_dims* d, int bits, const uint16_t* x, const i
     return ok();
 }
 
+int moe_expert_ffn_fused_shared(const moe_dims* d, int bits, const uint16_t* x, const int32_t* work_list,
+                                const int32_t* n_work, const moe_qweights* w, int algo, void* ws, size_t ws_bytes,
+                                uint16_t* y, int32_t* sync, void* stream) {
+    const char* fn = "moe_expert_ffn_fused_shared";
+    int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 0, 3);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    if (d->E + 1 > 1024 || d->k + 1 > 32)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: E + 1 or k + 1 beyond the library's limits", fn);
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(y, 16);
+    REQUIRE_PTR(sync, 256);
+    moe_dims d1 = *d;
+    d1.E = d->E + 1;
+    d1.k = d->k + 1;
+    st = check_workspace(fn, &d1, bits, algo, ws, ws_bytes);
+    if (st) return st;
+    if (moe::resolve_algo(d1, bits, algo) != MOE_ALGO_MFMA)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: only the matrix-core decode path takes a shared expert", fn);
+    moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), y);
+    st = moe::launch_ffn_fused_dec_shared(a, sync, as_stream(stream));
+    if (st == MOE_ERR_UNSUPPORTED)
+        return fail(st, "%s: the decode kernels do not take this shape; run the shared expert as its own call", fn);
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 int moe_combine(const moe_dims* d, const uint16_t* y_rows, const int32_t* pair_to_row,
                 const float* topk_w, const uint16_t* residual, uint16_t* out, void* stream) {
     const char* fn = "moe_combine";

@@ -201,6 +201,7 @@ bool dec_down_fits(const moe_dims& d);
 int launch_gateup_dec(const FfnArgs& a, hipStream_t s);
 int launch_down_dec(const FfnArgs& a, hipStream_t s);
 int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s);
+int launch_ffn_fused_dec_shared(const FfnArgs& a, int32_t* sync, hipStream_t s);
 int launch_combine(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,
                    const uint16_t* residual, uint16_t* out, hipStream_t s);
 int launch_combine_shared(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,

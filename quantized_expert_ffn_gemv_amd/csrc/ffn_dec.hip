@@ -55,8 +55,10 @@ struct DecParams {
     uint16_t* y;        // [P][H]
     int T, H, I, E, P;
     int ipe;            // items per work-list entry
-    int cap;            // work-list capacity (entries)
+    int cap;            // work-list capacity (entries); the grid covers cap + n_shared
     int rows_cap;       // token rows of the LDS tile: min(16, T)
+    int n_shared;       // shared-expert tiles after the routed entries (0: none)
+    int shared_row0;    // first row of the shared expert's rows (the routed pair count)
 };
 
 __host__ __device__ constexpr size_t round_dma(size_t b) { return (b + kDma - 1) / kDma * kDma; }
@@ -115,11 +117,15 @@ __device__ __forceinline__ void lds_barrier() {
 // l % 16, clamped into [0, T)).  The whole entry is read with the count,
 // before any branch, so all of it arrives in one scalar round trip (every
 // entry below the grid's capacity is allocated, whatever the count).
+// With a shared expert, entries n_work .. n_work + n_shared - 1 are its tiles,
+// made here rather than read: expert E - 1 (the last of the weight arrays),
+// tokens 16 j .. 16 j + 15 of tile j, rows shared_row0 + token.
 struct DecItem {
     int entry, rb, e, row0, n;
     int tokv;
 };
 
+template <bool SHARED = false>
 __device__ __forceinline__ DecItem dec_item_at(const DecParams& p, int entry, int rb) {
     typedef int int4v __attribute__((ext_vector_type(4)));
     DecItem it;
@@ -131,14 +137,32 @@ __device__ __forceinline__ DecItem dec_item_at(const DecParams& p, int entry, in
     int4v v[kWorkInts / 4];
 #pragma unroll
     for (int i = 0; i < kWorkInts / 4; ++i) v[i] = ld_scalar(ent, i);
+    if constexpr (SHARED) {
+        // The values are taken here, so the loads stay unconditional and fly
+        // with the count's (else the compiler sinks them under the shared-tile
+        // test below, one more scalar round trip per item).
+#pragma unroll
+        for (int i = 0; i < kWorkInts / 4; ++i) asm volatile("" : "+s"(v[i]));
+    }
     const int l16 = threadIdx.x & 15;
     int tok = v[1][0];
 #pragma unroll
     for (int j = 1; j < kWorkRows; ++j) tok = (l16 == j) ? v[1 + j / 4][j % 4] : tok;
+    int e = v[0][0], row0 = v[0][1], n = v[0][2];
+    bool shared = false;
+    if constexpr (SHARED) {
+        const int sj = it.entry - n_work;             // shared tile index, if in [0, n_shared)
+        shared = sj >= 0 && sj < p.n_shared;
+        if (shared) {
+            e = p.E - 1;
+            row0 = p.shared_row0 + 16 * sj;
+            n = min(16, p.T - 16 * sj);
+            tok = 16 * sj + l16;
+        }
+    }
     it.tokv = (tok >= 0 && tok < p.T) ? tok : 0;
-    const int e = v[0][0], row0 = v[0][1], n = v[0][2];
-    const bool ok = it.entry < n_work && e >= 0 && e < p.E && row0 >= 0 && n >= 1 && n <= p.rows_cap &&
-                    row0 + n <= p.P;
+    const bool ok = (it.entry < n_work || shared) && e >= 0 && e < p.E && row0 >= 0 && n >= 1 &&
+                    n <= p.rows_cap && row0 + n <= p.P;
     it.e = ok ? e : 0;
     it.row0 = ok ? row0 : 0;
     it.n = ok ? n : 0;
@@ -150,9 +174,10 @@ __device__ __forceinline__ DecItem dec_item_at(const DecParams& p, int entry, in
 // and row block (r / 8) % ipe: the items of entry e all run on one XCD, so its
 // activation or h tile is fetched into that XCD's L2 once and hit by the other
 // items.
+template <bool SHARED = false>
 __device__ __forceinline__ DecItem dec_item_xcd(const DecParams& p, int entry0, int r) {
     const int xcd = r & 7, s = r >> 3;
-    return dec_item_at(p, entry0 + (s / p.ipe) * 8 + xcd, s % p.ipe);
+    return dec_item_at<SHARED>(p, entry0 + (s / p.ipe) * 8 + xcd, s % p.ipe);
 }
 
 // The activation tile in LDS: rows of `rowb` bytes, each group of 128 along K
@@ -392,10 +417,10 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     }
 }
 
-template <int BITS, int RW, int D>
+template <int BITS, int RW, int D, bool SHARED = false>
 __global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    gateup_item<BITS, RW, D, false>(p, dec_item_xcd(p, 0, (int)blockIdx.x), smem);
+    gateup_item<BITS, RW, D, false>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
 }
 
 // ------------------------------------------------------------------- down
@@ -551,10 +576,10 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
     }
 }
 
-template <int BITS, int RT, int D>
+template <int BITS, int RT, int D, bool SHARED = false>
 __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    down_item<BITS, RT, D, false>(p, dec_item_xcd(p, 0, (int)blockIdx.x), smem);
+    down_item<BITS, RT, D, false>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
 }
 
 // ------------------------------------------------------------ one-launch FFN
@@ -579,14 +604,14 @@ struct FusedParams {
     int ipe_d;                                                   // down items per entry
 };
 
-template <int BITS, int RW, int DG, int RT, int DD>
+template <int BITS, int RW, int DG, int RT, int DD, bool SHARED = false>
 __global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, int32_t* sync) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int ng = kFfnChunk * f.p.ipe, span = ng + kFfnChunk * f.ipe_d;
     const int b = (int)blockIdx.x, chunk = b / span, r = b - chunk * span;
     const int entry0 = chunk * kFfnChunk;
     if (r < ng) {
-        const DecItem it = dec_item_xcd(f.p, entry0, r);
+        const DecItem it = dec_item_xcd<SHARED>(f.p, entry0, r);
         gateup_item<BITS, RW, DG, true>(f.p, it, smem);
         if (it.n == 0) return;
         __builtin_amdgcn_s_waitcnt(0);          // this wave's h stores have completed
@@ -596,7 +621,7 @@ __global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, in
     } else {
         DecParams pd = f.p;
         pd.qa = f.qd; pd.sa = f.sd; pd.ba = f.bd; pd.ipe = f.ipe_d;
-        const DecItem it = dec_item_xcd(pd, entry0, r - ng);
+        const DecItem it = dec_item_xcd<SHARED>(pd, entry0, r - ng);
         if (it.n == 0) return;
         int32_t* ctr = &sync[kFfnStride * it.entry];
         down_item<BITS, RT, DD, true>(pd, it, smem, ctr, f.p.ipe, &sync[kFfnErr]);
@@ -673,30 +698,29 @@ static int dec_depth(int ng, int cap) {
 bool dec_gateup_fits(const moe_dims& d) { return dec_gateup_lds(d, dec_gateup_rw(d)) <= kDecLdsLimit; }
 bool dec_down_fits(const moe_dims& d) { return dec_down_lds(d, dec_down_rt(d)) <= kDecLdsLimit; }
 
-template <int BITS, int RW, int D>
+template <int BITS, int RW, int D, bool SHARED>
 static void gu_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    const dim3 grid((unsigned)((p.cap + 7) / 8 * 8 * p.ipe));      // entries rounded up to 8 (one per XCD)
-    hipLaunchKernelGGL((ffn_gateup_dec_kernel<BITS, RW, D>), grid, dim3(256), lds, s, p);
+    const dim3 grid((unsigned)((p.cap + p.n_shared + 7) / 8 * 8 * p.ipe));   // entries rounded up to 8 (one per XCD)
+    hipLaunchKernelGGL((ffn_gateup_dec_kernel<BITS, RW, D, SHARED>), grid, dim3(256), lds, s, p);
 }
 
-template <int BITS, int RW>
+template <int BITS, int RW, bool SHARED>
 static void gu_depth(int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (D >= 4) gu_go<BITS, RW, 4>(d, lds, s, p);
-    else if (D >= 2) gu_go<BITS, RW, 2>(d, lds, s, p);
-    else gu_go<BITS, RW, 1>(d, lds, s, p);
+    if (D >= 4) gu_go<BITS, RW, 4, SHARED>(d, lds, s, p);
+    else if (D >= 2) gu_go<BITS, RW, 2, SHARED>(d, lds, s, p);
+    else gu_go<BITS, RW, 1, SHARED>(d, lds, s, p);
 }
 
-template <int BITS>
+template <int BITS, bool SHARED>
 static void gu_rw(int rw, int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (rw == 4) gu_depth<BITS, 4>(D, d, lds, s, p);
-    else if (rw == 2) gu_depth<BITS, 2>(D, d, lds, s, p);
-    else gu_depth<BITS, 1>(D, d, lds, s, p);
+    if (rw == 4) gu_depth<BITS, 4, SHARED>(D, d, lds, s, p);
+    else if (rw == 2) gu_depth<BITS, 2, SHARED>(D, d, lds, s, p);
+    else gu_depth<BITS, 1, SHARED>(D, d, lds, s, p);
 }
 
-int launch_gateup_dec(const FfnArgs& a, hipStream_t s) {
-    const moe_dims& d = a.d;
-    if (d.T * d.k == 0) return MOE_OK;
-    DecParams p = dec_params(a);
+// d sizes the items; p carries the entries (and any shared tiles).
+template <bool SHARED>
+static int gateup_dec_run(const FfnArgs& a, const moe_dims& d, DecParams p, hipStream_t s) {
     p.qa = a.w.q[0]; p.sa = a.w.scale[0]; p.ba = a.w.bias[0];
     p.qb = a.w.q[1]; p.sb = a.w.scale[1]; p.bb = a.w.bias[1];
     const int rw = dec_gateup_rw(d);
@@ -704,27 +728,30 @@ int launch_gateup_dec(const FfnArgs& a, hipStream_t s) {
     const size_t lds = dec_gateup_lds(d, rw);
     if (lds > kDecLdsLimit) return MOE_ERR_UNSUPPORTED;
     const int D = dec_depth((d.H / kGroup) / (4 / rw), 4);
-    if (a.bits == 4) gu_rw<4>(rw, D, d, lds, s, p);
-    else gu_rw<2>(rw, D, d, lds, s, p);
+    if (a.bits == 4) gu_rw<4, SHARED>(rw, D, d, lds, s, p);
+    else gu_rw<2, SHARED>(rw, D, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-template <int BITS, int RT, int D>
+int launch_gateup_dec(const FfnArgs& a, hipStream_t s) {
+    if (a.d.T * a.d.k == 0) return MOE_OK;
+    return gateup_dec_run<false>(a, a.d, dec_params(a), s);
+}
+
+template <int BITS, int RT, int D, bool SHARED>
 static void dn_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    const dim3 grid((unsigned)((p.cap + 7) / 8 * 8 * p.ipe));      // entries rounded up to 8 (one per XCD)
-    hipLaunchKernelGGL((ffn_down_dec_kernel<BITS, RT, D>), grid, dim3(256), lds, s, p);
+    const dim3 grid((unsigned)((p.cap + p.n_shared + 7) / 8 * 8 * p.ipe));   // entries rounded up to 8 (one per XCD)
+    hipLaunchKernelGGL((ffn_down_dec_kernel<BITS, RT, D, SHARED>), grid, dim3(256), lds, s, p);
 }
 
-template <int BITS, int RT>
+template <int BITS, int RT, bool SHARED>
 static void dn_depth(int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (D >= 2) dn_go<BITS, RT, 2>(d, lds, s, p);
-    else dn_go<BITS, RT, 1>(d, lds, s, p);
+    if (D >= 2) dn_go<BITS, RT, 2, SHARED>(d, lds, s, p);
+    else dn_go<BITS, RT, 1, SHARED>(d, lds, s, p);
 }
 
-int launch_down_dec(const FfnArgs& a, hipStream_t s) {
-    const moe_dims& d = a.d;
-    if (d.T * d.k == 0) return MOE_OK;
-    DecParams p = dec_params(a);
+template <bool SHARED>
+static int down_dec_run(const FfnArgs& a, const moe_dims& d, DecParams p, hipStream_t s) {
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
     const int rt = dec_down_rt(d);
     p.ipe = d.H / (64 * rt);
@@ -732,44 +759,48 @@ int launch_down_dec(const FfnArgs& a, hipStream_t s) {
     if (lds > kDecLdsLimit) return MOE_ERR_UNSUPPORTED;
     const int D = dec_depth(d.I / kGroup, 2);
     if (a.bits == 4) {
-        if (rt == 4) dn_depth<4, 4>(D, d, lds, s, p);
-        else if (rt == 2) dn_depth<4, 2>(D, d, lds, s, p);
-        else dn_depth<4, 1>(D, d, lds, s, p);
+        if (rt == 4) dn_depth<4, 4, SHARED>(D, d, lds, s, p);
+        else if (rt == 2) dn_depth<4, 2, SHARED>(D, d, lds, s, p);
+        else dn_depth<4, 1, SHARED>(D, d, lds, s, p);
     } else {
-        if (rt == 4) dn_depth<2, 4>(D, d, lds, s, p);
-        else if (rt == 2) dn_depth<2, 2>(D, d, lds, s, p);
-        else dn_depth<2, 1>(D, d, lds, s, p);
+        if (rt == 4) dn_depth<2, 4, SHARED>(D, d, lds, s, p);
+        else if (rt == 2) dn_depth<2, 2, SHARED>(D, d, lds, s, p);
+        else dn_depth<2, 1, SHARED>(D, d, lds, s, p);
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int launch_down_dec(const FfnArgs& a, hipStream_t s) {
+    if (a.d.T * a.d.k == 0) return MOE_OK;
+    return down_dec_run<false>(a, a.d, dec_params(a), s);
+}
+
 // ------------------------------------------------------------ one-launch FFN
 
-template <int BITS, int RW, int DG, int RT, int DD>
+template <int BITS, int RW, int DG, int RT, int DD, bool SHARED>
 static int fused_go(size_t lds, hipStream_t s, const FusedParams& f, int32_t* sync) {
-    const int chunks = (f.p.cap + kFfnChunk - 1) / kFfnChunk;
+    const int chunks = (f.p.cap + f.p.n_shared + kFfnChunk - 1) / kFfnChunk;
     const dim3 grid((unsigned)(chunks * kFfnChunk * (f.p.ipe + f.ipe_d)));
-    hipLaunchKernelGGL((ffn_fused_dec_kernel<BITS, RW, DG, RT, DD>), grid, dim3(256), lds, s, f, sync);
+    hipLaunchKernelGGL((ffn_fused_dec_kernel<BITS, RW, DG, RT, DD, SHARED>), grid, dim3(256), lds, s, f, sync);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // The decode configurations with a one-launch kernel; others take two launches.
-template <int BITS>
+template <int BITS, bool SHARED>
 static int fused_pick(int rw, int dg, int rt, int dd, size_t lds, hipStream_t s, const FusedParams& f,
                       int32_t* sync) {
-    if (rw == 4 && dg == 4 && rt == 4 && dd == 2) return fused_go<BITS, 4, 4, 4, 2>(lds, s, f, sync);
-    if (rw == 4 && dg == 4 && rt == 2 && dd == 2) return fused_go<BITS, 4, 4, 2, 2>(lds, s, f, sync);
-    if (rw == 1 && dg == 4 && rt == 1 && dd == 4) return fused_go<BITS, 1, 4, 1, 4>(lds, s, f, sync);
-    if (rw == 1 && dg == 4 && rt == 1 && dd == 2) return fused_go<BITS, 1, 4, 1, 2>(lds, s, f, sync);
+    if (rw == 4 && dg == 4 && rt == 4 && dd == 2) return fused_go<BITS, 4, 4, 4, 2, SHARED>(lds, s, f, sync);
+    if (rw == 4 && dg == 4 && rt == 2 && dd == 2) return fused_go<BITS, 4, 4, 2, 2, SHARED>(lds, s, f, sync);
+    if (rw == 1 && dg == 4 && rt == 1 && dd == 4) return fused_go<BITS, 1, 4, 1, 4, SHARED>(lds, s, f, sync);
+    if (rw == 1 && dg == 4 && rt == 1 && dd == 2) return fused_go<BITS, 1, 4, 1, 2, SHARED>(lds, s, f, sync);
     return MOE_ERR_UNSUPPORTED;
 }
 
-int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s) {
-    const moe_dims& d = a.d;
-    if (d.T * d.k == 0) return MOE_OK;
-    if (!dec_gateup_fits(d) || !dec_down_fits(d) || work_capacity(d) > kFfnMaxEntries) return MOE_ERR_UNSUPPORTED;
+// The one-launch FFN with decode parameters p; d sizes the items.
+template <bool SHARED>
+static int fused_run(const FfnArgs& a, const moe_dims& d, const DecParams& p, int32_t* sync, hipStream_t s) {
     FusedParams f{};
-    f.p = dec_params(a);
+    f.p = p;
     f.p.qa = a.w.q[0]; f.p.sa = a.w.scale[0]; f.p.ba = a.w.bias[0];
     f.p.qb = a.w.q[1]; f.p.sb = a.w.scale[1]; f.p.bb = a.w.bias[1];
     f.qd = a.w.q[2]; f.sd = a.w.scale[2]; f.bd = a.w.bias[2];
@@ -783,8 +814,41 @@ int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s) {
     const int dg = dec_depth((d.H / kGroup) / (4 / rw), 4), dd = dec_depth(d.I / kGroup, rt == 1 ? 4 : 2);
     const size_t lg = dec_gateup_lds(d, rw), ld = dec_down_lds(d, rt);
     const size_t lds = lg > ld ? lg : ld;
-    return a.bits == 4 ? fused_pick<4>(rw, dg, rt, dd, lds, s, f, sync)
-                       : fused_pick<2>(rw, dg, rt, dd, lds, s, f, sync);
+    return a.bits == 4 ? fused_pick<4, SHARED>(rw, dg, rt, dd, lds, s, f, sync)
+                       : fused_pick<2, SHARED>(rw, dg, rt, dd, lds, s, f, sync);
+}
+
+int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s) {
+    const moe_dims& d = a.d;
+    if (d.T * d.k == 0) return MOE_OK;
+    if (!dec_gateup_fits(d) || !dec_down_fits(d) || work_capacity(d) > kFfnMaxEntries) return MOE_ERR_UNSUPPORTED;
+    return fused_run<false>(a, d, dec_params(a), sync, s);
+}
+
+// With a shared expert: a.d are the routed dims; the weights hold E + 1
+// experts (the shared one last) and y / the workspace have T (k + 1) rows.  The
+// shared tiles are ceil(T / 16) entries after the routed ones (dec_item_at),
+// so one launch streams the shared expert with the routed ones; shapes without
+// a one-launch kernel take the two decode launches, with the same entries.
+int launch_ffn_fused_dec_shared(const FfnArgs& a, int32_t* sync, hipStream_t s) {
+    const moe_dims& d = a.d;
+    if (d.T == 0) return MOE_OK;
+    moe_dims d1 = d;
+    d1.E = d.E + 1;
+    d1.k = d.k + 1;
+    const int n_sh = (d.T + kWorkRows - 1) / kWorkRows;
+    if (!dec_gateup_fits(d1) || !dec_down_fits(d1) || work_capacity(d) + n_sh > kFfnMaxEntries)
+        return MOE_ERR_UNSUPPORTED;
+    FfnArgs a1 = a;
+    a1.d = d1;
+    DecParams p = dec_params(a1);          // E + 1 experts, T (k + 1) rows
+    p.cap = (int)work_capacity(d);         // the routed work list's size
+    p.n_shared = n_sh;
+    p.shared_row0 = d.T * d.k;
+    int st = fused_run<true>(a1, d1, p, sync, s);
+    if (st != MOE_ERR_UNSUPPORTED) return st;
+    st = gateup_dec_run<true>(a1, d1, p, s);
+    return st ? st : down_dec_run<true>(a1, d1, p, s);
 }
 
 }  // namespace moe

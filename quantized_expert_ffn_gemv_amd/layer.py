@@ -10,11 +10,15 @@ C calls on one stream with no allocation and no host synchronisation:
 two-launch FFN (expert_ffn_q{4,2}).
 
 With a shared expert (``SharedExpert``: one more quantised FFN that every token
-uses, scaled by a per-token sigmoid gate), its FFN runs first, on the same
-stream, and ``combine_shared`` replaces ``combine``.  Its work list (every token
-on expert 0 of a one-expert layer) depends only on T and is built once, when
-``SharedBuffers`` are allocated.  (A second stream measured slower here: the
-cross-stream event wait held the host for the whole step.)
+uses, scaled by a per-token sigmoid gate) ``combine_shared`` replaces
+``combine``, and its FFN runs either
+  * inside the routed FFN launch (``expert_ffn_fused_shared``), when its weights
+    are given as the last of E + 1 experts (``fused_weights``) and the buffers
+    were allocated with ``shared_rows``; or
+  * as a launch of its own before the routing, a one-expert layer whose work
+    list (every token on expert 0) depends only on T and is built once, when
+    ``SharedBuffers`` are allocated.  (A second stream measured slower here:
+    the cross-stream event wait held the host for the whole step.)
 
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
@@ -26,7 +30,7 @@ from typing import Optional
 import torch
 
 from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, FFN_SYNC_INTS, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine,
-               combine_shared, dims, expert_ffn_fused, expert_ffn_q2, expert_ffn_q4, permute, route_dispatch,
+               combine_shared, dims, expert_ffn_fused, expert_ffn_fused_shared, expert_ffn_q2, expert_ffn_q4, permute, route_dispatch,
                route_topk, slot_lookup, work_list_capacity, workspace_bytes)
 
 
@@ -52,12 +56,15 @@ class LayerBuffers:
     y_rows: torch.Tensor          # bf16 bits as int16 [T*k, H]
     sync: torch.Tensor            # int32 [DISPATCH_SYNC_INTS], zeros (route_dispatch's counters)
     ffn_sync: torch.Tensor        # int32 [FFN_SYNC_INTS], zeros (expert_ffn_fused's counters)
+    shared_rows: bool = False     # y_rows and workspace also hold a shared expert's T rows
 
     @staticmethod
-    def allocate(d: Dims, bits: int = 4, algo: int = ALGO_AUTO, device="cuda") -> "LayerBuffers":
+    def allocate(d: Dims, bits: int = 4, algo: int = ALGO_AUTO, device="cuda",
+                 shared_rows: bool = False) -> "LayerBuffers":
         T, H, E, k = d.T, d.H, d.E, d.k
         i32 = dict(dtype=torch.int32, device=device)
-        ws = workspace_bytes(d, OP_FFN, bits, algo)
+        ws = workspace_bytes(dims(T, H, d.I, E + 1, k + 1) if shared_rows else d, OP_FFN, bits, algo)
+        rows = T * (k + 1) if shared_rows else T * k
         cap = work_list_capacity(d)
         return LayerBuffers(
             d=d, bits=bits,
@@ -76,9 +83,10 @@ class LayerBuffers:
             work_list=torch.empty((max(cap, 1), WORK_ENTRY_INTS), **i32),
             n_work=torch.zeros((1,), **i32),
             workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
-            y_rows=torch.empty((max(T * k, 1), H), dtype=torch.int16, device=device),
+            y_rows=torch.empty((max(rows, 1), H), dtype=torch.int16, device=device),
             sync=torch.zeros((DISPATCH_SYNC_INTS,), **i32),
             ffn_sync=torch.zeros((FFN_SYNC_INTS,), **i32),
+            shared_rows=shared_rows,
         )
 
 
@@ -89,6 +97,7 @@ class SharedExpert:
     weights: QWeights             # one expert: q[m] [1][K/128][N][16*bits], scale / bias [1][N][K/128]
     gate_w: torch.Tensor          # float32 [H]
     I: int
+    fused_weights: Optional[QWeights] = None   # the routed experts, then this one (E + 1): one FFN launch
 
 
 @dataclass
@@ -115,11 +124,16 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
                   out: torch.Tensor, algo: int = ALGO_AUTO, renormalize: bool = True,
                   host_doorbell=None, last_use=None, step: int = 0, stream=None, fused: bool = True,
                   shared: Optional[SharedExpert] = None, shared_buf: Optional[SharedBuffers] = None) -> None:
-    """Enqueue one layer step; `out` may be `residual`.  With `shared` (and its
-    `shared_buf`), the shared expert's FFN runs first and the combine adds its
-    gated rows."""
+    """Enqueue one layer step; `out` may be `residual`.  With `shared`, the
+    combine adds the shared expert's gated rows; its FFN runs inside the routed
+    FFN launch when shared.fused_weights is set (buffers with shared_rows;
+    `shared_buf`, if given, only receives the gate values), else first, as its
+    own launch on `shared_buf`."""
     d = buf.d
-    if shared is not None:
+    one_launch = shared is not None and shared.fused_weights is not None
+    if one_launch and not buf.shared_rows:
+        raise ValueError("the one-launch shared expert needs LayerBuffers allocated with shared_rows")
+    if shared is not None and not one_launch:
         sb = shared_buf
         if sb is None or sb.d.T != d.T or sb.d.H != d.H or sb.d.I != shared.I:
             raise ValueError("shared expert needs SharedBuffers allocated for this T, H and its I")
@@ -136,7 +150,10 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
                     host_doorbell, last_use, step, stream)
         permute(d, buf.topk_ids, buf.counts, buf.offsets, buf.sorted_pairs, buf.pair_to_row, buf.active,
                 buf.n_active, buf.work_list, buf.n_work, stream)
-    if fused:
+    if one_launch:
+        expert_ffn_fused_shared(d, weights.bits, x, buf.work_list, buf.n_work, shared.fused_weights, buf.workspace,
+                                buf.y_rows, buf.ffn_sync, algo, stream)
+    elif fused:
         expert_ffn_fused(d, weights.bits, x, buf.work_list, buf.n_work, weights, buf.workspace, buf.y_rows,
                          buf.ffn_sync, algo, stream)
     else:
@@ -145,5 +162,10 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
     if shared is None:
         combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out, stream)
         return
-    combine_shared(d, buf.y_rows, buf.pair_to_row, buf.topk_w, sb.buf.y_rows, x, shared.gate_w, residual, out,
-                   sb.gate_out, stream)
+    if one_launch:
+        ys = buf.y_rows[d.T * d.k: d.T * d.k + d.T]
+        gate_out = shared_buf.gate_out if shared_buf is not None else None
+    else:
+        ys, gate_out = sb.buf.y_rows, sb.gate_out
+    combine_shared(d, buf.y_rows, buf.pair_to_row, buf.topk_w, ys, x, shared.gate_w, residual, out, gate_out,
+                   stream)

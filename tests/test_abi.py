@@ -220,3 +220,17 @@ def test_combine_shared_validation():
     assert L.moe_combine_shared(ctypes.byref(d), *args, FAKE + 1, None) == moe.ERR_INVALID_ARG
     d0 = moe.dims(0, 256, 512, 8, 2)
     assert L.moe_combine_shared(ctypes.byref(d0), *([None] * 9), None) == moe.OK
+
+
+def test_fused_shared_ffn_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    w = moe.QWeightsC()
+    for m in range(3):
+        w.q[m], w.scale[m], w.bias[m] = FAKE, FAKE, FAKE
+    args = (ctypes.byref(d), 4, FAKE, FAKE, FAKE, ctypes.byref(w), moe.ALGO_AUTO)
+    assert L.moe_expert_ffn_fused_shared(*args, FAKE, 1 << 30, FAKE, None, None) == moe.ERR_INVALID_ARG  # no sync
+    assert L.moe_expert_ffn_fused_shared(*args, FAKE, 16, FAKE, FAKE, None) == moe.ERR_WORKSPACE        # too small
+    d32 = moe.dims(4, 256, 512, 8, 32)
+    assert L.moe_expert_ffn_fused_shared(ctypes.byref(d32), *args[1:], FAKE, 1 << 30, FAKE, FAKE,
+                                         None) == moe.ERR_UNSUPPORTED                                   # k + 1 > 32

@@ -656,3 +656,53 @@ def test_shared_expert_layer(name, bits, T, i_mul):
                                         g["gates"], ys, to_host(sbuf.gate_out)[:T], res)
         assert np.array_equal(to_host(out_d, np.uint16), ref_out)
         say(f"[ok] shared expert {name} T={T}: FFN max_rel {max_rel:.2e} mae_norm {mae:.2e}")
+
+
+@pytest.mark.parametrize("name,bits,T", [("tiny", 4, 4), ("a3b", 4, 1), ("a3b", 2, 8), ("a3b", 4, 32)])
+def test_shared_expert_one_launch(name, bits, T):
+    """The shared expert inside the routed FFN launch (expert_ffn_fused_shared,
+    its weights the last of E + 1 experts): routed rows and shared rows match the
+    oracle (FFN tolerance), the output is the oracle's combine_shared of the
+    GPU's rows and gates bit for bit, the counters are left zero; two steps in a
+    row.  Other algorithms are refused before anything is enqueued."""
+    L = layer(name, bits)
+    sh = L.shape
+    one, mats, gw = mi.make_shared_expert(sh, bits, seed=4)
+    sep = _upload_shared(mats, bits, gw, one.I)
+    cat = lambda a, b: [torch.cat([u, v]) for u, v in zip(a, b)]
+    fw = moe.QWeights(bits, cat(L.weights_d.q, sep.weights.q), cat(L.weights_d.scale, sep.weights.scale),
+                      cat(L.weights_d.bias, sep.weights.bias))
+    shared = moe.SharedExpert(sep.weights, sep.gate_w, one.I, fused_weights=fw)
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+    buf = moe.LayerBuffers.allocate(d, bits, shared_rows=True)
+    sbuf = moe.SharedBuffers.allocate(T, sh.H, one.I, bits)
+    P = T * sh.k
+    for seed in (15, 16):
+        xb, res = mi.make_activations(sh.H, T, seed)
+        x_d, r_d = to_dev(xb), to_dev(res)
+        out_d = torch.empty_like(r_d)
+        say(f"[run] one-launch shared expert {name} q{bits} T={T} seed={seed}")
+        moe.layer_forward(buf, x_d, L.Wr_d, L.bias_d, L.weights_d, L.table_d, sh.E, r_d, out_d,
+                          shared=shared, shared_buf=sbuf)
+        torch.cuda.synchronize()
+        assert int(buf.ffn_sync.abs().sum().item()) == 0
+        g = dict(logits=to_host(buf.logits), ids=to_host(buf.topk_ids), gates=to_host(buf.topk_w),
+                 sorted_pairs=to_host(buf.sorted_pairs)[:P])
+        check_topk(g, L)
+        rows = to_host(buf.y_rows, np.uint16)
+        ids = g["ids"].ravel()
+        W = mi.make_expert_weights(sh, bits, L.seed, experts=sorted({int(e) for e in ids}))
+        _, ys = oracle.expert_ffn(xb, ids, g["sorted_pairs"], W, sh.k)
+        mr_r, mae_r = tolerance_metrics(rows[:P], np.stack([ys[r] for r in range(P)]))
+        ref_s = np.stack([oracle.expert_ffn_row(xb[t], mats, bits)[1] for t in range(T)])
+        mr_s, mae_s = tolerance_metrics(rows[P:P + T], ref_s)
+        say(f"[ok] one-launch shared {name} T={T}: routed max_rel {mr_r:.2e} mae {mae_r:.2e}; "
+            f"shared max_rel {mr_s:.2e} mae {mae_s:.2e}")
+        assert mr_r <= 1e-2 and mae_r <= 1e-3 and mr_s <= 1e-2 and mae_s <= 1e-3
+        ref_out = oracle.combine_shared(rows[:P], to_host(buf.pair_to_row)[:P], g["gates"], rows[P:P + T],
+                                        to_host(sbuf.gate_out)[:T], res)
+        assert np.array_equal(to_host(out_d, np.uint16), ref_out)
+    with pytest.raises(moe.MoeError) as ex:
+        moe.expert_ffn_fused_shared(d, bits, x_d, buf.work_list, buf.n_work, fw, buf.workspace, buf.y_rows,
+                                    buf.ffn_sync, moe.ALGO_GEMV)
+    assert ex.value.status == moe.ERR_UNSUPPORTED

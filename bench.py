@@ -171,6 +171,39 @@ class Runner:
             ys = b.y_rows[T * k: T * k + T] if self.one_launch else sb.buf.y_rows
             moe.combine_shared(d, b.y_rows, b.pair_to_row, b.topk_w, ys, x, S.gate_w, res, self.out, sb.gate_out)
 
+    def timed_ffn_launches(self, steps, warmup):
+        """Mean duration (us) of the one-launch FFN alone: every weight set is
+        routed once into a buffer set of its own, then `steps` FFN launches run
+        back to back over the weight sets in turn, with HIP events on their
+        stream only before the first and after the last (no event between
+        kernels adds a dispatch gap), so the figure is the kernel's own
+        average, the one rocprofv3 reports."""
+        torch, moe, d = self.torch, self.moe, self.d
+        n = len(self.layers)
+        bits = self.layers[0]["w"].bits
+        bufs = [moe.LayerBuffers.allocate(d, bits, self.algo) for _ in range(n)]
+        for li in range(n):
+            L, b = self.layers[li], bufs[li]
+            moe.route_dispatch(d, self.x[li], L["Wr"], L["bias"], True, b.logits, b.topk_ids, b.topk_w, L["table"],
+                               self.shape.E, b.pair_slot, b.miss, b.n_miss, b.counts, b.offsets, b.sorted_pairs,
+                               b.pair_to_row, b.active, b.n_active, b.work_list, b.n_work, sync=b.sync)
+
+        def launch(i):
+            L, b = self.layers[i % n], bufs[i % n]
+            moe.expert_ffn_fused(d, bits, self.x[i % n], b.work_list, b.n_work, L["w"], b.workspace, b.y_rows,
+                                 b.ffn_sync, self.algo)
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            launch(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps * 1e3
+
     def experts_used(self):
         """Distinct experts per weight set for this batch (read back once, untimed)."""
         U = []
@@ -450,6 +483,7 @@ def main():
         # step a little, so these passes do not set the throughput); the
         # two-launch FFN is timed too, for its halves
         ev_total_ms, _, ffn_ms, _ = r.timed(steps, 0)
+        ffn_launch_us = r.timed_ffn_launches(steps, warmup) if fused else None
         r.fused_ffn = False
         split_total_ms, _, gate_ms, down_ms = r.timed(steps, 2)
         r.fused_ffn = fused
@@ -471,7 +505,8 @@ def main():
                     split_ffn_GBps=(gate_bytes + down_bytes) / (gate_s + down_s) / 1e9,
                     layer_GBps=(sum(Us) * per_expert + steps * router_bytes) / (total_ms / 1e3) / 1e9,
                     gateup_bytes_per_launch=gate_bytes / steps,
-                    ffn_bytes_per_launch=(gate_bytes + down_bytes) / steps)
+                    ffn_bytes_per_launch=(gate_bytes + down_bytes) / steps,
+                    ffn_launch_us=ffn_launch_us)
 
     log(f"[bench] T={args.tokens}: {args.warmup} warmup + {args.steps} timed steps")
     main_run = measure(args.tokens, args.steps, args.warmup)
@@ -520,12 +555,17 @@ def main():
             f"({100 * prefill['mfma_util']:.1f}% of bf16 MFMA peak)")
 
     if fused:
-        achieved = main_run["ffn_GBps"]
+        # the FFN launches timed back to back (events only at the ends): the
+        # kernel's own average; the per-step event figure, which also holds the
+        # dispatch gap an event between kernels adds, is reported beside it
+        achieved = main_run["ffn_bytes_per_launch"] / (main_run["ffn_launch_us"] * 1e-6) / 1e9
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                         frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic_record(args.algo, "fused"),
                         kernel=FFN_KERNELS[args.algo]["fused"] + " (gate/up matvec + SwiGLU + down matvec, one launch)",
                         algorithmic_bytes_per_launch=round(main_run["ffn_bytes_per_launch"]),
-                        mean_launch_us=round(main_run["ffn_us"], 3))
+                        mean_launch_us=round(main_run["ffn_launch_us"], 3),
+                        launches_timed=args.steps,
+                        in_step_event_us=round(main_run["ffn_us"], 3))
     else:
         achieved = main_run["gateup_GBps"]
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",

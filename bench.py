@@ -114,7 +114,8 @@ class Runner:
     FFN halves; optionally a shared expert per weight set (its FFN first, its
     gate in the combine)."""
 
-    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False, shared=None, one_launch=True):
+    def __init__(self, torch, mi, moe, shape, layers, T, algo, fused_ffn=False, shared=None, one_launch=True,
+                 acts=None):
         self.torch, self.mi, self.moe = torch, mi, moe
         self.shape, self.layers, self.T, self.algo = shape, layers, T, algo
         self.fused_ffn = fused_ffn
@@ -127,7 +128,7 @@ class Runner:
             self.sbuf = moe.SharedBuffers.allocate(T, sh.H, shared[0].I, layers[0]["w"].bits, algo)
         self.x, self.res = [], []
         for li in range(len(layers)):
-            xb, rb = mi.make_activations(sh.H, T, seed=1000 + li)
+            xb, rb = acts(li) if acts is not None else mi.make_activations(sh.H, T, seed=1000 + li)
             self.x.append(torch.from_numpy(xb.view("int16")).cuda())
             self.res.append(torch.from_numpy(rb.view("int16")).cuda())
         self.out = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
@@ -548,6 +549,24 @@ def main():
                 f"tokens/s (+{shared_run[key]['added_us_per_step']} us per step)")
             del rs
 
+    # speculative verify ("Strata" page, sec. 3.4): the same T as n_seq sequences of
+    # 4 draft tokens whose hidden states correlate, so drafts share expert fetches
+    spec_run = None
+    if args.tokens % 4 == 0:
+        n_seq = args.tokens // 4
+        rsv = Runner(torch, mi, moe, shape, layers, args.tokens, algo, fused_ffn=fused,
+                     acts=lambda li: mi.make_spec_verify_activations(shape.H, n_seq, 4, seed=2000 + li))
+        U_sv = rsv.experts_used()
+        n_sv = max(args.steps // 2, 10)
+        sv_ms, _, _, _ = rsv.timed(n_sv, max(args.warmup // 2, 2), with_events=False)
+        spec_run = dict(sequences=n_seq, drafts_per_sequence=4, rho=0.8,
+                        tokens_per_s=round(args.tokens * n_sv / (sv_ms / 1e3), 1), ms_per_step=round(sv_ms / n_sv, 5),
+                        experts_used_mean=float(np.mean(U_sv)),
+                        experts_used_mean_independent_tokens=main_run["U_mean"])
+        log(f"[bench] speculative verify {n_seq} x 4: {spec_run['tokens_per_s']:.0f} tokens/s, "
+            f"{spec_run['experts_used_mean']:.1f} experts per step (independent tokens: {main_run['U_mean']:.1f})")
+        del rsv
+
     prefill = None
     if args.prefill_steps > 0:
         prefill = measure_prefill(torch, mi, moe, args.prefill_steps, 3)
@@ -633,6 +652,7 @@ def main():
                                 "ms_per_step": round(warm["ms_per_step"], 5),
                                 "ffn_GBps": round(warm["ffn_GBps"], 1)},
         "shared_expert": shared_run,
+        "spec_verify": spec_run,
         "prefill": prefill,
         "context_not_comparable": CONTEXT,
     }

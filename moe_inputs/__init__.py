@@ -41,7 +41,7 @@ GROUP = 128
 MATRICES = ("gate", "up", "down")
 
 # tags of the independent random streams
-_TAG_X, _TAG_RES, _TAG_WR, _TAG_PERM, _TAG_Q, _TAG_S, _TAG_B, _TAG_Z, _TAG_SG = 1, 2, 3, 4, 5, 6, 7, 8, 9
+_TAG_X, _TAG_RES, _TAG_WR, _TAG_PERM, _TAG_Q, _TAG_S, _TAG_B, _TAG_Z, _TAG_SG, _TAG_SV = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -113,6 +113,21 @@ def make_activations(H: int, T: int, seed: int = 0) -> Tuple[np.ndarray, np.ndar
     x = _rng(seed, _TAG_X, T, H).standard_normal((T, H), dtype=np.float32)
     r = _rng(seed, _TAG_RES, T, H).standard_normal((T, H), dtype=np.float32)
     return f32_to_bf16_bits(x), f32_to_bf16_bits(r)
+
+
+def make_spec_verify_activations(H: int, n_seq: int, n_draft: int = 4, seed: int = 0,
+                                 rho: float = 0.8) -> Tuple[np.ndarray, np.ndarray]:
+    """A speculative-verify batch: n_seq sequences of n_draft draft tokens each,
+    token (b, d) at row b * n_draft + d, x = rho * base_b + sqrt(1 - rho^2) * noise
+    (unit variance, correlation rho between the drafts of one sequence, none
+    across sequences), so the drafts of a sequence tend to pick the same experts.
+    Returns (x, residual) as bf16 bits [n_seq * n_draft, H]."""
+    T = n_seq * n_draft
+    base = _rng(seed, _TAG_SV, 0, n_seq, H).standard_normal((n_seq, H), dtype=np.float32)
+    noise = _rng(seed, _TAG_SV, 1, T, H).standard_normal((T, H), dtype=np.float32)
+    x = rho * np.repeat(base, n_draft, axis=0) + np.float32(math.sqrt(1.0 - rho * rho)) * noise
+    r = _rng(seed, _TAG_RES, T, H).standard_normal((T, H), dtype=np.float32)
+    return f32_to_bf16_bits(x.astype(np.float32)), f32_to_bf16_bits(r)
 
 
 def expert_popularity(shape: LayerShape, seed: int = 0) -> np.ndarray:
@@ -259,6 +274,6 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
 __all__ = [
     "GROUP", "MATRICES", "LayerShape", "CONFIGS", "CONFIG_ORDER", "ExpertWeights",
     "make_activations", "make_router", "make_slot_table", "make_expert_weights",
-    "iter_expert_weights", "make_zero_points", "make_shared_expert", "expert_popularity", "popularity_order", "matrix_dims",
+    "iter_expert_weights", "make_zero_points", "make_shared_expert", "make_spec_verify_activations", "expert_popularity", "popularity_order", "matrix_dims",
     "pack_codes", "f32_to_bf16_bits", "f32_to_f16_bits",
 ]

@@ -706,3 +706,21 @@ def test_shared_expert_one_launch(name, bits, T):
         moe.expert_ffn_fused_shared(d, bits, x_d, buf.work_list, buf.n_work, fw, buf.workspace, buf.y_rows,
                                     buf.ffn_sync, moe.ALGO_GEMV)
     assert ex.value.status == moe.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n_seq,n_draft", [(8, 4), (2, 8)])
+def test_spec_verify_batch(n_seq, n_draft):
+    """A speculative-verify batch (drafts of one sequence share most experts,
+    so the FFN tiles hold several rows each) through every stage against the
+    oracle: A3B-style shape, T = n_seq * n_draft."""
+    L = layer("a3b")
+    xb, res = mi.make_spec_verify_activations(L.shape.H, n_seq, n_draft, seed=7)
+    say(f"[run] spec-verify a3b {n_seq} x {n_draft}")
+    g = run_layer(L, xb, res)
+    check_logits(g, L, xb)
+    check_topk(g, L)
+    check_lookup(g, L)
+    check_permute(g, L)
+    mr, mae = check_ffn(g, L, xb)
+    check_combine_exact(g, L, res)
+    say(f"[ok] spec-verify {n_seq} x {n_draft}: {g['n_active']} experts, FFN max_rel {mr:.2e} mae_norm {mae:.2e}")

@@ -210,3 +210,29 @@ def test_work_list_covers_every_pair_once(orc):
                     seen.append((t, e))
         assert sorted(seen) == sorted((t, int(e)) for t in range(T) for e in ids[t])
     assert orc.work_list(np.zeros((0, 2), np.int32), 8, 2).shape == (0, 20)
+
+
+def test_spec_verify_drafts_share_experts(orc):
+    """The speculative-verify inputs ("Strata" page, sec. 3.4: several draft
+    tokens of one sequence verified in one pass share expert fetches): drafts of
+    one sequence correlate at rho, tokens of different sequences do not, and
+    through the oracle's router and top-k the drafts of a sequence pick more
+    common experts than tokens of different sequences."""
+    sh = mi.CONFIGS["a3b"]
+    n_seq, n_draft = 8, 4
+    xb, _ = mi.make_spec_verify_activations(sh.H, n_seq, n_draft, seed=3)
+    x = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    c = np.corrcoef(x)
+    same = np.array([c[i, j] for i in range(len(x)) for j in range(len(x)) if i != j and i // n_draft == j // n_draft])
+    diff = np.array([c[i, j] for i in range(len(x)) for j in range(len(x)) if i // n_draft != j // n_draft])
+    assert abs(same.mean() - 0.64) < 0.05 and abs(diff.mean()) < 0.05      # rho^2 with unit-variance parts
+    Wr, bias = mi.make_router(sh, 0)
+    ids, _ = orc.topk(orc.router_logits(xb, Wr, bias), sh.k, True)
+    sets = [set(r) for r in ids.tolist()]
+    share = lambda i, j: len(sets[i] & sets[j])
+    within = np.mean([share(i, j) for i in range(len(sets)) for j in range(len(sets)) if i != j and i // n_draft == j // n_draft])
+    across = np.mean([share(i, j) for i in range(len(sets)) for j in range(len(sets)) if i // n_draft != j // n_draft])
+    assert within > across + 1.0
+    xi, _ = mi.make_activations(sh.H, n_seq * n_draft, 3)
+    ids_i, _ = orc.topk(orc.router_logits(xi, Wr, bias), sh.k, True)
+    assert len(set(ids.ravel().tolist())) < len(set(ids_i.ravel().tolist()))  # fewer distinct experts per batch

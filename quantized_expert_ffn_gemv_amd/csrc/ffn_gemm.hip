@@ -19,9 +19,10 @@
 //     up while the tile is staged.
 // The exact code operands and the fold are those of mfma_ops.h.  h leaves the
 // gate/up kernel in the same three bf16 planes (plus 16-row partial sums) as
-// the decode path; the down kernel here reads the hi and mid planes, i.e. h to
-// 16 significant bits (relative error below 2^-16 per element, far under the
-// bf16 rounding of the expert output).
+// the decode path, and the down kernel here reads all three (h to about 24
+// significant bits: with two, h's 2^-18 relative error summed over I moved
+// outputs far below the rms by a few bf16 ulps where the weights are large,
+// as zero-point weights are).
 #include <atomic>
 
 #include "launch_util.h"
@@ -363,18 +364,20 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemm_kernel(GemmParams p) {
 // ------------------------------------------------------------------- down
 // Item = (head, block): the same 64 token rows times output rows
 // block*128 .. +128.  Wave w computes all 64 tokens against its own 32 down
-// rows (2 weight tiles x 4 token tiles x 2 planes of h = 16 MFMAs per step).
+// rows (2 weight tiles x 4 token tiles x 3 planes of h = 24 MFMAs per step).
 // Per group of 128 along I:
-//   LDS: the hi and mid planes of h for the 64 rows (2 x 16 KB; h is already
+//   LDS: the three planes of h for the 64 rows (3 x 16 KB; h is already
 //        stored in code pair order) and each row's sum of h over the group,
 //        taken from the 16-row partial sums; double-buffered.
 //   Rings of depth D: each thread's share of the h tile (64 bytes per plane)
 //   and two partial sums; each lane's 2 weight pieces and their scales.
+constexpr int kGemmDnPlanes = 3;    // bf16 planes of h the down kernel multiplies
+
 template <int D>
 __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int kTileBytes = kTokRows * kActRowBytes;       // one plane of one group
-    constexpr int kBufBytes = 2 * kTileBytes + kTokRows * 4;  // hi, mid, sums
+    constexpr int kBufBytes = kGemmDnPlanes * kTileBytes + kTokRows * 4;  // hi, mid, lo, sums
     int* rows_lds = reinterpret_cast<int*>(smem + 2 * kBufBytes);
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -402,13 +405,13 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
         it.rbase = it.mt.e * H + it.mt.blk * kDnRows + 32 * wu + m;
     };
 
-    uint32_t hr[D][2][16];                    // staged h: 32 values of 2 planes
+    uint32_t hr[D][kGemmDnPlanes][16];        // staged h: 32 values of each plane
     float2 pr[D];                             // 2 partial sums of the staged row
     uint32_t cr[D][2][4];
     uint32_t ssr[D][2], sbr[D][2];
     auto issue_h = [&](int slot, const Item& it, int g) {
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl) {
+        for (int pl = 0; pl < kGemmDnPlanes; ++pl) {
             const uint4* src = reinterpret_cast<const uint4*>(it.h + pl * plane + (size_t)g * kGroup);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
     auto stage = [&](int slot, int buf) {
         uint8_t* base = smem + buf * kBufBytes;
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
+        for (int pl = 0; pl < kGemmDnPlanes; ++pl)
 #pragma unroll
             for (int st = 0; st < 4; ++st)
                 *reinterpret_cast<uint4*>(base + pl * kTileBytes + act_lds_offset(tr, 4 * tq + st)) =
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
         float sum = pr[slot].x + pr[slot].y;
         sum += __shfl_xor(sum, 1, kWave);
         sum += __shfl_xor(sum, 2, kWave);
-        if (tq == 0) reinterpret_cast<float*>(base + 2 * kTileBytes)[tr] = sum;
+        if (tq == 0) reinterpret_cast<float*>(base + kGemmDnPlanes * kTileBytes)[tr] = sum;
     };
 
     Item cur, nxt;
@@ -480,9 +483,9 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
                     for (int tk = 0; tk < 4; ++tk) C[wt][tk] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    uint32_t A[2][4][4];
+                    uint32_t A[kGemmDnPlanes][4][4];
 #pragma unroll
-                    for (int pl = 0; pl < 2; ++pl)
+                    for (int pl = 0; pl < kGemmDnPlanes; ++pl)
 #pragma unroll
                         for (int tk = 0; tk < 4; ++tk) {
                             const uint4 a4 = *reinterpret_cast<const uint4*>(
@@ -497,10 +500,11 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
                         for (int tk = 0; tk < 4; ++tk) {
                             C[wt][tk] = mfma16(A[0][tk], B, C[wt][tk]);
                             C[wt][tk] = mfma16(A[1][tk], B, C[wt][tk]);
+                            C[wt][tk] = mfma16(A[2][tk], B, C[wt][tk]);
                         }
                     }
                 }
-                const float* Xs = reinterpret_cast<const float*>(base + 2 * kTileBytes);
+                const float* Xs = reinterpret_cast<const float*>(base + kGemmDnPlanes * kTileBytes);
                 float4 X[4];
 #pragma unroll
                 for (int tk = 0; tk < 4; ++tk) X[tk] = *reinterpret_cast<const float4*>(Xs + 16 * tk + 4 * q);
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------- launch
 
 constexpr size_t kGuLds = 2 * ((size_t)kTokRows * kActRowBytes + kTokRows * 4) + 8 * sizeof(int);
-constexpr size_t kDnLds = 2 * ((size_t)2 * kTokRows * kActRowBytes + kTokRows * 4) + 8 * sizeof(int);
+constexpr size_t kDnLds = 2 * ((size_t)kGemmDnPlanes * kTokRows * kActRowBytes + kTokRows * 4) + 8 * sizeof(int);
 
 // LDS one workgroup may take on the current device (gfx950: 160 KB).
 static size_t max_lds_per_block() {

@@ -724,3 +724,37 @@ def test_spec_verify_batch(n_seq, n_draft):
     mr, mae = check_ffn(g, L, xb)
     check_combine_exact(g, L, res)
     say(f"[ok] spec-verify {n_seq} x {n_draft}: {g['n_active']} experts, FFN max_rel {mr:.2e} mae_norm {mae:.2e}")
+
+
+@pytest.mark.parametrize("algo", [moe.ALGO_AUTO, moe.ALGO_MFMA], ids=["auto_gemm", "decode"])
+def test_zero_point_weights_prefill(algo):
+    """Zero-point weights at the prefill shape (T = 4096), on the grouped GEMM
+    and on the decode kernels: 96 sampled rows against the oracle fed the
+    oracle's biases.  (Large dequantised weights are where a down kernel that
+    drops h's third bf16 plane leaves the tolerance.)"""
+    L = layer("prefill")
+    sh = L.shape
+    saved = [b.clone() for b in L.weights_d.bias]
+    try:
+        zs = {}
+        for i, m in enumerate(mi.MATRICES):
+            zs[m] = np.stack([mi.make_zero_points(sh, m, e, 4, seed=5) for e in range(sh.E)])
+            moe.zero_point_bias(L.weights_d.scale[i], to_dev(zs[m]), L.weights_d.bias[i])
+        T = sh.tokens[0]
+        xb, res = mi.make_activations(sh.H, T, 9)
+        say(f"[run] zero-point prefill algo={algo}")
+        g = run_layer(L, xb, res, algo=algo)
+        ids = g["ids"].ravel()
+        rows = [int(r) for r in np.random.default_rng(1).choice(T * sh.k, 96, replace=False)]
+        W = mi.make_expert_weights(sh, 4, L.seed, experts=sorted({int(ids[int(g["sorted_pairs"][r])]) for r in rows}))
+        for m in mi.MATRICES:
+            for i, e in enumerate(W.experts):
+                W.bias[m][i] = oracle.zero_point_bias(W.scale[m][i], zs[m][int(e)])
+        _, ys = oracle.expert_ffn(xb, ids, g["sorted_pairs"], W, sh.k, rows=rows)
+        max_rel, mae = tolerance_metrics(np.stack([g["y_rows"][r] for r in rows]), np.stack([ys[r] for r in rows]))
+        say(f"[ok] zero-point prefill algo={algo}: max_rel {max_rel:.2e} mae_norm {mae:.2e}")
+        assert max_rel <= 1e-2 and mae <= 1e-3, (max_rel, mae)
+    finally:
+        for b, s in zip(L.weights_d.bias, saved):
+            b.copy_(s)
+        torch.cuda.synchronize()

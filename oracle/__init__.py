@@ -186,29 +186,6 @@ def permute(ids: np.ndarray, E: int):
                 active=active[:na].copy(), n_active=na)
 
 
-def work_list(ids: np.ndarray, E: int, k: int, tile: int = 16) -> np.ndarray:
-    """FFN work list of the grouped pairs: int32 [n][tile + 4].
-
-    Grouping by expert ("Strata" page, sec. 2.3) gives each expert a run of
-    consecutive sorted rows; the library hands that run to its FFN in tiles of
-    at most `tile` rows.  The tile format is the library's own (the pages fix
-    only the grouping): per expert in ascending id, per tile in row order,
-    [expert, first row, rows, index of the tile among the expert's tiles,
-    token of each row..., then the token of the tile's first row repeated].  Built here from the oracle's permutation with
-    plain loops."""
-    perm = permute(ids, E)
-    counts, offsets, sp = perm["counts"], perm["offsets"], perm["sorted_pairs"]
-    out = []
-    for e in range(E):
-        for start in range(0, int(counts[e]), tile):
-            row0 = int(offsets[e]) + start
-            rows = min(tile, int(counts[e]) - start)
-            toks = [int(sp[row0 + j]) // k for j in range(rows)]
-            toks += [toks[0]] * (tile - rows)
-            out.append([e, row0, rows, start // tile] + toks)
-    return np.array(out, dtype=np.int32).reshape(-1, tile + 4)
-
-
 def expert_ffn_row(x_row: np.ndarray, w: Dict[str, Sequence[np.ndarray]], bits: int,
                    n_idx: Optional[np.ndarray] = None):
     """FFN of one expert on one token.  w[m] = (q [N, K*bits/8], scale, bias).

@@ -397,7 +397,7 @@ def test_dispatch_crafted_ids(E, H, T, k, pool):
             assert np.array_equal(to_host(getattr(buf, key))[:n], ref[key]), key
         na = int(to_host(buf.n_active)[0])
         assert na == ref["n_active"] and np.array_equal(to_host(buf.active)[:na], ref["active"])
-        wl = oracle.work_list(ids, E, k, moe.WORK_TILE_ROWS)
+        wl = expected_work_list(ids, E, k, moe.WORK_TILE_ROWS)
         assert int(to_host(buf.n_work)[0]) == wl.shape[0]
         assert np.array_equal(to_host(buf.work_list)[: wl.shape[0]], wl)
         assert int(buf.sync.abs().sum().item()) == 0

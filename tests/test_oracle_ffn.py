@@ -248,3 +248,143 @@ def test_combine_shared_closed_forms(orc):
     one = orc.combine_shared(Y, p2r, g, Ys, sg, res)
     assert np.array_equal(one[1:], base[1:])
     assert not np.array_equal(one[0], base[0])
+
+
+# ------------------------------------------- combine: an independent float32 chain
+#
+# The combine accumulates in float32 in pick order, one fused multiply-add per
+# pick, and rounds once to bf16 (the "Flash-MoE" page, sec. 3: combine +
+# residual in one kernel; the pick order and the rounding points are this
+# library's reading).  The reference below does not call fmaf: it takes every
+# step exactly in float64 -- the inputs have few significant bits (bf16 rows,
+# gates m/64), so g*y is exact and so is acc + g*y, which TwoSum verifies -- and
+# rounds that exact value once to float32, which is what a fused multiply-add
+# returns.  Crafted columns make the chain's order visible in the bf16 output.
+
+def _two_sum_exact(a, b):
+    s = a + b
+    bb = s - a
+    err = (a - (s - bb)) + (b - bb)
+    assert np.all(err == 0.0), "an exact float64 step was expected"
+    return s
+
+
+def _chain(res_bits, terms):
+    """acc = float32(residual); for (g, y) in order: acc = float32(exact(acc + g*y)).
+    terms: list of (g float64 [T, 1 or H], y float64 [T, H]).  Returns bf16 bits."""
+    acc = _bf16_f64(res_bits).astype(np.float32)
+    for g, y in terms:
+        prod = np.asarray(g, np.float64) * np.asarray(y, np.float64)
+        acc = _two_sum_exact(acc.astype(np.float64), prod).astype(np.float32)
+    u = acc.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)     # bf16, nearest even
+
+
+def _few_bit_bf16(rng, shape, emin, emax):
+    """bf16 values m * 2^(e-7), m in [128, 255] with a random sign: 8 significant bits."""
+    m = rng.integers(128, 256, shape).astype(np.float64) * rng.choice([-1.0, 1.0], shape)
+    e = rng.integers(emin, emax + 1, shape)
+    return mi.f32_to_bf16_bits(np.ldexp(m, e - 7).astype(np.float32))
+
+
+def _combine_case(seed=63):
+    """Six tokens, four picks each over seven experts; rows stored in expert order
+    through a permutation that is not its own inverse.  Token 0 has power-of-two
+    gates and crafted columns 0-1 (see below); the others random gates m/64."""
+    rng = np.random.default_rng(seed)
+    T, H, k, E = 6, 64, 4, 7
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    sorted_pairs = np.argsort(ids.ravel(), kind="stable").astype(np.int32)
+    pair_to_row = np.empty_like(sorted_pairs)
+    pair_to_row[sorted_pairs] = np.arange(T * k, dtype=np.int32)
+    assert not np.array_equal(sorted_pairs, pair_to_row)
+    g = np.stack([rng.choice(np.arange(1, 64), k, replace=False) / 64.0 for _ in range(T)]).astype(np.float32)
+    g[0] = [0.5, 0.25, 0.125, 0.0625]
+    Y = _few_bit_bf16(rng, (T * k, H), -12, 6)          # row r serves pair sorted_pairs[r]
+    res = _few_bit_bf16(rng, (T, H), -2, 6)
+    f = lambda v: int(mi.f32_to_bf16_bits(np.array([v], np.float32))[0])
+    row = lambda j: pair_to_row[0 * k + j]
+    # column 0: residual 1, pick 0 adds 0.75 float32 ulp of 1 (rounds up to one
+    # ulp), pick 1 adds -1: forward order leaves 2^-23, reversed 1.5 * 2^-24
+    res[0, 0] = f(1.0)
+    Y[row(0), 0], Y[row(1), 0], Y[row(2), 0], Y[row(3), 0] = f(1.5 * 2.0 ** -23), f(-4.0), f(0.0), f(0.0)
+    # column 1: the same with the -1 from the last pick (any single reordering shows)
+    res[0, 1] = f(1.0)
+    Y[row(0), 1], Y[row(1), 1], Y[row(2), 1], Y[row(3), 1] = f(1.5 * 2.0 ** -23), f(0.0), f(0.0), f(-16.0)
+    return dict(T=T, H=H, k=k, ids=ids, sorted_pairs=sorted_pairs, pair_to_row=pair_to_row, g=g, Y=Y, res=res)
+
+
+def _routed_terms(c, gate_of=None, row_map=None, order=None):
+    T, k = c["T"], c["k"]
+    gate_of = gate_of or (lambda t, j: c["g"][t, j])
+    row_map = c["pair_to_row"] if row_map is None else row_map
+    order = list(range(k)) if order is None else order
+    Yf = _bf16_f64(c["Y"])
+    terms = []
+    for j in order:
+        gj = np.array([[float(gate_of(t, j))] for t in range(T)])
+        yj = np.stack([Yf[row_map[t * k + j]] for t in range(T)])
+        terms.append((gj, yj))
+    return terms
+
+
+def test_combine_matches_an_exact_float32_chain(orc):
+    """orc_combine, bit for bit, against the chain computed exactly step by step,
+    with distinct rows per pick and unequal gates; and each plausible slip --
+    picks in reverse order, a gate of the wrong pick or token, rows gathered
+    through sorted_pairs instead of pair_to_row -- changes the bf16 output."""
+    c = _combine_case()
+    T, k = c["T"], c["k"]
+    ref = _chain(c["res"], _routed_terms(c))
+    got = orc.combine(c["Y"], c["pair_to_row"], c["g"], c["res"])
+    assert np.array_equal(got, ref)
+    assert got[0, 0] == mi.f32_to_bf16_bits(np.array([2.0 ** -23], np.float32))[0]
+    slips = {
+        "reversed picks": _routed_terms(c, order=list(range(k))[::-1]),
+        "gate of the mirrored pick": _routed_terms(c, gate_of=lambda t, j: c["g"][t, k - 1 - j]),
+        "gate of the next token": _routed_terms(c, gate_of=lambda t, j: c["g"][(t + 1) % T, j]),
+        "rows through sorted_pairs": _routed_terms(c, row_map=c["sorted_pairs"]),
+    }
+    for name, terms in slips.items():
+        assert not np.array_equal(_chain(c["res"], terms), ref), name
+    # the reversal shows in the crafted columns of token 0 even where rows agree
+    rev = _chain(c["res"], slips["reversed picks"])
+    assert rev[0, 0] != ref[0, 0] and rev[0, 1] != ref[0, 1]
+
+
+def test_combine_shared_matches_an_exact_float32_chain(orc):
+    """orc_combine_shared: the routed chain, then the shared row's term last, bit
+    for bit against the exact step-by-step chain; the shared term taken first,
+    or with another token's gate, changes the output."""
+    c = _combine_case(64)
+    T, H = c["T"], c["H"]
+    rng = np.random.default_rng(65)
+    Ys = _few_bit_bf16(rng, (T, H), -12, 6)
+    sg = (rng.choice(np.arange(1, 64), T, replace=False) / 64.0).astype(np.float32)
+    # token 0, column 2: residual 1, pick 0 adds 0.75 ulp, the shared term -1
+    f = lambda v: int(mi.f32_to_bf16_bits(np.array([v], np.float32))[0])
+    k = c["k"]
+    c["res"][0, 2] = f(1.0)
+    for j in range(k):
+        c["Y"][c["pair_to_row"][j], 2] = f(1.5 * 2.0 ** -23 if j == 0 else 0.0)
+    sg[0] = 0.5
+    Ys[0, 2] = f(-2.0)
+    Ys[0, 0] = Ys[0, 1] = f(0.0)        # the routed crafted columns stay visible
+    shared = (sg.astype(np.float64)[:, None], _bf16_f64(Ys))
+    routed = _routed_terms(c)
+    ref = _chain(c["res"], routed + [shared])
+    got = orc.combine_shared(c["Y"], c["pair_to_row"], c["g"], Ys, sg, c["res"])
+    assert np.array_equal(got, ref)
+    first = _chain(c["res"], [shared] + routed)
+    assert first[0, 2] != ref[0, 2]
+    other = (np.roll(sg, -1).astype(np.float64)[:, None], _bf16_f64(Ys))
+    assert not np.array_equal(_chain(c["res"], routed + [other]), ref)
+    # the routed slips show through the shared chain as well
+    T = c["T"]
+    for name, terms in {
+        "reversed picks": _routed_terms(c, order=list(range(k))[::-1]),
+        "gate of the mirrored pick": _routed_terms(c, gate_of=lambda t, j: c["g"][t, k - 1 - j]),
+        "gate of the next token": _routed_terms(c, gate_of=lambda t, j: c["g"][(t + 1) % T, j]),
+        "rows through sorted_pairs": _routed_terms(c, row_map=c["sorted_pairs"]),
+    }.items():
+        assert not np.array_equal(_chain(c["res"], terms + [shared]), ref), name

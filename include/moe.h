@@ -32,7 +32,8 @@
  * Conventions for every call
  *   - All array pointers are DEVICE pointers unless a parameter says
  *     otherwise.  The caller allocates and owns every buffer, including the
- *     workspace; the library keeps no device memory between calls.
+ *     workspace; the library keeps no device memory between calls, except the
+ *     fixed per-GPU array of moe_expert_ffn_fused_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Calls only enqueue work on `stream` and return; they never synchronise
  *     and never allocate.
@@ -306,11 +307,36 @@ int moe_expert_down(const moe_dims* dims, int bits, const int32_t* work_list, co
  *         share one sync buffer must be ordered (one stream).  The last 32
  *         ints are a fault flag: nonzero after a call means a down item gave
  *         up waiting for its h (about 10 ms), and that call's outputs are not
- *         valid; the caller clears it. */
+ *         valid.  After such a call the counters may not be back to zero
+ *         either: the caller zeroes the whole buffer before the next call. */
 #define MOE_FFN_SYNC_INTS 32800
 int moe_expert_ffn_fused(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* work_list,
                          const int32_t* n_work, const moe_qweights* weights, int algo, void* workspace,
                          size_t workspace_bytes, uint16_t* y_rows, int32_t* sync, void* stream);
+
+/* Step 5 in one launch without allocating: moe_expert_ffn_fused with its
+ * workspace and counters taken from a fixed device array of the library.  For
+ * callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It runs the same kernels, so its
+ * y_rows equal moe_expert_ffn_fused's bit for bit.
+ *   The array holds MOE_NOALLOC_WORKSPACE_BYTES of workspace: a call whose
+ *   moe_workspace_bytes(dims, MOE_OP_FFN, bits, algo) is larger fails with
+ *   MOE_ERR_WORKSPACE before anything is enqueued.
+ *   Every GPU the library runs on holds one such array until the process ends,
+ *   and every call on a GPU (the current device) uses that GPU's array and
+ *   leaves its last contents there: calls that overlap on one GPU (two
+ *   streams, two threads) race, so order them.  Each call first clears the
+ *   counters with a small kernel on `stream` (no memset node, so the call can
+ *   be captured).  The first call on a device looks the array up (no
+ *   allocation); make that call outside graph capture.
+ *   fault  NULL, or device int32 set to 1 by a call whose down items gave up
+ *          waiting for their h (that call's y_rows are then invalid); never
+ *          cleared by the library.  4-byte aligned.
+ * Other arguments, alignment and errors as for moe_expert_ffn_fused. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (16u << 20)
+int moe_expert_ffn_fused_noalloc(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* work_list,
+                                 const int32_t* n_work, const moe_qweights* weights, int algo, uint16_t* y_rows,
+                                 int32_t* fault, void* stream);
 
 /* Step 5 with an always-on shared expert in the same launch: the results of
  * moe_expert_ffn_fused for the routed rows, and the shared expert's FFN for

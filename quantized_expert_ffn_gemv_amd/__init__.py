@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_route_topk", "moe_topk_from_logits", "moe_slot_lookup", "moe_permute", "moe_work_list_capacity",
     "moe_route_dispatch",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_expert_ffn_fused",
-    "moe_expert_ffn_fused_shared",
+    "moe_expert_ffn_fused_shared", "moe_expert_ffn_fused_noalloc",
     "moe_combine", "moe_combine_shared",
     "moe_zero_point_bias",
 )
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_down.argtypes = [Dp, ctypes.c_int, P, P, Wp, ctypes.c_int, P, sz, P, P]
     L.moe_expert_ffn_fused.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P, P, P]
     L.moe_expert_ffn_fused_shared.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, sz, P, P, P]
+    L.moe_expert_ffn_fused_noalloc.argtypes = [Dp, ctypes.c_int, P, P, P, Wp, ctypes.c_int, P, P, P]
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
     L.moe_combine_shared.argtypes = [Dp, P, P, P, P, P, P, P, P, P, P]
     L.moe_zero_point_bias.argtypes = [ctypes.c_int64, P, P, P, P]
@@ -193,6 +194,7 @@ def slot_lookup(d: Dims, topk_ids, slot_of_expert, n_slots: int, pair_slot, miss
 WORK_TILE_ROWS, WORK_ENTRY_INTS = 16, 20     # MOE_WORK_TILE_ROWS, MOE_WORK_ENTRY_INTS
 DISPATCH_SYNC_INTS = 576                     # MOE_DISPATCH_SYNC_INTS
 FFN_SYNC_INTS = 32800                        # MOE_FFN_SYNC_INTS (the last 32: the fault flag)
+NOALLOC_WORKSPACE_BYTES = 16 << 20           # MOE_NOALLOC_WORKSPACE_BYTES
 
 
 def work_list_capacity(d: Dims) -> int:
@@ -271,6 +273,16 @@ def expert_ffn_fused(d: Dims, bits: int, x, work_list, n_work, weights: QWeights
                                       _ptr(y_rows), _ptr(sync), _stream(stream)))
 
 
+def expert_ffn_fused_noalloc(d: Dims, bits: int, x, work_list, n_work, weights: QWeights, y_rows, fault=None,
+                             algo: int = ALGO_AUTO, stream=None):
+    """moe_expert_ffn_fused_noalloc: expert_ffn_fused with the workspace and
+    counters in the library's fixed device array (nothing allocated); `fault`:
+    None or an int32 device tensor set to 1 if a wait timed out."""
+    w = weights.c_struct()
+    _check(lib().moe_expert_ffn_fused_noalloc(ctypes.byref(d), int(bits), _ptr(x), _ptr(work_list), _ptr(n_work),
+                                              ctypes.byref(w), int(algo), _ptr(y_rows), _ptr(fault), _stream(stream)))
+
+
 def expert_ffn_fused_shared(d: Dims, bits: int, x, work_list, n_work, weights: QWeights, workspace, y_rows, sync,
                             algo: int = ALGO_AUTO, stream=None):
     """moe_expert_ffn_fused_shared: the routed FFN and an always-on shared expert
@@ -311,6 +323,6 @@ __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
-    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "expert_ffn_fused_shared", "combine", "combine_shared", "zero_point_bias", "LayerBuffers", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
+    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "expert_ffn_fused_shared", "expert_ffn_fused_noalloc", "NOALLOC_WORKSPACE_BYTES", "combine", "combine_shared", "zero_point_bias", "LayerBuffers", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
     "group_major", "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

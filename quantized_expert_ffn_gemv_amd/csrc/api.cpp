@@ -394,6 +394,42 @@ int moe_expert_ffn_fused(const moe_dims* d, int bits, const uint16_t* x, const i
     return ok();
 }
 
+int moe_expert_ffn_fused_noalloc(const moe_dims* d, int bits, const uint16_t* x, const int32_t* work_list,
+                                 const int32_t* n_work, const moe_qweights* w, int algo, uint16_t* y, int32_t* fault,
+                                 void* stream) {
+    const char* fn = "moe_expert_ffn_fused_noalloc";
+    int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 0, 3);
+    if (st) return st;
+    if (d->T == 0) return ok();
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(y, 16);
+    if (fault && !aligned(fault, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: fault misaligned", fn);
+    const size_t need = moe::ffn_workspace_bytes(*d, bits, algo);
+    if (need > (size_t)MOE_NOALLOC_WORKSPACE_BYTES)
+        return fail(MOE_ERR_WORKSPACE, "%s: these dims need %zu bytes of workspace; the fixed scratch holds %zu",
+                    fn, need, (size_t)MOE_NOALLOC_WORKSPACE_BYTES);
+    int32_t* sync = nullptr;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (moe::noalloc_scratch(&sync, &ws, &ws_bytes) != MOE_OK)
+        return fail(MOE_ERR_HIP, "%s: looking up the scratch array failed: %s", fn,
+                    hipGetErrorString(hipGetLastError()));
+    moe::FfnArgs a = ffn_args(d, bits, x, work_list, n_work, w, static_cast<float*>(ws), y);
+    const int alg = moe::resolve_algo(*d, bits, algo);
+    const hipStream_t s = as_stream(stream);
+    st = MOE_ERR_UNSUPPORTED;
+    if (alg == MOE_ALGO_MFMA) {
+        st = moe::launch_clear_sync(sync, s);
+        if (!st) st = moe::launch_ffn_fused_dec(a, sync, s, fault);
+    }
+    if (st == MOE_ERR_UNSUPPORTED) {
+        st = launch_gateup(alg, a, s);
+        if (!st) st = launch_down(alg, a, s);
+    }
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 int moe_expert_ffn_fused_shared(const moe_dims* d, int bits, const uint16_t* x, const int32_t* work_list,
                                 const int32_t* n_work, const moe_qweights* w, int algo, void* ws, size_t ws_bytes,
                                 uint16_t* y, int32_t* sync, void* stream) {

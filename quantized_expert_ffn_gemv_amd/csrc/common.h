@@ -200,7 +200,13 @@ bool dec_gateup_fits(const moe_dims& d);
 bool dec_down_fits(const moe_dims& d);
 int launch_gateup_dec(const FfnArgs& a, hipStream_t s);
 int launch_down_dec(const FfnArgs& a, hipStream_t s);
-int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s);
+// err: where a down item that gives up waiting writes 1 (NULL: the flag at the
+// end of sync).
+int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s, int32_t* err = nullptr);
+// The fixed scratch of the entry point that allocates nothing (noalloc.hip):
+// the current device's counters and workspace, and a fill that zeroes the counters.
+int noalloc_scratch(int32_t** sync, void** workspace, size_t* workspace_bytes);
+int launch_clear_sync(int32_t* sync, hipStream_t s);
 int launch_ffn_fused_dec_shared(const FfnArgs& a, int32_t* sync, hipStream_t s);
 int launch_combine(const moe_dims& d, const uint16_t* y, const int32_t* p2r, const float* gates,
                    const uint16_t* residual, uint16_t* out, hipStream_t s);

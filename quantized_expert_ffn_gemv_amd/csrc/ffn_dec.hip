@@ -602,6 +602,7 @@ struct FusedParams {
     DecParams p;                                                 // gate/up: weights qa..bb, ipe
     const uint8_t* qd; const uint16_t* sd; const uint16_t* bd;   // down weights
     int ipe_d;                                                   // down items per entry
+    int32_t* err;                                                // set to 1 when a wait times out
 };
 
 template <int BITS, int RW, int DG, int RT, int DD, bool SHARED = false>
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, in
         const DecItem it = dec_item_xcd<SHARED>(pd, entry0, r - ng);
         if (it.n == 0) return;
         int32_t* ctr = &sync[kFfnStride * it.entry];
-        down_item<BITS, RT, DD, true>(pd, it, smem, ctr, f.p.ipe, &sync[kFfnErr]);
+        down_item<BITS, RT, DD, true>(pd, it, smem, ctr, f.p.ipe, f.err);
         if (threadIdx.x == 0 &&
             __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == f.ipe_d - 1) {
             __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -798,9 +799,11 @@ static int fused_pick(int rw, int dg, int rt, int dd, size_t lds, hipStream_t s,
 
 // The one-launch FFN with decode parameters p; d sizes the items.
 template <bool SHARED>
-static int fused_run(const FfnArgs& a, const moe_dims& d, const DecParams& p, int32_t* sync, hipStream_t s) {
+static int fused_run(const FfnArgs& a, const moe_dims& d, const DecParams& p, int32_t* sync, hipStream_t s,
+                     int32_t* err = nullptr) {
     FusedParams f{};
     f.p = p;
+    f.err = err != nullptr ? err : sync + kFfnErr;
     f.p.qa = a.w.q[0]; f.p.sa = a.w.scale[0]; f.p.ba = a.w.bias[0];
     f.p.qb = a.w.q[1]; f.p.sb = a.w.scale[1]; f.p.bb = a.w.bias[1];
     f.qd = a.w.q[2]; f.sd = a.w.scale[2]; f.bd = a.w.bias[2];
@@ -818,11 +821,11 @@ static int fused_run(const FfnArgs& a, const moe_dims& d, const DecParams& p, in
                        : fused_pick<2, SHARED>(rw, dg, rt, dd, lds, s, f, sync);
 }
 
-int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s) {
+int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s, int32_t* err) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     if (!dec_gateup_fits(d) || !dec_down_fits(d) || work_capacity(d) > kFfnMaxEntries) return MOE_ERR_UNSUPPORTED;
-    return fused_run<false>(a, d, dec_params(a), sync, s);
+    return fused_run<false>(a, d, dec_params(a), sync, s, err);
 }
 
 // With a shared expert: a.d are the routed dims; the weights hold E + 1

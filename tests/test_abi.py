@@ -234,3 +234,21 @@ def test_fused_shared_ffn_validation():
     d32 = moe.dims(4, 256, 512, 8, 32)
     assert L.moe_expert_ffn_fused_shared(ctypes.byref(d32), *args[1:], FAKE, 1 << 30, FAKE, FAKE,
                                          None) == moe.ERR_UNSUPPORTED                                   # k + 1 > 32
+
+
+def test_noalloc_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    w = _qw()
+    call = lambda x=FAKE, y=FAKE, fault=None, bits=4: L.moe_expert_ffn_fused_noalloc(
+        ctypes.byref(d), bits, x, FAKE, FAKE, ctypes.byref(w), moe.ALGO_AUTO, y, fault, None)
+    assert call(x=None) == moe.ERR_INVALID_ARG
+    assert call(y=MISALIGNED) == moe.ERR_INVALID_ARG
+    assert call(fault=MISALIGNED) == moe.ERR_INVALID_ARG
+    assert call(bits=3) == moe.ERR_UNSUPPORTED
+    big = moe.dims(4096, 2048, 768, 128, 8)
+    assert L.moe_expert_ffn_fused_noalloc(ctypes.byref(big), 4, FAKE, FAKE, FAKE, ctypes.byref(w), moe.ALGO_MFMA,
+                                          FAKE, None, None) == moe.ERR_WORKSPACE
+    z = moe.dims(0, 256, 512, 8, 2)
+    assert L.moe_expert_ffn_fused_noalloc(ctypes.byref(z), 4, None, None, None, ctypes.byref(w), 0, None, None,
+                                          None) == moe.OK

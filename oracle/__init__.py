@@ -59,6 +59,9 @@ def lib():
         L.orc_combine.argtypes = [i32, i32, i32, P, P, P, P, P]; L.orc_combine.restype = None
         L.orc_shared_gate.argtypes = [i32, i32, P, P, P]; L.orc_shared_gate.restype = None
         L.orc_combine_shared.argtypes = [i32, i32, i32] + [P] * 7; L.orc_combine_shared.restype = None
+        L.orc_freq_update.argtypes = [i32, P, P]; L.orc_freq_update.restype = None
+        L.orc_hot_set.argtypes = [i32, P, i32, P]; L.orc_hot_set.restype = None
+        L.orc_warm_ring_step.argtypes = [i32, i32, P, i32, u32, P, P, P, P, P]; L.orc_warm_ring_step.restype = i32
         _lib = L
     return _lib
 
@@ -268,6 +271,42 @@ def combine_shared(y_rows: np.ndarray, pair_to_row: np.ndarray, gates: np.ndarra
     lib().orc_combine_shared(T, H, k, _p(y_rows), _p(p2r), _p(gates), _p(y_shared), _p(sgate), _p(residual),
                              _p(out))
     return out
+
+
+# --------------------------------------------------------- residency tiers
+
+def freq_update(counts: np.ndarray, freq: np.ndarray) -> np.ndarray:
+    """Routing-frequency counters after one call: freq + counts (uint32)."""
+    counts = _c(counts, np.int32)
+    out = np.array(freq, dtype=np.uint32, copy=True)
+    lib().orc_freq_update(int(counts.shape[0]), _p(counts), _p(out))
+    return out
+
+
+def hot_set(freq: np.ndarray, n: int) -> np.ndarray:
+    """The n most routed experts, most used first, ties to the lower id."""
+    freq = _c(freq, np.uint32)
+    out = np.empty(n, dtype=np.int32)
+    lib().orc_hot_set(int(freq.shape[0]), _p(freq), int(n), _p(out))
+    return out
+
+
+def warm_ring_step(n_hot: int, miss: np.ndarray, step: int, slot_of_expert: np.ndarray,
+                   expert_of_slot: np.ndarray, last_use: np.ndarray):
+    """One step of the LRU warm ring for this step's missing experts (ascending).
+    Returns dict(slot_of_expert, expert_of_slot, last_use, copies [(expert, slot)])
+    with new arrays (the inputs are not modified)."""
+    miss = _c(miss, np.int32)
+    soe = np.array(slot_of_expert, dtype=np.int32, copy=True)
+    eos = np.array(expert_of_slot, dtype=np.int32, copy=True)
+    lu = np.array(last_use, dtype=np.uint32, copy=True)
+    n_slots = int(eos.shape[0])
+    ce = np.zeros(max(n_slots, 1), np.int32)
+    cs = np.zeros(max(n_slots, 1), np.int32)
+    n = lib().orc_warm_ring_step(int(n_hot), n_slots, _p(miss), int(miss.shape[0]), int(step) & 0xFFFFFFFF,
+                                 _p(soe), _p(eos), _p(lu), _p(ce), _p(cs))
+    return dict(slot_of_expert=soe, expert_of_slot=eos, last_use=lu,
+                copies=[(int(ce[i]), int(cs[i])) for i in range(n)])
 
 
 def layer(x_bits, Wr, router_bias, weights, k: int, slot_of_expert, n_slots: int, residual,

@@ -342,3 +342,65 @@ void orc_combine(int T, int H, int k, const uint16_t* y_rows, const int32_t* pai
             out[(size_t)t * H + n] = orc_f32_to_bf16(acc);
         }
 }
+
+/* ---------------------------------------------------------- residency tiers */
+/* "Luce Spark" page, sec. 1 (calibrated placement: count how often traffic
+ * routes to each expert, keep the most used set resident, "hot") and sec. 2
+ * (a bounded ring of spare slots: a routed expert that is not resident is
+ * copied from pinned host memory into a spare slot, the least recently used
+ * entry making room when the ring is full; tiers hot / warm / cold). */
+
+/* Routing-frequency counters: freq[e] += counts[e] (counts = pairs routed to
+ * expert e in one call, as orc_permute gives them). */
+void orc_freq_update(int E, const int32_t* counts, uint32_t* freq) {
+    for (int e = 0; e < E; ++e) freq[e] += (uint32_t)counts[e];
+}
+
+/* Calibrated hot set: the n experts with the highest counts, most used first,
+ * equal counts to the lower expert id. */
+void orc_hot_set(int E, const uint32_t* freq, int n, int32_t* hot) {
+    for (int j = 0; j < n; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            int taken = 0;
+            for (int jj = 0; jj < j; ++jj) taken |= (hot[jj] == e);
+            if (taken) continue;
+            if (best < 0 || freq[e] > freq[best]) best = e;     /* ascending e: ties keep the lower id */
+        }
+        hot[j] = best;
+    }
+}
+
+/* One step of the warm ring.  Slots [0, n_hot) hold the hot set and are never
+ * evicted; slots [n_hot, n_slots) are the ring.  last_use[s] is the step a
+ * slot was last used (0 = never; steps count from 1); slots already used in
+ * this step carry last_use == step.  For each missing expert, in ascending
+ * id order (miss[0..n_miss)), the ring slot with the oldest last_use, ties to
+ * the lowest slot, among those not used in this step, takes it: the slot's
+ * previous expert (if any) stops being resident, the new one becomes
+ * resident there, the slot is stamped with this step, and (expert, slot) is
+ * listed as a copy to make.  A missing expert that finds no such slot stays
+ * cold for this step.  Returns the number of copies. */
+int orc_warm_ring_step(int n_hot, int n_slots, const int32_t* miss, int n_miss, uint32_t step,
+                       int32_t* slot_of_expert, int32_t* expert_of_slot, uint32_t* last_use,
+                       int32_t* copy_expert, int32_t* copy_slot) {
+    int n_copy = 0;
+    for (int i = 0; i < n_miss; ++i) {
+        const int e = miss[i];
+        int victim = -1;
+        for (int s = n_hot; s < n_slots; ++s) {
+            if (last_use[s] == step) continue;
+            if (victim < 0 || last_use[s] < last_use[victim]) victim = s;   /* ascending s: ties keep the lower slot */
+        }
+        if (victim < 0) continue;
+        const int old = expert_of_slot[victim];
+        if (old >= 0) slot_of_expert[old] = -1;
+        expert_of_slot[victim] = e;
+        slot_of_expert[e] = victim;
+        last_use[victim] = step;
+        copy_expert[n_copy] = e;
+        copy_slot[n_copy] = victim;
+        ++n_copy;
+    }
+    return n_copy;
+}

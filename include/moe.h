@@ -409,6 +409,92 @@ int moe_combine_shared(const moe_dims* dims, const uint16_t* y_rows, const int32
  * MOE_ERR_INVALID_ARG before anything is enqueued.  Asynchronous on `stream`. */
 int moe_zero_point_bias(int64_t n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias, void* stream);
 
+/* ------------------------------------------------------ residency tiers
+ * "Luce Spark" page, sec. 1 (calibrated placement: count how often traffic
+ * routes to each expert and keep the most used set resident, the hot tier)
+ * and sec. 2 (a bounded ring of spare slots: an expert routed to while not
+ * resident is copied from pinned host memory into a spare slot, the least
+ * recently used slot giving way; hot / warm / cold tiers); "Strata" page,
+ * sec. 2.4 (copies run on a stream of their own beside the compute) and
+ * sec. 4.5 (pinned host memory).
+ *
+ * The layer's E experts live in pinned host memory in the moe_qweights
+ * layout (the cold tier; device-visible pointers, e.g. hipHostMalloc); an
+ * HBM pool of n_slots expert slots, in the same layout with n_slots experts,
+ * holds the resident ones.  Slots [0, n_hot) hold the hot set and are never
+ * evicted; slots [n_hot, n_slots) are the warm ring.  The tables are device
+ * memory the caller owns and the calls below update:
+ *   slot_of_expert  int32 [E]: slot holding expert e, -1 when cold; it is the
+ *                   resident table of the slot lookup (moe_slot_lookup /
+ *                   moe_route_dispatch with this n_slots);
+ *   expert_of_slot  int32 [n_slots]: expert in slot s, -1 when empty;
+ *   last_use        uint32 [n_slots]: step of the slot's last use, 0 = never.
+ *                   Steps count up from 1; the slot lookup of each step stamps
+ *                   the slots it hits (pass last_use and the same step).
+ * A step: slot lookup (stamps hits, lists misses) -> moe_residency_plan ->
+ * moe_expert_copy of its copy list (src = host experts, dst = pool), on a
+ * second stream after an event -> the FFN on list 0 with the pool's weights,
+ * overlapping the copy -> (after the copy's event) the FFN on list 1 with the
+ * pool's weights and on list 2 with the host experts -> combine.  The FFN's
+ * rows are the same bits as with every expert resident. */
+typedef struct moe_residency {
+    int32_t n_hot;            /* 0 <= n_hot <= n_slots */
+    int32_t n_slots;          /* 1 <= n_slots <= E */
+    int32_t* slot_of_expert;  /* [E] */
+    int32_t* expert_of_slot;  /* [n_slots] */
+    uint32_t* last_use;       /* [n_slots] */
+} moe_residency;
+
+/* Routing-frequency counters: freq[e] += expert_counts[e] for e < E (the
+ * per-expert pair counts moe_permute / moe_route_dispatch wrote).  freq:
+ * uint32 [E] device memory (wraps at 2^32). */
+int moe_route_counts(const moe_dims* dims, const int32_t* expert_counts, uint32_t* freq, void* stream);
+
+/* The calibrated hot set: hot[0..n) = the n experts of highest freq, most used
+ * first, equal counts to the lower id.  0 <= n <= E; hot: int32 [n]. */
+int moe_hot_set(const moe_dims* dims, const uint32_t* freq, int32_t n, int32_t* hot, void* stream);
+
+/* One step of the warm ring, on the device.  Inputs: this step's miss list
+ * (miss_experts / n_miss, ascending, from the slot lookup on r's tables) and
+ * FFN work list (work_list / n_work, from moe_permute).  For each missing
+ * expert in ascending id order, the ring slot with the oldest last_use (ties
+ * to the lowest slot) that this step has not used takes it: the slot's old
+ * expert goes cold, the tables point the new one at the slot, the slot is
+ * stamped with `step`, and (expert, slot) is appended to copies.  A missing
+ * expert that finds no such slot stays cold this step.  Outputs:
+ *   copies       int32 [n_slots][2]: (expert, slot) pairs, *n_copy of them;
+ *   lists        int32 [MOE_RESIDENCY_LISTS][capacity][MOE_WORK_ENTRY_INTS]
+ *                (capacity from moe_work_list_capacity), 16-byte aligned: the
+ *                work list's entries in order, split by where their expert is
+ *                read: list 0 = resident before this step, list 1 = copied in
+ *                this step (expert field replaced by the slot in both), list 2
+ *                = still cold (expert field unchanged, read from host memory);
+ *   list_counts  int32 [MOE_RESIDENCY_LISTS]: entries in each list.
+ * Each list is a work list for the FFN calls with n_work = list_counts + i. */
+#define MOE_RESIDENCY_LISTS 3
+int moe_residency_plan(const moe_dims* dims, const moe_residency* r, const int32_t* miss_experts,
+                       const int32_t* n_miss, uint32_t step, const int32_t* work_list, const int32_t* n_work,
+                       int32_t* lists, int32_t* list_counts, int32_t* copies, int32_t* n_copy, void* stream);
+
+/* Copy experts between two weight sets of one layer shape and code width:
+ * for i < *n_copy, expert copies[2i] of src (E experts) into slot copies[2i+1]
+ * of dst (n_dst experts), all three matrices' codes, scales and biases.  src
+ * may be pinned host memory (device-visible pointers).  max_copies bounds
+ * *n_copy (the grid is sized for it); pairs out of range are skipped. */
+int moe_expert_copy(const moe_dims* dims, int bits, const moe_qweights* src, const moe_qweights* dst, int32_t n_dst,
+                    const int32_t* copies, const int32_t* n_copy, int32_t max_copies, void* stream);
+
+/* Measurement aid, not a step of the layer: reads `bytes` of device memory at
+ * `src` once, with 16-byte loads spread over every compute unit, and writes
+ * the XOR of what each workgroup read into sink[0 .. MOE_STREAM_SINK_INTS),
+ * so that the HBM read rate of a plain stream can be timed beside the expert
+ * FFN's weight stream ("Strata" page, sec. 1.2: decode is bound by how fast
+ * weights move).  src 16-byte aligned and bytes a multiple of 16; sink
+ * uint32 [MOE_STREAM_SINK_INTS] device memory, 4-byte aligned.  bytes == 0 is
+ * a no-op.  Errors: MOE_ERR_INVALID_ARG before anything is enqueued. */
+#define MOE_STREAM_SINK_INTS 4096
+int moe_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

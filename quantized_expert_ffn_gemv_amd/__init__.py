@@ -31,7 +31,8 @@ EXPORTS = (
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_expert_gateup", "moe_expert_down", "moe_expert_ffn_fused",
     "moe_expert_ffn_fused_shared", "moe_expert_ffn_fused_noalloc",
     "moe_combine", "moe_combine_shared",
-    "moe_zero_point_bias",
+    "moe_zero_point_bias", "moe_stream_read",
+    "moe_route_counts", "moe_hot_set", "moe_residency_plan", "moe_expert_copy",
 )
 
 
@@ -60,6 +61,12 @@ class DispatchC(ctypes.Structure):
 
 class QWeightsC(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p * 3), ("scale", ctypes.c_void_p * 3), ("bias", ctypes.c_void_p * 3)]
+
+
+class ResidencyC(ctypes.Structure):
+    """struct moe_residency (include/moe.h)."""
+    _fields_ = [("n_hot", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("slot_of_expert", ctypes.c_void_p),
+                ("expert_of_slot", ctypes.c_void_p), ("last_use", ctypes.c_void_p)]
 
 
 _lib = None
@@ -96,6 +103,11 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.argtypes = [Dp, P, P, P, P, P, P]
     L.moe_combine_shared.argtypes = [Dp, P, P, P, P, P, P, P, P, P, P]
     L.moe_zero_point_bias.argtypes = [ctypes.c_int64, P, P, P, P]
+    L.moe_stream_read.argtypes = [P, sz, P, P]
+    L.moe_route_counts.argtypes = [Dp, P, P, P]
+    L.moe_hot_set.argtypes = [Dp, P, i32, P, P]
+    L.moe_residency_plan.argtypes = [Dp, ctypes.POINTER(ResidencyC), P, P, u32, P, P, P, P, P, P, P]
+    L.moe_expert_copy.argtypes = [Dp, ctypes.c_int, Wp, Wp, i32, P, P, i32, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -195,6 +207,8 @@ WORK_TILE_ROWS, WORK_ENTRY_INTS = 16, 20     # MOE_WORK_TILE_ROWS, MOE_WORK_ENTR
 DISPATCH_SYNC_INTS = 576                     # MOE_DISPATCH_SYNC_INTS
 FFN_SYNC_INTS = 32800                        # MOE_FFN_SYNC_INTS (the last 32: the fault flag)
 NOALLOC_WORKSPACE_BYTES = 16 << 20           # MOE_NOALLOC_WORKSPACE_BYTES
+STREAM_SINK_INTS = 4096                      # MOE_STREAM_SINK_INTS
+RESIDENCY_LISTS = 3                          # MOE_RESIDENCY_LISTS
 
 
 def work_list_capacity(d: Dims) -> int:
@@ -317,12 +331,49 @@ def zero_point_bias(scale, zeros, bias, stream=None):
     _check(lib().moe_zero_point_bias(n, _ptr(scale), _ptr(zeros), _ptr(bias), _stream(stream)))
 
 
-from .layer import LayerBuffers, SharedBuffers, SharedExpert, layer_forward  # noqa: E402  (orchestration of the calls above)
+def stream_read(src, sink, nbytes: Optional[int] = None, stream=None):
+    """moe_stream_read: one streaming read of `src` (nbytes, default all of it);
+    sink is a uint32/int32 device tensor of STREAM_SINK_INTS entries."""
+    n = _nbytes(src) if nbytes is None else int(nbytes)
+    _check(lib().moe_stream_read(_ptr(src), n, _ptr(sink), _stream(stream)))
+
+
+def route_counts(d: Dims, expert_counts, freq, stream=None):
+    """moe_route_counts: freq[e] += expert_counts[e] (uint32 counters as int32 tensors)."""
+    _check(lib().moe_route_counts(ctypes.byref(d), _ptr(expert_counts), _ptr(freq), _stream(stream)))
+
+
+def hot_set(d: Dims, freq, n: int, hot, stream=None):
+    """moe_hot_set: hot[0..n) = the n most routed experts (ties to the lower id)."""
+    _check(lib().moe_hot_set(ctypes.byref(d), _ptr(freq), int(n), _ptr(hot), _stream(stream)))
+
+
+def residency_plan(d: Dims, n_hot: int, n_slots: int, slot_of_expert, expert_of_slot, last_use, miss, n_miss,
+                   step: int, work_list, n_work, lists, list_counts, copies, n_copy, stream=None):
+    """moe_residency_plan: one step of the warm ring (victims, tables, copy list,
+    and the work list split into resident / copied / cold lists)."""
+    r = ResidencyC(int(n_hot), int(n_slots), _ptr(slot_of_expert), _ptr(expert_of_slot), _ptr(last_use))
+    _check(lib().moe_residency_plan(ctypes.byref(d), ctypes.byref(r), _ptr(miss), _ptr(n_miss),
+                                    int(step) & 0xFFFFFFFF, _ptr(work_list), _ptr(n_work), _ptr(lists),
+                                    _ptr(list_counts), _ptr(copies), _ptr(n_copy), _stream(stream)))
+
+
+def expert_copy(d: Dims, bits: int, src: "QWeights", dst: "QWeights", n_dst: int, copies, n_copy, max_copies: int,
+                stream=None):
+    """moe_expert_copy: experts copies[2i] of src into slots copies[2i+1] of dst."""
+    ws, wd = src.c_struct(), dst.c_struct()
+    _check(lib().moe_expert_copy(ctypes.byref(d), int(bits), ctypes.byref(ws), ctypes.byref(wd), int(n_dst),
+                                 _ptr(copies), _ptr(n_copy), int(max_copies), _stream(stream)))
+
+
+from .layer import (LayerBuffers, ResidentExperts, SharedBuffers, SharedExpert, layer_forward,  # noqa: E402
+                    resident_layer_forward)  # (orchestration of the calls above)
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
-    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "expert_ffn_fused_shared", "expert_ffn_fused_noalloc", "NOALLOC_WORKSPACE_BYTES", "combine", "combine_shared", "zero_point_bias", "LayerBuffers", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
+    "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "expert_ffn_fused_shared", "expert_ffn_fused_noalloc", "NOALLOC_WORKSPACE_BYTES", "combine", "combine_shared", "zero_point_bias", "stream_read", "STREAM_SINK_INTS", "route_counts", "hot_set", "residency_plan",
+    "expert_copy", "RESIDENCY_LISTS", "ResidencyC", "LayerBuffers", "ResidentExperts", "resident_layer_forward", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
     "group_major", "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

@@ -513,4 +513,98 @@ int moe_zero_point_bias(int64_t n, const uint16_t* scale, const uint8_t* zeros, 
     return ok();
 }
 
+int moe_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    const char* fn = "moe_stream_read";
+    if (bytes == 0) return ok();
+    REQUIRE_PTR(src, 16);
+    REQUIRE_PTR(sink, 4);
+    if (bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: bytes = %zu is not a multiple of 16", fn, bytes);
+    const int st = moe::launch_stream_read(src, bytes, sink, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_route_counts(const moe_dims* d, const int32_t* counts, uint32_t* freq, void* stream) {
+    const char* fn = "moe_route_counts";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    REQUIRE_PTR(counts, 4);
+    REQUIRE_PTR(freq, 4);
+    st = moe::launch_route_counts(counts, freq, d->E, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_hot_set(const moe_dims* d, const uint32_t* freq, int32_t n, int32_t* hot, void* stream) {
+    const char* fn = "moe_hot_set";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    if (n < 0 || n > d->E) return fail(MOE_ERR_INVALID_ARG, "%s: n = %d outside [0, E = %d]", fn, n, d->E);
+    if (n == 0) return ok();
+    REQUIRE_PTR(freq, 4);
+    REQUIRE_PTR(hot, 4);
+    st = moe::launch_hot_set(freq, d->E, n, hot, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_residency_plan(const moe_dims* d, const moe_residency* r, const int32_t* miss, const int32_t* n_miss,
+                       uint32_t step, const int32_t* work_list, const int32_t* n_work, int32_t* lists,
+                       int32_t* list_counts, int32_t* copies, int32_t* n_copy, void* stream) {
+    const char* fn = "moe_residency_plan";
+    int st = check_dims(fn, d, false, false);
+    if (st) return st;
+    if (r == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: residency is NULL", fn);
+    if (r->n_slots < 1 || r->n_slots > d->E || r->n_hot < 0 || r->n_hot > r->n_slots)
+        return fail(MOE_ERR_INVALID_ARG, "%s: need 0 <= n_hot (%d) <= n_slots (%d) <= E (%d), n_slots >= 1", fn,
+                    r->n_hot, r->n_slots, d->E);
+    if (step == 0) return fail(MOE_ERR_INVALID_ARG, "%s: step 0 marks never-used slots; steps count from 1", fn);
+    REQUIRE_PTR(r->slot_of_expert, 4);
+    REQUIRE_PTR(r->expert_of_slot, 4);
+    REQUIRE_PTR(r->last_use, 4);
+    REQUIRE_PTR(miss, 4);
+    REQUIRE_PTR(n_miss, 4);
+    REQUIRE_PTR(n_work, 4);
+    REQUIRE_PTR(list_counts, 4);
+    REQUIRE_PTR(copies, 4);
+    REQUIRE_PTR(n_copy, 4);
+    const long cap = moe::work_capacity(*d);
+    if (cap > 0) {
+        REQUIRE_PTR(work_list, 16);
+        REQUIRE_PTR(lists, 16);
+    }
+    moe::PlanArgs a{};
+    a.E = d->E; a.n_hot = r->n_hot; a.n_slots = r->n_slots; a.cap = (int)cap; a.step = step;
+    a.slot_of_expert = r->slot_of_expert; a.expert_of_slot = r->expert_of_slot; a.last_use = r->last_use;
+    a.miss = miss; a.n_miss = n_miss; a.work = work_list; a.n_work = n_work;
+    a.lists = lists; a.list_counts = list_counts; a.copies = copies; a.n_copy = n_copy;
+    st = moe::launch_residency_plan(a, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
+int moe_expert_copy(const moe_dims* d, int bits, const moe_qweights* src, const moe_qweights* dst, int32_t n_dst,
+                    const int32_t* copies, const int32_t* n_copy, int32_t max_copies, void* stream) {
+    const char* fn = "moe_expert_copy";
+    int st = check_dims(fn, d, true, true);
+    if (st) return st;
+    if (bits != 2 && bits != 4) return fail(MOE_ERR_UNSUPPORTED, "%s: bits = %d (2 or 4)", fn, bits);
+    if (src == nullptr || dst == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: weights is NULL", fn);
+    if (n_dst < 1) return fail(MOE_ERR_INVALID_ARG, "%s: n_dst = %d", fn, n_dst);
+    if (max_copies < 0 || max_copies > 65535) return fail(MOE_ERR_INVALID_ARG, "%s: max_copies = %d", fn, max_copies);
+    if (max_copies == 0) return ok();
+    REQUIRE_PTR(copies, 4);
+    REQUIRE_PTR(n_copy, 4);
+    for (int m = 0; m < 3; ++m) {
+        if (!src->q[m] || !src->scale[m] || !src->bias[m] || !dst->q[m] || !dst->scale[m] || !dst->bias[m])
+            return fail(MOE_ERR_INVALID_ARG, "%s: matrix %d has a NULL pointer", fn, m);
+        if (!aligned(src->q[m], 16) || !aligned(dst->q[m], 16) || !aligned(src->scale[m], 16) ||
+            !aligned(dst->scale[m], 16) || !aligned(src->bias[m], 16) || !aligned(dst->bias[m], 16))
+            return fail(MOE_ERR_INVALID_ARG, "%s: matrix %d is not 16-byte aligned", fn, m);
+    }
+    st = moe::launch_expert_copy(*d, bits, *src, *dst, n_dst, copies, n_copy, max_copies, as_stream(stream));
+    if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
+    return ok();
+}
+
 }  // extern "C"

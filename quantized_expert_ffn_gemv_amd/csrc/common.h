@@ -214,5 +214,28 @@ int launch_combine_shared(const moe_dims& d, const uint16_t* y, const int32_t* p
                           const uint16_t* ys, const uint16_t* x, const float* w, const uint16_t* residual,
                           uint16_t* out, float* gate_out, hipStream_t s);
 int launch_zero_point_bias(long n, const uint16_t* scale, const uint8_t* zeros, uint16_t* bias, hipStream_t s);
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
+// Residency tiers (residency.hip).
+struct PlanArgs {
+    int E, n_hot, n_slots, cap;
+    uint32_t step;
+    int32_t* slot_of_expert;
+    int32_t* expert_of_slot;
+    uint32_t* last_use;
+    const int32_t* miss;
+    const int32_t* n_miss;
+    const int32_t* work;
+    const int32_t* n_work;
+    int32_t* lists;            // [3][cap][kWorkInts]
+    int32_t* list_counts;      // [3]
+    int32_t* copies;           // [n_slots][2]: (expert, slot)
+    int32_t* n_copy;
+};
+int launch_residency_plan(const PlanArgs& a, hipStream_t s);
+int launch_route_counts(const int32_t* counts, uint32_t* freq, int E, hipStream_t s);
+int launch_hot_set(const uint32_t* freq, int E, int n, int32_t* hot, hipStream_t s);
+int launch_expert_copy(const moe_dims& d, int bits, const moe_qweights& src, const moe_qweights& dst, int n_dst,
+                       const int32_t* copies, const int32_t* n_copy, int max_copies, hipStream_t s);
 
 }  // namespace moe

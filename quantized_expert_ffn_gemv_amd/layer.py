@@ -20,6 +20,12 @@ uses, scaled by a per-token sigmoid gate) ``combine_shared`` replaces
     ``SharedBuffers`` are allocated.  (A second stream measured slower here:
     the cross-stream event wait held the host for the whole step.)
 
+``ResidentExperts`` and ``resident_layer_forward`` run the step with the
+experts behind residency tiers (pinned host memory, an HBM pool of hot and
+warm slots): the plan kernel after the routing picks warm slots for the
+misses, the copies run on a second stream while the FFN of the experts
+already resident runs, then the FFN of the rest and the combine.
+
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
 from __future__ import annotations
@@ -29,9 +35,10 @@ from typing import Optional
 
 import torch
 
-from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, FFN_SYNC_INTS, OP_FFN, WORK_ENTRY_INTS, Dims, QWeights, combine,
-               combine_shared, dims, expert_ffn_fused, expert_ffn_fused_shared, expert_ffn_q2, expert_ffn_q4, permute, route_dispatch,
-               route_topk, slot_lookup, work_list_capacity, workspace_bytes)
+from . import (ALGO_AUTO, DISPATCH_SYNC_INTS, FFN_SYNC_INTS, OP_FFN, RESIDENCY_LISTS, WORK_ENTRY_INTS, Dims,
+               QWeights, combine, combine_shared, dims, expert_copy, expert_ffn_fused, expert_ffn_fused_shared,
+               expert_ffn_q2, expert_ffn_q4, permute, residency_plan, route_counts, route_dispatch, route_topk,
+               slot_lookup, work_list_capacity, workspace_bytes)
 
 
 @dataclass
@@ -57,6 +64,23 @@ class LayerBuffers:
     sync: torch.Tensor            # int32 [DISPATCH_SYNC_INTS], zeros (route_dispatch's counters)
     ffn_sync: torch.Tensor        # int32 [FFN_SYNC_INTS], zeros (expert_ffn_fused's counters)
     shared_rows: bool = False     # y_rows and workspace also hold a shared expert's T rows
+
+    def ffn_timed_out(self) -> bool:
+        """True if an expert_ffn_fused call on these buffers had a down item give
+        up waiting for its h (that call's rows are not valid).  Reads the flag at
+        the end of ffn_sync, so it waits for the stream's work so far."""
+        return bool(int(self.ffn_sync[FFN_SYNC_INTS - 32:].abs().sum().item()))
+
+    def counters_clean(self) -> bool:
+        """True if both counter buffers are back to all zeros, as every call that
+        completed normally leaves them (waits for the stream's work so far)."""
+        return int(self.sync.abs().sum().item()) == 0 and int(self.ffn_sync.abs().sum().item()) == 0
+
+    def reset_counters(self) -> None:
+        """After a time-out: zero both counter buffers (a fill kernel on the
+        current stream) before the next call uses them."""
+        self.sync.zero_()
+        self.ffn_sync.zero_()
 
     @staticmethod
     def allocate(d: Dims, bits: int = 4, algo: int = ALGO_AUTO, device="cuda",
@@ -169,3 +193,107 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
         ys, gate_out = sb.buf.y_rows, sb.gate_out
     combine_shared(d, buf.y_rows, buf.pair_to_row, buf.topk_w, ys, x, shared.gate_w, residual, out, gate_out,
                    stream)
+
+
+@dataclass
+class ResidentExperts:
+    """The residency tiers of one layer's experts ("Luce Spark" page, sec. 1-2):
+    every expert in pinned host memory (cold, `host`), an HBM pool of n_slots
+    slots (`pool`): slots [0, n_hot) the calibrated hot set, the rest the warm
+    ring.  The tables, the routing-frequency counters and the plan's outputs
+    are device tensors; the library's kernels update them at every step."""
+    d: Dims
+    bits: int
+    n_hot: int
+    n_slots: int
+    host: QWeights                # E experts, pinned host tensors (device-visible)
+    pool: QWeights                # n_slots experts, device tensors
+    slot_of_expert: torch.Tensor  # int32 [E], -1 = cold
+    expert_of_slot: torch.Tensor  # int32 [n_slots], -1 = empty
+    last_use: torch.Tensor        # int32 [n_slots] (uint32 step stamps, 0 = never)
+    freq: torch.Tensor            # int32 [E] (uint32 routing-frequency counters)
+    lists: torch.Tensor           # int32 [RESIDENCY_LISTS, capacity, WORK_ENTRY_INTS]
+    list_counts: torch.Tensor     # int32 [RESIDENCY_LISTS]
+    copies: torch.Tensor          # int32 [n_slots, 2]
+    n_copy: torch.Tensor          # int32 [1]
+
+    @staticmethod
+    def allocate(d: Dims, bits: int, host: QWeights, n_hot: int, n_slots: int, device="cuda") -> "ResidentExperts":
+        if not 0 <= n_hot <= n_slots <= d.E:
+            raise ValueError("need 0 <= n_hot <= n_slots <= E")
+        i32 = dict(dtype=torch.int32, device=device)
+        pool = QWeights(bits, [torch.empty((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=device) for t in host.q],
+                        [torch.empty((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=device) for t in host.scale],
+                        [torch.empty((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=device) for t in host.bias])
+        cap = max(work_list_capacity(d), 1)
+        return ResidentExperts(
+            d=d, bits=bits, n_hot=n_hot, n_slots=n_slots, host=host, pool=pool,
+            slot_of_expert=torch.full((d.E,), -1, **i32), expert_of_slot=torch.full((n_slots,), -1, **i32),
+            last_use=torch.zeros((n_slots,), **i32), freq=torch.zeros((d.E,), **i32),
+            lists=torch.empty((RESIDENCY_LISTS, cap, WORK_ENTRY_INTS), **i32),
+            list_counts=torch.zeros((RESIDENCY_LISTS,), **i32),
+            copies=torch.zeros((n_slots, 2), **i32), n_copy=torch.zeros((1,), **i32))
+
+    def install(self, experts: torch.Tensor, stream=None) -> None:
+        """Make slots 0 .. len(experts)-1 hold these experts (e.g. the hot set
+        from hot_set()), every other slot empty and every stamp 0: the tables
+        are set here and the weights copied from host memory by the library."""
+        n = int(experts.numel())
+        if n > self.n_slots:
+            raise ValueError("more experts than slots")
+        e = experts.to(torch.int32)
+        slots = torch.arange(n, dtype=torch.int32, device=e.device)
+        self.slot_of_expert.fill_(-1)
+        self.slot_of_expert[e.long()] = slots
+        self.expert_of_slot.fill_(-1)
+        self.expert_of_slot[:n] = e
+        self.last_use.zero_()
+        self.copies[:n, 0] = e
+        self.copies[:n, 1] = slots
+        self.n_copy.fill_(n)
+        expert_copy(self.d, self.bits, self.host, self.pool, self.n_slots, self.copies, self.n_copy, max(n, 1), stream)
+
+
+def resident_layer_forward(buf: LayerBuffers, res: ResidentExperts, x: torch.Tensor, w_router: torch.Tensor,
+                           router_bias: Optional[torch.Tensor], residual: torch.Tensor, out: torch.Tensor,
+                           step: int, algo: int = ALGO_AUTO, copy_stream=None, count: bool = True,
+                           host_doorbell=None) -> None:
+    """Enqueue one layer step with the experts behind the residency tiers
+    (steps count from 1).  Routing and the slot lookup run against res's
+    tables (stamping the slots they hit); the routing counters are updated
+    (count); the plan picks warm slots for the misses and splits the work
+    list; the copies from host memory run on copy_stream (or the current
+    stream) while the FFN of the experts already resident runs; then the FFN
+    of the experts copied in this step and of those still cold (read from host
+    memory), then the combine.  The expert rows are bit for bit those of
+    layer_forward with every expert resident."""
+    import torch as _t
+    d = buf.d
+    main = _t.cuda.current_stream() if copy_stream is not None else None
+    route_dispatch(d, x, w_router, router_bias, True, buf.logits, buf.topk_ids, buf.topk_w, res.slot_of_expert,
+                   res.n_slots, buf.pair_slot, buf.miss, buf.n_miss, buf.counts, buf.offsets, buf.sorted_pairs,
+                   buf.pair_to_row, buf.active, buf.n_active, buf.work_list, buf.n_work, host_doorbell,
+                   res.last_use, step, buf.sync)
+    if count:
+        route_counts(d, buf.counts, res.freq)
+    residency_plan(d, res.n_hot, res.n_slots, res.slot_of_expert, res.expert_of_slot, res.last_use, buf.miss,
+                   buf.n_miss, step, buf.work_list, buf.n_work, res.lists, res.list_counts, res.copies, res.n_copy)
+    n_warm = max(res.n_slots - res.n_hot, 1)
+    if copy_stream is not None:
+        planned = _t.cuda.Event()
+        planned.record(main)
+        copy_stream.wait_event(planned)
+        expert_copy(d, res.bits, res.host, res.pool, res.n_slots, res.copies, res.n_copy, n_warm,
+                    copy_stream.cuda_stream)
+        copied = _t.cuda.Event()
+        copied.record(copy_stream)
+    else:
+        expert_copy(d, res.bits, res.host, res.pool, res.n_slots, res.copies, res.n_copy, n_warm)
+    lists = [res.lists[i] for i in range(RESIDENCY_LISTS)]
+    counts = [res.list_counts[i:i + 1] for i in range(RESIDENCY_LISTS)]
+    expert_ffn_fused(d, res.bits, x, lists[0], counts[0], res.pool, buf.workspace, buf.y_rows, buf.ffn_sync, algo)
+    if copy_stream is not None:
+        main.wait_event(copied)
+    expert_ffn_fused(d, res.bits, x, lists[1], counts[1], res.pool, buf.workspace, buf.y_rows, buf.ffn_sync, algo)
+    expert_ffn_fused(d, res.bits, x, lists[2], counts[2], res.host, buf.workspace, buf.y_rows, buf.ffn_sync, algo)
+    combine(d, buf.y_rows, buf.pair_to_row, buf.topk_w, residual, out)

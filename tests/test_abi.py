@@ -236,6 +236,52 @@ def test_fused_shared_ffn_validation():
                                          None) == moe.ERR_UNSUPPORTED                                   # k + 1 > 32
 
 
+def test_stream_read_validation():
+    L = moe.lib()
+    assert L.moe_stream_read(None, 0, None, None) == moe.OK                       # nothing to read
+    assert L.moe_stream_read(None, 4096, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_stream_read(MISALIGNED, 4096, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_stream_read(FAKE, 4100, FAKE, None) == moe.ERR_INVALID_ARG         # not whole 16-byte words
+    assert "multiple of 16" in moe.last_error()
+    assert L.moe_stream_read(FAKE, 4096, None, None) == moe.ERR_INVALID_ARG
+
+
+def _res(**over):
+    f = dict(n_hot=2, n_slots=4, slot_of_expert=FAKE, expert_of_slot=FAKE, last_use=FAKE)
+    f.update(over)
+    return moe.ResidencyC(**f)
+
+
+def test_residency_validation():
+    L = moe.lib()
+    d = moe.dims(4, 256, 512, 8, 2)
+    plan = lambda r, step=1, lists=FAKE: L.moe_residency_plan(ctypes.byref(d), None if r is None else ctypes.byref(r),
+                                                               FAKE, FAKE, step, FAKE, FAKE, lists, FAKE, FAKE, FAKE,
+                                                               None)
+    assert plan(None) == moe.ERR_INVALID_ARG
+    assert plan(_res(n_slots=9)) == moe.ERR_INVALID_ARG                            # more slots than experts
+    assert plan(_res(n_hot=5)) == moe.ERR_INVALID_ARG                              # hot set beyond the pool
+    assert plan(_res(n_slots=0, n_hot=0)) == moe.ERR_INVALID_ARG
+    assert plan(_res(), step=0) == moe.ERR_INVALID_ARG                             # 0 marks never-used slots
+    assert "steps count from 1" in moe.last_error()
+    assert plan(_res(last_use=None)) == moe.ERR_INVALID_ARG
+    assert plan(_res(), lists=FAKE + 4) == moe.ERR_INVALID_ARG
+    assert L.moe_hot_set(ctypes.byref(d), FAKE, 9, FAKE, None) == moe.ERR_INVALID_ARG   # n > E
+    assert L.moe_hot_set(ctypes.byref(d), None, 0, None, None) == moe.OK
+    assert L.moe_hot_set(ctypes.byref(d), None, 3, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_route_counts(ctypes.byref(d), FAKE, None, None) == moe.ERR_INVALID_ARG
+    w = _qw()
+    copy = lambda bits=4, n_dst=4, maxc=4, src=w: L.moe_expert_copy(ctypes.byref(d), bits, ctypes.byref(src),
+                                                                    ctypes.byref(w), n_dst, FAKE, FAKE, maxc, None)
+    assert copy(bits=3) == moe.ERR_UNSUPPORTED
+    assert copy(n_dst=0) == moe.ERR_INVALID_ARG
+    assert copy(maxc=-1) == moe.ERR_INVALID_ARG
+    assert copy(maxc=0) == moe.OK
+    bad = _qw()
+    bad.q[1] = MISALIGNED
+    assert copy(src=bad) == moe.ERR_INVALID_ARG
+
+
 def test_noalloc_validation():
     L = moe.lib()
     d = moe.dims(4, 256, 512, 8, 2)

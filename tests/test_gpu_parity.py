@@ -15,6 +15,7 @@ import moe_inputs as mi
 import oracle
 import quantized_expert_ffn_gemv_amd as moe
 
+from work_tiles import expected_work_list
 from gpu_util import (check_combine_exact, check_ffn, check_logits, check_lookup, check_permute,
                       check_topk, run_layer, say, to_dev, to_host, tolerance_metrics, upload_layer)
 
@@ -127,6 +128,22 @@ RAGGED = [
 def test_ragged_shapes(shape, bits, algo):
     L = layer(shape.name, bits, shape)
     _stages(L, shape.tokens[0], seed=3, algo=algo)
+
+
+# A shape whose decode tiles do not fit LDS at T = 16 (the x tile alone is 96 KB),
+# so the matrix-core path takes the persistent kernels (the 64-expert layer's
+# kernels) at a small E and I: every element checked, both algorithms, both
+# code widths, several entries per expert and ragged rows.
+BIG_TILE = mi.LayerShape("big_tile", H=3072, E=4, k=2, I=2048, tokens=(16,), bits=(4, 2), zipf_s=None,
+                         n_resident=2)
+
+
+@pytest.mark.parametrize("algo", ALGOS, ids=ALGO_IDS)
+@pytest.mark.parametrize("bits", [4, 2])
+def test_persistent_kernel_shape_every_element(bits, algo):
+    L = layer(BIG_TILE.name, bits, BIG_TILE)
+    g, _, _ = _stages(L, 16, seed=8, algo=algo)
+    assert g["counts"].max() > 1
 
 
 @pytest.mark.parametrize("bits", [4, 2])

@@ -65,12 +65,12 @@ PER_CONFIG = [("a3b", 4, 1, 4, 1), ("a3b", 4, 8, 4, 2), ("a3b", 4, 32, 4, 4),
 
 # FFN kernels of each decode workload (the library's choice at these sizes)
 FFN_KERNELS = {
-    "e64": ("ffn_gateup_mfma_kernel", "ffn_down_mfma_kernel"),
+    "e64": ("ffn_gateup_mfma_kernel", "ffn_down_stream_kernel"),
     "a3b": ("ffn_fused_dec_kernel",),
     "e512": ("ffn_fused_dec_kernel",),
 }
 FFN_SOURCES = {
-    "e64": ("ffn_mfma.hip", "mfma_ops.h", "common.h"),
+    "e64": ("ffn_mfma.hip", "ffn_dec.hip", "mfma_ops.h", "common.h"),
     "a3b": ("ffn_dec.hip", "mfma_ops.h", "common.h"),
     "e512": ("ffn_dec.hip", "mfma_ops.h", "common.h"),
 }

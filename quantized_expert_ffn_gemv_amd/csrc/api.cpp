@@ -354,7 +354,7 @@ int moe_expert_gateup(const moe_dims* d, int bits, const uint16_t* x, const int3
 }
 
 int moe_expert_down(const moe_dims* d, int bits, const int32_t* work_list, const int32_t* n_work,
-                    const moe_qweights* w, int algo, const void* ws, size_t ws_bytes, uint16_t* y,
+                    const moe_qweights* w, int algo, void* ws, size_t ws_bytes, uint16_t* y,
                     void* stream) {
     const char* fn = "moe_expert_down";
     int st = check_ffn_args(fn, d, bits, work_list, n_work, w, algo, 2, 3);
@@ -363,8 +363,7 @@ int moe_expert_down(const moe_dims* d, int bits, const int32_t* work_list, const
     REQUIRE_PTR(y, 16);
     st = check_workspace(fn, d, bits, algo, ws, ws_bytes);
     if (st) return st;
-    moe::FfnArgs a = ffn_args(d, bits, nullptr, work_list, n_work, w,
-                              static_cast<float*>(const_cast<void*>(ws)), y);
+    moe::FfnArgs a = ffn_args(d, bits, nullptr, work_list, n_work, w, static_cast<float*>(ws), y);
     st = launch_down(moe::resolve_algo(*d, bits, algo), a, as_stream(stream));
     if (st) return fail(st, "%s: kernel launch failed: %s", fn, hipGetErrorString(hipGetLastError()));
     return ok();

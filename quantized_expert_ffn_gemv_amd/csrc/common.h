@@ -200,6 +200,21 @@ bool dec_gateup_fits(const moe_dims& d);
 bool dec_down_fits(const moe_dims& d);
 int launch_gateup_dec(const FfnArgs& a, hipStream_t s);
 int launch_down_dec(const FfnArgs& a, hipStream_t s);
+int launch_down_stream(const FfnArgs& a, hipStream_t s);
+
+// The streaming down (shapes whose h tile does not fit LDS): output rows per
+// row block, and workgroups per launch (two per CU of a 256-CU device).  Its
+// arrival counters and partial sums follow the h planes in the workspace;
+// the gate/up kernels clear the counters.
+constexpr int kStreamRows = 128;
+constexpr int kStreamGrid = 512;
+struct SplitSpace {
+    int32_t* ctr;       // [cap][H / kStreamRows]
+    float* part;        // [2 kStreamGrid][rows_cap][kStreamRows]
+    int n_ctr;          // 0: the down projection does not stream at these dims
+};
+size_t down_split_bytes(const moe_dims& d);
+SplitSpace down_split_space(const moe_dims& d, void* ws);
 // err: where a down item that gives up waiting writes 1 (NULL: the flag at the
 // end of sync).
 int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s, int32_t* err = nullptr);

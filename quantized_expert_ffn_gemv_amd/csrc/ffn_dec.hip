@@ -59,6 +59,9 @@ struct DecParams {
     int rows_cap;       // token rows of the LDS tile: min(16, T)
     int n_shared;       // shared-expert tiles after the routed entries (0: none)
     int shared_row0;    // first row of the shared expert's rows (the routed pair count)
+    int32_t* split_ctr; // streaming down: arrival counters [cap][ipe] (gate/up clears them)
+    float* split_part;  // streaming down: partial sums [2 G][rows_cap][RI]
+    int n_split_ctr;    // gate/up: counters to clear (0: none)
 };
 
 __host__ __device__ constexpr size_t round_dma(size_t b) { return (b + kDma - 1) / kDma * kDma; }
@@ -420,6 +423,8 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
 template <int BITS, int RW, int D, bool SHARED = false>
 __global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (blockIdx.x == 0)                                  // the streaming down's counters start at zero
+        for (int i = threadIdx.x; i < p.n_split_ctr; i += 256) p.split_ctr[i] = 0;
     gateup_item<BITS, RW, D, false>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
 }
 
@@ -582,6 +587,271 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
     down_item<BITS, RT, D, false>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
 }
 
+// ------------------------------------------------------------ streaming down
+// The down projection for shapes whose h tile does not fit LDS (a large
+// intermediate size I).  Work: every (work-list entry, block of RI = 64 RT
+// output rows, group of K) unit, n_work * ipe * NG of them, flattened in that
+// order and cut into G equal ranges, one per workgroup (G: two workgroups per
+// CU).  Such shapes have few entries (16 pairs over about 7 experts at the
+// 64-expert shape, 260 row blocks of full K), so whole row blocks per
+// workgroup would leave half of the chip idle; equal ranges keep every
+// workgroup busy to the end.  A range covers the tail of one row block, whole
+// row blocks, and the head of another: the row blocks it covers whole are
+// written straight to y; a part of a row block leaves its float partial sums
+// in the workspace, and the last of the row block's workgroups to arrive (a
+// counter per row block) adds the parts in the order of K and writes y.
+// Workgroup b takes range (b % 8) (G / 8) + b / 8, so the ranges of one XCD
+// are adjacent and an entry's h rows are fetched into few L2s.
+// In a part of a row block, the item's h rows pass through LDS one chunk of
+// CG groups of K at a time, double-buffered: chunk c + 1 goes straight from
+// L2 into the other buffer (direct-to-LDS loads, no registers) while chunk c
+// is consumed, and the code ring runs on across chunk boundaries.  The four
+// waves share each staged chunk, so a part reads its h rows once, not once
+// per wave.
+// Packed planes: the A operand's 16 rows hold the three bf16 planes of h for
+// the tile's n tokens, plane-major (row 16 b + r is plane r' / n, token r' % n
+// for r' = 16 b + r < 3 n), so one MFMA per row tile and step covers all three
+// planes, and one all-ones MFMA gives every packed row's group sum: 4 (RT + 1)
+// MFMAs per group per row block b, against 4 (3 RT + 3) with one plane per
+// MFMA.  Each packed row is folded with its own sum, and the three planes of a
+// token are added at the end, in plane order.
+// Wave wid computes rows 16 RT wid .. +16 RT of the row block.  LDS: two h
+// buffers [3 n][CG][16 pieces of 16 B] (row r's pieces swizzled by r & 15,
+// like the decode tile), then the row block's raw fp16 scales and biases
+// [RI][NG]; after the K loop the h buffers hold the packed rows' results
+// [3 n][RI] float.
+// Waits: a wave's loads complete in issue order.  The first chunk is waited
+// for past the D ring slots issued after it; every later chunk's loads are
+// issued at the start of the chunk before it, and exactly CG RT ring loads
+// follow them before the wait at that chunk's end.
+struct SplitRange {
+    long long total;    // units: n_work * ipe * NG
+    int G;              // workgroups holding a non-empty range: min(grid, total)
+};
+
+__device__ __forceinline__ long long split_start(const SplitRange& r, int v) {
+    return (long long)v * r.total / r.G;
+}
+
+// The range holding unit u: the largest v with split_start(v) <= u.
+__device__ __forceinline__ int split_owner(const SplitRange& r, long long u) {
+    return (int)(((u + 1) * r.G - 1) / r.total);
+}
+
+// Partial-sum slot of range v's part of the row block starting at unit u0:
+// 2 v for the range's first part, 2 v + 1 for its last.
+__device__ __forceinline__ int split_slot(const SplitRange& r, int v, long long u0) {
+    return 2 * v + (split_start(r, v) < u0 ? 1 : 0);
+}
+
+// Arrive at `counter` (out of `n` arrivals); true in every thread of the last
+// workgroup to arrive.  Partial sums pass between workgroups as device-scope
+// atomic stores and loads, which bypass the non-coherent per-CU caches; the
+// full s_waitcnt before the count makes this workgroup's stores complete
+// before its arrival is counted.
+__device__ __forceinline__ bool split_arrive(int32_t* counter, int n, int* flag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+    __syncthreads();
+    return *flag != 0;
+}
+
+template <int BITS, int RT, int D, int CG, int NBM>
+__device__ __forceinline__ void down_stream_part(const DecParams& p, const DecItem& it, int ga, int gb,
+                                                 uint8_t* smem, const SplitRange& sr, int v, long long u0) {
+    constexpr int LB = 128 * BITS / 8 / 4;
+    constexpr int LW = LB / 4;
+    constexpr int RI = 64 * RT;
+    constexpr int U = CG > D ? CG : D;         // groups per unrolled block: whole chunks and ring turns
+    static_assert(U % CG == 0 && U % D == 0, "chunks and ring turns must tile the block");
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.H, I = p.I, NG = I / kGroup;
+    const int n = it.n, rows3 = 3 * n;         // packed rows
+    const int NB = (rows3 + 15) / 16;          // row blocks of 16 (NB <= NBM)
+    const int rowb = CG * 256;                 // one packed row of a chunk in LDS
+    const int buf_b = (int)round_dma((size_t)3 * p.rows_cap * rowb);
+    const int sc_bytes = RI * NG * 2;
+    const int sc_stride = (int)round_dma(sc_bytes);
+    const int nch = (gb - ga + CG - 1) / CG;   // chunks of this part
+    uint8_t* scl = smem + 2 * (size_t)buf_b;
+
+    // ---- chunk c of the packed h rows into buffer c & 1: piece (row r, group
+    // gl, slot cs) holds 16-byte chunk cs ^ (r & 15) of row r's group; pieces
+    // past the 3 n rows (the last 1 KB load's tail) reload row 0 into slack,
+    // and groups past the part (the last chunk's tail) reload the last group
+    const size_t plane = (size_t)p.P * I;
+    auto stage = [&](int c) {
+        uint8_t* dst = smem + (size_t)(c & 1) * buf_b;
+        const int pieces = (rows3 * rowb + kDma - 1) / kDma;
+        for (int i = wid; i < pieces; i += 4) {
+            const int slot = i * (kDma / 16) + lane;
+            const int cs = slot & 15, rest = slot >> 4, gl = rest % CG;
+            int r = rest / CG;
+            r = r < rows3 ? r : 0;
+            const int pl = r / n, j = r - pl * n;
+            const int g = min(ga + c * CG + gl, gb - 1);
+            const uint16_t* src = p.hp + pl * plane + (size_t)(it.row0 + j) * I + (size_t)g * kGroup + 8 * (cs ^ (r & 15));
+            dma16(src, dst + i * kDma);
+        }
+    };
+    {
+        const size_t first = ((size_t)it.e * H + (size_t)it.rb * RI) * NG;
+        dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
+        dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
+    }
+    stage(0);
+
+    // ---- code ring: RT rows of this lane, groups ga .. gb
+    const int rloc = 16 * RT * wid + m;
+    const size_t gstride = (size_t)H * (4 * LB);
+    const uint8_t* cp = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
+    uint32_t rc[D][RT][LW];
+    auto issue = [&](int slot, int g) {
+        const size_t off = (size_t)(g < gb ? g : gb - 1) * gstride;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const uint8_t* src = cp + (size_t)(16 * rt) * (4 * LB) + off;
+            if constexpr (BITS == 4) {
+                const uint4 A = *reinterpret_cast<const uint4*>(src);
+                rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y; rc[slot][rt][2] = A.z; rc[slot][rt][3] = A.w;
+            } else {
+                const uint2 A = *reinterpret_cast<const uint2*>(src);
+                rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y;
+            }
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, ga + d);
+    wait_vmem<RT * D>();                       // the scales and chunk 0 (older than the ring loads)
+    lds_barrier();
+
+    // packed row of this lane in block b (rows past 3 n read row 0; never stored)
+    int roff[NBM], coff[NBM][4];
+#pragma unroll
+    for (int b = 0; b < NBM; ++b) {
+        const int r = 16 * b + m < rows3 ? 16 * b + m : 0;
+        roff[b] = r * rowb;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) coff[b][st] = 16 * ((4 * q + st) ^ (r & 15));
+    }
+    const uint16_t* dsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NG;
+    const uint16_t* dbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NG;
+    const uint32_t ONES[4] = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
+    floatx4_t acc[NBM][RT];
+#pragma unroll
+    for (int b = 0; b < NBM; ++b)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[b][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int g0 = ga; g0 < gb; g0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u, gl = u % CG, c = (g - ga) / CG, d = u % D;
+            if (gl == 0 && c + 1 < nch) stage(c + 1);           // the other buffer: its chunk was read before the last barrier
+            if (g < gb) {
+                const uint8_t* hb = smem + (size_t)(c & 1) * buf_b + gl * 256;
+#pragma unroll
+                for (int b = 0; b < NBM; ++b) {
+                    if (b < NB) {                                 // uniform per workgroup
+                        floatx4_t C[RT], Cx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) C[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int st = 0; st < 4; ++st) {
+                            const uint4 a4 = *reinterpret_cast<const uint4*>(hb + roff[b] + coff[b][st]);
+                            const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                            for (int rt = 0; rt < RT; ++rt) {
+                                uint32_t B[4];
+                                code_operand<BITS>(rc[d][rt], st, B);
+                                C[rt] = mfma16(A, B, C[rt]);
+                            }
+                            Cx = mfma16(A, ONES, Cx);             // group sum of every packed row
+                        }
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            fold<BITS>(acc[b][rt], C[rt], dsc[16 * rt * NG + g], dbi[16 * rt * NG + g], Cx);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue(d, g + D);                            // past the part: reloads its last group, unused
+            if (gl == CG - 1 && c + 1 < nch) {
+                wait_vmem<CG * RT>();                   // chunk c + 1: issued before this chunk's CG RT ring loads
+                lds_barrier();                          // every wave's pieces landed; chunk c no longer read
+            }
+        }
+    }
+
+    // ---- the packed rows' results to LDS [3 n][RI]
+    lds_barrier();                                      // the h buffers are no longer read
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int b = 0; b < NBM; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * b + 4 * q + i;
+            if (b < NB && r < rows3)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) red[r * RI + rloc + 16 * rt] = acc[b][rt][i];
+        }
+    lds_barrier();
+    uint16_t* yb = p.y + (size_t)it.row0 * H + (size_t)it.rb * RI;
+    if (ga == 0 && gb == NG) {                          // the whole row block: y = hi + mid + lo in bf16
+        for (int o = tid; o < n * RI; o += 256) {
+            const int t = o / RI, col = o - t * RI;
+            const float y = (red[t * RI + col] + red[(n + t) * RI + col]) + red[(2 * n + t) * RI + col];
+            yb[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(y);
+        }
+        return;
+    }
+    // a part: its sums to slot split_slot(v, u0); the last part to arrive adds
+    // the parts of the row block in the order of their ranges (of K)
+    const int rsz = p.rows_cap * RI;
+    float* mine = p.split_part + (size_t)split_slot(sr, v, u0) * rsz;
+    for (int o = tid; o < n * RI; o += 256) {
+        const int t = o / RI, col = o - t * RI;
+        const float y = (red[t * RI + col] + red[(n + t) * RI + col]) + red[(2 * n + t) * RI + col];
+        __hip_atomic_store(mine + o, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int vf = split_owner(sr, u0), vl = split_owner(sr, u0 + NG - 1);
+    int32_t* ctr = p.split_ctr + (size_t)it.entry * p.ipe + it.rb;
+    if (!split_arrive(ctr, vl - vf + 1, reinterpret_cast<int*>(scl))) return;   // the scales are no longer read
+    for (int o = tid; o < n * RI; o += 256) {
+        const int t = o / RI, col = o - t * RI;
+        float y = 0.f;
+        for (int w = vf; w <= vl; ++w)
+            y += __hip_atomic_load(p.split_part + (size_t)split_slot(sr, w, u0) * rsz + o, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        yb[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(y);
+    }
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+}
+
+template <int BITS, int RT, int D, int CG, int NBM>
+__global__ __launch_bounds__(256, 2) void ffn_down_stream_kernel(DecParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int NG = p.I / kGroup;
+    const int nw = min(ld_scalar(p.n_work, 0), p.cap);
+    SplitRange sr;
+    sr.total = (long long)(nw > 0 ? nw : 0) * p.ipe * NG;
+    sr.G = (int)min((long long)gridDim.x, sr.total);
+    const int b = (int)blockIdx.x, v = (b & 7) * ((int)gridDim.x >> 3) + (b >> 3);
+    if (v >= sr.G) return;
+    const long long end = split_start(sr, v + 1);
+    for (long long u = split_start(sr, v); u < end;) {
+        const long long blk = u / NG, u0 = blk * NG;
+        const int ga = (int)(u - u0), gb = (int)min((long long)NG, end - u0);
+        const DecItem it = dec_item_at<false>(p, (int)(blk / p.ipe), (int)(blk % p.ipe));
+        if (u > split_start(sr, v)) lds_barrier();      // the last part's LDS is no longer read
+        if (it.n > 0) down_stream_part<BITS, RT, D, CG, NBM>(p, it, ga, gb, smem, sr, v, u0);
+        u = u0 + gb;
+    }
+}
+
 // ------------------------------------------------------------ one-launch FFN
 // Gate/up and down in one launch.  The grid is cut into chunks of kFfnChunk
 // work-list entries; a chunk is its gate/up items, then its down items, each
@@ -647,6 +917,10 @@ static DecParams dec_params(const FfnArgs& a) {
     const size_t P = (size_t)p.P;
     p.hp = reinterpret_cast<uint16_t*>(ws);
     p.hpart = reinterpret_cast<float*>(ws + ((3 * P * d.I * sizeof(uint16_t) + 255) & ~(size_t)255));
+    const SplitSpace sp = down_split_space(d, a.h);
+    p.split_ctr = sp.ctr;
+    p.split_part = sp.part;
+    p.n_split_ctr = sp.n_ctr;
     return p;
 }
 
@@ -774,6 +1048,88 @@ static int down_dec_run(const FfnArgs& a, const moe_dims& d, DecParams p, hipStr
 int launch_down_dec(const FfnArgs& a, hipStream_t s) {
     if (a.d.T * a.d.k == 0) return MOE_OK;
     return down_dec_run<false>(a, a.d, dec_params(a), s);
+}
+
+// ------------------------------------------------------------ streaming down
+
+// Chunk of K groups staged at a time: 4, or 2 for tiles of more than 8 rows,
+// so that two buffers and the row block's scales fit the decode LDS limit
+// (two workgroups per CU); the buffers also hold the packed rows' results.
+static size_t down_stream_lds(const moe_dims& d, int cg) {
+    const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
+    const int NG = d.I / kGroup;
+    size_t bufs = 2 * round_dma((size_t)3 * rows_cap * cg * 256);
+    const size_t red = (size_t)3 * rows_cap * kStreamRows * sizeof(float);
+    bufs = bufs > red ? bufs : red;
+    return bufs + 2 * round_dma((size_t)kStreamRows * NG * 2);
+}
+
+// The chunk size of the streaming down at these dims, or 0 where it does not
+// run: where the decode down kernel fits, or K is not whole blocks of 8 groups,
+// or H is not whole row blocks, or no chunk size fits LDS.
+static int down_stream_cg(const moe_dims& d) {
+    if (d.T * d.k == 0 || dec_down_fits(d)) return 0;
+    if ((d.I / kGroup) % 8 != 0 || d.H % kStreamRows != 0) return 0;
+    for (int c = 4; c >= 2; c >>= 1)
+        if (down_stream_lds(d, c) <= kDecLdsLimit) return c;
+    return 0;
+}
+
+// Counters [cap][H / RI] and partial sums [2 G][rows_cap][RI] of the
+// streaming down, after the h planes and their partial sums in the workspace.
+size_t down_split_bytes(const moe_dims& d) {
+    if (down_stream_cg(d) == 0) return 0;
+    const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
+    const size_t ctr = work_capacity(d) * (size_t)(d.H / kStreamRows) * sizeof(int32_t);
+    const size_t part = (size_t)2 * kStreamGrid * rows_cap * kStreamRows * sizeof(float);
+    return ((ctr + 255) & ~(size_t)255) + part;
+}
+
+SplitSpace down_split_space(const moe_dims& d, void* ws) {
+    SplitSpace sp{nullptr, nullptr, 0};
+    if (down_split_bytes(d) == 0) return sp;
+    const size_t P = (size_t)d.T * d.k;
+    const size_t planes = (3 * P * d.I * sizeof(uint16_t) + 255) & ~(size_t)255;
+    const size_t part = (P * (d.I / 16) * sizeof(float) + 255) & ~(size_t)255;
+    char* base = reinterpret_cast<char*>(ws) + planes + part;
+    sp.n_ctr = (int)(work_capacity(d) * (size_t)(d.H / kStreamRows));
+    sp.ctr = reinterpret_cast<int32_t*>(base);
+    sp.part = reinterpret_cast<float*>(base + ((sp.n_ctr * sizeof(int32_t) + 255) & ~(size_t)255));
+    return sp;
+}
+
+template <int BITS, int D, int CG, int NBM>
+static void ds_go(size_t lds, hipStream_t s, const DecParams& p) {
+    hipLaunchKernelGGL((ffn_down_stream_kernel<BITS, kStreamRows / 64, D, CG, NBM>), dim3(kStreamGrid), dim3(256),
+                       lds, s, p);
+}
+
+// NBM: row blocks of packed planes the tile can need, ceil(3 rows_cap / 16)
+template <int BITS>
+static void ds_cg(int cg, size_t lds, hipStream_t s, const DecParams& p) {
+    const int nbm = (3 * p.rows_cap + 15) / 16;
+    if (cg == 4) {
+        if (nbm == 1) ds_go<BITS, 8, 4, 1>(lds, s, p);
+        else if (nbm == 2) ds_go<BITS, 8, 4, 2>(lds, s, p);
+        else ds_go<BITS, 8, 4, 3>(lds, s, p);
+    } else {
+        ds_go<BITS, 4, 2, 3>(lds, s, p);
+    }
+}
+
+int launch_down_stream(const FfnArgs& a, hipStream_t s) {
+    const moe_dims& d = a.d;
+    if (d.T * d.k == 0) return MOE_OK;
+    const int cg = down_stream_cg(d);
+    if (cg == 0) return MOE_ERR_UNSUPPORTED;
+    DecParams p = dec_params(a);
+    p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
+    p.ipe = d.H / kStreamRows;
+    p.n_split_ctr = 0;                                    // the counters are the gate/up call's to clear
+    const size_t lds = down_stream_lds(d, cg);
+    if (a.bits == 4) ds_cg<4>(cg, lds, s, p);
+    else ds_cg<2>(cg, lds, s, p);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // ------------------------------------------------------------ one-launch FFN

@@ -29,6 +29,7 @@
 // Gate/up writes h = silu(a) * u as three bf16 planes hi + mid + lo (about 24
 // significant bits, i.e. float32 h) in the pair order the down kernel's B
 // operand needs, plus per-16-row partial sums of h for the down bias fold.
+#include <algorithm>
 #include <atomic>
 
 #include "launch_util.h"
@@ -44,6 +45,8 @@ namespace moe {
 // are summed in LDS in a fixed wave order, then wave 0 runs the epilogue.
 constexpr int kWaves = 4;
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 struct MfmaParams {
     const uint16_t* x;
     const int32_t* work;        // work list entries (kWorkInts int32 each)
@@ -55,6 +58,8 @@ struct MfmaParams {
     uint16_t* y;        // [P][H]
     int T, H, I, k, E, P;
     int items_per_entry;        // output blocks per work-list entry
+    int32_t* split_ctr;         // gate/up: counters of the streaming down to clear
+    int n_split_ctr;
 };
 
 // Groups [gb, ge) of K handled by wave w (an even split; a wave may get none).
@@ -81,6 +86,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int ipe = p.items_per_entry;
+    if (blockIdx.x == 0)                                  // the streaming down's counters start at zero
+        for (int i = tid; i < p.n_split_ctr; i += 256) p.split_ctr[i] = 0;
     const int n_items = ld_scalar(p.n_work, 0) * ipe;
     if ((int)blockIdx.x >= n_items) return;
     const int n_my = (n_items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
@@ -149,10 +156,12 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
     };
 
     uint32_t wg[D][LW], wu[D][LW], xv[D][16];
+    // codes: non-temporal loads, since each byte is read once (72 -> 67 us for
+    // the 64-expert shape's gate/up with the grid and depth below)
     auto issue = [&](int slot, const uint8_t* gp, const uint8_t* up, const uint16_t* xp, int g) {
         if constexpr (BITS == 4) {
-            const uint4 A = *reinterpret_cast<const uint4*>(gp + (size_t)g * gstride);
-            const uint4 B = *reinterpret_cast<const uint4*>(up + (size_t)g * gstride);
+            const u32x4_t A = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(gp + (size_t)g * gstride));
+            const u32x4_t B = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(up + (size_t)g * gstride));
             wg[slot][0] = A.x; wg[slot][1] = A.y; wg[slot][2] = A.z; wg[slot][3] = A.w;
             wu[slot][0] = B.x; wu[slot][1] = B.y; wu[slot][2] = B.z; wu[slot][3] = B.w;
         } else {
@@ -478,7 +487,7 @@ size_t mfma_workspace_bytes(const moe_dims& d) {
     const size_t P = (size_t)d.T * d.k;
     const size_t planes = 3 * P * d.I * sizeof(uint16_t);
     const size_t part = P * (d.I / 16) * sizeof(float);
-    return ((planes + 255) & ~(size_t)255) + ((part + 255) & ~(size_t)255);
+    return ((planes + 255) & ~(size_t)255) + ((part + 255) & ~(size_t)255) + down_split_bytes(d);
 }
 
 static MfmaParams mfma_params(const FfnArgs& a) {
@@ -519,10 +528,17 @@ static int ring_depth_waves(int NG, int parts, int cap) {
 
 static int ring_depth(int NG, int cap) { return ring_depth_waves(NG, kWaves, cap); }
 
+// Gate/up: at most 3 workgroups per CU.  The HBM streams fastest with a
+// moderate number of loads in flight (a plain read peaks at one to two
+// workgroups per CU with 8 loads each and slows down past that); measured on
+// the 64-expert shape: 1 / 2 / 3 / 4 per CU = 97 / 77 / 72 / 75 us.
+constexpr int kGateupMaxPerCu = 3;
+
 template <int BITS, int D, int SJ>
 static void gateup_launch(const moe_dims& d, size_t lds, hipStream_t s, const MfmaParams& p) {
     static std::atomic<uint64_t> occ{0};
-    const dim3 grid = persistent_grid(ffn_gateup_mfma_kernel<BITS, D, SJ>, occ, lds, d, p.items_per_entry);
+    dim3 grid = persistent_grid(ffn_gateup_mfma_kernel<BITS, D, SJ>, occ, lds, d, p.items_per_entry);
+    grid.x = std::min<unsigned>(grid.x, (unsigned)(kGateupMaxPerCu * device_cus()));
     hipLaunchKernelGGL((ffn_gateup_mfma_kernel<BITS, D, SJ>), grid, dim3(256), lds, s, p);
 }
 
@@ -584,11 +600,14 @@ int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     p.qa = a.w.q[0]; p.sa = a.w.scale[0]; p.ba = a.w.bias[0];
     p.qb = a.w.q[1]; p.sb = a.w.scale[1]; p.bb = a.w.bias[1];
     p.items_per_entry = d.I / 16;
+    const SplitSpace sp = down_split_space(d, a.h);
+    p.split_ctr = sp.ctr;
+    p.n_split_ctr = sp.n_ctr;
     const int NG = d.H / kGroup, NGW = (NG + kWaves - 1) / kWaves;
     const int SJ = (16 * NGW + 63) / 64;
     if (SJ > 4) return MOE_ERR_UNSUPPORTED;
     const size_t lds = mfma_lds_bytes(NG);
-    const int D = ring_depth(NG, 4);
+    const int D = ring_depth(NG, 2);           // 2 deep: 72 us against 81 us at 4 (64-expert shape)
     if (a.bits == 4) gateup_dispatch<4>(D, SJ, d, lds, s, p);
     else gateup_dispatch<2>(D, SJ, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -602,6 +621,10 @@ int launch_down_mfma(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     if (dec_down_fits(d)) return launch_down_dec(a, s);
+    {
+        const int st = launch_down_stream(a, s);        // h through LDS in chunks of K
+        if (st != MOE_ERR_UNSUPPORTED) return st;
+    }
     MfmaParams p = mfma_params(a);
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
     const int NG = d.I / kGroup, KS = down_k_split(NG), NGW = (NG + KS - 1) / KS;

@@ -146,6 +146,24 @@ def test_persistent_kernel_shape_every_element(bits, algo):
     assert g["counts"].max() > 1
 
 
+# Shapes whose down tile does not fit LDS, so the down projection streams h
+# through LDS in chunks of K: tiles of 1 to 5 rows (one 16-row block of packed
+# planes), 6 to 10 rows (two) and 11 to 16 rows (three), with chunks of four
+# groups, every element checked.
+STREAM_SHAPES = [
+    mi.LayerShape("stream_1blk", H=512, E=3, k=1, I=16384, tokens=(2,), bits=(4, 2), zipf_s=None, n_resident=1),
+    mi.LayerShape("stream_2blk", H=3072, E=2, k=2, I=2048, tokens=(7,), bits=(4, 2), zipf_s=None, n_resident=1),
+    mi.LayerShape("stream_3blk", H=3072, E=2, k=2, I=2048, tokens=(12,), bits=(4, 2), zipf_s=None, n_resident=1),
+]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("shape", STREAM_SHAPES, ids=[s.name for s in STREAM_SHAPES])
+def test_streaming_down_shapes(shape, bits):
+    L = layer(shape.name, bits, shape)
+    _stages(L, shape.tokens[0], seed=9, algo=moe.ALGO_MFMA)
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 def test_many_tokens_per_expert_mfma(bits):
     """Experts serving more than one 16-token tile (several MFMA passes)."""

@@ -207,6 +207,7 @@ int launch_down_stream(const FfnArgs& a, hipStream_t s);
 // arrival counters and partial sums follow the h planes in the workspace;
 // the gate/up kernels clear the counters.
 constexpr int kStreamRows = 128;
+constexpr int kStreamWaves = 4;     // waves per workgroup, 32 rows each
 constexpr int kStreamGrid = 512;
 struct SplitSpace {
     int32_t* ctr;       // [cap][H / kStreamRows]

@@ -26,6 +26,7 @@
 #include "mfma_ops.h"
 
 namespace moe {
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -62,6 +63,7 @@ struct DecParams {
     int32_t* split_ctr; // streaming down: arrival counters [cap][ipe] (gate/up clears them)
     float* split_part;  // streaming down: partial sums [2 G][rows_cap][RI]
     int n_split_ctr;    // gate/up: counters to clear (0: none)
+    int split_plan_off; // streaming down: LDS offset of the work split's tables
 };
 
 __host__ __device__ constexpr size_t round_dma(size_t b) { return (b + kDma - 1) / kDma * kDma; }
@@ -589,82 +591,105 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
 
 // ------------------------------------------------------------ streaming down
 // The down projection for shapes whose h tile does not fit LDS (a large
-// intermediate size I).  Work: every (work-list entry, block of RI = 64 RT
-// output rows, group of K) unit, n_work * ipe * NG of them, flattened in that
-// order and cut into G equal ranges, one per workgroup (G: two workgroups per
-// CU).  Such shapes have few entries (16 pairs over about 7 experts at the
-// 64-expert shape, 260 row blocks of full K), so whole row blocks per
-// workgroup would leave half of the chip idle; equal ranges keep every
-// workgroup busy to the end.  A range covers the tail of one row block, whole
-// row blocks, and the head of another: the row blocks it covers whole are
-// written straight to y; a part of a row block leaves its float partial sums
-// in the workspace, and the last of the row block's workgroups to arrive (a
-// counter per row block) adds the parts in the order of K and writes y.
-// Workgroup b takes range (b % 8) (G / 8) + b / 8, so the ranges of one XCD
-// are adjacent and an entry's h rows are fetched into few L2s.
+// intermediate size I).  Work: every (work-list entry, block of RI = 128
+// output rows, group of K) unit, cut into G ranges of equal estimated cost,
+// one per workgroup (G: two workgroups per CU).  Such shapes have few entries
+// (16 pairs over about 7 experts at the 64-expert shape, 260 row blocks of
+// full K), so whole row blocks per workgroup would leave half of the chip
+// idle; ranges keep every workgroup busy to the end.  A range covers the tail
+// of one row block, whole row blocks, and the head of another: the row blocks
+// it covers whole are written straight to y; a part of a row block leaves its
+// float partial sums in the workspace, and the last of the row block's
+// workgroups to arrive (a counter per row block) adds the parts in the order
+// of K and writes y.  Workgroup b takes range (b % 8) (G / 8) + b / 8, so the
+// ranges of one XCD are adjacent and an entry's h rows are fetched into few
+// L2s.
 // In a part of a row block, the item's h rows pass through LDS one chunk of
 // CG groups of K at a time, double-buffered: chunk c + 1 goes straight from
 // L2 into the other buffer (direct-to-LDS loads, no registers) while chunk c
-// is consumed, and the code ring runs on across chunk boundaries.  The four
-// waves share each staged chunk, so a part reads its h rows once, not once
-// per wave.
+// is consumed, and the code ring runs on across chunk boundaries.  The waves
+// share each staged chunk, so a part reads its h rows once, not once per wave.
+// A lane's fp16 scales and biases come straight to registers, 8 groups (16
+// bytes) per row at a time, a block of 8 groups ahead; the loop runs over
+// whole such blocks and skips the groups outside the part.
 // Packed planes: the A operand's 16 rows hold the three bf16 planes of h for
 // the tile's n tokens, plane-major (row 16 b + r is plane r' / n, token r' % n
 // for r' = 16 b + r < 3 n), so one MFMA per row tile and step covers all three
-// planes, and one all-ones MFMA gives every packed row's group sum: 4 (RT + 1)
-// MFMAs per group per row block b, against 4 (3 RT + 3) with one plane per
-// MFMA.  Each packed row is folded with its own sum, and the three planes of a
-// token are added at the end, in plane order.
+// planes: 4 RT MFMAs per group per row block b, against 12 RT with one plane
+// per MFMA.  The group sums X of the fold come from the gate/up kernels'
+// float sums of h (a table per part); the three planes of a token are added at
+// the end, in plane order.
 // Wave wid computes rows 16 RT wid .. +16 RT of the row block.  LDS: two h
 // buffers [3 n][CG][16 pieces of 16 B] (row r's pieces swizzled by r & 15,
-// like the decode tile), then the row block's raw fp16 scales and biases
-// [RI][NG]; after the K loop the h buffers hold the packed rows' results
-// [3 n][RI] float.
+// like the decode tile), then the X table [groups][rows_cap rounded up to 4];
+// after the K loop the h buffers hold the packed rows' results [3 n][RI]
+// float; the work split's tables follow.
 // Waits: a wave's loads complete in issue order.  The first chunk is waited
-// for past the D ring slots issued after it; every later chunk's loads are
-// issued at the start of the chunk before it, and exactly CG RT ring loads
-// follow them before the wait at that chunk's end.
-struct SplitRange {
-    long long total;    // units: n_work * ipe * NG
-    int G;              // workgroups holding a non-empty range: min(grid, total)
+// for past the scale and ring loads issued after it; every later chunk's
+// loads are issued at the start of the chunk before it, and exactly CG RT
+// ring loads follow them before the wait at that chunk's end (a block's scale
+// loads are issued before its first chunk load).
+// The work split.  Units (entry e, row block rb, group g) are numbered entry
+// by entry, U = e per + rb NG + g (per = ipe NG), and a unit of entry e
+// weighs w_e = kSplitW0 + kSplitW1 n_e: its codes cost the same in every
+// entry, but its h rows are staged and multiplied once per token (a tile of
+// 7 tokens costs about twice one of 1).  The weight axis [0, Wt) is cut into
+// G equal ranges (G <= the number of units); range v owns the units whose
+// weight start lies in [v Wt / G, (v + 1) Wt / G), a run of consecutive
+// units [F(v), F(v + 1)) that may be empty when a unit outweighs a range.
+constexpr int kSplitW0 = 16, kSplitW1 = 4;
+
+struct SplitPlan {
+    const int* base;    // LDS: weight before entry e, e = 0 .. nw
+    const int* wt;      // LDS: weight of one unit of entry e
+    const int* first;   // LDS: F(v), v = 0 .. G
+    int nw, per, G;
+    long long Wt;
 };
 
-__device__ __forceinline__ long long split_start(const SplitRange& r, int v) {
-    return (long long)v * r.total / r.G;
+__device__ __forceinline__ long long split_start(const SplitPlan& s, int v) { return (long long)v * s.Wt / s.G; }
+
+// The first unit whose weight start is at least x (the tables' set-up).
+__device__ __forceinline__ int split_first_unit(const SplitPlan& s, long long x) {
+    if (x >= s.Wt) return s.nw * s.per;
+    int lo = 0, hi = s.nw - 1;                  // the entry e with base[e] <= x < base[e + 1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s.base[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    const long long off = x - s.base[lo];
+    return lo * s.per + (int)((off + s.wt[lo] - 1) / s.wt[lo]);   // per: the next entry's first unit
 }
 
-// The range holding unit u: the largest v with split_start(v) <= u.
-__device__ __forceinline__ int split_owner(const SplitRange& r, long long u) {
-    return (int)(((u + 1) * r.G - 1) / r.total);
+__device__ __forceinline__ int split_first(const SplitPlan& s, int v) { return s.first[v]; }
+
+// The range owning unit u: the largest v with F(v) <= u (its range is not
+// empty: F(v + 1) > u).
+__device__ __forceinline__ int split_owner(const SplitPlan& s, int u) {
+    int lo = 0, hi = s.G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s.first[mid] <= u) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 // Partial-sum slot of range v's part of the row block starting at unit u0:
 // 2 v for the range's first part, 2 v + 1 for its last.
-__device__ __forceinline__ int split_slot(const SplitRange& r, int v, long long u0) {
-    return 2 * v + (split_start(r, v) < u0 ? 1 : 0);
+__device__ __forceinline__ int split_slot(const SplitPlan& s, int v, int u0) {
+    return 2 * v + (split_first(s, v) < u0 ? 1 : 0);
 }
 
-// Arrive at `counter` (out of `n` arrivals); true in every thread of the last
-// workgroup to arrive.  Partial sums pass between workgroups as device-scope
-// atomic stores and loads, which bypass the non-coherent per-CU caches; the
-// full s_waitcnt before the count makes this workgroup's stores complete
-// before its arrival is counted.
-__device__ __forceinline__ bool split_arrive(int32_t* counter, int n, int* flag) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0)
-        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
-    __syncthreads();
-    return *flag != 0;
-}
-
-template <int BITS, int RT, int D, int CG, int NBM>
+template <int BITS, int NW, int RT, int D, int CG, int NBM>
 __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecItem& it, int ga, int gb,
-                                                 uint8_t* smem, const SplitRange& sr, int v, long long u0) {
+                                                 uint8_t* smem, const SplitPlan& sp, int v, int u0) {
     constexpr int LB = 128 * BITS / 8 / 4;
     constexpr int LW = LB / 4;
-    constexpr int RI = 64 * RT;
-    constexpr int U = CG > D ? CG : D;         // groups per unrolled block: whole chunks and ring turns
+    constexpr int RI = 16 * RT * NW;           // output rows of a row block
+    constexpr int NT = 64 * NW;                // threads
+    constexpr int U = 8;                       // groups per unrolled block: one 16-byte run of fp16 scales
     static_assert(U % CG == 0 && U % D == 0, "chunks and ring turns must tile the block");
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -673,49 +698,54 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
     const int NB = (rows3 + 15) / 16;          // row blocks of 16 (NB <= NBM)
     const int rowb = CG * 256;                 // one packed row of a chunk in LDS
     const int buf_b = (int)round_dma((size_t)3 * p.rows_cap * rowb);
-    const int sc_bytes = RI * NG * 2;
-    const int sc_stride = (int)round_dma(sc_bytes);
-    const int nch = (gb - ga + CG - 1) / CG;   // chunks of this part
-    uint8_t* scl = smem + 2 * (size_t)buf_b;
+    const int g8a = ga & ~(U - 1);             // the part runs over whole blocks of U groups from here,
+    const int nch = (gb - g8a + CG - 1) / CG;  // skipping groups outside [ga, gb); chunks from g8a
 
-    // ---- chunk c of the packed h rows into buffer c & 1: piece (row r, group
-    // gl, slot cs) holds 16-byte chunk cs ^ (r & 15) of row r's group; pieces
-    // past the 3 n rows (the last 1 KB load's tail) reload row 0 into slack,
-    // and groups past the part (the last chunk's tail) reload the last group
+    // ---- chunk c (groups g8a + CG c ..) of the packed h rows into buffer c & 1:
+    // piece (row r, group gl, slot cs) holds 16-byte chunk cs ^ (r & 15) of row
+    // r's group; pieces past the 3 n rows (the last 1 KB load's tail) reload
+    // row 0 into slack, and groups outside the part load its nearest group
     const size_t plane = (size_t)p.P * I;
     auto stage = [&](int c) {
         uint8_t* dst = smem + (size_t)(c & 1) * buf_b;
         const int pieces = (rows3 * rowb + kDma - 1) / kDma;
-        for (int i = wid; i < pieces; i += 4) {
+        for (int i = wid; i < pieces; i += NW) {
             const int slot = i * (kDma / 16) + lane;
             const int cs = slot & 15, rest = slot >> 4, gl = rest % CG;
             int r = rest / CG;
             r = r < rows3 ? r : 0;
             const int pl = r / n, j = r - pl * n;
-            const int g = min(ga + c * CG + gl, gb - 1);
+            const int g = min(max(g8a + c * CG + gl, ga), gb - 1);
             const uint16_t* src = p.hp + pl * plane + (size_t)(it.row0 + j) * I + (size_t)g * kGroup + 8 * (cs ^ (r & 15));
             dma16(src, dst + i * kDma);
         }
     };
-    {
-        const size_t first = ((size_t)it.e * H + (size_t)it.rb * RI) * NG;
-        dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
-        dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
-    }
-    stage(0);
 
-    // ---- code ring: RT rows of this lane, groups ga .. gb
+    // ---- fp16 scales and biases of this lane's RT rows, one block of U groups
+    // (16 bytes per row) at a time, a block ahead
     const int rloc = 16 * RT * wid + m;
+    const size_t srow = ((size_t)it.e * H + (size_t)it.rb * RI + rloc) * NG;
+    uint4 sc[RT], bc[RT], sn[RT], bn[RT];
+    auto load_scales = [&](int g8, uint4 (&s_)[RT], uint4 (&b_)[RT]) {
+        const int gg = g8 < gb ? g8 : g8a;                     // past the part: an in-range block, unused
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            s_[rt] = *reinterpret_cast<const uint4*>(p.sa + srow + (size_t)(16 * rt) * NG + gg);
+            b_[rt] = *reinterpret_cast<const uint4*>(p.ba + srow + (size_t)(16 * rt) * NG + gg);
+        }
+    };
+
+    // ---- code ring: RT rows of this lane, groups clamped to [ga, gb)
     const size_t gstride = (size_t)H * (4 * LB);
     const uint8_t* cp = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
     uint32_t rc[D][RT][LW];
     auto issue = [&](int slot, int g) {
-        const size_t off = (size_t)(g < gb ? g : gb - 1) * gstride;
+        const size_t off = (size_t)min(max(g, ga), gb - 1) * gstride;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const uint8_t* src = cp + (size_t)(16 * rt) * (4 * LB) + off;
             if constexpr (BITS == 4) {
-                const uint4 A = *reinterpret_cast<const uint4*>(src);
+                const u32x4_t A = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
                 rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y; rc[slot][rt][2] = A.z; rc[slot][rt][3] = A.w;
             } else {
                 const uint2 A = *reinterpret_cast<const uint2*>(src);
@@ -723,9 +753,47 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
             }
         }
     };
+    // ---- X[t][g] = sum of h over group g for token t, from the gate/up
+    // kernel's float sums over 16 consecutive i (8 per group, added in a fixed
+    // order); rows t in [n, rowsX) are zero.  It stands in for the all-ones
+    // MFMA: in the fold, a token's whole X goes with its hi plane row and the
+    // mid and lo rows get none, which gives the same sum over the planes.
+    const int rowsX = (p.rows_cap + 3) & ~3;
+    const int W = ((gb + U - 1) & ~(U - 1)) - g8a;              // groups of the table (whole blocks)
+    float* xg = reinterpret_cast<float*>(smem + 2 * (size_t)buf_b);   // [W][rowsX]
+    const float* hsum = p.hpart + (size_t)it.row0 * (I / 16) + (size_t)g8a * 8;
+    constexpr int XPT = 4;                                     // table entries per thread per pass
+    float4 xa[XPT], xb[XPT];
+    auto x_load = [&](int base) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(d, ga + d);
-    wait_vmem<RT * D>();                       // the scales and chunk 0 (older than the ring loads)
+        for (int k = 0; k < XPT; ++k) {
+            const int o = base + tid + NT * k, gg = o / rowsX, t = o - gg * rowsX;
+            const bool ok = gg < W && t < n;
+            const float4* src = reinterpret_cast<const float4*>(hsum + (size_t)(ok ? t : 0) * (I / 16) + (ok ? gg : 0) * 8);
+            xa[k] = src[0];
+            xb[k] = src[1];
+        }
+    };
+    auto x_store = [&](int base) {
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int o = base + tid + NT * k, gg = o / rowsX, t = o - gg * rowsX;
+            if (gg < W)
+                xg[o] = t < n ? ((xa[k].x + xa[k].y) + (xa[k].z + xa[k].w)) + ((xb[k].x + xb[k].y) + (xb[k].z + xb[k].w))
+                              : 0.f;
+        }
+    };
+    x_load(0);                                  // first, so that the waits for it do not cover the ring
+    stage(0);
+    load_scales(g8a, sc, bc);
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, g8a + d);
+    x_store(0);
+    for (int base = NT * XPT; base < W * rowsX; base += NT * XPT) {   // parts longer than 64 groups
+        x_load(base);
+        x_store(base);
+    }
+    wait_vmem<RT * D + 2 * RT>();              // chunk 0 (older than the scales and the ring loads)
     lds_barrier();
 
     // packed row of this lane in block b (rows past 3 n read row 0; never stored)
@@ -737,26 +805,24 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
 #pragma unroll
         for (int st = 0; st < 4; ++st) coff[b][st] = 16 * ((4 * q + st) ^ (r & 15));
     }
-    const uint16_t* dsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NG;
-    const uint16_t* dbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NG;
-    const uint32_t ONES[4] = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
     floatx4_t acc[NBM][RT];
 #pragma unroll
     for (int b = 0; b < NBM; ++b)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[b][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int g0 = ga; g0 < gb; g0 += U) {
+    for (int g0 = g8a; g0 < gb; g0 += U) {
+        load_scales(g0 + U, sn, bn);                     // before this block's chunk loads (the waits count after them)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int g = g0 + u, gl = u % CG, c = (g - ga) / CG, d = u % D;
+            const int g = g0 + u, gl = u % CG, c = (g0 - g8a) / CG + u / CG, d = u % D;
             if (gl == 0 && c + 1 < nch) stage(c + 1);           // the other buffer: its chunk was read before the last barrier
-            if (g < gb) {
+            if (g >= ga && g < gb) {                            // uniform per workgroup
                 const uint8_t* hb = smem + (size_t)(c & 1) * buf_b + gl * 256;
 #pragma unroll
                 for (int b = 0; b < NBM; ++b) {
-                    if (b < NB) {                                 // uniform per workgroup
-                        floatx4_t C[RT], Cx = {0.f, 0.f, 0.f, 0.f};
+                    if (b < NB) {
+                        floatx4_t C[RT];
 #pragma unroll
                         for (int rt = 0; rt < RT; ++rt) C[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -769,11 +835,19 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
                                 code_operand<BITS>(rc[d][rt], st, B);
                                 C[rt] = mfma16(A, B, C[rt]);
                             }
-                            Cx = mfma16(A, ONES, Cx);             // group sum of every packed row
+                        }
+                        // X of packed rows 16 b + 4 q .. +3: the hi-plane rows' tokens, else zero
+                        floatx4_t X = {0.f, 0.f, 0.f, 0.f};
+                        if (16 * b + 4 * q < rowsX) {
+                            const float4 x4 = *reinterpret_cast<const float4*>(xg + (g - g8a) * rowsX + 16 * b + 4 * q);
+                            X = floatx4_t{x4.x, x4.y, x4.z, x4.w};
                         }
 #pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-                            fold<BITS>(acc[b][rt], C[rt], dsc[16 * rt * NG + g], dbi[16 * rt * NG + g], Cx);
+                        for (int rt = 0; rt < RT; ++rt) {
+                            const uint32_t sw = (&sc[rt].x)[u >> 1], bw = (&bc[rt].x)[u >> 1];
+                            fold<BITS>(acc[b][rt], C[rt], (u & 1) ? sw >> 16 : sw & 0xFFFFu,
+                                       (u & 1) ? bw >> 16 : bw & 0xFFFFu, X);
+                        }
                     }
                 }
             }
@@ -784,6 +858,8 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
                 lds_barrier();                          // every wave's pieces landed; chunk c no longer read
             }
         }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) { sc[rt] = sn[rt]; bc[rt] = bn[rt]; }
     }
 
     // ---- the packed rows' results to LDS [3 n][RI]
@@ -801,53 +877,130 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
     lds_barrier();
     uint16_t* yb = p.y + (size_t)it.row0 * H + (size_t)it.rb * RI;
     if (ga == 0 && gb == NG) {                          // the whole row block: y = hi + mid + lo in bf16
-        for (int o = tid; o < n * RI; o += 256) {
+        for (int o = tid; o < n * RI; o += NT) {
             const int t = o / RI, col = o - t * RI;
             const float y = (red[t * RI + col] + red[(n + t) * RI + col]) + red[(2 * n + t) * RI + col];
             yb[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(y);
         }
         return;
     }
-    // a part: its sums to slot split_slot(v, u0); the last part to arrive adds
-    // the parts of the row block in the order of their ranges (of K)
-    const int rsz = p.rows_cap * RI;
-    float* mine = p.split_part + (size_t)split_slot(sr, v, u0) * rsz;
-    for (int o = tid; o < n * RI; o += 256) {
+    // a part: its sums to slot split_slot(v, u0), then the caller arrives at
+    // the row block's counter
+    float* mine = p.split_part + (size_t)split_slot(sp, v, u0) * (p.rows_cap * RI);
+    for (int o = tid; o < n * RI; o += NT) {
         const int t = o / RI, col = o - t * RI;
         const float y = (red[t * RI + col] + red[(n + t) * RI + col]) + red[(2 * n + t) * RI + col];
         __hip_atomic_store(mine + o, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int vf = split_owner(sr, u0), vl = split_owner(sr, u0 + NG - 1);
-    int32_t* ctr = p.split_ctr + (size_t)it.entry * p.ipe + it.rb;
-    if (!split_arrive(ctr, vl - vf + 1, reinterpret_cast<int*>(scl))) return;   // the scales are no longer read
-    for (int o = tid; o < n * RI; o += 256) {
-        const int t = o / RI, col = o - t * RI;
-        float y = 0.f;
-        for (int w = vf; w <= vl; ++w)
-            y += __hip_atomic_load(p.split_part + (size_t)split_slot(sr, w, u0) * rsz + o, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        yb[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(y);
-    }
-    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
 }
 
-template <int BITS, int RT, int D, int CG, int NBM>
-__global__ __launch_bounds__(256, 2) void ffn_down_stream_kernel(DecParams p) {
+// The parts of the row block starting at unit u0: the non-empty ranges from
+// its first unit's owner to its last unit's.  Returns their number; with
+// lst, thread 0 also lists their slots there.
+__device__ __forceinline__ int split_parts(const SplitPlan& sp, int u0, int NG, int* lst) {
+    const int vf = split_owner(sp, u0), vl = split_owner(sp, u0 + NG - 1);
+    int parts = 0;
+    for (int w = vf, f0 = split_first(sp, vf); w <= vl; ++w) {
+        const int f1 = split_first(sp, w + 1);
+        if (f0 < f1) {
+            if (lst && threadIdx.x == 0) lst[parts] = 2 * w + (f0 < u0 ? 1 : 0);
+            ++parts;
+        }
+        f0 = f1;
+    }
+    return parts;
+}
+
+// The last workgroup to arrive at a row block adds its parts in the order of
+// their ranges (of K), writes y and clears the counter for the next call.
+template <int NT, int RI>
+__device__ __forceinline__ void split_reduce(const DecParams& p, const SplitPlan& sp, int u0, int* lst) {
+    const int NG = p.I / kGroup, blk = u0 / NG;
+    const DecItem it = dec_item_at<false>(p, blk / p.ipe, blk % p.ipe);
+    const int parts = split_parts(sp, u0, NG, lst);
+    __syncthreads();
+    const int rsz = p.rows_cap * RI;
+    uint16_t* yb = p.y + (size_t)it.row0 * p.H + (size_t)it.rb * RI;
+    for (int o = threadIdx.x; o < it.n * RI; o += NT) {
+        const int t = o / RI, col = o - t * RI;
+        float y = 0.f;
+        for (int j = 0; j < parts; ++j)
+            y += __hip_atomic_load(p.split_part + (size_t)lst[j] * rsz + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        yb[(size_t)t * p.H + col] = (uint16_t)f32_to_bf16_bits(y);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(p.split_ctr + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+    __syncthreads();                                    // lst is reused
+}
+
+template <int BITS, int NW, int RT, int D, int CG, int NBM>
+__global__ __launch_bounds__(64 * NW, NW / 2) void ffn_down_stream_kernel(DecParams p) {   // two workgroups per CU
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
     const int NG = p.I / kGroup;
-    const int nw = min(ld_scalar(p.n_work, 0), p.cap);
-    SplitRange sr;
-    sr.total = (long long)(nw > 0 ? nw : 0) * p.ipe * NG;
-    sr.G = (int)min((long long)gridDim.x, sr.total);
+    SplitPlan sp;
+    sp.nw = max(0, min(ld_scalar(p.n_work, 0), p.cap));
+    sp.per = p.ipe * NG;
+    if (sp.nw == 0) return;
+    // ---- unit weights and their prefix sums over the entries (LDS, after the part's space)
+    int* pbase = reinterpret_cast<int*>(smem + p.split_plan_off);
+    int* pwt = pbase + p.cap + 1;
+    for (int e = tid; e < sp.nw; e += 64 * NW) {
+        const int32_t* ent = p.work + (size_t)e * kWorkInts;
+        const int ee = ent[0], r0 = ent[1], nn = ent[2];
+        const bool ok = ee >= 0 && ee < p.E && r0 >= 0 && nn >= 1 && nn <= p.rows_cap && r0 + nn <= p.P;
+        pwt[e] = kSplitW0 + kSplitW1 * (ok ? nn : 0);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        int carry = 0;
+        for (int c0 = 0; c0 < sp.nw; c0 += 64) {
+            const int e = c0 + lane;
+            int x = e < sp.nw ? pwt[e] * sp.per : 0;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off, kWave);
+                if (lane >= off) x += y;
+            }
+            if (e < sp.nw) pbase[e + 1] = carry + x;
+            carry += __shfl(x, 63, kWave);
+        }
+        if (lane == 0) pbase[0] = 0;
+    }
+    __syncthreads();
+    sp.base = pbase;
+    sp.wt = pwt;
+    sp.Wt = pbase[sp.nw];
+    sp.G = (int)min((long long)gridDim.x, (long long)sp.nw * sp.per);
+    int* pfirst = pwt + p.cap;
+    for (int w = tid; w <= sp.G; w += 64 * NW) pfirst[w] = split_first_unit(sp, split_start(sp, w));
+    sp.first = pfirst;
+    __syncthreads();
     const int b = (int)blockIdx.x, v = (b & 7) * ((int)gridDim.x >> 3) + (b >> 3);
-    if (v >= sr.G) return;
-    const long long end = split_start(sr, v + 1);
-    for (long long u = split_start(sr, v); u < end;) {
-        const long long blk = u / NG, u0 = blk * NG;
-        const int ga = (int)(u - u0), gb = (int)min((long long)NG, end - u0);
-        const DecItem it = dec_item_at<false>(p, (int)(blk / p.ipe), (int)(blk % p.ipe));
-        if (u > split_start(sr, v)) lds_barrier();      // the last part's LDS is no longer read
-        if (it.n > 0) down_stream_part<BITS, RT, D, CG, NBM>(p, it, ga, gb, smem, sr, v, u0);
+    if (v >= sp.G) return;
+    const int first = split_first(sp, v), end = split_first(sp, v + 1);
+    int* lst = reinterpret_cast<int*>(smem);            // after a part: its LDS is no longer read
+    for (int u = first; u < end;) {
+        const int blk = u / NG, u0 = blk * NG;
+        const int ga = u - u0, gb = min(NG, end - u0);
+        const DecItem it = dec_item_at<false>(p, blk / p.ipe, blk % p.ipe);
+        if (u > first) lds_barrier();                   // the last part's LDS is no longer read
+        if (it.n > 0) {
+            down_stream_part<BITS, NW, RT, D, CG, NBM>(p, it, ga, gb, smem, sp, v, u0);
+            if (ga > 0 || gb < NG) {
+                // arrival: this workgroup's part stores have completed (the
+                // full wait), then one count; partial sums pass between
+                // workgroups as device-scope atomic stores and loads, which
+                // bypass the non-coherent per-CU caches
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (tid == 0)
+                    lst[64] = __hip_atomic_fetch_add(p.split_ctr + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                              split_parts(sp, u0, NG, nullptr) - 1;
+                __syncthreads();
+                if (lst[64]) split_reduce<64 * NW, 16 * RT * NW>(p, sp, u0, lst + 128);
+            }
+        }
         u = u0 + gb;
     }
 }
@@ -1052,16 +1205,23 @@ int launch_down_dec(const FfnArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------ streaming down
 
-// Chunk of K groups staged at a time: 4, or 2 for tiles of more than 8 rows,
-// so that two buffers and the row block's scales fit the decode LDS limit
-// (two workgroups per CU); the buffers also hold the packed rows' results.
+// Chunk of K groups staged at a time: 4, or 2 for tiles of more rows than fit
+// two buffers of 4 groups in the decode LDS limit; the buffers also hold the
+// packed rows' results at the end.  Then the X table [NG][rows_cap rounded up
+// to 4] float (the arrival flag at the end).
 static size_t down_stream_lds(const moe_dims& d, int cg) {
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
-    const int NG = d.I / kGroup;
     size_t bufs = 2 * round_dma((size_t)3 * rows_cap * cg * 256);
     const size_t red = (size_t)3 * rows_cap * kStreamRows * sizeof(float);
     bufs = bufs > red ? bufs : red;
-    return bufs + 2 * round_dma((size_t)kStreamRows * NG * 2);
+    const size_t xtab = (size_t)(d.I / kGroup) * ((rows_cap + 3) & ~3) * sizeof(float);
+    return bufs + ((xtab + 255) & ~(size_t)255);
+}
+
+// The work split's tables (entry weights, their prefix sums, the ranges'
+// first units) after the part's LDS.
+static size_t down_stream_plan_lds(const moe_dims& d) {
+    return (size_t)(2 * work_capacity(d) + 1 + kStreamGrid + 1) * sizeof(int);
 }
 
 // The chunk size of the streaming down at these dims, or 0 where it does not
@@ -1070,8 +1230,9 @@ static size_t down_stream_lds(const moe_dims& d, int cg) {
 static int down_stream_cg(const moe_dims& d) {
     if (d.T * d.k == 0 || dec_down_fits(d)) return 0;
     if ((d.I / kGroup) % 8 != 0 || d.H % kStreamRows != 0) return 0;
+    if (work_capacity(d) > 1024) return 0;     // the work split's tables
     for (int c = 4; c >= 2; c >>= 1)
-        if (down_stream_lds(d, c) <= kDecLdsLimit) return c;
+        if (down_stream_lds(d, c) + down_stream_plan_lds(d) <= kDecLdsLimit) return c;
     return 0;
 }
 
@@ -1100,7 +1261,8 @@ SplitSpace down_split_space(const moe_dims& d, void* ws) {
 
 template <int BITS, int D, int CG, int NBM>
 static void ds_go(size_t lds, hipStream_t s, const DecParams& p) {
-    hipLaunchKernelGGL((ffn_down_stream_kernel<BITS, kStreamRows / 64, D, CG, NBM>), dim3(kStreamGrid), dim3(256),
+    hipLaunchKernelGGL((ffn_down_stream_kernel<BITS, kStreamWaves, kStreamRows / (16 * kStreamWaves), D, CG, NBM>),
+                       dim3(kStreamGrid), dim3(64 * kStreamWaves),
                        lds, s, p);
 }
 
@@ -1109,9 +1271,9 @@ template <int BITS>
 static void ds_cg(int cg, size_t lds, hipStream_t s, const DecParams& p) {
     const int nbm = (3 * p.rows_cap + 15) / 16;
     if (cg == 4) {
-        if (nbm == 1) ds_go<BITS, 8, 4, 1>(lds, s, p);
-        else if (nbm == 2) ds_go<BITS, 8, 4, 2>(lds, s, p);
-        else ds_go<BITS, 8, 4, 3>(lds, s, p);
+        if (nbm == 1) ds_go<BITS, 4, 4, 1>(lds, s, p);
+        else if (nbm == 2) ds_go<BITS, 4, 4, 2>(lds, s, p);
+        else ds_go<BITS, 4, 4, 3>(lds, s, p);
     } else {
         ds_go<BITS, 4, 2, 3>(lds, s, p);
     }
@@ -1126,7 +1288,8 @@ int launch_down_stream(const FfnArgs& a, hipStream_t s) {
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
     p.ipe = d.H / kStreamRows;
     p.n_split_ctr = 0;                                    // the counters are the gate/up call's to clear
-    const size_t lds = down_stream_lds(d, cg);
+    p.split_plan_off = (int)down_stream_lds(d, cg);
+    const size_t lds = down_stream_lds(d, cg) + down_stream_plan_lds(d);
     if (a.bits == 4) ds_cg<4>(cg, lds, s, p);
     else ds_cg<2>(cg, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

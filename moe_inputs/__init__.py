@@ -18,12 +18,13 @@ Storage formats (fixed for the whole library):
       q[m]     uint8  [E, N, K*bits/8]  codes packed along K; for 4-bit the low
                nibble holds the even k, for 2-bit bits 2j..2j+1 of a byte hold
                k % 4 == j;
-      scale[m] uint16 [E, N, K/128]     fp16 bit patterns;
-      bias[m]  uint16 [E, N, K/128]     fp16 bit patterns;
+      scale[m] uint16 [E, N, K/group]   fp16 bit patterns;
+      bias[m]  uint16 [E, N, K/group]   fp16 bit patterns;
     with (N, K) = (I, H) for gate and up and (H, I) for down.  The dequantised
-    weight is code * scale + bias of the element's 128-wide group along K
-    (page 2 section 2.2 for the group of 128, page 5 section 2 for the
-    nibble*scale+bias form).
+    weight is code * scale + bias of the element's group along K, 128 wide
+    by default (page 2 section 2.2 for the group of 128; 64 and 32 from the
+    finer-group passages: page 2 section 4.4, the laptop page section 4.2;
+    page 5 section 2 for the nibble*scale+bias form).
 
 Random draws: every tensor has its own ``numpy.random.Generator`` (PCG64)
 seeded from ``SeedSequence([seed, tag, ...])`` so that any expert can be
@@ -57,10 +58,11 @@ class LayerShape:
     zipf_s: Optional[float]   # Zipf exponent of expert popularity; None = uniform
     n_resident: int           # experts marked resident in the slot table
     description: str = ""
+    group: int = GROUP        # quantisation group along K: 128, 64 or 32
 
     def bytes_per_expert(self, bits: int) -> int:
         """Bytes of one expert's three matrices: codes plus fp16 scale and bias."""
-        per_matrix = self.H * self.I * bits // 8 + (self.H * self.I // GROUP) * 4
+        per_matrix = self.H * self.I * bits // 8 + (self.H * self.I // self.group) * 4
         return 3 * per_matrix
 
 
@@ -192,7 +194,7 @@ def _draw_expert_matrix(shape: LayerShape, m: str, e: int, bits: int, seed: int)
     raw = _rng(seed, _TAG_Q, bits, mi, e).bit_generator.random_raw((nbytes + 7) // 8)
     # every byte is 8/bits independent uniform codes in 0..2^bits-1
     q = raw.view(np.uint8)[:nbytes].reshape(N, K * bits // 8)
-    ng = K // GROUP
+    ng = K // shape.group
     s = _rng(seed, _TAG_S, bits, mi, e).uniform(0.005, 0.02, size=(N, ng))
     b = _rng(seed, _TAG_B, bits, mi, e).normal(0.0, 0.01, size=(N, ng))
     return q, f32_to_f16_bits(s), f32_to_f16_bits(b)
@@ -204,8 +206,8 @@ class ExpertWeights:
     bits: int
     experts: np.ndarray                     # expert ids held, in storage order
     q: Dict[str, np.ndarray]                # m -> uint8 [n, N, K*bits/8]
-    scale: Dict[str, np.ndarray]            # m -> uint16 [n, N, K/128]
-    bias: Dict[str, np.ndarray]             # m -> uint16 [n, N, K/128]
+    scale: Dict[str, np.ndarray]            # m -> uint16 [n, N, K/group]
+    bias: Dict[str, np.ndarray]             # m -> uint16 [n, N, K/group]
 
     def index_of(self, e: int) -> int:
         hit = np.nonzero(self.experts == e)[0]
@@ -224,8 +226,8 @@ def make_expert_weights(shape: LayerShape, bits: int = 4, seed: int = 0,
     for m in MATRICES:
         N, K = matrix_dims(shape, m)
         q[m] = np.empty((len(ids), N, K * bits // 8), dtype=np.uint8)
-        s[m] = np.empty((len(ids), N, K // GROUP), dtype=np.uint16)
-        b[m] = np.empty((len(ids), N, K // GROUP), dtype=np.uint16)
+        s[m] = np.empty((len(ids), N, K // shape.group), dtype=np.uint16)
+        b[m] = np.empty((len(ids), N, K // shape.group), dtype=np.uint16)
         for i, e in enumerate(ids):
             q[m][i], s[m][i], b[m][i] = _draw_expert_matrix(shape, m, int(e), bits, seed)
     return ExpertWeights(bits=bits, experts=np.asarray(ids), q=q, scale=s, bias=b)
@@ -239,9 +241,9 @@ def iter_expert_weights(shape: LayerShape, bits: int = 4, seed: int = 0):
 
 def make_zero_points(shape: LayerShape, m: str, e: int, bits: int = 4, seed: int = 0) -> np.ndarray:
     """Zero points of matrix m of expert e for zero-point weights (q - z) s:
-    uint8 [N][K/128], uniform over the codes 0 .. 2^bits - 1."""
+    uint8 [N][K/group], uniform over the codes 0 .. 2^bits - 1."""
     N, K = matrix_dims(shape, m)
-    return _rng(seed, _TAG_Z, bits, MATRICES.index(m), e).integers(0, 1 << bits, size=(N, K // GROUP),
+    return _rng(seed, _TAG_Z, bits, MATRICES.index(m), e).integers(0, 1 << bits, size=(N, K // shape.group),
                                                                     dtype=np.uint8)
 
 

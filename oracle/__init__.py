@@ -48,13 +48,13 @@ def lib():
         L.orc_f64_to_f16.argtypes = [f64]; L.orc_f64_to_f16.restype = ctypes.c_uint16
         L.orc_zero_point_bias.argtypes = [ctypes.c_int64, P, P, P]; L.orc_zero_point_bias.restype = None
         L.orc_code.argtypes = [P, i32, i32]; L.orc_code.restype = i32
-        L.orc_weight.argtypes = [P, P, P, i32, i32]; L.orc_weight.restype = f64
-        L.orc_dequant_matrix.argtypes = [i32, i32, i32, P, P, P, P]; L.orc_dequant_matrix.restype = None
+        L.orc_weight.argtypes = [P, P, P, i32, i32, i32]; L.orc_weight.restype = f64
+        L.orc_dequant_matrix.argtypes = [i32, i32, i32, i32, P, P, P, P]; L.orc_dequant_matrix.restype = None
         L.orc_router_logits.argtypes = [i32, i32, i32, P, P, P, P]; L.orc_router_logits.restype = None
         L.orc_topk.argtypes = [i32, i32, i32, P, i32, P, P]; L.orc_topk.restype = None
         L.orc_slot_lookup.argtypes = [i32, i32, i32, P, P, P, P, P, P, u32, P]; L.orc_slot_lookup.restype = i32
         L.orc_permute.argtypes = [i32, i32, P, P, P, P, P, P, P]; L.orc_permute.restype = None
-        L.orc_expert_ffn_row.argtypes = [i32, i32, i32, P] + [P] * 9 + [i32, P, P, P]
+        L.orc_expert_ffn_row.argtypes = [i32, i32, i32, i32, P] + [P] * 9 + [i32, P, P, P]
         L.orc_expert_ffn_row.restype = None
         L.orc_combine.argtypes = [i32, i32, i32, P, P, P, P, P]; L.orc_combine.restype = None
         L.orc_shared_gate.argtypes = [i32, i32, P, P, P]; L.orc_shared_gate.restype = None
@@ -123,13 +123,22 @@ def code(row: np.ndarray, k: int, bits: int) -> int:
     return int(lib().orc_code(_p(row), k, bits))
 
 
+def group_of(K: int, scale: np.ndarray) -> int:
+    """Group size of a matrix with reduction length K and scales [..., K/group]."""
+    ng = int(np.asarray(scale).shape[-1])
+    if ng <= 0 or K % ng or K // ng not in (32, 64, 128):
+        raise ValueError(f"{ng} scales per row of {K} do not make groups of 32, 64 or 128")
+    return K // ng
+
+
 def dequant_matrix(q: np.ndarray, scale: np.ndarray, bias: np.ndarray, bits: int) -> np.ndarray:
-    """Dense float64 [N, K] weights of one packed matrix."""
+    """Dense float64 [N, K] weights of one packed matrix (group size from the
+    scales' shape)."""
     q, scale, bias = _c(q, np.uint8), _c(scale, np.uint16), _c(bias, np.uint16)
     N = q.shape[0]
     K = q.shape[1] * 8 // bits
     out = np.empty((N, K), dtype=np.float64)
-    lib().orc_dequant_matrix(N, K, bits, _p(q), _p(scale), _p(bias), _p(out))
+    lib().orc_dequant_matrix(N, K, bits, group_of(K, scale), _p(q), _p(scale), _p(bias), _p(out))
     return out
 
 
@@ -191,7 +200,8 @@ def permute(ids: np.ndarray, E: int):
 
 def expert_ffn_row(x_row: np.ndarray, w: Dict[str, Sequence[np.ndarray]], bits: int,
                    n_idx: Optional[np.ndarray] = None):
-    """FFN of one expert on one token.  w[m] = (q [N, K*bits/8], scale, bias).
+    """FFN of one expert on one token.  w[m] = (q [N, K*bits/8], scale, bias);
+    the group size follows from the scales' shape.
 
     Returns (h float32 [I], y bf16 bits [H] or [len(n_idx)])."""
     x_row = _c(x_row, np.uint16)
@@ -200,15 +210,18 @@ def expert_ffn_row(x_row: np.ndarray, w: Dict[str, Sequence[np.ndarray]], bits: 
     qd, sd, bd = (_c(a, t) for a, t in zip(w["down"], (np.uint8, np.uint16, np.uint16)))
     H = x_row.shape[0]
     I = qg.shape[0]
+    group = group_of(H, sg)
+    if group_of(I, sd) != group:
+        raise ValueError("gate/up and down weights have different group sizes")
     h = np.empty(I, dtype=np.float32)
     if n_idx is None:
         y = np.empty(H, dtype=np.uint16)
-        lib().orc_expert_ffn_row(H, I, bits, _p(x_row), _p(qg), _p(sg), _p(bg), _p(qu), _p(su), _p(bu),
+        lib().orc_expert_ffn_row(H, I, bits, group, _p(x_row), _p(qg), _p(sg), _p(bg), _p(qu), _p(su), _p(bu),
                                  _p(qd), _p(sd), _p(bd), 0, None, _p(h), _p(y))
     else:
         n_idx = _c(n_idx, np.int32)
         y = np.empty(n_idx.shape[0], dtype=np.uint16)
-        lib().orc_expert_ffn_row(H, I, bits, _p(x_row), _p(qg), _p(sg), _p(bg), _p(qu), _p(su), _p(bu),
+        lib().orc_expert_ffn_row(H, I, bits, group, _p(x_row), _p(qg), _p(sg), _p(bg), _p(qu), _p(su), _p(bu),
                                  _p(qd), _p(sd), _p(bd), int(n_idx.shape[0]), _p(n_idx), _p(h), _p(y))
     return h, y
 

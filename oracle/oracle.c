@@ -12,7 +12,9 @@
  *   decode of codes       "Flash-MoE ... (translation)" sec. 2, FMA-optimised
  *                         dequant: weight = nibble * scale + bias;
  *                         "Strata" page sec. 2.2: groups of 128 weights share
- *                         one scale/offset pair.
+ *                         one scale/offset pair; finer groups: "Strata" page
+ *                         sec. 4.4 (64 for quality), the laptop page sec. 4.2
+ *                         (32 weights per scale and zero point).
  *   router logits         "12GB card runs a 68GB model (Betelgeuse)", MoE
  *                         primer: the router scores every expert from the
  *                         token's hidden state.
@@ -38,8 +40,6 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
-
-#define ORC_GROUP 128
 
 /* ---------------------------------------------------------------- formats */
 
@@ -139,20 +139,22 @@ int orc_code(const uint8_t* row, int k, int bits) {
     return (row[k >> 2] >> (2 * (k & 3))) & 0x3;
 }
 
-/* Dequantised weight (exact in double): code * scale + bias of k's group. */
-double orc_weight(const uint8_t* qrow, const uint16_t* srow, const uint16_t* brow, int k, int bits) {
-    int g = k / ORC_GROUP;
+/* Dequantised weight (exact in double): code * scale + bias of k's group, the
+ * group being `group` consecutive k (32, 64 or 128). */
+double orc_weight(const uint8_t* qrow, const uint16_t* srow, const uint16_t* brow, int k, int bits, int group) {
+    int g = k / group;
     return (double)orc_code(qrow, k, bits) * (double)orc_f16_to_f32(srow[g])
          + (double)orc_f16_to_f32(brow[g]);
 }
 
 /* Dequantise rows [N, K] into a dense double matrix (test helper). */
-void orc_dequant_matrix(int N, int K, int bits, const uint8_t* q, const uint16_t* s,
+void orc_dequant_matrix(int N, int K, int bits, int group, const uint8_t* q, const uint16_t* s,
                         const uint16_t* b, double* out) {
-    size_t rowb = (size_t)K * bits / 8, ng = (size_t)K / ORC_GROUP;
+    size_t rowb = (size_t)K * bits / 8, ng = (size_t)K / group;
     for (int n = 0; n < N; ++n)
         for (int k = 0; k < K; ++k)
-            out[(size_t)n * K + k] = orc_weight(q + (size_t)n * rowb, s + (size_t)n * ng, b + (size_t)n * ng, k, bits);
+            out[(size_t)n * K + k] =
+                orc_weight(q + (size_t)n * rowb, s + (size_t)n * ng, b + (size_t)n * ng, k, bits, group);
 }
 
 /* ---------------------------------------------------------- router logits */
@@ -263,24 +265,24 @@ void orc_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* off
  *   a_i = sum_k Wg[i,k] x_k,  u_i = sum_k Wu[i,k] x_k      (double, -> float)
  *   h_i = silu(a_i) * u_i,  silu(z) = z / (1 + e^-z)        (double, -> float)
  *   y_n = sum_i Wd[n,i] h_i                                 (double, -> bf16)
- * Weights: gate/up rows [I][H*bits/8] with scale/bias [I][H/128]; down rows
- * [H][I*bits/8] with scale/bias [H][I/128].
+ * Weights: gate/up rows [I][H*bits/8] with scale/bias [I][H/group]; down rows
+ * [H][I*bits/8] with scale/bias [H][I/group].
  * n_idx == NULL: y_out[n] for every n < H.  Otherwise y_out[j] holds output
  * n_idx[j] for j < n_count (a sample of the row's outputs). */
-void orc_expert_ffn_row(int H, int I, int bits, const uint16_t* x,
+void orc_expert_ffn_row(int H, int I, int bits, int group, const uint16_t* x,
                         const uint8_t* qg, const uint16_t* sg, const uint16_t* bg,
                         const uint8_t* qu, const uint16_t* su, const uint16_t* bu,
                         const uint8_t* qd, const uint16_t* sd, const uint16_t* bd,
                         int n_count, const int32_t* n_idx,
                         float* h_out, uint16_t* y_out) {
-    size_t rowH = (size_t)H * bits / 8, ngH = (size_t)H / ORC_GROUP;
-    size_t rowI = (size_t)I * bits / 8, ngI = (size_t)I / ORC_GROUP;
+    size_t rowH = (size_t)H * bits / 8, ngH = (size_t)H / group;
+    size_t rowI = (size_t)I * bits / 8, ngI = (size_t)I / group;
     for (int i = 0; i < I; ++i) {
         double a = 0.0, u = 0.0;
         for (int kk = 0; kk < H; ++kk) {
             double xv = (double)orc_bf16_to_f32(x[kk]);
-            a += orc_weight(qg + (size_t)i * rowH, sg + (size_t)i * ngH, bg + (size_t)i * ngH, kk, bits) * xv;
-            u += orc_weight(qu + (size_t)i * rowH, su + (size_t)i * ngH, bu + (size_t)i * ngH, kk, bits) * xv;
+            a += orc_weight(qg + (size_t)i * rowH, sg + (size_t)i * ngH, bg + (size_t)i * ngH, kk, bits, group) * xv;
+            u += orc_weight(qu + (size_t)i * rowH, su + (size_t)i * ngH, bu + (size_t)i * ngH, kk, bits, group) * xv;
         }
         double af = (double)(float)a, uf = (double)(float)u;
         double silu = af / (1.0 + exp(-af));
@@ -291,7 +293,7 @@ void orc_expert_ffn_row(int H, int I, int bits, const uint16_t* x,
         int n = n_idx ? n_idx[j] : j;
         double y = 0.0;
         for (int i = 0; i < I; ++i)
-            y += orc_weight(qd + (size_t)n * rowI, sd + (size_t)n * ngI, bd + (size_t)n * ngI, i, bits)
+            y += orc_weight(qd + (size_t)n * rowI, sd + (size_t)n * ngI, bd + (size_t)n * ngI, i, bits, group)
                * (double)h_out[i];
         y_out[j] = orc_f64_to_bf16(y);
     }

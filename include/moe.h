@@ -44,7 +44,7 @@
  *     synchronisation.
  *   - Limits: 0 <= T, T*k <= 65536; 1 <= E <= 1024; 1 <= k <= min(E, 32);
  *     H and I multiples of 128 with 128 <= H <= 8192 and 128 <= I <= 16384;
- *     group_size == 128.  Device pointers to codes and activations must be
+ *     group_size 128, 64 or 32.  Device pointers to codes and activations must be
  *     16-byte aligned, and so must scale and bias arrays.
  *   - Ids passed back in must come from these calls (or satisfy the same
  *     invariants); kernels skip out-of-range ids rather than touch memory
@@ -115,12 +115,15 @@ typedef struct moe_dims {
     int32_t I;           /* expert intermediate size */
     int32_t E;           /* routed experts */
     int32_t k;           /* experts per token */
-    int32_t group_size;  /* quantisation group along K; must be 128 */
+    int32_t group_size;  /* quantisation group along K: 128, 64 or 32 (see the
+                            FFN calls for which paths take 64 and 32) */
 } moe_dims;
 
 /* Quantised expert weights, expert-major so that every expert's matrices sit
  * in one buffer per matrix ("Strata" sec. 3.4).  Index m: 0 = gate [I][H],
- * 1 = up [I][H], 2 = down [H][I], written [N][K] below.
+ * 1 = up [I][H], 2 = down [H][I], written [N][K] below; G = dims.group_size
+ * (one scale and bias per G consecutive k: 128, the "Strata" page sec. 2.2;
+ * 64, the same page sec. 4.4; 32, the laptop page sec. 4.2).
  *   q[m]      uint8 [E][K/128][N][16*bits], group-major: for each group of
  *             128 along K, the codes of that group of all N rows follow one
  *             another (row n's piece of group g at ((e K/128 + g) N + n)
@@ -131,8 +134,8 @@ typedef struct moe_dims {
  *             start).  A row-major [N][K*bits/8] array becomes this layout by
  *             viewing it as [N][K/128][16*bits] and swapping the first two
  *             axes (group_major() in the Python binding).
- *   scale[m]  fp16 bit patterns [E][N][K/128]
- *   bias[m]   fp16 bit patterns [E][N][K/128]
+ *   scale[m]  fp16 bit patterns [E][N][K/G]
+ *   bias[m]   fp16 bit patterns [E][N][K/G]
  * The struct itself is a host object holding device pointers; it is read
  * during the call only. */
 typedef struct moe_qweights {
@@ -262,6 +265,13 @@ int moe_work_list_capacity(const moe_dims* dims, int32_t* entries);
  * Each expert's weights are read once per call for all of its tokens (once per
  * work-list tile of up to 16 tokens).  n_work is read on the device, so the
  * call never waits for routing results on the host.
+ * Groups of 64 and 32 (dims.group_size): the matrix-core algorithm takes them
+ * where the decode kernels' tiles fit LDS (T up to 16 tokens per tile, the
+ * activation row and h planes in 80 KB); the vector-ALU algorithm where one
+ * scale group holds a whole 16-byte chunk of codes (groups of 64 and 32 at
+ * 4 bits, 64 at 2 bits); MOE_ALGO_AUTO picks one of these.  Other cases
+ * (the grouped GEMM, the persistent and streaming matrix-core kernels of
+ * larger shapes) fail with MOE_ERR_UNSUPPORTED.
  * workspace: at least moe_workspace_bytes(dims, MOE_OP_FFN, 4, algo), 256-byte
  * aligned.  algo: MOE_ALGO_*. */
 int moe_expert_ffn_q4(const moe_dims* dims, const uint16_t* x, const int32_t* work_list,

@@ -47,8 +47,8 @@ int check_dims(const char* fn, const moe_dims* d, bool need_h, bool need_i) {
         return fail(MOE_ERR_UNSUPPORTED, "%s: k = %d outside [1, min(E, 32)]", fn, d->k);
     if ((long long)d->T * d->k > 65536)
         return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld exceeds 65536", fn, (long long)d->T * d->k);
-    if (d->group_size != 128)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: group_size = %d (only 128 is supported)", fn, d->group_size);
+    if (d->group_size != 128 && d->group_size != 64 && d->group_size != 32)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: group_size = %d (32, 64 or 128)", fn, d->group_size);
     if (need_h && (d->H < 128 || d->H > 8192 || d->H % 128 != 0))
         return fail(MOE_ERR_UNSUPPORTED, "%s: H = %d must be a multiple of 128 in [128, 8192]", fn, d->H);
     if (need_i && (d->I < 128 || d->I > 16384 || d->I % 128 != 0))
@@ -68,7 +68,13 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* w
     if (algo != MOE_ALGO_AUTO && algo != MOE_ALGO_GEMV && algo != MOE_ALGO_MFMA && algo != MOE_ALGO_GEMM)
         return fail(MOE_ERR_UNSUPPORTED, "%s: unknown algo %d", fn, algo);
     if (algo == MOE_ALGO_GEMM && !moe::gemm_supported(*d, bits))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: the grouped GEMM needs 4-bit codes and H, I multiples of 128, at least 256", fn);
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: the grouped GEMM needs 4-bit codes, groups of 128 and H, I multiples of 128, at least 256", fn);
+    if (!moe::ffn_group_supported(*d, bits, algo))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: groups of %d need the decode kernels (tiles that fit LDS) or, for groups of at least one "
+                    "16-byte chunk of codes (%d), the vector-ALU path",
+                    fn, d->group_size, 128 / bits);
     if (d->T == 0) return MOE_OK;
     REQUIRE_PTR(work_list, 16);
     REQUIRE_PTR(n_work, 4);

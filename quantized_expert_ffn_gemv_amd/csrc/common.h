@@ -192,6 +192,7 @@ size_t gemm_workspace_bytes(const moe_dims& d);
 int launch_gateup_gemm(const FfnArgs& a, hipStream_t s);
 int launch_down_gemm(const FfnArgs& a, hipStream_t s);
 int resolve_algo(const moe_dims& d, int bits, int algo);
+bool ffn_group_supported(const moe_dims& d, int bits, int algo);
 int launch_gateup_gemv(const FfnArgs& a, hipStream_t s);
 int launch_down_gemv(const FfnArgs& a, hipStream_t s);
 int launch_gateup_mfma(const FfnArgs& a, hipStream_t s);

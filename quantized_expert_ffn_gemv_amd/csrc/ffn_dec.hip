@@ -233,21 +233,51 @@ constexpr uint32_t kOnesBf16 = 0x3F803F80u;   // two bf16 ones
 // code loads.  LDS: the x tile [rows_cap][H] bf16, then the raw fp16 scales
 // and biases of the block's gate and up rows, [RI][NG] each; after the loop
 // the first 8 KB holds the partial sums over K.
+// Groups of 64 or 32 (SPG = 2 or 4 scale groups per 128 codes).  In the
+// natural operand order, lane quarter q holds the 32 codes k = 32 q .. +31
+// of a 128-code run and MFMA step st takes 8 of them from every quarter, so a
+// step mixes all four quarters.  For finer groups the roles of q and st are
+// swapped: lane quarter q at step st supplies what quarter st supplies at step
+// q in the natural order (codes: one 32-bit word per step, from quarter st's
+// bytes; activations: chunk 4 st + q of the pair-ordered row instead of
+// 4 q + st), so step st covers exactly quarter st, i.e. k = 32 st .. +31, and
+// a group of 32 is one step, a group of 64 two.  The products and their pair
+// order are unchanged; only which step carries them moves.
+// Byte offset of the word lane quarter q loads for step st, within a row's
+// run of 128 codes.
+template <int BITS>
+__device__ __forceinline__ int tr_word_offset(int st, int q) {
+    return BITS == 4 ? 16 * st + 4 * q : 8 * st + 4 * (q >> 1);
+}
+
+// B operand of step st in the swapped order from the step's word w[st].
+template <int BITS>
+__device__ __forceinline__ void code_operand_tr(const uint32_t* w, int st, int q, uint32_t (&out)[4]) {
+    if constexpr (BITS == 4) {
+        code_operand<4>(w, st, out);
+    } else {
+        const uint32_t v[2] = {w[st] >> (8 * (q & 1)), 0u};   // 2-bit: quarter st's half word for step q
+        code_operand<2>(v, 0, out);
+    }
+}
+
 // COH: h leaves through device-scope stores (read by down items of the same
 // launch) and without the 16-row partial sums (only the non-staged down
 // kernel reads those).
-template <int BITS, int RW, int D, bool COH>
+template <int BITS, int RW, int D, bool COH, int SPG = 1>
 __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& it, uint8_t* smem) {
     constexpr int KS = 4 / RW;
     constexpr int LB = 128 * BITS / 8 / 4;     // code bytes per lane per group
-    constexpr int LW = LB / 4;
+    constexpr bool TR = SPG > 1;               // steps swapped: one quarter of the 128 codes per step
+    constexpr int LW = TR ? 4 : LB / 4;        // code words per lane per group
+    constexpr int SST = 4 / SPG;               // MFMA steps per scale group
     constexpr int RI = 16 * RW;                // gate (and up) rows per item
     if (it.n == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wid / KS, wk = wid % KS;
-    const int H = p.H, I = p.I, NG = H / kGroup, rowb = H * 2;
-    const int sc_bytes = RI * NG * 2;
+    const int H = p.H, I = p.I, NG = H / kGroup, NS = NG * SPG, rowb = H * 2;
+    const int sc_bytes = RI * NS * 2;
     const int sc_stride = (int)round_dma(sc_bytes);
     uint8_t* xs = smem;
     uint8_t* scl = smem + round_dma((size_t)p.rows_cap * rowb);          // gate s, gate b, up s, up b
@@ -259,7 +289,7 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
         return p.x + (size_t)__shfl(tokv, j, kWave) * H + g * kGroup + 8 * c;
     });
     {
-        const size_t first = ((size_t)it.e * I + (size_t)it.rb * RI) * NG;
+        const size_t first = ((size_t)it.e * I + (size_t)it.rb * RI) * NS;
         dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
         dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
         dma_copy(reinterpret_cast<const uint8_t*>(p.sb + first), scl + 2 * sc_stride, sc_bytes, wid, lane);
@@ -271,13 +301,19 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     const int rloc = 16 * wr + pair_order_row<BITS>(m);
     // codes are group-major: row r of expert e, group g at ((e NG + g) I + r) 4 LB
     const size_t gstride = (size_t)I * (4 * LB);
-    const size_t cbase = (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
+    const size_t cbase = (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + (TR ? 0 : q * LB);
     const uint8_t* cg = p.qa + cbase;
     const uint8_t* cu = p.qb + cbase;
     uint32_t rg[D][LW], ru[D][LW];
     auto issue = [&](int slot, int gl) {
         const size_t off = (size_t)(gb + (gl < ng ? gl : ng - 1)) * gstride;
-        if constexpr (BITS == 4) {
+        if constexpr (TR) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                rg[slot][st] = *reinterpret_cast<const uint32_t*>(cg + off + tr_word_offset<BITS>(st, q));
+                ru[slot][st] = *reinterpret_cast<const uint32_t*>(cu + off + tr_word_offset<BITS>(st, q));
+            }
+        } else if constexpr (BITS == 4) {
             const uint4 A = *reinterpret_cast<const uint4*>(cg + off);
             const uint4 B = *reinterpret_cast<const uint4*>(cu + off);
             rg[slot][0] = A.x; rg[slot][1] = A.y; rg[slot][2] = A.z; rg[slot][3] = A.w;
@@ -291,7 +327,7 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d, d);
-    wait_vmem<2 * D>();                        // the staging loads, older than the 2 D ring loads
+    wait_vmem<2 * D * (TR ? 4 : 1)>();         // the staging loads, older than the ring loads
     lds_barrier();
 
     // ---- the x tile into code pair order, once per workgroup.  Unit (j, g,
@@ -323,11 +359,11 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     const uint8_t* xrow = xs + mrow * rowb;
     int coff[4];                               // swizzled chunk offsets of this lane's quarter
 #pragma unroll
-    for (int st = 0; st < 4; ++st) coff[st] = 16 * ((4 * q + st) ^ (mrow & 15));
-    const uint16_t* gsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NG;
-    const uint16_t* gbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NG;
-    const uint16_t* usc = reinterpret_cast<const uint16_t*>(scl + 2 * sc_stride) + rloc * NG;
-    const uint16_t* ubi = reinterpret_cast<const uint16_t*>(scl + 3 * sc_stride) + rloc * NG;
+    for (int st = 0; st < 4; ++st) coff[st] = 16 * ((TR ? 4 * st + q : 4 * q + st) ^ (mrow & 15));
+    const uint16_t* gsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NS;
+    const uint16_t* gbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NS;
+    const uint16_t* usc = reinterpret_cast<const uint16_t*>(scl + 2 * sc_stride) + rloc * NS;
+    const uint16_t* ubi = reinterpret_cast<const uint16_t*>(scl + 3 * sc_stride) + rloc * NS;
     const uint32_t ONES[4] = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
 
     floatx4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
@@ -335,21 +371,32 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     // repeat the last group (codes and activations) with zero scale and bias.
     auto step = [&](int d, int gl, bool valid) {
         const int g = gb + gl;
+        const uint32_t keep = valid ? 0xFFFFu : 0u;    // loads stay unconditional (no branch)
         floatx4_t Cg = {0.f, 0.f, 0.f, 0.f}, Cu = Cg, Cx = Cg;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const uint4 v = *reinterpret_cast<const uint4*>(xrow + g * 256 + coff[st]);
             const uint32_t A[4] = {v.x, v.y, v.z, v.w};
             uint32_t Bg[4], Bu[4];
-            code_operand<BITS>(rg[d], st, Bg);
-            code_operand<BITS>(ru[d], st, Bu);
+            if constexpr (TR) {
+                code_operand_tr<BITS>(rg[d], st, q, Bg);
+                code_operand_tr<BITS>(ru[d], st, q, Bu);
+            } else {
+                code_operand<BITS>(rg[d], st, Bg);
+                code_operand<BITS>(ru[d], st, Bu);
+            }
             Cg = mfma16(A, Bg, Cg);
             Cu = mfma16(A, Bu, Cu);
             Cx = mfma16(A, ONES, Cx);           // group sum of x per token (any order)
+            if (st % SST == SST - 1) {          // the scale group's last step
+                const int sg = g * SPG + st / SST;
+                fold<BITS>(accg, Cg, gsc[sg] & keep, gbi[sg] & keep, Cx);
+                fold<BITS>(accu, Cu, usc[sg] & keep, ubi[sg] & keep, Cx);
+                Cg = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                Cu = Cg;
+                Cx = Cg;
+            }
         }
-        const uint32_t keep = valid ? 0xFFFFu : 0u;    // loads stay unconditional (no branch)
-        fold<BITS>(accg, Cg, gsc[g] & keep, gbi[g] & keep, Cx);
-        fold<BITS>(accu, Cu, usc[g] & keep, ubi[g] & keep, Cx);
     };
     // Full blocks refill every slot unconditionally (the compiler then keeps
     // exact load counts across the loop and waits only for the slot it
@@ -422,12 +469,12 @@ __device__ __forceinline__ void gateup_item(const DecParams& p, const DecItem& i
     }
 }
 
-template <int BITS, int RW, int D, bool SHARED = false>
+template <int BITS, int RW, int D, bool SHARED = false, int SPG = 1>
 __global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (blockIdx.x == 0)                                  // the streaming down's counters start at zero
         for (int i = threadIdx.x; i < p.n_split_ctr; i += 256) p.split_ctr[i] = 0;
-    gateup_item<BITS, RW, D, false>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
+    gateup_item<BITS, RW, D, false, SPG>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
 }
 
 // ------------------------------------------------------------------- down
@@ -440,18 +487,20 @@ __global__ __launch_bounds__(256, 2) void ffn_gateup_dec_kernel(DecParams p) {
 // scales and the first code-ring slots are requested first; then thread 0
 // waits until *ready reaches `need` (bounded; on time-out *err is set), and
 // only then are the h planes loaded (device-scope loads).
-template <int BITS, int RT, int D, bool WAIT>
+template <int BITS, int RT, int D, bool WAIT, int SPG = 1>
 __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it, uint8_t* smem,
                                           int32_t* ready = nullptr, int need = 0, int32_t* err = nullptr) {
     constexpr int LB = 128 * BITS / 8 / 4;
-    constexpr int LW = LB / 4;
+    constexpr bool TR = SPG > 1;               // steps swapped (groups of 64 or 32)
+    constexpr int LW = TR ? 4 : LB / 4;
+    constexpr int SST = 4 / SPG;
     constexpr int RI = 64 * RT;
     if (it.n == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.H, I = p.I, NG = I / kGroup, rowb = I * 2;
+    const int H = p.H, I = p.I, NG = I / kGroup, NS = NG * SPG, rowb = I * 2;
     const int plane_b = (int)round_dma((size_t)p.rows_cap * rowb);
-    const int sc_bytes = RI * NG * 2;
+    const int sc_bytes = RI * NS * 2;
     const int sc_stride = (int)round_dma(sc_bytes);
     uint8_t* hs = smem;
     uint8_t* scl = smem + 3 * (size_t)plane_b;                          // s, then b
@@ -468,7 +517,7 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
     };
     if constexpr (!WAIT) stage_h();
     {
-        const size_t first = ((size_t)it.e * H + (size_t)it.rb * RI) * NG;
+        const size_t first = ((size_t)it.e * H + (size_t)it.rb * RI) * NS;
         dma_copy(reinterpret_cast<const uint8_t*>(p.sa + first), scl, sc_bytes, wid, lane);
         dma_copy(reinterpret_cast<const uint8_t*>(p.ba + first), scl + sc_stride, sc_bytes, wid, lane);
     }
@@ -477,14 +526,18 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
     const int rloc = 16 * RT * wid + m;               // + 16 rt
     // codes are group-major: row r of expert e, group g at ((e NG + g) H + r) 4 LB
     const size_t gstride = (size_t)H * (4 * LB);
-    const uint8_t* cp = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
+    const uint8_t* cp = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + (TR ? 0 : q * LB);
     uint32_t rc[D][RT][LW];
     auto issue = [&](int slot, int g) {
         const size_t off = (size_t)(g < NG ? g : NG - 1) * gstride;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const uint8_t* src = cp + (size_t)(16 * rt) * (4 * LB) + off;
-            if constexpr (BITS == 4) {
+            if constexpr (TR) {
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    rc[slot][rt][st] = *reinterpret_cast<const uint32_t*>(src + tr_word_offset<BITS>(st, q));
+            } else if constexpr (BITS == 4) {
                 const uint4 A = *reinterpret_cast<const uint4*>(src);
                 rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y; rc[slot][rt][2] = A.z; rc[slot][rt][3] = A.w;
             } else {
@@ -493,6 +546,7 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
             }
         }
     };
+    constexpr int LPI = TR ? 4 : 1;            // loads per ring slot and row tile
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d, d);
     if constexpr (WAIT) {
@@ -508,7 +562,7 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
         stage_h();
         wait_vmem<0>();
     } else {
-        wait_vmem<RT * D>();
+        wait_vmem<RT * D * LPI>();
     }
     lds_barrier();
 
@@ -516,9 +570,9 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
     const uint8_t* hrow = hs + mrow * rowb;
     int coff[4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) coff[st] = 16 * ((4 * q + st) ^ (mrow & 15));
-    const uint16_t* dsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NG;
-    const uint16_t* dbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NG;
+    for (int st = 0; st < 4; ++st) coff[st] = 16 * ((TR ? 4 * st + q : 4 * q + st) ^ (mrow & 15));
+    const uint16_t* dsc = reinterpret_cast<const uint16_t*>(scl) + rloc * NS;
+    const uint16_t* dbi = reinterpret_cast<const uint16_t*>(scl + sc_stride) + rloc * NS;
     const uint32_t ONES[4] = {kOnesBf16, kOnesBf16, kOnesBf16, kOnesBf16};
     floatx4_t acc[RT];
 #pragma unroll
@@ -526,6 +580,7 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
     // `valid` false: padding step of the last block (last group again, zero
     // scale and bias)
     auto step = [&](int d, int g, bool valid) {
+        const uint32_t keep = valid ? 0xFFFFu : 0u;    // loads stay unconditional (no branch)
         floatx4_t C[RT], Cx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) C[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -540,7 +595,8 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 uint32_t B[4];
-                code_operand<BITS>(rc[d][rt], st, B);
+                if constexpr (TR) code_operand_tr<BITS>(rc[d][rt], st, q, B);
+                else code_operand<BITS>(rc[d][rt], st, B);
                 C[rt] = mfma16(A[0], B, C[rt]);
                 C[rt] = mfma16(A[1], B, C[rt]);
                 C[rt] = mfma16(A[2], B, C[rt]);
@@ -548,11 +604,16 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
             Cx = mfma16(A[0], ONES, Cx);        // group sum of h per token, all three planes
             Cx = mfma16(A[1], ONES, Cx);
             Cx = mfma16(A[2], ONES, Cx);
-        }
-        const uint32_t keep = valid ? 0xFFFFu : 0u;    // loads stay unconditional (no branch)
+            if (st % SST == SST - 1) {          // the scale group's last step
+                const int sg = g * SPG + st / SST;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            fold<BITS>(acc[rt], C[rt], dsc[16 * rt * NG + g] & keep, dbi[16 * rt * NG + g] & keep, Cx);
+                for (int rt = 0; rt < RT; ++rt) {
+                    fold<BITS>(acc[rt], C[rt], dsc[16 * rt * NS + sg] & keep, dbi[16 * rt * NS + sg] & keep, Cx);
+                    C[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                Cx = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
     };
     // full blocks refill unconditionally, the peeled last block issues nothing
     const int NGP = (NG + D - 1) / D * D;
@@ -583,10 +644,10 @@ __device__ __forceinline__ void down_item(const DecParams& p, const DecItem& it,
     }
 }
 
-template <int BITS, int RT, int D, bool SHARED = false>
+template <int BITS, int RT, int D, bool SHARED = false, int SPG = 1>
 __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    down_item<BITS, RT, D, false>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
+    down_item<BITS, RT, D, false, SPG>(p, dec_item_xcd<SHARED>(p, 0, (int)blockIdx.x), smem);
 }
 
 // ------------------------------------------------------------ streaming down
@@ -1028,7 +1089,7 @@ struct FusedParams {
     int32_t* err;                                                // set to 1 when a wait times out
 };
 
-template <int BITS, int RW, int DG, int RT, int DD, bool SHARED = false>
+template <int BITS, int RW, int DG, int RT, int DD, bool SHARED = false, int SPG = 1>
 __global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, int32_t* sync) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int ng = kFfnChunk * f.p.ipe, span = ng + kFfnChunk * f.ipe_d;
@@ -1036,7 +1097,7 @@ __global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, in
     const int entry0 = chunk * kFfnChunk;
     if (r < ng) {
         const DecItem it = dec_item_xcd<SHARED>(f.p, entry0, r);
-        gateup_item<BITS, RW, DG, true>(f.p, it, smem);
+        gateup_item<BITS, RW, DG, true, SPG>(f.p, it, smem);
         if (it.n == 0) return;
         __builtin_amdgcn_s_waitcnt(0);          // this wave's h stores have completed
         __syncthreads();
@@ -1048,7 +1109,7 @@ __global__ __launch_bounds__(256, 2) void ffn_fused_dec_kernel(FusedParams f, in
         const DecItem it = dec_item_xcd<SHARED>(pd, entry0, r - ng);
         if (it.n == 0) return;
         int32_t* ctr = &sync[kFfnStride * it.entry];
-        down_item<BITS, RT, DD, true>(pd, it, smem, ctr, f.p.ipe, f.err);
+        down_item<BITS, RT, DD, true, SPG>(pd, it, smem, ctr, f.p.ipe, f.err);
         if (threadIdx.x == 0 &&
             __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == f.ipe_d - 1) {
             __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1097,16 +1158,16 @@ static int dec_down_rt(const moe_dims& d) {
 
 static size_t dec_gateup_lds(const moe_dims& d, int rw) {
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
-    const int NG = d.H / kGroup;
-    const size_t stage = round_dma((size_t)rows_cap * d.H * 2) + 4 * round_dma((size_t)16 * rw * NG * 2);
+    const int NS = d.H / d.group_size;                  // scale groups per row
+    const size_t stage = round_dma((size_t)rows_cap * d.H * 2) + 4 * round_dma((size_t)16 * rw * NS * 2);
     const size_t red = (rw < 4) ? (size_t)4 * 64 * 8 * 4 : 0;
     return stage > red ? stage : red;
 }
 
 static size_t dec_down_lds(const moe_dims& d, int rt) {
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
-    const int NG = d.I / kGroup;
-    return 3 * round_dma((size_t)rows_cap * d.I * 2) + 2 * round_dma((size_t)64 * rt * NG * 2);
+    const int NS = d.I / d.group_size;
+    return 3 * round_dma((size_t)rows_cap * d.I * 2) + 2 * round_dma((size_t)64 * rt * NS * 2);
 }
 
 // Ring depth: the deepest of `cap`, cap / 2, ..., 2 that pads a wave's groups
@@ -1126,24 +1187,36 @@ static int dec_depth(int ng, int cap) {
 bool dec_gateup_fits(const moe_dims& d) { return dec_gateup_lds(d, dec_gateup_rw(d)) <= kDecLdsLimit; }
 bool dec_down_fits(const moe_dims& d) { return dec_down_lds(d, dec_down_rt(d)) <= kDecLdsLimit; }
 
-template <int BITS, int RW, int D, bool SHARED>
+template <int BITS, int RW, int D, bool SHARED, int SPG>
 static void gu_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
     const dim3 grid((unsigned)((p.cap + p.n_shared + 7) / 8 * 8 * p.ipe));   // entries rounded up to 8 (one per XCD)
-    hipLaunchKernelGGL((ffn_gateup_dec_kernel<BITS, RW, D, SHARED>), grid, dim3(256), lds, s, p);
+    hipLaunchKernelGGL((ffn_gateup_dec_kernel<BITS, RW, D, SHARED, SPG>), grid, dim3(256), lds, s, p);
 }
 
-template <int BITS, int RW, bool SHARED>
+template <int BITS, int RW, bool SHARED, int SPG>
 static void gu_depth(int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (D >= 4) gu_go<BITS, RW, 4, SHARED>(d, lds, s, p);
-    else if (D >= 2) gu_go<BITS, RW, 2, SHARED>(d, lds, s, p);
-    else gu_go<BITS, RW, 1, SHARED>(d, lds, s, p);
+    if (D >= 4) gu_go<BITS, RW, 4, SHARED, SPG>(d, lds, s, p);
+    else if (D >= 2) gu_go<BITS, RW, 2, SHARED, SPG>(d, lds, s, p);
+    else gu_go<BITS, RW, 1, SHARED, SPG>(d, lds, s, p);
 }
+
+template <int BITS, bool SHARED, int SPG>
+static void gu_rw(int rw, int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
+    if (rw == 4) gu_depth<BITS, 4, SHARED, SPG>(D, d, lds, s, p);
+    else if (rw == 2) gu_depth<BITS, 2, SHARED, SPG>(D, d, lds, s, p);
+    else gu_depth<BITS, 1, SHARED, SPG>(D, d, lds, s, p);
+}
+
+// Scale groups per run of 128 codes: 1, 2 or 4 (groups of 128, 64 or 32).
+inline int scale_groups(const moe_dims& d) { return kGroup / d.group_size; }
 
 template <int BITS, bool SHARED>
-static void gu_rw(int rw, int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (rw == 4) gu_depth<BITS, 4, SHARED>(D, d, lds, s, p);
-    else if (rw == 2) gu_depth<BITS, 2, SHARED>(D, d, lds, s, p);
-    else gu_depth<BITS, 1, SHARED>(D, d, lds, s, p);
+static void gu_spg(int rw, int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
+    switch (scale_groups(d)) {
+        case 4: gu_rw<BITS, SHARED, 4>(rw, D, d, lds, s, p); break;
+        case 2: gu_rw<BITS, SHARED, 2>(rw, D, d, lds, s, p); break;
+        default: gu_rw<BITS, SHARED, 1>(rw, D, d, lds, s, p); break;
+    }
 }
 
 // d sizes the items; p carries the entries (and any shared tiles).
@@ -1156,8 +1229,8 @@ static int gateup_dec_run(const FfnArgs& a, const moe_dims& d, DecParams p, hipS
     const size_t lds = dec_gateup_lds(d, rw);
     if (lds > kDecLdsLimit) return MOE_ERR_UNSUPPORTED;
     const int D = dec_depth((d.H / kGroup) / (4 / rw), 4);
-    if (a.bits == 4) gu_rw<4, SHARED>(rw, D, d, lds, s, p);
-    else gu_rw<2, SHARED>(rw, D, d, lds, s, p);
+    if (a.bits == 4) gu_spg<4, SHARED>(rw, D, d, lds, s, p);
+    else gu_spg<2, SHARED>(rw, D, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -1166,16 +1239,32 @@ int launch_gateup_dec(const FfnArgs& a, hipStream_t s) {
     return gateup_dec_run<false>(a, a.d, dec_params(a), s);
 }
 
-template <int BITS, int RT, int D, bool SHARED>
+template <int BITS, int RT, int D, bool SHARED, int SPG>
 static void dn_go(const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
     const dim3 grid((unsigned)((p.cap + p.n_shared + 7) / 8 * 8 * p.ipe));   // entries rounded up to 8 (one per XCD)
-    hipLaunchKernelGGL((ffn_down_dec_kernel<BITS, RT, D, SHARED>), grid, dim3(256), lds, s, p);
+    hipLaunchKernelGGL((ffn_down_dec_kernel<BITS, RT, D, SHARED, SPG>), grid, dim3(256), lds, s, p);
 }
 
-template <int BITS, int RT, bool SHARED>
+template <int BITS, int RT, bool SHARED, int SPG>
 static void dn_depth(int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
-    if (D >= 2) dn_go<BITS, RT, 2, SHARED>(d, lds, s, p);
-    else dn_go<BITS, RT, 1, SHARED>(d, lds, s, p);
+    if (D >= 2) dn_go<BITS, RT, 2, SHARED, SPG>(d, lds, s, p);
+    else dn_go<BITS, RT, 1, SHARED, SPG>(d, lds, s, p);
+}
+
+template <int BITS, bool SHARED, int SPG>
+static void dn_rt(int rt, int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
+    if (rt == 4) dn_depth<BITS, 4, SHARED, SPG>(D, d, lds, s, p);
+    else if (rt == 2) dn_depth<BITS, 2, SHARED, SPG>(D, d, lds, s, p);
+    else dn_depth<BITS, 1, SHARED, SPG>(D, d, lds, s, p);
+}
+
+template <int BITS, bool SHARED>
+static void dn_spg(int rt, int D, const moe_dims& d, size_t lds, hipStream_t s, const DecParams& p) {
+    switch (scale_groups(d)) {
+        case 4: dn_rt<BITS, SHARED, 4>(rt, D, d, lds, s, p); break;
+        case 2: dn_rt<BITS, SHARED, 2>(rt, D, d, lds, s, p); break;
+        default: dn_rt<BITS, SHARED, 1>(rt, D, d, lds, s, p); break;
+    }
 }
 
 template <bool SHARED>
@@ -1186,15 +1275,8 @@ static int down_dec_run(const FfnArgs& a, const moe_dims& d, DecParams p, hipStr
     const size_t lds = dec_down_lds(d, rt);
     if (lds > kDecLdsLimit) return MOE_ERR_UNSUPPORTED;
     const int D = dec_depth(d.I / kGroup, 2);
-    if (a.bits == 4) {
-        if (rt == 4) dn_depth<4, 4, SHARED>(D, d, lds, s, p);
-        else if (rt == 2) dn_depth<4, 2, SHARED>(D, d, lds, s, p);
-        else dn_depth<4, 1, SHARED>(D, d, lds, s, p);
-    } else {
-        if (rt == 4) dn_depth<2, 4, SHARED>(D, d, lds, s, p);
-        else if (rt == 2) dn_depth<2, 2, SHARED>(D, d, lds, s, p);
-        else dn_depth<2, 1, SHARED>(D, d, lds, s, p);
-    }
+    if (a.bits == 4) dn_spg<4, SHARED>(rt, D, d, lds, s, p);
+    else dn_spg<2, SHARED>(rt, D, d, lds, s, p);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -1228,7 +1310,7 @@ static size_t down_stream_plan_lds(const moe_dims& d) {
 // run: where the decode down kernel fits, or K is not whole blocks of 8 groups,
 // or H is not whole row blocks, or no chunk size fits LDS.
 static int down_stream_cg(const moe_dims& d) {
-    if (d.T * d.k == 0 || dec_down_fits(d)) return 0;
+    if (d.T * d.k == 0 || dec_down_fits(d) || d.group_size != kGroup) return 0;
     if ((d.I / kGroup) % 8 != 0 || d.H % kStreamRows != 0) return 0;
     if (work_capacity(d) > 1024) return 0;     // the work split's tables
     for (int c = 4; c >= 2; c >>= 1)
@@ -1297,23 +1379,35 @@ int launch_down_stream(const FfnArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------ one-launch FFN
 
-template <int BITS, int RW, int DG, int RT, int DD, bool SHARED>
+template <int BITS, int RW, int DG, int RT, int DD, bool SHARED, int SPG>
 static int fused_go(size_t lds, hipStream_t s, const FusedParams& f, int32_t* sync) {
     const int chunks = (f.p.cap + f.p.n_shared + kFfnChunk - 1) / kFfnChunk;
     const dim3 grid((unsigned)(chunks * kFfnChunk * (f.p.ipe + f.ipe_d)));
-    hipLaunchKernelGGL((ffn_fused_dec_kernel<BITS, RW, DG, RT, DD, SHARED>), grid, dim3(256), lds, s, f, sync);
+    hipLaunchKernelGGL((ffn_fused_dec_kernel<BITS, RW, DG, RT, DD, SHARED, SPG>), grid, dim3(256), lds, s, f, sync);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // The decode configurations with a one-launch kernel; others take two launches.
-template <int BITS, bool SHARED>
-static int fused_pick(int rw, int dg, int rt, int dd, size_t lds, hipStream_t s, const FusedParams& f,
-                      int32_t* sync) {
-    if (rw == 4 && dg == 4 && rt == 4 && dd == 2) return fused_go<BITS, 4, 4, 4, 2, SHARED>(lds, s, f, sync);
-    if (rw == 4 && dg == 4 && rt == 2 && dd == 2) return fused_go<BITS, 4, 4, 2, 2, SHARED>(lds, s, f, sync);
-    if (rw == 1 && dg == 4 && rt == 1 && dd == 4) return fused_go<BITS, 1, 4, 1, 4, SHARED>(lds, s, f, sync);
-    if (rw == 1 && dg == 4 && rt == 1 && dd == 2) return fused_go<BITS, 1, 4, 1, 2, SHARED>(lds, s, f, sync);
+template <int BITS, bool SHARED, int SPG>
+static int fused_cfg(int rw, int dg, int rt, int dd, size_t lds, hipStream_t s, const FusedParams& f,
+                     int32_t* sync) {
+    if (rw == 4 && dg == 4 && rt == 4 && dd == 2) return fused_go<BITS, 4, 4, 4, 2, SHARED, SPG>(lds, s, f, sync);
+    if (rw == 4 && dg == 4 && rt == 2 && dd == 2) return fused_go<BITS, 4, 4, 2, 2, SHARED, SPG>(lds, s, f, sync);
+    if (rw == 1 && dg == 4 && rt == 1 && dd == 4) return fused_go<BITS, 1, 4, 1, 4, SHARED, SPG>(lds, s, f, sync);
+    if (rw == 1 && dg == 4 && rt == 1 && dd == 2) return fused_go<BITS, 1, 4, 1, 2, SHARED, SPG>(lds, s, f, sync);
     return MOE_ERR_UNSUPPORTED;
+}
+
+template <int BITS, bool SHARED>
+static int fused_pick(int spg, int rw, int dg, int rt, int dd, size_t lds, hipStream_t s, const FusedParams& f,
+                      int32_t* sync) {
+    // groups of 32 take the two decode launches: their one-launch variants
+    // spill registers (a fold per MFMA step on top of both items' state)
+    switch (spg) {
+        case 2: return fused_cfg<BITS, SHARED, 2>(rw, dg, rt, dd, lds, s, f, sync);
+        case 1: return fused_cfg<BITS, SHARED, 1>(rw, dg, rt, dd, lds, s, f, sync);
+        default: return MOE_ERR_UNSUPPORTED;
+    }
 }
 
 // The one-launch FFN with decode parameters p; d sizes the items.
@@ -1336,8 +1430,9 @@ static int fused_run(const FfnArgs& a, const moe_dims& d, const DecParams& p, in
     const int dg = dec_depth((d.H / kGroup) / (4 / rw), 4), dd = dec_depth(d.I / kGroup, rt == 1 ? 4 : 2);
     const size_t lg = dec_gateup_lds(d, rw), ld = dec_down_lds(d, rt);
     const size_t lds = lg > ld ? lg : ld;
-    return a.bits == 4 ? fused_pick<4, SHARED>(rw, dg, rt, dd, lds, s, f, sync)
-                       : fused_pick<2, SHARED>(rw, dg, rt, dd, lds, s, f, sync);
+    const int spg = scale_groups(d);
+    return a.bits == 4 ? fused_pick<4, SHARED>(spg, rw, dg, rt, dd, lds, s, f, sync)
+                       : fused_pick<2, SHARED>(spg, rw, dg, rt, dd, lds, s, f, sync);
 }
 
 int launch_ffn_fused_dec(const FfnArgs& a, int32_t* sync, hipStream_t s, int32_t* err) {

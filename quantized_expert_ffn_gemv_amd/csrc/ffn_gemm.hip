@@ -578,7 +578,8 @@ static size_t max_lds_per_block() {
 // The rings read up to D + 1 groups ahead and at most into the next item,
 // which needs at least two groups along each K.
 bool gemm_supported(const moe_dims& d, int bits) {
-    return bits == 4 && d.I % kGuRows == 0 && d.H % kDnRows == 0 && d.H >= 2 * kGroup && d.I >= 2 * kGroup;
+    return bits == 4 && d.group_size == kGroup && d.I % kGuRows == 0 && d.H % kDnRows == 0 && d.H >= 2 * kGroup &&
+           d.I >= 2 * kGroup;
 }
 
 // Ring depth: D must divide the group count and stay below it (the activation

@@ -44,6 +44,7 @@ struct GemvParams {
     int T, H, I, k, E;
     int LG;                 // lanes per row (power of two, divides the chunks per row)
     int items_per_expert;
+    int gs;                 // scale group along K: 128, 64 or 32 (at least one 16-byte chunk)
 };
 
 // codes of one 32-bit word -> bf16 pairs (128 + L q_j, 128 + L q_{j+W/2})
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
     constexpr int CK = 128 / BITS;       // codes per 16-byte chunk (one lane load)
     constexpr int PPW = 16 / BITS;       // bf16 pairs per 32-bit code word
     extern __shared__ uint32_t smem[];
-    const int H = p.H, I = p.I, NC = H / CK, NG = H / kGroup;
+    const int H = p.H, I = p.I, NC = H / CK, NG = H / kGroup, NS = H / p.gs;
     const int P = p.T * p.k;
     uint32_t* xs = smem;
     float* xc = reinterpret_cast<float*>(smem + PT * (H / 2));
@@ -122,10 +123,10 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
         {
             const size_t ri0 = (size_t)e * I + (v0 ? i0 : 0), ri1 = (size_t)e * I + (v1 ? i0 + 1 : 0);
             const size_t ci0 = ((size_t)e * NG * I + (v0 ? i0 : 0)) * GB, ci1 = ((size_t)e * NG * I + (v1 ? i0 + 1 : 0)) * GB;
-            qrow[0] = p.qa + ci0; srow[0] = p.sa + ri0 * NG; brow[0] = p.ba + ri0 * NG;
-            qrow[1] = p.qa + ci1; srow[1] = p.sa + ri1 * NG; brow[1] = p.ba + ri1 * NG;
-            qrow[2] = p.qb + ci0; srow[2] = p.sb + ri0 * NG; brow[2] = p.bb + ri0 * NG;
-            qrow[3] = p.qb + ci1; srow[3] = p.sb + ri1 * NG; brow[3] = p.bb + ri1 * NG;
+            qrow[0] = p.qa + ci0; srow[0] = p.sa + ri0 * NS; brow[0] = p.ba + ri0 * NS;
+            qrow[1] = p.qa + ci1; srow[1] = p.sa + ri1 * NS; brow[1] = p.ba + ri1 * NS;
+            qrow[2] = p.qb + ci0; srow[2] = p.sb + ri0 * NS; brow[2] = p.bb + ri0 * NS;
+            qrow[3] = p.qb + ci1; srow[3] = p.sb + ri1 * NS; brow[3] = p.bb + ri1 * NS;
         }
 
         for (int tt = 0; tt < cnt; tt += PT) {
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_gemv_kernel(GemvParams p) {
                     raw[r] = ok ? *reinterpret_cast<const uint4*>(qrow[r] + (size_t)c * 16 + (size_t)(c / BITS) * gskip)
                                 : make_uint4(0, 0, 0, 0);
                 }
-                const int g = (c * CK) / kGroup;
+                const int g = (c * CK) / p.gs;          // the chunk's scale group
                 float sc[4], bc[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
     constexpr int CK = 128 / BITS;       // codes per 16-byte chunk
     constexpr int WC = 32 / BITS;        // codes per 32-bit word
     extern __shared__ uint32_t smem[];
-    const int H = p.H, I = p.I, NC = I / CK, NG = I / kGroup;
+    const int H = p.H, I = p.I, NC = I / CK, NG = I / kGroup, NS = I / p.gs;
     float* hs = reinterpret_cast<float*>(smem);
     float* hc = hs + PT * I;
 
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
             vr[r] = n0 + r < H;
             const size_t ri = (size_t)e * H + (vr[r] ? n0 + r : 0);
             qrow[r] = p.qa + ((size_t)e * NG * H + (vr[r] ? n0 + r : 0)) * GB;
-            srow[r] = p.sa + ri * NG; brow[r] = p.ba + ri * NG;
+            srow[r] = p.sa + ri * NS; brow[r] = p.ba + ri * NS;
         }
 
         for (int tt = 0; tt < cnt; tt += PT) {
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemv_kernel(GemvParams p) {
             for (int c = sub; c < NC; c += LG) {
                 uint4 raw[4];
                 float sc[4], bc[4];
-                const int g = (c * CK) / kGroup;
+                const int g = (c * CK) / p.gs;          // the chunk's scale group
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     raw[r] = vr[r] ? *reinterpret_cast<const uint4*>(qrow[r] + (size_t)c * 16 + (size_t)(c / BITS) * gskip)
@@ -429,6 +430,7 @@ static GemvParams base_params(const FfnArgs& a) {
     GemvParams p{};
     p.x = a.x; p.work = a.work; p.n_work = a.n_work; p.h = a.h; p.y = a.y;
     p.T = d.T; p.H = d.H; p.I = d.I; p.k = d.k; p.E = d.E;
+    p.gs = d.group_size;
     return p;
 }
 
@@ -442,6 +444,7 @@ static int launch_gateup_bits(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     constexpr int CK = 128 / BITS;
+    if (d.group_size < CK) return MOE_ERR_UNSUPPORTED;     // one scale per 16-byte chunk
     GemvParams p = base_params<BITS>(a);
     p.qa = a.w.q[0]; p.sa = a.w.scale[0]; p.ba = a.w.bias[0];
     p.qb = a.w.q[1]; p.sb = a.w.scale[1]; p.bb = a.w.bias[1];
@@ -464,6 +467,7 @@ static int launch_down_bits(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     constexpr int CK = 128 / BITS;
+    if (d.group_size < CK) return MOE_ERR_UNSUPPORTED;     // one scale per 16-byte chunk
     GemvParams p = base_params<BITS>(a);
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
     const int NC = d.I / CK;
@@ -494,7 +498,22 @@ size_t gemv_workspace_bytes(const moe_dims& d) {
 int resolve_algo(const moe_dims& d, int bits, int algo) {
     if (algo != MOE_ALGO_AUTO) return algo;
     const long P = (long)d.T * d.k;
+    if (d.group_size < kGroup && !(dec_gateup_fits(d) && dec_down_fits(d)))
+        return MOE_ALGO_GEMV;                  // finer groups beyond the decode tiles: the vector-ALU path
     return (gemm_supported(d, bits) && P >= 64L * d.E) ? MOE_ALGO_GEMM : MOE_ALGO_MFMA;
+}
+
+// Groups of 64 or 32: the decode kernels take them (matrix cores, tiles that
+// fit LDS), and the vector-ALU kernels where one scale covers a 16-byte chunk
+// of codes (32 codes at 4 bits, 64 at 2 bits); the persistent, streaming and
+// grouped-GEMM kernels take groups of 128 only.
+bool ffn_group_supported(const moe_dims& d, int bits, int algo) {
+    if (d.group_size == kGroup) return true;
+    switch (resolve_algo(d, bits, algo)) {
+        case MOE_ALGO_GEMV: return d.group_size >= 128 / bits;
+        case MOE_ALGO_GEMM: return false;
+        default: return dec_gateup_fits(d) && dec_down_fits(d);
+    }
 }
 
 size_t ffn_workspace_bytes(const moe_dims& d, int bits, int algo) {

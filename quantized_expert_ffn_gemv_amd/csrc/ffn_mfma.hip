@@ -596,6 +596,7 @@ int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     if (d.T * d.k == 0) return MOE_OK;
     // shapes whose activation tile fits in LDS take the staged-tile kernel
     if (dec_gateup_fits(d)) return launch_gateup_dec(a, s);
+    if (d.group_size != kGroup) return MOE_ERR_UNSUPPORTED;     // one scale per 128 codes here
     MfmaParams p = mfma_params(a);
     p.qa = a.w.q[0]; p.sa = a.w.scale[0]; p.ba = a.w.bias[0];
     p.qb = a.w.q[1]; p.sb = a.w.scale[1]; p.bb = a.w.bias[1];
@@ -621,6 +622,7 @@ int launch_down_mfma(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     if (dec_down_fits(d)) return launch_down_dec(a, s);
+    if (d.group_size != kGroup) return MOE_ERR_UNSUPPORTED;     // one scale per 128 codes here
     {
         const int st = launch_down_stream(a, s);        // h through LDS in chunks of K
         if (st != MOE_ERR_UNSUPPORTED) return st;

@@ -231,7 +231,7 @@ int launch_expert_copy(const moe_dims& d, int bits, const moe_qweights& src, con
     for (int m = 0; m < 3; ++m) {
         const size_t N = m < 2 ? d.I : d.H, K = m < 2 ? d.H : d.I;
         a.bytes[3 * m] = N * K * bits / 8;
-        a.bytes[3 * m + 1] = a.bytes[3 * m + 2] = N * (K / kGroup) * 2;
+        a.bytes[3 * m + 1] = a.bytes[3 * m + 2] = N * (K / d.group_size) * 2;
         a.src[3 * m] = src.q[m];
         a.src[3 * m + 1] = reinterpret_cast<const uint8_t*>(src.scale[m]);
         a.src[3 * m + 2] = reinterpret_cast<const uint8_t*>(src.bias[m]);

@@ -77,8 +77,8 @@ def upload_layer(shape: mi.LayerShape, bits: int = 4, seed: int = 0) -> Layer:
     for m in mi.MATRICES:
         N, K = mi.matrix_dims(shape, m)
         q.append(torch.empty((shape.E, K // 128, N, 16 * bits), dtype=torch.uint8, device=DEV))
-        s.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device=DEV))
-        b.append(torch.empty((shape.E, N, K // 128), dtype=torch.int16, device=DEV))
+        s.append(torch.empty((shape.E, N, K // shape.group), dtype=torch.int16, device=DEV))
+        b.append(torch.empty((shape.E, N, K // shape.group), dtype=torch.int16, device=DEV))
     for e, mats in mi.iter_expert_weights(shape, bits, seed):
         for i, m in enumerate(mi.MATRICES):
             qq, ss, bb = mats[m]
@@ -104,7 +104,7 @@ def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, tab
     """All stages on the GPU; returns host copies of every output."""
     sh = L.shape
     T = xb.shape[0]
-    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k)
+    d = moe.dims(T, sh.H, sh.I, sh.E, sh.k, sh.group)
     buf = moe.LayerBuffers.allocate(d, L.bits, algo)
     for name in ("logits", "topk_ids", "topk_w", "pair_slot", "miss", "counts", "offsets",
                  "sorted_pairs", "pair_to_row", "active", "work_list", "y_rows"):

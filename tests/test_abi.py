@@ -49,7 +49,8 @@ def test_library_exports_nothing_else_with_the_prefix():
     (4, 256, 200, 8, 2, 128, moe.ERR_UNSUPPORTED),      # I not a multiple of 128
     (4, 256, 256, 8, 9, 128, moe.ERR_UNSUPPORTED),      # k > E
     (4, 256, 256, 2000, 2, 128, moe.ERR_UNSUPPORTED),   # E too large
-    (4, 256, 256, 8, 2, 64, moe.ERR_UNSUPPORTED),       # group size
+    (4, 256, 256, 8, 2, 96, moe.ERR_UNSUPPORTED),       # group size (32, 64 or 128)
+    (4, 256, 256, 8, 2, 16, moe.ERR_UNSUPPORTED),
     (40000, 256, 256, 8, 2, 128, moe.ERR_UNSUPPORTED),  # T*k too large
     (4, 16384, 256, 8, 2, 128, moe.ERR_UNSUPPORTED),    # H too large
 ])
@@ -71,6 +72,28 @@ def test_workspace_size():
     assert moe.workspace_bytes(d, moe.OP_ROUTE, 4) == 0
     with pytest.raises(moe.MoeError):
         moe.workspace_bytes(d, moe.OP_FFN, 3)
+
+
+def test_group_sizes_by_path():
+    """Groups of 64 and 32: the decode kernels (tiles that fit LDS) and the
+    vector-ALU path where one scale covers a 16-byte chunk of codes; the
+    grouped GEMM and the kernels of larger shapes take groups of 128 only."""
+    L = moe.lib()
+    w = _qw()
+    small = moe.dims(8, 2048, 512, 256, 8, 64)               # decode tiles fit
+    for algo in (moe.ALGO_AUTO, moe.ALGO_MFMA, moe.ALGO_GEMV):
+        moe.workspace_bytes(small, moe.OP_FFN, 4, algo)
+    assert _ffn(small, algo=moe.ALGO_GEMM) == moe.ERR_UNSUPPORTED
+    assert "groups of 128" in moe.last_error()
+    g32 = moe.dims(8, 2048, 512, 256, 8, 32)
+    # 2-bit codes: 64 per 16-byte chunk, more than a group of 32
+    assert L.moe_expert_ffn_q2(ctypes.byref(g32), FAKE, FAKE, FAKE, ctypes.byref(w), FAKE, moe.ALGO_GEMV, FAKE,
+                               1 << 30, None) == moe.ERR_UNSUPPORTED
+    assert "groups of 32" in moe.last_error()
+    big = moe.dims(8, 5120, 8192, 64, 2, 64)                 # the down tile does not fit LDS
+    assert _ffn(big, algo=moe.ALGO_MFMA) == moe.ERR_UNSUPPORTED
+    assert _ffn(big, algo=moe.ALGO_AUTO, ws_bytes=1) == moe.ERR_WORKSPACE   # AUTO takes the vector-ALU path
+    assert moe.workspace_bytes(big, moe.OP_FFN, 4) == moe.workspace_bytes(big, moe.OP_FFN, 4, moe.ALGO_GEMV)
 
 
 def _qw(ptr=FAKE):

@@ -566,6 +566,35 @@ def measure_residency(ctx, steps, warmup, n_hot=24, n_warm=8, T=8, batches=64):
     return out_d
 
 
+def measure_stack(torch, mi, moe, shape, layers, T, steps, warmup):
+    """A decode step through the weight sets as a stack of layers (layer l's
+    output is layer l+1's input and residual), enqueued call by call and as one
+    HIP graph per token step (moe.stack_forward captured once, replayed)."""
+    d = moe.dims(T, shape.H, shape.I, shape.E, shape.k)
+    bits = layers[0]["w"].bits
+    bufs = [moe.LayerBuffers.allocate(d, bits) for _ in layers]
+    outs = [torch.empty((T, shape.H), dtype=torch.int16, device="cuda") for _ in layers]
+    x = torch.from_numpy(mi.make_activations(shape.H, T, seed=3000)[0].view("int16")).cuda()
+    sl = [moe.StackLayer(L["Wr"], L["bias"], L["w"], L["table"], shape.E) for L in layers]
+    run = lambda i: moe.stack_forward(bufs, x, sl, outs)
+    eager_ms = timed_loop(torch, run, steps, warmup)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(0)
+    torch.cuda.synchronize()
+    graph_ms = timed_loop(torch, lambda i: graph.replay(), steps, warmup)
+    for b in bufs:
+        if not b.counters_clean():
+            raise CounterFault("[bench] stack: counters not back to zero after the timed replays")
+    n = len(layers)
+    res = dict(layers=n, T=T, eager_us_per_token_step=round(eager_ms / steps * 1e3, 2),
+               graph_us_per_token_step=round(graph_ms / steps * 1e3, 2),
+               graph_us_per_layer=round(graph_ms / steps * 1e3 / n, 2),
+               graph_tokens_per_s=round(T / (graph_ms / steps / 1e3), 1))
+    del graph, bufs, outs
+    return res
+
+
 def measure_a3b_extras(ctx, steps, warmup):
     """The A3B-style T=32 step with an always-on shared expert (inside the routed
     FFN launch, sigmoid gate fused into the combine), on a speculative-verify
@@ -598,6 +627,10 @@ def measure_a3b_extras(ctx, steps, warmup):
     out["cold_ms_per_step"] = round(base_ms, 5)
     log(f"[bench] a3b T=32 extras: shared expert +{out['shared_expert']['added_us_per_step']} us/step; "
         f"spec verify {out['spec_verify']['tokens_per_s']:.0f} tokens/s; warm {out['warm_one_weight_set']['tokens_per_s']:.0f}")
+    out["stack"] = [measure_stack(torch, mi, moe, shape, layers, t, steps, warmup) for t in (1, 8)]
+    for s in out["stack"]:
+        log(f"[bench] a3b stack of {s['layers']} layers, T={s['T']}: {s['graph_us_per_token_step']} us per token step "
+            f"as one graph ({s['graph_us_per_layer']} us/layer), {s['eager_us_per_token_step']} us call by call")
     del base, sh, sv, warm, layers
     ctx["layers"].clear()
     torch.cuda.empty_cache()

@@ -366,14 +366,14 @@ def expert_copy(d: Dims, bits: int, src: "QWeights", dst: "QWeights", n_dst: int
                                  _ptr(copies), _ptr(n_copy), int(max_copies), _stream(stream)))
 
 
-from .layer import (LayerBuffers, ResidentExperts, SharedBuffers, SharedExpert, layer_forward,  # noqa: E402
-                    resident_layer_forward)  # (orchestration of the calls above)
+from .layer import (LayerBuffers, ResidentExperts, SharedBuffers, SharedExpert, StackLayer, layer_forward,  # noqa: E402
+                    resident_layer_forward, stack_forward)  # (orchestration of the calls above)
 
 __all__ = [
     "lib", "abi_version", "status_string", "last_error", "MoeError", "Dims", "dims", "QWeights",
     "workspace_bytes", "work_list_capacity", "WORK_TILE_ROWS", "WORK_ENTRY_INTS", "route_topk", "route_dispatch", "DISPATCH_SYNC_INTS", "FFN_SYNC_INTS",
     "topk_from_logits", "slot_lookup", "permute", "expert_ffn_q4",
     "expert_ffn_q2", "expert_gateup", "expert_down", "expert_ffn_fused", "expert_ffn_fused_shared", "expert_ffn_fused_noalloc", "NOALLOC_WORKSPACE_BYTES", "combine", "combine_shared", "zero_point_bias", "stream_read", "STREAM_SINK_INTS", "route_counts", "hot_set", "residency_plan",
-    "expert_copy", "RESIDENCY_LISTS", "ResidencyC", "LayerBuffers", "ResidentExperts", "resident_layer_forward", "SharedBuffers", "SharedExpert", "layer_forward", "EXPORTS",
+    "expert_copy", "RESIDENCY_LISTS", "ResidencyC", "LayerBuffers", "ResidentExperts", "resident_layer_forward", "SharedBuffers", "SharedExpert", "layer_forward", "StackLayer", "stack_forward", "EXPORTS",
     "group_major", "ALGO_AUTO", "ALGO_GEMV", "ALGO_MFMA", "ALGO_GEMM", "OP_ROUTE", "OP_LOOKUP", "OP_PERMUTE", "OP_FFN", "OP_COMBINE",
 ]

@@ -26,12 +26,16 @@ warm slots): the plan kernel after the routing picks warm slots for the
 misses, the copies run on a second stream while the FFN of the experts
 already resident runs, then the FFN of the rest and the combine.
 
+``StackLayer`` and ``stack_forward`` run a decode step through several
+layers back to back (each layer's output is the next one's input), the unit
+that is captured once in a HIP graph and replayed per token.
+
 This module only orders the calls; the arithmetic is in the HIP kernels.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Sequence
 
 import torch
 
@@ -193,6 +197,34 @@ def layer_forward(buf: LayerBuffers, x: torch.Tensor, w_router: torch.Tensor,
         ys, gate_out = sb.buf.y_rows, sb.gate_out
     combine_shared(d, buf.y_rows, buf.pair_to_row, buf.topk_w, ys, x, shared.gate_w, residual, out, gate_out,
                    stream)
+
+
+@dataclass
+class StackLayer:
+    """One layer of a stack: its router and expert weights."""
+    w_router: torch.Tensor
+    router_bias: Optional[torch.Tensor]
+    weights: QWeights
+    slot_of_expert: torch.Tensor
+    n_slots: int
+
+
+def stack_forward(bufs: Sequence[LayerBuffers], x: torch.Tensor, layers: Sequence[StackLayer],
+                  outs: Sequence[torch.Tensor], algo: int = ALGO_AUTO, stream=None) -> torch.Tensor:
+    """A decode step through a stack of MoE layers, back to back on one batch:
+    layer l takes h_l (h_0 = x) as its input and its residual and writes
+    h_(l+1) = h_l + MoE_l(h_l) to outs[l] ("Luce Spark" page, sec. 3: the
+    routed FFN of every layer in one graph per token).  Nothing here waits on
+    the host, so the whole stack can be captured in one HIP graph and replayed
+    once per token step.  Returns outs[-1]."""
+    if not (len(bufs) == len(layers) == len(outs)):
+        raise ValueError("one buffer set and one output per layer")
+    h = x
+    for buf, L, out in zip(bufs, layers, outs):
+        layer_forward(buf, h, L.w_router, L.router_bias, L.weights, L.slot_of_expert, L.n_slots, h, out,
+                      algo=algo, stream=stream)
+        h = out
+    return h
 
 
 @dataclass

@@ -115,7 +115,11 @@ def run_layer(L: Layer, xb: np.ndarray, res: np.ndarray, algo=moe.ALGO_AUTO, tab
     tab = L.table_d if table is None else to_dev(table)
     moe.layer_forward(buf, x_d, L.Wr_d, L.bias_d, L.weights_d, tab, sh.E, r_d, out_d, algo=algo, fused=fused)
     torch.cuda.synchronize()
-    P = T * sh.k
+    return host_outputs(buf, out_d, T * sh.k)
+
+
+def host_outputs(buf, out_d: torch.Tensor, P: int) -> Dict:
+    """Host copies of every output of a layer step (buffers `buf`, output out_d)."""
     return dict(
         logits=to_host(buf.logits), ids=to_host(buf.topk_ids), gates=to_host(buf.topk_w),
         pair_slot=to_host(buf.pair_slot)[:P], miss=to_host(buf.miss), n_miss=int(to_host(buf.n_miss)[0]),

@@ -555,7 +555,7 @@ __device__ bool ticket(int32_t* counter, int n, int* winner) {
     return *winner;
 }
 
-template <int EB, int NJ, int PER>
+template <int EB, int NJ, int PER, bool WIDE = false>
 __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __restrict__ x,
                                                               const float* __restrict__ w,
                                                               const float* __restrict__ bias,
@@ -565,6 +565,7 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     // activation registers would not fit the 1024-thread budget
     constexpr int TT = NJ >= 6 ? kRouteTG / 2 : kRouteTG;
     __shared__ float part[4][4][EB][TT];
+    __shared__ float partw[16][kRouteTG];
     __shared__ int ids_s[kDispatchMaxP];
     __shared__ int scratch[kPermWaves * kMaxE];
     __shared__ int offs[kMaxE];
@@ -578,8 +579,11 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const uint16_t* __
     int32_t* group_counter = sync + kSyncStride * (1 + tg);
 
     // 1. logits of this (expert block, token group)
-    router_block<EB, TT, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
-                                   part[sub], tid & 255);
+    if constexpr (WIDE)
+        router_block_wide<kRouteTG, NJ, true>(x, w, bias, logits, a.H, a.E, (int)blockIdx.x, tb, te, partw);
+    else
+        router_block<EB, TT, NJ, true>(x, w, bias, logits, a.H, a.E, ((int)blockIdx.x * 4 + sub) * EB, tb, te,
+                                       part[sub], tid & 255);
     if (!ticket(group_counter, (int)gridDim.x, &winner)) return;
     // the resident table, requested now, parked in `cnts` for the lookup
     const int tab_v = tid < a.E ? a.table[tid] : -1;
@@ -650,7 +654,17 @@ int launch_route_dispatch(const moe_dims& d, const uint16_t* x, const float* w, 
     if (!route_dispatch_fused(d)) return MOE_ERR_UNSUPPORTED;
     DispatchArgs a = args;
     a.T = d.T; a.H = d.H; a.E = d.E; a.k = d.k; a.P = d.T * d.k;
-    // one expert per 256-thread group; NJ 256-wide steps cover a quarter of H
+    // layers with at most 64 experts: one expert per workgroup (16 waves split K),
+    // else one expert per 256-thread group (NJ 256-wide steps cover a quarter of H)
+    if (d.E <= 64) {
+        const dim3 grid((unsigned)d.E, (unsigned)((d.T + kRouteTG - 1) / kRouteTG));
+        const int njw = (d.H / 16 + 255) / 256;
+        if (njw <= 1)
+            hipLaunchKernelGGL((route_dispatch_kernel<1, 1, 1, true>), grid, dim3(1024), 0, s, x, w, bias, logits, a, sync);
+        else
+            hipLaunchKernelGGL((route_dispatch_kernel<1, 2, 1, true>), grid, dim3(1024), 0, s, x, w, bias, logits, a, sync);
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
     const int nj = (d.H / 4 + 255) / 256;
     switch (nj) {
         case 1: rd_go<1, 1>(d, x, w, bias, logits, a, sync, s); break;

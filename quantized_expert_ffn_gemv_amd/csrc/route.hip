@@ -19,6 +19,18 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
     router_block<EB, TT, NJ>(x, w, bias, logits, H, E, (int)blockIdx.x * EB, 0, T, part, threadIdx.x);
 }
 
+// Layers with at most 64 experts: one 1024-thread workgroup per expert, its 16
+// waves splitting K (the same sums, in the same order, as the one-launch
+// routing's router phase at these sizes).
+template <int NJ>
+__global__ __launch_bounds__(1024) void router_gemv_wide_kernel(const uint16_t* __restrict__ x,
+                                                                const float* __restrict__ w,
+                                                                const float* __restrict__ bias,
+                                                                float* __restrict__ logits, int T, int H, int E) {
+    __shared__ float part[16][8];
+    router_block_wide<8, NJ>(x, w, bias, logits, H, E, (int)blockIdx.x, 0, T, part);
+}
+
 // ------------------------------------------------------------ router, large T
 // Prefill shapes: a 64x64 (tokens x experts) tile per 256-thread workgroup,
 // K staged through LDS 32 at a time, 4x4 outputs per thread, float32 FMA.
@@ -90,7 +102,12 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t* __res
 int launch_router_logits(const moe_dims& d, const uint16_t* x, const float* w, const float* bias,
                          float* logits, hipStream_t s) {
     if (d.T == 0) return MOE_OK;
-    if (d.T <= 64) {
+    if (d.T <= 64 && d.E <= 64) {
+        if ((d.H / 16 + 255) / 256 <= 1)
+            hipLaunchKernelGGL(router_gemv_wide_kernel<1>, dim3(d.E), dim3(1024), 0, s, x, w, bias, logits, d.T, d.H, d.E);
+        else
+            hipLaunchKernelGGL(router_gemv_wide_kernel<2>, dim3(d.E), dim3(1024), 0, s, x, w, bias, logits, d.T, d.H, d.E);
+    } else if (d.T <= 64) {
         // each lane covers NJ steps of 4 k within its wave's quarter of H
         const int nj = (d.H / 4 + 255) / 256;
         constexpr int EB = 4, TT = 8;

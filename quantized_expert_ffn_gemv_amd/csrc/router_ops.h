@@ -89,4 +89,64 @@ __device__ __forceinline__ void router_block(const uint16_t* __restrict__ x, con
     }
 }
 
+// The whole 1024-thread workgroup on one expert e0 (layers with few experts,
+// where one expert per 256-thread group would leave most of the chip idle):
+// its 16 waves split K into 16 parts, each lane covering 4 consecutive k per
+// 256-wide step (NJ steps); partial sums are reduced across the wave with
+// xor shuffles and across the 16 waves through `part` in a fixed order.  The
+// same loads-first structure as router_block; contains __syncthreads().
+template <int TT, int NJ, bool COHERENT = false>
+__device__ __forceinline__ void router_block_wide(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                  const float* __restrict__ bias, float* __restrict__ logits,
+                                                  int H, int E, int e0, int tb, int te, float (*part)[TT]) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int kp = H / 16;                       // this wave's part of K
+    const int kbase = wv * kp + lane * 4;
+    float4 wr[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const bool ok = (e0 < E) && (lane * 4 + 256 * j < kp);
+        wr[j] = ok ? *reinterpret_cast<const float4*>(w + (size_t)e0 * H + kbase + 256 * j)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int t0 = tb; t0 < te; t0 += TT) {
+        uint2 xv[TT][NJ];
+#pragma unroll
+        for (int b = 0; b < TT; ++b)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool ok = (t0 + b < te) && (lane * 4 + 256 * j < kp);
+                xv[b][j] = ok ? *reinterpret_cast<const uint2*>(x + (size_t)(t0 + b) * H + kbase + 256 * j)
+                              : make_uint2(0, 0);
+            }
+        float acc[TT];
+#pragma unroll
+        for (int b = 0; b < TT; ++b) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                s = fmaf(bf16_bits_to_f32(xv[b][j].x & 0xFFFFu), wr[j].x, s);
+                s = fmaf(bf16_bits_to_f32(xv[b][j].x >> 16), wr[j].y, s);
+                s = fmaf(bf16_bits_to_f32(xv[b][j].y & 0xFFFFu), wr[j].z, s);
+                s = fmaf(bf16_bits_to_f32(xv[b][j].y >> 16), wr[j].w, s);
+            }
+            acc[b] = s;
+        }
+        const float tot = wave_transpose_sum<TT>(acc);
+        const int idx = wave_transpose_index<TT>(lane);
+        if ((lane & ((64 / TT) - 1)) == 0) part[wv][idx] = tot;
+        __syncthreads();
+        if (tid < TT && e0 < E && t0 + tid < te) {
+            float v = 0.f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v += part[q][tid];
+            const float out = v + (bias ? bias[e0] : 0.f);
+            float* dst = logits + (size_t)(t0 + tid) * E + e0;
+            if constexpr (COHERENT) __hip_atomic_store(dst, out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = out;
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace moe

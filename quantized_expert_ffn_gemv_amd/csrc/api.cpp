@@ -69,7 +69,8 @@ int check_ffn_args(const char* fn, const moe_dims* d, int bits, const int32_t* w
         return fail(MOE_ERR_UNSUPPORTED, "%s: unknown algo %d", fn, algo);
     if (algo == MOE_ALGO_GEMM && !moe::gemm_supported(*d, bits))
         return fail(MOE_ERR_UNSUPPORTED,
-                    "%s: the grouped GEMM needs 4-bit codes, groups of 128 and H, I multiples of 128, at least 256", fn);
+                    "%s: the grouped GEMM needs 4-bit codes, groups of 32, 64 or 128 and H, I multiples of 128, at "
+                    "least 256", fn);
     if (!moe::ffn_group_supported(*d, bits, algo))
         return fail(MOE_ERR_UNSUPPORTED,
                     "%s: groups of %d need the decode kernels (tiles that fit LDS) or, for groups of at least one "

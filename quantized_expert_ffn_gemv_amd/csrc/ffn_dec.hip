@@ -33,7 +33,6 @@ namespace {
 // Largest LDS a decode item may take (two workgroups per CU at 160 KB, with
 // room for the rest); bigger shapes use the kernels of ffn_mfma.hip.
 constexpr size_t kDecLdsLimit = 80 * 1024;
-constexpr int kDma = 1024;          // bytes one wave moves with one direct-to-LDS load
 
 // One-launch FFN (ffn_fused_dec_kernel): work-list entries per chunk of the
 // grid, the per-entry counters in `sync` (one 128-byte line each), the
@@ -67,54 +66,6 @@ struct DecParams {
 };
 
 __host__ __device__ constexpr size_t round_dma(size_t b) { return (b + kDma - 1) / kDma * kDma; }
-
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-// One direct-to-LDS load of the wave: lane l copies 16 bytes from `src` to
-// lds_base + 16 l (lds_base must be the same in every lane).  Written as
-// inline assembly so that the compiler does not track it: its own tracking
-// waits for every outstanding load (the code ring too) before the first LDS
-// access after it; completion is waited for explicitly with wait_vmem.
-// M0 holds the LDS address; one wait state between writing M0 and the load.
-// COH: a device-scope load (sc1), for data that other workgroups of the same
-// launch wrote with device-scope stores.
-template <bool COH = false>
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-    const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)lds_base;
-    if constexpr (COH)
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src), "{m0}"(lds) : "memory");
-    else
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
-}
-
-// Copy `bytes` (a multiple of 16) of contiguous global memory to LDS, waves
-// taking 1 KB pieces in turn; lanes past the end reload the last 16 bytes into
-// the padding (the LDS region is rounded up to a whole piece).
-__device__ __forceinline__ void dma_copy(const uint8_t* src, uint8_t* dst, int bytes, int wid, int lane) {
-    const int pieces = (bytes + kDma - 1) / kDma;
-    for (int i = wid; i < pieces; i += 4) {
-        const int off = i * kDma + 16 * lane;
-        dma16(src + (off < bytes ? off : bytes - 16), dst + i * kDma);
-    }
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt off).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier that orders LDS only: global loads stay in flight (a plain
-// __syncthreads() waits for every outstanding load, the code ring included).
-// Direct-to-LDS data must be waited for with wait_vmem first.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Item of a decode launch: work-list entry and row block of blockIdx.x; the
 // entry's expert, first sorted row, row count (n = 0: nothing to do) and the
@@ -233,34 +184,6 @@ constexpr uint32_t kOnesBf16 = 0x3F803F80u;   // two bf16 ones
 // code loads.  LDS: the x tile [rows_cap][H] bf16, then the raw fp16 scales
 // and biases of the block's gate and up rows, [RI][NG] each; after the loop
 // the first 8 KB holds the partial sums over K.
-// Groups of 64 or 32 (SPG = 2 or 4 scale groups per 128 codes).  In the
-// natural operand order, lane quarter q holds the 32 codes k = 32 q .. +31
-// of a 128-code run and MFMA step st takes 8 of them from every quarter, so a
-// step mixes all four quarters.  For finer groups the roles of q and st are
-// swapped: lane quarter q at step st supplies what quarter st supplies at step
-// q in the natural order (codes: one 32-bit word per step, from quarter st's
-// bytes; activations: chunk 4 st + q of the pair-ordered row instead of
-// 4 q + st), so step st covers exactly quarter st, i.e. k = 32 st .. +31, and
-// a group of 32 is one step, a group of 64 two.  The products and their pair
-// order are unchanged; only which step carries them moves.
-// Byte offset of the word lane quarter q loads for step st, within a row's
-// run of 128 codes.
-template <int BITS>
-__device__ __forceinline__ int tr_word_offset(int st, int q) {
-    return BITS == 4 ? 16 * st + 4 * q : 8 * st + 4 * (q >> 1);
-}
-
-// B operand of step st in the swapped order from the step's word w[st].
-template <int BITS>
-__device__ __forceinline__ void code_operand_tr(const uint32_t* w, int st, int q, uint32_t (&out)[4]) {
-    if constexpr (BITS == 4) {
-        code_operand<4>(w, st, out);
-    } else {
-        const uint32_t v[2] = {w[st] >> (8 * (q & 1)), 0u};   // 2-bit: quarter st's half word for step q
-        code_operand<2>(v, 0, out);
-    }
-}
-
 // COH: h leaves through device-scope stores (read by down items of the same
 // launch) and without the 16-row partial sums (only the non-staged down
 // kernel reads those).

@@ -494,24 +494,27 @@ size_t gemv_workspace_bytes(const moe_dims& d) {
 // MOE_ALGO_AUTO -> the matrix-core path (its cost per weight does not grow with
 // the tokens an expert serves); explicit choices are kept.
 // AUTO: the grouped GEMM once experts average at least 64 tokens (a weight
-// tile then meets a full 64-token item), else the per-tile matrix-core path.
+// tile then meets most of a 128-token item), else the per-tile matrix-core
+// path; groups of 64 or 32 whose decode tiles do not fit LDS take the
+// vector-ALU path.
 int resolve_algo(const moe_dims& d, int bits, int algo) {
     if (algo != MOE_ALGO_AUTO) return algo;
     const long P = (long)d.T * d.k;
+    if (gemm_supported(d, bits) && P >= 64L * d.E) return MOE_ALGO_GEMM;
     if (d.group_size < kGroup && !(dec_gateup_fits(d) && dec_down_fits(d)))
-        return MOE_ALGO_GEMV;                  // finer groups beyond the decode tiles: the vector-ALU path
-    return (gemm_supported(d, bits) && P >= 64L * d.E) ? MOE_ALGO_GEMM : MOE_ALGO_MFMA;
+        return MOE_ALGO_GEMV;
+    return MOE_ALGO_MFMA;
 }
 
 // Groups of 64 or 32: the decode kernels take them (matrix cores, tiles that
-// fit LDS), and the vector-ALU kernels where one scale covers a 16-byte chunk
-// of codes (32 codes at 4 bits, 64 at 2 bits); the persistent, streaming and
-// grouped-GEMM kernels take groups of 128 only.
+// fit LDS), the grouped GEMM, and the vector-ALU kernels where one scale covers
+// a 16-byte chunk of codes (32 codes at 4 bits, 64 at 2 bits); the persistent
+// and streaming kernels take groups of 128 only.
 bool ffn_group_supported(const moe_dims& d, int bits, int algo) {
     if (d.group_size == kGroup) return true;
     switch (resolve_algo(d, bits, algo)) {
         case MOE_ALGO_GEMV: return d.group_size >= 128 / bits;
-        case MOE_ALGO_GEMM: return false;
+        case MOE_ALGO_GEMM: return gemm_supported(d, bits);
         default: return dec_gateup_fits(d) && dec_down_fits(d);
     }
 }

@@ -103,4 +103,84 @@ __device__ __forceinline__ int pair_order_row(int m) {
     else return (m >> 1) + 8 * (m & 1);                                           // 0,8,1,9,...,7,15
 }
 
+// ------------------------------------------------- direct-to-LDS staging
+
+constexpr int kDma = 1024;          // bytes one wave moves with one direct-to-LDS load
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// One direct-to-LDS load of the wave: lane l copies 16 bytes from `src` to
+// lds_base + 16 l (lds_base must be the same in every lane).  Written as
+// inline assembly so that the compiler does not track it: its own tracking
+// waits for every outstanding load (the code ring too) before the first LDS
+// access after it; completion is waited for explicitly with wait_vmem.
+// M0 holds the LDS address; one wait state between writing M0 and the load.
+// COH: a device-scope load (sc1), for data that other workgroups of the same
+// launch wrote with device-scope stores.
+template <bool COH = false>
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)lds_base;
+    if constexpr (COH)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" : : "v"(src), "{m0}"(lds) : "memory");
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Copy `bytes` (a multiple of 16) of contiguous global memory to LDS, waves
+// taking 1 KB pieces in turn; lanes past the end reload the last 16 bytes into
+// the padding (the LDS region is rounded up to a whole piece).
+__device__ __forceinline__ void dma_copy(const uint8_t* src, uint8_t* dst, int bytes, int wid, int lane) {
+    const int pieces = (bytes + kDma - 1) / kDma;
+    for (int i = wid; i < pieces; i += 4) {
+        const int off = i * kDma + 16 * lane;
+        dma16(src + (off < bytes ? off : bytes - 16), dst + i * kDma);
+    }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt off).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS only: global loads stay in flight (a plain
+// __syncthreads() waits for every outstanding load, the code ring included).
+// Direct-to-LDS data must be waited for with wait_vmem first.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Groups of 64 or 32 (SPG = 2 or 4 scale groups per 128 codes).  In the
+// natural operand order, lane quarter q holds the 32 codes k = 32 q .. +31
+// of a 128-code run and MFMA step st takes 8 of them from every quarter, so a
+// step mixes all four quarters.  For finer groups the roles of q and st are
+// swapped: lane quarter q at step st supplies what quarter st supplies at step
+// q in the natural order (codes: one 32-bit word per step, from quarter st's
+// bytes; activations: chunk 4 st + q of the pair-ordered row instead of
+// 4 q + st), so step st covers exactly quarter st, i.e. k = 32 st .. +31, and
+// a group of 32 is one step, a group of 64 two.  The products and their pair
+// order are unchanged; only which step carries them moves.
+// Byte offset of the word lane quarter q loads for step st, within a row's
+// run of 128 codes.
+template <int BITS>
+__device__ __forceinline__ int tr_word_offset(int st, int q) {
+    return BITS == 4 ? 16 * st + 4 * q : 8 * st + 4 * (q >> 1);
+}
+
+// B operand of step st in the swapped order from the step's word w[st].
+template <int BITS>
+__device__ __forceinline__ void code_operand_tr(const uint32_t* w, int st, int q, uint32_t (&out)[4]) {
+    if constexpr (BITS == 4) {
+        code_operand<4>(w, st, out);
+    } else {
+        const uint32_t v[2] = {w[st] >> (8 * (q & 1)), 0u};   // 2-bit: quarter st's half word for step q
+        code_operand<2>(v, 0, out);
+    }
+}
+
 }  // namespace moe

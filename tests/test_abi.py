@@ -75,16 +75,22 @@ def test_workspace_size():
 
 
 def test_group_sizes_by_path():
-    """Groups of 64 and 32: the decode kernels (tiles that fit LDS) and the
-    vector-ALU path where one scale covers a 16-byte chunk of codes; the
-    grouped GEMM and the kernels of larger shapes take groups of 128 only."""
+    """Groups of 64 and 32: the decode kernels (tiles that fit LDS), the
+    grouped GEMM (4-bit codes), and the vector-ALU path where one scale covers
+    a 16-byte chunk of codes; the persistent and streaming kernels of larger
+    shapes take groups of 128 only."""
     L = moe.lib()
     w = _qw()
     small = moe.dims(8, 2048, 512, 256, 8, 64)               # decode tiles fit
-    for algo in (moe.ALGO_AUTO, moe.ALGO_MFMA, moe.ALGO_GEMV):
+    for algo in (moe.ALGO_AUTO, moe.ALGO_MFMA, moe.ALGO_GEMV, moe.ALGO_GEMM):
         moe.workspace_bytes(small, moe.OP_FFN, 4, algo)
-    assert _ffn(small, algo=moe.ALGO_GEMM) == moe.ERR_UNSUPPORTED
-    assert "groups of 128" in moe.last_error()
+    # the grouped GEMM takes the finer group; the check stops at the workspace
+    assert _ffn(small, algo=moe.ALGO_GEMM, ws_bytes=1) == moe.ERR_WORKSPACE
+    # its per-group activation sums grow with the group count
+    g128 = moe.dims(8, 2048, 512, 256, 8)
+    assert moe.workspace_bytes(small, moe.OP_FFN, 4, moe.ALGO_GEMM) > moe.workspace_bytes(g128, moe.OP_FFN, 4, moe.ALGO_GEMM)
+    prefill64 = moe.dims(4096, 2048, 768, 128, 8, 64)        # 256 pairs per expert: AUTO takes the GEMM
+    assert moe.workspace_bytes(prefill64, moe.OP_FFN, 4) == moe.workspace_bytes(prefill64, moe.OP_FFN, 4, moe.ALGO_GEMM)
     g32 = moe.dims(8, 2048, 512, 256, 8, 32)
     # 2-bit codes: 64 per 16-byte chunk, more than a group of 32
     assert L.moe_expert_ffn_q2(ctypes.byref(g32), FAKE, FAKE, FAKE, ctypes.byref(w), FAKE, moe.ALGO_GEMV, FAKE,

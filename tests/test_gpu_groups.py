@@ -83,3 +83,25 @@ def test_large_tiles_take_the_vector_alu_path():
     with pytest.raises(moe.MoeError) as ex:
         run_layer(L, xb, res, algo=moe.ALGO_MFMA, fused=False)
     assert ex.value.status == moe.ERR_UNSUPPORTED
+
+
+# Grouped GEMM at groups of 64 and 32: token counts that make AUTO take it
+# (at least 64 pairs per expert), items with fewer than 8 (gate/up) or 4 (down)
+# tiles, row blocks past I and H (I = 384, H = 640), every FFN row checked.
+GEMM_GROUPS = [
+    (mi.LayerShape("gemm_g64a", H=256, E=4, k=2, I=256, tokens=(200,), bits=(4,), zipf_s=None, n_resident=2, group=64),
+     200),
+    (mi.LayerShape("gemm_g32a", H=256, E=4, k=2, I=256, tokens=(200,), bits=(4,), zipf_s=None, n_resident=2, group=32),
+     200),
+    (mi.LayerShape("gemm_g64b", H=1024, E=6, k=3, I=384, tokens=(130,), bits=(4,), zipf_s=0.8, n_resident=3, group=64),
+     130),
+    (mi.LayerShape("gemm_g32c", H=640, E=3, k=1, I=512, tokens=(197,), bits=(4,), zipf_s=None, n_resident=1,
+                   group=32), 197),
+]
+
+
+@pytest.mark.parametrize("shape,T", GEMM_GROUPS, ids=[s.name for s, _ in GEMM_GROUPS])
+def test_grouped_gemm_at_finer_groups(shape, T):
+    L = layer(shape, 4)
+    stages(L, T, seed=26, algo=moe.ALGO_GEMM, fused=False)
+    stages(L, T, seed=27, algo=moe.ALGO_AUTO, fused=True)

@@ -34,6 +34,10 @@ COMMON = [
 # VGPRs, which saves an accumulator-register read per result element.
 PER_FILE = {
     "ffn_dec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # The grouped GEMM runs one workgroup per CU (two waves per SIMD, its LDS
+    # ring takes most of the CU's LDS): schedule for latency, so each LDS
+    # operand read is issued ahead of the MFMAs that precede its use.
+    "ffn_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

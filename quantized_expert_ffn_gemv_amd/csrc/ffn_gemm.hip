@@ -1,7 +1,7 @@
 // Grouped GEMM on the matrix cores for experts that serve many tokens (prefill
 // and large batches): the same products as the decode kernels (exact code
-// operands, mfma_ops.h), tiled for reuse of each unpacked code across 128
-// tokens and of each staged activation across 256 weight rows.
+// operands, mfma_ops.h), on v_mfma_f32_32x32x16_bf16, which does twice the
+// work per cycle of the 16 x 16 x 32 form on gfx950.
 //
 // Why a separate path: the decode kernels give each 16-token work tile its own
 // pass over the expert's weights, which is right when a weight byte meets a
@@ -9,31 +9,29 @@
 // 2.3: a batch's tokens share an expert) the contraction is dense and the
 // matrix cores should set the pace, so
 //   * a gate/up item is 128 token rows (8 consecutive work-list tiles of one
-//     expert) times 256 intermediate rows of gate and of up; each of the 8
-//     waves owns 32 of them (two 16-row tiles of gate and the same two of up,
-//     a 4 x 8 grid of 16 x 16 accumulator tiles), so one unpacked code
-//     operand feeds 8 MFMAs and one activation operand 4;
-//   * a down item is 64 token rows times 512 output rows, 64 per wave, with
-//     the three bf16 planes of h (4 x 4 tiles x 3 planes);
+//     expert) times 128 intermediate rows of gate and of up, on a workgroup of
+//     4 waves (two workgroups per CU); each wave owns 32 rows (a gate tile and
+//     an up tile of 32 x 32 accumulators for each 32 tokens);
+//   * a down item is 64 token rows times 512 output rows, on 8 waves of 64
+//     rows, with the three bf16 planes of h;
 //   * activations (x, pre-permuted into code pair order by gemm_xprep_kernel,
-//     or the h planes) and the codes of the item's rows go from L2/HBM
-//     straight into LDS ring slots with direct-to-LDS loads, one group of 128
-//     along K per slot, one group ahead, shared by the 8 waves;
-//   * workgroups take items in an order that keeps all row blocks of one token
-//     chunk on one XCD, so the chunk's activations are fetched into that XCD's
-//     L2 once.
+//     or the h planes), the codes of the item's rows and their scales go from
+//     L2/HBM straight into LDS ring slots with direct-to-LDS loads, half a
+//     group (64 along K) per slot, two slots ahead, shared by the waves;
+//   * workgroups take items in an order that keeps consecutive items (the
+//     row blocks of one token chunk, then the next chunk of the same expert)
+//     on one XCD, so their activations and codes meet in that XCD's L2.
 // The per-group fold uses a ratio chain instead of a separate accumulator per
 // group.  With t_j = s_j / L for scale group j of a weight row and
 // C_j = sum (128 + L q) x over the group (the matrix cores' sum),
 //     acc_j = acc_(j-1) * (t_(j-1) / t_j) + C_j,
 // so after the last group J, acc_J * t_J = sum_j t_j C_j.  The group sums of
 // the activations enter once per item: acc += (sum_j beta_j X_j) / t_J with
-// beta_j = b_j - (128 / L) s_j and X_j = sum x over the group, which is four
-// float32 MFMAs (16 x 16 x 4) per tile and 16 groups, and y = acc * t_J is
-// sum_j (s_j sum q x + b_j X_j) = sum (q s + b) x: the FMA form of the
-// Flash-MoE page, sec. 2, per group.  A zero scale is replaced by 2^-40 in the
-// ratios (its group's code part then adds 2^-43 C instead of 0), so that no
-// ratio divides by zero.
+// beta_j = b_j - (128 / L) s_j and X_j = sum x over the group, on float32
+// MFMAs (32 x 32 x 2), and y = acc * t_J is sum_j (s_j sum q x + b_j X_j) =
+// sum (q s + b) x: the FMA form of the Flash-MoE page, sec. 2, per group.  A
+// zero scale is replaced by 2^-40 in the ratios (its group's code part then
+// adds 2^-43 C instead of 0), so that no ratio divides by zero.
 // h leaves the gate/up kernel in three bf16 planes in code pair order plus
 // 16-row partial sums, as from every other gate/up kernel; the down kernel
 // multiplies all three planes (with two, h's 2^-18 relative error summed over
@@ -55,13 +53,8 @@ constexpr int kGuTiles = 8;                            // work-list tiles per ga
 constexpr int kDnTiles = 4;                            // per down item
 constexpr int kGuTok = kGuTiles * kWorkRows;           // token rows per gate/up item (128)
 constexpr int kDnTok = kDnTiles * kWorkRows;           // per down item (64)
-constexpr int kGuRows = 32 * kWaves;                   // intermediate rows per gate/up item (256)
 constexpr int kDnRows = 64 * kWaves;                   // output rows per down item (512)
 constexpr int kRowB = kGroup * 2;                      // one bf16 row of a 128-wide group in LDS
-constexpr int kGuSlot = kGuTok * kRowB;                // LDS ring slot of gate/up (32 KB)
-constexpr int kDnSlot = 3 * kDnTok * kRowB;            // of down: three planes (48 KB)
-constexpr int kGuStage = kGuSlot / kDma / kWaves;      // direct-to-LDS loads per wave and group (4)
-constexpr int kDnStage = kDnSlot / kDma / kWaves;      // (6)
 constexpr float kTinyScale = 0x1p-40f;
 
 struct GemmParams {
@@ -106,6 +99,19 @@ __device__ __forceinline__ void row16_stage(float (&v)[N], int lane) {
 __device__ __forceinline__ float ring_scale(const uint32_t* w, int j) {
     const float s = f16_bits_to_f32((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
     return s == 0.f ? kTinyScale : s;
+}
+
+// h = hi + mid + lo exactly, each part the top 16 bits of what is left (a
+// float32 significand has 24 bits: 8 per part).
+__device__ __forceinline__ void split3_trunc(float h, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+#pragma clang fp contract(off)
+    const uint32_t u = __float_as_uint(h);
+    const float r1 = h - __uint_as_float(u & 0xFFFF0000u);
+    const uint32_t v = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(v & 0xFFFF0000u);
+    hi = u >> 16;
+    mid = v >> 16;
+    lo = __float_as_uint(r2) >> 16;
 }
 
 // Items of a launch in XCD order: slot s (workgroup b takes slots b, b + G,
@@ -238,19 +244,27 @@ __global__ __launch_bounds__(256) void gemm_xprep_kernel(const uint16_t* __restr
 // & 3) so that 16 consecutive rows read at one piece hit 16 bank groups.
 __device__ __forceinline__ int code_lds_offset(int r, int piece) { return r * 64 + 16 * (piece ^ ((r >> 2) & 3)); }
 
-// Stage one ring slot of codes: `rows` contiguous rows of 64 bytes from `src`
-// (rows at or past `valid` re-read row valid - 1), pieces of 1 KB (16 rows)
-// ii = NPW w + j of wave w.
+// Codes of one ring slot: contiguous rows of 64 bytes from a block's first
+// row, pieces of 1 KB (16 rows) ii = NPW w + j of wave w.  The lane offsets
+// are fixed per item (rows at or past `valid` re-read row valid - 1); the
+// block's base moves along K.
 template <int NPW>
-__device__ __forceinline__ void stage_codes(const uint8_t* src, int valid, uint8_t* dst, int wu, int lane) {
+struct CodeStage {
+    uint32_t off[NPW];
+    __device__ __forceinline__ void init(int valid, int wu, int lane) {
 #pragma unroll
-    for (int j = 0; j < NPW; ++j) {
-        const int ii = NPW * wu + j;
-        const int rr = 16 * ii + (lane >> 2), pp = lane & 3;
-        const int rc = rr < valid ? rr : valid - 1;
-        dma16(src + (size_t)rc * 64 + 16 * (pp ^ ((rr >> 2) & 3)), dst + ii * kDma);
+        for (int j = 0; j < NPW; ++j) {
+            const int ii = NPW * wu + j;
+            const int rr = 16 * ii + (lane >> 2), pp = lane & 3;
+            const int rc = rr < valid ? rr : valid - 1;
+            off[j] = (uint32_t)rc * 64u + 16u * (uint32_t)(pp ^ ((rr >> 2) & 3));
+        }
     }
-}
+    __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* dst, int wu) const {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) dma16_sv(base, off[j], dst + (NPW * wu + j) * kDma);
+    }
+};
 
 // The code word of one weight tile for MFMA step st (natural order: word st of
 // the lane's piece q; swapped order: word q of quarter st's piece).
@@ -290,38 +304,72 @@ __device__ __forceinline__ void tile_rows(const GemmParams& p, int h0, int jt, i
 }
 
 // -------------------------------------------------------------- gate/up
-// Item = (head of 8 tiles, block of 256 intermediate rows).  Wave w: gate and
-// up rows blk*256 + 32 w + 16 hf + (pair order of m), hf = 0, 1; weight tiles
-// wt = 0, 1 gate (hf), 2, 3 up (hf); token tiles tk = 0..7 (rows 16 tk ..).
-// Per group g of 128 along H: activation slot g % 2 holds the 128 x rows of
-// the group (wave w stages tile w), code slot g % 2 the codes of the 256 gate
-// and 256 up rows, both staged one group ahead, and registers the wave's
-// scales of the next group.
-// SPG scale groups per 128 (1, 2 or 4): for SPG > 1 the steps carry one
-// quarter of the run each (tr_word_offset), and the ratio chain advances at
-// each scale group.
-constexpr int kGuActRing = 2, kGuCodeRing = 2;
-constexpr int kGuCodeSlot = 2 * kGuRows * 64;          // 32 KB
-constexpr int kGuCodeStage = kGuCodeSlot / kDma / kWaves;   // 4
-constexpr size_t kGuLds = (size_t)kGuActRing * kGuSlot + (size_t)kGuCodeRing * kGuCodeSlot;   // 128 KB
+// On v_mfma_f32_32x32x16_bf16 (lane layout: A lane l holds row l % 32 and
+// k = 8 (l / 32) + i; B column l % 32, the same k; accumulator element 4 j + i
+// is row 8 j + 4 (l / 32) + i of column l % 32).  Activations are A (rows =
+// tokens), codes B (columns = weight rows), so a lane's accumulators belong
+// to one weight row and one scale.
+// Item = (head of 8 tiles = 128 token rows, block of 256 intermediate rows).
+// Wave w: gate and up rows blk*256 + 32 w + (pair order of n), n = lane % 32,
+// weight tiles wt = 0 (gate) and 1 (up); token tiles tk = 0..NT-1 of 32 rows.
+// The pipeline unit is half a group: unit u = (g, f) covers K 128 g + 64 f ..
+// + 63, four MFMA steps of 16.  Step s (0..3) of a unit takes from lane half
+// h = lane / 32 the 8 codes (and the 8 pair-ordered activations) of chunk
+//     c(s, h) = (s / S) 2 S + h S + s % S   (S = 4 for groups of 128 and 64, 2 for 32)
+// of the unit's 8 chunks, so a step stays inside one scale group and a lane's
+// code words of a unit are contiguous in the row.
+// Two workgroups of 4 waves per CU (80 KB of LDS each), so that one
+// workgroup's barriers, prologue and epilogue overlap the other's MFMAs.
+// LDS: three unit slots (the 128 x rows, 128 bytes each; 32 bytes of codes of
+// each of the 128 gate and 128 up rows) and two scale slots (each row's
+// 16-byte aligned run of scales holding group g's).  Units are staged two
+// ahead, scales with the first half of their group; every load of the main
+// loop goes straight to LDS and is waited for by count.
+constexpr int kGuWarps = 4;                                      // waves per gate/up workgroup
+constexpr int kGuThreads = kGuWarps * kWave;
+constexpr int kGuWaveRows = 32;                                  // gate (and up) rows per wave
+constexpr int kGuRows = kGuWaveRows * kGuWarps;                  // 128 per item
+constexpr int kUnitRowB = 128;                                   // bytes of one x row per unit
+constexpr int kGuActUnit = kGuTok * kUnitRowB;                   // 16 KB
+constexpr int kGuCodeUnit = 2 * kGuRows * 32;                    // 8 KB
+constexpr int kGuUnitB = kGuActUnit + kGuCodeUnit;               // 24 KB
+constexpr int kGuUnits = 3;
+constexpr int kGuScaleSlot = 2 * kGuRows * 16;                   // 4 KB
+constexpr int kGuScaleSlots = 2;
+constexpr size_t kGuLds = (size_t)kGuUnits * kGuUnitB + (size_t)kGuScaleSlots * kGuScaleSlot;   // 80 KB
+constexpr int kGuActDma = kGuActUnit / kDma / kGuWarps;          // 4 per wave
+constexpr int kGuCodeDma = kGuCodeUnit / kDma / kGuWarps;        // 2 per wave
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ floatx16_t mfma32(const uint32_t (&a)[4], const uint32_t (&b)[4], floatx16_t c) {
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a);
+    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, b);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, c, 0, 0, 0);
+}
+
+// Weight row held by column n (0..31) of a 32-row tile: pair order within each
+// run of 8 (0,4,1,5,2,6,3,7), so that h stored at column n lands in the pair
+// order of the down kernels' operands.
+__device__ __forceinline__ int pair_order_row32(int n) { return 8 * (n >> 3) + ((n & 7) >> 1) + 4 * (n & 1); }
+
+// A unit's codes of one row: 32 bytes (two 16-byte pieces) at r * 32, the
+// pieces swapped on every fourth row pair so that 8 consecutive lanes reading
+// one piece of 8 rows (4 distinct 32-byte rows mod 128 bytes) hit all banks.
+__device__ __forceinline__ int unit_code_offset(int r, int piece) { return r * 32 + 16 * (piece ^ ((r >> 2) & 1)); }
 
 template <int SPG>
-__global__ __launch_bounds__(kThreads, 1) void ffn_gateup_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kGuThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gateup_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr bool TR = SPG > 1;
-    constexpr int SPS = 4 / SPG;                       // MFMA steps per scale group
-    constexpr int NSW = SPG > 2 ? 2 : 1;               // 32-bit scale words per weight row and group
-    uint8_t* const abuf = smem;
-    uint8_t* const cbuf = smem + kGuActRing * kGuSlot;
-    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
+    constexpr int S = SPG == 4 ? 2 : 4;                 // MFMA steps per scale group within a unit
+    constexpr int GPU = 4 / S;                          // scale groups per unit
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.H, I = p.I, NG = H / kGroup, NGS = p.NGS;
+    const int H = p.H, I = p.I, NG = H / kGroup, NGS = p.NGS, NU = 2 * NG;
     const int n_items = ld_scalar(p.n_heads, 0) * p.blocks;
     const int per = (n_items + 7) >> 3;
-
-    int lrow[4];                                       // row within the block, per weight tile
-#pragma unroll
-    for (int wt = 0; wt < 4; ++wt) lrow[wt] = 32 * wu + 16 * (wt & 1) + pair_order_row<4>(m);
+    const int lrow = kGuWaveRows * wu + pair_order_row32(n);        // row within the block
+    uint8_t* const sbuf = smem + kGuUnits * kGuUnitB;
 
     for (int slot_i = blockIdx.x; slot_i < 8 * per; slot_i += gridDim.x) {
         const int item = xcd_item(slot_i, per);
@@ -329,271 +377,285 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gateup_gemm_kernel(GemmParams
         Meta<kGuTiles> mt;
         gemm_meta<kGuTiles>(p, item, mt);
         const int row_base = mt.blk * kGuRows;
-        const int valid = I - row_base < kGuRows ? I - row_base : kGuRows;   // rows of the block inside I
-        const bool rows_ok = 32 * wu < valid;          // waves past I stage and wait, nothing more
-        // activation staging: wave wu stages tile wu (rows 16 wu + 4 j + q)
-        uint32_t soff[kGuStage];
-        {
-            int r0, rn;
-            tile_rows(p, mt.h0, wu, r0, rn);
+        const int valid = I - row_base < kGuRows ? I - row_base : kGuRows;
+        const bool rows_ok = kGuWaveRows * wu < valid;     // waves past I stage and wait, nothing more
+        // activation staging: load j of wave w is 1 KB piece 4 w + j of the
+        // unit slot: token rows 32 w + 8 j + lane / 8 (work tile 2 w + j / 2),
+        // 16-byte position lane % 8, which holds chunk (lane % 8) ^ (row % 8)
+        uint32_t soff[kGuActDma];
 #pragma unroll
-            for (int j = 0; j < kGuStage; ++j) {
-                int tok = 0;
-                if (rn > 0) {
-                    const int sl = 4 * j + q;
-                    tok = p.work[(size_t)(mt.h0 + wu) * kWorkInts + 4 + (sl < rn ? sl : 0)];
-                    tok = (tok >= 0 && tok < p.T) ? tok : 0;
-                }
-                soff[j] = (uint32_t)tok * (uint32_t)(H * 2) + 16u * (uint32_t)(m ^ ((4 * j + q) & 15));
+        for (int j = 0; j < kGuActDma; ++j) {
+            int r0, rn;
+            tile_rows(p, mt.h0, 2 * wu + (j >> 1), r0, rn);
+            const int sl = 8 * (j & 1) + (lane >> 3);
+            int tok = 0;
+            if (rn > 0) {
+                tok = p.work[(size_t)(mt.h0 + 2 * wu + (j >> 1)) * kWorkInts + 4 + (sl < rn ? sl : 0)];
+                tok = (tok >= 0 && tok < p.T) ? tok : 0;
             }
+            soff[j] = (uint32_t)tok * (uint32_t)(H * 2) + 16u * (uint32_t)((lane & 7) ^ (sl & 7));
+        }
+        // code staging: load j of wave w is piece ii = 2 (w & 1) + j of the
+        // gate (w < 2) or up rows: rows 32 ii + lane / 2, piece lane % 2
+        uint32_t coff[kGuCodeDma];
+#pragma unroll
+        for (int j = 0; j < kGuCodeDma; ++j) {
+            const int rr = 32 * (kGuCodeDma * (wu & 1) + j) + (lane >> 1);
+            const int rc = rr < valid ? rr : valid - 1;
+            coff[j] = (uint32_t)rc * 64u + 16u * (uint32_t)((lane & 1) ^ ((rr >> 2) & 1));
         }
         const uint8_t* xbytes = reinterpret_cast<const uint8_t*>(p.xp);
-        auto stage_act = [&](int g) {
-            uint8_t* dst = abuf + (g % kGuActRing) * kGuSlot + (kGuStage * wu) * kDma;
+        const uint8_t* cmat = wu < 2 ? p.qa : p.qb;
+        // scales: waves 0-1 gate rows 64 (w & 1) + lane, waves 2-3 up rows
+        const int srow = 64 * (wu & 1) + lane;
+        const uint16_t* smat = wu < 2 ? p.sa : p.sb;
+        const size_t srow_g = (size_t)mt.e * I + row_base + (srow < valid ? srow : valid - 1);
+        // stage unit u (and, for the first half of a group, its scales)
+        auto stage = [&](int u) {
+            const int g = u >> 1, f = u & 1;
+            uint8_t* base = smem + (u % kGuUnits) * kGuUnitB;
 #pragma unroll
-            for (int j = 0; j < kGuStage; ++j) dma16(xbytes + soff[j] + (size_t)g * kRowB, dst + j * kDma);
-        };
-        // codes: waves 0-3 stage the gate rows, 4-7 the up rows
-        const uint8_t* cmat = wu < 4 ? p.qa : p.qb;
-        auto stage_cod = [&](int g) {
-            const uint8_t* src = cmat + (((size_t)mt.e * NG + g) * I + row_base) * 64;
-            stage_codes<kGuCodeStage>(src, valid, cbuf + (g % kGuCodeRing) * kGuCodeSlot + (wu >> 2) * (kGuCodeSlot / 2),
-                                          wu & 3, lane);
-        };
-        const int rows_c = rows_ok ? row_base : 0;     // idle waves load valid scales
-        uint32_t srn[4][NSW];                          // scales of the next group
-        auto load_sc = [&](int g) {
+            for (int j = 0; j < kGuActDma; ++j)
+                dma16_sv(xbytes + (size_t)g * kRowB + f * kUnitRowB, soff[j], base + (kGuActDma * wu + j) * kDma);
+            const uint8_t* cb = cmat + (((size_t)mt.e * NG + g) * I + row_base) * 64 + f * 32;
 #pragma unroll
-            for (int wt = 0; wt < 4; ++wt)
-                load_scales<SPG, NSW>((wt < 2 ? p.sa : p.sb) + ((size_t)mt.e * I + rows_c + lrow[wt]) * NGS + (size_t)g * SPG,
-                                      srn[wt]);
+            for (int j = 0; j < kGuCodeDma; ++j)
+                dma16_sv(cb, coff[j], base + kGuActUnit + (wu >> 1) * (kGuCodeUnit / 2) + (kGuCodeDma * (wu & 1) + j) * kDma);
+            if (f == 0) {
+                const size_t e_off = (srow_g * NGS + (size_t)g * SPG) * 2;
+                dma16(reinterpret_cast<const uint8_t*>(smat) + (e_off & ~(size_t)15),
+                      sbuf + (g % kGuScaleSlots) * kGuScaleSlot + wu * kDma);
+            }
+        };
+        const size_t lrow_g = (size_t)mt.e * I + row_base + (rows_ok ? lrow : 0);
+        auto scale_at = [&](int g, int j) {                // j: scale group within group g
+            const uint32_t k = (uint32_t)(lrow_g * NGS + (size_t)g * SPG + j) & 7u;
+            const uint8_t* sb = sbuf + (g % kGuScaleSlots) * kGuScaleSlot + lrow * 16 + 2 * k;
+            const float f0 = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb));
+            const float f1 = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sb + kGuScaleSlot / 2));
+            return float2{f0 == 0.f ? kTinyScale : f0, f1 == 0.f ? kTinyScale : f1};
         };
 
-        // Every ring is one group deep: at the top of iteration g all loads are
-        // waited for, the scales of g are taken out of the registers, and only
-        // then are the next group's scales, activations and codes issued.  (The
-        // direct-to-LDS loads are invisible to the compiler's load tracking, so
-        // a tracked scale load with direct-to-LDS loads behind it would make
-        // the compiler's own wait for it wait for those as well.)
-        load_sc(0);
-        stage_act(0);
-        stage_cod(0);
-        // the item's body for NT token tiles (8, or 4 when the item has at most
-        // 4 non-empty tiles)
+        stage(0);
+        stage(1);
         auto run = [&](auto ntc) {
             constexpr int NT = decltype(ntc)::value;
-            floatx4_t acc[4][NT];
+            floatx16_t acc[2][NT];
 #pragma unroll
-            for (int wt = 0; wt < 4; ++wt)
+            for (int wt = 0; wt < 2; ++wt)
 #pragma unroll
-                for (int tk = 0; tk < NT; ++tk) acc[wt][tk] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            float sprev[4] = {1.f, 1.f, 1.f, 1.f};
+                for (int tk = 0; tk < NT; ++tk)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[wt][tk][e] = 0.f;
+            float sprev[2] = {1.f, 1.f};
 
-            for (int g = 0; g < NG; ++g) {
-                wait_vmem<0>();
-                lds_barrier();
-                float scg[SPG][4];
-#pragma unroll
-                for (int j = 0; j < SPG; ++j)
-#pragma unroll
-                    for (int wt = 0; wt < 4; ++wt) {
-                        scg[j][wt] = ring_scale(srn[wt], j);
-                        asm volatile("" : : "v"(scg[j][wt]));   // taken before the next loads are issued
-                    }
-                if (g + 1 < NG) {
-                    load_sc(g + 1);
-                    stage_act(g + 1);
-                    stage_cod(g + 1);
+            for (int u = 0; u < NU; ++u) {
+                // unit u has landed: the loads after it are unit u + 1's (6 per
+                // wave, plus 1 when it starts a group)
+                if (u + 1 < NU) {
+                    if ((u & 1) != 0) wait_vmem<kGuActDma + kGuCodeDma + 1>();
+                    else wait_vmem<kGuActDma + kGuCodeDma>();
+                } else {
+                    wait_vmem<0>();
                 }
-                const uint8_t* buf = abuf + (g % kGuActRing) * kGuSlot;
-                const uint8_t* cslot = cbuf + (g % kGuCodeRing) * kGuCodeSlot;
+                lds_barrier();
+                if (u + 2 < NU) stage(u + 2);
+                const int g = u >> 1, f = u & 1;
+                const uint8_t* base = smem + (u % kGuUnits) * kGuUnitB;
                 if (rows_ok) {
-                    // Software pipeline: the activation operand of the next
-                    // token tile (or of tile 0 of the next step) is read while
-                    // the current tile's MFMAs run, and a step's code words
-                    // during the step before.
-                    auto lds_a = [&](int tk, int st) {
-                        const int c = TR ? 4 * st + q : 4 * q + st;
-                        return *reinterpret_cast<const uint4*>(buf + (16 * tk + m) * kRowB + 16 * (c ^ m));
-                    };
-                    auto code_w = [&](int wt, int st) {
-                        return read_code_word<TR>(cslot + (wt >> 1) * (kGuCodeSlot / 2), lrow[wt], q, st);
-                    };
-                    uint32_t cw[4];
+                    // this lane's 4 code words of the unit: words h S .. of each
+                    // scale group's 2 S words (S = 4: piece h; S = 2: half of
+                    // pieces 0 and 1)
+                    uint32_t cw[2][4];
 #pragma unroll
-                    for (int wt = 0; wt < 4; ++wt) cw[wt] = code_w(wt, 0);
-                    uint4 a_cur = lds_a(0, 0);
+                    for (int wt = 0; wt < 2; ++wt) {
+                        const uint8_t* cs = base + kGuActUnit + wt * (kGuCodeUnit / 2);
+                        if constexpr (S == 4) {
+                            const uint4 c = *reinterpret_cast<const uint4*>(cs + unit_code_offset(lrow, hh));
+                            cw[wt][0] = c.x; cw[wt][1] = c.y; cw[wt][2] = c.z; cw[wt][3] = c.w;
+                        } else {
 #pragma unroll
-                    for (int st = 0; st < 4; ++st) {
-                        if (st % SPS == 0) {
-                            const int j = st / SPS;
-                            if (g > 0 || j > 0) {
+                            for (int pc = 0; pc < 2; ++pc) {
+                                const uint2 c = *reinterpret_cast<const uint2*>(cs + unit_code_offset(lrow, pc) + 8 * hh);
+                                cw[wt][2 * pc] = c.x; cw[wt][2 * pc + 1] = c.y;
+                            }
+                        }
+                    }
 #pragma unroll
-                                for (int wt = 0; wt < 4; ++wt) {
-                                    const float r = sprev[wt] * __builtin_amdgcn_rcpf(scg[j][wt]);
+                    for (int j = 0; j < GPU; ++j) {
+                        const int gj = f * GPU + j;               // scale group within group g
+                        if (gj < SPG) {
+                            const float2 sc = scale_at(g, gj);
+                            if (g > 0 || gj > 0) {
+                                const float r0 = sprev[0] * __builtin_amdgcn_rcpf(sc.x);
+                                const float r1 = sprev[1] * __builtin_amdgcn_rcpf(sc.y);
 #pragma unroll
-                                    for (int tk = 0; tk < NT; ++tk) acc[wt][tk] *= r;
+                                for (int tk = 0; tk < NT; ++tk) {
+                                    acc[0][tk] *= r0;
+                                    acc[1][tk] *= r1;
                                 }
                             }
-#pragma unroll
-                            for (int wt = 0; wt < 4; ++wt) sprev[wt] = scg[j][wt];
-                        }
-                        uint32_t B[4][4];
-#pragma unroll
-                        for (int wt = 0; wt < 4; ++wt) code_operand<4>(&cw[wt], 0, B[wt]);
-                        if (st + 1 < 4) {
-#pragma unroll
-                            for (int wt = 0; wt < 4; ++wt) cw[wt] = code_w(wt, st + 1);
+                            sprev[0] = sc.x;
+                            sprev[1] = sc.y;
                         }
 #pragma unroll
-                        for (int tk = 0; tk < NT; ++tk) {
-                            uint4 a_nxt = a_cur;
-                            if (tk + 1 < NT) a_nxt = lds_a(tk + 1, st);
-                            else if (st + 1 < 4) a_nxt = lds_a(0, st + 1);
-                            const uint32_t A[4] = {a_cur.x, a_cur.y, a_cur.z, a_cur.w};
+                        for (int s2 = 0; s2 < S; ++s2) {
+                            const int c = j * 2 * S + hh * S + s2;       // chunk of the unit
+                            uint32_t B[2][4];
+                            code_operand<4>(&cw[0][j * S + s2], 0, B[0]);
+                            code_operand<4>(&cw[1][j * S + s2], 0, B[1]);
 #pragma unroll
-                            for (int wt = 0; wt < 4; ++wt) acc[wt][tk] = mfma16(A, B[wt], acc[wt][tk]);
-                            a_cur = a_nxt;
-                            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // one LDS read, then
-                            __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);   // four MFMAs
+                            for (int tk = 0; tk < NT; ++tk) {
+                                const int r = 32 * tk + n;
+                                const uint4 a4 =
+                                    *reinterpret_cast<const uint4*>(base + r * kUnitRowB + 16 * (c ^ (r & 7)));
+                                const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
+                                acc[0][tk] = mfma32(A, B[0], acc[0][tk]);
+                                acc[1][tk] = mfma32(A, B[1], acc[1][tk]);
+                            }
                         }
-                        __builtin_amdgcn_sched_barrier(0);   // one step's operands live at a time
                     }
                 }
             }
 
-            // ---- group sums of x: acc += (sum_j beta_j X_j) / t_J per tile, on
-            // float32 MFMAs (A: token row 16 tk + m, group 4 jb + q; B: weight row
-            // m of tile wt, the same group)
+            // ---- group sums of x on float32 MFMAs (32 x 32 x 2: A lane l: token
+            // row l % 32, group 2 jb + h; B: weight row n, the same group)
             wait_vmem<0>();
             if (rows_ok) {
-                float invt[4];
-#pragma unroll
-                for (int wt = 0; wt < 4; ++wt) invt[wt] = kLever<4> * __builtin_amdgcn_rcpf(sprev[wt]);
+                const float invt[2] = {kLever<4> * __builtin_amdgcn_rcpf(sprev[0]),
+                                       kLever<4> * __builtin_amdgcn_rcpf(sprev[1])};
                 int tokx[NT];
 #pragma unroll
-                for (int tk = 0; tk < NT; ++tk) tokx[tk] = meta_token<kGuTiles>(p, mt, tk, m);
-                // loads of step jb + 1 are issued before the MFMAs of step jb
-                uint32_t sn[4], bn[4];
-                float xn[NT];
-                auto load_bias = [&](int jb) {
-                    const int gs = 4 * jb + q < NGS ? 4 * jb + q : 0;
+                for (int tk = 0; tk < NT; ++tk) tokx[tk] = meta_token<kGuTiles>(p, mt, 2 * tk + (n >> 4), n & 15);
+                // inputs of 4 MFMA steps (8 groups) per batch, all loads of a
+                // batch issued together
+                constexpr int BJ = 4;
+                const size_t orow = ((size_t)mt.e * I + row_base + lrow) * NGS;
+                const int NJ = (NGS + 1) / 2;
+                for (int jb0 = 0; jb0 < NJ; jb0 += BJ) {
+                    uint32_t sn[BJ][2], bn[BJ][2];
+                    float xn[BJ][NT];
 #pragma unroll
-                    for (int wt = 0; wt < 4; ++wt) {
-                        const size_t o = ((size_t)mt.e * I + row_base + lrow[wt]) * NGS + gs;
-                        sn[wt] = (wt < 2 ? p.sa : p.sb)[o];
-                        bn[wt] = (wt < 2 ? p.ba : p.bb)[o];
+                    for (int b = 0; b < BJ; ++b) {
+                        const int gs0 = 2 * (jb0 + b) + hh;
+                        const int gs = gs0 < NGS ? gs0 : 0;
+                        sn[b][0] = p.sa[orow + gs]; bn[b][0] = p.ba[orow + gs];
+                        sn[b][1] = p.sb[orow + gs]; bn[b][1] = p.bb[orow + gs];
+#pragma unroll
+                        for (int tk = 0; tk < NT; ++tk) xn[b][tk] = p.xs[(size_t)tokx[tk] * NGS + gs];
                     }
 #pragma unroll
-                    for (int tk = 0; tk < NT; ++tk) xn[tk] = p.xs[(size_t)tokx[tk] * NGS + gs];
-                };
-                const int NJ = (NGS + 3) / 4;
-                load_bias(0);
-                for (int jb = 0; jb < NJ; ++jb) {
-                    const bool gv = 4 * jb + q < NGS;
-                    float Bv[4], Xv[NT];
+                    for (int b = 0; b < BJ; ++b) {
+                        const bool gv = 2 * (jb0 + b) + hh < NGS;
+                        float Bv[2];
 #pragma unroll
-                    for (int wt = 0; wt < 4; ++wt)
-                        Bv[wt] = gv ? fmaf(-kOffset<4>, f16_bits_to_f32(sn[wt]), f16_bits_to_f32(bn[wt])) * invt[wt] : 0.f;
+                        for (int wt = 0; wt < 2; ++wt)
+                            Bv[wt] = gv ? fmaf(-kOffset<4>, f16_bits_to_f32(sn[b][wt]), f16_bits_to_f32(bn[b][wt])) * invt[wt]
+                                        : 0.f;
 #pragma unroll
-                    for (int tk = 0; tk < NT; ++tk) Xv[tk] = gv ? xn[tk] : 0.f;
-                    if (jb + 1 < NJ) load_bias(jb + 1);
-#pragma unroll
-                    for (int tk = 0; tk < NT; ++tk)
-#pragma unroll
-                        for (int wt = 0; wt < 4; ++wt) acc[wt][tk] = mfma16_f32(Xv[tk], Bv[wt], acc[wt][tk]);
+                        for (int tk = 0; tk < NT; ++tk) {
+                            const float Xv = gv ? xn[b][tk] : 0.f;
+                            acc[0][tk] = __builtin_amdgcn_mfma_f32_32x32x2f32(Xv, Bv[0], acc[0][tk], 0, 0, 0);
+                            acc[1][tk] = __builtin_amdgcn_mfma_f32_32x32x2f32(Xv, Bv[1], acc[1][tk], 0, 0, 0);
+                        }
+                    }
                 }
 
-                // ---- epilogue: h = silu(gate) * up, three planes, 16-row partial
-                // sums; value index v = 32 hf + 4 tk + i: token row 16 tk + 4 q + i,
-                // column 32 w + 16 hf + m of the block
-                float hv[8 * NT];
+                // ---- epilogue: h = silu(gate) * up, three planes, partial sums
+                // over each 16 columns.  Value index v = 16 tk + 4 j + i: token
+                // row 32 tk + 8 j + 4 h + i, column 32 w + n of the block.
+                float hv[16 * NT];
+                const float tg = sprev[0] * kInvLever<4>, tu = sprev[1] * kInvLever<4>;
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const float tg = sprev[hf] * kInvLever<4>, tu = sprev[2 + hf] * kInvLever<4>;
+                for (int tk = 0; tk < NT; ++tk)
 #pragma unroll
-                    for (int tk = 0; tk < NT; ++tk)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float gt = acc[hf][tk][i] * tg, upv = acc[2 + hf][tk][i] * tu;
-                            hv[4 * NT * hf + 4 * tk + i] = gt / (1.f + expf(-gt)) * upv;
-                        }
-                }
+                    for (int e = 0; e < 16; ++e) {
+                        const float gt = acc[0][tk][e] * tg, upv = acc[1][tk][e] * tu;
+                        hv[16 * tk + e] = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * upv;
+                    }
                 const size_t plane = (size_t)p.P * I;
-                const int i0 = row_base + 32 * wu;
+                const int col = row_base + kGuWaveRows * wu + n;
 #pragma unroll
-                for (int tk = 0; tk < NT; ++tk) {
-                    const int r0 = mt.row0[tk], rn = mt.n[tk];
+                for (int tk = 0; tk < NT; ++tk)
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
+                    for (int jj = 0; jj < 4; ++jj) {
+                        // token rows 32 tk + 8 jj + 4 h + i lie in work tile 2 tk + jj / 2
+                        const int wt_tile = 2 * tk + (jj >> 1);
+                        const int r0 = mt.row0[wt_tile], rn = mt.n[wt_tile];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int row = 4 * q + i;
-                            if (row < rn) {
+                            const int slot = 8 * (jj & 1) + 4 * hh + i;
+                            if (slot < rn) {
                                 uint32_t hi, mid, lo;
-                                split3_bf16(hv[4 * NT * hf + 4 * tk + i], hi, mid, lo);
-                                uint16_t* dst = p.hp + (size_t)(r0 + row) * I + i0 + 16 * hf + m;
+                                split3_trunc(hv[16 * tk + 4 * jj + i], hi, mid, lo);
+                                uint16_t* dst = p.hp + (size_t)(r0 + slot) * I + col;
                                 dst[0] = (uint16_t)hi;
                                 dst[plane] = (uint16_t)mid;
                                 dst[2 * plane] = (uint16_t)lo;
                             }
                         }
-                }
-                // partial sums over each 16 columns: lane m ends with value indices
-                // NV m .. NV m + NV - 1 (NV = NT / 2), i.e. token rows of one tile
-                // and one 16-column half of the wave
-                row16_stage<8 * NT, 0>(hv, lane);
-                row16_stage<8 * NT, 1>(hv, lane);
-                row16_stage<8 * NT, 2>(hv, lane);
-                row16_stage<8 * NT, 3>(hv, lane);
-                constexpr int NV = NT / 2;                 // totals per lane
-                const int tk = (NV * m / 4) % NT, hf = NV * m / (4 * NT);
-                int r0 = 0, rn = 0;
+                    }
+                // partial sums over 16 columns (lanes of the same n / 16 and h):
+                // lane n % 16 ends with value indices NT (n % 16) .. + NT - 1
+                row16_stage<16 * NT, 0>(hv, lane);
+                row16_stage<16 * NT, 1>(hv, lane);
+                row16_stage<16 * NT, 2>(hv, lane);
+                row16_stage<16 * NT, 3>(hv, lane);
 #pragma unroll
-                for (int t2 = 0; t2 < NT; ++t2) {
-                    r0 = t2 == tk ? mt.row0[t2] : r0;
-                    rn = t2 == tk ? mt.n[t2] : rn;
-                }
+                for (int uu = 0; uu < NT; ++uu) {
+                    const int v = NT * (n & 15) + uu;           // value index: 16 tk + 4 jj + i
+                    const int tk = v >> 4, jj = (v >> 2) & 3, i = v & 3;
+                    const int wt_tile = 2 * tk + (jj >> 1);
+                    int r0 = 0, rn = 0;
 #pragma unroll
-                for (int u = 0; u < NV; ++u) {
-                    const int row = 4 * q + (NV * m + u) % 4;
-                    if (row < rn) p.hpart[(size_t)(r0 + row) * (I / 16) + (i0 + 16 * hf) / 16] = hv[u];
+                    for (int t2 = 0; t2 < kGuTiles; ++t2) {
+                        r0 = t2 == wt_tile ? mt.row0[t2] : r0;
+                        rn = t2 == wt_tile ? mt.n[t2] : rn;
+                    }
+                    const int slot = 8 * (jj & 1) + 4 * hh + i;
+                    if (slot < rn)
+                        p.hpart[(size_t)(r0 + slot) * (I / 16) + (row_base + kGuWaveRows * wu + 16 * (n >> 4)) / 16] = hv[uu];
                 }
             }
         };
-        if (mt.ntk > 4) run(std::integral_constant<int, 8>{});
-        else run(std::integral_constant<int, 4>{});
-        lds_barrier();                       // every wave is done with the rings before the next item
+        if (mt.ntk > 4) run(std::integral_constant<int, 4>{});
+        else run(std::integral_constant<int, 2>{});
+        lds_barrier();                       // every wave is done with the ring before the next item
     }
 }
 
 // ------------------------------------------------------------------- down
-// Item = (head of 4 tiles, block of 512 output rows).  Wave w: output rows
-// blk*512 + 64 w + 16 wt + m, wt = 0..3; token tiles tk = 0..3 (rows 16 tk ..).
-// Per group g of 128 along I: activation slot g % 2 holds the three planes of
-// h for the 64 rows (plane pl, row r at (pl * 64 + r) * 256, chunks swizzled
-// by the row's low 4 bits), code slot g % 2 the codes of the 512 rows, both
-// staged one group ahead, and registers the wave's scales of the next group.
-constexpr int kDnActRing = 2, kDnCodeRing = 2;
-constexpr int kDnCodeSlot = kDnRows * 64;              // 32 KB
-constexpr int kDnCodeStage = kDnCodeSlot / kDma / kWaves;   // 4
-constexpr size_t kDnLds = (size_t)kDnActRing * kDnSlot + (size_t)kDnCodeRing * kDnCodeSlot;   // 160 KB
+// On v_mfma_f32_32x32x16_bf16, as the gate/up kernel: A = the three bf16 planes
+// of h (rows = tokens), B = codes (columns = output rows).
+// Item = (head of 4 tiles = 64 token rows, block of 512 output rows).  Wave w:
+// output rows blk*512 + 64 w + 32 wt + n, wt = 0, 1; token tiles tk = 0..NT-1
+// of 32 rows.  Units of 64 along I with the chunk mapping of the gate/up
+// kernel.  LDS: three unit slots (each: the three planes of h for the 64 token
+// rows, 128 bytes per row and plane; 32 bytes of codes of each of the 512
+// rows) and two scale slots; units staged two ahead.
+constexpr int kDnActUnit = 3 * kDnTok * kUnitRowB;               // 24 KB
+constexpr int kDnCodeUnit = kDnRows * 32;                        // 16 KB
+constexpr int kDnUnitB = kDnActUnit + kDnCodeUnit;               // 40 KB
+constexpr int kDnUnits = 3;
+constexpr int kDnScaleSlot = kDnRows * 16;                       // 8 KB
+constexpr int kDnScaleSlots = 2;
+constexpr size_t kDnLds = (size_t)kDnUnits * kDnUnitB + (size_t)kDnScaleSlots * kDnScaleSlot;   // 136 KB
+constexpr int kDnActDma = kDnActUnit / kDma / kWaves;            // 3 per wave
+constexpr int kDnCodeDma = kDnCodeUnit / kDma / kWaves;          // 2 per wave
 
 template <int SPG>
-__global__ __launch_bounds__(kThreads, 1) void ffn_down_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_down_gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr bool TR = SPG > 1;
-    constexpr int SPS = 4 / SPG;
-    constexpr int NSW = SPG > 2 ? 2 : 1;
+    constexpr int S = SPG == 4 ? 2 : 4;                 // MFMA steps per scale group within a unit
+    constexpr int GPU = 4 / S;                          // scale groups per unit
     constexpr int G = kGroup / SPG;
-    uint8_t* const abuf = smem;
-    uint8_t* const cbuf = smem + kDnActRing * kDnSlot;
-    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.H, I = p.I, NG = I / kGroup, NGS = p.NGS;
+    const int H = p.H, I = p.I, NG = I / kGroup, NGS = p.NGS, NU = 2 * NG;
     const int n_items = ld_scalar(p.n_heads, 0) * p.blocks;
     const int per = (n_items + 7) >> 3;
     const size_t plane_b = (size_t)p.P * I * 2;
+    uint8_t* const sbuf = smem + kDnUnits * kDnUnitB;
 
     for (int slot_i = blockIdx.x; slot_i < 8 * per; slot_i += gridDim.x) {
         const int item = xcd_item(slot_i, per);
@@ -602,109 +664,141 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_gemm_kernel(GemmParams p
         gemm_meta<kDnTiles>(p, item, mt);
         const int blk_base = mt.blk * kDnRows;
         const int valid = H - blk_base < kDnRows ? H - blk_base : kDnRows;
-        const int n_base = blk_base + 64 * wu;
         const bool rows_ok = 64 * wu < valid;
-        // activation staging: load j of wave wu is LDS piece ii = 6 wu + j:
-        // plane ii / 16, rows 4 (ii % 16) + q
-        uint64_t soff[kDnStage];
+        // activation staging: load j of wave w is 1 KB piece ii = 3 w + j of
+        // the unit slot: plane ii / 8, token rows 8 (ii % 8) + lane / 8 (work
+        // tile (ii % 8) / 2), position lane % 8 holding chunk (lane % 8) ^ (row % 8)
+        uint32_t soff[kDnActDma];
 #pragma unroll
-        for (int j = 0; j < kDnStage; ++j) {
-            const int ii = kDnStage * wu + j, pl = ii >> 4, rr = 4 * (ii & 15) + q;
+        for (int j = 0; j < kDnActDma; ++j) {
+            const int ii = kDnActDma * wu + j, pl = ii >> 3, rr = 8 * (ii & 7) + (lane >> 3);
             int row = 0;
 #pragma unroll
             for (int t2 = 0; t2 < kDnTiles; ++t2)
                 row = (rr >> 4) == t2 ? meta_row<kDnTiles>(mt, t2, rr & 15) : row;
-            soff[j] = pl * plane_b + (uint64_t)row * (I * 2) + 16u * (uint32_t)(m ^ (rr & 15));
+            soff[j] = (uint32_t)(pl * plane_b + (size_t)row * (I * 2)) + 16u * (uint32_t)((lane & 7) ^ (rr & 7));
         }
+        // code staging: load j of wave w is piece ii = 2 w + j: rows 32 ii + lane / 2, piece lane % 2
+        uint32_t coff[kDnCodeDma];
+#pragma unroll
+        for (int j = 0; j < kDnCodeDma; ++j) {
+            const int rr = 32 * (kDnCodeDma * wu + j) + (lane >> 1);
+            const int rc = rr < valid ? rr : valid - 1;
+            coff[j] = (uint32_t)rc * 64u + 16u * (uint32_t)((lane & 1) ^ ((rr >> 2) & 1));
+        }
+        // scales: wave w stages rows 64 w + lane
+        const int srow = 64 * wu + lane;
+        const size_t srow_g = (size_t)mt.e * H + blk_base + (srow < valid ? srow : valid - 1);
         const uint8_t* hbytes = reinterpret_cast<const uint8_t*>(p.hp);
-        auto stage_act = [&](int g) {
-            uint8_t* dst = abuf + (g % kDnActRing) * kDnSlot + (kDnStage * wu) * kDma;
+        auto stage = [&](int u) {
+            const int g = u >> 1, f = u & 1;
+            uint8_t* base = smem + (u % kDnUnits) * kDnUnitB;
 #pragma unroll
-            for (int j = 0; j < kDnStage; ++j) dma16(hbytes + soff[j] + (size_t)g * kRowB, dst + j * kDma);
-        };
-        auto stage_cod = [&](int g) {
-            const uint8_t* src = p.qa + (((size_t)mt.e * NG + g) * H + blk_base) * 64;
-            stage_codes<kDnCodeStage>(src, valid, cbuf + (g % kDnCodeRing) * kDnCodeSlot, wu, lane);
-        };
-        const int nb_c = rows_ok ? n_base : 0;
-        uint32_t srn[4][NSW];
-        auto load_sc = [&](int g) {
+            for (int j = 0; j < kDnActDma; ++j)
+                dma16_sv(hbytes + (size_t)g * kRowB + f * kUnitRowB, soff[j], base + (kDnActDma * wu + j) * kDma);
+            const uint8_t* cb = p.qa + (((size_t)mt.e * NG + g) * H + blk_base) * 64 + f * 32;
 #pragma unroll
-            for (int wt = 0; wt < 4; ++wt)
-                load_scales<SPG, NSW>(p.sa + ((size_t)mt.e * H + nb_c + 16 * wt + m) * NGS + (size_t)g * SPG, srn[wt]);
+            for (int j = 0; j < kDnCodeDma; ++j) dma16_sv(cb, coff[j], base + kDnActUnit + (kDnCodeDma * wu + j) * kDma);
+            if (f == 0) {
+                const size_t e_off = (srow_g * NGS + (size_t)g * SPG) * 2;
+                dma16(reinterpret_cast<const uint8_t*>(p.sa) + (e_off & ~(size_t)15),
+                      sbuf + (g % kDnScaleSlots) * kDnScaleSlot + wu * kDma);
+            }
+        };
+        int lrow[2];
+#pragma unroll
+        for (int wt = 0; wt < 2; ++wt) lrow[wt] = 64 * wu + 32 * wt + n;
+        const size_t lrow_g0 = (size_t)mt.e * H + blk_base + (rows_ok ? lrow[0] : 0);
+        auto scale_at = [&](int g, int j) {
+            float2 r;
+#pragma unroll
+            for (int wt = 0; wt < 2; ++wt) {
+                const uint32_t k = (uint32_t)((lrow_g0 + 32 * wt) * NGS + (size_t)g * SPG + j) & 7u;
+                const float v = f16_bits_to_f32(
+                    *reinterpret_cast<const uint16_t*>(sbuf + (g % kDnScaleSlots) * kDnScaleSlot + lrow[wt] * 16 + 2 * k));
+                const float vv = v == 0.f ? kTinyScale : v;
+                if (wt == 0) r.x = vv; else r.y = vv;
+            }
+            return r;
         };
 
-        // The same one-group rings as the gate/up kernel.
-        load_sc(0);
-        stage_act(0);
-        stage_cod(0);
-        // the item's body for NT token tiles (4, or 2 when the item has at most
-        // 2 non-empty tiles)
+        stage(0);
+        stage(1);
         auto run = [&](auto ntc) {
             constexpr int NT = decltype(ntc)::value;
-            floatx4_t acc[4][NT];
+            floatx16_t acc[2][NT];
 #pragma unroll
-            for (int wt = 0; wt < 4; ++wt)
+            for (int wt = 0; wt < 2; ++wt)
 #pragma unroll
-                for (int tk = 0; tk < NT; ++tk) acc[wt][tk] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            float sprev[4] = {1.f, 1.f, 1.f, 1.f};
+                for (int tk = 0; tk < NT; ++tk)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[wt][tk][e] = 0.f;
+            float sprev[2] = {1.f, 1.f};
 
-            for (int g = 0; g < NG; ++g) {
-                wait_vmem<0>();
-                lds_barrier();
-                float scg[SPG][4];
-#pragma unroll
-                for (int j = 0; j < SPG; ++j)
-#pragma unroll
-                    for (int wt = 0; wt < 4; ++wt) {
-                        scg[j][wt] = ring_scale(srn[wt], j);
-                        asm volatile("" : : "v"(scg[j][wt]));
-                    }
-                if (g + 1 < NG) {
-                    load_sc(g + 1);
-                    stage_act(g + 1);
-                    stage_cod(g + 1);
+            for (int u = 0; u < NU; ++u) {
+                // unit u has landed: the loads after it are unit u + 1's (5 per
+                // wave, plus 1 when it starts a group)
+                if (u + 1 < NU) {
+                    if ((u & 1) != 0) wait_vmem<kDnActDma + kDnCodeDma + 1>();
+                    else wait_vmem<kDnActDma + kDnCodeDma>();
+                } else {
+                    wait_vmem<0>();
                 }
-                const uint8_t* buf = abuf + (g % kDnActRing) * kDnSlot;
-                const uint8_t* cslot = cbuf + (g % kDnCodeRing) * kDnCodeSlot;
+                lds_barrier();
+                if (u + 2 < NU) stage(u + 2);
+                const int g = u >> 1, f = u & 1;
+                const uint8_t* base = smem + (u % kDnUnits) * kDnUnitB;
                 if (rows_ok) {
+                    uint32_t cw[2][4];
 #pragma unroll
-                    for (int j = 0; j < SPG; ++j) {
-                        float sc[4];
+                    for (int wt = 0; wt < 2; ++wt) {
+                        const uint8_t* cs = base + kDnActUnit;
+                        if constexpr (S == 4) {
+                            const uint4 c = *reinterpret_cast<const uint4*>(cs + unit_code_offset(lrow[wt], hh));
+                            cw[wt][0] = c.x; cw[wt][1] = c.y; cw[wt][2] = c.z; cw[wt][3] = c.w;
+                        } else {
 #pragma unroll
-                        for (int wt = 0; wt < 4; ++wt) sc[wt] = scg[j][wt];
-                        if (g > 0 || j > 0) {
-#pragma unroll
-                            for (int wt = 0; wt < 4; ++wt) {
-                                const float r = sprev[wt] * __builtin_amdgcn_rcpf(sc[wt]);
-#pragma unroll
-                                for (int tk = 0; tk < NT; ++tk) acc[wt][tk] *= r;
+                            for (int pc = 0; pc < 2; ++pc) {
+                                const uint2 c = *reinterpret_cast<const uint2*>(cs + unit_code_offset(lrow[wt], pc) + 8 * hh);
+                                cw[wt][2 * pc] = c.x; cw[wt][2 * pc + 1] = c.y;
                             }
                         }
+                    }
 #pragma unroll
-                        for (int wt = 0; wt < 4; ++wt) sprev[wt] = sc[wt];
+                    for (int j = 0; j < GPU; ++j) {
+                        const int gj = f * GPU + j;
+                        if (gj < SPG) {
+                            const float2 sc = scale_at(g, gj);
+                            if (g > 0 || gj > 0) {
+                                const float r0 = sprev[0] * __builtin_amdgcn_rcpf(sc.x);
+                                const float r1 = sprev[1] * __builtin_amdgcn_rcpf(sc.y);
 #pragma unroll
-                        for (int s2 = 0; s2 < SPS; ++s2) {
-                            const int st = j * SPS + s2;
-                            const int c = TR ? 4 * st + q : 4 * q + st;
-                            uint32_t B[4][4];
-#pragma unroll
-                            for (int wt = 0; wt < 4; ++wt) {
-                                const uint32_t w = read_code_word<TR>(cslot, 64 * wu + 16 * wt + m, q, st);
-                                code_operand<4>(&w, 0, B[wt]);
+                                for (int tk = 0; tk < NT; ++tk) {
+                                    acc[0][tk] *= r0;
+                                    acc[1][tk] *= r1;
+                                }
                             }
+                            sprev[0] = sc.x;
+                            sprev[1] = sc.y;
+                        }
+#pragma unroll
+                        for (int s2 = 0; s2 < S; ++s2) {
+                            const int c = j * 2 * S + hh * S + s2;
+                            uint32_t B[2][4];
+                            code_operand<4>(&cw[0][j * S + s2], 0, B[0]);
+                            code_operand<4>(&cw[1][j * S + s2], 0, B[1]);
 #pragma unroll
                             for (int tk = 0; tk < NT; ++tk) {
+                                const int r = 32 * tk + n;
 #pragma unroll
                                 for (int pl = 0; pl < 3; ++pl) {
                                     const uint4 a4 = *reinterpret_cast<const uint4*>(
-                                        buf + (pl * kDnTok + 16 * tk + m) * kRowB + 16 * (c ^ m));
+                                        base + (pl * kDnTok + r) * kUnitRowB + 16 * (c ^ (r & 7)));
                                     const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-                                    for (int wt = 0; wt < 4; ++wt) acc[wt][tk] = mfma16(A, B[wt], acc[wt][tk]);
+                                    acc[0][tk] = mfma32(A, B[0], acc[0][tk]);
+                                    acc[1][tk] = mfma32(A, B[1], acc[1][tk]);
                                 }
                             }
-                            __builtin_amdgcn_sched_barrier(0);
                         }
                     }
                 }
@@ -712,71 +806,84 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_gemm_kernel(GemmParams p
 
             wait_vmem<0>();
             if (rows_ok) {
-                // ---- group sums of h (from the 16-row partial sums), as in gate/up
-                float invt[4];
-#pragma unroll
-                for (int wt = 0; wt < 4; ++wt) invt[wt] = kLever<4> * __builtin_amdgcn_rcpf(sprev[wt]);
+                // ---- group sums of h (from the 16-row partial sums) on float32
+                // MFMAs (32 x 32 x 2: A token row l % 32, group 2 jb + h)
+                const float invt[2] = {kLever<4> * __builtin_amdgcn_rcpf(sprev[0]),
+                                       kLever<4> * __builtin_amdgcn_rcpf(sprev[1])};
                 int rowx[NT];
 #pragma unroll
-                for (int tk = 0; tk < NT; ++tk) rowx[tk] = meta_row<kDnTiles>(mt, tk, m);
-                // loads of step jb + 1 are issued before the MFMAs of step jb
-                uint32_t sn[4], bn[4];
-                float xn[NT][G / 16];
-                auto load_bias = [&](int jb) {
-                    const int gs = 4 * jb + q < NGS ? 4 * jb + q : 0;
-#pragma unroll
-                    for (int wt = 0; wt < 4; ++wt) {
-                        const size_t o = ((size_t)mt.e * H + n_base + 16 * wt + m) * NGS + gs;
-                        sn[wt] = p.sa[o];
-                        bn[wt] = p.ba[o];
-                    }
-#pragma unroll
-                    for (int tk = 0; tk < NT; ++tk) {
-                        const float* hp = p.hpart + (size_t)rowx[tk] * (I / 16) + gs * (G / 16);
-#pragma unroll
-                        for (int u = 0; u < G / 16; ++u) xn[tk][u] = hp[u];
-                    }
-                };
-                const int NJ = (NGS + 3) / 4;
-                load_bias(0);
-                for (int jb = 0; jb < NJ; ++jb) {
-                    const bool gv = 4 * jb + q < NGS;
-                    float Bv[4], Xv[NT];
-#pragma unroll
-                    for (int wt = 0; wt < 4; ++wt)
-                        Bv[wt] = gv ? fmaf(-kOffset<4>, f16_bits_to_f32(sn[wt]), f16_bits_to_f32(bn[wt])) * invt[wt] : 0.f;
-#pragma unroll
-                    for (int tk = 0; tk < NT; ++tk) {
-                        float xs = 0.f;
-#pragma unroll
-                        for (int u = 0; u < G / 16; ++u) xs += xn[tk][u];
-                        Xv[tk] = gv ? xs : 0.f;
-                    }
-                    if (jb + 1 < NJ) load_bias(jb + 1);
-#pragma unroll
-                    for (int tk = 0; tk < NT; ++tk)
-#pragma unroll
-                        for (int wt = 0; wt < 4; ++wt) acc[wt][tk] = mfma16_f32(Xv[tk], Bv[wt], acc[wt][tk]);
-                }
-                // ---- Y rows in bf16 (token row 16 tk + 4 q + i, column 16 wt + m)
-#pragma unroll
                 for (int tk = 0; tk < NT; ++tk) {
-                    const int r0 = mt.row0[tk], rn = mt.n[tk];
+                    const int rr = 32 * tk + n;
+                    int row = 0;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 4 * q + i;
-                        if (row < rn) {
-                            uint16_t* yrow = p.y + (size_t)(r0 + row) * H + n_base + m;
+                    for (int t2 = 0; t2 < kDnTiles; ++t2)
+                        row = (rr >> 4) == t2 ? meta_row<kDnTiles>(mt, t2, rr & 15) : row;
+                    rowx[tk] = row;
+                }
+                constexpr int BJ = 4;
+                const int NJ = (NGS + 1) / 2;
+                for (int jb0 = 0; jb0 < NJ; jb0 += BJ) {
+                    uint32_t sn[BJ][2], bn[BJ][2];
+                    float xn[BJ][NT][G / 16];
 #pragma unroll
-                            for (int wt = 0; wt < 4; ++wt)
-                                yrow[16 * wt] = (uint16_t)f32_to_bf16_bits(acc[wt][tk][i] * sprev[wt] * kInvLever<4>);
+                    for (int b = 0; b < BJ; ++b) {
+                        const int gs0 = 2 * (jb0 + b) + hh;
+                        const int gs = gs0 < NGS ? gs0 : 0;
+#pragma unroll
+                        for (int wt = 0; wt < 2; ++wt) {
+                            const size_t o = ((size_t)mt.e * H + blk_base + lrow[wt]) * NGS + gs;
+                            sn[b][wt] = p.sa[o];
+                            bn[b][wt] = p.ba[o];
+                        }
+#pragma unroll
+                        for (int tk = 0; tk < NT; ++tk) {
+                            const float* hp = p.hpart + (size_t)rowx[tk] * (I / 16) + gs * (G / 16);
+#pragma unroll
+                            for (int uu = 0; uu < G / 16; ++uu) xn[b][tk][uu] = hp[uu];
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < BJ; ++b) {
+                        const bool gv = 2 * (jb0 + b) + hh < NGS;
+                        float Bv[2];
+#pragma unroll
+                        for (int wt = 0; wt < 2; ++wt)
+                            Bv[wt] = gv ? fmaf(-kOffset<4>, f16_bits_to_f32(sn[b][wt]), f16_bits_to_f32(bn[b][wt])) * invt[wt]
+                                        : 0.f;
+#pragma unroll
+                        for (int tk = 0; tk < NT; ++tk) {
+                            float xs = 0.f;
+#pragma unroll
+                            for (int uu = 0; uu < G / 16; ++uu) xs += xn[b][tk][uu];
+                            const float Xv = gv ? xs : 0.f;
+                            acc[0][tk] = __builtin_amdgcn_mfma_f32_32x32x2f32(Xv, Bv[0], acc[0][tk], 0, 0, 0);
+                            acc[1][tk] = __builtin_amdgcn_mfma_f32_32x32x2f32(Xv, Bv[1], acc[1][tk], 0, 0, 0);
                         }
                     }
                 }
+                // ---- Y rows in bf16: token row 32 tk + 8 jj + 4 h + i (work
+                // tile 2 tk + jj / 2, slot 8 (jj % 2) + 4 h + i), column lrow[wt]
+#pragma unroll
+                for (int tk = 0; tk < NT; ++tk)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int wt_tile = 2 * tk + (jj >> 1);
+                        const int r0 = mt.row0[wt_tile], rn = mt.n[wt_tile];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int slot = 8 * (jj & 1) + 4 * hh + i;
+                            if (slot < rn) {
+                                uint16_t* yrow = p.y + (size_t)(r0 + slot) * H + blk_base;
+#pragma unroll
+                                for (int wt = 0; wt < 2; ++wt)
+                                    yrow[lrow[wt]] = (uint16_t)f32_to_bf16_bits(acc[wt][tk][4 * jj + i] * sprev[wt] * kInvLever<4>);
+                            }
+                        }
+                    }
             }
         };
-        if (mt.ntk > 2) run(std::integral_constant<int, 4>{});
-        else run(std::integral_constant<int, 2>{});
+        if (mt.ntk > 2) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
         lds_barrier();
     }
 }
@@ -796,10 +903,13 @@ static size_t max_lds_per_block() {
 }
 
 // The rings stage two groups ahead within an item, so each K holds at least
-// two groups of 128; 4-bit codes; groups of 128, 64 or 32.
+// two groups of 128; 4-bit codes; groups of 128, 64 or 32; the staging
+// offsets into x and into the h planes fit 32 bits.
 bool gemm_supported(const moe_dims& d, int bits) {
+    const uint64_t P = (uint64_t)d.T * d.k;
     return bits == 4 && (d.group_size == 128 || d.group_size == 64 || d.group_size == 32) && d.I % kGroup == 0 &&
-           d.H % kGroup == 0 && d.H >= 2 * kGroup && d.I >= 2 * kGroup;
+           d.H % kGroup == 0 && d.H >= 2 * kGroup && d.I >= 2 * kGroup && (uint64_t)d.T * d.H * 2 < (1ull << 32) &&
+           3 * P * d.I * 2 < (1ull << 32);
 }
 
 static long max_heads(const moe_dims& d, int tiles) {
@@ -859,7 +969,8 @@ static unsigned gemm_grid() {
 
 template <int SPG>
 static void launch_gu(const GemmParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(ffn_gateup_gemm_kernel<SPG>, dim3(gemm_grid()), dim3(kThreads), kGuLds, s, p);
+    // two workgroups per CU
+    hipLaunchKernelGGL(ffn_gateup_gemm_kernel<SPG>, dim3(2 * gemm_grid()), dim3(kGuThreads), kGuLds, s, p);
 }
 
 template <int SPG>

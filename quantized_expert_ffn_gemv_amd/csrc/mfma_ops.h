@@ -127,6 +127,18 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
+// The same load addressed as a wave-uniform 64-bit base (scalar registers)
+// plus a 32-bit per-lane byte offset, so that moving the base along K costs
+// scalar instructions only.  A vector-memory instruction that reads an SGPR a
+// VALU instruction wrote (v_readlane, v_readfirstlane: the compiler restores
+// spilled scalars that way) needs 5 wait states in between, and the
+// compiler's hazard checks do not look inside inline assembly: s_nop 5
+// provides 6 (and the one M0 needs).
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, void* lds_base) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)lds_base;
+    asm volatile("s_nop 5\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // Copy `bytes` (a multiple of 16) of contiguous global memory to LDS, waves
 // taking 1 KB pieces in turn; lanes past the end reload the last 16 bytes into
 // the padding (the LDS region is rounded up to a whole piece).

@@ -99,6 +99,8 @@ def parse():
                     help="skip the 64-expert layer behind the residency tiers (hot set + warm ring + host memory)")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed steps of the T=4096 prefill layer on the grouped GEMM (0 = skip)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the T=4096 prefill layer and print its measurement as one JSON line")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the runs, copy a buffer of this many MiB device to device 5 times "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -700,6 +702,9 @@ def main():
     moe.lib()
     algo = {"auto": moe.ALGO_AUTO, "gemv": moe.ALGO_GEMV, "mfma": moe.ALGO_MFMA}[args.algo]
     ctx = dict(torch=torch, mi=mi, moe=moe, layers={}, cpu=not args.no_cpu_baseline)
+    if args.prefill_only:
+        print(json.dumps({"prefill": measure_prefill(ctx, max(args.prefill_steps, 1), 3)}), flush=True)
+        return
 
     if args.only:
         name, bits, T = args.only.split(":")

@@ -353,10 +353,13 @@ __device__ __forceinline__ floatx16_t mfma32(const uint32_t (&a)[4], const uint3
 // order of the down kernels' operands.
 __device__ __forceinline__ int pair_order_row32(int n) { return 8 * (n >> 3) + ((n & 7) >> 1) + 4 * (n & 1); }
 
-// A unit's codes of one row: 32 bytes (two 16-byte pieces) at r * 32, the
-// pieces swapped on every fourth row pair so that 8 consecutive lanes reading
-// one piece of 8 rows (4 distinct 32-byte rows mod 128 bytes) hit all banks.
-__device__ __forceinline__ int unit_code_offset(int r, int piece) { return r * 32 + 16 * (piece ^ ((r >> 2) & 1)); }
+// LDS placement of the unit slots, for 64 banks served 16 lanes at a time: a
+// unit's x (or h) row is 128 bytes, its 16-byte chunk c at position
+// c ^ ((r >> 1) & 7), so that the 16 rows one read touches at one chunk (two
+// rows per 256-byte bank line) hit 16 distinct bank groups; a row's codes are
+// 32 bytes, piece p at position p ^ ((r >> 3) & 1), for the same reason.
+__device__ __forceinline__ int unit_act_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int unit_code_offset(int r, int piece) { return r * 32 + 16 * (piece ^ ((r >> 3) & 1)); }
 
 template <int SPG>
 __global__ __launch_bounds__(kGuThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gateup_gemm_kernel(GemmParams p) {
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kGuThreads, 2) __attribute__((amdgpu_waves_per_eu(2
         const bool rows_ok = kGuWaveRows * wu < valid;     // waves past I stage and wait, nothing more
         // activation staging: load j of wave w is 1 KB piece 4 w + j of the
         // unit slot: token rows 32 w + 8 j + lane / 8 (work tile 2 w + j / 2),
-        // 16-byte position lane % 8, which holds chunk (lane % 8) ^ (row % 8)
+        // 16-byte position lane % 8, which holds the chunk unit_act_pos maps there
         uint32_t soff[kGuActDma];
 #pragma unroll
         for (int j = 0; j < kGuActDma; ++j) {
@@ -393,7 +396,8 @@ __global__ __launch_bounds__(kGuThreads, 2) __attribute__((amdgpu_waves_per_eu(2
                 tok = p.work[(size_t)(mt.h0 + 2 * wu + (j >> 1)) * kWorkInts + 4 + (sl < rn ? sl : 0)];
                 tok = (tok >= 0 && tok < p.T) ? tok : 0;
             }
-            soff[j] = (uint32_t)tok * (uint32_t)(H * 2) + 16u * (uint32_t)((lane & 7) ^ (sl & 7));
+            const int row = 32 * wu + 8 * j + (lane >> 3);
+            soff[j] = (uint32_t)tok * (uint32_t)(H * 2) + 16u * (uint32_t)unit_act_pos(row, lane & 7);
         }
         // code staging: load j of wave w is piece ii = 2 (w & 1) + j of the
         // gate (w < 2) or up rows: rows 32 ii + lane / 2, piece lane % 2
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(kGuThreads, 2) __attribute__((amdgpu_waves_per_eu(2
         for (int j = 0; j < kGuCodeDma; ++j) {
             const int rr = 32 * (kGuCodeDma * (wu & 1) + j) + (lane >> 1);
             const int rc = rr < valid ? rr : valid - 1;
-            coff[j] = (uint32_t)rc * 64u + 16u * (uint32_t)((lane & 1) ^ ((rr >> 2) & 1));
+            coff[j] = (uint32_t)rc * 64u + 16u * (uint32_t)((lane & 1) ^ ((rr >> 3) & 1));
         }
         const uint8_t* xbytes = reinterpret_cast<const uint8_t*>(p.xp);
         const uint8_t* cmat = wu < 2 ? p.qa : p.qb;
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(kGuThreads, 2) __attribute__((amdgpu_waves_per_eu(2
                             for (int tk = 0; tk < NT; ++tk) {
                                 const int r = 32 * tk + n;
                                 const uint4 a4 =
-                                    *reinterpret_cast<const uint4*>(base + r * kUnitRowB + 16 * (c ^ (r & 7)));
+                                    *reinterpret_cast<const uint4*>(base + r * kUnitRowB + 16 * unit_act_pos(r, c));
                                 const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
                                 acc[0][tk] = mfma32(A, B[0], acc[0][tk]);
                                 acc[1][tk] = mfma32(A, B[1], acc[1][tk]);
@@ -667,7 +671,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         const bool rows_ok = 64 * wu < valid;
         // activation staging: load j of wave w is 1 KB piece ii = 3 w + j of
         // the unit slot: plane ii / 8, token rows 8 (ii % 8) + lane / 8 (work
-        // tile (ii % 8) / 2), position lane % 8 holding chunk (lane % 8) ^ (row % 8)
+        // tile (ii % 8) / 2), position lane % 8 holding the chunk unit_act_pos maps there
         uint32_t soff[kDnActDma];
 #pragma unroll
         for (int j = 0; j < kDnActDma; ++j) {
@@ -676,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
             for (int t2 = 0; t2 < kDnTiles; ++t2)
                 row = (rr >> 4) == t2 ? meta_row<kDnTiles>(mt, t2, rr & 15) : row;
-            soff[j] = (uint32_t)(pl * plane_b + (size_t)row * (I * 2)) + 16u * (uint32_t)((lane & 7) ^ (rr & 7));
+            soff[j] = (uint32_t)(pl * plane_b + (size_t)row * (I * 2)) + 16u * (uint32_t)unit_act_pos(rr, lane & 7);
         }
         // code staging: load j of wave w is piece ii = 2 w + j: rows 32 ii + lane / 2, piece lane % 2
         uint32_t coff[kDnCodeDma];
@@ -684,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         for (int j = 0; j < kDnCodeDma; ++j) {
             const int rr = 32 * (kDnCodeDma * wu + j) + (lane >> 1);
             const int rc = rr < valid ? rr : valid - 1;
-            coff[j] = (uint32_t)rc * 64u + 16u * (uint32_t)((lane & 1) ^ ((rr >> 2) & 1));
+            coff[j] = (uint32_t)rc * 64u + 16u * (uint32_t)((lane & 1) ^ ((rr >> 3) & 1));
         }
         // scales: wave w stages rows 64 w + lane
         const int srow = 64 * wu + lane;
@@ -793,7 +797,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
                                 for (int pl = 0; pl < 3; ++pl) {
                                     const uint4 a4 = *reinterpret_cast<const uint4*>(
-                                        base + (pl * kDnTok + r) * kUnitRowB + 16 * (c ^ (r & 7)));
+                                        base + (pl * kDnTok + r) * kUnitRowB + 16 * unit_act_pos(r, c));
                                     const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
                                     acc[0][tk] = mfma32(A, B[0], acc[0][tk]);
                                     acc[1][tk] = mfma32(A, B[1], acc[1][tk]);

@@ -285,6 +285,293 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
     }
 }
 
+// ------------------------------------ gate / up with the activation tile in LDS
+// For shapes whose tile of x rows (min(T, 16) rows of H bf16) fits in LDS at
+// one workgroup per CU.  Workgroup b owns a contiguous range of items, so its
+// consecutive items mostly belong to one work-list entry: it stages that
+// entry's x rows in LDS once, already in the pair order of the code operands
+// (each 8-element run as 0,4,1,5,2,6,3,7 for 4-bit codes, each 16-element run
+// as 0,8,1,9,...,7,15 for 2-bit codes), so a step's B operand is one 16-byte
+// LDS read and needs no permutes, together with the rows' float32 sums over
+// each group of 128 (the X of the per-group fold, so no all-ones MFMA).  Only the codes stream, through a
+// D-deep register ring per wave that runs across item boundaries.  The NW
+// waves split K as in the kernel above; the partial sums meet in LDS, and
+// four waves share the epilogue (each takes four token columns), adding the
+// partials in wave order; with eight or more waves the two halves take turns
+// by item parity, so that neither half falls behind the other.  The partial sums are double-buffered by item
+// parity, so an item costs one barrier.  Token columns past the tile's rows
+// read one row of zeros.  Rows of the x tile are padded by 16 bytes, so the 16
+// rows one step reads fall in 16 different bank groups.
+// LDS: x tile [rows_cap + 1][H + 8] bf16 (the last row zero); group sums
+// [rows_cap + 1][NG] float (the last row zero); scales [NW][2][NGW][64] float
+// (by item parity); partial sums [2][NW][64][8] float.
+// A wave-uniform global pointer, passed through readfirstlane so that the
+// compiler keeps it whole: a load at uniform_gptr(base) + (32-bit lane offset)
+// then takes the scalar-base form (base in SGPRs, offset in one VGPR) instead
+// of 64-bit per-lane address arithmetic.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
+typedef const __attribute__((address_space(1))) u32x4_t* gu32x4_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) u32x2_t* gu32x2_t;
+
+__device__ __forceinline__ gbytes_t uniform_gptr(const uint8_t* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<gbytes_t>(((uint64_t)hi << 32) | lo);
+}
+
+template <int BITS, int D, int SJ, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p) {
+    static_assert(NW >= 4, "four waves share the epilogue");
+    constexpr int LB = 128 * BITS / 8 / 4;     // bytes per lane per group (16 or 8)
+    constexpr int LW = LB / 4;                 // code words per lane per group
+    constexpr int NT = 64 * NW;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ipe = p.items_per_entry;
+    if (blockIdx.x == 0)                                  // the streaming down's counters start at zero
+        for (int i = tid; i < p.n_split_ctr; i += NT) p.split_ctr[i] = 0;
+    const int n_items = ld_scalar(p.n_work, 0) * ipe;
+    const int per = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int i0 = (int)blockIdx.x * per;
+    const int n_my = min(n_items - i0, per);
+    if (n_my <= 0) return;
+    const int H = p.H, I = p.I, NG = H / kGroup, NGW = (NG + NW - 1) / NW;
+    const int rows_cap = p.T < kWorkRows ? p.T : kWorkRows;
+    const int xrow = H + 8;                               // bf16 per LDS row of the x tile
+    const int gb = (w * NG) / NW, ng = ((w + 1) * NG) / NW - gb;
+    constexpr int GB = kGroup * BITS / 8;      // code bytes of one row in one group
+    const size_t gstride = (size_t)I * GB;     // from one group of all I rows to the next
+    uint16_t* xt = reinterpret_cast<uint16_t*>(smem);
+    float* xs = reinterpret_cast<float*>(smem + (((size_t)(rows_cap + 1) * xrow * 2 + 15) & ~(size_t)15));
+    float* sc_all = xs + (((rows_cap + 1) * NG + 3) & ~3);
+    float* sc_base = sc_all + w * 2 * NGW * 64;
+    float* red = sc_all + NW * 2 * NGW * 64;
+
+    // a lane's codes of group g: base + g * gstride + loff (base uniform)
+    const uint32_t loff = (uint32_t)(pair_order_row<BITS>(m) * GB + q * LB);
+    struct Item {
+        int entry, e, it, row0, n;
+        const uint8_t* g;
+        const uint8_t* u;
+        uint32_t sv[4][SJ];
+    };
+    auto fetch = [&](int j, Item& I_) {
+        const int idx = i0 + j;
+        I_.entry = idx / ipe;
+        I_.it = idx - I_.entry * ipe;
+        const int32_t* ent = p.work + (size_t)I_.entry * kWorkInts;
+        I_.e = ld_scalar(ent, 0);
+        I_.row0 = ld_scalar(ent, 1);
+        I_.n = ld_scalar(ent, 2);
+        const int e = (I_.e >= 0 && I_.e < p.E) ? I_.e : 0;
+        const size_t wcode = (size_t)e * NG * gstride + (size_t)I_.it * 16 * GB;
+        I_.g = p.qa + wcode;
+        I_.u = p.qb + wcode;
+        if (ng > 0) {
+#pragma unroll
+            for (int jj = 0; jj < SJ; ++jj) {
+                const int id2 = lane + 64 * jj;
+                const int gl = min(id2 >> 4, ng - 1), r = id2 & 15;
+                const size_t src = ((size_t)e * I + I_.it * 16 + pair_order_row<BITS>(r)) * NG + gb + gl;
+                I_.sv[0][jj] = p.sa[src]; I_.sv[1][jj] = p.ba[src];
+                I_.sv[2][jj] = p.sb[src]; I_.sv[3][jj] = p.bb[src];
+            }
+        }
+    };
+    auto stage = [&](const Item& I_, float* dst_base) {
+#pragma unroll
+        for (int jj = 0; jj < SJ; ++jj) {
+            const int id2 = lane + 64 * jj;
+            const int gl = id2 >> 4, r = id2 & 15;
+            if (gl < ng) {
+                const float s1 = f16_bits_to_f32(I_.sv[0][jj]), b1 = f16_bits_to_f32(I_.sv[1][jj]);
+                const float s2 = f16_bits_to_f32(I_.sv[2][jj]), b2 = f16_bits_to_f32(I_.sv[3][jj]);
+                float* dst = dst_base + gl * 64 + r;
+                dst[0] = s1 * kInvLever<BITS>;
+                dst[16] = fmaf(-kOffset<BITS>, s1, b1);
+                dst[32] = s2 * kInvLever<BITS>;
+                dst[48] = fmaf(-kOffset<BITS>, s2, b2);
+            }
+        }
+    };
+    // the entry's x rows into the tile, in pair order (all threads)
+    auto stage_x = [&](int entry) {
+        const int32_t* ent = p.work + (size_t)entry * kWorkInts;
+        const int n = max(0, min(ld_scalar(ent, 2), rows_cap));
+        constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;
+        constexpr int RUN = BITS == 4 ? 8 : 16;           // elements per permuted run
+        const int runs = H / RUN;
+        for (int idx = tid; idx < n * runs; idx += NT) {
+            const int t = idx / runs, c = idx - t * runs;
+            int tok = ent[4 + t];
+            tok = (tok >= 0 && tok < p.T) ? tok : 0;
+            const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * H + c * RUN);
+            uint4* dst = reinterpret_cast<uint4*>(xt + t * xrow + c * RUN);
+            if constexpr (BITS == 4) {
+                const uint4 v = src[0];                   // (x0,x1) (x2,x3) (x4,x5) (x6,x7)
+                dst[0] = make_uint4(__builtin_amdgcn_perm(v.z, v.x, LO), __builtin_amdgcn_perm(v.z, v.x, HI),
+                                    __builtin_amdgcn_perm(v.w, v.y, LO), __builtin_amdgcn_perm(v.w, v.y, HI));
+            } else {
+                const uint4 a = src[0], b = src[1];       // (x0,x1) .. (x6,x7), (x8,x9) .. (x14,x15)
+                dst[0] = make_uint4(__builtin_amdgcn_perm(b.x, a.x, LO), __builtin_amdgcn_perm(b.x, a.x, HI),
+                                    __builtin_amdgcn_perm(b.y, a.y, LO), __builtin_amdgcn_perm(b.y, a.y, HI));
+                dst[1] = make_uint4(__builtin_amdgcn_perm(b.z, a.z, LO), __builtin_amdgcn_perm(b.z, a.z, HI),
+                                    __builtin_amdgcn_perm(b.w, a.w, LO), __builtin_amdgcn_perm(b.w, a.w, HI));
+            }
+        }
+        // X of row t, group g: the float32 sum of its 128 elements in order
+        for (int idx = tid; idx < n * NG; idx += NT) {
+            const int t = idx / NG, g = idx - t * NG;
+            int tok = ent[4 + t];
+            tok = (tok >= 0 && tok < p.T) ? tok : 0;
+            const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * H + g * kGroup);
+            float sum = 0.f;
+            for (int c = 0; c < kGroup / 8; ++c) {
+                const uint4 v = src[c];
+                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    sum += __uint_as_float(wv[e2] << 16);
+                    sum += __uint_as_float(wv[e2] & 0xFFFF0000u);
+                }
+            }
+            xs[t * NG + g] = sum;
+        }
+    };
+
+    uint32_t wg[D][LW], wu[D][LW];
+    auto issue = [&](int slot, const uint8_t* gp, const uint8_t* up, int g) {
+        const gbytes_t gq = uniform_gptr(gp + (size_t)g * gstride);
+        const gbytes_t uq = uniform_gptr(up + (size_t)g * gstride);
+        if constexpr (BITS == 4) {
+            const u32x4_t A = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t>(gq + loff));
+            const u32x4_t B = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t>(uq + loff));
+            wg[slot][0] = A.x; wg[slot][1] = A.y; wg[slot][2] = A.z; wg[slot][3] = A.w;
+            wu[slot][0] = B.x; wu[slot][1] = B.y; wu[slot][2] = B.z; wu[slot][3] = B.w;
+        } else {
+            const u32x2_t A = *reinterpret_cast<gu32x2_t>(gq + loff);
+            const u32x2_t B = *reinterpret_cast<gu32x2_t>(uq + loff);
+            wg[slot][0] = A.x; wg[slot][1] = A.y;
+            wu[slot][0] = B.x; wu[slot][1] = B.y;
+        }
+    };
+
+    Item cur, nxt;
+    fetch(0, cur);
+    const int NGP = (NGW + D - 1) / D * D;
+    auto gaddr = [&](int gl) { return gb + max(0, min(gl, ng - 1)); };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, cur.g, cur.u, gaddr(d));
+    stage(cur, sc_base);
+    for (int i = tid; i < xrow / 8; i += NT)
+        reinterpret_cast<uint4*>(xt + rows_cap * xrow)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < NG; i += NT) xs[rows_cap * NG + i] = 0.f;
+    stage_x(cur.entry);
+    lds_barrier();
+
+    for (int j = 0; j < n_my; ++j) {
+        const bool has_next = j + 1 < n_my;
+        if (has_next) fetch(j + 1, nxt);
+        else nxt = cur;
+        const float* my_sc = sc_base + (j & 1) * NGW * 64;
+        const int xr = m < cur.n ? m : rows_cap;
+        const uint16_t* xcol = xt + xr * xrow + 32 * q;
+        const float* xsum = xs + xr * NG + gb;
+        floatx4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+        int g0 = 0;
+        do {
+            const bool last = g0 + D >= NGP;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int gl = g0 + d;
+                if (gl < ng) {
+                    floatx4_t Cg = {0.f, 0.f, 0.f, 0.f}, Cu = Cg;
+                    const uint16_t* xg = xcol + (gb + gl) * kGroup;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        uint32_t Ag[4], Au[4];
+                        code_operand<BITS>(wg[d], s, Ag);
+                        code_operand<BITS>(wu[d], s, Au);
+                        const uint4 X = *reinterpret_cast<const uint4*>(xg + 8 * s);
+                        const uint32_t Bx[4] = {X.x, X.y, X.z, X.w};
+                        Cg = mfma16(Ag, Bx, Cg);
+                        Cu = mfma16(Au, Bx, Cu);
+                    }
+                    const float Xg = xsum[gl];
+                    const float* scg = my_sc + gl * 64 + 4 * q;
+                    const float4 sg = *reinterpret_cast<const float4*>(scg);
+                    const float4 bg = *reinterpret_cast<const float4*>(scg + 16);
+                    const float4 su = *reinterpret_cast<const float4*>(scg + 32);
+                    const float4 bu = *reinterpret_cast<const float4*>(scg + 48);
+                    accg[0] = fmaf(sg.x, Cg[0], fmaf(bg.x, Xg, accg[0]));
+                    accg[1] = fmaf(sg.y, Cg[1], fmaf(bg.y, Xg, accg[1]));
+                    accg[2] = fmaf(sg.z, Cg[2], fmaf(bg.z, Xg, accg[2]));
+                    accg[3] = fmaf(sg.w, Cg[3], fmaf(bg.w, Xg, accg[3]));
+                    accu[0] = fmaf(su.x, Cu[0], fmaf(bu.x, Xg, accu[0]));
+                    accu[1] = fmaf(su.y, Cu[1], fmaf(bu.y, Xg, accu[1]));
+                    accu[2] = fmaf(su.z, Cu[2], fmaf(bu.z, Xg, accu[2]));
+                    accu[3] = fmaf(su.w, Cu[3], fmaf(bu.w, Xg, accu[3]));
+                }
+                // consume slot d, then refill the same registers (a scheduling
+                // barrier keeps the refill after the use and in ring order)
+                __builtin_amdgcn_sched_barrier(0);
+                const bool go_next = last && has_next;
+                issue(d, go_next ? nxt.g : cur.g, go_next ? nxt.u : cur.u,
+                      gaddr(!last ? gl + D : (has_next ? d : ng - 1)));
+            }
+            g0 += D;
+        } while (g0 < NGP);
+
+        // ---- the NW waves' partials meet in LDS; waves ew..ew+3 finish the
+        // item: wave ew + w takes token columns 4w..4w+3, lane v = 64 w + lane
+        // holds column v / 16, rows 4 ((v / 4) % 4) + v % 4 of the 16-row tile
+        float* redb = red + (j & 1) * (NW * 64 * 8);
+        float* mine = redb + (w * 64 + lane) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { mine[i] = accg[i]; mine[4 + i] = accu[i]; }
+        lds_barrier();
+        const int ew = (NW >= 8 && (j & 1)) ? 4 : 0;
+        if (w >= ew && w < ew + 4) {
+            const int v = (w - ew) * 64 + lane, mc = v >> 4, qc = (v >> 2) & 3, ic = v & 3;
+            const int src = (qc * 16 + mc) * 8 + ic;      // the MFMA lane (qc, mc), value ic
+            float gt = redb[src], upv = redb[src + 4];
+            for (int w2 = 1; w2 < NW; ++w2) {
+                gt += redb[w2 * 64 * 8 + src];
+                upv += redb[w2 * 64 * 8 + src + 4];
+            }
+            const float hv = gt / (1.f + expf(-gt)) * upv;
+            // sum of h over the tile's 16 rows for this token (fixed order)
+            float part = hv + __shfl_xor(hv, 1, kWave);
+            part += __shfl_xor(part, 2, kWave);
+            part += __shfl_xor(part, 4, kWave);
+            part += __shfl_xor(part, 8, kWave);
+            if (mc < cur.n && cur.row0 >= 0 && cur.row0 + cur.n <= p.P) {
+                const int r = cur.row0 + mc;
+                if ((v & 15) == 0) p.hpart[(size_t)r * (I / 16) + cur.it] = part;
+                uint32_t hi, mid, lo;
+                split3_bf16(hv, hi, mid, lo);
+                const size_t plane = (size_t)p.P * I;
+                uint16_t* base = p.hp + (size_t)r * I + cur.it * 16 + 4 * qc + ic;
+                base[0] = (uint16_t)hi;
+                base[plane] = (uint16_t)mid;
+                base[2 * plane] = (uint16_t)lo;
+            }
+        }
+        if (has_next) {
+            stage(nxt, sc_base + ((j + 1) & 1) * NGW * 64);
+            // past the barrier above every wave is done with the old x rows
+            if (nxt.entry != cur.entry) {
+                stage_x(nxt.entry);
+                lds_barrier();
+            }
+        }
+        cur = nxt;
+    }
+}
+
 // ------------------------------------------------------------------- down
 // Persistent like gate/up.  The 4 waves form 4/KS row tiles of 32 output rows
 // times KS parts of K: with a short K (I / 128 small) each wave keeps several
@@ -591,6 +878,58 @@ static void down_dispatch(int D, int SJ, int KS, const moe_dims& d, size_t lds, 
     }
 }
 
+// The x-tile gate/up kernel: waves per workgroup (one workgroup per CU), the
+// LDS it needs, and its launch.
+constexpr int kXtWaves = 8;
+constexpr size_t kXtLdsLimit = 160 * 1024;
+
+static size_t xt_lds_bytes(const moe_dims& d, int nw) {
+    const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
+    const int NG = d.H / kGroup, NGW = (NG + nw - 1) / nw;
+    const size_t xb = ((size_t)(rows_cap + 1) * (d.H + 8) * 2 + 15) & ~(size_t)15;
+    const size_t xsb = (size_t)(((rows_cap + 1) * NG + 3) & ~3) * sizeof(float);
+    return xb + xsb + ((size_t)nw * 2 * NGW * 64 + (size_t)2 * nw * 64 * 8) * sizeof(float);
+}
+
+template <int BITS, int D, int SJ, int NW>
+static void xt_launch(size_t lds, hipStream_t s, const MfmaParams& p) {
+    hipLaunchKernelGGL((ffn_gateup_xt_kernel<BITS, D, SJ, NW>), dim3((unsigned)device_cus()), dim3(64 * NW), lds, s, p);
+}
+
+template <int BITS, int SJ, int NW>
+static void xt_depth(int D, size_t lds, hipStream_t s, const MfmaParams& p) {
+    switch (D) {
+        case 8: xt_launch<BITS, 8, SJ, NW>(lds, s, p); break;
+        case 6: xt_launch<BITS, 6, SJ, NW>(lds, s, p); break;
+        case 5: xt_launch<BITS, 5, SJ, NW>(lds, s, p); break;
+        case 4: xt_launch<BITS, 4, SJ, NW>(lds, s, p); break;
+        case 3: xt_launch<BITS, 3, SJ, NW>(lds, s, p); break;
+        case 2: xt_launch<BITS, 2, SJ, NW>(lds, s, p); break;
+        default: xt_launch<BITS, 1, SJ, NW>(lds, s, p); break;
+    }
+}
+
+template <int BITS, int NW>
+static void xt_dispatch(int D, int SJ, size_t lds, hipStream_t s, const MfmaParams& p) {
+    if (SJ <= 1) xt_depth<BITS, 1, NW>(D, lds, s, p);
+    else xt_depth<BITS, 2, NW>(D, lds, s, p);
+}
+
+// Ring depth of the x-tile kernel: the deepest of 8, 6, 5, 4, 3, 2 that pads a
+// wave's groups by at most a quarter.  With a wave's whole share of K in its
+// ring, each workgroup keeps the next item's codes in flight while it computes
+// the current one, which is what keeps this HBM busy (about 2.5 us per round
+// trip under load against about 2 us of arithmetic per item).
+static int xt_depth_for(int NG, int nw) {
+    const int NGW = (NG + nw - 1) / nw;
+    for (int d : {8, 6, 5, 4, 3, 2}) {
+        if (d > NGW) continue;
+        const int ngp = (NGW + d - 1) / d * d;
+        if (4 * ngp <= 5 * NGW) return d;
+    }
+    return 1;
+}
+
 int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
@@ -604,6 +943,17 @@ int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     const SplitSpace sp = down_split_space(d, a.h);
     p.split_ctr = sp.ctr;
     p.n_split_ctr = sp.n_ctr;
+    {
+        const int NG = d.H / kGroup, NGW = (NG + kXtWaves - 1) / kXtWaves;
+        const int SJ = (16 * NGW + 63) / 64;
+        const size_t lds = xt_lds_bytes(d, kXtWaves);
+        if (SJ <= 2 && lds <= kXtLdsLimit) {
+            const int D = xt_depth_for(NG, kXtWaves);
+            if (a.bits == 4) xt_dispatch<4, kXtWaves>(D, SJ, lds, s, p);
+            else xt_dispatch<2, kXtWaves>(D, SJ, lds, s, p);
+            return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        }
+    }
     const int NG = d.H / kGroup, NGW = (NG + kWaves - 1) / kWaves;
     const int SJ = (16 * NGW + 63) / 64;
     if (SJ > 4) return MOE_ERR_UNSUPPORTED;

@@ -26,7 +26,6 @@
 #include "mfma_ops.h"
 
 namespace moe {
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -719,20 +718,23 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
         }
     };
 
-    // ---- code ring: RT rows of this lane, groups clamped to [ga, gb)
+    // ---- code ring: RT rows of this lane, groups clamped to [ga, gb); a
+    // group's codes of the wave's rows start at a uniform base (scalar-base
+    // loads, the lane's offset in one VGPR)
     const size_t gstride = (size_t)H * (4 * LB);
-    const uint8_t* cp = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + rloc) * (4 * LB) + q * LB;
+    const uint8_t* cbase = p.qa + (size_t)it.e * NG * gstride + ((size_t)it.rb * RI + 16 * RT * wid) * (4 * LB);
+    const uint32_t clane = (uint32_t)(m * (4 * LB) + q * LB);
     uint32_t rc[D][RT][LW];
     auto issue = [&](int slot, int g) {
-        const size_t off = (size_t)min(max(g, ga), gb - 1) * gstride;
+        const gbytes_t src0 = uniform_gptr(cbase + (size_t)min(max(g, ga), gb - 1) * gstride);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const uint8_t* src = cp + (size_t)(16 * rt) * (4 * LB) + off;
+            const gbytes_t src = src0 + clane + (16 * rt) * (4 * LB);
             if constexpr (BITS == 4) {
-                const u32x4_t A = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+                const u32x4_t A = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t>(src));
                 rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y; rc[slot][rt][2] = A.z; rc[slot][rt][3] = A.w;
             } else {
-                const uint2 A = *reinterpret_cast<const uint2*>(src);
+                const u32x2_t A = *reinterpret_cast<gu32x2_t>(src);
                 rc[slot][rt][0] = A.x; rc[slot][rt][1] = A.y;
             }
         }

@@ -45,8 +45,6 @@ namespace moe {
 // are summed in LDS in a fixed wave order, then wave 0 runs the epilogue.
 constexpr int kWaves = 4;
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
 struct MfmaParams {
     const uint16_t* x;
     const int32_t* work;        // work list entries (kWorkInts int32 each)
@@ -305,22 +303,6 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
 // LDS: x tile [rows_cap + 1][H + 8] bf16 (the last row zero); group sums
 // [rows_cap + 1][NG] float (the last row zero); scales [NW][2][NGW][64] float
 // (by item parity); partial sums [2][NW][64][8] float.
-// A wave-uniform global pointer, passed through readfirstlane so that the
-// compiler keeps it whole: a load at uniform_gptr(base) + (32-bit lane offset)
-// then takes the scalar-base form (base in SGPRs, offset in one VGPR) instead
-// of 64-bit per-lane address arithmetic.
-typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
-typedef const __attribute__((address_space(1))) u32x4_t* gu32x4_t;
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(1))) u32x2_t* gu32x2_t;
-
-__device__ __forceinline__ gbytes_t uniform_gptr(const uint8_t* p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<gbytes_t>(((uint64_t)hi << 32) | lo);
-}
-
 template <int BITS, int D, int SJ, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p) {
     static_assert(NW >= 4, "four waves share the epilogue");

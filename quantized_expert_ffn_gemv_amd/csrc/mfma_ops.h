@@ -103,6 +103,23 @@ __device__ __forceinline__ int pair_order_row(int m) {
     else return (m >> 1) + 8 * (m & 1);                                           // 0,8,1,9,...,7,15
 }
 
+// A wave-uniform global pointer, passed through readfirstlane so that the
+// compiler keeps it whole: a load at uniform_gptr(base) + (32-bit lane offset)
+// then takes the scalar-base form (base in SGPRs, offset in one VGPR) instead
+// of 64-bit per-lane address arithmetic.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4_t* gu32x4_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) u32x2_t* gu32x2_t;
+
+__device__ __forceinline__ gbytes_t uniform_gptr(const uint8_t* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<gbytes_t>(((uint64_t)hi << 32) | lo);
+}
+
 // ------------------------------------------------- direct-to-LDS staging
 
 constexpr int kDma = 1024;          // bytes one wave moves with one direct-to-LDS load

@@ -18,8 +18,11 @@ grouped GEMM (matrix-core utilisation).
 Successive steps cycle through independently generated weight sets (like the
 layers of a model), and each weight set has its own activations, so a step
 finds neither its weights nor its routing in the 256 MB last-level cache from
-the step before.  Inputs are resident in HBM before a timed region starts; the
-timed steps are eager library calls.
+the step before.  Inputs are resident in HBM before a timed region starts.
+The layer steps are timed twice: as eager library calls, and as replays of one
+HIP graph per weight set (the whole step captured once: the same kernels and
+work, without the host's per-call launch cost); tokens/s is the faster of the
+two, and both are in the line (eager_*, graph_*, `launch` names the one used).
 
 Per workload:
   tokens/s      T * K / elapsed over K steps back to back (HIP events on the
@@ -255,6 +258,26 @@ class Runner:
         self.check_counters("layer steps")
         return ms
 
+    def capture(self):
+        """One HIP graph per weight set: that set's whole layer step (routing,
+        FFN, combine) captured once (after eager steps); a replay redoes all of
+        it on the resident inputs, without the host's per-call launch cost."""
+        torch = self.torch
+        self.graphs = []
+        for li in range(len(self.layers)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(li)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def timed_graph_steps(self, steps, warmup):
+        """Total ms of `steps` layer steps as graph replays (weight sets in turn)."""
+        n = len(self.graphs)
+        ms = self._timed(lambda i: self.graphs[i % n].replay(), steps, warmup)
+        self.check_counters("graph steps")
+        return ms
+
     def timed_ffn(self, steps, warmup):
         """Mean us of one expert FFN call: every weight set routed once into its
         own buffers, then `steps` FFN calls back to back over the weight sets in
@@ -439,7 +462,11 @@ def measure_decode(ctx, name, bits, T, sets, n_cpu, steps, warmup, algo, with_cp
         torch.cuda.synchronize()
     r = Runner(torch, mi, moe, shape, layers, T, algo)
     U = r.experts_used()
-    total_ms = r.timed_steps(steps, warmup)
+    eager_ms = r.timed_steps(steps, warmup)
+    r.capture()
+    graph_ms = r.timed_graph_steps(steps, warmup)
+    total_ms = min(eager_ms, graph_ms)
+    launch = "one HIP graph per layer step (routing, FFN, combine), replayed" if graph_ms < eager_ms else "eager calls"
     ffn_us = r.timed_ffn(steps, warmup)
     ffn_bytes = sum(U[i % len(U)] for i in range(steps)) / steps * per_expert
     stream_us = stream_ceiling(torch, moe, ffn_bytes, steps)
@@ -450,7 +477,9 @@ def measure_decode(ctx, name, bits, T, sets, n_cpu, steps, warmup, algo, with_cp
     out = dict(
         workload=describe(shape, bits, T, sets), key=key, H=shape.H, E=shape.E, k=shape.k, I=shape.I, T=T,
         bits=bits, group=128, weight_sets=sets, algo=algo_name,
-        tokens_per_s=round(T * steps / (total_ms / 1e3), 1), ms_per_step=round(total_ms / steps, 5),
+        tokens_per_s=round(T * steps / (total_ms / 1e3), 1), ms_per_step=round(total_ms / steps, 5), launch=launch,
+        eager_tokens_per_s=round(T * steps / (eager_ms / 1e3), 1), eager_ms_per_step=round(eager_ms / steps, 5),
+        graph_tokens_per_s=round(T * steps / (graph_ms / 1e3), 1), graph_ms_per_step=round(graph_ms / steps, 5),
         experts_used_mean=sum(U) / len(U), experts_used_per_set=U,
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBPS, 4),
@@ -464,7 +493,8 @@ def measure_decode(ctx, name, bits, T, sets, n_cpu, steps, warmup, algo, with_cp
     if with_cpu and ctx["cpu"]:
         log(f"[bench] {key}: timing the CPU oracle on {n_cpu} token(s)")
         out["cpu_baseline"] = cpu_baseline(mi, shape, bits, layers[0], r.xb[0], n_cpu)
-    log(f"[bench] {key} ({algo_name}): {out['tokens_per_s']:.0f} tokens/s, {out['ms_per_step'] * 1e3:.1f} us/step, "
+    log(f"[bench] {key} ({algo_name}): {out['tokens_per_s']:.0f} tokens/s, {out['ms_per_step'] * 1e3:.1f} us/step "
+        f"(eager {out['eager_ms_per_step'] * 1e3:.1f}, graph {out['graph_ms_per_step'] * 1e3:.1f}), "
         f"FFN {ffn_us:.2f} us = {achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s, "
         f"{100 * achieved / stream_gbps:.1f}% of a {stream_gbps:.0f} GB/s plain read), U={out['experts_used_mean']:.1f}")
     del r
@@ -742,7 +772,7 @@ def main():
         del src, dst
 
     config = {k: head[k] for k in ("workload", "H", "E", "k", "I", "T", "bits", "group", "weight_sets", "algo")}
-    config.update(ffn="one call (expert_ffn_fused)", launch="eager calls", parallelism="none (one GPU)")
+    config.update(ffn="one call (expert_ffn_fused)", launch=head["launch"], parallelism="none (one GPU)")
     result = {
         "metric": "MoE-layer decode tokens/s + weight-stream HBM GB/s (% of MI355X peak)",
         "value": head["tokens_per_s"],

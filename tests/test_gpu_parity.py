@@ -474,9 +474,10 @@ def test_ffn_one_launch_matches_two_launches(name, bits, T, shape):
         assert np.array_equal(a, b), f"{int((a != b).any(axis=1).sum())} of {P} rows differ"
 
 
-@pytest.mark.parametrize("name,T", [("a3b", 8), ("a3b", 32), ("tiny", 4)])
+@pytest.mark.parametrize("name,T", [("a3b", 8), ("a3b", 32), ("tiny", 4), ("e512", 1), ("e64", 8)])
 def test_layer_step_graph_replay(name, T):
-    """A layer step (one-launch routing, one-launch FFN, combine) captured in a
+    """A layer step (one-launch routing, the FFN (one launch, or the x-tile
+    gate/up and the streaming down at the 64-expert shape), combine) captured in a
     HIP graph and replayed three times, with eager work and synchronisations
     between the replays and new activations copied into the captured input
     buffer each time: every replay matches an eager run on the same input bit

@@ -295,17 +295,18 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaParams p) {
 // D-deep register ring per wave that runs across item boundaries.  The NW
 // waves split K as in the kernel above; the partial sums meet in LDS, and
 // four waves share the epilogue (each takes four token columns), adding the
-// partials in wave order; with eight or more waves the two halves take turns
-// by item parity, so that neither half falls behind the other.  The partial sums are double-buffered by item
+// partials in wave order; the groups of four waves take turns by item, so
+// that none falls behind the others.  The partial sums are double-buffered by item
 // parity, so an item costs one barrier.  Token columns past the tile's rows
 // read one row of zeros.  Rows of the x tile are padded by 16 bytes, so the 16
 // rows one step reads fall in 16 different bank groups.
 // LDS: x tile [rows_cap + 1][H + 8] bf16 (the last row zero); group sums
-// [rows_cap + 1][NG] float (the last row zero); scales [NW][2][NGW][64] float
-// (by item parity); partial sums [2][NW][64][8] float.
+// [rows_cap + 1][NG] float (the last row zero); scales [NW][NGW][64] float (a
+// wave reads only its own, and stages the next item's once its K loop is
+// done); partial sums [2][NW][64][8] float.
 template <int BITS, int D, int SJ, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p) {
-    static_assert(NW >= 4, "four waves share the epilogue");
+    static_assert(NW >= 4 && NW % 4 == 0, "groups of four waves share the epilogue");
     constexpr int LB = 128 * BITS / 8 / 4;     // bytes per lane per group (16 or 8)
     constexpr int LW = LB / 4;                 // code words per lane per group
     constexpr int NT = 64 * NW;
@@ -329,8 +330,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p)
     uint16_t* xt = reinterpret_cast<uint16_t*>(smem);
     float* xs = reinterpret_cast<float*>(smem + (((size_t)(rows_cap + 1) * xrow * 2 + 15) & ~(size_t)15));
     float* sc_all = xs + (((rows_cap + 1) * NG + 3) & ~3);
-    float* sc_base = sc_all + w * 2 * NGW * 64;
-    float* red = sc_all + NW * 2 * NGW * 64;
+    float* sc_base = sc_all + w * NGW * 64;
+    float* red = sc_all + NW * NGW * 64;
 
     // a lane's codes of group g: base + g * gstride + loff (base uniform)
     const uint32_t loff = (uint32_t)(pair_order_row<BITS>(m) * GB + q * LB);
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p)
         const bool has_next = j + 1 < n_my;
         if (has_next) fetch(j + 1, nxt);
         else nxt = cur;
-        const float* my_sc = sc_base + (j & 1) * NGW * 64;
+        const float* my_sc = sc_base;
         const int xr = m < cur.n ? m : rows_cap;
         const uint16_t* xcol = xt + xr * xrow + 32 * q;
         const float* xsum = xs + xr * NG + gb;
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) { mine[i] = accg[i]; mine[4 + i] = accu[i]; }
         lds_barrier();
-        const int ew = (NW >= 8 && (j & 1)) ? 4 : 0;
+        const int ew = 4 * (j % (NW / 4));
         if (w >= ew && w < ew + 4) {
             const int v = (w - ew) * 64 + lane, mc = v >> 4, qc = (v >> 2) & 3, ic = v & 3;
             const int src = (qc * 16 + mc) * 8 + ic;      // the MFMA lane (qc, mc), value ic
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p)
             }
         }
         if (has_next) {
-            stage(nxt, sc_base + ((j + 1) & 1) * NGW * 64);
+            stage(nxt, sc_base);
             // past the barrier above every wave is done with the old x rows
             if (nxt.entry != cur.entry) {
                 stage_x(nxt.entry);
@@ -862,7 +863,7 @@ static void down_dispatch(int D, int SJ, int KS, const moe_dims& d, size_t lds, 
 
 // The x-tile gate/up kernel: waves per workgroup (one workgroup per CU), the
 // LDS it needs, and its launch.
-constexpr int kXtWaves = 8;
+constexpr int kXtWaves = 12;
 constexpr size_t kXtLdsLimit = 160 * 1024;
 
 static size_t xt_lds_bytes(const moe_dims& d, int nw) {
@@ -870,7 +871,7 @@ static size_t xt_lds_bytes(const moe_dims& d, int nw) {
     const int NG = d.H / kGroup, NGW = (NG + nw - 1) / nw;
     const size_t xb = ((size_t)(rows_cap + 1) * (d.H + 8) * 2 + 15) & ~(size_t)15;
     const size_t xsb = (size_t)(((rows_cap + 1) * NG + 3) & ~3) * sizeof(float);
-    return xb + xsb + ((size_t)nw * 2 * NGW * 64 + (size_t)2 * nw * 64 * 8) * sizeof(float);
+    return xb + xsb + ((size_t)nw * NGW * 64 + (size_t)2 * nw * 64 * 8) * sizeof(float);
 }
 
 template <int BITS, int D, int SJ, int NW>

@@ -77,6 +77,9 @@ FFN_SOURCES = {
     "a3b": ("ffn_dec.hip", "mfma_ops.h", "common.h"),
     "e512": ("ffn_dec.hip", "mfma_ops.h", "common.h"),
 }
+# the grouped GEMM's kernels and sources (its counter summary is valid for these)
+GEMM_KERNELS = ("ffn_gateup_gemm_kernel", "ffn_down_gemm_kernel")
+GEMM_SOURCES = ("ffn_gemm.hip", "mfma_ops.h", "common.h")
 CSRC = os.path.join(ROOT, "quantized_expert_ffn_gemv_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -107,6 +110,8 @@ def parse():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the runs, copy a buffer of this many MiB device to device 5 times "
                          "(the known-size kernel that scales the HBM byte counters)")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="write profiles/gemm_prefill_T4096_mfma.json from a rocprofv3 --pmc MfmaUtil folder")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                          "'bench.py --only W --copy-calib-mib N' into the traffic record of W under profiles/")
@@ -359,6 +364,44 @@ def _counter_rows(d):
             for r in csv.DictReader(f):
                 out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
     return out
+
+
+MFMA_RECORD = "gemm_prefill_T4096_mfma.json"
+
+
+def summarize_mfma(d):
+    """Mean rocprofv3 `MfmaUtil` (matrix-core busy cycles summed over the SIMDs
+    over the GPU's active cycles times the SIMD count, percent) per grouped-GEMM
+    kernel, into profiles/gemm_prefill_T4096_mfma.json."""
+    import statistics
+    rows = _counter_rows(d)
+    per = {}
+    for k in GEMM_KERNELS:
+        vals = [v for kn, c, v in rows if c == "MfmaUtil" and k in kn]
+        if vals:
+            per[k] = dict(mfma_util_pct=round(statistics.mean(vals), 3), dispatches=len(vals))
+    rec = dict(workload="prefill layer T=4096 (bench.py --prefill-only)", per_kernel=per,
+               counter="MfmaUtil = sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMD_NUM) * 100",
+               sources=list(GEMM_SOURCES), source_sha256_16=source_hash(GEMM_SOURCES),
+               command='rocprofv3 --kernel-include-regex "ffn_(gateup|down)_gemm" --pmc MfmaUtil -d <dir> -o run '
+                       '--output-format csv -- python3 bench.py --prefill-only --prefill-steps 3')
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, MFMA_RECORD), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def mfma_record():
+    """The committed MfmaUtil summary of the grouped GEMM, if taken on the current sources."""
+    path = os.path.join(PROFILES, MFMA_RECORD)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(GEMM_SOURCES):
+        return None
+    return {k: v["mfma_util_pct"] / 100.0 for k, v in rec.get("per_kernel", {}).items()}
 
 
 def summarize_counters(fetch_dir, write_dir, copy_mib, only):
@@ -702,8 +745,11 @@ def measure_prefill(ctx, steps, warmup):
                ffn_tflops=round((gate_flop + down_flop) / (g_s + d_s) / 1e12, 1),
                gateup_tflops=round(gate_flop / g_s / 1e12, 1), down_tflops=round(down_flop / d_s / 1e12, 1),
                mfma_util=round(util, 4), mfma_peak_tflops=MFMA_BF16_PEAK_TFLOPS,
-               note="useful FFN flops (2*T*k*3*H*I) over the two GEMM kernels' time, each timed over the steps "
-                    "back to back")
+               mfma_busy_counter=mfma_record(),
+               note="mfma_util: useful FFN flops (2*T*k*3*H*I) over the two GEMM kernels' time, each timed over "
+                    "the steps back to back, against the dense bf16 peak; mfma_busy_counter: the fraction of "
+                    "cycles the matrix cores were busy per kernel (rocprofv3 MfmaUtil, "
+                    "profiles/gemm_prefill_T4096_mfma.json; null when taken on other sources)")
     log(f"[bench] prefill: {out['tokens_per_s']:.0f} tokens/s, FFN {out['ffn_tflops']} TFLOP/s "
         f"({100 * util:.1f}% of bf16 MFMA peak)")
     return out
@@ -711,6 +757,9 @@ def measure_prefill(ctx, steps, warmup):
 
 def main():
     args = parse()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
     if args.summarize_counters:
         if not args.only:
             raise SystemExit("--summarize-counters needs --only name:bits:T (the workload the counters ran)")

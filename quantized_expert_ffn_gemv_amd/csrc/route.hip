@@ -1,6 +1,7 @@
 // Router logits and top-k gating (Betelgeuse page, MoE primer: the router
 // scores every expert from the token's hidden state and only the k best run;
 // gates are a softmax renormalised over the k picked).
+#include "mfma_ops.h"
 #include "router_ops.h"
 #include "topk_ops.h"
 
@@ -99,6 +100,98 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t* __res
     }
 }
 
+// Prefill shapes on the matrix cores (v_mfma_f32_16x16x4f32, float32
+// operands: x converted exactly from bf16, Wr as given): a workgroup of 4
+// waves owns 32 tokens x 32 experts, each wave a 16 x 16 tile; K runs in
+// chunks of 64 staged through LDS k-major (so that the 16 lanes of an operand
+// read 16 consecutive words), with the global loads of the next RM_P chunks in
+// flight in registers (one chunk's arithmetic is far shorter than a round
+// trip).  Four accumulators (k steps taken in turn) keep four independent
+// MFMA chains in flight; they are added in a fixed order at the end.  Lane
+// layout: A lane l row l % 16, k = l / 16; B column l % 16, the
+// same k; D rows 4 (l / 16) + i of column l % 16.
+constexpr int RM_T = 32, RM_E = 32, RM_K = 64, RM_P = 6;
+// Words per LDS row: 49, so that the 8 lanes of a staging write (one column,
+// k rows 8 apart) fall in 8 different banks; an operand read (16 columns of 4
+// k rows) then meets at most one doubled bank.
+constexpr int RM_ROW = 49;
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ logits, int T, int H, int E) {
+    __shared__ float xs[2][RM_K][RM_ROW];                     // two buffers: one barrier per chunk
+    __shared__ float ws[2][RM_K][RM_ROW];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int t0 = blockIdx.x * RM_T, e0 = blockIdx.y * RM_E;
+    // staging: thread tid loads 8 k of one token row (16 bytes of bf16) and of
+    // one expert row (32 bytes of float)
+    const int sr = tid >> 3, sk = (tid & 7) * 8;               // row 0..31, k 0..56
+    const int st = min(t0 + sr, T - 1), se = min(e0 + sr, E - 1);
+    const uint16_t* xsrc = x + (size_t)st * H + sk;
+    const float* wsrc = w + (size_t)se * H + sk;
+    const int NC = H / RM_K;
+    uint4 xr[RM_P];
+    float4 wr[RM_P][2];
+    auto load = [&](int slot, int c) {
+        xr[slot] = *reinterpret_cast<const uint4*>(xsrc + c * RM_K);
+        wr[slot][0] = *reinterpret_cast<const float4*>(wsrc + c * RM_K);
+        wr[slot][1] = *reinterpret_cast<const float4*>(wsrc + c * RM_K + 4);
+    };
+    auto put = [&](int slot, int buf) {
+        const uint32_t xw[4] = {xr[slot].x, xr[slot].y, xr[slot].z, xr[slot].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xs[buf][sk + 2 * i][sr] = bf16_bits_to_f32(xw[i] & 0xFFFFu);
+            xs[buf][sk + 2 * i + 1][sr] = bf16_bits_to_f32(xw[i] >> 16);
+        }
+        ws[buf][sk + 0][sr] = wr[slot][0].x; ws[buf][sk + 1][sr] = wr[slot][0].y;
+        ws[buf][sk + 2][sr] = wr[slot][0].z; ws[buf][sk + 3][sr] = wr[slot][0].w;
+        ws[buf][sk + 4][sr] = wr[slot][1].x; ws[buf][sk + 5][sr] = wr[slot][1].y;
+        ws[buf][sk + 6][sr] = wr[slot][1].z; ws[buf][sk + 7][sr] = wr[slot][1].w;
+    };
+#pragma unroll
+    for (int j = 0; j < RM_P; ++j)
+        if (j < NC) load(j, j);
+    const int m = lane & 15, kq = lane >> 4;
+    const int wt = (wv >> 1) * 16, we = (wv & 1) * 16;        // this wave's tile in the workgroup's
+    floatx4_t acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc[a] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    put(0, 0);
+    __syncthreads();
+    if (RM_P < NC) load(0, RM_P);
+    for (int c0 = 0; c0 < NC; c0 += RM_P) {
+#pragma unroll
+        for (int j = 0; j < RM_P; ++j) {
+            // chunk c is in buffer c & 1; chunk c + 1 waits in slot (j + 1) % RM_P
+            const int c = c0 + j;
+            if (c >= NC) break;
+            const int buf = c & 1;
+#pragma unroll
+            for (int kk = 0; kk < RM_K; kk += 4)
+                acc[(kk >> 2) & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[buf][kk + kq][wt + m],
+                                                                         ws[buf][kk + kq][we + m],
+                                                                         acc[(kk >> 2) & 3], 0, 0, 0);
+            if (c + 1 < NC) {
+                const int nj = (j + 1) % RM_P;
+                put(nj, buf ^ 1);                    // the other buffer: last read before the previous barrier
+                if (c + 1 + RM_P < NC) load(nj, c + 1 + RM_P);
+            }
+            __syncthreads();
+        }
+    }
+    const int e = e0 + we + m;
+    if (e < E) {
+        const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + wt + 4 * kq + i;
+            if (t < T) logits[(size_t)t * E + e] = ((acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i])) + b;
+        }
+    }
+}
+
 int launch_router_logits(const moe_dims& d, const uint16_t* x, const float* w, const float* bias,
                          float* logits, hipStream_t s) {
     if (d.T == 0) return MOE_OK;
@@ -120,6 +213,9 @@ int launch_router_logits(const moe_dims& d, const uint16_t* x, const float* w, c
             case 5: case 6: hipLaunchKernelGGL((router_gemv_kernel<2, TT, 6>), dim3((d.E + 1) / 2), dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
             default: hipLaunchKernelGGL((router_gemv_kernel<2, TT, 8>), dim3((d.E + 1) / 2), dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E); break;
         }
+    } else if (d.H % RM_K == 0) {
+        dim3 grid((d.T + RM_T - 1) / RM_T, (d.E + RM_E - 1) / RM_E);
+        hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H, d.E);
     } else {
         dim3 grid((d.T + RT_BM - 1) / RT_BM, (d.E + RT_BN - 1) / RT_BN);
         hipLaunchKernelGGL(router_tiled_kernel, grid, dim3(256), 0, s, x, w, bias, logits, d.T, d.H,

@@ -180,7 +180,10 @@ struct LookupArgs {
     uint32_t step;
 };
 
-template <bool LOOKUP>
+// R > 0: each wave first loads its whole range of ids into registers (R per
+// lane, all loads in flight at once) and walks them from there, so the two
+// passes do not wait on a load per 64 pairs; requires P <= kPermWaves * 64 * R.
+template <bool LOOKUP, int R = 0>
 __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* __restrict__ counts,
                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
                              int32_t* __restrict__ pair_to_row, int32_t* __restrict__ active,
@@ -195,10 +198,27 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
     if constexpr (LOOKUP)
         for (int e = tid; e < E; e += kBodyThreads) offs[e] = 0;
     lds_sync();
+    constexpr int RU = R > 0 ? R : 1;                   // unroll count of the two passes
+    int idr[RU];
+    if constexpr (R > 0) {
+        const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int p = p0 + lane + 64 * r;
+            idr[r] = (wid < kPermWaves && p < p1) ? ids[p] : -1;
+        }
+    }
+    auto id_at = [&](int r, int p) -> int {
+        if constexpr (R > 0) return idr[r];
+        else return ids[p];
+    };
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
-        for (int p = p0 + lane; p < p1; p += 64) {
-            const int e = ids[p];
+#pragma unroll RU
+        for (int r = 0; r < (R > 0 ? R : (p1 - p0 + 63) / 64); ++r) {
+            const int p = p0 + lane + 64 * r;
+            if (p >= p1) continue;
+            const int e = id_at(r, p);
             const bool ok = e >= 0 && e < E;
             if (ok) atomicAdd(&cnt(wid, e), 1);
             if constexpr (LOOKUP) {
@@ -272,10 +292,13 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int k, int32_t* _
 
     if (wid < kPermWaves) {
         const int p0 = wid * chunk, p1 = min(P, p0 + chunk);
-        for (int pb = p0; pb < p1; pb += 64) {
+#pragma unroll RU
+        for (int r = 0; r < (R > 0 ? R : (p1 - p0 + 63) / 64); ++r) {
+            const int pb = p0 + 64 * r;
+            if (pb >= p1) break;
             const int p = pb + lane;
             const bool live = p < p1;
-            int e = live ? ids[p] : -1;
+            int e = live ? id_at(r, p) : -1;
             const bool ok = live && e >= 0 && e < E;
             if (!ok) e = -1;
             // lanes with the same expert id: AND over the id's bits of the
@@ -431,6 +454,7 @@ __device__ void lookup_permute_wave(const int* ids, int P, int E, int k, const i
     }
 }
 
+template <int R>
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                        int k, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets,
@@ -445,15 +469,24 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     __shared__ int cnts[kMaxE];
     __shared__ int wpos[kMaxE];
     __shared__ int wsum[32];
-    permute_body<false>(ids, P, E, k, counts, offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work, cnt,
-                 offs, cnts, wpos, wsum);
+    permute_body<false, R>(ids, P, E, k, counts, offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work,
+                           cnt, offs, cnts, wpos, wsum);
 }
+
+// ids per lane held in registers by the separate-call permutation (prefill
+// sizes: T k <= 32768 pairs)
+constexpr int kPermRegIds = 64;
 
 int launch_permute(const moe_dims& d, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* sorted_pairs, int32_t* pair_to_row, int32_t* active, int32_t* n_active,
                    int32_t* work, int32_t* n_work, hipStream_t s) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, ids, d.T * d.k, d.E, d.k, counts,
-                       offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work);
+    const int P = d.T * d.k;
+    if (P <= kPermWaves * 64 * kPermRegIds)
+        hipLaunchKernelGGL(permute_kernel<kPermRegIds>, dim3(1), dim3(1024), 0, s, ids, P, d.E, d.k, counts,
+                           offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work);
+    else
+        hipLaunchKernelGGL(permute_kernel<0>, dim3(1), dim3(1024), 0, s, ids, P, d.E, d.k, counts,
+                           offsets, sorted_pairs, pair_to_row, active, n_active, work, n_work);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -294,9 +294,11 @@ int moe_expert_ffn_q2(const moe_dims* dims, const uint16_t* x, const int32_t* wo
  *     with hi + mid + lo == h to float32 precision, stored in the pair order
  *     of the matrix-core operands, followed by float32 partial sums of h over
  *     16 consecutive i [T*k][I/16]; at dims whose down projection streams h
- *     through LDS in chunks of K (a large I), then int32 arrival counters and
- *     float32 partial output sums that moe_expert_down uses as scratch: the
- *     gate/up call clears the counters and every down call leaves them clear.
+ *     through LDS in chunks of K (a large I), then int32 arrival counters,
+ *     float32 partial output sums and four int8 planes of h per group of 128
+ *     with their scale and sum, all of which moe_expert_down uses as scratch:
+ *     the gate/up call clears the counters and every down call leaves them
+ *     clear.
  * moe_expert_ffn_q4/q2 == moe_expert_gateup followed by moe_expert_down. */
 int moe_expert_gateup(const moe_dims* dims, int bits, const uint16_t* x, const int32_t* work_list,
                       const int32_t* n_work, const moe_qweights* weights, int algo, void* workspace,

@@ -205,14 +205,16 @@ int launch_down_stream(const FfnArgs& a, hipStream_t s);
 
 // The streaming down (shapes whose h tile does not fit LDS): output rows per
 // row block, and workgroups per launch (two per CU of a 256-CU device).  Its
-// arrival counters and partial sums follow the h planes in the workspace;
-// the gate/up kernels clear the counters.
+// arrival counters, partial sums and int8 planes of h follow the bf16 planes
+// in the workspace; the gate/up kernels clear the counters.
 constexpr int kStreamRows = 128;
 constexpr int kStreamWaves = 4;     // waves per workgroup, 32 rows each
 constexpr int kStreamGrid = 512;
 struct SplitSpace {
     int32_t* ctr;       // [cap][H / kStreamRows]
     float* part;        // [2 kStreamGrid][rows_cap][kStreamRows]
+    int8_t* hq;         // int8 planes of h [P][I / 128][4][128]
+    float* tab;         // their scale and group sum [P][I / 128][2]
     int n_ctr;          // 0: the down projection does not stream at these dims
 };
 size_t down_split_bytes(const moe_dims& d);

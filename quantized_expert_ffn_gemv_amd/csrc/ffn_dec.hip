@@ -60,6 +60,8 @@ struct DecParams {
     int shared_row0;    // first row of the shared expert's rows (the routed pair count)
     int32_t* split_ctr; // streaming down: arrival counters [cap][ipe] (gate/up clears them)
     float* split_part;  // streaming down: partial sums [2 G][rows_cap][RI]
+    const int8_t* hq;   // streaming down: int8 planes of h [P][I / 128][4][128]
+    const float* htab;  // streaming down: (hs, X) per row and group [P][I / 128][2]
     int n_split_ctr;    // gate/up: counters to clear (0: none)
     int split_plan_off; // streaming down: LDS offset of the work split's tables
 };
@@ -595,18 +597,20 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
 // A lane's fp16 scales and biases come straight to registers, 8 groups (16
 // bytes) per row at a time, a block of 8 groups ahead; the loop runs over
 // whole such blocks and skips the groups outside the part.
-// Packed planes: the A operand's 16 rows hold the three bf16 planes of h for
-// the tile's n tokens, plane-major (row 16 b + r is plane r' / n, token r' % n
-// for r' = 16 b + r < 3 n), so one MFMA per row tile and step covers all three
-// planes: 4 RT MFMAs per group per row block b, against 12 RT with one plane
-// per MFMA.  The group sums X of the fold come from the gate/up kernels'
-// float sums of h (a table per part); the three planes of a token are added at
-// the end, in plane order.
+// Integer planes: the products run on v_mfma_i32_16x16x64_i8 (codes as bytes
+// 0..15 or 0..3, h as four int8 planes with a power-of-two scale per row and
+// group, made by ffn_hquant_kernel), so the sum over a group is exact in
+// int32 and costs 2 MFMAs per 16-row tile for up to 4 tokens.  The A
+// operand's 16 rows are 4 tokens x 4 planes (row 4 t + p of block b is plane p
+// of token 4 b + t), so a lane's four accumulators (D rows 4 q .. 4 q + 3) are
+// the four planes of one token and fold into one float in the lane:
+// F = C0 + 2^-7 C1 + 2^-14 C2 + 2^-21 C3, y += s hs F + b X, with hs the
+// row's scale and X its float sum of h over the group.
 // Wave wid computes rows 16 RT wid .. +16 RT of the row block.  LDS: two h
-// buffers [3 n][CG][16 pieces of 16 B] (row r's pieces swizzled by r & 15,
-// like the decode tile), then the X table [groups][rows_cap rounded up to 4];
-// after the K loop the h buffers hold the packed rows' results [3 n][RI]
-// float; the work split's tables follow.
+// buffers [4 n][CG][128 B] (row r's groups swizzled by r & 1 and its 16-byte
+// pieces by (r / 2) & 7: the 16 rows one read phase touches fall on distinct
+// banks), then the (hs, X) table [groups][rows_cap rounded up to 4]; the work
+// split's tables follow.
 // Waits: a wave's loads complete in issue order.  The first chunk is waited
 // for past the scale and ring loads issued after it; every later chunk's
 // loads are issued at the start of the chunk before it, and exactly CG RT
@@ -665,6 +669,89 @@ __device__ __forceinline__ int split_slot(const SplitPlan& s, int v, int u0) {
     return 2 * v + (split_first(s, v) < u0 ? 1 : 0);
 }
 
+// ---------------------------------------------- int8 planes of h (down input)
+// For row r and group g of 128 along I: e = max(exponent(max |h|) - 5, -100),
+// hs = 2^e (so max |h| / hs lies in [32, 64)), and planes q_p in [-64, 64]:
+// q_p = rint(rem_p / 2^(e - 7 p)), rem_{p+1} = rem_p - q_p 2^(e - 7 p) (every
+// remainder exact), so h = hs (q_0 + 2^-7 q_1 + 2^-14 q_2 + 2^-21 q_3) + a
+// tail of at most 2^-22 hs.  h itself is hi + mid + lo of the bf16 planes,
+// exactly.  Layout: hq [P][NG][4][128 B], the bytes of a plane's 16-code runs
+// ordered as i8_code_operand delivers codes; tab [P][NG] of (hs, X), X the
+// float sum of h over the group (a fixed butterfly order).
+template <int BITS>
+__device__ __forceinline__ int i8_operand_byte(int kl) {
+    if constexpr (BITS == 4) return 4 * (2 * (kl >> 3) + (kl & 1)) + ((kl & 7) >> 1);
+    else return 4 * (kl & 3) + (kl >> 2);
+}
+
+// Codes of MFMA step st (16 of the lane's 32 codes of a group) as bytes: 4-bit,
+// dword d holds nibbles (d & 1) + 2 b of word 2 st + d / 2; 2-bit, dword t holds
+// crumbs t + 4 b of word st (b: byte in the dword).
+template <int BITS>
+__device__ __forceinline__ void i8_code_operand(const uint32_t* w, int st, uint32_t (&out)[4]) {
+    if constexpr (BITS == 4) {
+        const uint32_t a = w[2 * st], b = w[2 * st + 1], M = 0x0F0F0F0Fu;
+        out[0] = a & M; out[1] = (a >> 4) & M;
+        out[2] = b & M; out[3] = (b >> 4) & M;
+    } else {
+        const uint32_t a = w[st], M = 0x03030303u;
+        out[0] = a & M; out[1] = (a >> 2) & M; out[2] = (a >> 4) & M; out[3] = (a >> 6) & M;
+    }
+}
+
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int32x4_t mfma_i8(const uint32_t (&a)[4], const uint32_t (&b)[4], int32x4_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int32x4_t, a), __builtin_bit_cast(int32x4_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// One wave per (row, group); lane l takes stored positions 2 l and 2 l + 1.
+template <int BITS>
+__global__ __launch_bounds__(256) void ffn_hquant_kernel(const uint16_t* hp, int8_t* hq, float* tab, int P, int I) {
+    const int NG = I / kGroup, lane = threadIdx.x & 63;
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= P * NG) return;
+    const int r = wv / NG, g = wv - r * NG;
+    const size_t plane = (size_t)P * I, at = (size_t)r * I + (size_t)g * kGroup + 2 * lane;
+    const uint32_t a = *reinterpret_cast<const uint32_t*>(hp + at);
+    const uint32_t b = *reinterpret_cast<const uint32_t*>(hp + at + plane);
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(hp + at + 2 * plane);
+    float h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int sh = 16 * e;
+        h[e] = (bf16_bits_to_f32((a >> sh) & 0xFFFFu) + bf16_bits_to_f32((b >> sh) & 0xFFFFu)) +
+               bf16_bits_to_f32((c >> sh) & 0xFFFFu);
+    }
+    float mx = fmaxf(fabsf(h[0]), fabsf(h[1])), sum = h[0] + h[1];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        sum += __shfl_xor(sum, o, kWave);
+    }
+    const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127;
+    const int e0 = max(ex - 5, -100);
+    // stored position j of a 16-row tile holds weight row pair_order_row(j)
+    const int j0 = (2 * lane) & 15, tile = (2 * lane) >> 4;
+    int8_t* dst = hq + ((size_t)r * NG + g) * 4 * 128 + 16 * tile;
+    float rem[2] = {h[0], h[1]};
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl) {
+        const float up = ldexpf(1.f, 7 * pl - e0), dn = ldexpf(1.f, e0 - 7 * pl);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float qv = __builtin_rintf(rem[e] * up);
+            rem[e] = fmaf(-qv, dn, rem[e]);
+            dst[pl * 128 + i8_operand_byte<BITS>(pair_order_row<BITS>(j0 + e))] = (int8_t)(int)qv;
+        }
+    }
+    if (lane == 0) {
+        tab[2 * ((size_t)r * NG + g)] = ldexpf(1.f, e0);
+        tab[2 * ((size_t)r * NG + g) + 1] = sum;
+    }
+}
+
 template <int BITS, int NW, int RT, int D, int CG, int NBM>
 __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecItem& it, int ga, int gb,
                                                  uint8_t* smem, const SplitPlan& sp, int v, int u0) {
@@ -673,33 +760,31 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
     constexpr int RI = 16 * RT * NW;           // output rows of a row block
     constexpr int NT = 64 * NW;                // threads
     constexpr int U = 8;                       // groups per unrolled block: one 16-byte run of fp16 scales
-    static_assert(U % CG == 0 && U % D == 0, "chunks and ring turns must tile the block");
+    constexpr int rowb = CG * 128;             // one packed row of a chunk in LDS
+    static_assert(U % CG == 0 && U % D == 0 && CG >= 2, "chunks and ring turns must tile the block");
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.H, I = p.I, NG = I / kGroup;
-    const int n = it.n, rows3 = 3 * n;         // packed rows
-    const int NB = (rows3 + 15) / 16;          // row blocks of 16 (NB <= NBM)
-    const int rowb = CG * 256;                 // one packed row of a chunk in LDS
-    const int buf_b = (int)round_dma((size_t)3 * p.rows_cap * rowb);
+    const int n = it.n, rows4 = 4 * n;         // packed rows
+    const int NB = (n + 3) / 4;                // row blocks of 4 tokens (NB <= NBM)
+    const int buf_b = (int)round_dma((size_t)4 * p.rows_cap * rowb);
     const int g8a = ga & ~(U - 1);             // the part runs over whole blocks of U groups from here,
     const int nch = (gb - g8a + CG - 1) / CG;  // skipping groups outside [ga, gb); chunks from g8a
 
-    // ---- chunk c (groups g8a + CG c ..) of the packed h rows into buffer c & 1:
-    // piece (row r, group gl, slot cs) holds 16-byte chunk cs ^ (r & 15) of row
-    // r's group; pieces past the 3 n rows (the last 1 KB load's tail) reload
-    // row 0 into slack, and groups outside the part load its nearest group
-    const size_t plane = (size_t)p.P * I;
+    // ---- chunk c (groups g8a + CG c ..) of the packed rows into buffer c & 1;
+    // slots past the 4 n rows (the last 1 KB load's tail) reload row 0 into
+    // slack, and groups outside the part load its nearest group
     auto stage = [&](int c) {
         uint8_t* dst = smem + (size_t)(c & 1) * buf_b;
-        const int pieces = (rows3 * rowb + kDma - 1) / kDma;
+        const int pieces = (rows4 * rowb + kDma - 1) / kDma;
         for (int i = wid; i < pieces; i += NW) {
             const int slot = i * (kDma / 16) + lane;
-            const int cs = slot & 15, rest = slot >> 4, gl = rest % CG;
-            int r = rest / CG;
-            r = r < rows3 ? r : 0;
-            const int pl = r / n, j = r - pl * n;
+            int r = slot / (CG * 8);
+            const int rem = slot - r * (CG * 8);
+            r = r < rows4 ? r : 0;
+            const int gl = (rem >> 3) ^ (r & 1), pc = (rem & 7) ^ ((r >> 1) & 7);
             const int g = min(max(g8a + c * CG + gl, ga), gb - 1);
-            const uint16_t* src = p.hp + pl * plane + (size_t)(it.row0 + j) * I + (size_t)g * kGroup + 8 * (cs ^ (r & 15));
+            const int8_t* src = p.hq + (((size_t)(it.row0 + (r >> 2)) * NG + g) * 4 + (r & 3)) * 128 + 16 * pc;
             dma16(src, dst + i * kDma);
         }
     };
@@ -739,34 +824,27 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
             }
         }
     };
-    // ---- X[t][g] = sum of h over group g for token t, from the gate/up
-    // kernel's float sums over 16 consecutive i (8 per group, added in a fixed
-    // order); rows t in [n, rowsX) are zero.  It stands in for the all-ones
-    // MFMA: in the fold, a token's whole X goes with its hi plane row and the
-    // mid and lo rows get none, which gives the same sum over the planes.
+    // ---- the (hs, X) table of the part's tokens and groups; rows t in
+    // [n, rowsX) are zero
     const int rowsX = (p.rows_cap + 3) & ~3;
     const int W = ((gb + U - 1) & ~(U - 1)) - g8a;              // groups of the table (whole blocks)
-    float* xg = reinterpret_cast<float*>(smem + 2 * (size_t)buf_b);   // [W][rowsX]
-    const float* hsum = p.hpart + (size_t)it.row0 * (I / 16) + (size_t)g8a * 8;
+    float2* xg = reinterpret_cast<float2*>(smem + 2 * (size_t)buf_b);   // [W][rowsX]
+    const float2* htab = reinterpret_cast<const float2*>(p.htab) + (size_t)it.row0 * NG + g8a;
     constexpr int XPT = 4;                                     // table entries per thread per pass
-    float4 xa[XPT], xb[XPT];
+    float2 xa[XPT];
     auto x_load = [&](int base) {
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
             const int o = base + tid + NT * k, gg = o / rowsX, t = o - gg * rowsX;
             const bool ok = gg < W && t < n;
-            const float4* src = reinterpret_cast<const float4*>(hsum + (size_t)(ok ? t : 0) * (I / 16) + (ok ? gg : 0) * 8);
-            xa[k] = src[0];
-            xb[k] = src[1];
+            xa[k] = htab[(size_t)(ok ? t : 0) * NG + (ok ? gg : 0)];
         }
     };
     auto x_store = [&](int base) {
 #pragma unroll
         for (int k = 0; k < XPT; ++k) {
             const int o = base + tid + NT * k, gg = o / rowsX, t = o - gg * rowsX;
-            if (gg < W)
-                xg[o] = t < n ? ((xa[k].x + xa[k].y) + (xa[k].z + xa[k].w)) + ((xb[k].x + xb[k].y) + (xb[k].z + xb[k].w))
-                              : 0.f;
+            if (gg < W) xg[o] = t < n ? xa[k] : make_float2(0.f, 0.f);
         }
     };
     x_load(0);                                  // first, so that the waits for it do not cover the ring
@@ -782,20 +860,23 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
     wait_vmem<RT * D + 2 * RT>();              // chunk 0 (older than the scales and the ring loads)
     lds_barrier();
 
-    // packed row of this lane in block b (rows past 3 n read row 0; never stored)
-    int roff[NBM], coff[NBM][4];
+    // packed row of this lane in block b (rows past 4 n read row m & 3, a
+    // plane of token 0; never stored): its offsets for even and odd groups
+    // and for the two steps' 16-byte pieces
+    int off0[NBM], off1[NBM], pco[NBM][2];
 #pragma unroll
     for (int b = 0; b < NBM; ++b) {
-        const int r = 16 * b + m < rows3 ? 16 * b + m : 0;
-        roff[b] = r * rowb;
+        const int r = 16 * b + m < rows4 ? 16 * b + m : (m & 3);
+        off0[b] = r * rowb + 128 * (r & 1);
+        off1[b] = r * rowb + 128 * ((r & 1) ^ 1);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) coff[b][st] = 16 * ((4 * q + st) ^ (r & 15));
+        for (int st = 0; st < 2; ++st) pco[b][st] = 16 * ((2 * q + st) ^ ((r >> 1) & 7));
     }
-    floatx4_t acc[NBM][RT];
+    float acc[NBM][RT];
 #pragma unroll
     for (int b = 0; b < NBM; ++b)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[b][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) acc[b][rt] = 0.f;
 
     for (int g0 = g8a; g0 < gb; g0 += U) {
         load_scales(g0 + U, sn, bn);                     // before this block's chunk loads (the waits count after them)
@@ -804,35 +885,36 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
             const int g = g0 + u, gl = u % CG, c = (g0 - g8a) / CG + u / CG, d = u % D;
             if (gl == 0 && c + 1 < nch) stage(c + 1);           // the other buffer: its chunk was read before the last barrier
             if (g >= ga && g < gb) {                            // uniform per workgroup
-                const uint8_t* hb = smem + (size_t)(c & 1) * buf_b + gl * 256;
+                const uint8_t* hb = smem + (size_t)(c & 1) * buf_b + 128 * (gl & ~1);
+                uint32_t B[RT][2][4];
+                float sv[RT], bv[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    i8_code_operand<BITS>(rc[d][rt], 0, B[rt][0]);
+                    i8_code_operand<BITS>(rc[d][rt], 1, B[rt][1]);
+                    const uint32_t sw = (&sc[rt].x)[u >> 1], bw = (&bc[rt].x)[u >> 1];
+                    sv[rt] = f16_bits_to_f32((u & 1) ? sw >> 16 : sw & 0xFFFFu);
+                    bv[rt] = f16_bits_to_f32((u & 1) ? bw >> 16 : bw & 0xFFFFu);
+                }
 #pragma unroll
                 for (int b = 0; b < NBM; ++b) {
                     if (b < NB) {
-                        floatx4_t C[RT];
+                        int32x4_t C[RT];
 #pragma unroll
-                        for (int rt = 0; rt < RT; ++rt) C[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                        for (int rt = 0; rt < RT; ++rt) C[rt] = int32x4_t{0, 0, 0, 0};
 #pragma unroll
-                        for (int st = 0; st < 4; ++st) {
-                            const uint4 a4 = *reinterpret_cast<const uint4*>(hb + roff[b] + coff[b][st]);
+                        for (int st = 0; st < 2; ++st) {
+                            const uint4 a4 = *reinterpret_cast<const uint4*>(hb + ((gl & 1) ? off1[b] : off0[b]) + pco[b][st]);
                             const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-                            for (int rt = 0; rt < RT; ++rt) {
-                                uint32_t B[4];
-                                code_operand<BITS>(rc[d][rt], st, B);
-                                C[rt] = mfma16(A, B, C[rt]);
-                            }
+                            for (int rt = 0; rt < RT; ++rt) C[rt] = mfma_i8(A, B[rt][st], C[rt]);
                         }
-                        // X of packed rows 16 b + 4 q .. +3: the hi-plane rows' tokens, else zero
-                        floatx4_t X = {0.f, 0.f, 0.f, 0.f};
-                        if (16 * b + 4 * q < rowsX) {
-                            const float4 x4 = *reinterpret_cast<const float4*>(xg + (g - g8a) * rowsX + 16 * b + 4 * q);
-                            X = floatx4_t{x4.x, x4.y, x4.z, x4.w};
-                        }
+                        const float2 hx = xg[(g - g8a) * rowsX + 4 * b + q];   // token 4 b + q
 #pragma unroll
                         for (int rt = 0; rt < RT; ++rt) {
-                            const uint32_t sw = (&sc[rt].x)[u >> 1], bw = (&bc[rt].x)[u >> 1];
-                            fold<BITS>(acc[b][rt], C[rt], (u & 1) ? sw >> 16 : sw & 0xFFFFu,
-                                       (u & 1) ? bw >> 16 : bw & 0xFFFFu, X);
+                            const float F = fmaf(0x1p-7f, fmaf(0x1p-7f, fmaf(0x1p-7f, (float)C[rt][3], (float)C[rt][2]),
+                                                               (float)C[rt][1]), (float)C[rt][0]);
+                            acc[b][rt] = fmaf(sv[rt] * hx.x, F, fmaf(bv[rt], hx.y, acc[b][rt]));
                         }
                     }
                 }
@@ -847,37 +929,25 @@ __device__ __forceinline__ void down_stream_part(const DecParams& p, const DecIt
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) { sc[rt] = sn[rt]; bc[rt] = bn[rt]; }
     }
-
-    // ---- the packed rows' results to LDS [3 n][RI]
-    lds_barrier();                                      // the h buffers are no longer read
-    float* red = reinterpret_cast<float*>(smem);
+    // ---- lane (q, m) holds token 4 b + q of output rows rloc + 16 rt
+    if (ga == 0 && gb == NG) {                          // the whole row block: y in bf16
+        uint16_t* yb = p.y + (size_t)it.row0 * H + (size_t)it.rb * RI + rloc;
 #pragma unroll
-    for (int b = 0; b < NBM; ++b)
+        for (int b = 0; b < NBM; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * b + 4 * q + i;
-            if (b < NB && r < rows3)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) red[r * RI + rloc + 16 * rt] = acc[b][rt][i];
-        }
-    lds_barrier();
-    uint16_t* yb = p.y + (size_t)it.row0 * H + (size_t)it.rb * RI;
-    if (ga == 0 && gb == NG) {                          // the whole row block: y = hi + mid + lo in bf16
-        for (int o = tid; o < n * RI; o += NT) {
-            const int t = o / RI, col = o - t * RI;
-            const float y = (red[t * RI + col] + red[(n + t) * RI + col]) + red[(2 * n + t) * RI + col];
-            yb[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(y);
-        }
+            for (int rt = 0; rt < RT; ++rt)
+                if (b < NB && 4 * b + q < n) yb[(size_t)(4 * b + q) * H + 16 * rt] = (uint16_t)f32_to_bf16_bits(acc[b][rt]);
         return;
     }
     // a part: its sums to slot split_slot(v, u0), then the caller arrives at
     // the row block's counter
-    float* mine = p.split_part + (size_t)split_slot(sp, v, u0) * (p.rows_cap * RI);
-    for (int o = tid; o < n * RI; o += NT) {
-        const int t = o / RI, col = o - t * RI;
-        const float y = (red[t * RI + col] + red[(n + t) * RI + col]) + red[(2 * n + t) * RI + col];
-        __hip_atomic_store(mine + o, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    float* mine = p.split_part + (size_t)split_slot(sp, v, u0) * (p.rows_cap * RI) + rloc;
+#pragma unroll
+    for (int b = 0; b < NBM; ++b)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            if (b < NB && 4 * b + q < n)
+                __hip_atomic_store(mine + (4 * b + q) * RI + 16 * rt, acc[b][rt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The parts of the row block starting at unit u0: the non-empty ranges from
@@ -1059,6 +1129,8 @@ static DecParams dec_params(const FfnArgs& a) {
     const SplitSpace sp = down_split_space(d, a.h);
     p.split_ctr = sp.ctr;
     p.split_part = sp.part;
+    p.hq = sp.hq;
+    p.htab = sp.tab;
     p.n_split_ctr = sp.n_ctr;
     return p;
 }
@@ -1213,15 +1285,12 @@ int launch_down_dec(const FfnArgs& a, hipStream_t s) {
 // ------------------------------------------------------------ streaming down
 
 // Chunk of K groups staged at a time: 4, or 2 for tiles of more rows than fit
-// two buffers of 4 groups in the decode LDS limit; the buffers also hold the
-// packed rows' results at the end.  Then the X table [NG][rows_cap rounded up
-// to 4] float (the arrival flag at the end).
+// two buffers of 4 groups in the decode LDS limit.  Then the (hs, X) table
+// [NG][rows_cap rounded up to 4] of float pairs.
 static size_t down_stream_lds(const moe_dims& d, int cg) {
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
-    size_t bufs = 2 * round_dma((size_t)3 * rows_cap * cg * 256);
-    const size_t red = (size_t)3 * rows_cap * kStreamRows * sizeof(float);
-    bufs = bufs > red ? bufs : red;
-    const size_t xtab = (size_t)(d.I / kGroup) * ((rows_cap + 3) & ~3) * sizeof(float);
+    const size_t bufs = 2 * round_dma((size_t)4 * rows_cap * cg * 128);
+    const size_t xtab = (size_t)(d.I / kGroup) * ((rows_cap + 3) & ~3) * 2 * sizeof(float);
     return bufs + ((xtab + 255) & ~(size_t)255);
 }
 
@@ -1243,26 +1312,38 @@ static int down_stream_cg(const moe_dims& d) {
     return 0;
 }
 
-// Counters [cap][H / RI] and partial sums [2 G][rows_cap][RI] of the
-// streaming down, after the h planes and their partial sums in the workspace.
+// Counters [cap][H / RI], partial sums [2 G][rows_cap][RI], the int8 planes
+// of h [P][NG][4][128] and their (hs, X) table [P][NG][2] of the streaming
+// down, after the bf16 planes and their partial sums in the workspace.
+static size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 size_t down_split_bytes(const moe_dims& d) {
     if (down_stream_cg(d) == 0) return 0;
     const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
+    const size_t P = (size_t)d.T * d.k;
     const size_t ctr = work_capacity(d) * (size_t)(d.H / kStreamRows) * sizeof(int32_t);
     const size_t part = (size_t)2 * kStreamGrid * rows_cap * kStreamRows * sizeof(float);
-    return ((ctr + 255) & ~(size_t)255) + part;
+    const size_t hq = P * (size_t)d.I * 4;
+    const size_t tab = P * (size_t)(d.I / kGroup) * 2 * sizeof(float);
+    return r256(ctr) + r256(part) + r256(hq) + tab;
 }
 
 SplitSpace down_split_space(const moe_dims& d, void* ws) {
-    SplitSpace sp{nullptr, nullptr, 0};
+    SplitSpace sp{nullptr, nullptr, nullptr, nullptr, 0};
     if (down_split_bytes(d) == 0) return sp;
+    const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
     const size_t P = (size_t)d.T * d.k;
-    const size_t planes = (3 * P * d.I * sizeof(uint16_t) + 255) & ~(size_t)255;
-    const size_t part = (P * (d.I / 16) * sizeof(float) + 255) & ~(size_t)255;
-    char* base = reinterpret_cast<char*>(ws) + planes + part;
+    const size_t planes = r256(3 * P * d.I * sizeof(uint16_t));
+    const size_t hpart = r256(P * (d.I / 16) * sizeof(float));
+    char* base = reinterpret_cast<char*>(ws) + planes + hpart;
     sp.n_ctr = (int)(work_capacity(d) * (size_t)(d.H / kStreamRows));
     sp.ctr = reinterpret_cast<int32_t*>(base);
-    sp.part = reinterpret_cast<float*>(base + ((sp.n_ctr * sizeof(int32_t) + 255) & ~(size_t)255));
+    base += r256(sp.n_ctr * sizeof(int32_t));
+    sp.part = reinterpret_cast<float*>(base);
+    base += r256((size_t)2 * kStreamGrid * rows_cap * kStreamRows * sizeof(float));
+    sp.hq = reinterpret_cast<int8_t*>(base);
+    base += r256(P * (size_t)d.I * 4);
+    sp.tab = reinterpret_cast<float*>(base);
     return sp;
 }
 
@@ -1273,16 +1354,17 @@ static void ds_go(size_t lds, hipStream_t s, const DecParams& p) {
                        lds, s, p);
 }
 
-// NBM: row blocks of packed planes the tile can need, ceil(3 rows_cap / 16)
+// NBM: row blocks of 4 tokens the tile can need, ceil(rows_cap / 4)
 template <int BITS>
 static void ds_cg(int cg, size_t lds, hipStream_t s, const DecParams& p) {
-    const int nbm = (3 * p.rows_cap + 15) / 16;
+    const int nbm = (p.rows_cap + 3) / 4;
     if (cg == 4) {
         if (nbm == 1) ds_go<BITS, 4, 4, 1>(lds, s, p);
         else if (nbm == 2) ds_go<BITS, 4, 4, 2>(lds, s, p);
-        else ds_go<BITS, 4, 4, 3>(lds, s, p);
+        else if (nbm == 3) ds_go<BITS, 4, 4, 3>(lds, s, p);
+        else ds_go<BITS, 4, 4, 4>(lds, s, p);
     } else {
-        ds_go<BITS, 4, 2, 3>(lds, s, p);
+        ds_go<BITS, 4, 2, 4>(lds, s, p);
     }
 }
 
@@ -1297,8 +1379,16 @@ int launch_down_stream(const FfnArgs& a, hipStream_t s) {
     p.n_split_ctr = 0;                                    // the counters are the gate/up call's to clear
     p.split_plan_off = (int)down_stream_lds(d, cg);
     const size_t lds = down_stream_lds(d, cg) + down_stream_plan_lds(d);
-    if (a.bits == 4) ds_cg<4>(cg, lds, s, p);
-    else ds_cg<2>(cg, lds, s, p);
+    const int P = d.T * d.k, nq = P * (d.I / kGroup);
+    int8_t* hq = const_cast<int8_t*>(p.hq);
+    float* tab = const_cast<float*>(p.htab);
+    if (a.bits == 4) {
+        hipLaunchKernelGGL(ffn_hquant_kernel<4>, dim3((nq + 3) / 4), dim3(256), 0, s, p.hp, hq, tab, P, d.I);
+        ds_cg<4>(cg, lds, s, p);
+    } else {
+        hipLaunchKernelGGL(ffn_hquant_kernel<2>, dim3((nq + 3) / 4), dim3(256), 0, s, p.hp, hq, tab, P, d.I);
+        ds_cg<2>(cg, lds, s, p);
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -1394,3 +1484,4 @@ int launch_ffn_fused_dec_shared(const FfnArgs& a, int32_t* sync, hipStream_t s) 
 }
 
 }  // namespace moe
+

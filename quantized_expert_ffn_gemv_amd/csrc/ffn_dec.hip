@@ -684,28 +684,6 @@ __device__ __forceinline__ int i8_operand_byte(int kl) {
     else return 4 * (kl & 3) + (kl >> 2);
 }
 
-// Codes of MFMA step st (16 of the lane's 32 codes of a group) as bytes: 4-bit,
-// dword d holds nibbles (d & 1) + 2 b of word 2 st + d / 2; 2-bit, dword t holds
-// crumbs t + 4 b of word st (b: byte in the dword).
-template <int BITS>
-__device__ __forceinline__ void i8_code_operand(const uint32_t* w, int st, uint32_t (&out)[4]) {
-    if constexpr (BITS == 4) {
-        const uint32_t a = w[2 * st], b = w[2 * st + 1], M = 0x0F0F0F0Fu;
-        out[0] = a & M; out[1] = (a >> 4) & M;
-        out[2] = b & M; out[3] = (b >> 4) & M;
-    } else {
-        const uint32_t a = w[st], M = 0x03030303u;
-        out[0] = a & M; out[1] = (a >> 2) & M; out[2] = (a >> 4) & M; out[3] = (a >> 6) & M;
-    }
-}
-
-typedef int int32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int32x4_t mfma_i8(const uint32_t (&a)[4], const uint32_t (&b)[4], int32x4_t c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int32x4_t, a), __builtin_bit_cast(int32x4_t, b),
-                                                 c, 0, 0, 0);
-}
-
 // One wave per (row, group); lane l takes stored positions 2 l and 2 l + 1.
 template <int BITS>
 __global__ __launch_bounds__(256) void ffn_hquant_kernel(const uint16_t* hp, int8_t* hq, float* tab, int P, int I) {

@@ -555,6 +555,336 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p)
     }
 }
 
+// ------------------------------ gate / up with int8 activation planes in LDS
+// The x-tile kernel above with the products on v_mfma_i32_16x16x64_i8.  Each
+// entry's x rows are staged once as three int8 planes per group of 128 with a
+// power-of-two scale: hs = 2^e, e = max(exponent(max |x|) - 5, -100), so that
+// max |x| / hs lies in [32, 64), and q_p = rint(rem_p / 2^(e - 7 p)) with
+// rem_{p+1} = rem_p - q_p 2^(e - 7 p) (each remainder exact), i.e.
+// x = hs (q_0 + 2^-7 q_1 + 2^-14 q_2) + a tail of at most 2^-15 hs.  The codes
+// are bytes (i8_code_operand) and the B operand (columns = weight rows in
+// pair order, as the A rows of the kernel above); the A operand's 16 rows are
+// 4 tokens x (planes 0-2 and a zero row), so a lane's D rows are the planes of
+// one token and the group sum over K is exact in int32: the lane folds
+// F = C_0 + 2^-7 C_1 + 2^-14 C_2 as s hs F + b X per group (s, b: the weight
+// row's fp16 scale and bias; X: the token's float sum of x over the group).
+// Two MFMAs per 16-row tile, matrix and group for up to 4 tokens, against 8
+// in the kernel above.
+// LDS: planes [rows_cap][NG][3][128] int8 (the 16-byte pieces of plane row
+// (t, p) swizzled by (t % 4) | 4 (p / 2): the 12 rows one read phase touches
+// fall on distinct banks), a 128-byte zero row, (hs, X) [rows_cap][NG] float
+// pairs, scales [NW][NGW][16][4] float (gate s, b, up s, b of weight row m),
+// partial sums [2][NW][64][2 NBM] float.
+constexpr int kXt8Row = 3 * 128;                  // bytes of one (token, group) of the plane tile
+
+__device__ __forceinline__ int xt8_swz(int t, int pl) { return (t & 3) | ((pl >> 1) << 2); }
+
+template <int BITS, int D, int SJ, int NW, int NBM>
+__global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt8_kernel(MfmaParams p) {
+    static_assert(NW >= 4 && NW % 4 == 0, "groups of four waves share the epilogue");
+    constexpr int LB = 128 * BITS / 8 / 4;     // bytes per lane per group (16 or 8)
+    constexpr int LW = LB / 4;                 // code words per lane per group
+    constexpr int NT = 64 * NW;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, q = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ipe = p.items_per_entry;
+    if (blockIdx.x == 0)                                  // the streaming down's counters start at zero
+        for (int i = tid; i < p.n_split_ctr; i += NT) p.split_ctr[i] = 0;
+    const int n_items = ld_scalar(p.n_work, 0) * ipe;
+    const int per = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int i0 = (int)blockIdx.x * per;
+    const int n_my = min(n_items - i0, per);
+    if (n_my <= 0) return;
+    const int H = p.H, I = p.I, NG = H / kGroup, NGW = (NG + NW - 1) / NW;
+    const int rows_cap = p.T < kWorkRows ? p.T : kWorkRows;
+    const int gb = (w * NG) / NW, ng = ((w + 1) * NG) / NW - gb;
+    constexpr int GB = kGroup * BITS / 8;      // code bytes of one row in one group
+    const size_t gstride = (size_t)I * GB;     // from one group of all I rows to the next
+    uint8_t* xq = smem;
+    const int zoff = rows_cap * NG * kXt8Row;             // the zero row
+    float2* xs = reinterpret_cast<float2*>(smem + zoff + 128);
+    float* sc_all = reinterpret_cast<float*>(smem + ((zoff + 128 + rows_cap * NG * 8 + 15) & ~15));
+    float* sc_base = sc_all + w * NGW * 64;
+    float* red = sc_all + NW * NGW * 64;
+
+    // a lane's codes of group g: base + g * gstride + loff (base uniform)
+    const uint32_t loff = (uint32_t)(pair_order_row<BITS>(m) * GB + q * LB);
+    struct Item {
+        int entry, e, it, row0, n;
+        const uint8_t* g;
+        const uint8_t* u;
+        uint32_t sv[4][SJ];
+    };
+    auto fetch = [&](int j, Item& I_) {
+        const int idx = i0 + j;
+        I_.entry = idx / ipe;
+        I_.it = idx - I_.entry * ipe;
+        const int32_t* ent = p.work + (size_t)I_.entry * kWorkInts;
+        I_.e = ld_scalar(ent, 0);
+        I_.row0 = ld_scalar(ent, 1);
+        I_.n = ld_scalar(ent, 2);
+        const int e = (I_.e >= 0 && I_.e < p.E) ? I_.e : 0;
+        const size_t wcode = (size_t)e * NG * gstride + (size_t)I_.it * 16 * GB;
+        I_.g = p.qa + wcode;
+        I_.u = p.qb + wcode;
+        if (ng > 0) {
+#pragma unroll
+            for (int jj = 0; jj < SJ; ++jj) {
+                const int id2 = lane + 64 * jj;
+                const int gl = min(id2 >> 4, ng - 1), r = id2 & 15;
+                const size_t src = ((size_t)e * I + I_.it * 16 + pair_order_row<BITS>(r)) * NG + gb + gl;
+                I_.sv[0][jj] = p.sa[src]; I_.sv[1][jj] = p.ba[src];
+                I_.sv[2][jj] = p.sb[src]; I_.sv[3][jj] = p.bb[src];
+            }
+        }
+    };
+    auto stage = [&](const Item& I_, float* dst_base) {
+#pragma unroll
+        for (int jj = 0; jj < SJ; ++jj) {
+            const int id2 = lane + 64 * jj;
+            const int gl = id2 >> 4, r = id2 & 15;
+            if (gl < ng)
+                *reinterpret_cast<float4*>(dst_base + gl * 64 + 4 * r) =
+                    make_float4(f16_bits_to_f32(I_.sv[0][jj]), f16_bits_to_f32(I_.sv[1][jj]),
+                                f16_bits_to_f32(I_.sv[2][jj]), f16_bits_to_f32(I_.sv[3][jj]));
+        }
+    };
+    // the entry's x rows as int8 planes (all threads): a thread takes runs of
+    // RUN consecutive elements of one row, whose bytes are contiguous in the
+    // operand order (8 for 4-bit codes: half a 16-byte piece; 16 for 2-bit: a
+    // whole piece); the RPG threads of a group are adjacent lanes and reduce
+    // max |x| and the sum of x among themselves in a fixed butterfly order.
+    auto stage_x = [&](int entry) {
+        const int32_t* ent = p.work + (size_t)entry * kWorkInts;
+        const int n = max(0, min(ld_scalar(ent, 2), rows_cap));
+        constexpr int RUN = BITS == 4 ? 8 : 16, RPG = kGroup / RUN, V = RUN / 8;
+        constexpr int U = 4;                                    // runs per thread per pass, loads in flight together
+        const int runs = H / RUN, total = n * runs;
+        constexpr float kMagic = 12582912.f;                    // 1.5 * 2^23: adding it rounds to an integer
+        for (int base = 0; base < total; base += U * NT) {
+            uint4 v[U][V];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = base + u * NT + tid, ii = idx < total ? idx : 0;
+                const int t = ii / runs, c = ii - t * runs;
+                int tok = ent[4 + t];
+                tok = (tok >= 0 && tok < p.T) ? tok : 0;
+                const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)tok * H + c * RUN);
+#pragma unroll
+                for (int r8 = 0; r8 < V; ++r8) v[u][r8] = src[r8];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = base + u * NT + tid;          // a group's RPG lanes agree on idx < total
+                const int ii = idx < total ? idx : 0;
+                const int t = ii / runs, c = ii - t * runs, g = c / RPG, cr = c - g * RPG;
+                float xf[RUN];
+#pragma unroll
+                for (int r8 = 0; r8 < V; ++r8) {
+                    const uint32_t wv[4] = {v[u][r8].x, v[u][r8].y, v[u][r8].z, v[u][r8].w};
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        xf[8 * r8 + 2 * e2] = __uint_as_float(wv[e2] << 16);
+                        xf[8 * r8 + 2 * e2 + 1] = __uint_as_float(wv[e2] & 0xFFFF0000u);
+                    }
+                }
+                float mx = 0.f, sm = 0.f;
+#pragma unroll
+                for (int e2 = 0; e2 < RUN; ++e2) {
+                    mx = fmaxf(mx, fabsf(xf[e2]));
+                    sm += xf[e2];
+                }
+#pragma unroll
+                for (int o = 1; o < RPG; o <<= 1) {
+                    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+                    sm += __shfl_xor(sm, o, kWave);
+                }
+                const int e0 = max((int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127 - 5, -100);
+                uint32_t tb[3][RUN];
+#pragma unroll
+                for (int e2 = 0; e2 < RUN; ++e2) {
+                    float rem = xf[e2];
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl) {
+                        const float tv = fmaf(rem, ldexpf(1.f, 7 * pl - e0), kMagic);
+                        tb[pl][e2] = __float_as_uint(tv);              // low byte: the plane's int8 value
+                        rem = fmaf(-(tv - kMagic), ldexpf(1.f, e0 - 7 * pl), rem);
+                    }
+                }
+                if (idx < total) {
+                    uint8_t* row = xq + ((size_t)t * NG + g) * kXt8Row;
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl) {
+                        // dword d of a piece holds elements kl with byte order 4 d + b (i8_code_operand)
+                        if constexpr (BITS == 4) {
+                            // elements 0..7 of the run -> dword 0: 0, 2, 4, 6; dword 1: 1, 3, 5, 7
+                            const uint32_t d0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(tb[pl][6], tb[pl][4], 0x0C0C0400u),
+                                                                      __builtin_amdgcn_perm(tb[pl][2], tb[pl][0], 0x0C0C0400u), 0x05040100u);
+                            const uint32_t d1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(tb[pl][7], tb[pl][5], 0x0C0C0400u),
+                                                                      __builtin_amdgcn_perm(tb[pl][3], tb[pl][1], 0x0C0C0400u), 0x05040100u);
+                            const int piece = (cr >> 1) ^ xt8_swz(t, pl);
+                            *reinterpret_cast<uint2*>(row + pl * 128 + 16 * piece + 8 * (cr & 1)) = make_uint2(d0, d1);
+                        } else {
+                            // dword d holds elements d, d + 4, d + 8, d + 12
+                            uint32_t dd[4];
+#pragma unroll
+                            for (int d = 0; d < 4; ++d)
+                                dd[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(tb[pl][d + 12], tb[pl][d + 8], 0x0C0C0400u),
+                                                              __builtin_amdgcn_perm(tb[pl][d + 4], tb[pl][d], 0x0C0C0400u), 0x05040100u);
+                            const int piece = cr ^ xt8_swz(t, pl);
+                            *reinterpret_cast<uint4*>(row + pl * 128 + 16 * piece) = make_uint4(dd[0], dd[1], dd[2], dd[3]);
+                        }
+                    }
+                    if (cr == 0) xs[t * NG + g] = make_float2(ldexpf(1.f, e0), sm);
+                }
+            }
+        }
+    };
+
+    uint32_t wg[D][LW], wu[D][LW];
+    auto issue = [&](int slot, const uint8_t* gp, const uint8_t* up, int g) {
+        const gbytes_t gq = uniform_gptr(gp + (size_t)g * gstride);
+        const gbytes_t uq = uniform_gptr(up + (size_t)g * gstride);
+        if constexpr (BITS == 4) {
+            const u32x4_t A = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t>(gq + loff));
+            const u32x4_t B = __builtin_nontemporal_load(reinterpret_cast<gu32x4_t>(uq + loff));
+            wg[slot][0] = A.x; wg[slot][1] = A.y; wg[slot][2] = A.z; wg[slot][3] = A.w;
+            wu[slot][0] = B.x; wu[slot][1] = B.y; wu[slot][2] = B.z; wu[slot][3] = B.w;
+        } else {
+            const u32x2_t A = *reinterpret_cast<gu32x2_t>(gq + loff);
+            const u32x2_t B = *reinterpret_cast<gu32x2_t>(uq + loff);
+            wg[slot][0] = A.x; wg[slot][1] = A.y;
+            wu[slot][0] = B.x; wu[slot][1] = B.y;
+        }
+    };
+
+    Item cur, nxt;
+    fetch(0, cur);
+    const int NGP = (NGW + D - 1) / D * D;
+    auto gaddr = [&](int gl) { return gb + max(0, min(gl, ng - 1)); };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, cur.g, cur.u, gaddr(d));
+    stage(cur, sc_base);
+    if (tid < 8) reinterpret_cast<uint4*>(smem + zoff)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    stage_x(cur.entry);
+    lds_barrier();
+
+    // A operand rows: lane row m = 4 t + pl of token 4 b + t (tokens past the
+    // tile's rows read token 0; pl = 3 reads the zero row)
+    const int at = m >> 2, apl = m & 3;
+    const int gsz = apl == 3 ? 0 : kXt8Row;            // a group's step in the plane tile
+    for (int j = 0; j < n_my; ++j) {
+        const bool has_next = j + 1 < n_my;
+        if (has_next) fetch(j + 1, nxt);
+        else nxt = cur;
+        const float* my_sc = sc_base;
+        const int ncl = max(1, min(cur.n, rows_cap));
+        const int NB = (ncl + 3) >> 2;
+        int aoff[NBM][2];
+#pragma unroll
+        for (int b = 0; b < NBM; ++b) {
+            const int t = 4 * b + at < ncl ? 4 * b + at : 0;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                aoff[b][st] = apl == 3 ? zoff + 16 * (2 * q + st)
+                                       : t * NG * kXt8Row + apl * 128 + 16 * ((2 * q + st) ^ xt8_swz(t, apl));
+        }
+        float accg[NBM], accu[NBM];
+#pragma unroll
+        for (int b = 0; b < NBM; ++b) { accg[b] = 0.f; accu[b] = 0.f; }
+        int g0 = 0;
+        do {
+            const bool last = g0 + D >= NGP;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int gl = g0 + d;
+                if (gl < ng) {
+                    uint32_t Bg[2][4], Bu[2][4];
+                    i8_code_operand<BITS>(wg[d], 0, Bg[0]);
+                    i8_code_operand<BITS>(wg[d], 1, Bg[1]);
+                    i8_code_operand<BITS>(wu[d], 0, Bu[0]);
+                    i8_code_operand<BITS>(wu[d], 1, Bu[1]);
+                    const float4 sv = *reinterpret_cast<const float4*>(my_sc + gl * 64 + 4 * m);
+                    const int goff = (gb + gl) * gsz;
+#pragma unroll
+                    for (int b = 0; b < NBM; ++b) {
+                        if (b < NB) {
+                            int32x4_t Cg = {0, 0, 0, 0}, Cu = Cg;
+#pragma unroll
+                            for (int st = 0; st < 2; ++st) {
+                                const uint4 a4 = *reinterpret_cast<const uint4*>(smem + aoff[b][st] + goff);
+                                const uint32_t A[4] = {a4.x, a4.y, a4.z, a4.w};
+                                Cg = mfma_i8(A, Bg[st], Cg);
+                                Cu = mfma_i8(A, Bu[st], Cu);
+                            }
+                            const float2 hx = xs[min(4 * b + q, rows_cap - 1) * NG + gb + gl];
+                            const float Fg = fmaf(0x1p-7f, fmaf(0x1p-7f, (float)Cg[2], (float)Cg[1]), (float)Cg[0]);
+                            const float Fu = fmaf(0x1p-7f, fmaf(0x1p-7f, (float)Cu[2], (float)Cu[1]), (float)Cu[0]);
+                            accg[b] = fmaf(sv.x * hx.x, Fg, fmaf(sv.y, hx.y, accg[b]));
+                            accu[b] = fmaf(sv.z * hx.x, Fu, fmaf(sv.w, hx.y, accu[b]));
+                        }
+                    }
+                }
+                // consume slot d, then refill the same registers (a scheduling
+                // barrier keeps the refill after the use and in ring order)
+                __builtin_amdgcn_sched_barrier(0);
+                const bool go_next = last && has_next;
+                issue(d, go_next ? nxt.g : cur.g, go_next ? nxt.u : cur.u,
+                      gaddr(!last ? gl + D : (has_next ? d : ng - 1)));
+            }
+            g0 += D;
+        } while (g0 < NGP);
+
+        // ---- the NW waves' partials meet in LDS; waves ew..ew+3 finish the
+        // item: lane v = 64 (w - ew) + lane takes token v / 16, row v % 16 (the
+        // MFMA lane (token % 4) * 16 + row, block token / 4)
+        float* redb = red + (j & 1) * (NW * 64 * 2 * NBM);
+        float* mine = redb + (w * 64 + lane) * (2 * NBM);
+#pragma unroll
+        for (int b = 0; b < NBM; ++b) { mine[2 * b] = accg[b]; mine[2 * b + 1] = accu[b]; }
+        lds_barrier();
+        const int ew = 4 * (j % (NW / 4));
+        if (w >= ew && w < ew + 4) {
+            const int v = (w - ew) * 64 + lane, t = v >> 4, mm = v & 15;
+            if (t < 4 * NBM) {                                // uniform over the 16 lanes of a token
+                const int src = ((t & 3) * 16 + mm) * (2 * NBM) + 2 * (t >> 2);
+                float gt = redb[src], upv = redb[src + 1];
+                for (int w2 = 1; w2 < NW; ++w2) {
+                    gt += redb[w2 * 64 * 2 * NBM + src];
+                    upv += redb[w2 * 64 * 2 * NBM + src + 1];
+                }
+                const float hv = gt / (1.f + expf(-gt)) * upv;
+                // sum of h over the tile's 16 rows for this token (fixed order)
+                float part = hv + __shfl_xor(hv, 1, kWave);
+                part += __shfl_xor(part, 2, kWave);
+                part += __shfl_xor(part, 4, kWave);
+                part += __shfl_xor(part, 8, kWave);
+                if (t < ncl && cur.row0 >= 0 && cur.row0 + cur.n <= p.P) {
+                    const int r = cur.row0 + t;
+                    if (mm == 0) p.hpart[(size_t)r * (I / 16) + cur.it] = part;
+                    uint32_t hi, mid, lo;
+                    split3_bf16(hv, hi, mid, lo);
+                    const size_t plane = (size_t)p.P * I;
+                    uint16_t* hb = p.hp + (size_t)r * I + cur.it * 16 + mm;
+                    hb[0] = (uint16_t)hi;
+                    hb[plane] = (uint16_t)mid;
+                    hb[2 * plane] = (uint16_t)lo;
+                }
+            }
+        }
+        if (has_next) {
+            stage(nxt, sc_base);
+            // past the barrier above every wave is done with the old x planes
+            if (nxt.entry != cur.entry) {
+                stage_x(nxt.entry);
+                lds_barrier();
+            }
+        }
+        cur = nxt;
+    }
+}
+
 // ------------------------------------------------------------------- down
 // Persistent like gate/up.  The 4 waves form 4/KS row tiles of 32 output rows
 // times KS parts of K: with a short K (I / 128 small) each wave keeps several
@@ -879,6 +1209,41 @@ static void xt_launch(size_t lds, hipStream_t s, const MfmaParams& p) {
     hipLaunchKernelGGL((ffn_gateup_xt_kernel<BITS, D, SJ, NW>), dim3((unsigned)device_cus()), dim3(64 * NW), lds, s, p);
 }
 
+// The int8-plane x-tile kernel: LDS for NBM blocks of 4 tokens, and launch.
+static size_t xt8_lds_bytes(const moe_dims& d, int nw, int nbm) {
+    const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows;
+    const int NG = d.H / kGroup, NGW = (NG + nw - 1) / nw;
+    const size_t tiles = (((size_t)rows_cap * NG * kXt8Row + 128 + (size_t)rows_cap * NG * 8) + 15) & ~(size_t)15;
+    return tiles + ((size_t)nw * NGW * 64 + (size_t)2 * nw * 64 * 2 * nbm) * sizeof(float);
+}
+
+template <int BITS, int D, int SJ, int NW, int NBM>
+static void xt8_launch(size_t lds, hipStream_t s, const MfmaParams& p) {
+    hipLaunchKernelGGL((ffn_gateup_xt8_kernel<BITS, D, SJ, NW, NBM>), dim3((unsigned)device_cus()), dim3(64 * NW), lds, s,
+                       p);
+}
+
+template <int BITS, int SJ, int NW, int NBM>
+static void xt8_depth(int D, size_t lds, hipStream_t s, const MfmaParams& p) {
+    switch (D) {
+        case 8: xt8_launch<BITS, 8, SJ, NW, NBM>(lds, s, p); break;
+        case 6: xt8_launch<BITS, 6, SJ, NW, NBM>(lds, s, p); break;
+        case 5: xt8_launch<BITS, 5, SJ, NW, NBM>(lds, s, p); break;
+        case 4: xt8_launch<BITS, 4, SJ, NW, NBM>(lds, s, p); break;
+        case 3: xt8_launch<BITS, 3, SJ, NW, NBM>(lds, s, p); break;
+        case 2: xt8_launch<BITS, 2, SJ, NW, NBM>(lds, s, p); break;
+        default: xt8_launch<BITS, 1, SJ, NW, NBM>(lds, s, p); break;
+    }
+}
+
+// Tiles of 5 to 8 token rows (two blocks of 4); fewer rows fit the decode
+// kernels' LDS tile at any H whose plane tile fits here.
+template <int BITS, int NW>
+static void xt8_dispatch(int D, int SJ, size_t lds, hipStream_t s, const MfmaParams& p) {
+    if (SJ <= 1) xt8_depth<BITS, 1, NW, 2>(D, lds, s, p);
+    else xt8_depth<BITS, 2, NW, 2>(D, lds, s, p);
+}
+
 template <int BITS, int SJ, int NW>
 static void xt_depth(int D, size_t lds, hipStream_t s, const MfmaParams& p) {
     switch (D) {
@@ -929,6 +1294,14 @@ int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
     {
         const int NG = d.H / kGroup, NGW = (NG + kXtWaves - 1) / kXtWaves;
         const int SJ = (16 * NGW + 63) / 64;
+        const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows, nbm = (rows_cap + 3) / 4;
+        const size_t lds8 = xt8_lds_bytes(d, kXtWaves, nbm);
+        if (SJ <= 2 && nbm == 2 && lds8 <= kXtLdsLimit) {
+            const int D = xt_depth_for(NG, kXtWaves);
+            if (a.bits == 4) xt8_dispatch<4, kXtWaves>(D, SJ, lds8, s, p);
+            else xt8_dispatch<2, kXtWaves>(D, SJ, lds8, s, p);
+            return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        }
         const size_t lds = xt_lds_bytes(d, kXtWaves);
         if (SJ <= 2 && lds <= kXtLdsLimit) {
             const int D = xt_depth_for(NG, kXtWaves);

@@ -103,6 +103,29 @@ __device__ __forceinline__ int pair_order_row(int m) {
     else return (m >> 1) + 8 * (m & 1);                                           // 0,8,1,9,...,7,15
 }
 
+// ---------------------------------------------- integer matrix cores
+// Codes of MFMA step st (16 of the lane's 32 codes of a group) as bytes: 4-bit,
+// dword d holds nibbles (d & 1) + 2 b of word 2 st + d / 2; 2-bit, dword t holds
+// crumbs t + 4 b of word st (b: byte in the dword).
+template <int BITS>
+__device__ __forceinline__ void i8_code_operand(const uint32_t* w, int st, uint32_t (&out)[4]) {
+    if constexpr (BITS == 4) {
+        const uint32_t a = w[2 * st], b = w[2 * st + 1], M = 0x0F0F0F0Fu;
+        out[0] = a & M; out[1] = (a >> 4) & M;
+        out[2] = b & M; out[3] = (b >> 4) & M;
+    } else {
+        const uint32_t a = w[st], M = 0x03030303u;
+        out[0] = a & M; out[1] = (a >> 2) & M; out[2] = (a >> 4) & M; out[3] = (a >> 6) & M;
+    }
+}
+
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int32x4_t mfma_i8(const uint32_t (&a)[4], const uint32_t (&b)[4], int32x4_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int32x4_t, a), __builtin_bit_cast(int32x4_t, b),
+                                                 c, 0, 0, 0);
+}
+
 // A wave-uniform global pointer, passed through readfirstlane so that the
 // compiler keeps it whole: a load at uniform_gptr(base) + (32-bit lane offset)
 // then takes the scalar-base form (base in SGPRs, offset in one VGPR) instead

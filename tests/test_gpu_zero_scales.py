@@ -25,12 +25,16 @@ GEMM_G32 = mi.LayerShape("zs_gemm_g32", H=256, E=4, k=2, I=256, tokens=(200,), b
                          group=32)
 # the x tile does not fit 80 KB at T = 16: the x-tile gate/up and the streaming down
 BIG_SHAPE = mi.LayerShape("zs_big", H=3072, E=4, k=2, I=2048, tokens=(16,), bits=(4, 2), zipf_s=None, n_resident=2)
+# 8 token rows of H = 5120 do not fit the decode tile: the int8-plane x-tile gate/up
+XT8_SHAPE = mi.LayerShape("zs_xt8", H=5120, E=4, k=2, I=1024, tokens=(8,), bits=(4, 2), zipf_s=None, n_resident=2)
 
 CASES = [
     ("gemm_q4", GEMM_SHAPE, 4, moe.ALGO_GEMM),
     ("gemm_q4_g32", GEMM_G32, 4, moe.ALGO_GEMM),
     ("big_q4_mfma", BIG_SHAPE, 4, moe.ALGO_MFMA),
     ("big_q2_mfma", BIG_SHAPE, 2, moe.ALGO_MFMA),
+    ("xt8_q4_mfma", XT8_SHAPE, 4, moe.ALGO_MFMA),
+    ("xt8_q2_mfma", XT8_SHAPE, 2, moe.ALGO_MFMA),
     ("tiny_q4_mfma", mi.CONFIGS["tiny"], 4, moe.ALGO_MFMA),
     ("tiny_q2_gemv", mi.CONFIGS["tiny"], 2, moe.ALGO_GEMV),
 ]

@@ -28,7 +28,8 @@ Per workload:
   tokens/s      T * K / elapsed over K steps back to back (HIP events on the
                 stream at the two ends only);
   roofline      the expert FFN call (one launch at the A3B-style and
-                512-expert shapes; gate/up then down at the 64-expert shape):
+                512-expert shapes; at the 64-expert shape gate/up, then the
+                down call: its int8 conversion of h and the down kernel):
                 algorithmic weight bytes per call (experts used * 3 * H * I *
                 (bits/8 + 4/128)) over its mean duration, timed over K calls
                 back to back with events at the two ends, against 8 TB/s;
@@ -68,7 +69,7 @@ PER_CONFIG = [("a3b", 4, 1, 4, 1), ("a3b", 4, 8, 4, 2), ("a3b", 4, 32, 4, 4),
 
 # FFN kernels of each decode workload (the library's choice at these sizes)
 FFN_KERNELS = {
-    "e64": ("ffn_gateup_xt_kernel", "ffn_down_stream_kernel"),
+    "e64": ("ffn_gateup_xt8_kernel", "ffn_hquant_kernel", "ffn_down_stream_kernel"),
     "a3b": ("ffn_fused_dec_kernel",),
     "e512": ("ffn_fused_dec_kernel",),
 }

@@ -569,7 +569,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt_kernel(MfmaParams p)
 // F = C_0 + 2^-7 C_1 + 2^-14 C_2 as s hs F + b X per group (s, b: the weight
 // row's fp16 scale and bias; X: the token's float sum of x over the group).
 // Two MFMAs per 16-row tile, matrix and group for up to 4 tokens, against 8
-// in the kernel above.
+// in the kernel above.  NW is 10 or 12 (the launcher picks the count that
+// splits K most evenly); with 10, waves 0-3 and 4-7 take the epilogue in turns.
 // LDS: planes [rows_cap][NG][3][128] int8 (the 16-byte pieces of plane row
 // (t, p) swizzled by (t % 4) | 4 (p / 2): the 12 rows one read phase touches
 // fall on distinct banks), a 128-byte zero row, (hs, X) [rows_cap][NG] float
@@ -581,7 +582,7 @@ __device__ __forceinline__ int xt8_swz(int t, int pl) { return (t & 3) | ((pl >>
 
 template <int BITS, int D, int SJ, int NW, int NBM>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_gateup_xt8_kernel(MfmaParams p) {
-    static_assert(NW >= 4 && NW % 4 == 0, "groups of four waves share the epilogue");
+    static_assert(NW >= 4, "groups of four waves share the epilogue");
     constexpr int LB = 128 * BITS / 8 / 4;     // bytes per lane per group (16 or 8)
     constexpr int LW = LB / 4;                 // code words per lane per group
     constexpr int NT = 64 * NW;
@@ -1194,6 +1195,14 @@ static void down_dispatch(int D, int SJ, int KS, const moe_dims& d, size_t lds, 
 // The x-tile gate/up kernel: waves per workgroup (one workgroup per CU), the
 // LDS it needs, and its launch.
 constexpr int kXtWaves = 12;
+
+// Waves of the int8 x-tile kernel: 10 or 12, whichever gives the waves fewer
+// groups of K each (10 on a tie: 40 groups split 4 each over 10 waves took
+// 55.0-55.6 us at the 64-expert shape, 3 or 4 over 12 waves 56.9-57.8, 5 over 8
+// 57.5-58.7).
+static int xt8_waves(int NG) {
+    return (NG + 9) / 10 <= (NG + 11) / 12 ? 10 : 12;
+}
 constexpr size_t kXtLdsLimit = 160 * 1024;
 
 static size_t xt_lds_bytes(const moe_dims& d, int nw) {
@@ -1295,11 +1304,17 @@ int launch_gateup_mfma(const FfnArgs& a, hipStream_t s) {
         const int NG = d.H / kGroup, NGW = (NG + kXtWaves - 1) / kXtWaves;
         const int SJ = (16 * NGW + 63) / 64;
         const int rows_cap = d.T < kWorkRows ? d.T : kWorkRows, nbm = (rows_cap + 3) / 4;
-        const size_t lds8 = xt8_lds_bytes(d, kXtWaves, nbm);
-        if (SJ <= 2 && nbm == 2 && lds8 <= kXtLdsLimit) {
-            const int D = xt_depth_for(NG, kXtWaves);
-            if (a.bits == 4) xt8_dispatch<4, kXtWaves>(D, SJ, lds8, s, p);
-            else xt8_dispatch<2, kXtWaves>(D, SJ, lds8, s, p);
+        const int nw8 = xt8_waves(NG), NGW8 = (NG + nw8 - 1) / nw8, SJ8 = (16 * NGW8 + 63) / 64;
+        const size_t lds8 = xt8_lds_bytes(d, nw8, nbm);
+        if (SJ8 <= 2 && nbm == 2 && lds8 <= kXtLdsLimit) {
+            const int D = xt_depth_for(NG, nw8);
+            if (nw8 == 10) {
+                if (a.bits == 4) xt8_dispatch<4, 10>(D, SJ8, lds8, s, p);
+                else xt8_dispatch<2, 10>(D, SJ8, lds8, s, p);
+            } else {
+                if (a.bits == 4) xt8_dispatch<4, 12>(D, SJ8, lds8, s, p);
+                else xt8_dispatch<2, 12>(D, SJ8, lds8, s, p);
+            }
             return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
         }
         const size_t lds = xt_lds_bytes(d, kXtWaves);

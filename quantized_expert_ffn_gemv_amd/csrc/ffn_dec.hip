@@ -23,6 +23,7 @@
 // can follow either gate/up kernel.
 #include <algorithm>
 
+#include "launch_util.h"
 #include "mfma_ops.h"
 
 namespace moe {
@@ -1040,6 +1041,29 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void ffn_down_stream_kernel(DecPar
     }
 }
 
+// ---------------------------------------------------------- down by row block
+// The streaming down's parts with no split of K: workgroup b takes the items
+// (entry, block of 16 NW rows) b, b + G, ... over all of K, each a whole row
+// block written straight to y, so there are no partial sums, arrivals or range
+// tables.  NW waves of one 16-row tile each, the code ring D groups deep.
+// Taken when the work list's capacity gives at least one item per CU: at the
+// 64-expert shape (about 7 entries of 64 blocks of 80 rows) the items fill the
+// chip once, and the fixed costs of the split (range tables, part prologues,
+// partial sums and their reduction: about a third of its time) are gone.
+template <int BITS, int NW, int D, int CG, int NBM>
+__global__ __launch_bounds__(64 * NW) void ffn_down_rows_kernel(DecParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int NG = p.I / kGroup;
+    const int nw = max(0, min(ld_scalar(p.n_work, 0), p.cap));
+    const int items = nw * p.ipe;
+    SplitPlan sp{};                                     // unused: every part is a whole row block
+    for (int item = (int)blockIdx.x; item < items; item += (int)gridDim.x) {
+        const DecItem it = dec_item_at<false>(p, item / p.ipe, item % p.ipe);
+        if (item != (int)blockIdx.x) lds_barrier();     // the last item's LDS is no longer read
+        if (it.n > 0) down_stream_part<BITS, NW, 1, D, CG, NBM>(p, it, 0, NG, smem, sp, 0, 0);
+    }
+}
+
 // ------------------------------------------------------------ one-launch FFN
 // Gate/up and down in one launch.  The grid is cut into chunks of kFfnChunk
 // work-list entries; a chunk is its gate/up items, then its down items, each
@@ -1347,11 +1371,63 @@ static void ds_cg(int cg, size_t lds, hipStream_t s, const DecParams& p) {
     }
 }
 
+// The row-block down: waves per workgroup (one 16-row tile each): 5 where H
+// is a multiple of 80, else 4 (H is a multiple of 128 here); its code ring
+// depth and workgroups per CU.  Measured at the 64-expert shape (down call
+// with the conversion, us): 5 waves ring 4 32.4-33.2, ring 8 33.4-34.1; 4
+// waves 33.9-34.4; 8 waves 37.4-38.1; against 43.5-44.1 for the split of K.
+constexpr int kRowsDepth = 4, kRowsPerCu = 3;
+
+static int down_rows_waves(const moe_dims& d) { return d.H % 80 == 0 ? 5 : (d.H % 64 == 0 ? 4 : 0); }
+
+template <int BITS, int NW, int NBM>
+static void dr_go(int cg, size_t lds, hipStream_t s, const DecParams& p, int grid) {
+    if (cg == 4) hipLaunchKernelGGL((ffn_down_rows_kernel<BITS, NW, kRowsDepth, 4, NBM>), dim3(grid), dim3(64 * NW), lds, s, p);
+    else hipLaunchKernelGGL((ffn_down_rows_kernel<BITS, NW, kRowsDepth, 2, NBM>), dim3(grid), dim3(64 * NW), lds, s, p);
+}
+
+template <int BITS, int NW>
+static void dr_nbm(int nbm, int cg, size_t lds, hipStream_t s, const DecParams& p, int grid) {
+    if (nbm == 1) dr_go<BITS, NW, 1>(cg, lds, s, p, grid);
+    else if (nbm == 2) dr_go<BITS, NW, 2>(cg, lds, s, p, grid);
+    else dr_go<BITS, NW, 4>(cg, lds, s, p, grid);
+}
+
+// The row-block down (ffn_down_rows_kernel): the conversion of h, then whole
+// row blocks of 16 rw rows per workgroup.
+static int launch_down_rows(const FfnArgs& a, hipStream_t s, int cg, int rw) {
+    const moe_dims& d = a.d;
+    DecParams p = dec_params(a);
+    p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
+    p.ipe = d.H / (16 * rw);
+    p.n_split_ctr = 0;
+    const size_t lds = down_stream_lds(d, cg);
+    const int P = d.T * d.k, nq = P * (d.I / kGroup);
+    const int grid = (int)std::min<long>((long)p.cap * p.ipe, (long)kRowsPerCu * device_cus());
+    int8_t* hq = const_cast<int8_t*>(p.hq);
+    float* tab = const_cast<float*>(p.htab);
+    const int nbm = (p.rows_cap + 3) / 4;
+    if (a.bits == 4) {
+        hipLaunchKernelGGL(ffn_hquant_kernel<4>, dim3((nq + 3) / 4), dim3(256), 0, s, p.hp, hq, tab, P, d.I);
+        if (rw == 5) dr_nbm<4, 5>(nbm, cg, lds, s, p, grid);
+        else dr_nbm<4, 4>(nbm, cg, lds, s, p, grid);
+    } else {
+        hipLaunchKernelGGL(ffn_hquant_kernel<2>, dim3((nq + 3) / 4), dim3(256), 0, s, p.hp, hq, tab, P, d.I);
+        if (rw == 5) dr_nbm<2, 5>(nbm, cg, lds, s, p, grid);
+        else dr_nbm<2, 4>(nbm, cg, lds, s, p, grid);
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int launch_down_stream(const FfnArgs& a, hipStream_t s) {
     const moe_dims& d = a.d;
     if (d.T * d.k == 0) return MOE_OK;
     const int cg = down_stream_cg(d);
     if (cg == 0) return MOE_ERR_UNSUPPORTED;
+    // whole row blocks per workgroup when the call can have at least one per
+    // CU (the work-list capacity's worth); else K split over the workgroups
+    const int rw = down_rows_waves(d);
+    if (rw > 0 && (long)work_capacity(d) * (d.H / (16 * rw)) >= device_cus()) return launch_down_rows(a, s, cg, rw);
     DecParams p = dec_params(a);
     p.qa = a.w.q[2]; p.sa = a.w.scale[2]; p.ba = a.w.bias[2];
     p.ipe = d.H / kStreamRows;

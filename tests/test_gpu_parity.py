@@ -147,13 +147,15 @@ def test_persistent_kernel_shape_every_element(bits, algo):
 
 
 # Shapes whose down tile does not fit LDS, so the down projection streams h
-# through LDS in chunks of K: tiles of 1 to 5 rows (one 16-row block of packed
-# planes), 6 to 10 rows (two) and 11 to 16 rows (three), with chunks of four
-# groups, every element checked.
+# (as int8 planes) through LDS in chunks of K: tiles of 2, 7 and 12 token rows
+# (one, two and three blocks of 4 tokens), every element checked.  The first
+# three have fewer row blocks than CUs, so K is split over the workgroups; the
+# last has enough for whole row blocks of 80 rows per workgroup.
 STREAM_SHAPES = [
     mi.LayerShape("stream_1blk", H=512, E=3, k=1, I=16384, tokens=(2,), bits=(4, 2), zipf_s=None, n_resident=1),
     mi.LayerShape("stream_2blk", H=3072, E=2, k=2, I=2048, tokens=(7,), bits=(4, 2), zipf_s=None, n_resident=1),
     mi.LayerShape("stream_3blk", H=3072, E=2, k=2, I=2048, tokens=(12,), bits=(4, 2), zipf_s=None, n_resident=1),
+    mi.LayerShape("rows_80", H=2560, E=8, k=2, I=2048, tokens=(16,), bits=(4, 2), zipf_s=None, n_resident=2),
 ]
 
 

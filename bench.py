@@ -69,7 +69,7 @@ PER_CONFIG = [("a3b", 4, 1, 4, 1), ("a3b", 4, 8, 4, 2), ("a3b", 4, 32, 4, 4),
 
 # FFN kernels of each decode workload (the library's choice at these sizes)
 FFN_KERNELS = {
-    "e64": ("ffn_gateup_xt8_kernel", "ffn_hquant_kernel", "ffn_down_stream_kernel"),
+    "e64": ("ffn_gateup_xt8_kernel", "ffn_hquant_kernel", "ffn_down_rows_kernel"),
     "a3b": ("ffn_fused_dec_kernel",),
     "e512": ("ffn_fused_dec_kernel",),
 }

@@ -577,12 +577,12 @@ __global__ __launch_bounds__(256, 2) void ffn_down_dec_kernel(DecParams p) {
 
 // ------------------------------------------------------------ streaming down
 // The down projection for shapes whose h tile does not fit LDS (a large
-// intermediate size I).  Work: every (work-list entry, block of RI = 128
-// output rows, group of K) unit, cut into G ranges of equal estimated cost,
-// one per workgroup (G: two workgroups per CU).  Such shapes have few entries
-// (16 pairs over about 7 experts at the 64-expert shape, 260 row blocks of
-// full K), so whole row blocks per workgroup would leave half of the chip
-// idle; ranges keep every workgroup busy to the end.  A range covers the tail
+// intermediate size I) when the call has fewer row blocks than CUs (few
+// entries, or few rows: e.g. two entries of a 3072-row output); calls with
+// more take the row-block kernel below.  Work: every (work-list entry, block
+// of RI = 128 output rows, group of K) unit, cut into G ranges of equal
+// estimated cost, one per workgroup (G: two workgroups per CU), so every
+// workgroup stays busy to the end even with few row blocks.  A range covers the tail
 // of one row block, whole row blocks, and the head of another: the row blocks
 // it covers whole are written straight to y; a part of a row block leaves its
 // float partial sums in the workspace, and the last of the row block's

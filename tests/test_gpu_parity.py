@@ -167,6 +167,18 @@ def test_streaming_down_shapes(shape, bits):
 
 
 @pytest.mark.parametrize("bits", [4, 2])
+def test_row_block_down_second_round(bits):
+    """More row blocks than the row-block down's grid (3 workgroups per CU, 80
+    rows per block at H = 2560): some workgroups take a second block."""
+    shape = mi.LayerShape("rows_multi", H=2560, E=32, k=2, I=2048, tokens=(32,), bits=(4, 2), zipf_s=None,
+                          n_resident=2)
+    L = layer(shape.name, bits, shape)
+    g, _, _ = _stages(L, 32, seed=10, algo=moe.ALGO_MFMA)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert g["n_work"] * (shape.H // 80) > 3 * cus, g["n_work"]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
 def test_many_tokens_per_expert_mfma(bits):
     """Experts serving more than one 16-token tile (several MFMA passes)."""
     shape = mi.LayerShape("crowd", H=512, E=4, k=2, I=256, tokens=(40,), bits=(bits,), zipf_s=None, n_resident=2)
